@@ -1,0 +1,284 @@
+"""CPU oracle for DeepSeek-V3.2-style sparse MLA decode.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+__graft_entry__ and the CPU-baseline leg of bench.py may import this module.
+The product path (the HIP library and its Python binding) never calls it, and
+this module shares no code, table or constant generator with that path.
+
+Everything here is the plain definition, written out slowly in float64 with
+numpy (a matrix product, max, exp and log from the library are the only
+primitives used; no blocking, fusion or online rescaling):
+
+* e4m3fn decode -- the pages give the FP8 format as 1 sign, 4 exponent and
+  3 mantissa bits with range +-448 ("FlashMLA Sparse Decode 完整计算过程详解",
+  step 4.3, hardware note).  Subnormals (exponent field 0) and the NaN codes
+  (S.1111.111) are not spelled out there; the OCP E4M3 "fn" encoding is taken
+  (bias 7, subnormal = m/8 * 2^-6, no infinities).
+* 656-byte token row -- same page, step 2.2 and step 4.3: bytes [0,512) e4m3
+  NoPE codes, [512,528) four little-endian fp32 scales (one per 128 NoPE
+  dims), [528,656) 64 little-endian bf16 RoPE values.  Dequant is
+  code * scale (step 7.4); K = [NoPE || RoPE] (576 dims) and V = NoPE (512).
+* paged addressing -- step 7.2: block = idx // page_block_size,
+  offset = idx % page_block_size.  An index names a physical token; -1 is an
+  empty slot (step 1, step 7.7).  Indices outside [0, num_tokens) are treated
+  as empty as well (the sparse-prefill contract in "FlashMLA 与 DSA：内核、
+  流水线和正确性边界" section 4.0 calls -1 or out-of-range invalid).
+* attention -- "FlashMLA 与 DSA：内核、流水线和正确性边界" section 4.3 gives
+  the reference semantics: gather the selected rows, scores = q K^T * sm_scale,
+  invalid slots -> -inf, lse = logsumexp(scores), out = exp(scores - lse) V.
+  A slot that repeats a token counts once per slot.  When no slot is valid the
+  sparse-decode walkthrough (step 14.2) writes lse = +inf; out is then 0.
+* split-KV combine -- walkthrough step 14.2 (split partials are normalised
+  O_j and lse_j = log2(l_j) + m_j in base 2, -inf when empty) and step 16
+  (max over splits, weights 2^(lse_j - max), weighted mean of the O_j);
+  "FlashMLA 与 DSA" section 3.2 states the same merge.
+* tile scheduler -- walkthrough step 3 (blocks per request = ceil(topk/64),
+  a fixed overhead of 5 blocks per request, payload = ceil(total/parts) +
+  overhead, partitions filled left to right, a request that does not fit is
+  split).  The block size, overhead and partition count are parameters here.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NOPE = 512
+ROPE = 64
+DQK = NOPE + ROPE
+DV = 512
+ROW_FP8 = 656
+ROW_BF16 = 2 * DQK
+
+FMT_FP8 = 0
+FMT_BF16 = 1
+
+
+# ----------------------------------------------------------------------------
+# element decoders
+# ----------------------------------------------------------------------------
+def e4m3fn_value(code: np.ndarray) -> np.ndarray:
+    """uint8 e4m3fn codes -> float64 values (exact)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = (m / 8.0) * 2.0 ** -6
+    val = np.where(e == 0, sub, normal)
+    val = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+    return sign * val
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bit patterns -> float64 (exact: bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def f32le_value(b4: np.ndarray) -> np.ndarray:
+    """[..., 4] uint8 little-endian -> float64."""
+    b4 = np.ascontiguousarray(b4, dtype=np.uint8)
+    return b4.view("<f4")[..., 0].astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# row decoders
+# ----------------------------------------------------------------------------
+def decode_fp8_rows(rows: np.ndarray) -> np.ndarray:
+    """uint8 [..., 656] -> K float64 [..., 576] (V is K[..., :512])."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    lead = rows.shape[:-1]
+    codes = rows[..., :NOPE]
+    scales = f32le_value(rows[..., NOPE:NOPE + 16].reshape(*lead, 4, 4))   # [..., 4]
+    nope = e4m3fn_value(codes).reshape(*lead, 4, 128) * scales[..., None]
+    rope_bits = np.ascontiguousarray(rows[..., 528:656]).view("<u2")
+    rope = bf16_value(rope_bits)
+    return np.concatenate([nope.reshape(*lead, NOPE), rope], axis=-1)
+
+
+def decode_bf16_rows(rows: np.ndarray) -> np.ndarray:
+    """uint8 [..., 1152] (576 little-endian bf16) -> float64 [..., 576]."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    return bf16_value(rows.view("<u2"))
+
+
+def token_rows(kv: np.ndarray, kv_format: int) -> np.ndarray:
+    """View the cache as [num_tokens, row_bytes] bytes (fp8: [nb, P, 1, 656])."""
+    if kv_format == FMT_FP8:
+        nb, P, hk, rb = kv.shape
+        assert hk == 1 and rb == ROW_FP8
+        return kv.reshape(nb * P, ROW_FP8)
+    s_kv, rb = kv.shape
+    assert rb == ROW_BF16
+    return kv
+
+
+def fetch_row(kv: np.ndarray, kv_format: int, idx: int, page_block_size: int) -> np.ndarray:
+    """Bytes of one token row, addressed as page (idx // P), offset (idx % P)."""
+    if kv_format == FMT_FP8:
+        return kv[idx // page_block_size, idx % page_block_size, 0]
+    return kv[idx]
+
+
+def num_tokens_of(kv: np.ndarray, kv_format: int) -> int:
+    return kv.shape[0] * kv.shape[1] if kv_format == FMT_FP8 else kv.shape[0]
+
+
+def slot_valid(indices: np.ndarray, num_tokens: int) -> np.ndarray:
+    idx = np.asarray(indices, dtype=np.int64)
+    return (idx >= 0) & (idx < num_tokens)
+
+
+def gather_dequant(kv: np.ndarray, indices: np.ndarray, kv_format: int,
+                   page_block_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows selected by `indices` [..., topk], decoded to float64 [..., topk, 576].
+
+    Empty slots give zero rows.  Returns (rows, valid_mask)."""
+    P = page_block_size if kv_format == FMT_FP8 else 1
+    n_tok = num_tokens_of(kv, kv_format)
+    idx = np.asarray(indices, dtype=np.int64)
+    valid = slot_valid(idx, n_tok)
+    flat = token_rows(kv, kv_format)
+    safe = np.where(valid, idx, 0)
+    if kv_format == FMT_FP8:
+        # page / offset addressing (identical to flat row idx for a dense [nb, P] cache)
+        raw = kv[safe // P, safe % P, 0]
+        rows = decode_fp8_rows(raw)
+    else:
+        rows = decode_bf16_rows(flat[safe])
+    rows = np.where(valid[..., None], rows, 0.0)
+    return rows, valid
+
+
+# ----------------------------------------------------------------------------
+# attention (definition)
+# ----------------------------------------------------------------------------
+def logsumexp(s: np.ndarray) -> np.ndarray:
+    """Natural-log log-sum-exp over the last axis (max taken out first)."""
+    m = s.max(axis=-1, keepdims=True)
+    return m[..., 0] + np.log(np.exp(s - m).sum(axis=-1))
+
+
+def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, valid: np.ndarray,
+           sm_scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One query token.  qh [H, 576], K [n, 576], V [n, 512], valid [n].
+
+    Returns out [H, 512] and natural-log lse [H] (float64); +inf / 0 when no
+    slot is valid."""
+    H = qh.shape[0]
+    if not np.any(valid):
+        return np.zeros((H, DV)), np.full(H, np.inf)
+    s = (qh @ K.T) * sm_scale                          # [H, n]
+    s = np.where(valid[None, :], s, -np.inf)
+    lse = logsumexp(s)
+    w = np.exp(s - lse[:, None])
+    return w @ V, lse
+
+
+def sparse_mla_decode(q_bits: np.ndarray, kv: np.ndarray, indices: np.ndarray,
+                      sm_scale: float, kv_format: int, page_block_size: int,
+                      queries: Optional[Iterable[Tuple[int, int]]] = None):
+    """Sparse MLA decode by definition.
+
+    q_bits: uint16 bf16 [b, s_q, H, 576]; kv: fp8 uint8 [nb, P, 1, 656] or
+    bf16-row bytes uint8 [s_kv, 1152]; indices int32 [b, s_q, topk].
+    Returns out float64 [b, s_q, H, 512] and lse float64 [b, H, s_q]
+    (natural log).  With `queries`, only those (bi, sj) pairs are filled and
+    the others are NaN.
+    """
+    b, s_q, H, d = q_bits.shape
+    assert d == DQK
+    out = np.full((b, s_q, H, DV), np.nan)
+    lse = np.full((b, H, s_q), np.nan)
+    if queries is None:
+        queries = [(bi, sj) for bi in range(b) for sj in range(s_q)]
+    for bi, sj in queries:
+        rows, valid = gather_dequant(kv, indices[bi, sj], kv_format, page_block_size)
+        qh = bf16_value(q_bits[bi, sj])
+        o, l = attend(qh, rows, rows[:, :DV], valid, sm_scale)
+        out[bi, sj] = o
+        lse[bi, :, sj] = l
+    return out, lse
+
+
+def partial_attention(qh, K, V, valid, sm_scale):
+    """Split partial over a subset of slots in the form a split writes:
+    normalised O_j [H, 512] and lse_j in base 2 (-inf when the subset is empty)."""
+    o, l = attend(qh, K, V, valid, sm_scale)
+    lse2 = np.where(np.isinf(l), -np.inf, l / math.log(2.0))
+    o = np.where(np.isinf(l)[:, None], 0.0, o)
+    return o, lse2
+
+
+def splitkv_combine(o_parts: np.ndarray, lse2_parts: np.ndarray):
+    """Merge split partials.  o_parts [n, H, 512] (normalised), lse2_parts [n, H]
+    (base 2).  Returns out [H, 512] and natural-log lse [H]."""
+    lse2 = np.asarray(lse2_parts, dtype=np.float64)
+    M = lse2.max(axis=0)                                   # [H]
+    empty = np.isneginf(M)
+    Ms = np.where(empty, 0.0, M)
+    w = np.exp2(lse2 - Ms[None, :])                        # [n, H]; 0 for -inf parts
+    tot = w.sum(axis=0)
+    out = (w[:, :, None] * o_parts).sum(axis=0) / np.where(empty, 1.0, tot)[:, None]
+    out = np.where(empty[:, None], 0.0, out)
+    lse = np.where(empty, np.inf, (Ms + np.log2(np.where(empty, 1.0, tot))) * math.log(2.0))
+    return out, lse
+
+
+# ----------------------------------------------------------------------------
+# scheduler (greedy left-to-right partition fill)
+# ----------------------------------------------------------------------------
+SCHED_FIELDS = ("begin_req", "end_req", "begin_block", "end_block",
+                "begin_split", "first_splitted", "last_splitted")
+
+
+def sched_plan(topk_per_req: Sequence[int], block: int, overhead: int,
+               num_parts: int) -> Tuple[List[Tuple[int, ...]], List[int]]:
+    """Greedy tile scheduler.
+
+    Returns (parts, prefix): parts[p] = (begin_req, end_req, begin_block,
+    end_block, begin_split, first_splitted, last_splitted) with end_req
+    inclusive and end_block exclusive (blocks of end_req); a partition with no
+    work has begin_req == number of requests.  prefix[r] is the index of the
+    first split of request r (prefix[-1] = total splits)."""
+    n = len(topk_per_req)
+    blocks = [(t + block - 1) // block for t in topk_per_req]
+    total = sum(bl + overhead for bl in blocks)
+    payload = (total + num_parts - 1) // num_parts + overhead if n else 0
+    splits = [0] * n
+    parts = []
+    req, done_blocks, cursor = 0, 0, 0
+    for _ in range(num_parts):
+        if req >= n:
+            parts.append((n, n, 0, 0, cursor, 0, 0))
+            continue
+        begin_req, begin_block = req, done_blocks
+        first_splitted = int(done_blocks > 0)
+        remain = payload
+        end_req, end_block, last_splitted = req, done_blocks, 0
+        while req < n:
+            left = blocks[req] - done_blocks
+            if left + overhead <= remain:
+                remain -= left + overhead
+                splits[req] += 1
+                end_req, end_block, last_splitted = req, blocks[req], 0
+                req, done_blocks = req + 1, 0
+            else:
+                take = remain - overhead
+                if take > 0:
+                    splits[req] += 1
+                    done_blocks += take
+                    end_req, end_block, last_splitted = req, done_blocks, 1
+                break
+        parts.append((begin_req, end_req, begin_block, end_block, cursor,
+                      first_splitted, last_splitted))
+        # number of splits this partition opened
+        cursor += end_req - begin_req + 1
+    prefix = [0]
+    for s in splits:
+        prefix.append(prefix[-1] + s)
+    assert prefix[-1] == cursor
+    return parts, prefix
