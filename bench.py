@@ -1,0 +1,163 @@
+#!/usr/bin/env python3
+"""Sparse MLA decode benchmark (one MI355X).
+
+A step is one pass of the whole hot path on one batch: the tile scheduler,
+the decode kernel and the split-KV combine, for b=64 query tokens, 128 heads,
+topk=2048 slots into a paged FP8 cache of 32768 tokens per sequence.  Steps
+rotate over --layers independent layers (own cache, Q and indices each) so
+the gathered rows of one step are not still cached in the 256 MB Infinity
+Cache when that layer comes round again.  Inputs are resident in HBM before
+the timed region starts.
+
+Prints one JSON line.  With --gpus N > 1 it exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode query-tokens/s at b=64,h=128,topk=2048; % of MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+
+
+def algorithmic(w):
+    """Flops of the two contractions over valid slots and compulsory HBM bytes
+    (gathered rows + Q + out + indices + lse) of one decode of workload w."""
+    import numpy as np
+    valid = (w.indices >= 0) & (w.indices < w.num_kv_tokens)
+    n_valid = int(valid.sum())
+    flops = 2.0 * w.h_q * n_valid * (576 + 512)
+    bytes_ = (n_valid * w.row_bytes + w.b * w.s_q * w.h_q * 576 * 2 + w.b * w.s_q * w.h_q * 512 * 2
+              + w.indices.size * 4 + w.b * w.s_q * w.h_q * 4)
+    return flops, float(bytes_), n_valid
+
+
+def cpu_baseline(w, budget_s: float):
+    """The CPU oracle, as it stands, on the first query tokens of layer 0 until
+    the time budget is spent; returns query-tokens/s and what was run."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import mla_oracle as O
+    kv = w.kv_host()
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        bi, sj = divmod(done, w.s_q)
+        if bi >= w.b:
+            break
+        O.sparse_mla_decode(w.q_bits, kv, w.indices, w.sm_scale, w.kv_format, w.page_block_size,
+                            queries=[(bi, sj)])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": done / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.b * w.s_q} query tokens of the same workload (layer 0), "
+                      f"{dt:.1f} s, numpy float64 with {threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--split-granularity", type=int, default=32)
+    ap.add_argument("--fixed-overhead", type=int, default=2)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sparse decode shards by query token with no exchange); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sparse_mla_attention_decode_amd as M
+    from sparse_mla_attention_decode_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    M.load_library()
+
+    print(f"[bench] building {args.layers} layers of {W.CONFIG_NAMES[1]}", file=sys.stderr, flush=True)
+    layers = []
+    for l in range(args.layers):
+        w = W.make_config(1) if l == 0 else W.paged_decode(
+            f"{W.CONFIG_NAMES[1]}_layer{l}", W.BASE_SEED + 1 + 1000 * l, b=64, s_q=1, h_q=128,
+            topk=2048, tokens_per_seq=32768)
+        layers.append((w, w.q_device(dev), w.kv_device(dev), w.indices_device(dev)))
+    w0 = layers[0][0]
+    shape = M.make_shape(w0.b, w0.s_q, w0.h_q, w0.topk, w0.num_kv_tokens, w0.kv_format,
+                         w0.page_block_size, split_granularity=args.split_granularity,
+                         fixed_overhead=args.fixed_overhead)
+    plan = M.DecodePlan(shape, device=dev)
+    argsets = [plan.args(q, kv, idx, w.sm_scale) for (w, q, kv, idx) in layers]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        a = argsets[i % len(argsets)]
+        plan.get_sched_meta()
+        if ev is not None:
+            ev[0].record(stream)
+        M.mla_sparse_decode_fwd(a)
+        if ev is not None:
+            ev[1].record(stream)
+        M.mla_splitkv_combine(a)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    flops, bytes_, n_valid = algorithmic(w0)
+    achieved_tflops = flops / (decode_ms * 1e-3) / 1e12
+    t_roof_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
+    q_tokens = w0.b * w0.s_q
+    value = q_tokens / (ms_per_step * 1e-3)
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.CONFIG_NAMES[1], "b": w0.b, "s_q": w0.s_q, "h_q": w0.h_q,
+                   "topk": w0.topk, "kv_cache": "fp8 656 B/token, page 64, 32768 tokens/seq",
+                   "layers_rotated": args.layers, "split_granularity": args.split_granularity,
+                   "fixed_overhead": args.fixed_overhead, "num_parts": plan.shape.num_parts,
+                   "step": "sched + decode + combine"},
+        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "decode_kernel<fp8,4 waves>", "kernel_ms": decode_ms,
+                     "algorithmic_flop_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
+                     "hbm_achieved_GBs": bytes_ / (decode_ms * 1e-3) / 1e9},
+        "step_roofline_frac": t_roof_ms / ms_per_step,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w0, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

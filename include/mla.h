@@ -1,0 +1,180 @@
+/*
+ * mla.h -- C ABI of libmla, a gfx950 (MI355X) sparse MLA attention decode
+ * library for DeepSeek-V3.2-shaped attention: h_q query heads (64 or 128)
+ * share one compressed KV head, d_qk = 576 (512 NoPE + 64 RoPE), d_v = 512.
+ *
+ * Operation (reference semantics: "FlashMLA 与 DSA：内核、流水线和正确性边界",
+ * section 4.3; call shapes: "FlashMLA Sparse Decode 完整计算过程详解", steps 1,
+ * 2.2, 2.3 and 19):
+ *   for every query token (b, s) and head h, over the topk slots k with
+ *   t = indices[b, s, k]:
+ *     slot k is valid iff 0 <= t < num_kv_tokens  (-1 marks an empty slot);
+ *     K_t = dequantised token row t (576 values), V_t = K_t[0:512];
+ *     score_k = sm_scale * <q[b,s,h,:], K_t>        (-inf when invalid)
+ *     lse[b,h,s] = ln sum_k exp(score_k)            (+inf when no slot is valid)
+ *     out[b,s,h,:] = sum_k exp(score_k - lse) V_t   (0 when no slot is valid)
+ *   A repeated token counts once per slot.
+ *
+ * KV formats:
+ *   MLA_KV_FP8_656  paged cache [num_blocks, page_block_size, 1, 656] bytes; a
+ *                   token row holds 512 e4m3fn NoPE codes, four little-endian
+ *                   fp32 power-of-two scales (one per 128 NoPE dims) and 64
+ *                   bf16 RoPE values ("FlashMLA Sparse Decode 完整计算过程详解",
+ *                   steps 2.2 and 4.3).  Token t lives in page t / P at offset
+ *                   t % P (step 7.2); NoPE dequant is code * scale (step 7.4).
+ *   MLA_KV_BF16_576 flat cache [s_kv, 576] bf16 with logical indices (the
+ *                   sparse-prefill contract of "FlashMLA 与 DSA", section 4.0).
+ *
+ * Work split (step 3 of the walkthrough): the topk list of every request is cut
+ * into blocks of split_granularity slots; a greedy left-to-right plan assigns
+ * (request, block range) pieces to num_parts partitions with a fixed per-request
+ * cost of fixed_overhead blocks.  A request whose blocks land in more than one
+ * partition is "split": each piece writes a normalised fp32 partial O and a
+ * base-2 lse (step 14) and mla_splitkv_combine merges them (step 16).  A request
+ * that lands in exactly one partition is written to out/lse directly.
+ *
+ * Conventions:
+ *   - Every pointer in mla_decode_args is device memory owned by the caller; the
+ *     library allocates nothing, keeps no per-call state, and never frees.
+ *   - Calls that take a stream are asynchronous on that stream (hipStream_t
+ *     passed as void*, NULL = the default stream).  Kernel launch failures are
+ *     reported as MLA_ERR_HIP.
+ *   - Every argument is validated on the host before anything is launched; on
+ *     error nothing is launched, the status is returned and mla_last_error()
+ *     holds a message (thread-local).  The library never aborts the process.
+ *   - Calls that overlap on one stream-ordered pipeline must use distinct
+ *     sched/workspace buffers if they run concurrently on different streams.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MLA_OK                0
+#define MLA_ERR_INVALID_ARG  -1   /* a pointer, size, stride or shape is wrong     */
+#define MLA_ERR_UNSUPPORTED  -2   /* a valid request this build does not support   */
+#define MLA_ERR_WORKSPACE    -3   /* a sched or workspace buffer is too small      */
+#define MLA_ERR_HIP          -4   /* the HIP runtime reported an error             */
+#define MLA_ERR_NO_DEVICE    -5   /* a device property was needed and none exists  */
+
+/* KV cache formats */
+#define MLA_KV_FP8_656   0
+#define MLA_KV_BF16_576  1
+
+/* Problem shape.  All fields are plain host values. */
+typedef struct mla_shape {
+    int32_t b;                 /* requests (batch), >= 1                               */
+    int32_t s_q;               /* query tokens per request, >= 1                       */
+    int32_t h_q;               /* query heads: 64 or 128                                */
+    int32_t h_kv;              /* KV heads: must be 1                                   */
+    int32_t d_qk;              /* must be 576                                           */
+    int32_t d_v;               /* must be 512                                           */
+    int32_t topk;              /* slots per query token, >= 1                           */
+    int32_t page_block_size;   /* FP8: tokens per page (>= 1); BF16: ignored (use 1)    */
+    int64_t num_kv_tokens;     /* FP8: num_blocks * page_block_size; BF16: s_kv; >= 1   */
+    int32_t kv_format;         /* MLA_KV_FP8_656 or MLA_KV_BF16_576                     */
+    int32_t num_parts;         /* scheduler partitions (work-groups per query-token
+                                  column); 0 = derive from the current device's CU count */
+    int32_t split_granularity; /* topk slots per scheduler block, a multiple of 32;
+                                  0 = 64 (the walkthrough's TOPK_BLOCK_SIZE)            */
+    int32_t fixed_overhead;    /* per-request scheduler cost in blocks; < 0 = 5 (the
+                                  walkthrough's fixed_overhead_num_blocks)              */
+} mla_shape;
+
+/* One scheduler partition (32 bytes, int32 fields).  end_req is inclusive,
+ * end_block is exclusive and counts blocks of end_req; begin_split is the
+ * global split index of the first piece; a partition with begin_req >= b is idle. */
+typedef struct mla_sched_part {
+    int32_t begin_req, end_req, begin_block, end_block;
+    int32_t begin_split, first_splitted, last_splitted, reserved;
+} mla_sched_part;
+
+typedef struct mla_decode_args {
+    mla_shape shape;
+    float sm_scale;                     /* softmax scale; <= 0 means 1/sqrt(d_qk)         */
+
+    const void* q;                      /* bf16 [b, s_q, h_q, 576], last dim contiguous    */
+    int64_t q_stride_b, q_stride_s, q_stride_h;          /* in elements, multiples of 8   */
+
+    const void* kv;                     /* FP8: [num_blocks, P, 1, 656] bytes (token stride
+                                           656 B); BF16: [s_kv, kv_stride_block/2] bf16     */
+    int64_t kv_stride_block;            /* FP8: bytes per page (>= P*656); BF16: bytes per
+                                           token row (>= 1152); multiple of 16              */
+
+    const int32_t* indices;             /* [b, s_q, topk], last dim contiguous; FP8:
+                                           physical token ids, BF16: row ids; -1 = empty   */
+    int64_t idx_stride_b, idx_stride_s; /* in elements                                      */
+
+    void* out;                          /* bf16 [b, s_q, h_q, 512], last dim contiguous    */
+    int64_t out_stride_b, out_stride_s, out_stride_h;    /* in elements, multiples of 4   */
+    float* lse;                         /* fp32 [b, h_q, s_q] contiguous, natural log      */
+
+    const float* attn_sink;             /* must be NULL (not supported by this build)      */
+    const int32_t* topk_length;         /* must be NULL (not supported by this build)      */
+
+    const void* sched_meta;             /* from mla_get_sched_meta (same shape)            */
+    const int32_t* num_splits;          /* [b + 1] split prefix from mla_get_sched_meta    */
+
+    float* o_accum;                     /* workspace, >= mla_workspace_size bytes          */
+    float* lse_accum;                   /* workspace, >= mla_workspace_size bytes          */
+    size_t o_accum_bytes, lse_accum_bytes;               /* capacities of the two above   */
+} mla_decode_args;
+
+/* Sizes of the scheduler outputs for `shape`: meta = num_parts * 32 bytes,
+ * num_splits = (b + 1) * 4 bytes.  Needs a device only when num_parts == 0. */
+int mla_sched_meta_size(const mla_shape* shape, size_t* meta_bytes, size_t* num_splits_bytes);
+
+/* Split workspace sizes: (b + num_parts) * s_q * h_q * 512 * 4 bytes for
+ * o_accum and (b + num_parts) * s_q * h_q * 4 bytes for lse_accum. */
+int mla_workspace_size(const mla_shape* shape, size_t* o_accum_bytes, size_t* lse_accum_bytes);
+
+/* Resolve the defaults of `shape` (num_parts, split_granularity, fixed_overhead)
+ * in place, exactly as the other calls do. */
+int mla_resolve_shape(mla_shape* shape);
+
+/* Tile scheduler ("FlashMLA Sparse Decode 完整计算过程详解", step 3): computes
+ * the partition plan on the device (one wave) into sched_meta_dev
+ * (num_parts mla_sched_part records) and num_splits_dev (b + 1 int32 prefix).
+ * It depends on the shape only, so one plan serves every layer of a step. */
+int mla_get_sched_meta(const mla_shape* shape, void* sched_meta_dev,
+                       int32_t* num_splits_dev, void* stream);
+
+/* The same plan computed on the host into host buffers of the same sizes. */
+int mla_plan_sched_meta_host(const mla_shape* shape, void* sched_meta_host,
+                             int32_t* num_splits_host);
+
+/* Sparse decode ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14):
+ * gathers and dequantises the selected rows, runs the two bf16 contractions with
+ * an online softmax, and writes out/lse for unsplit requests and o_accum /
+ * lse_accum (base 2) for split ones. */
+int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream);
+
+/* Split-KV combine (step 16): merges the partials of every split request into
+ * out / lse; unsplit requests are left untouched. */
+int mla_splitkv_combine(const mla_decode_args* args, void* stream);
+
+/* Test hook for the gather + dequant stage: for every (b, s, slot) writes the
+ * dequantised 576-value row as the decode kernel stages it, bf16
+ * [b, s_q, topk, 576] into k_rows; if v_rows is not NULL also the 512 V values
+ * read back through the decode kernel's transposed V layout, bf16
+ * [b, s_q, topk, 512].  Empty slots give zero rows.  Both contiguous. */
+int mla_debug_gather_dequant(const mla_decode_args* args, void* k_rows, void* v_rows,
+                             void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* Library version string. */
+const char* mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,224 @@
+"""ctypes binding of libmla (include/mla.h).
+
+Argument marshalling only: every function here forwards to the C ABI of the
+same name; torch tensors are used for device memory and the current stream.
+If libmla.so has not been built, importing the binding raises -- there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_WORKSPACE = -3
+MLA_ERR_HIP = -4
+MLA_ERR_NO_DEVICE = -5
+
+MLA_KV_FP8_656 = 0
+MLA_KV_BF16_576 = 1
+
+EXPORTED = ("mla_sched_meta_size", "mla_workspace_size", "mla_resolve_shape",
+            "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_sparse_decode_fwd",
+            "mla_splitkv_combine", "mla_debug_gather_dequant", "mla_last_error", "mla_version")
+
+
+class mla_shape(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int32), ("s_q", ctypes.c_int32), ("h_q", ctypes.c_int32),
+                ("h_kv", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("page_block_size", ctypes.c_int32),
+                ("num_kv_tokens", ctypes.c_int64), ("kv_format", ctypes.c_int32),
+                ("num_parts", ctypes.c_int32), ("split_granularity", ctypes.c_int32),
+                ("fixed_overhead", ctypes.c_int32)]
+
+
+class mla_decode_args(ctypes.Structure):
+    _fields_ = [("shape", mla_shape), ("sm_scale", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("q_stride_b", ctypes.c_int64),
+                ("q_stride_s", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+                ("kv", ctypes.c_void_p), ("kv_stride_block", ctypes.c_int64),
+                ("indices", ctypes.c_void_p), ("idx_stride_b", ctypes.c_int64),
+                ("idx_stride_s", ctypes.c_int64),
+                ("out", ctypes.c_void_p), ("out_stride_b", ctypes.c_int64),
+                ("out_stride_s", ctypes.c_int64), ("out_stride_h", ctypes.c_int64),
+                ("lse", ctypes.c_void_p),
+                ("attn_sink", ctypes.c_void_p), ("topk_length", ctypes.c_void_p),
+                ("sched_meta", ctypes.c_void_p), ("num_splits", ctypes.c_void_p),
+                ("o_accum", ctypes.c_void_p), ("lse_accum", ctypes.c_void_p),
+                ("o_accum_bytes", ctypes.c_size_t), ("lse_accum_bytes", ctypes.c_size_t)]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m sparse_mla_attention_decode_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    sig = {
+        "mla_sched_meta_size": [P(mla_shape), sz, sz],
+        "mla_workspace_size": [P(mla_shape), sz, sz],
+        "mla_resolve_shape": [P(mla_shape)],
+        "mla_get_sched_meta": [P(mla_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
+        "mla_plan_sched_meta_host": [P(mla_shape), ctypes.c_void_p, ctypes.c_void_p],
+        "mla_sparse_decode_fwd": [P(mla_decode_args), ctypes.c_void_p],
+        "mla_splitkv_combine": [P(mla_decode_args), ctypes.c_void_p],
+        "mla_debug_gather_dequant": [P(mla_decode_args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
+    }
+    for name, argtypes in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = argtypes
+        f.restype = ctypes.c_int
+    for name in ("mla_last_error", "mla_version"):
+        f = getattr(lib, name)
+        f.argtypes = []
+        f.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int) -> int:
+    if code != MLA_OK:
+        raise MlaError(fn, code, load_library().mla_last_error().decode())
+    return code
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return int(stream)
+
+
+# ----------------------------------------------------------------------------- thin wrappers
+def mla_version() -> str:
+    return load_library().mla_version().decode()
+
+
+def mla_last_error() -> str:
+    return load_library().mla_last_error().decode()
+
+
+def mla_resolve_shape(shape: mla_shape) -> mla_shape:
+    s = mla_shape.from_buffer_copy(shape)
+    _check("mla_resolve_shape", load_library().mla_resolve_shape(ctypes.byref(s)))
+    return s
+
+
+def mla_sched_meta_size(shape: mla_shape) -> Tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("mla_sched_meta_size", load_library().mla_sched_meta_size(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def mla_workspace_size(shape: mla_shape) -> Tuple[int, int]:
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("mla_workspace_size", load_library().mla_workspace_size(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def mla_plan_sched_meta_host(shape: mla_shape, meta_ptr: int, num_splits_ptr: int) -> None:
+    _check("mla_plan_sched_meta_host", load_library().mla_plan_sched_meta_host(ctypes.byref(shape), meta_ptr, num_splits_ptr))
+
+
+def mla_get_sched_meta(shape: mla_shape, meta_ptr: int, num_splits_ptr: int, stream=None) -> None:
+    _check("mla_get_sched_meta", load_library().mla_get_sched_meta(ctypes.byref(shape), meta_ptr, num_splits_ptr, _stream(stream)))
+
+
+def mla_sparse_decode_fwd(args: mla_decode_args, stream=None) -> None:
+    _check("mla_sparse_decode_fwd", load_library().mla_sparse_decode_fwd(ctypes.byref(args), _stream(stream)))
+
+
+def mla_splitkv_combine(args: mla_decode_args, stream=None) -> None:
+    _check("mla_splitkv_combine", load_library().mla_splitkv_combine(ctypes.byref(args), _stream(stream)))
+
+
+def mla_debug_gather_dequant(args: mla_decode_args, k_rows_ptr: int, v_rows_ptr: int, stream=None) -> None:
+    _check("mla_debug_gather_dequant",
+           load_library().mla_debug_gather_dequant(ctypes.byref(args), k_rows_ptr, v_rows_ptr, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- torch plumbing
+def make_shape(b, s_q, h_q, topk, num_kv_tokens, kv_format=MLA_KV_FP8_656, page_block_size=64,
+               num_parts=0, split_granularity=0, fixed_overhead=-1) -> mla_shape:
+    return mla_shape(b=b, s_q=s_q, h_q=h_q, h_kv=1, d_qk=576, d_v=512, topk=topk,
+                     page_block_size=page_block_size if kv_format == MLA_KV_FP8_656 else 1,
+                     num_kv_tokens=num_kv_tokens, kv_format=kv_format, num_parts=num_parts,
+                     split_granularity=split_granularity, fixed_overhead=fixed_overhead)
+
+
+class DecodePlan:
+    """Device buffers (sched meta, split prefix, workspace, outputs) for one shape,
+    allocated with torch.  The plan can be reused for every call of that shape."""
+
+    def __init__(self, shape: mla_shape, device="cuda"):
+        import torch
+        self.shape = mla_resolve_shape(shape)
+        meta_b, ns_b = mla_sched_meta_size(self.shape)
+        o_b, l_b = mla_workspace_size(self.shape)
+        s = self.shape
+        self.sched_meta = torch.empty(meta_b // 4, dtype=torch.int32, device=device)
+        self.num_splits = torch.empty(ns_b // 4, dtype=torch.int32, device=device)
+        self.o_accum = torch.empty(o_b // 4, dtype=torch.float32, device=device)
+        self.lse_accum = torch.empty(l_b // 4, dtype=torch.float32, device=device)
+        self.out = torch.empty((s.b, s.s_q, s.h_q, 512), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((s.b, s.h_q, s.s_q), dtype=torch.float32, device=device)
+
+    def get_sched_meta(self, stream=None):
+        mla_get_sched_meta(self.shape, self.sched_meta.data_ptr(), self.num_splits.data_ptr(), stream)
+
+    def args(self, q, kv, indices, sm_scale: float = 0.0, out=None, lse=None) -> mla_decode_args:
+        out = self.out if out is None else out
+        lse = self.lse if lse is None else lse
+        if self.shape.kv_format == MLA_KV_FP8_656:
+            kv_stride = kv.stride(0) * kv.element_size()
+        else:
+            kv_stride = kv.stride(0) * kv.element_size()
+        a = mla_decode_args()
+        a.shape = self.shape
+        a.sm_scale = sm_scale
+        a.q = q.data_ptr()
+        a.q_stride_b, a.q_stride_s, a.q_stride_h = q.stride(0), q.stride(1), q.stride(2)
+        a.kv = kv.data_ptr()
+        a.kv_stride_block = kv_stride
+        a.indices = indices.data_ptr()
+        a.idx_stride_b, a.idx_stride_s = indices.stride(0), indices.stride(1)
+        a.out = out.data_ptr()
+        a.out_stride_b, a.out_stride_s, a.out_stride_h = out.stride(0), out.stride(1), out.stride(2)
+        a.lse = lse.data_ptr()
+        a.attn_sink = None
+        a.topk_length = None
+        a.sched_meta = self.sched_meta.data_ptr()
+        a.num_splits = self.num_splits.data_ptr()
+        a.o_accum = self.o_accum.data_ptr()
+        a.lse_accum = self.lse_accum.data_ptr()
+        a.o_accum_bytes = self.o_accum.numel() * 4
+        a.lse_accum_bytes = self.lse_accum.numel() * 4
+        return a
+
+    def run(self, q, kv, indices, sm_scale: float = 0.0, stream=None, with_sched: bool = True):
+        """sched (optional) -> decode -> combine, all on `stream`."""
+        if with_sched:
+            self.get_sched_meta(stream)
+        a = self.args(q, kv, indices, sm_scale)
+        mla_sparse_decode_fwd(a, stream)
+        mla_splitkv_combine(a, stream)
+        return self.out, self.lse

@@ -1,0 +1,263 @@
+// Host side of libmla: argument validation, default resolution, scheduler
+// export and kernel launches behind the C ABI declared in include/mla.h.
+// Validation happens before anything touches the device, so every error path
+// can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "mla.h"
+#include "mla_internal.h"
+#include "sched_plan.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return MLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validate `in` and fill `out` with every default resolved.
+int resolve(const mla_shape* in, mla::ResolvedShape* out) {
+    if (!in) return fail(MLA_ERR_INVALID_ARG, "shape is NULL");
+    const mla_shape& s = *in;
+    if (s.b < 1) return fail(MLA_ERR_INVALID_ARG, "b must be >= 1 (got %d)", s.b);
+    if (s.s_q < 1) return fail(MLA_ERR_INVALID_ARG, "s_q must be >= 1 (got %d)", s.s_q);
+    if (s.topk < 1) return fail(MLA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", s.topk);
+    if (s.h_q < 1) return fail(MLA_ERR_INVALID_ARG, "h_q must be >= 1 (got %d)", s.h_q);
+    if (s.h_q != 64 && s.h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "h_q must be 64 or 128 (got %d)", s.h_q);
+    if (s.h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv must be 1 (got %d)", s.h_kv);
+    if (s.d_qk != 576) return fail(MLA_ERR_UNSUPPORTED, "d_qk must be 576 (got %d)", s.d_qk);
+    if (s.d_v != 512) return fail(MLA_ERR_UNSUPPORTED, "d_v must be 512 (got %d)", s.d_v);
+    if (s.kv_format != MLA_KV_FP8_656 && s.kv_format != MLA_KV_BF16_576)
+        return fail(MLA_ERR_INVALID_ARG, "unknown kv_format %d", s.kv_format);
+    if (s.num_kv_tokens < 1 || s.num_kv_tokens > INT32_MAX)
+        return fail(MLA_ERR_INVALID_ARG, "num_kv_tokens must be in [1, 2^31) (got %lld)",
+                    (long long)s.num_kv_tokens);
+    int P = 1;
+    if (s.kv_format == MLA_KV_FP8_656) {
+        P = s.page_block_size;
+        if (P < 1) return fail(MLA_ERR_INVALID_ARG, "page_block_size must be >= 1 (got %d)", P);
+        if (s.num_kv_tokens % P != 0)
+            return fail(MLA_ERR_INVALID_ARG, "num_kv_tokens (%lld) is not a multiple of page_block_size (%d)",
+                        (long long)s.num_kv_tokens, P);
+    }
+    int block = s.split_granularity == 0 ? 64 : s.split_granularity;
+    if (block < 32 || block % 32 != 0)
+        return fail(MLA_ERR_INVALID_ARG, "split_granularity must be a positive multiple of 32 (got %d)",
+                    s.split_granularity);
+    int overhead = s.fixed_overhead < 0 ? 5 : s.fixed_overhead;
+    if (overhead > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "fixed_overhead too large (%d)", overhead);
+    int parts = s.num_parts;
+    if (parts < 0) return fail(MLA_ERR_INVALID_ARG, "num_parts must be >= 0 (got %d)", parts);
+    if (parts == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+            (void)hipGetLastError();
+            return fail(MLA_ERR_NO_DEVICE, "num_parts = 0 needs a device to read its CU count");
+        }
+        const int wgs_per_cu = s.h_q == 128 ? 1 : 2;
+        parts = cus * wgs_per_cu / s.s_q;
+        if (parts < 1) parts = 1;
+    }
+    if (parts > 65535) return fail(MLA_ERR_INVALID_ARG, "num_parts must be <= 65535 (got %d)", parts);
+    out->b = s.b;
+    out->s_q = s.s_q;
+    out->h_q = s.h_q;
+    out->topk = s.topk;
+    out->page_block_size = P;
+    out->kv_format = s.kv_format;
+    out->num_kv_tokens = s.num_kv_tokens;
+    out->num_parts = parts;
+    out->block = block;
+    out->overhead = overhead;
+    return MLA_OK;
+}
+
+void workspace_bytes(const mla::ResolvedShape& r, size_t* o, size_t* l) {
+    const size_t rows = (size_t)(r.b + r.num_parts) * r.s_q * r.h_q;
+    if (o) *o = rows * 512 * sizeof(float);
+    if (l) *l = rows * sizeof(float);
+}
+
+int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::DecodeParams* p) {
+    if (!a) return fail(MLA_ERR_INVALID_ARG, "args is NULL");
+    int st = resolve(&a->shape, rs);
+    if (st != MLA_OK) return st;
+    const mla::ResolvedShape& r = *rs;
+    if (!a->q || !a->kv || !a->indices || !a->out || !a->lse)
+        return fail(MLA_ERR_INVALID_ARG, "q, kv, indices, out and lse must be non-NULL");
+    if (!a->sched_meta || !a->num_splits)
+        return fail(MLA_ERR_INVALID_ARG, "sched_meta and num_splits must be non-NULL (mla_get_sched_meta)");
+    if (a->attn_sink) return fail(MLA_ERR_UNSUPPORTED, "attn_sink is not supported by this build");
+    if (a->topk_length) return fail(MLA_ERR_UNSUPPORTED, "topk_length is not supported by this build");
+    if (!aligned(a->q, 16) || a->q_stride_h % 8 || a->q_stride_s % 8 || a->q_stride_b % 8)
+        return fail(MLA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
+    if (a->q_stride_h < 576 && r.h_q > 1)
+        return fail(MLA_ERR_INVALID_ARG, "q_stride_h (%lld) < 576", (long long)a->q_stride_h);
+    if (!aligned(a->kv, 16) || a->kv_stride_block % 16)
+        return fail(MLA_ERR_INVALID_ARG, "kv must be 16-byte aligned and kv_stride_block a multiple of 16");
+    if (r.kv_format == MLA_KV_FP8_656 && a->kv_stride_block < (int64_t)r.page_block_size * 656)
+        return fail(MLA_ERR_INVALID_ARG, "kv_stride_block (%lld) < page_block_size * 656",
+                    (long long)a->kv_stride_block);
+    if (r.kv_format == MLA_KV_BF16_576 && a->kv_stride_block < 1152)
+        return fail(MLA_ERR_INVALID_ARG, "kv_stride_block (%lld) < 1152 bytes per bf16 row",
+                    (long long)a->kv_stride_block);
+    if (!aligned(a->indices, 4)) return fail(MLA_ERR_INVALID_ARG, "indices must be 4-byte aligned");
+    if (!aligned(a->out, 16) || a->out_stride_h % 8 || a->out_stride_s % 8 || a->out_stride_b % 8)
+        return fail(MLA_ERR_INVALID_ARG, "out must be 16-byte aligned with strides that are multiples of 8 elements");
+    if (!aligned(a->lse, 4)) return fail(MLA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (!aligned(a->sched_meta, 4) || !aligned(a->num_splits, 4))
+        return fail(MLA_ERR_INVALID_ARG, "sched_meta / num_splits must be 4-byte aligned");
+    size_t need_o = 0, need_l = 0;
+    workspace_bytes(r, &need_o, &need_l);
+    if (!a->o_accum || !a->lse_accum || a->o_accum_bytes < need_o || a->lse_accum_bytes < need_l)
+        return fail(MLA_ERR_WORKSPACE, "workspace too small: need o_accum %zu and lse_accum %zu bytes", need_o,
+                    need_l);
+    if (!aligned(a->o_accum, 16) || !aligned(a->lse_accum, 4))
+        return fail(MLA_ERR_INVALID_ARG, "o_accum must be 16-byte aligned, lse_accum 4-byte aligned");
+    float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(576.0f);
+    if (!std::isfinite(sm)) return fail(MLA_ERR_INVALID_ARG, "sm_scale must be finite");
+
+    p->q = static_cast<const uint16_t*>(a->q);
+    p->q_sb = a->q_stride_b;
+    p->q_ss = a->q_stride_s;
+    p->q_sh = a->q_stride_h;
+    p->kv = static_cast<const uint8_t*>(a->kv);
+    p->kv_block_stride = a->kv_stride_block;
+    p->indices = a->indices;
+    p->idx_sb = a->idx_stride_b;
+    p->idx_ss = a->idx_stride_s;
+    p->out = static_cast<uint16_t*>(a->out);
+    p->out_sb = a->out_stride_b;
+    p->out_ss = a->out_stride_s;
+    p->out_sh = a->out_stride_h;
+    p->lse = a->lse;
+    p->sched_meta = static_cast<const int32_t*>(a->sched_meta);
+    p->num_splits = a->num_splits;
+    p->o_accum = a->o_accum;
+    p->lse_accum = a->lse_accum;
+    p->n_tok = r.num_kv_tokens;
+    p->b = r.b;
+    p->s_q = r.s_q;
+    p->h_q = r.h_q;
+    p->topk = r.topk;
+    p->page_block_size = r.page_block_size;
+    p->block = r.block;
+    p->c = sm * 1.4426950408889634f;
+    p->threshold = mla::kRefGapLog2;
+    return MLA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_resolve_shape(mla_shape* shape) {
+    mla::ResolvedShape r;
+    int st = resolve(shape, &r);
+    if (st != MLA_OK) return st;
+    shape->num_parts = r.num_parts;
+    shape->split_granularity = r.block;
+    shape->fixed_overhead = r.overhead;
+    if (shape->kv_format == MLA_KV_BF16_576) shape->page_block_size = 1;
+    return ok();
+}
+
+int mla_sched_meta_size(const mla_shape* shape, size_t* meta_bytes, size_t* num_splits_bytes) {
+    mla::ResolvedShape r;
+    int st = resolve(shape, &r);
+    if (st != MLA_OK) return st;
+    if (meta_bytes) *meta_bytes = (size_t)r.num_parts * sizeof(mla_sched_part);
+    if (num_splits_bytes) *num_splits_bytes = (size_t)(r.b + 1) * sizeof(int32_t);
+    return ok();
+}
+
+int mla_workspace_size(const mla_shape* shape, size_t* o_accum_bytes, size_t* lse_accum_bytes) {
+    mla::ResolvedShape r;
+    int st = resolve(shape, &r);
+    if (st != MLA_OK) return st;
+    workspace_bytes(r, o_accum_bytes, lse_accum_bytes);
+    return ok();
+}
+
+int mla_plan_sched_meta_host(const mla_shape* shape, void* sched_meta_host, int32_t* num_splits_host) {
+    mla::ResolvedShape r;
+    int st = resolve(shape, &r);
+    if (st != MLA_OK) return st;
+    if (!sched_meta_host || !num_splits_host)
+        return fail(MLA_ERR_INVALID_ARG, "sched_meta_host and num_splits_host must be non-NULL");
+    mla::plan_schedule(r.b, r.topk, r.block, r.overhead, r.num_parts,
+                       static_cast<int32_t*>(sched_meta_host), num_splits_host,
+                       [](int32_t* p, int32_t v) { *p = v; });
+    return ok();
+}
+
+int mla_get_sched_meta(const mla_shape* shape, void* sched_meta_dev, int32_t* num_splits_dev, void* stream) {
+    mla::ResolvedShape r;
+    int st = resolve(shape, &r);
+    if (st != MLA_OK) return st;
+    if (!sched_meta_dev || !num_splits_dev)
+        return fail(MLA_ERR_INVALID_ARG, "sched_meta_dev and num_splits_dev must be non-NULL");
+    if (!aligned(sched_meta_dev, 4) || !aligned(num_splits_dev, 4))
+        return fail(MLA_ERR_INVALID_ARG, "sched buffers must be 4-byte aligned");
+    return hip_status(mla::launch_sched(r, static_cast<int32_t*>(sched_meta_dev), num_splits_dev,
+                                        static_cast<hipStream_t>(stream)),
+                      "sched kernel launch");
+}
+
+int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream) {
+    mla::ResolvedShape r;
+    mla::DecodeParams p;
+    int st = check_decode_args(args, &r, &p);
+    if (st != MLA_OK) return st;
+    return hip_status(mla::launch_decode(p, r.kv_format, r.num_parts, static_cast<hipStream_t>(stream)),
+                      "decode kernel launch");
+}
+
+int mla_splitkv_combine(const mla_decode_args* args, void* stream) {
+    mla::ResolvedShape r;
+    mla::DecodeParams p;
+    int st = check_decode_args(args, &r, &p);
+    if (st != MLA_OK) return st;
+    return hip_status(mla::launch_combine(p, static_cast<hipStream_t>(stream)), "combine kernel launch");
+}
+
+int mla_debug_gather_dequant(const mla_decode_args* args, void* k_rows, void* v_rows, void* stream) {
+    mla::ResolvedShape r;
+    mla::DecodeParams p;
+    int st = check_decode_args(args, &r, &p);
+    if (st != MLA_OK) return st;
+    if (!k_rows || !aligned(k_rows, 16) || (v_rows && !aligned(v_rows, 2)))
+        return fail(MLA_ERR_INVALID_ARG, "k_rows must be non-NULL and 16-byte aligned");
+    return hip_status(mla::launch_gather(p, r.kv_format, static_cast<uint16_t*>(k_rows),
+                                         static_cast<uint16_t*>(v_rows), static_cast<hipStream_t>(stream)),
+                      "gather kernel launch");
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+const char* mla_version(void) { return "libmla 0.1 gfx950"; }
+
+}  // extern "C"

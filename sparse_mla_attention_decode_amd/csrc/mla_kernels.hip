@@ -1,0 +1,565 @@
+// gfx950 kernels for sparse MLA decode: scheduler, decode, split-KV combine
+// and a gather/dequant test hook.
+//
+// Decode work-group = NW waves of 64 lanes; wave w owns query heads
+// [32w, 32w+32).  Each wave keeps Q for its heads in VGPRs (the B operand of
+// the score contraction) and the transposed output accumulator O^T [512 x 32]
+// in AGPRs.  The work-group walks its topk slots in tiles of 32 keys:
+//
+//   1. gather: the tile's token rows (656 B FP8 or 1152 B bf16) are copied
+//      HBM -> LDS by direct-to-LDS loads (16 B per lane, no registers), one
+//      tile ahead of the compute; empty slots are skipped;
+//   2. stage: rows are dequantised to bf16 (code * power-of-two scale, exact)
+//      into K rows [32 keys][576] in LDS; empty slots become zero rows;
+//   3. S^T[key][head] = K Q^T: 36 MFMA 32x32x16 bf16 per wave;
+//   4. softmax in base 2 on the accumulator, masked by slot validity; every
+//      lane holds 16 keys of one head so the row max needs one exchange;
+//   5. O^T[dim][head] += V^T P^T: 32 MFMA per wave; P comes straight from
+//      the score accumulator (its layout is the B layout) and V^T fragments
+//      are read from the K rows with the LDS transpose read.
+//
+// The reference max of a piece is the max score of its first tile holding a
+// valid key; later tiles are accumulated against it as long as no score
+// exceeds it by more than 2^64 (so p <= 2^64 and all sums stay finite in
+// fp32).  If one does, the piece is recomputed with the larger reference --
+// equal to the exact online-softmax result, without rescaling O in place.
+//
+// Sources: "FlashMLA Sparse Decode 完整计算过程详解" steps 3 (scheduler), 7
+// (index load, address, dequant), 8-11 (contractions, base-2 softmax with
+// c = sm_scale*log2(e)), 12 and 14 (epilogue: out = O/l, lse = ln l + m/log2(e),
+// +inf when l = 0; split partials O/l in fp32 and lse = log2 l + m, -inf when
+// l = 0) and 16 (combine).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+#include "sched_plan.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int TILE = 32;                   // keys per tile
+constexpr int KROW = 1168;                 // LDS bytes per staged bf16 K row (1152 + 16 pad)
+constexpr int KB_BYTES = TILE * KROW;      // 37376
+
+// Per-format constants of the raw token row.
+template <int FMT> struct RowFmt;
+template <> struct RowFmt<MLA_KV_FP8_656> {
+    static constexpr int ROWB = 656, ROPE_OFF = 528;
+};
+template <> struct RowFmt<MLA_KV_BF16_576> {
+    static constexpr int ROWB = 1152, ROPE_OFF = 1024;
+};
+
+// LDS map: [raw tile][staged K rows][2 validity masks][4 restart flags]
+template <int FMT> struct Lds {
+    static constexpr int RAW = 0;
+    static constexpr int RAW_BYTES = TILE * RowFmt<FMT>::ROWB;
+    static constexpr int KB = RAW + RAW_BYTES;
+    static constexpr int MASK = KB + KB_BYTES;
+    static constexpr int FLAGS = MASK + 8;
+    static constexpr int BYTES = FLAGS + 8;
+    static constexpr int CHUNKS = RAW_BYTES / 16;              // 16-byte DMA units per tile
+    static constexpr int CPR = RowFmt<FMT>::ROWB / 16;         // chunks per row
+    static_assert(RAW_BYTES % 1024 == 0 || true, "");
+};
+
+constexpr float INIT_MAX = -1e30f;
+
+// ----------------------------------------------------------------------------
+// small helpers
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 lds_read16(const LDS_AS uint8_t* base, int off) {
+    return *(const LDS_AS u32x4*)(base + off);
+}
+__device__ __forceinline__ void lds_write16(LDS_AS uint8_t* base, int off, u32x4 v) {
+    *(LDS_AS u32x4*)(base + off) = v;
+}
+
+// Transposing LDS read: in each group of 16 lanes, lane 4b+c receives column c
+// (16-bit) of the 8-byte rows addressed by lanes b, b+4, b+8, b+12.
+__device__ __forceinline__ u32x2 lds_read_tr16(const LDS_AS uint8_t* base, int off) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + off));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// two e4m3fn codes (bytes 2*HI, 2*HI+1 of w) times a power-of-two scale -> two
+// bf16 packed in a dword; the product is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t dequant2(uint32_t w, float scale) {
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    bf16x2 r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// MFMA helpers with explicit register classes.  At occupancy 1 a wave owns
+// 256 VGPRs + 256 AGPRs: the output accumulator takes all AGPRs, Q (144),
+// the score accumulator and everything else live in VGPRs.  Without the
+// constraints the compiler puts every accumulator in AGPRs and spills.
+__device__ __forceinline__ void mfma_qk_first(f32x16& s, const bf16x8& a, const bf16x8& q) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(q));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& s, const bf16x8& a, const bf16x8& q) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(q));
+}
+__device__ __forceinline__ void mfma_pv(f32x16& o, const bf16x8& a, const bf16x8& pm) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(pm));
+}
+// The hazard recognizer does not look inside inline asm.  These fences wait
+// out the MFMA result latency before VALU reads an accumulator, and the VALU
+// write -> MFMA operand read latency before freshly computed P is consumed.
+__device__ __forceinline__ void mfma_result_fence(f32x16& s) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s));
+}
+__device__ __forceinline__ void valu_to_mfma_fence(bf16x8& a, bf16x8& b) {
+    asm volatile("s_nop 4" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ----------------------------------------------------------------------------
+// scheduler kernel: one wave; the plan is sequential, lane 0 runs it and writes
+// through ordinary (vector) global stores.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) sched_kernel(int b, int topk, int block, int overhead,
+                                                   int num_parts, int32_t* meta, int32_t* prefix) {
+    if (threadIdx.x != 0) return;
+    plan_schedule(b, topk, block, overhead, num_parts, meta, prefix,
+                  [](int32_t* p, int32_t v) { *(volatile int32_t*)p = v; });
+}
+
+// ----------------------------------------------------------------------------
+// decode
+// ----------------------------------------------------------------------------
+// Address of token t (bytes) or nullptr when the slot is empty.
+template <int FMT>
+__device__ __forceinline__ const uint8_t* row_ptr(const DecodeParams& p, int t) {
+    if (t < 0 || (int64_t)t >= p.n_tok) return nullptr;
+    if (FMT == MLA_KV_FP8_656) {
+        const int64_t blk = t / p.page_block_size;
+        const int64_t off = t - blk * p.page_block_size;
+        return p.kv + blk * p.kv_block_stride + off * 656;
+    }
+    return p.kv + (int64_t)t * p.kv_block_stride;
+}
+
+// Gather: start the HBM -> LDS copy of the rows of slots [k0, k0 + 32) (those
+// below k_end and valid) into the raw tile, and record the validity mask of
+// the tile in mask slot `ms`.  Every wave resolves the 32 row addresses with
+// lanes 0..31 and copies its share of the 16-byte chunks.
+template <int FMT, int NW>
+__device__ __forceinline__ void gather_tile(const DecodeParams& p, const int32_t* idx, int k0,
+                                            int k_end, LDS_AS uint8_t* lds, int ms) {
+    using L = Lds<FMT>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int key = k0 + (lane & 31);
+    const int t = (lane < 32 && key < k_end) ? idx[key] : -1;
+    const uint8_t* rp = row_ptr<FMT>(p, t);
+    const uint64_t valid = __ballot(rp != nullptr);
+    if (threadIdx.x == 0) *(LDS_AS uint32_t*)(lds + L::MASK + 4 * ms) = (uint32_t)valid;
+    const uint64_t addr = (uint64_t)(uintptr_t)(rp ? rp : p.kv);
+    const uint32_t a_lo = (uint32_t)addr, a_hi = (uint32_t)(addr >> 32);
+    constexpr int NINST = (L::CHUNKS + 63) / 64;
+#pragma unroll
+    for (int j = wave; j < NINST; j += NW) {
+        const int f = 64 * j + lane;
+        const int row = f / L::CPR;
+        const int chunk = f - row * L::CPR;
+        const uint32_t lo = __shfl(a_lo, row & 31), hi = __shfl(a_hi, row & 31);
+        const bool act = f < L::CHUNKS && ((valid >> (row & 31)) & 1u);
+        const uint8_t* g = (const uint8_t*)(((uint64_t)hi << 32) | lo) + 16 * chunk;
+        if (act) __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)(lds + L::RAW + 1024 * j), 16, 0, 0);
+    }
+}
+
+// Stage: raw rows -> bf16 K rows (dequantised NoPE, copied RoPE); empty slots
+// become zero rows.
+template <int FMT, int NW>
+__device__ __forceinline__ void stage_tile(LDS_AS uint8_t* lds, uint32_t valid) {
+    using L = Lds<FMT>;
+    constexpr int NT = NW * 64;
+    constexpr int ROWB = RowFmt<FMT>::ROWB;
+    const u32x4 zero = {0, 0, 0, 0};
+    if (FMT == MLA_KV_FP8_656) {
+        // NoPE: (row, 16-code chunk) units, 32 x 32
+#pragma unroll
+        for (int u = threadIdx.x; u < 32 * 32; u += NT) {
+            const int row = u >> 5, c = u & 31;
+            u32x4 lo = zero, hi = zero;
+            if ((valid >> row) & 1u) {
+                const u32x4 raw = lds_read16(lds, L::RAW + row * ROWB + 16 * c);
+                const float sc = *(const LDS_AS float*)(lds + L::RAW + row * ROWB + 512 + 4 * (c >> 3));
+                lo = u32x4{dequant2<false>(raw[0], sc), dequant2<true>(raw[0], sc),
+                           dequant2<false>(raw[1], sc), dequant2<true>(raw[1], sc)};
+                hi = u32x4{dequant2<false>(raw[2], sc), dequant2<true>(raw[2], sc),
+                           dequant2<false>(raw[3], sc), dequant2<true>(raw[3], sc)};
+            }
+            lds_write16(lds, L::KB + row * KROW + 32 * c, lo);
+            lds_write16(lds, L::KB + row * KROW + 32 * c + 16, hi);
+        }
+    } else {
+        // NoPE: (row, 8-value chunk) units, 32 x 64, plain copy
+#pragma unroll
+        for (int u = threadIdx.x; u < 32 * 64; u += NT) {
+            const int row = u >> 6, c = u & 63;
+            const u32x4 v = ((valid >> row) & 1u) ? lds_read16(lds, L::RAW + row * ROWB + 16 * c) : zero;
+            lds_write16(lds, L::KB + row * KROW + 16 * c, v);
+        }
+    }
+    // RoPE: (row, 8-value chunk) units, 32 x 8, plain copy
+    for (int u = threadIdx.x; u < 32 * 8; u += NT) {
+        const int row = u >> 3, c = u & 7;
+        const u32x4 v = ((valid >> row) & 1u)
+                            ? lds_read16(lds, L::RAW + row * ROWB + RowFmt<FMT>::ROPE_OFF + 16 * c)
+                            : zero;
+        lds_write16(lds, L::KB + row * KROW + 1024 + 16 * c, v);
+    }
+}
+
+// Byte offset (relative to the staged K rows) of this lane's transposing read
+// for the value contraction: output block mb (dims 32mb..32mb+31), k-step t,
+// half `second` (keys +8).  Lane l feeds the 8-byte row of key
+// 16t + 4(l/32) + (l%16)/4 (+8) at dims 32mb + 16((l/16)%2) + 4(l%4); the
+// transpose hands lane l dim 32mb + l%32 of keys 16t + 4(l/32) + 0..3 (+8),
+// which is the key order the score accumulator gives P.
+__device__ __forceinline__ int pv_read_base(int lane) {
+    const int key = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    return key * KROW + 2 * dim;
+}
+
+template <int FMT, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
+    using L = Lds<FMT>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
+
+    const int part = blockIdx.x, sq = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int head = 32 * wave + n;
+
+    const int32_t* meta = p.sched_meta + 8 * part;
+    const int begin_req = meta[0];
+    if (begin_req >= p.b) return;
+    const int end_req = meta[1], begin_block = meta[2], end_block = meta[3];
+    const int begin_split = meta[4];
+    const int nblocks = (p.topk + p.block - 1) / p.block;
+    const int qk_base = n * KROW + 16 * h;          // score operand: key n, dims 16j + 8h
+    const int pv_base = pv_read_base(lane);
+    if (threadIdx.x < 4) lds[L::FLAGS + threadIdx.x] = 0;   // ordered by the first barrier
+
+    for (int req = begin_req; req <= end_req; ++req) {
+        const int blk_lo = req == begin_req ? begin_block : 0;
+        const int blk_hi = req == end_req ? end_block : nblocks;
+        const int k_lo = blk_lo * p.block;
+        const int k_hi = min(blk_hi * p.block, p.topk);
+        const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
+        const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+
+        // Q for this wave's heads as B operands: k-step j covers dims
+        // 16j + 8h .. 16j + 8h + 7, matching the K row reads
+        bf16x8 qb[36];
+        {
+            const uint16_t* qrow = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss +
+                                   (int64_t)head * p.q_sh;
+#pragma unroll
+            for (int j = 0; j < 36; ++j)
+                qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * j + 8 * h));
+        }
+
+        f32x16 O[16];
+        float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
+        for (int pass = 0;; ++pass) {
+#pragma unroll
+            for (int mb = 0; mb < 16; ++mb) O[mb] = f32x16{};
+            l_part = 0.f;
+            __syncthreads();                        // LDS free (previous piece / pass done)
+            if (n_tiles > 0) gather_tile<FMT, NW>(p, idx, k_lo, k_hi, lds, 0);
+
+            for (int it = 0; it < n_tiles; ++it) {
+                const int k0 = k_lo + it * TILE;
+                __builtin_amdgcn_s_waitcnt(0);      // this wave's tile copies have landed
+                __syncthreads();                    // ... and every wave's; tile it-1 consumed
+                const uint32_t vmask = *(const LDS_AS uint32_t*)(lds + L::MASK + 4 * (it & 1));
+                stage_tile<FMT, NW>(lds, vmask);
+                __syncthreads();                    // staged rows visible, raw tile free
+                if (it + 1 < n_tiles) gather_tile<FMT, NW>(p, idx, k0 + TILE, k_hi, lds, (it + 1) & 1);
+
+                // ---- S^T = K Q^T
+                f32x16 S;
+#pragma unroll
+                for (int j = 0; j < 36; ++j) {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(lds, L::KB + qk_base + 32 * j));
+                    if (j == 0) mfma_qk_first(S, a, qb[j]);
+                    else mfma_qk(S, a, qb[j]);
+                }
+                mfma_result_fence(S);
+
+                // ---- masked softmax in base 2 against the reference max
+                float mx = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = 8 * (v >> 2) + 4 * h + (v & 3);
+                    S[v] = ((vmask >> key) & 1u) ? S[v] : -INFINITY;
+                    mx = fmaxf(mx, S[v]);
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mnew = mx * p.c;
+                m_seen = fmaxf(m_seen, mnew);
+                if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                if (__any(mnew > m_ref + p.threshold) && lane == 0) lds[L::FLAGS + wave] = 1;
+
+                float psum = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
+                    psum += S[v];
+                }
+                l_part += psum;
+                bf16x8 pb[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    u32x4 w = {pack_bf16(S[8 * t + 0], S[8 * t + 1]), pack_bf16(S[8 * t + 2], S[8 * t + 3]),
+                               pack_bf16(S[8 * t + 4], S[8 * t + 5]), pack_bf16(S[8 * t + 6], S[8 * t + 7])};
+                    pb[t] = __builtin_bit_cast(bf16x8, w);
+                }
+
+                // ---- O^T += V^T P^T
+                valu_to_mfma_fence(pb[0], pb[1]);
+#pragma unroll
+                for (int mb = 0; mb < 16; ++mb) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int off = L::KB + pv_base + t * 16 * KROW + mb * 64;
+                        const u32x2 r0 = lds_read_tr16(lds, off);
+                        const u32x2 r1 = lds_read_tr16(lds, off + 8 * KROW);
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
+                        mfma_pv(O[mb], a, pb[t]);
+                    }
+                }
+            }
+            // A score exceeded the reference by more than 2^threshold in some
+            // wave: recompute the piece against the true max (rare).
+            __syncthreads();
+            const uint32_t flags = *(const LDS_AS uint32_t*)(lds + L::FLAGS);
+            __syncthreads();
+            if (flags == 0u || pass > 0) break;         // the second pass uses the true max
+            if (threadIdx.x < 4) lds[L::FLAGS + threadIdx.x] = 0;
+            m_ref = m_seen;
+        }
+
+        // ---- epilogue
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[mb]));
+        const float l_tot = l_part + __shfl_xor(l_part, 32);
+        const int nsplit = p.num_splits[req + 1] - p.num_splits[req];
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        if (nsplit == 1) {
+            uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss +
+                             (int64_t)head * p.out_sh;
+#pragma unroll
+            for (int mb = 0; mb < 16; ++mb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = 32 * mb + 8 * g + 4 * h;
+                    u32x2 w = {pack_bf16(O[mb][4 * g] * inv, O[mb][4 * g + 1] * inv),
+                               pack_bf16(O[mb][4 * g + 2] * inv, O[mb][4 * g + 3] * inv)};
+                    *(u32x2*)(orow + d) = w;
+                }
+            }
+            if (h == 0)
+                p.lse[((int64_t)req * p.h_q + head) * p.s_q + sq] =
+                    l_tot > 0.f ? (__log2f(l_tot) + m_ref) * 0.69314718055994531f : INFINITY;
+        } else {
+            const int split = req == begin_req ? begin_split : p.num_splits[req];
+            const int64_t base = ((int64_t)split * p.s_q + sq) * p.h_q + head;
+            float* orow = p.o_accum + base * 512;
+#pragma unroll
+            for (int mb = 0; mb < 16; ++mb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d = 32 * mb + 8 * g + 4 * h;
+                    *(f32x4*)(orow + d) = f32x4{O[mb][4 * g] * inv, O[mb][4 * g + 1] * inv,
+                                                O[mb][4 * g + 2] * inv, O[mb][4 * g + 3] * inv};
+                }
+            }
+            if (h == 0) p.lse_accum[base] = l_tot > 0.f ? __log2f(l_tot) + m_ref : -INFINITY;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// gather/dequant test hook: gathers and stages every tile exactly as decode
+// does and reads the staged rows back through the decode kernel's two operand
+// read paths (row reads for K, transposing reads for V).
+// ----------------------------------------------------------------------------
+template <int FMT, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) gather_kernel(DecodeParams p, uint16_t* k_rows,
+                                                            uint16_t* v_rows) {
+    using L = Lds<FMT>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
+    const int qi = blockIdx.x;                    // query token = req * s_q + sq
+    const int req = qi / p.s_q, sq = qi % p.s_q;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+    const int n_tiles = (p.topk + TILE - 1) / TILE;
+    for (int it = 0; it < n_tiles; ++it) {
+        const int k0 = it * TILE;
+        __syncthreads();
+        gather_tile<FMT, NW>(p, idx, k0, p.topk, lds, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        stage_tile<FMT, NW>(lds, *(const LDS_AS uint32_t*)(lds + L::MASK));
+        __syncthreads();
+        if (wave == 0) {
+            const int key = k0 + n;
+            if (key < p.topk) {
+                uint16_t* dst = k_rows + ((int64_t)qi * p.topk + key) * 576;
+                for (int j = 0; j < 36; ++j)
+                    *(u32x4*)(dst + 16 * j + 8 * h) = lds_read16(lds, L::KB + n * KROW + 16 * h + 32 * j);
+            }
+        }
+        if (v_rows != nullptr && wave == NW - 1) {
+            const int pv_base = pv_read_base(lane);
+            for (int mb = 0; mb < 16; ++mb) {
+                for (int t = 0; t < 2; ++t) {
+                    const int off = L::KB + pv_base + t * 16 * KROW + mb * 64;
+                    const u32x2 r0 = lds_read_tr16(lds, off);
+                    const u32x2 r1 = lds_read_tr16(lds, off + 8 * KROW);
+                    const uint32_t d[4] = {r0[0], r0[1], r1[0], r1[1]};
+                    for (int e = 0; e < 8; ++e) {
+                        const int key = k0 + 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if (key < p.topk) {
+                            const uint16_t val = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
+                            v_rows[((int64_t)qi * p.topk + key) * 512 + 32 * mb + n] = val;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// combine: one wave per (query token, head); lanes own 8 output dims each.
+// ----------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
+    const int qi = blockIdx.x;
+    const int req = qi / p.s_q, sq = qi % p.s_q;
+    const int lane = threadIdx.x & 63;
+    const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (head >= p.h_q) return;
+    const int first = p.num_splits[req];
+    const int ns = p.num_splits[req + 1] - first;
+    if (ns <= 1) return;
+    auto lse_at = [&](int j) {
+        return p.lse_accum[((int64_t)(first + j) * p.s_q + sq) * p.h_q + head];
+    };
+    float mx = -INFINITY;
+    for (int j = lane; j < ns; j += 64) mx = fmaxf(mx, lse_at(j));
+    mx = wave_max(mx);
+    uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh;
+    float* lse_out = p.lse + ((int64_t)req * p.h_q + head) * p.s_q + sq;
+    if (mx == -INFINITY) {
+        *(u32x4*)(orow + 8 * lane) = u32x4{0, 0, 0, 0};
+        if (lane == 0) *lse_out = INFINITY;
+        return;
+    }
+    float tot = 0.f;
+    for (int j = lane; j < ns; j += 64) tot += __builtin_amdgcn_exp2f(lse_at(j) - mx);
+    tot = wave_sum(tot);
+    const float inv = 1.0f / tot;
+    f32x4 a0 = {}, a1 = {};
+    for (int j = 0; j < ns; ++j) {
+        const float w = __builtin_amdgcn_exp2f(lse_at(j) - mx) * inv;
+        const float* src = p.o_accum + (((int64_t)(first + j) * p.s_q + sq) * p.h_q + head) * 512 + 8 * lane;
+        a0 += w * *(const f32x4*)src;
+        a1 += w * *(const f32x4*)(src + 4);
+    }
+    *(u32x4*)(orow + 8 * lane) = u32x4{pack_bf16(a0[0], a0[1]), pack_bf16(a0[2], a0[3]),
+                                       pack_bf16(a1[0], a1[1]), pack_bf16(a1[2], a1[3])};
+    if (lane == 0) *lse_out = (mx + __log2f(tot)) * 0.69314718055994531f;
+}
+
+
+// ----------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------
+hipError_t launch_sched(const ResolvedShape& s, int32_t* meta, int32_t* prefix, hipStream_t st) {
+    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(64), 0, st, s.b, s.topk, s.block, s.overhead,
+                       s.num_parts, meta, prefix);
+    return hipGetLastError();
+}
+
+template <typename K>
+static hipError_t allow_lds(K k, int bytes, bool& done) {
+    if (done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
+template <int FMT, int NW>
+static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, hipStream_t st) {
+    auto k = decode_kernel<FMT, NW>;
+    static bool done = false;
+    hipError_t e = allow_lds(k, Lds<FMT>::BYTES, done);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(num_parts, p.s_q), dim3(NW * 64), Lds<FMT>::BYTES, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
+    if (kv_format == MLA_KV_FP8_656)
+        return p.h_q == 128 ? launch_decode_t<MLA_KV_FP8_656, 4>(p, num_parts, st)
+                            : launch_decode_t<MLA_KV_FP8_656, 2>(p, num_parts, st);
+    return p.h_q == 128 ? launch_decode_t<MLA_KV_BF16_576, 4>(p, num_parts, st)
+                        : launch_decode_t<MLA_KV_BF16_576, 2>(p, num_parts, st);
+}
+
+template <int FMT>
+static hipError_t launch_gather_t(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows,
+                                  hipStream_t st) {
+    auto k = gather_kernel<FMT, 4>;
+    static bool done = false;
+    hipError_t e = allow_lds(k, Lds<FMT>::BYTES, done);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(p.b * p.s_q), dim3(256), Lds<FMT>::BYTES, st, p, k_rows, v_rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows, uint16_t* v_rows,
+                         hipStream_t st) {
+    return kv_format == MLA_KV_FP8_656 ? launch_gather_t<MLA_KV_FP8_656>(p, k_rows, v_rows, st)
+                                       : launch_gather_t<MLA_KV_BF16_576>(p, k_rows, v_rows, st);
+}
+
+hipError_t launch_combine(const DecodeParams& p, hipStream_t st) {
+    hipLaunchKernelGGL(combine_kernel, dim3(p.b * p.s_q, (p.h_q + 3) / 4), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace mla

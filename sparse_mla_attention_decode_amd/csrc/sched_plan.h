@@ -1,0 +1,62 @@
+// Greedy split-KV tile scheduler ("FlashMLA Sparse Decode 完整计算过程详解",
+// step 3): the topk list of each request is cut into blocks of `block`
+// slots; every request costs its block count plus a fixed overhead; the
+// payload of a partition is ceil(total / num_parts) + overhead; partitions are
+// filled left to right and a request that does not fit whole is split, the
+// partition taking (remaining capacity - overhead) of its blocks when that is
+// positive.  One implementation serves the host export and the device kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Writes num_parts records of 8 int32 (begin_req, end_req, begin_block,
+// end_block, begin_split, first_splitted, last_splitted, 0) and the split
+// prefix (b + 1 int32).  `store` is called as store(ptr, value) so the device
+// caller can route writes through vector stores.
+template <typename Store>
+__host__ __device__ inline void plan_schedule(int b, int topk, int block, int overhead,
+                                              int num_parts, int32_t* meta, int32_t* prefix,
+                                              Store store) {
+    const int blocks = (topk + block - 1) / block;          // same for every request
+    const int64_t total = (int64_t)b * (blocks + overhead);
+    const int payload = (int)((total + num_parts - 1) / num_parts) + overhead;
+    int req = 0, done = 0, cursor = 0;
+    store(prefix + 0, 0);
+    for (int p = 0; p < num_parts; ++p) {
+        int32_t* m = meta + 8 * p;
+        if (req >= b) {
+            store(m + 0, b); store(m + 1, b); store(m + 2, 0); store(m + 3, 0);
+            store(m + 4, cursor); store(m + 5, 0); store(m + 6, 0); store(m + 7, 0);
+            continue;
+        }
+        const int begin_req = req, begin_block = done;
+        const int first_splitted = done > 0;
+        int remain = payload;
+        int end_req = req, end_block = done, last_splitted = 0;
+        while (req < b) {
+            const int left = blocks - done;
+            if (left + overhead <= remain) {
+                remain -= left + overhead;
+                end_req = req; end_block = blocks; last_splitted = 0;
+                ++req; done = 0;
+                store(prefix + req, cursor + (req - begin_req));   // splits of requests < req
+            } else {
+                const int take = remain - overhead;
+                if (take > 0) {
+                    done += take;
+                    end_req = req; end_block = done; last_splitted = 1;
+                }
+                break;
+            }
+        }
+        store(m + 0, begin_req); store(m + 1, end_req); store(m + 2, begin_block);
+        store(m + 3, end_block); store(m + 4, cursor); store(m + 5, first_splitted);
+        store(m + 6, last_splitted); store(m + 7, 0);
+        cursor += end_req - begin_req + 1;
+    }
+}
+
+}  // namespace mla

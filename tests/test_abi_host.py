@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/mla.h declares, validates arguments before touching a device, and its
+host scheduler matches the oracle's plan bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_mla_attention_decode_amd as M
+from oracle import mla_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return M.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("mla_get_sched_meta", "mla_sparse_decode_fwd", "mla_splitkv_combine"):
+        assert must in names
+    assert sorted(M.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert "gfx950" in M.mla_version()
+
+
+def shape(**kw):
+    base = dict(b=2, s_q=1, h_q=128, topk=128, num_kv_tokens=512, num_parts=66)
+    base.update(kw)
+    return M.make_shape(**base)
+
+
+def test_struct_layout_matches_header():
+    # mla_shape: 8 int32 + int64 + 4 int32 (with alignment) ; mla_sched_part: 32 bytes
+    assert ctypes.sizeof(M.mla_shape) == 56
+    assert M.mla_shape.num_kv_tokens.offset == 32
+
+
+def test_sizes():
+    s = shape()
+    meta, ns = M.mla_sched_meta_size(s)
+    assert meta == 66 * 32 and ns == 3 * 4
+    o, l = M.mla_workspace_size(s)
+    assert o == (2 + 66) * 1 * 128 * 512 * 4 and l == (2 + 66) * 128 * 4
+    r = M.mla_resolve_shape(s)
+    assert (r.split_granularity, r.fixed_overhead, r.num_parts) == (64, 5, 66)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=0), M.MLA_ERR_INVALID_ARG), (dict(s_q=0), M.MLA_ERR_INVALID_ARG),
+    (dict(topk=0), M.MLA_ERR_INVALID_ARG), (dict(h_q=96), M.MLA_ERR_UNSUPPORTED),
+    (dict(h_q=-1), M.MLA_ERR_INVALID_ARG), (dict(num_kv_tokens=0), M.MLA_ERR_INVALID_ARG),
+    (dict(num_kv_tokens=100), M.MLA_ERR_INVALID_ARG),           # not a multiple of the page size
+    (dict(num_kv_tokens=1 << 31), M.MLA_ERR_INVALID_ARG),
+    (dict(split_granularity=48), M.MLA_ERR_INVALID_ARG), (dict(num_parts=-3), M.MLA_ERR_INVALID_ARG),
+    (dict(page_block_size=0), M.MLA_ERR_INVALID_ARG), (dict(kv_format=7), M.MLA_ERR_INVALID_ARG),
+])
+def test_shape_validation(kw, code):
+    s = shape(**kw)
+    with pytest.raises(M.MlaError) as e:
+        M.mla_sched_meta_size(s)
+    assert e.value.code == code
+    assert M.mla_last_error() != ""
+
+
+def test_model_dims_validated():
+    for field, val in (("h_kv", 2), ("d_qk", 512), ("d_v", 576)):
+        s = shape()
+        setattr(s, field, val)
+        with pytest.raises(M.MlaError) as e:
+            M.mla_workspace_size(s)
+        assert e.value.code == M.MLA_ERR_UNSUPPORTED
+
+
+def _args(s, **over):
+    a = M.mla_decode_args()
+    a.shape = s
+    a.q, a.kv, a.indices, a.out, a.lse = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000
+    a.q_stride_b, a.q_stride_s, a.q_stride_h = 128 * 576, 128 * 576, 576
+    a.kv_stride_block = 64 * 656
+    a.idx_stride_b, a.idx_stride_s = 128, 128
+    a.out_stride_b, a.out_stride_s, a.out_stride_h = 128 * 512, 128 * 512, 512
+    a.sched_meta, a.num_splits = 0x6000, 0x7000
+    o, l = M.mla_workspace_size(s)
+    a.o_accum, a.lse_accum, a.o_accum_bytes, a.lse_accum_bytes = 0x8000, 0x9000, o, l
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), M.MLA_ERR_INVALID_ARG), (dict(kv=None), M.MLA_ERR_INVALID_ARG),
+    (dict(sched_meta=None), M.MLA_ERR_INVALID_ARG),
+    (dict(attn_sink=0xA000), M.MLA_ERR_UNSUPPORTED), (dict(topk_length=0xA000), M.MLA_ERR_UNSUPPORTED),
+    (dict(q=0x1008), M.MLA_ERR_INVALID_ARG), (dict(q_stride_h=580), M.MLA_ERR_INVALID_ARG),
+    (dict(kv_stride_block=64 * 656 - 16), M.MLA_ERR_INVALID_ARG), (dict(kv=0x2004), M.MLA_ERR_INVALID_ARG),
+    (dict(out_stride_h=513), M.MLA_ERR_INVALID_ARG), (dict(o_accum_bytes=16), M.MLA_ERR_WORKSPACE),
+    (dict(lse_accum=None), M.MLA_ERR_WORKSPACE),
+])
+def test_decode_args_validated_before_launch(over, code):
+    s = shape()
+    a = _args(s, **over)
+    for fn in (M.mla_sparse_decode_fwd, M.mla_splitkv_combine):
+        with pytest.raises(M.MlaError) as e:
+            fn(a, stream=0)
+        assert e.value.code == code
+
+
+def _host_plan(s):
+    r = M.mla_resolve_shape(s)
+    meta = np.zeros((r.num_parts, 8), np.int32)
+    ns = np.zeros(r.b + 1, np.int32)
+    M.mla_plan_sched_meta_host(s, meta.ctypes.data, ns.ctypes.data)
+    return r, meta, ns
+
+
+@pytest.mark.parametrize("b,topk,parts,gran,ovh", [
+    (2, 128, 66, 64, 5), (64, 2048, 256, 64, 5), (64, 2048, 256, 32, 5), (64, 2048, 256, 32, 0),
+    (128, 2048, 512, 64, 5), (4, 2048, 128, 32, 0), (1, 4096, 256, 32, 5), (3, 100, 7, 32, 2),
+    (1, 1, 1, 64, 5), (17, 33, 300, 32, 1),
+])
+def test_host_plan_matches_oracle(b, topk, parts, gran, ovh):
+    s = shape(b=b, topk=topk, num_parts=parts, split_granularity=gran, fixed_overhead=ovh)
+    r, meta, ns = _host_plan(s)
+    want, prefix = O.sched_plan([topk] * b, gran, ovh, parts)
+    assert ns.tolist() == prefix
+    assert [tuple(m[:7]) for m in meta.tolist()] == [tuple(w) for w in want]
+
+
+def test_host_plan_reproduces_walkthrough_example():
+    r, meta, ns = _host_plan(shape())
+    assert [tuple(m[:4]) + tuple(m[5:7]) for m in meta[:4].tolist()] == [
+        (0, 0, 0, 1, 0, 1), (0, 0, 1, 2, 1, 0), (1, 1, 0, 1, 0, 1), (1, 1, 1, 2, 1, 0)]
+    assert ns.tolist() == [0, 2, 4]
+    assert (meta[4:, 0] >= 2).all()

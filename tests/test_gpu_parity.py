@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded
+inputs.  Gather/dequant and the scheduler must match bit for bit; decode +
+combine within |dout| <= 1e-2 + 1e-2 |ref| and |dlse| <= 2e-3."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_mla_attention_decode_amd as M
+from oracle import mla_oracle as O
+from sparse_mla_attention_decode_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, LSE_TOL = 1e-2, 1e-2, 2e-3
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _plan(w, **kw):
+    shape = M.make_shape(w.b, w.s_q, w.h_q, w.topk, w.num_kv_tokens, w.kv_format,
+                         w.page_block_size, **kw)
+    return M.DecodePlan(shape)
+
+
+def run_gpu(w, q=None, kv=None, idx=None, **kw):
+    _need_gpu()
+    q = w.q_device() if q is None else q
+    kv = w.kv_device() if kv is None else kv
+    idx = w.indices_device() if idx is None else idx
+    plan = _plan(w, **kw)
+    out, lse = plan.run(q, kv, idx, w.sm_scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy(), plan
+
+
+def oracle(w, queries=None, kv_host=None):
+    kv = w.kv_host() if kv_host is None else kv_host
+    return O.sparse_mla_decode(w.q_bits, kv, w.indices, w.sm_scale, w.kv_format,
+                               w.page_block_size, queries=queries)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, queries, tag=""):
+    worst_o, worst_l = 0.0, 0.0
+    for bi, sj in queries:
+        o, r = out[bi, sj], ref_out[bi, sj]
+        err = np.abs(o - r)
+        bound = ATOL + RTOL * np.abs(r)
+        assert np.all(np.isfinite(o)), (tag, bi, sj)
+        assert np.all(err <= bound), (tag, bi, sj, float((err - bound).max()))
+        worst_o = max(worst_o, float(err.max()))
+        l, lr = lse[bi, :, sj], ref_lse[bi, :, sj]
+        inf = np.isposinf(lr)
+        assert np.array_equal(np.isposinf(l), inf), (tag, bi, sj)
+        if (~inf).any():
+            dl = np.abs(l[~inf] - lr[~inf])
+            assert np.all(dl <= LSE_TOL), (tag, bi, sj, float(dl.max()))
+            worst_l = max(worst_l, float(dl.max()))
+    print(f"[parity {tag}] queries={len(queries)} max|dout|={worst_o:.3e} max|dlse|={worst_l:.3e}", flush=True)
+
+
+def all_queries(w):
+    return [(bi, sj) for bi in range(w.b) for sj in range(w.s_q)]
+
+
+# ----------------------------------------------------------------------------- scheduler
+@pytest.mark.parametrize("b,topk,parts,gran,ovh", [(2, 128, 66, 64, 5), (64, 2048, 256, 32, 5),
+                                                   (4, 2048, 256, 32, 0), (128, 2048, 512, 64, 5)])
+def test_sched_meta_device_matches_oracle(b, topk, parts, gran, ovh):
+    _need_gpu()
+    shape = M.make_shape(b, 1, 128, topk, 64 * 64, num_parts=parts, split_granularity=gran,
+                         fixed_overhead=ovh)
+    plan = M.DecodePlan(shape)
+    plan.get_sched_meta()
+    torch.cuda.synchronize()
+    meta = plan.sched_meta.cpu().numpy().reshape(parts, 8)
+    want, prefix = O.sched_plan([topk] * b, gran, ovh, parts)
+    assert plan.num_splits.cpu().tolist() == prefix
+    assert [tuple(m[:7]) for m in meta.tolist()] == [tuple(x) for x in want]
+
+
+# ----------------------------------------------------------------------------- gather / dequant
+def _gather(w, kv=None):
+    plan = _plan(w, num_parts=1)
+    q, kv, idx = w.q_device(), (w.kv_device() if kv is None else kv), w.indices_device()
+    k_rows = torch.zeros((w.b, w.s_q, w.topk, 576), dtype=torch.int16, device="cuda")
+    v_rows = torch.zeros((w.b, w.s_q, w.topk, 512), dtype=torch.int16, device="cuda")
+    M.mla_debug_gather_dequant(plan.args(q, kv, idx, w.sm_scale), k_rows.data_ptr(), v_rows.data_ptr())
+    torch.cuda.synchronize()
+    return (k_rows.cpu().numpy().view(np.uint16), v_rows.cpu().numpy().view(np.uint16))
+
+
+def _bf16_bits_exact(x):
+    """float64 values that are exact in bf16 -> their bit patterns."""
+    f = x.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), x)
+    bits = f.view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0), "value not representable in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("variant", ["cfg0", "ragged", "bf16"])
+def test_gather_dequant_bit_exact(variant):
+    _need_gpu()
+    if variant == "cfg0":
+        w = W.make_config(0)
+    elif variant == "ragged":
+        w = W.paged_decode("ragged", 7, b=3, s_q=2, h_q=128, topk=77, tokens_per_seq=320, P=16)
+        w.indices[0, 0, 5] = -1
+        w.indices[1, 1, :] = -1
+        w.indices[2, 0, 70] = w.num_kv_tokens + 3          # out of range -> empty
+    else:
+        w = W.sparse_prefill("bf16", 9, s_q=5, h_q=128, topk=40, s_kv=96, prior=60)
+    k_rows, v_rows = _gather(w)
+    rows, valid = O.gather_dequant(w.kv_host(), w.indices, w.kv_format, w.page_block_size)
+    want = _bf16_bits_exact(rows)
+    assert np.array_equal(k_rows, want)
+    assert np.array_equal(v_rows, want[..., :512])
+    print(f"[gather {variant}] rows={valid.size} valid={int(valid.sum())} bit-exact", flush=True)
+
+
+# ----------------------------------------------------------------------------- decode + combine
+@pytest.mark.parametrize("num_parts", [0, 1, 7, 300])
+def test_decode_cfg0(num_parts):
+    w = W.make_config(0)
+    out, lse, plan = run_gpu(w, num_parts=num_parts)
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"cfg0 parts={num_parts}")
+
+
+@pytest.mark.parametrize("topk,gran", [(1, 32), (31, 32), (33, 32), (100, 64), (257, 32), (64, 64)])
+def test_decode_ragged_topk(topk, gran):
+    w = W.paged_decode("ragged", 100 + topk, b=3, s_q=2, h_q=128, topk=topk, tokens_per_seq=512, P=64)
+    for parts in (0, 1):
+        out, lse, _ = run_gpu(w, num_parts=parts, split_granularity=gran)
+        ref_out, ref_lse = oracle(w)
+        assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"topk={topk} parts={parts}")
+
+
+def test_decode_empty_and_duplicate_slots():
+    w = W.paged_decode("edge", 21, b=4, s_q=1, h_q=128, topk=96, tokens_per_seq=256, P=64)
+    w.indices[0, 0, :] = -1                               # no valid slot at all
+    w.indices[1, 0, 40:] = -1                             # valid slots only in the first tiles
+    w.indices[2, 0, :64] = -1                             # first two tiles empty
+    w.indices[3, 0, :] = w.indices[3, 0, 0]               # every slot the same token
+    w.indices[3, 0, 10] = w.num_kv_tokens + 5             # plus an out-of-range slot
+    w = W._finish("edge", np.random.default_rng(5), w.kv_format, w.b, w.s_q, w.h_q, w.topk,
+                  w.page_block_size, w.num_kv_tokens, w.indices, q_bits=w.q_bits)
+    for parts in (0, 1, 5):
+        out, lse, _ = run_gpu(w, num_parts=parts, split_granularity=32)
+        ref_out, ref_lse = oracle(w)
+        assert np.all(out[0, 0] == 0) and np.all(np.isposinf(lse[0, :, 0]))
+        assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"edge parts={parts}")
+
+
+def test_single_repeated_row_is_exact():
+    """All slots name one token: out = V of that row exactly (p = 1 for every
+    slot, sums of equal bf16 values are exact), lse = score + ln(topk)."""
+    w = W.paged_decode("rep", 31, b=2, s_q=1, h_q=128, topk=256, tokens_per_seq=256, P=64)
+    w.indices[:] = w.indices[:, :, :1]
+    w = W._finish("rep", np.random.default_rng(6), w.kv_format, w.b, w.s_q, w.h_q, w.topk,
+                  w.page_block_size, w.num_kv_tokens, w.indices, q_bits=w.q_bits)
+    for parts in (0, 1):
+        out, lse, _ = run_gpu(w, num_parts=parts, split_granularity=32, fixed_overhead=0)
+        kv = w.kv_host()
+        for bi in range(w.b):
+            t = int(w.indices[bi, 0, 0])
+            row = O.decode_fp8_rows(kv[t // 64, t % 64, 0])
+            assert np.array_equal(out[bi, 0], np.broadcast_to(row[:512], (128, 512)).astype(np.float32))
+            s = O.bf16_value(w.q_bits[bi, 0]) @ row / 24.0
+            assert np.all(np.abs(lse[bi, :, 0] - (s + math.log(w.topk))) <= LSE_TOL)
+
+
+def test_reference_max_recompute_path():
+    """A late tile whose scores exceed the first tile's max by far more than
+    2^64 (log2 units) forces the piece to be recomputed; the result must still
+    match the definition."""
+    rng = np.random.default_rng(41)
+    w = W.paged_decode("jump", 41, b=2, s_q=1, h_q=128, topk=128, tokens_per_seq=256, P=64)
+    q = O.bf16_value(w.q_bits[0, 0, 0])
+    big_tok = int(w.indices[0, 0, 100])                  # slot in the 4th tile
+    nope = (q[:512] * 6.0).astype(np.float32)[None]
+    rope = W.to_bf16_bits((q[512:] * 6.0).astype(np.float32))[None]
+    row = W.encode_fp8_rows(nope, rope)[0]
+    pos = int(np.searchsorted(w.ref_ids, big_tok))
+    assert w.ref_ids[pos] == big_tok
+    w.ref_rows[pos] = row
+    for parts in (0, 1):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        ref_out, ref_lse = oracle(w)
+        assert ref_lse[0, 0, 0] * math.log2(math.e) > 100      # really beyond the threshold
+        assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"jump parts={parts}")
+
+
+def test_deterministic():
+    w = W.make_config(0)
+    a = run_gpu(w)
+    b = run_gpu(w)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_strided_q_and_out():
+    _need_gpu()
+    w = W.make_config(0)
+    q_full = torch.zeros((w.b, w.s_q, w.h_q, 640), dtype=torch.bfloat16, device="cuda")
+    q_full[..., :576] = w.q_device()
+    q = q_full[..., :576]
+    plan = _plan(w)
+    out_full = torch.zeros((w.b, w.s_q, w.h_q, 520), dtype=torch.bfloat16, device="cuda")
+    out = out_full[..., :512]
+    plan.get_sched_meta()
+    a = plan.args(q, w.kv_device(), w.indices_device(), w.sm_scale, out=out)
+    M.mla_sparse_decode_fwd(a)
+    M.mla_splitkv_combine(a)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out.float().cpu().numpy(), plan.lse.cpu().numpy(), ref_out, ref_lse,
+                  all_queries(w), "strided")
+    assert torch.all(out_full[..., 512:] == 0)
+
+
+# ----------------------------------------------------------------------------- the five workloads
+@pytest.fixture(scope="module")
+def cfg1():
+    return W.make_config(1)
+
+
+def test_cfg1_production_all_queries(cfg1):
+    w = cfg1
+    out, lse, plan = run_gpu(w)
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), "cfg1")
+
+
+def test_cfg1_fine_split(cfg1):
+    w = cfg1
+    out, lse, plan = run_gpu(w, split_granularity=32, fixed_overhead=2)
+    qs = [(0, 0), (17, 0), (63, 0)]
+    ref_out, ref_lse = oracle(w, qs)
+    assert_parity(out, lse, ref_out, ref_lse, qs, "cfg1 gran32")
+
+
+def test_cfg2_half_heads_short_sequences():
+    w = W.make_config(2)
+    out, lse, plan = run_gpu(w)
+    short = w.meta["short_seqs"]
+    qs = sorted(set([(s, 0) for s in short[:6]] + [(0, 0), (1, 0), (64, 0), (127, 0)]))
+    ref_out, ref_lse = oracle(w, qs)
+    assert_parity(out, lse, ref_out, ref_lse, qs, "cfg2")
+    assert len(short) == 13
+
+
+def test_cfg3_sparse_prefill_bf16():
+    w = W.make_config(3)
+    out, lse, plan = run_gpu(w)
+    qs = [(0, t) for t in (0, 1, 2, 1000, 2047, 3000, 4094, 4095)]
+    ref_out, ref_lse = oracle(w, qs)
+    assert_parity(out, lse, ref_out, ref_lse, qs, "cfg3")
+
+
+@pytest.mark.parametrize("sort_slots", [False, True])
+def test_cfg4_split_stress(sort_slots):
+    w = W.make_config(4, sort_slots=sort_slots)
+    out, lse, plan = run_gpu(w, num_parts=256, split_granularity=32, fixed_overhead=0)
+    ns = plan.num_splits.cpu().numpy()
+    assert np.all(np.diff(ns) >= 64)                      # >= 64 topk chunks per query
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"cfg4 sorted={sort_slots}")
+
+
+def test_cfg4_shuffled_equals_sorted():
+    a = run_gpu(W.make_config(4, sort_slots=False), num_parts=256, split_granularity=32, fixed_overhead=0)
+    b = run_gpu(W.make_config(4, sort_slots=True), num_parts=256, split_granularity=32, fixed_overhead=0)
+    assert np.all(np.abs(a[0] - b[0]) <= ATOL + RTOL * np.abs(b[0]))
+    assert np.all(np.abs(a[1] - b[1]) <= LSE_TOL)
