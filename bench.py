@@ -71,7 +71,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--split-granularity", type=int, default=32)
-    ap.add_argument("--fixed-overhead", type=int, default=2)
+    ap.add_argument("--fixed-overhead", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

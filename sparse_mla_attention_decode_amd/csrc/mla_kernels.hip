@@ -60,17 +60,21 @@ template <> struct RowFmt<MLA_KV_BF16_576> {
     static constexpr int ROWB = 1152, ROPE_OFF = 1024;
 };
 
-// LDS map: [raw tile][staged K rows][2 validity masks][4 restart flags]
-template <int FMT> struct Lds {
+// LDS map: [NRAW raw tiles][2 staged K-row tiles][validity masks][4 restart flags].
+// Raw tiles are padded so every wave issues the same number of 1 KB
+// direct-to-LDS copies per tile (exact vmcnt accounting).
+template <int FMT, int NW> struct Lds {
+    static constexpr int CPR = RowFmt<FMT>::ROWB / 16;                 // 16-byte chunks per row
+    static constexpr int CHUNKS = TILE * CPR;                          // per tile
+    static constexpr int NI = ((CHUNKS + 63) / 64 + NW - 1) / NW;      // copies per wave per tile
+    static constexpr int RAW_BYTES = NI * NW * 1024;
+    static constexpr int NRAW = (FMT == MLA_KV_FP8_656 && NW == 4) ? 3 : 2;
     static constexpr int RAW = 0;
-    static constexpr int RAW_BYTES = TILE * RowFmt<FMT>::ROWB;
-    static constexpr int KB = RAW + RAW_BYTES;
-    static constexpr int MASK = KB + KB_BYTES;
-    static constexpr int FLAGS = MASK + 8;
-    static constexpr int BYTES = FLAGS + 8;
-    static constexpr int CHUNKS = RAW_BYTES / 16;              // 16-byte DMA units per tile
-    static constexpr int CPR = RowFmt<FMT>::ROWB / 16;         // chunks per row
-    static_assert(RAW_BYTES % 1024 == 0 || true, "");
+    static constexpr int KB = RAW + NRAW * RAW_BYTES;
+    static constexpr int MASK = KB + 2 * KB_BYTES;                      // 4 slots
+    static constexpr int FLAGS = MASK + 16;
+    static constexpr int BYTES = FLAGS + 16;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 constexpr float INIT_MAX = -1e30f;
@@ -138,14 +142,132 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ----------------------------------------------------------------------------
-// scheduler kernel: one wave; the plan is sequential, lane 0 runs it and writes
-// through ordinary (vector) global stores.
+// scheduler
 // ----------------------------------------------------------------------------
+// Every request has the same block count B, so the greedy fill is a walk on
+// one small state: d = blocks of the current request already assigned when a
+// partition opens.  One partition maps d to g(d) and finishes h(d) requests.
+// g and h are tabulated for all d, their 2^k-fold compositions are built by
+// pointer doubling, and each partition finds its opening state from the bits
+// of its index.  Splits are numbered by a block-wide prefix sum.  The result
+// equals the sequential left-to-right fill step by step.
+constexpr int SCHED_THREADS = 1024;
+constexpr int SCHED_MAX_STATES = 512;      // B = ceil(topk / block) handled here
+constexpr int SCHED_LOG = 16;              // up to 65535 partitions
+
+struct SchedStep {               // one partition opened with d blocks of request r done
+    int begin_block, end_rel, end_block, last_splitted, next_d, finished;
+};
+
+__device__ __forceinline__ SchedStep sched_step(int d, int B, int ovh, int64_t payload) {
+    SchedStep s;
+    s.begin_block = d;
+    const int64_t left = B - d;
+    if (left + ovh <= payload) {
+        const int64_t rem = payload - (left + ovh);
+        const int64_t k = rem / (B + ovh);                  // whole requests after the first
+        const int64_t x = rem - k * (B + ovh) - ovh;        // blocks of the next one
+        if (x > 0) {
+            s.end_rel = (int)(1 + k); s.end_block = (int)x; s.last_splitted = 1;
+        } else {
+            s.end_rel = (int)k; s.end_block = B; s.last_splitted = 0;
+        }
+        s.next_d = x > 0 ? (int)x : 0;
+        s.finished = (int)(1 + k);
+    } else {
+        const int x = (int)(payload - ovh);
+        s.end_rel = 0; s.end_block = d + x; s.last_splitted = 1;
+        s.next_d = d + x;
+        s.finished = 0;
+    }
+    return s;
+}
+
+__global__ void __launch_bounds__(SCHED_THREADS) sched_parallel_kernel(int b, int topk, int block,
+                                                                     int ovh, int num_parts,
+                                                                     int32_t* meta, int32_t* prefix) {
+    __shared__ int16_t Gt[SCHED_LOG][SCHED_MAX_STATES];
+    __shared__ int32_t Ht[SCHED_LOG][SCHED_MAX_STATES];
+    __shared__ int32_t scan[SCHED_THREADS];
+    const int tid = threadIdx.x;
+    const int B = (topk + block - 1) / block;
+    const int64_t total = (int64_t)b * (B + ovh);
+    const int64_t payload = (total + num_parts - 1) / num_parts + ovh;
+    int levels = 1;
+    while ((1 << levels) <= num_parts && levels < SCHED_LOG) ++levels;
+
+    for (int d = tid; d < B; d += SCHED_THREADS) {
+        const SchedStep st = sched_step(d, B, ovh, payload);
+        Gt[0][d] = (int16_t)st.next_d;
+        Ht[0][d] = st.finished;
+    }
+    for (int k = 1; k < levels; ++k) {
+        __syncthreads();
+        for (int d = tid; d < B; d += SCHED_THREADS) {
+            const int mid = Gt[k - 1][d];
+            Gt[k][d] = Gt[k - 1][mid];
+            Ht[k][d] = min(Ht[k - 1][d] + Ht[k - 1][mid], b);   // saturate: only r < b matters
+        }
+    }
+    __syncthreads();
+
+    // each thread owns a contiguous run of partitions
+    const int per = (num_parts + SCHED_THREADS - 1) / SCHED_THREADS;
+    const int p0 = min(tid * per, num_parts), p1 = min(p0 + per, num_parts);
+    // opening state of p0
+    int r = 0, d = 0;
+    for (int k = 0; k < levels; ++k) {
+        if ((p0 >> k) & 1) {
+            r = min(r + Ht[k][d], b);
+            d = Gt[k][d];
+        }
+    }
+    // pieces of the run, then a block-wide exclusive scan of the counts
+    int count = 0;
+    {
+        int rr = r, dd = d;
+        for (int p = p0; p < p1 && rr < b; ++p) {
+            const SchedStep st = sched_step(dd, B, ovh, payload);
+            count += min(rr + st.end_rel, b - 1) - rr + 1;
+            rr = min(rr + st.finished, b);
+            dd = st.next_d;
+        }
+    }
+    scan[tid] = count;
+    __syncthreads();
+    for (int off = 1; off < SCHED_THREADS; off <<= 1) {
+        const int v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    int cursor = scan[tid] - count;
+    const int total_pieces = scan[SCHED_THREADS - 1];
+    for (int p = p0; p < p1; ++p) {
+        int32_t* m = meta + 8 * p;
+        if (r >= b) {
+            m[0] = b; m[1] = b; m[2] = 0; m[3] = 0; m[4] = cursor; m[5] = 0; m[6] = 0; m[7] = 0;
+            continue;
+        }
+        const SchedStep st = sched_step(d, B, ovh, payload);
+        int end_req = r + st.end_rel, end_block = st.end_block, last = st.last_splitted;
+        if (end_req >= b) { end_req = b - 1; end_block = B; last = 0; }
+        m[0] = r; m[1] = end_req; m[2] = d; m[3] = end_block; m[4] = cursor;
+        m[5] = d > 0; m[6] = last; m[7] = 0;
+        for (int q = (d > 0 ? r + 1 : r); q <= end_req; ++q) prefix[q] = cursor + (q - r);
+        cursor += end_req - r + 1;
+        r = min(r + st.finished, b);
+        d = st.next_d;
+    }
+    if (tid == 0) prefix[b] = total_pieces;
+}
+
+// Sequential fill, one lane (used when the state table does not fit).
 __global__ void __launch_bounds__(64) sched_kernel(int b, int topk, int block, int overhead,
                                                    int num_parts, int32_t* meta, int32_t* prefix) {
     if (threadIdx.x != 0) return;
     plan_schedule(b, topk, block, overhead, num_parts, meta, prefix,
-                  [](int32_t* p, int32_t v) { *(volatile int32_t*)p = v; });
+                  [](int32_t* p, int32_t v) { *p = v; });
 }
 
 // ----------------------------------------------------------------------------
@@ -163,82 +285,144 @@ __device__ __forceinline__ const uint8_t* row_ptr(const DecodeParams& p, int t) 
     return p.kv + (int64_t)t * p.kv_block_stride;
 }
 
-// Gather: start the HBM -> LDS copy of the rows of slots [k0, k0 + 32) (those
-// below k_end and valid) into the raw tile, and record the validity mask of
-// the tile in mask slot `ms`.  Every wave resolves the 32 row addresses with
-// lanes 0..31 and copies its share of the 16-byte chunks.
+// Direct-to-LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds_addr + 16 i.  Written as inline asm so the compiler's wait-count pass
+// does not treat every later LDS read as possibly aliasing the copy (it would
+// drain all copies in flight); the decode loop orders the copies itself with
+// an explicit vmcnt wait and a barrier before the copied bytes are read.
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
+}
+
+// Row address (as two dwords) of slot `key` of the piece for lanes 0..31; slots
+// that are empty, beyond k_end, or outside the cache get the cache base (a
+// harmless dummy source whose staged row is zeroed).  Returns the validity
+// bit of this lane's slot.
+template <int FMT>
+__device__ __forceinline__ bool slot_address(const DecodeParams& p, int t, bool in_range,
+                                             uint32_t& lo, uint32_t& hi) {
+    const uint8_t* rp = in_range ? row_ptr<FMT>(p, t) : nullptr;
+    const uint64_t a = (uint64_t)(uintptr_t)(rp ? rp : p.kv);
+    lo = (uint32_t)a;
+    hi = (uint32_t)(a >> 32);
+    return rp != nullptr;
+}
+
+// Gather: start the HBM -> LDS copy of the 32 rows of one tile into a raw
+// buffer.  `t` holds (lanes 0..31) the token ids of the tile's slots, or -1.
+// Every wave issues exactly NI 1 KB copies with all lanes active (padding
+// chunks re-read row 0 of the tile into the buffer's padding), so the number
+// of outstanding memory operations is the same in every iteration.  Thread 0
+// records the tile's validity mask in mask slot `ms`.
 template <int FMT, int NW>
-__device__ __forceinline__ void gather_tile(const DecodeParams& p, const int32_t* idx, int k0,
-                                            int k_end, LDS_AS uint8_t* lds, int ms) {
-    using L = Lds<FMT>;
+__device__ __forceinline__ void gather_tile(const DecodeParams& p, int t, bool in_range,
+                                            LDS_AS uint8_t* lds, int raw_off, int ms) {
+    using L = Lds<FMT, NW>;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int key = k0 + (lane & 31);
-    const int t = (lane < 32 && key < k_end) ? idx[key] : -1;
-    const uint8_t* rp = row_ptr<FMT>(p, t);
-    const uint64_t valid = __ballot(rp != nullptr);
+    uint32_t a_lo, a_hi;
+    const bool ok = slot_address<FMT>(p, t, in_range && lane < 32, a_lo, a_hi);
+    const uint64_t valid = __ballot(ok);
     if (threadIdx.x == 0) *(LDS_AS uint32_t*)(lds + L::MASK + 4 * ms) = (uint32_t)valid;
-    const uint64_t addr = (uint64_t)(uintptr_t)(rp ? rp : p.kv);
-    const uint32_t a_lo = (uint32_t)addr, a_hi = (uint32_t)(addr >> 32);
-    constexpr int NINST = (L::CHUNKS + 63) / 64;
+    const uint8_t* src[L::NI];
 #pragma unroll
-    for (int j = wave; j < NINST; j += NW) {
-        const int f = 64 * j + lane;
-        const int row = f / L::CPR;
-        const int chunk = f - row * L::CPR;
-        const uint32_t lo = __shfl(a_lo, row & 31), hi = __shfl(a_hi, row & 31);
-        const bool act = f < L::CHUNKS && ((valid >> (row & 31)) & 1u);
-        const uint8_t* g = (const uint8_t*)(((uint64_t)hi << 32) | lo) + 16 * chunk;
-        if (act) __builtin_amdgcn_global_load_lds(g, (LDS_AS void*)(lds + L::RAW + 1024 * j), 16, 0, 0);
+    for (int i = 0; i < L::NI; ++i) {
+        const int f = 64 * (wave + NW * i) + lane;   // chunk index in the tile
+        const int row = f < L::CHUNKS ? f / L::CPR : 0;
+        const int chunk = f < L::CHUNKS ? f - row * L::CPR : 0;
+        const uint32_t lo = __shfl(a_lo, row), hi = __shfl(a_hi, row);
+        src[i] = (const uint8_t*)(((uint64_t)hi << 32) | lo) + 16 * chunk;
+    }
+    // LDS byte address of the wave's first 1 KB block (wave-uniform, so an SGPR)
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds + raw_off) + 1024u * wave;
+#pragma unroll
+    for (int i = 0; i < L::NI; ++i)
+        dma16(src[i], __builtin_amdgcn_readfirstlane(lds_base + 1024u * NW * i));
+}
+
+// Stage: raw rows -> bf16 K rows (dequantised NoPE, copied RoPE), branch
+// free; empty slots become zero rows.  Split into a read half and a
+// convert+write half so the decode loop can spread it between MFMAs.
+template <int FMT, int NW> struct StageRegs {
+    static constexpr int NT = NW * 64;
+    static constexpr int NOPE_UNITS = FMT == MLA_KV_FP8_656 ? 32 * 32 / NT : 32 * 64 / NT;
+    static constexpr int ROPE_UNITS = (32 * 8 + NT - 1) / NT;
+    u32x4 nope[NOPE_UNITS];
+    float scale[FMT == MLA_KV_FP8_656 ? NOPE_UNITS : 1];
+    u32x4 rope[ROPE_UNITS];
+};
+
+template <int FMT, int NW>
+__device__ __forceinline__ void stage_read(const LDS_AS uint8_t* lds, int raw_off, StageRegs<FMT, NW>& R,
+                                           int i0 = 0, int i1 = StageRegs<FMT, NW>::NOPE_UNITS + 1) {
+    using SR = StageRegs<FMT, NW>;
+    constexpr int ROWB = RowFmt<FMT>::ROWB;
+#pragma unroll
+    for (int i = i0; i < min(i1, SR::NOPE_UNITS); ++i) {
+        const int u = i * SR::NT + threadIdx.x;
+        if (FMT == MLA_KV_FP8_656) {
+            const int row = u >> 5, c = u & 31;
+            R.nope[i] = lds_read16(lds, raw_off + row * ROWB + 16 * c);
+            R.scale[i] = *(const LDS_AS float*)(lds + raw_off + row * ROWB + 512 + 4 * (c >> 3));
+        } else {
+            const int row = u >> 6, c = u & 63;
+            R.nope[i] = lds_read16(lds, raw_off + row * ROWB + 16 * c);
+        }
+    }
+    if (i1 <= SR::NOPE_UNITS) return;
+#pragma unroll
+    for (int i = 0; i < SR::ROPE_UNITS; ++i) {
+        const int u = min(i * SR::NT + (int)threadIdx.x, 255);
+        R.rope[i] = lds_read16(lds, raw_off + (u >> 3) * ROWB + RowFmt<FMT>::ROPE_OFF + 16 * (u & 7));
     }
 }
 
-// Stage: raw rows -> bf16 K rows (dequantised NoPE, copied RoPE); empty slots
-// become zero rows.
+// convert + write NoPE unit i (or the RoPE units when i == NOPE_UNITS)
 template <int FMT, int NW>
-__device__ __forceinline__ void stage_tile(LDS_AS uint8_t* lds, uint32_t valid) {
-    using L = Lds<FMT>;
-    constexpr int NT = NW * 64;
-    constexpr int ROWB = RowFmt<FMT>::ROWB;
+__device__ __forceinline__ void stage_write(LDS_AS uint8_t* lds, int kb_off, uint32_t valid,
+                                            const StageRegs<FMT, NW>& R, int i) {
+    using SR = StageRegs<FMT, NW>;
     const u32x4 zero = {0, 0, 0, 0};
-    if (FMT == MLA_KV_FP8_656) {
-        // NoPE: (row, 16-code chunk) units, 32 x 32
-#pragma unroll
-        for (int u = threadIdx.x; u < 32 * 32; u += NT) {
+    if (i < SR::NOPE_UNITS) {
+        const int u = i * SR::NT + threadIdx.x;
+        if (FMT == MLA_KV_FP8_656) {
             const int row = u >> 5, c = u & 31;
-            u32x4 lo = zero, hi = zero;
-            if ((valid >> row) & 1u) {
-                const u32x4 raw = lds_read16(lds, L::RAW + row * ROWB + 16 * c);
-                const float sc = *(const LDS_AS float*)(lds + L::RAW + row * ROWB + 512 + 4 * (c >> 3));
-                lo = u32x4{dequant2<false>(raw[0], sc), dequant2<true>(raw[0], sc),
-                           dequant2<false>(raw[1], sc), dequant2<true>(raw[1], sc)};
-                hi = u32x4{dequant2<false>(raw[2], sc), dequant2<true>(raw[2], sc),
-                           dequant2<false>(raw[3], sc), dequant2<true>(raw[3], sc)};
-            }
-            lds_write16(lds, L::KB + row * KROW + 32 * c, lo);
-            lds_write16(lds, L::KB + row * KROW + 32 * c + 16, hi);
+            const bool ok = (valid >> row) & 1u;
+            const u32x4 raw = R.nope[i];
+            const float sc = R.scale[i];
+            u32x4 lo = {dequant2<false>(raw[0], sc), dequant2<true>(raw[0], sc),
+                        dequant2<false>(raw[1], sc), dequant2<true>(raw[1], sc)};
+            u32x4 hi = {dequant2<false>(raw[2], sc), dequant2<true>(raw[2], sc),
+                        dequant2<false>(raw[3], sc), dequant2<true>(raw[3], sc)};
+            lds_write16(lds, kb_off + row * KROW + 32 * c, ok ? lo : zero);
+            lds_write16(lds, kb_off + row * KROW + 32 * c + 16, ok ? hi : zero);
+        } else {
+            const int row = u >> 6, c = u & 63;
+            lds_write16(lds, kb_off + row * KROW + 16 * c, ((valid >> row) & 1u) ? R.nope[i] : zero);
         }
     } else {
-        // NoPE: (row, 8-value chunk) units, 32 x 64, plain copy
 #pragma unroll
-        for (int u = threadIdx.x; u < 32 * 64; u += NT) {
-            const int row = u >> 6, c = u & 63;
-            const u32x4 v = ((valid >> row) & 1u) ? lds_read16(lds, L::RAW + row * ROWB + 16 * c) : zero;
-            lds_write16(lds, L::KB + row * KROW + 16 * c, v);
+        for (int r = 0; r < SR::ROPE_UNITS; ++r) {
+            const int u = r * SR::NT + threadIdx.x;
+            if (SR::NT * SR::ROPE_UNITS == 256 || u < 256) {
+                const int row = u >> 3, c = u & 7;
+                lds_write16(lds, kb_off + row * KROW + 1024 + 16 * c, ((valid >> row) & 1u) ? R.rope[r] : zero);
+            }
         }
-    }
-    // RoPE: (row, 8-value chunk) units, 32 x 8, plain copy
-    for (int u = threadIdx.x; u < 32 * 8; u += NT) {
-        const int row = u >> 3, c = u & 7;
-        const u32x4 v = ((valid >> row) & 1u)
-                            ? lds_read16(lds, L::RAW + row * ROWB + RowFmt<FMT>::ROPE_OFF + 16 * c)
-                            : zero;
-        lds_write16(lds, L::KB + row * KROW + 1024 + 16 * c, v);
     }
 }
 
-// Byte offset (relative to the staged K rows) of this lane's transposing read
-// for the value contraction: output block mb (dims 32mb..32mb+31), k-step t,
-// half `second` (keys +8).  Lane l feeds the 8-byte row of key
+template <int FMT, int NW>
+__device__ __forceinline__ void stage_tile(LDS_AS uint8_t* lds, int raw_off, int kb_off, uint32_t valid) {
+    StageRegs<FMT, NW> R;
+    stage_read<FMT, NW>(lds, raw_off, R);
+#pragma unroll
+    for (int i = 0; i <= StageRegs<FMT, NW>::NOPE_UNITS; ++i) stage_write<FMT, NW>(lds, kb_off, valid, R, i);
+}
+
+// Byte offset (relative to a staged K-row tile) of this lane's transposing
+// read for the value contraction: output block mb (dims 32mb..32mb+31),
+// k-step t, half `second` (keys +8).  Lane l feeds the 8-byte row of key
 // 16t + 4(l/32) + (l%16)/4 (+8) at dims 32mb + 16((l/16)%2) + 4(l%4); the
 // transpose hands lane l dim 32mb + l%32 of keys 16t + 4(l/32) + 0..3 (+8),
 // which is the key order the score accumulator gives P.
@@ -248,9 +432,16 @@ __device__ __forceinline__ int pv_read_base(int lane) {
     return key * KROW + 2 * dim;
 }
 
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int FMT, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
-    using L = Lds<FMT>;
+    using L = Lds<FMT, NW>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
 
@@ -276,6 +467,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
         const int k_hi = min(blk_hi * p.block, p.topk);
         const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
         const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+        // raw token ids of slots k0 + lane (lanes 0..31); the load address is
+        // clamped so the load is always issued (fixed vmcnt accounting) and
+        // slots past the piece are masked where the ids are used
+        auto load_ids = [&](int tile) -> int {
+            const int k = k_lo + tile * TILE + (lane & 31);
+            return idx[min(k, k_hi - 1)];
+        };
+        auto ids_in_range = [&](int tile) -> bool {
+            return tile < n_tiles && k_lo + tile * TILE + (lane & 31) < k_hi;
+        };
 
         // Q for this wave's heads as B operands: k-step j covers dims
         // 16j + 8h .. 16j + 8h + 7, matching the K row reads
@@ -295,24 +496,63 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
             for (int mb = 0; mb < 16; ++mb) O[mb] = f32x16{};
             l_part = 0.f;
             __syncthreads();                        // LDS free (previous piece / pass done)
-            if (n_tiles > 0) gather_tile<FMT, NW>(p, idx, k_lo, k_hi, lds, 0);
+
+            // prologue: tiles 0 and 1 in flight, ids of tiles 2 and 3 loaded
+            const int ids0 = load_ids(0), ids1 = load_ids(1);
+            gather_tile<FMT, NW>(p, ids0, ids_in_range(0), lds, L::RAW, 0);
+            gather_tile<FMT, NW>(p, ids1, ids_in_range(1), lds, L::RAW + L::RAW_BYTES, 1);
+            int ids_a = load_ids(2), ids_b = load_ids(3);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            stage_tile<FMT, NW>(lds, L::RAW, L::KB, *(const LDS_AS uint32_t*)(lds + L::MASK));
+            __syncthreads();
 
             for (int it = 0; it < n_tiles; ++it) {
-                const int k0 = k_lo + it * TILE;
-                __builtin_amdgcn_s_waitcnt(0);      // this wave's tile copies have landed
-                __syncthreads();                    // ... and every wave's; tile it-1 consumed
-                const uint32_t vmask = *(const LDS_AS uint32_t*)(lds + L::MASK + 4 * (it & 1));
-                stage_tile<FMT, NW>(lds, vmask);
-                __syncthreads();                    // staged rows visible, raw tile free
-                if (it + 1 < n_tiles) gather_tile<FMT, NW>(p, idx, k0 + TILE, k_hi, lds, (it + 1) & 1);
+                const int kb_cur = L::KB + (it & 1) * KB_BYTES;
+                const uint32_t vmask = *(const LDS_AS uint32_t*)(lds + L::MASK + 4 * (it & 3));
+                // ---- start tile it+2 (ids loaded two iterations ago) and the ids of it+4
+                // The id load goes first: vmcnt is in order, so a later wait on
+                // these ids only forces copies older than them, never tile it+2.
+                const int ids_new = load_ids(it + 4);
+                gather_tile<FMT, NW>(p, ids_a, ids_in_range(it + 2), lds,
+                                     L::RAW + ((it + 2) % L::NRAW) * L::RAW_BYTES, (it + 2) & 3);
+                ids_a = ids_b;
+                ids_b = ids_new;
 
-                // ---- S^T = K Q^T
+                // ---- S^T = K Q^T, with the staging of tile it+1 spread between
+                // the MFMAs (the raw rows of tile it+1 landed before the last barrier)
+                StageRegs<FMT, NW> R;
+                const int raw_next = L::RAW + ((it + 1) % L::NRAW) * L::RAW_BYTES;
+                const int kb_next = L::KB + ((it + 1) & 1) * KB_BYTES;
+                const uint32_t vmask_next = *(const LDS_AS uint32_t*)(lds + L::MASK + 4 * ((it + 1) & 3));
+                constexpr int NSTAGE = StageRegs<FMT, NW>::NOPE_UNITS + 1;   // units incl. RoPE
+                constexpr int SPAN = 36 / NSTAGE > 1 ? 36 / NSTAGE : 1;        // MFMAs per unit
+                stage_read<FMT, NW>(lds, raw_next, R, 0, 1);
                 f32x16 S;
+                {
+                    constexpr int AHEAD = 2;
+                    bf16x8 a[AHEAD];
 #pragma unroll
-                for (int j = 0; j < 36; ++j) {
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(lds, L::KB + qk_base + 32 * j));
-                    if (j == 0) mfma_qk_first(S, a, qb[j]);
-                    else mfma_qk(S, a, qb[j]);
+                    for (int j = 0; j < AHEAD; ++j)
+                        a[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, kb_cur + qk_base + 32 * j));
+#pragma unroll
+                    for (int j = 0; j < 36; ++j) {
+                        const bf16x8 cur = a[j % AHEAD];
+                        if (j + AHEAD < 36)
+                            a[j % AHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, kb_cur + qk_base + 32 * (j + AHEAD)));
+                        if (j == 0) mfma_qk_first(S, cur, qb[j]);
+                        else mfma_qk(S, cur, qb[j]);
+                        // staging unit u is read at MFMA SPAN*u - SPAN/2 and written at SPAN*u + SPAN-1
+                        if (j % SPAN == SPAN / 2 && j / SPAN + 1 < NSTAGE)
+                            stage_read<FMT, NW>(lds, raw_next, R, j / SPAN + 1, j / SPAN + 2);
+                        if (j % SPAN == SPAN - 1 && j / SPAN < NSTAGE)
+                            stage_write<FMT, NW>(lds, kb_next, vmask_next, R, j / SPAN);
+                    }
+#pragma unroll
+                    for (int i = 36 / SPAN; i < NSTAGE; ++i) {
+                        stage_read<FMT, NW>(lds, raw_next, R, i, i + 1);
+                        stage_write<FMT, NW>(lds, kb_next, vmask_next, R, i);
+                    }
                 }
                 mfma_result_fence(S);
 
@@ -347,24 +587,34 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
 
                 // ---- O^T += V^T P^T
                 valu_to_mfma_fence(pb[0], pb[1]);
-#pragma unroll
-                for (int mb = 0; mb < 16; ++mb) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int off = L::KB + pv_base + t * 16 * KROW + mb * 64;
+                {
+                    constexpr int AHEAD = 2;
+                    auto vread = [&](int st) {          // step st = (block st/2, k-step st%2)
+                        const int off = kb_cur + pv_base + (st & 1) * 16 * KROW + (st >> 1) * 64;
                         const u32x2 r0 = lds_read_tr16(lds, off);
                         const u32x2 r1 = lds_read_tr16(lds, off + 8 * KROW);
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
-                        mfma_pv(O[mb], a, pb[t]);
+                        return __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
+                    };
+                    bf16x8 a[AHEAD];
+#pragma unroll
+                    for (int st = 0; st < AHEAD; ++st) a[st] = vread(st);
+#pragma unroll
+                    for (int st = 0; st < 32; ++st) {
+                        const bf16x8 cur = a[st % AHEAD];
+                        if (st + AHEAD < 32) a[st % AHEAD] = vread(st + AHEAD);
+                        mfma_pv(O[st >> 1], cur, pb[st & 1]);
                     }
                 }
+                // tile it+2 (the last memory operations issued) must have landed
+                // before it is staged in the next iteration
+                wait_vmcnt<0>();
+                __syncthreads();
             }
             // A score exceeded the reference by more than 2^threshold in some
             // wave: recompute the piece against the true max (rare).
-            __syncthreads();
             const uint32_t flags = *(const LDS_AS uint32_t*)(lds + L::FLAGS);
             __syncthreads();
-            if (flags == 0u || pass > 0) break;         // the second pass uses the true max
+            if (flags == 0u || pass > 0) break;          // the second pass uses the true max
             if (threadIdx.x < 4) lds[L::FLAGS + threadIdx.x] = 0;
             m_ref = m_seen;
         }
@@ -417,7 +667,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
 template <int FMT, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) gather_kernel(DecodeParams p, uint16_t* k_rows,
                                                             uint16_t* v_rows) {
-    using L = Lds<FMT>;
+    using L = Lds<FMT, NW>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
     const int qi = blockIdx.x;                    // query token = req * s_q + sq
@@ -428,11 +678,13 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_kernel(DecodeParams p, uint
     const int n_tiles = (p.topk + TILE - 1) / TILE;
     for (int it = 0; it < n_tiles; ++it) {
         const int k0 = it * TILE;
+        const int k = k0 + (lane & 31);
+        const int t = idx[min(k, p.topk - 1)];
         __syncthreads();
-        gather_tile<FMT, NW>(p, idx, k0, p.topk, lds, 0);
+        gather_tile<FMT, NW>(p, t, k < p.topk, lds, L::RAW, 0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        stage_tile<FMT, NW>(lds, *(const LDS_AS uint32_t*)(lds + L::MASK));
+        stage_tile<FMT, NW>(lds, L::RAW, L::KB, *(const LDS_AS uint32_t*)(lds + L::MASK));
         __syncthreads();
         if (wave == 0) {
             const int key = k0 + n;
@@ -445,13 +697,13 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_kernel(DecodeParams p, uint
         if (v_rows != nullptr && wave == NW - 1) {
             const int pv_base = pv_read_base(lane);
             for (int mb = 0; mb < 16; ++mb) {
-                for (int t = 0; t < 2; ++t) {
-                    const int off = L::KB + pv_base + t * 16 * KROW + mb * 64;
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int off = L::KB + pv_base + tt * 16 * KROW + mb * 64;
                     const u32x2 r0 = lds_read_tr16(lds, off);
                     const u32x2 r1 = lds_read_tr16(lds, off + 8 * KROW);
                     const uint32_t d[4] = {r0[0], r0[1], r1[0], r1[1]};
                     for (int e = 0; e < 8; ++e) {
-                        const int key = k0 + 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+                        const int key = k0 + 16 * tt + 8 * (e >> 2) + 4 * h + (e & 3);
                         if (key < p.topk) {
                             const uint16_t val = (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
                             v_rows[((int64_t)qi * p.topk + key) * 512 + 32 * mb + n] = val;
@@ -509,8 +761,13 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
 // launchers
 // ----------------------------------------------------------------------------
 hipError_t launch_sched(const ResolvedShape& s, int32_t* meta, int32_t* prefix, hipStream_t st) {
-    hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(64), 0, st, s.b, s.topk, s.block, s.overhead,
-                       s.num_parts, meta, prefix);
+    const int B = (s.topk + s.block - 1) / s.block;
+    if (B <= SCHED_MAX_STATES && s.num_parts < (1 << SCHED_LOG))
+        hipLaunchKernelGGL(sched_parallel_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, s.b, s.topk,
+                           s.block, s.overhead, s.num_parts, meta, prefix);
+    else
+        hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(64), 0, st, s.b, s.topk, s.block, s.overhead,
+                           s.num_parts, meta, prefix);
     return hipGetLastError();
 }
 
@@ -526,9 +783,10 @@ template <int FMT, int NW>
 static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, hipStream_t st) {
     auto k = decode_kernel<FMT, NW>;
     static bool done = false;
-    hipError_t e = allow_lds(k, Lds<FMT>::BYTES, done);
+    constexpr int bytes = Lds<FMT, NW>::BYTES;
+    hipError_t e = allow_lds(k, bytes, done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(num_parts, p.s_q), dim3(NW * 64), Lds<FMT>::BYTES, st, p);
+    hipLaunchKernelGGL(k, dim3(num_parts, p.s_q), dim3(NW * 64), bytes, st, p);
     return hipGetLastError();
 }
 
@@ -545,9 +803,10 @@ static hipError_t launch_gather_t(const DecodeParams& p, uint16_t* k_rows, uint1
                                   hipStream_t st) {
     auto k = gather_kernel<FMT, 4>;
     static bool done = false;
-    hipError_t e = allow_lds(k, Lds<FMT>::BYTES, done);
+    constexpr int bytes = Lds<FMT, 4>::BYTES;
+    hipError_t e = allow_lds(k, bytes, done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(p.b * p.s_q), dim3(256), Lds<FMT>::BYTES, st, p, k_rows, v_rows);
+    hipLaunchKernelGGL(k, dim3(p.b * p.s_q), dim3(256), bytes, st, p, k_rows, v_rows);
     return hipGetLastError();
 }
 
