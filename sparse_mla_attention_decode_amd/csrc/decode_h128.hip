@@ -1,0 +1,627 @@
+// gfx950 sparse MLA decode for 128 query heads over the FP8 656-byte token
+// cache ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14).
+//
+// One work-group of 4 waves per scheduler partition; it walks the topk slots
+// of each (request, block range) piece in tiles of 32 keys.  Wave w is
+// (head group w/2, dim half dh = w%2) for the score contraction and owns
+// output dims [128w, 128w+128) of all 128 heads for the value contraction.
+//
+//   gather   every wave copies its 8 rows of a tile (keys 8w..8w+7) HBM -> LDS
+//            with direct-to-LDS loads, three tiles ahead; the token ids are
+//            copied into LDS the same way, so memory-counter waits are
+//            explicit and wave-local.  Empty slots copy rows of a zero page.
+//   stage    every wave dequantises the NoPE chunks it copied (code *
+//            power-of-two scale -> bf16, exact) and moves the RoPE chunks
+//            into the staged tile [32 keys][576 bf16];
+//   S^T      = K Q^T over the wave's 288 dims for its 64 heads: each K
+//            fragment read from LDS feeds two MFMAs (36 per wave per tile);
+//            the partial for the partner's 32 heads is swapped through LDS, so
+//            wave w ends with full scores for heads [32w, 32w+32);
+//   softmax  base 2 on the accumulator, masked by slot validity, against a
+//            per-head reference max (see below); P rounded to bf16 and
+//            published in LDS;
+//   O^T     += V^T P^T for the wave's 128 dims and all 128 heads: each V^T
+//            fragment (transposing LDS read) feeds four MFMAs (32 per tile);
+//            O^T [128 dims x 128 heads] lives in the 256 AGPRs.
+//
+// Tile loop, three phases per tile t separated by work-group barriers:
+//   1. S^T(t) MFMAs; partner partial -> LDS;
+//   2. softmax(t) and the address/copy work for tile t+3, interleaved with
+//      the value MFMAs of tile t-1 (one branch-free scheduling region);
+//   3. P(t) -> LDS and staging of tile t+1;
+// so the VALU work of the softmax runs under matrix-core work.
+//
+// The reference max of a piece is the max score of its first tile holding a
+// valid key; later tiles are accumulated against it as long as no score
+// exceeds it by more than 2^64.  If one does, the piece is recomputed with the
+// true max, which gives the online-softmax result without rescaling O.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int NW = 4;                             // waves per work-group
+constexpr int ROWB = 656;                         // FP8 token row
+constexpr int RCH = ROWB / 16;                    // 41 16-byte chunks per row
+constexpr int WROWS = TILE / NW;                  // rows gathered and staged per wave
+constexpr int WAVE_RAW = WROWS * ROWB;            // 5248 bytes: one wave's slice
+constexpr int NDMA = (RCH + 7) / 8;               // 6 copies per lane per tile
+constexpr int RAW_BYTES = TILE * ROWB;            // 20992
+constexpr int NRAW = 3;                           // raw tiles in flight / in use
+constexpr int KP = 1168;                          // staged row pitch (1152 + 16)
+constexpr int KBB = TILE * KP;                    // 37376
+constexpr int IDS_SLOTS = 3;                      // token-id tiles per wave in LDS
+constexpr int ZERO_ROWS = 64;                     // rows of the zero page
+
+// LDS map (bytes).  The 16-byte pad at the end of every staged row is never
+// read by the contractions; row 0's pad of staged tile 0 holds the restart
+// flags.  The head statistics of the epilogue reuse the score-exchange area.
+constexpr int L_RAW = 0;                               // [3][4 slices][6][8 rows][8 chunks][16]
+constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;          // [2][32 rows][1168] bf16 K
+constexpr int L_XS = L_KB + 2 * KBB;                    // [4 dest waves][4][64 lanes][16]
+constexpr int L_XP = L_XS + NW * 4096;                  // [4 head blocks][2 k-steps][64][16]
+constexpr int L_IDS = L_XP + NW * 2048;                 // [4 waves][3 slots][32] int32
+constexpr int L_BYTES = L_IDS + NW * IDS_SLOTS * 128;
+constexpr int L_FLAGS = L_KB + 1152;                    // [4] restart flags (row pad)
+constexpr int L_LM = L_XS;                              // [128 heads] {l, m} (epilogue)
+static_assert(L_BYTES <= 160 * 1024, "LDS budget");
+static_assert(NDMA == 6 && RCH - 8 * (NDMA - 1) == 1, "copy layout");
+
+// Rows copied for empty or out-of-range slots: all zero bytes (zero codes,
+// zero scales, zero RoPE), so staged values of empty slots are zero without
+// masking.  Spread over 64 rows so the reads do not pile onto one L2 channel.
+__device__ __attribute__((aligned(256))) uint8_t g_zero_rows[ZERO_ROWS * ROWB];
+
+// Raw slice layout (5248 bytes): chunk c < 40 of row r at 1024 (c / 8) +
+// 128 r + 16 (c % 8); chunk 40 of row r at 5120 + 16 r.  Copy i < 5 of lane L
+// moves chunk (L % 8) + 8 i of row L / 8, i.e. LDS byte 1024 i + 16 L: every 8
+// lanes read 128 contiguous bytes of one row and each lane needs one row
+// address per tile.  The last copy moves chunk 40 of row L with lanes 0..7.
+__device__ __forceinline__ int raw_off(int row, int chunk) {
+    return chunk < 40 ? 1024 * (chunk >> 3) + 128 * row + 16 * (chunk & 7) : 5120 + 16 * row;
+}
+
+// Partitions of one request are adjacent in the plan and blocks are dealt to
+// the 8 XCDs round robin: map each XCD's blocks to a contiguous partition
+// range, so a request's partitions share one L2 (Q is fetched once per XCD).
+__device__ __forceinline__ int xcd_part(int bid, int nb) {
+    const int x = bid & 7, k = bid >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    return x * q + min(x, r) + k;
+}
+
+// Row address of token t, or a zero row when the slot is empty (out of the
+// piece, -1, or outside the cache); returns whether the slot is valid.
+__device__ __forceinline__ bool token_addr(const DecodeParams& p, int t, bool in_range, int zrow,
+                                           const uint8_t*& a) {
+    const bool ok = in_range && t >= 0 && (int64_t)t < p.n_tok;
+    const int tt = ok ? t : 0;
+    const int blk = p.page_shift >= 0 ? (tt >> p.page_shift) : tt / p.page_block_size;
+    const int off = tt - blk * p.page_block_size;
+    const uint8_t* r = p.kv + (int64_t)blk * p.kv_block_stride + (int64_t)off * ROWB;
+    a = ok ? r : g_zero_rows + zrow * ROWB;
+    return ok;
+}
+
+// Copies of this wave's 8 rows of a tile into its raw slice; `src` points at
+// chunk lane % 8 of row lane / 8 (key 8w + lane / 8).
+__device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, uint32_t slice) {
+#pragma unroll
+    for (int i = 0; i < NDMA - 1; ++i)
+        dma16(src + 128 * i, __builtin_amdgcn_readfirstlane(slice + 1024u * i));
+    // chunk 40 of row `lane` (lanes 0..7): row starts are held by lanes 8 r
+    const uint64_t row = (uint64_t)(uintptr_t)(src - 16 * (lane & 7));
+    const int from = 8 * (lane & 7);
+    const uint64_t rl = ((uint64_t)(uint32_t)__shfl((uint32_t)(row >> 32), from) << 32) |
+                        (uint32_t)__shfl((uint32_t)row, from);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(slice + 1024u * (NDMA - 1));
+    if (lane < 8) dma16((const uint8_t*)(uintptr_t)rl + 16 * 40, dst);
+}
+
+// Copy the 32 token ids of a tile (clamped to the piece) into an id slot.
+__device__ __forceinline__ void copy_ids(const int32_t* idx, int k_lo, int k_hi, int tile, int lane,
+                                         uint32_t slot_addr) {
+    const int k = min(k_lo + tile * TILE + (lane & 31), k_hi - 1);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(slot_addr);
+    if (lane < 32) dma4(idx + k, dst);
+}
+
+// Staging of this wave's 8 rows.  Lane L holds chunks (L % 8) + 8 i of row
+// r = L / 8 (copies i = 0..5).  Copies 0..3 are NoPE codes (dims 16 c ..
+// 16 c + 15, scale group i): dequantised into 32 bytes of the staged row.
+// Chunk 32 is the scale block; chunks 33..40 are RoPE (bf16 already): moved to
+// bytes 1024 + 16 (c - 33) of the staged row.
+__device__ __forceinline__ void stage_rows(LDS_AS uint8_t* lds, int slice, int kb, int wave, int lane) {
+    const int r = lane >> 3, c0 = lane & 7;
+    u32x4 w[4];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
+        sc[i] = *(const LDS_AS float*)(lds + slice + raw_off(r, 32) + 4 * i);
+    }
+    const u32x4 rope = lds_read16(lds, slice + raw_off(r, c0 ? 32 + c0 : 40));
+    const int row = kb + (WROWS * wave + r) * KP;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 lo = {dequant2<false>(w[i][0], sc[i]), dequant2<true>(w[i][0], sc[i]),
+                          dequant2<false>(w[i][1], sc[i]), dequant2<true>(w[i][1], sc[i])};
+        const u32x4 hi = {dequant2<false>(w[i][2], sc[i]), dequant2<true>(w[i][2], sc[i]),
+                          dequant2<false>(w[i][3], sc[i]), dequant2<true>(w[i][3], sc[i])};
+        const int off = row + 32 * (c0 + 8 * i);
+        lds_write16(lds, off, lo);
+        lds_write16(lds, off + 16, hi);
+    }
+    // lane c0 = 0 holds the scale chunk (32) in copy 4 and RoPE chunk 40 in copy 5
+    lds_write16(lds, row + 1024 + 16 * (c0 ? c0 - 1 : 7), rope);
+}
+
+// Value operand (V^T fragment) of the transposing LDS read, 32 dims x 16 keys
+// of k-step t.  In each 16-lane group, provider lane 4q + b points at the
+// 8-byte row of key 16t + s(q) + 2h + r (s = 0, 8, 4, 12; h = lane / 32;
+// r = 0 for the first read, 1 for the second) at dims 16((lane/16)%2) + 4b;
+// receiver lane l then holds dim l%32 of keys s(q) + 2h + r as element
+// 4r + q.  Rows are 1040 bytes apart, so each half-wave's 32 providers hit 32
+// distinct 8-byte bank pairs.  P is laid out in the same key order.
+__device__ __forceinline__ int pv_base(int lane) {
+    const int q = (lane & 15) >> 2;
+    const int key = 8 * (q & 1) + 4 * (q >> 1) + 2 * (lane >> 5);
+    const int dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    return key * KP + 2 * dim;
+}
+__device__ __forceinline__ bf16x8 v_frag(const LDS_AS uint8_t* lds, int off) {
+    const u32x2 r0 = lds_read_tr16(lds, off);
+    const u32x2 r1 = lds_read_tr16(lds, off + KP);
+    return __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
+}
+
+// P of k-step t as the value contraction's B operand.  The score accumulator
+// gives lane (head n, half h) keys 16t + 4h + e and 16t + 8 + 4h + e; pair_e
+// packs those two.  Element 4r + q of the operand must be key s(q) + 2h + r,
+// i.e. dwords {pair_2h of half 0, pair_2h of half 1, pair_2h+1 of half 0,
+// pair_2h+1 of half 1}: two half-wave swaps produce exactly that.
+__device__ __forceinline__ u32x4 p_fragment(const f32x16& p, int t) {
+    uint32_t pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = pack_bf16(p[8 * t + e], p[8 * t + 4 + e]);
+    const auto a = __builtin_amdgcn_permlane32_swap(pr[0], pr[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(pr[1], pr[3], false, false);
+    return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// Offset of the score A operand for k-step j: dims 288 dh + 16 j + 8 h .. +7
+// of key n in the staged tile.
+__device__ __forceinline__ int qk_base(int lane, int dh) {
+    return (lane & 31) * KP + 576 * dh + 16 * (lane >> 5);
+}
+
+__device__ __forceinline__ int opaque_lane() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
+__global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
+
+    const int part = xcd_part(blockIdx.x, gridDim.x), sq = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int dh = wave & 1;
+
+    const int32_t* meta = p.sched_meta + 8 * part;
+    const int begin_req = meta[0];
+    if (begin_req >= p.b) return;
+    const int end_req = meta[1], begin_block = meta[2], end_block = meta[3];
+    const int begin_split = meta[4];
+    const int nblocks = (p.topk + p.block - 1) / p.block;
+
+    const uint32_t lds0 = lds_u32(lds);
+    const uint32_t ids_wave = lds0 + L_IDS + wave * IDS_SLOTS * 128;
+    const int slice_off = L_RAW + wave * WAVE_RAW;            // this wave's slice in raw tile 0
+    if (threadIdx.x < 4) lds[L_FLAGS + threadIdx.x] = 0;   // ordered by the first barrier
+
+    for (int req = begin_req; req <= end_req; ++req) {
+        const int blk_lo = req == begin_req ? begin_block : 0;
+        const int blk_hi = req == end_req ? end_block : nblocks;
+        const int k_lo = blk_lo * p.block;
+        const int k_hi = min(blk_hi * p.block, p.topk);
+        const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
+        const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+
+        // ids of `tile` (copied earlier into its slot): validity mask of the
+        // tile's 32 keys and the copy source of this lane's row (key
+        // 8w + ln / 8, chunk ln % 8); tiles past the piece copy zero rows
+        auto tile_rows = [&](int tile, int ln, const uint8_t*& src) -> uint32_t {
+            const LDS_AS int32_t* slot =
+                (const LDS_AS int32_t*)(lds + L_IDS + (wave * IDS_SLOTS + tile % IDS_SLOTS) * 128);
+            const int kn = ln & 31, kr = WROWS * wave + (ln >> 3);
+            const int k0 = k_lo + tile * TILE;
+            const uint8_t* a;
+            const bool ok = token_addr(p, slot[kn], tile < n_tiles && k0 + kn < k_hi, 0, a);
+            token_addr(p, slot[kr], tile < n_tiles && k0 + kr < k_hi, (tile * TILE + kr) & (ZERO_ROWS - 1), a);
+            src = a + 16 * (ln & 7);
+            return (uint32_t)__ballot(ok);
+        };
+
+        // Q as B operands: qa = this wave's own heads 32w + n, qb = the partner
+        // wave's heads; k-step j covers dims 288 dh + 16 j + 8 h .. +7
+        bf16x8 qa[18], qb[18];
+        f32x16 O[16];
+        float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
+        for (int pass = 0;; ++pass) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) O[i] = f32x16{};
+            l_part = 0.f;
+            __syncthreads();                        // LDS free (previous piece / pass done)
+
+            // ---- prologue: ids of tiles 0..2; copies of tiles 0..2 with the
+            // ids of tiles 3 and 4 in the steady-state order; then Q; stage tile 0
+            for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, lane, ids_wave + 128 * t);
+            wait_vmcnt<0>();
+            uint32_t vm0 = 0, vm1 = 0, vm2 = 0;
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                const uint8_t* src;
+                const uint32_t vm = tile_rows(t, lane, src);
+                if (t == 0) vm0 = vm;
+                if (t == 1) vm1 = vm;
+                if (t == 2) vm2 = vm;
+                gather_rows(src, lane, lds0 + slice_off + t * RAW_BYTES);
+                if (t >= 1) copy_ids(idx, k_lo, k_hi, t + 2, lane, ids_wave + 128 * ((t + 2) % IDS_SLOTS));
+            }
+            {
+                const uint16_t* qbase = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss + 288 * dh + 8 * h;
+                const uint16_t* q_own = qbase + (int64_t)(32 * wave + n) * p.q_sh;
+                const uint16_t* q_oth = qbase + (int64_t)(32 * (wave ^ 1) + n) * p.q_sh;
+#pragma unroll
+                for (int j = 0; j < 18; ++j) {
+                    qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
+                    qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_oth + 16 * j));
+                }
+            }
+            wait_vmcnt<14>();                       // own copies of tile 0 (at least 14 newer ops)
+            stage_rows(lds, slice_off, L_KB, wave, lane);
+            __syncthreads();
+
+            // ---- tile loop: phase 1 S(t); phase 2 softmax(t) | PV(t-1) | copies
+            // of t+3; phase 3 P(t) and staging of t+1
+            bool restart = false;
+
+            // phase 1: S^T partials of tile t; the partner's heads go to the partner
+            auto scores = [&](int t, int ln) -> f32x16 {
+                const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
+                f32x16 S0, S1;
+                constexpr int AHEAD = 3;
+                bf16x8 a[AHEAD];
+#pragma unroll
+                for (int j = 0; j < AHEAD; ++j)
+                    a[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+#pragma unroll
+                for (int j = 0; j < 18; ++j) {
+                    const bf16x8 cur = a[j % AHEAD];
+                    if (j + AHEAD < 18)
+                        a[j % AHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (j + AHEAD)));
+                    if (j == 0) {
+                        mfma_qk_first(S0, cur, qa[0]);
+                        mfma_qk_first(S1, cur, qb[0]);
+                    } else {
+                        mfma_qk(S0, cur, qa[j]);
+                        mfma_qk(S1, cur, qb[j]);
+                    }
+                    // keep the reads AHEAD steps in front of their MFMAs
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                mfma_result_fence2(S0, S1);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const f32x4 v = {S1[4 * c], S1[4 * c + 1], S1[4 * c + 2], S1[4 * c + 3]};
+                    *(LDS_AS f32x4*)(lds + L_XS + (wave ^ 1) * 4096 + 1024 * c + 16 * ln) = v;
+                }
+                return S0;
+            };
+            // phase 2: softmax of tile ts (add the partner's partial, mask empty
+            // slots, base-2 softmax against the reference max, P fragments of both
+            // k-steps), in six pieces; with `pv` the value MFMAs of tile ts - 1
+            // (O^T += V^T P^T) run in eight steps between them.  Scheduling fences
+            // keep each piece between two MFMA groups.
+            auto softmax_values = [&](f32x16 S, uint32_t vm, int ts, int ln, bool pv, u32x4& pf0, u32x4& pf1) {
+                const int kb = L_KB + ((ts - 1) & 1) * KBB;
+                const int vb = kb + pv_base(ln) + 64 * 4 * wave;
+                bf16x8 pf[4], a_cur, a_nxt;
+                f32x4 xs[4];
+                float mx = -INFINITY, psum = 0.f;
+                auto piece = [&](int k) {
+                    if (k == 0) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            xs[c] = *(const LDS_AS f32x4*)(lds + L_XS + wave * 4096 + 1024 * c + 16 * ln);
+                    } else if (k == 1) {
+                        // accumulator element v holds key 8(v/4) + 4h + v%4: lanes 0..31
+                        // test bit 8(v/4) + v%4 of the tile mask, lanes 32..63 that + 4
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            S[v] += xs[v >> 2][v & 3];
+                            const int key = 8 * (v >> 2) + (v & 3);
+                            const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
+                                                   ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
+                            S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
+                            mx = fmaxf(mx, S[v]);
+                        }
+                    } else if (k == 2) {
+                        mx = fmaxf(mx, __shfl_xor(mx, 32));
+                        const float mnew = mx * p.c;
+                        m_seen = fmaxf(m_seen, mnew);
+                        if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                        restart |= __any(mnew > m_ref + p.threshold);
+                    } else if (k == 3 || k == 4) {
+#pragma unroll
+                        for (int v = 8 * (k - 3); v < 8 * (k - 2); ++v) {
+                            S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
+                            psum += S[v];
+                        }
+                    } else if (k == 5) {
+                        l_part += psum;
+                        pf0 = p_fragment(S, 0);
+                        pf1 = p_fragment(S, 1);
+                    }
+                };
+                if (pv) {
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb)
+                        pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
+                    a_cur = v_frag(lds, vb);
+                }
+                piece(0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    if (pv) {
+                        const int j = s & 3;
+                        if (s + 1 < 8) a_nxt = v_frag(lds, vb + ((s + 1) >> 2) * 16 * KP + ((s + 1) & 3) * 64);
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * j + hb], a_cur, pf[hb]);
+                        if (s == 3) {
+#pragma unroll
+                            for (int hb = 0; hb < 4; ++hb)
+                                pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                        }
+                        if (s + 1 < 8) a_cur = a_nxt;
+                    }
+                    if (s + 1 <= 5) piece(s + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            // value MFMAs of the last tile (no softmax left)
+            auto values_only = [&](int t, int ln) {
+                const int kb = L_KB + (t & 1) * KBB;
+                const int vb = kb + pv_base(ln) + 64 * 4 * wave;
+                bf16x8 pf[4];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb)
+                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
+                bf16x8 a_cur = v_frag(lds, vb);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int j = s & 3;
+                    bf16x8 a_nxt;
+                    if (s + 1 < 8) a_nxt = v_frag(lds, vb + ((s + 1) >> 2) * 16 * KP + ((s + 1) & 3) * 64);
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * j + hb], a_cur, pf[hb]);
+                    if (s == 3) {
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb)
+                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                    }
+                    if (s + 1 < 8) a_cur = a_nxt;
+                }
+            };
+            // phase 3: P(t) for every wave's value MFMAs, stage tile t+1
+            auto publish_and_stage = [&](int t, int ln, const u32x4& pf0, const u32x4& pf1) {
+                lds_write16(lds, L_XP + wave * 2048 + 16 * ln, pf0);
+                lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, pf1);
+                if (t + 1 < n_tiles) {
+                    const int slice_next = slice_off + ((t + 1) % NRAW) * RAW_BYTES;
+                    const int kb_next = L_KB + ((t + 1) & 1) * KBB;
+                    stage_rows(lds, slice_next, kb_next, wave, ln);
+                }
+            };
+
+            // tile 0: no value work yet
+            {
+                const int ln = opaque_lane();
+                f32x16 S = scores(0, ln);
+                __syncthreads();
+                wait_vmcnt<7>();                    // own copies of tile 1, ids of tile 3
+                const uint8_t* src3;
+                const uint32_t vm3 = tile_rows(3, ln, src3);
+                u32x4 pf0, pf1;
+                softmax_values(S, vm0, 0, ln, false, pf0, pf1);
+                gather_rows(src3, ln, lds0 + slice_off + (3 % NRAW) * RAW_BYTES);
+                copy_ids(idx, k_lo, k_hi, 5, ln, ids_wave + 128 * (5 % IDS_SLOTS));
+                __syncthreads();
+                publish_and_stage(0, ln, pf0, pf1);
+                vm0 = vm1;
+                vm1 = vm2;
+                vm2 = vm3;
+                __syncthreads();
+            }
+            for (int it = 1; it < n_tiles; ++it) {
+                // lane-derived offsets are recomputed every tile (cheap VALU)
+                // rather than held in registers across the loop
+                const int ln = opaque_lane();
+                f32x16 S = scores(it, ln);
+                __syncthreads();
+                u32x4 pf0, pf1;
+                softmax_values(S, vm0, it, ln, true, pf0, pf1);
+                // own copies of tile it+1 and the ids of tile it+3 have landed
+                // (7 newer ops: copies of it+2, ids of it+4)
+                wait_vmcnt<7>();
+                const uint8_t* src3;
+                const uint32_t vm3 = tile_rows(it + 3, ln, src3);
+                gather_rows(src3, ln, lds0 + slice_off + ((it + 3) % NRAW) * RAW_BYTES);
+                copy_ids(idx, k_lo, k_hi, it + 5, ln, ids_wave + 128 * ((it + 5) % IDS_SLOTS));
+                __syncthreads();
+                publish_and_stage(it, ln, pf0, pf1);
+                vm0 = vm1;
+                vm1 = vm2;
+                vm2 = vm3;
+                __syncthreads();
+            }
+            values_only(n_tiles - 1, opaque_lane());
+            if (lane == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
+            __syncthreads();
+            wait_vmcnt<0>();                                    // copies past the piece
+            // A score exceeded the reference by more than 2^threshold in some
+            // wave: recompute the piece against the true max (rare).
+            const uint32_t flags = *(const LDS_AS uint32_t*)(lds + L_FLAGS);
+            __syncthreads();
+            if (flags == 0u || pass > 0) break;
+            if (threadIdx.x < 4) lds[L_FLAGS + threadIdx.x] = 0;
+            m_ref = m_seen;
+        }
+
+        // ---- epilogue: l and m of every head through LDS
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[i]));
+        const float l_tot = l_part + __shfl_xor(l_part, 32);
+        if (lane < 32) *(LDS_AS f32x2*)(lds + L_LM + 8 * (32 * wave + n)) = f32x2{l_tot, m_ref};
+        __syncthreads();
+        float inv[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            const float l = *(const LDS_AS float*)(lds + L_LM + 8 * (32 * hb + n));
+            inv[hb] = l > 0.f ? 1.0f / l : 0.f;
+        }
+        const int nsplit = p.num_splits[req + 1] - p.num_splits[req];
+        const int own_head = 32 * wave + n;
+        if (nsplit == 1) {
+            uint16_t* obase = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+                uint16_t* orow = obase + (int64_t)(32 * hb + n) * p.out_sh + 128 * wave + 4 * h;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& o = O[4 * j + hb];
+                        const u32x2 w = {pack_bf16(o[4 * g] * inv[hb], o[4 * g + 1] * inv[hb]),
+                                         pack_bf16(o[4 * g + 2] * inv[hb], o[4 * g + 3] * inv[hb])};
+                        *(u32x2*)(orow + 32 * j + 8 * g) = w;
+                    }
+            }
+            if (h == 0)
+                p.lse[((int64_t)req * p.h_q + own_head) * p.s_q + sq] =
+                    l_tot > 0.f ? (__log2f(l_tot) + m_ref) * 0.69314718055994531f : INFINITY;
+        } else {
+            const int split = req == begin_req ? begin_split : p.num_splits[req];
+            const int64_t row0 = ((int64_t)split * p.s_q + sq) * p.h_q;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+                float* orow = p.o_accum + (row0 + 32 * hb + n) * 512 + 128 * wave + 4 * h;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& o = O[4 * j + hb];
+                        *(f32x4*)(orow + 32 * j + 8 * g) =
+                            f32x4{o[4 * g] * inv[hb], o[4 * g + 1] * inv[hb], o[4 * g + 2] * inv[hb], o[4 * g + 3] * inv[hb]};
+                    }
+            }
+            if (h == 0) p.lse_accum[row0 + own_head] = l_tot > 0.f ? __log2f(l_tot) + m_ref : -INFINITY;
+        }
+        __syncthreads();                                       // head statistics read
+    }
+}
+
+// Test hook: gathers and stages every tile exactly as the decode kernel does
+// and reads the operands back through its two read paths (score A operands
+// for K, transposing reads for V).  Rows of empty slots are the zero page.
+__global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParams p, uint16_t* k_rows,
+                                                                     uint16_t* v_rows) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
+    LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
+    const int qi = blockIdx.x;                    // query token = req * s_q + sq
+    const int req = qi / p.s_q, sq = qi % p.s_q;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 31, h = lane >> 5;
+    const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+    const int n_tiles = (p.topk + TILE - 1) / TILE;
+    const uint32_t lds0 = lds_u32(lds);
+    const int slice_off = L_RAW + wave * WAVE_RAW;
+    const LDS_AS int32_t* slot = (const LDS_AS int32_t*)(lds + L_IDS + wave * IDS_SLOTS * 128);
+    for (int it = 0; it < n_tiles; ++it) {
+        __syncthreads();
+        copy_ids(idx, 0, p.topk, it, lane, lds0 + L_IDS + wave * IDS_SLOTS * 128);
+        wait_vmcnt<0>();
+        const int kr = WROWS * wave + (lane >> 3);
+        const uint8_t* a;
+        const bool ok = token_addr(p, slot[n], it * TILE + n < p.topk, 0, a);
+        token_addr(p, slot[kr], it * TILE + kr < p.topk, kr, a);
+        const uint32_t vm = (uint32_t)__ballot(ok);
+        gather_rows(a + 16 * (lane & 7), lane, lds0 + slice_off);
+        wait_vmcnt<0>();
+        stage_rows(lds, slice_off, L_KB, wave, lane);
+        __syncthreads();
+        const int key = it * TILE + n;
+        if (wave < 2 && key < p.topk) {
+            const int qk = L_KB + qk_base(lane, wave);
+            uint16_t* dst = k_rows + ((int64_t)qi * p.topk + key) * 576 + 288 * wave + 8 * h;
+            const bool kok = (vm >> n) & 1u;
+            for (int j = 0; j < 18; ++j) {
+                u32x4 v = lds_read16(lds, qk + 32 * j);
+                if (!kok) v = u32x4{0, 0, 0, 0};
+                *(u32x4*)(dst + 16 * j) = v;
+            }
+        }
+        if (v_rows != nullptr && wave >= 2) {
+            const int vb = L_KB + pv_base(lane);
+            for (int mb = 8 * (wave - 2); mb < 8 * (wave - 1); ++mb) {
+                for (int tt = 0; tt < 2; ++tt) {
+                    const u32x4 r = __builtin_bit_cast(u32x4, v_frag(lds, vb + tt * 16 * KP + mb * 64));
+                    for (int e = 0; e < 8; ++e) {
+                        const int q = e & 3, rr = e >> 2;
+                        const int k = it * TILE + 16 * tt + 8 * (q & 1) + 4 * (q >> 1) + 2 * h + rr;
+                        if (k < p.topk) {
+                            const uint16_t val = (uint16_t)(r[e >> 1] >> (16 * (e & 1)));
+                            v_rows[((int64_t)qi * p.topk + k) * 512 + 32 * mb + n] = val;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+bool g_lds_decode = false, g_lds_gather = false;
+
+template <typename K>
+hipError_t allow_lds_once(K k, bool& done) {
+    if (done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, L_BYTES);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
+    hipError_t e = allow_lds_once(decode_fp8_h128_kernel, g_lds_decode);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_fp8_h128_kernel, dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows, hipStream_t st) {
+    hipError_t e = allow_lds_once(gather_fp8_h128_kernel, g_lds_gather);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gather_fp8_h128_kernel, dim3(p.b * p.s_q), dim3(NW * 64), L_BYTES, st, p, k_rows, v_rows);
+    return hipGetLastError();
+}
+
+}  // namespace mla

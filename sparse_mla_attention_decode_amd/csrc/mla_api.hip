@@ -159,6 +159,9 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     p->h_q = r.h_q;
     p->topk = r.topk;
     p->page_block_size = r.page_block_size;
+    p->page_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == r.page_block_size) p->page_shift = sh;
     p->block = r.block;
     p->c = sm * 1.4426950408889634f;
     p->threshold = mla::kRefGapLog2;

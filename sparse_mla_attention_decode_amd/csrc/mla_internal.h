@@ -34,6 +34,7 @@ struct DecodeParams {
     float* lse_accum;
     int64_t n_tok;
     int b, s_q, h_q, topk, page_block_size, block;
+    int page_shift;                 // log2(page_block_size) when a power of two, else -1
     float c;                        // sm_scale * log2(e)
     float threshold;                // log2-units gap above the reference max that
                                     // makes a piece recompute with a higher reference
@@ -46,6 +47,9 @@ constexpr float kRefGapLog2 = 64.0f;
 
 hipError_t launch_sched(const ResolvedShape& s, int32_t* meta, int32_t* prefix, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st);
+hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st);
+hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows,
+                                  hipStream_t st);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t st);
 hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows, uint16_t* v_rows,
                          hipStream_t st);

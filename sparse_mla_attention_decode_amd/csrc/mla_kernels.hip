@@ -32,22 +32,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "mla_internal.h"
 #include "sched_plan.h"
 
 namespace mla {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr int TILE = 32;                   // keys per tile
 constexpr int KROW = 1168;                 // LDS bytes per staged bf16 K row (1152 + 16 pad)
 constexpr int KB_BYTES = TILE * KROW;      // 37376
 
@@ -77,69 +67,7 @@ template <int FMT, int NW> struct Lds {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-constexpr float INIT_MAX = -1e30f;
 
-// ----------------------------------------------------------------------------
-// small helpers
-// ----------------------------------------------------------------------------
-__device__ __forceinline__ u32x4 lds_read16(const LDS_AS uint8_t* base, int off) {
-    return *(const LDS_AS u32x4*)(base + off);
-}
-__device__ __forceinline__ void lds_write16(LDS_AS uint8_t* base, int off, u32x4 v) {
-    *(LDS_AS u32x4*)(base + off) = v;
-}
-
-// Transposing LDS read: in each group of 16 lanes, lane 4b+c receives column c
-// (16-bit) of the 8-byte rows addressed by lanes b, b+4, b+8, b+12.
-__device__ __forceinline__ u32x2 lds_read_tr16(const LDS_AS uint8_t* base, int off) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(base + off));
-    return __builtin_bit_cast(u32x2, v);
-}
-
-// two e4m3fn codes (bytes 2*HI, 2*HI+1 of w) times a power-of-two scale -> two
-// bf16 packed in a dword; the product is exact.
-template <bool HI>
-__device__ __forceinline__ uint32_t dequant2(uint32_t w, float scale) {
-    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    bf16x2 r = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-// MFMA helpers with explicit register classes.  At occupancy 1 a wave owns
-// 256 VGPRs + 256 AGPRs: the output accumulator takes all AGPRs, Q (144),
-// the score accumulator and everything else live in VGPRs.  Without the
-// constraints the compiler puts every accumulator in AGPRs and spills.
-__device__ __forceinline__ void mfma_qk_first(f32x16& s, const bf16x8& a, const bf16x8& q) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(q));
-}
-__device__ __forceinline__ void mfma_qk(f32x16& s, const bf16x8& a, const bf16x8& q) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(q));
-}
-__device__ __forceinline__ void mfma_pv(f32x16& o, const bf16x8& a, const bf16x8& pm) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(pm));
-}
-// The hazard recognizer does not look inside inline asm.  These fences wait
-// out the MFMA result latency before VALU reads an accumulator, and the VALU
-// write -> MFMA operand read latency before freshly computed P is consumed.
-__device__ __forceinline__ void mfma_result_fence(f32x16& s) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s));
-}
-__device__ __forceinline__ void valu_to_mfma_fence(bf16x8& a, bf16x8& b) {
-    asm volatile("s_nop 4" : "+v"(a), "+v"(b));
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
 
 // ----------------------------------------------------------------------------
 // scheduler
@@ -285,15 +213,6 @@ __device__ __forceinline__ const uint8_t* row_ptr(const DecodeParams& p, int t) 
     return p.kv + (int64_t)t * p.kv_block_stride;
 }
 
-// Direct-to-LDS copy of 16 bytes per lane: lane i's bytes land at
-// lds_addr + 16 i.  Written as inline asm so the compiler's wait-count pass
-// does not treat every later LDS read as possibly aliasing the copy (it would
-// drain all copies in flight); the decode loop orders the copies itself with
-// an explicit vmcnt wait and a barrier before the copied bytes are read.
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
-}
 
 // Row address (as two dwords) of slot `key` of the piece for lanes 0..31; slots
 // that are empty, beyond k_end, or outside the cache get the cache base (a
@@ -432,12 +351,6 @@ __device__ __forceinline__ int pv_read_base(int lane) {
     return key * KROW + 2 * dim;
 }
 
-// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int FMT, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
@@ -792,7 +705,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, hipStrea
 
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
     if (kv_format == MLA_KV_FP8_656)
-        return p.h_q == 128 ? launch_decode_t<MLA_KV_FP8_656, 4>(p, num_parts, st)
+        return p.h_q == 128 ? launch_decode_fp8_h128(p, num_parts, st)
                             : launch_decode_t<MLA_KV_FP8_656, 2>(p, num_parts, st);
     return p.h_q == 128 ? launch_decode_t<MLA_KV_BF16_576, 4>(p, num_parts, st)
                         : launch_decode_t<MLA_KV_BF16_576, 2>(p, num_parts, st);
@@ -812,6 +725,7 @@ static hipError_t launch_gather_t(const DecodeParams& p, uint16_t* k_rows, uint1
 
 hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows, uint16_t* v_rows,
                          hipStream_t st) {
+    if (kv_format == MLA_KV_FP8_656 && p.h_q == 128) return launch_gather_fp8_h128(p, k_rows, v_rows, st);
     return kv_format == MLA_KV_FP8_656 ? launch_gather_t<MLA_KV_FP8_656>(p, k_rows, v_rows, st)
                                        : launch_gather_t<MLA_KV_BF16_576>(p, k_rows, v_rows, st);
 }
