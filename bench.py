@@ -149,7 +149,7 @@ def main():
                    "step": "sched + decode + combine"},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "decode_kernel<fp8,4 waves>", "kernel_ms": decode_ms,
+                     "kernel": "decode_fp8_h128_kernel", "kernel_ms": decode_ms,
                      "algorithmic_flop_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
                      "hbm_achieved_GBs": bytes_ / (decode_ms * 1e-3) / 1e9},
         "step_roofline_frac": t_roof_ms / ms_per_step,

@@ -25,9 +25,10 @@
 //            O^T [128 dims x 128 heads] lives in the 256 AGPRs.
 //
 // Tile loop, three phases per tile t separated by work-group barriers:
-//   1. S^T(t) MFMAs; partner partial -> LDS;
-//   2. softmax(t) and the address/copy work for tile t+3, interleaved with
-//      the value MFMAs of tile t-1 (one branch-free scheduling region);
+//   1. S^T(t) MFMAs with the address/copy work for tile t+3 between them;
+//      partner partial -> LDS;
+//   2. softmax(t) interleaved with the value MFMAs of tile t-1 (one
+//      branch-free scheduling region);
 //   3. P(t) -> LDS and staging of tile t+1;
 // so the VALU work of the softmax runs under matrix-core work.
 //
@@ -109,10 +110,7 @@ __device__ __forceinline__ bool token_addr(const DecodeParams& p, int t, bool in
 
 // Copies of this wave's 8 rows of a tile into its raw slice; `src` points at
 // chunk lane % 8 of row lane / 8 (key 8w + lane / 8).
-__device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, uint32_t slice) {
-#pragma unroll
-    for (int i = 0; i < NDMA - 1; ++i)
-        dma16(src + 128 * i, __builtin_amdgcn_readfirstlane(slice + 1024u * i));
+__device__ __forceinline__ void gather_tail(const uint8_t* src, int lane, uint32_t slice) {
     // chunk 40 of row `lane` (lanes 0..7): row starts are held by lanes 8 r
     const uint64_t row = (uint64_t)(uintptr_t)(src - 16 * (lane & 7));
     const int from = 8 * (lane & 7);
@@ -120,6 +118,12 @@ __device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, uint32
                         (uint32_t)__shfl((uint32_t)row, from);
     const uint32_t dst = __builtin_amdgcn_readfirstlane(slice + 1024u * (NDMA - 1));
     if (lane < 8) dma16((const uint8_t*)(uintptr_t)rl + 16 * 40, dst);
+}
+__device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, uint32_t slice) {
+#pragma unroll
+    for (int i = 0; i < NDMA - 1; ++i)
+        dma16(src + 128 * i, __builtin_amdgcn_readfirstlane(slice + 1024u * i));
+    gather_tail(src, lane, slice);
 }
 
 // Copy the 32 token ids of a tile (clamped to the piece) into an id slot.
@@ -197,6 +201,15 @@ __device__ __forceinline__ u32x4 p_fragment(const f32x16& p, int t) {
 // of key n in the staged tile.
 __device__ __forceinline__ int qk_base(int lane, int dh) {
     return (lane & 31) * KP + 576 * dh + 16 * (lane >> 5);
+}
+
+// Packed split partials: for split s and query column sq, 128 KB of bf16 laid
+// out as [wave 4][k 32][lane 64][8 bf16], where k = 2 i + half holds elements
+// 8 half .. 8 half + 7 of the lane's output block i = 4 j + hb (head
+// 32 hb + lane % 32, dims 128 wave + 32 j + 8 (e / 4) + 4 (lane / 32) + e % 4
+// for element e).  Every store and load of a wave moves 1 KB contiguously.
+__device__ __forceinline__ u32x4* packed_partial(const DecodeParams& p, int split, int sq) {
+    return (u32x4*)((uint16_t*)p.o_accum + ((int64_t)split * p.s_q + sq) * (128 * 512));
 }
 
 __device__ __forceinline__ int opaque_lane() {
@@ -294,8 +307,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             bool restart = false;
 
             // phase 1: S^T partials of tile t; the partner's heads go to the partner
-            auto scores = [&](int t, int ln) -> f32x16 {
+            // The copies of tile t + 3 (into the raw buffer staging of tile t
+            // emptied) and the ids of tile t + 5 ride between the MFMAs, one
+            // memory instruction every few steps, so the queue never fills.
+            auto scores = [&](int t, int ln, uint32_t& vm3) -> f32x16 {
                 const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
+                // own copies of tile t+1 and the ids of tile t+3 have landed
+                // (7 newer ops: copies of t+2, ids of t+4)
+                wait_vmcnt<7>();
+                const uint8_t* src3 = nullptr;
+                const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
                 f32x16 S0, S1;
                 constexpr int AHEAD = 3;
                 bf16x8 a[AHEAD];
@@ -314,6 +335,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         mfma_qk(S0, cur, qa[j]);
                         mfma_qk(S1, cur, qb[j]);
                     }
+                    if (j == 0) vm3 = tile_rows(t + 3, ln, src3);
+                    if (j >= 2 && j <= 14 && j % 3 == 2)
+                        dma16(src3 + 128 * (j / 3), __builtin_amdgcn_readfirstlane(slice3 + 1024u * (j / 3)));
+                    if (j == 16) gather_tail(src3, ln, slice3);
+                    if (j == 17) copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
                     // keep the reads AHEAD steps in front of their MFMAs
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -435,15 +461,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // tile 0: no value work yet
             {
                 const int ln = opaque_lane();
-                f32x16 S = scores(0, ln);
+                uint32_t vm3;
+                f32x16 S = scores(0, ln, vm3);
                 __syncthreads();
-                wait_vmcnt<7>();                    // own copies of tile 1, ids of tile 3
-                const uint8_t* src3;
-                const uint32_t vm3 = tile_rows(3, ln, src3);
                 u32x4 pf0, pf1;
                 softmax_values(S, vm0, 0, ln, false, pf0, pf1);
-                gather_rows(src3, ln, lds0 + slice_off + (3 % NRAW) * RAW_BYTES);
-                copy_ids(idx, k_lo, k_hi, 5, ln, ids_wave + 128 * (5 % IDS_SLOTS));
                 __syncthreads();
                 publish_and_stage(0, ln, pf0, pf1);
                 vm0 = vm1;
@@ -455,17 +477,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // lane-derived offsets are recomputed every tile (cheap VALU)
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
-                f32x16 S = scores(it, ln);
+                uint32_t vm3;
+                f32x16 S = scores(it, ln, vm3);
                 __syncthreads();
                 u32x4 pf0, pf1;
                 softmax_values(S, vm0, it, ln, true, pf0, pf1);
-                // own copies of tile it+1 and the ids of tile it+3 have landed
-                // (7 newer ops: copies of it+2, ids of it+4)
-                wait_vmcnt<7>();
-                const uint8_t* src3;
-                const uint32_t vm3 = tile_rows(it + 3, ln, src3);
-                gather_rows(src3, ln, lds0 + slice_off + ((it + 3) % NRAW) * RAW_BYTES);
-                copy_ids(idx, k_lo, k_hi, it + 5, ln, ids_wave + 128 * ((it + 5) % IDS_SLOTS));
                 __syncthreads();
                 publish_and_stage(it, ln, pf0, pf1);
                 vm0 = vm1;
@@ -519,19 +535,21 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 p.lse[((int64_t)req * p.h_q + own_head) * p.s_q + sq] =
                     l_tot > 0.f ? (__log2f(l_tot) + m_ref) * 0.69314718055994531f : INFINITY;
         } else {
+            // normalised partial O/l as bf16 in the lanes' own layout (packed
+            // partials, see combine_packed_kernel) and lse in base 2
             const int split = req == begin_req ? begin_split : p.num_splits[req];
             const int64_t row0 = ((int64_t)split * p.s_q + sq) * p.h_q;
+            u32x4* dst = packed_partial(p, split, sq) + (int64_t)wave * 32 * 64 + lane;
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
-                float* orow = p.o_accum + (row0 + 32 * hb + n) * 512 + 128 * wave + 4 * h;
+            for (int i = 0; i < 16; ++i) {
+                const f32x16& o = O[i];
+                const float sc = inv[i & 3];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x16& o = O[4 * j + hb];
-                        *(f32x4*)(orow + 32 * j + 8 * g) =
-                            f32x4{o[4 * g] * inv[hb], o[4 * g + 1] * inv[hb], o[4 * g + 2] * inv[hb], o[4 * g + 3] * inv[hb]};
-                    }
+                for (int half = 0; half < 2; ++half)
+                    dst[(2 * i + half) * 64] = u32x4{pack_bf16(o[8 * half] * sc, o[8 * half + 1] * sc),
+                                                     pack_bf16(o[8 * half + 2] * sc, o[8 * half + 3] * sc),
+                                                     pack_bf16(o[8 * half + 4] * sc, o[8 * half + 5] * sc),
+                                                     pack_bf16(o[8 * half + 6] * sc, o[8 * half + 7] * sc)};
             }
             if (h == 0) p.lse_accum[row0 + own_head] = l_tot > 0.f ? __log2f(l_tot) + m_ref : -INFINITY;
         }
@@ -598,6 +616,70 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
     }
 }
 
+// Split-KV combine over packed partials ("FlashMLA Sparse Decode 完整计算过程详解",
+// step 16): one wave per (query column, output block i = 4 j + hb of decode
+// wave w), 64 waves per column.  M = max_s lse_s (base 2), w_s = 2^(lse_s - M)
+// / sum, out = sum_s w_s O_s, lse = (M + log2 sum) ln 2; out 0 and lse +inf
+// when no split saw a valid key.  Loads of up to four splits are issued
+// together.
+__global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
+    const int qi = blockIdx.x, piece = blockIdx.y;          // piece = 16 w + 4 j + hb
+    const int req = qi / p.s_q, sq = qi % p.s_q;
+    const int first = p.num_splits[req];
+    const int ns = p.num_splits[req + 1] - first;
+    if (ns <= 1) return;
+    const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
+    const int w = piece >> 4, j = (piece >> 2) & 3, hb = piece & 3;
+    const int head = 32 * hb + n;
+    const float* lse_col = p.lse_accum + (int64_t)first * p.s_q * p.h_q + (int64_t)sq * p.h_q + head;
+    const int64_t lse_step = (int64_t)p.s_q * p.h_q;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = s0 + u < ns ? lse_col[(s0 + u) * lse_step] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) M = fmaxf(M, v[u]);
+    }
+    float W = 0.f;
+    f32x16 acc = {};
+    if (M != -INFINITY) {
+        const int64_t kofs = (int64_t)w * 32 * 64 + (2 * (4 * j + hb)) * 64 + lane;
+        for (int s0 = 0; s0 < ns; s0 += 4) {
+            float ws[4];
+            u32x4 raw[4][2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = min(s0 + u, ns - 1);
+                ws[u] = s0 + u < ns ? __builtin_amdgcn_exp2f(lse_col[s * lse_step] - M) : 0.f;
+                const u32x4* src = packed_partial(p, first + s, sq) + kofs;
+                raw[u][0] = src[0];
+                raw[u][1] = src[64];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                W += ws[u];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t word = raw[u][e >> 3][(e >> 1) & 3];
+                    const float x = __builtin_bit_cast(float, (e & 1) ? (word & 0xffff0000u) : (word << 16));
+                    acc[e] += ws[u] * x;
+                }
+            }
+        }
+    }
+    const float inv = W > 0.f ? 1.0f / W : 0.f;
+    uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh +
+                     128 * w + 32 * j + 4 * h;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        *(u32x2*)(orow + 8 * g) = u32x2{pack_bf16(acc[4 * g] * inv, acc[4 * g + 1] * inv),
+                                        pack_bf16(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv)};
+    if (w == 0 && j == 0 && h == 0)
+        p.lse[((int64_t)req * p.h_q + head) * p.s_q + sq] =
+            M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
+}
+
 bool g_lds_decode = false, g_lds_gather = false;
 
 template <typename K>
@@ -614,6 +696,11 @@ hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStrea
     hipError_t e = allow_lds_once(decode_fp8_h128_kernel, g_lds_decode);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_fp8_h128_kernel, dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_packed(const DecodeParams& p, hipStream_t st) {
+    hipLaunchKernelGGL(combine_packed_kernel, dim3(p.b * p.s_q, 64), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 

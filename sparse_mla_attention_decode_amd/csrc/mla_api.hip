@@ -162,6 +162,7 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     p->page_shift = -1;
     for (int sh = 0; sh < 31; ++sh)
         if ((1 << sh) == r.page_block_size) p->page_shift = sh;
+    p->packed_partials = r.kv_format == MLA_KV_FP8_656 && r.h_q == 128;
     p->block = r.block;
     p->c = sm * 1.4426950408889634f;
     p->threshold = mla::kRefGapLog2;

@@ -35,6 +35,7 @@ struct DecodeParams {
     int64_t n_tok;
     int b, s_q, h_q, topk, page_block_size, block;
     int page_shift;                 // log2(page_block_size) when a power of two, else -1
+    int packed_partials;            // split partials as packed bf16 (128-head FP8 decode)
     float c;                        // sm_scale * log2(e)
     float threshold;                // log2-units gap above the reference max that
                                     // makes a piece recompute with a higher reference
@@ -51,6 +52,7 @@ hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStrea
 hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows,
                                   hipStream_t st);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t st);
+hipError_t launch_combine_packed(const DecodeParams& p, hipStream_t st);
 hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows, uint16_t* v_rows,
                          hipStream_t st);
 

@@ -731,6 +731,8 @@ hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows,
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t st) {
+    // the 128-head FP8 decode writes packed bf16 partials (decode_h128.hip)
+    if (p.packed_partials) return launch_combine_packed(p, st);
     hipLaunchKernelGGL(combine_kernel, dim3(p.b * p.s_q, (p.h_q + 3) / 4), dim3(256), 0, st, p);
     return hipGetLastError();
 }
