@@ -95,17 +95,20 @@ __device__ __forceinline__ int xcd_part(int bid, int nb) {
     return x * q + min(x, r) + k;
 }
 
-// Row address of token t, or a zero row when the slot is empty (out of the
-// piece, -1, or outside the cache); returns whether the slot is valid.
-__device__ __forceinline__ bool token_addr(const DecodeParams& p, int t, bool in_range, int zrow,
-                                           const uint8_t*& a) {
-    const bool ok = in_range && t >= 0 && (int64_t)t < p.n_tok;
-    const int tt = ok ? t : 0;
-    const int blk = p.page_shift >= 0 ? (tt >> p.page_shift) : tt / p.page_block_size;
-    const int off = tt - blk * p.page_block_size;
-    const uint8_t* r = p.kv + (int64_t)blk * p.kv_block_stride + (int64_t)off * ROWB;
-    a = ok ? r : g_zero_rows + zrow * ROWB;
-    return ok;
+// Whether slot value t names a cache row (in the piece, not -1, inside the
+// cache); bitwise, so that no branch is generated.
+__device__ __forceinline__ bool slot_ok(const DecodeParams& p, int t, bool in_range) {
+    return in_range & ((uint32_t)t < p.n_tok32);
+}
+// Row address of token t when ok, else row zrow of the zero page.
+__device__ __forceinline__ const uint8_t* row_addr(const DecodeParams& p, int t, bool ok, int zrow) {
+    const uint32_t tt = ok ? (uint32_t)t : 0u;
+    const uint32_t blk = (__umulhi(tt, p.page_magic) + tt) >> p.page_mshift;
+    const uint32_t off = tt - blk * (uint32_t)p.page_block_size;
+    const uint64_t r = (uint64_t)(uintptr_t)p.kv + (uint64_t)blk * (uint64_t)p.kv_block_stride +
+                       (uint64_t)off * ROWB;
+    const uint64_t z = (uint64_t)(uintptr_t)g_zero_rows + (uint32_t)zrow * ROWB;
+    return (const uint8_t*)(uintptr_t)(ok ? r : z);
 }
 
 // Copies of this wave's 8 rows of a tile into its raw slice; `src` points at
@@ -138,30 +141,42 @@ __device__ __forceinline__ void copy_ids(const int32_t* idx, int k_lo, int k_hi,
 // r = L / 8 (copies i = 0..5).  Copies 0..3 are NoPE codes (dims 16 c ..
 // 16 c + 15, scale group i): dequantised into 32 bytes of the staged row.
 // Chunk 32 is the scale block; chunks 33..40 are RoPE (bf16 already): moved to
-// bytes 1024 + 16 (c - 33) of the staged row.
-__device__ __forceinline__ void stage_rows(LDS_AS uint8_t* lds, int slice, int kb, int wave, int lane) {
-    const int r = lane >> 3, c0 = lane & 7;
+// bytes 1024 + 16 (c - 33) of the staged row.  Split into the LDS reads and
+// the conversion + writes, so a caller can put other work between them.
+struct StageRegs {
     u32x4 w[4];
     float sc[4];
+    u32x4 rope;
+};
+__device__ __forceinline__ StageRegs stage_load(const LDS_AS uint8_t* lds, int slice, int lane) {
+    const int r = lane >> 3, c0 = lane & 7;
+    StageRegs g;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
-        sc[i] = *(const LDS_AS float*)(lds + slice + raw_off(r, 32) + 4 * i);
+        g.w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
+        g.sc[i] = *(const LDS_AS float*)(lds + slice + raw_off(r, 32) + 4 * i);
     }
-    const u32x4 rope = lds_read16(lds, slice + raw_off(r, c0 ? 32 + c0 : 40));
+    g.rope = lds_read16(lds, slice + raw_off(r, c0 ? 32 + c0 : 40));
+    return g;
+}
+__device__ __forceinline__ void stage_store(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
+    const int r = lane >> 3, c0 = lane & 7;
     const int row = kb + (WROWS * wave + r) * KP;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const u32x4 lo = {dequant2<false>(w[i][0], sc[i]), dequant2<true>(w[i][0], sc[i]),
-                          dequant2<false>(w[i][1], sc[i]), dequant2<true>(w[i][1], sc[i])};
-        const u32x4 hi = {dequant2<false>(w[i][2], sc[i]), dequant2<true>(w[i][2], sc[i]),
-                          dequant2<false>(w[i][3], sc[i]), dequant2<true>(w[i][3], sc[i])};
+        const u32x4 lo = {dequant2<false>(g.w[i][0], g.sc[i]), dequant2<true>(g.w[i][0], g.sc[i]),
+                          dequant2<false>(g.w[i][1], g.sc[i]), dequant2<true>(g.w[i][1], g.sc[i])};
+        const u32x4 hi = {dequant2<false>(g.w[i][2], g.sc[i]), dequant2<true>(g.w[i][2], g.sc[i]),
+                          dequant2<false>(g.w[i][3], g.sc[i]), dequant2<true>(g.w[i][3], g.sc[i])};
         const int off = row + 32 * (c0 + 8 * i);
         lds_write16(lds, off, lo);
         lds_write16(lds, off + 16, hi);
     }
     // lane c0 = 0 holds the scale chunk (32) in copy 4 and RoPE chunk 40 in copy 5
-    lds_write16(lds, row + 1024 + 16 * (c0 ? c0 - 1 : 7), rope);
+    lds_write16(lds, row + 1024 + 16 * (c0 ? c0 - 1 : 7), g.rope);
+}
+__device__ __forceinline__ void stage_rows(LDS_AS uint8_t* lds, int slice, int kb, int wave, int lane) {
+    stage_store(lds, stage_load(lds, slice, lane), kb, wave, lane);
 }
 
 // Value operand (V^T fragment) of the transposing LDS read, 32 dims x 16 keys
@@ -223,8 +238,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
 
     const int part = xcd_part(blockIdx.x, gridDim.x), sq = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = lane & 31, h = lane >> 5;
+    // wave-uniform values live in scalar registers; lane-derived offsets are
+    // recomputed where they are used (opaque_lane) instead of being held
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int dh = wave & 1;
 
     const int32_t* meta = p.sched_meta + 8 * part;
@@ -255,16 +271,29 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 (const LDS_AS int32_t*)(lds + L_IDS + (wave * IDS_SLOTS + tile % IDS_SLOTS) * 128);
             const int kn = ln & 31, kr = WROWS * wave + (ln >> 3);
             const int k0 = k_lo + tile * TILE;
-            const uint8_t* a;
-            const bool ok = token_addr(p, slot[kn], tile < n_tiles && k0 + kn < k_hi, 0, a);
-            token_addr(p, slot[kr], tile < n_tiles && k0 + kr < k_hi, (tile * TILE + kr) & (ZERO_ROWS - 1), a);
-            src = a + 16 * (ln & 7);
+            const bool ok = slot_ok(p, slot[kn], (tile < n_tiles) & (k0 + kn < k_hi));
+            const int tr = slot[kr];
+            const bool okr = slot_ok(p, tr, (tile < n_tiles) & (k0 + kr < k_hi));
+            src = row_addr(p, tr, okr, (tile * TILE + kr) & (ZERO_ROWS - 1)) + 16 * (ln & 7);
             return (uint32_t)__ballot(ok);
         };
 
-        // Q as B operands: qa = this wave's own heads 32w + n, qb = the partner
-        // wave's heads; k-step j covers dims 288 dh + 16 j + 8 h .. +7
+        // Q as B operands, loaded once per request: qa = this wave's own heads
+        // 32w + n, qb = the partner wave's heads; k-step j covers dims
+        // 288 dh + 16 j + 8 h .. +7
         bf16x8 qa[18], qb[18];
+        {
+            const int ln = opaque_lane();
+            for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
+            const uint16_t* qbase = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss + 288 * dh + 8 * (ln >> 5);
+            const uint16_t* q_own = qbase + (int64_t)(32 * wave + (ln & 31)) * p.q_sh;
+            const uint16_t* q_oth = qbase + (int64_t)(32 * (wave ^ 1) + (ln & 31)) * p.q_sh;
+#pragma unroll
+            for (int j = 0; j < 18; ++j) {
+                qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
+                qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_oth + 16 * j));
+            }
+        }
         f32x16 O[16];
         float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
         for (int pass = 0;; ++pass) {
@@ -273,74 +302,93 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             l_part = 0.f;
             __syncthreads();                        // LDS free (previous piece / pass done)
 
-            // ---- prologue: ids of tiles 0..2; copies of tiles 0..2 with the
-            // ids of tiles 3 and 4 in the steady-state order; then Q; stage tile 0
-            for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, lane, ids_wave + 128 * t);
-            wait_vmcnt<0>();
-            uint32_t vm0 = 0, vm1 = 0, vm2 = 0;
-#pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                const uint8_t* src;
-                const uint32_t vm = tile_rows(t, lane, src);
-                if (t == 0) vm0 = vm;
-                if (t == 1) vm1 = vm;
-                if (t == 2) vm2 = vm;
-                gather_rows(src, lane, lds0 + slice_off + t * RAW_BYTES);
-                if (t >= 1) copy_ids(idx, k_lo, k_hi, t + 2, lane, ids_wave + 128 * ((t + 2) % IDS_SLOTS));
-            }
+            // ---- prologue: ids of tiles 0..2 (copied with Q on the first pass);
+            // copies of tiles 0..2 with the ids of tiles 3 and 4; copy source
+            // of tile 3; stage tile 0
+            uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles t .. t+3
+            const uint8_t* src_nx;                  // this lane's copy source in tile t+3
             {
-                const uint16_t* qbase = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss + 288 * dh + 8 * h;
-                const uint16_t* q_own = qbase + (int64_t)(32 * wave + n) * p.q_sh;
-                const uint16_t* q_oth = qbase + (int64_t)(32 * (wave ^ 1) + n) * p.q_sh;
-#pragma unroll
-                for (int j = 0; j < 18; ++j) {
-                    qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
-                    qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_oth + 16 * j));
-                }
+                const int ln = opaque_lane();
+                if (pass > 0)
+                    for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
+                wait_vmcnt<0>();                    // ids of tiles 0..2, and Q on the first pass
+                const uint8_t* src;
+                vm0 = tile_rows(0, ln, src);
+                gather_rows(src, ln, lds0 + slice_off);
+                copy_ids(idx, k_lo, k_hi, 3, ln, ids_wave);
+                vm1 = tile_rows(1, ln, src);
+                gather_rows(src, ln, lds0 + slice_off + RAW_BYTES);
+                copy_ids(idx, k_lo, k_hi, 4, ln, ids_wave + 128);
+                vm2 = tile_rows(2, ln, src);
+                gather_rows(src, ln, lds0 + slice_off + 2 * RAW_BYTES);
+                wait_vmcnt<13>();                   // copies of tile 0, ids of tile 3 (13 newer ops)
+                vm3 = tile_rows(3, ln, src_nx);
+                stage_rows(lds, slice_off, L_KB, wave, ln);
             }
-            wait_vmcnt<14>();                       // own copies of tile 0 (at least 14 newer ops)
-            stage_rows(lds, slice_off, L_KB, wave, lane);
             __syncthreads();
 
-            // ---- tile loop: phase 1 S(t); phase 2 softmax(t) | PV(t-1) | copies
-            // of t+3; phase 3 P(t) and staging of t+1
             bool restart = false;
 
-            // phase 1: S^T partials of tile t; the partner's heads go to the partner
-            // The copies of tile t + 3 (into the raw buffer staging of tile t
-            // emptied) and the ids of tile t + 5 ride between the MFMAs, one
-            // memory instruction every few steps, so the queue never fills.
-            auto scores = [&](int t, int ln, uint32_t& vm3) -> f32x16 {
+            // Phase 1 of tile t: the score MFMAs of tile t (S^T partials for this
+            // wave's 64 heads over its 288 dims) and, with `pv`, the value MFMAs
+            // of tile t-1 (O^T += V^T P^T over this wave's 128 dims), 68 matrix
+            // instructions in one stream.  The ids of tile t + 5 and the copies
+            // of tile t + 3 (into the raw buffer emptied by the staging of tile
+            // t) ride between them.  The partner's partial goes to LDS.
+            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src3) -> f32x16 {
                 const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
-                // own copies of tile t+1 and the ids of tile t+3 have landed
-                // (7 newer ops: copies of t+2, ids of t+4)
-                wait_vmcnt<7>();
-                const uint8_t* src3 = nullptr;
+                const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
                 const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
                 f32x16 S0, S1;
-                constexpr int AHEAD = 3;
-                bf16x8 a[AHEAD];
+                bf16x8 ka[3], va, pf[4];
 #pragma unroll
-                for (int j = 0; j < AHEAD; ++j)
-                    a[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                for (int j = 0; j < 3; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                if (pv) {
 #pragma unroll
-                for (int j = 0; j < 18; ++j) {
-                    const bf16x8 cur = a[j % AHEAD];
-                    if (j + AHEAD < 18)
-                        a[j % AHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (j + AHEAD)));
-                    if (j == 0) {
-                        mfma_qk_first(S0, cur, qa[0]);
-                        mfma_qk_first(S1, cur, qb[0]);
+                    for (int hb = 0; hb < 4; ++hb)
+                        pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
+                    va = v_frag(lds, vb);
+                }
+                copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
+                // 26 slots: value steps at 2, 5, 8, 11, 14, 17, 21, 25, score
+                // steps elsewhere, so the last value MFMAs cover the score result
+                // latency before the partial is stored
+                int js = 0, jv = 0;
+#pragma unroll
+                for (int slot = 0; slot < 26; ++slot) {
+                    const bool vslot = slot == 2 || slot == 5 || slot == 8 || slot == 11 || slot == 14 ||
+                                       slot == 17 || slot == 21 || slot == 25;
+                    if (vslot) {
+                        if (pv) {
+                            const int jd = jv & 3;
+                            bf16x8 vn;
+                            if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * KP + ((jv + 1) & 3) * 64);
+#pragma unroll
+                            for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * jd + hb], va, pf[hb]);
+                            if (jv == 3) {
+#pragma unroll
+                                for (int hb = 0; hb < 4; ++hb)
+                                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                            }
+                            if (jv + 1 < 8) va = vn;
+                        }
+                        ++jv;
                     } else {
-                        mfma_qk(S0, cur, qa[j]);
-                        mfma_qk(S1, cur, qb[j]);
+                        const bf16x8 cur = ka[js % 3];
+                        if (js + 3 < 18)
+                            ka[js % 3] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + 3)));
+                        if (js == 0) {
+                            mfma_qk_first(S0, cur, qa[0]);
+                            mfma_qk_first(S1, cur, qb[0]);
+                        } else {
+                            mfma_qk(S0, cur, qa[js]);
+                            mfma_qk(S1, cur, qb[js]);
+                        }
+                        ++js;
                     }
-                    if (j == 0) vm3 = tile_rows(t + 3, ln, src3);
-                    if (j >= 2 && j <= 14 && j % 3 == 2)
-                        dma16(src3 + 128 * (j / 3), __builtin_amdgcn_readfirstlane(slice3 + 1024u * (j / 3)));
-                    if (j == 16) gather_tail(src3, ln, slice3);
-                    if (j == 17) copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
-                    // keep the reads AHEAD steps in front of their MFMAs
+                    if (slot >= 3 && slot <= 15 && slot % 3 == 0)
+                        dma16(src3 + 128 * (slot / 3 - 1), __builtin_amdgcn_readfirstlane(slice3 + 1024u * (slot / 3 - 1)));
+                    if (slot == 18) gather_tail(src3, ln, slice3);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 mfma_result_fence2(S0, S1);
@@ -351,82 +399,64 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 }
                 return S0;
             };
-            // phase 2: softmax of tile ts (add the partner's partial, mask empty
-            // slots, base-2 softmax against the reference max, P fragments of both
-            // k-steps), in six pieces; with `pv` the value MFMAs of tile ts - 1
-            // (O^T += V^T P^T) run in eight steps between them.  Scheduling fences
-            // keep each piece between two MFMA groups.
-            auto softmax_values = [&](f32x16 S, uint32_t vm, int ts, int ln, bool pv, u32x4& pf0, u32x4& pf1) {
-                const int kb = L_KB + ((ts - 1) & 1) * KBB;
-                const int vb = kb + pv_base(ln) + 64 * 4 * wave;
-                bf16x8 pf[4], a_cur, a_nxt;
+            // Phase 2 of tile t: softmax (add the partner's partial, mask empty
+            // slots, base-2 exponent against the reference max), P of both
+            // k-steps to LDS for every wave's value MFMAs, the staging of tile
+            // t + 1 into the K buffer the value MFMAs of tile t - 1 have
+            // released, and the copy source of tile t + 4.  Past the piece the
+            // staged rows are zero rows.
+            auto phase2 = [&](f32x16 S, uint32_t vm, int t, int ln, const uint8_t*& src4) -> uint32_t {
+                // copies of tile t+1 and the ids of tile t+4 have landed (13 newer
+                // ops: copies of tile t+2, ids of tile t+5, copies of tile t+3)
+                wait_vmcnt<13>();
+                const StageRegs g = stage_load(lds, slice_off + ((t + 1) % NRAW) * RAW_BYTES, ln);
                 f32x4 xs[4];
-                float mx = -INFINITY, psum = 0.f;
-                auto piece = [&](int k) {
-                    if (k == 0) {
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            xs[c] = *(const LDS_AS f32x4*)(lds + L_XS + wave * 4096 + 1024 * c + 16 * ln);
-                    } else if (k == 1) {
-                        // accumulator element v holds key 8(v/4) + 4h + v%4: lanes 0..31
-                        // test bit 8(v/4) + v%4 of the tile mask, lanes 32..63 that + 4
+                for (int c = 0; c < 4; ++c)
+                    xs[c] = *(const LDS_AS f32x4*)(lds + L_XS + wave * 4096 + 1024 * c + 16 * ln);
+                const uint32_t vm4 = tile_rows(t + 4, ln, src4);
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            S[v] += xs[v >> 2][v & 3];
-                            const int key = 8 * (v >> 2) + (v & 3);
-                            const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
-                                                   ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
-                            S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
-                            mx = fmaxf(mx, S[v]);
-                        }
-                    } else if (k == 2) {
-                        mx = fmaxf(mx, __shfl_xor(mx, 32));
-                        const float mnew = mx * p.c;
-                        m_seen = fmaxf(m_seen, mnew);
-                        if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
-                        restart |= __any(mnew > m_ref + p.threshold);
-                    } else if (k == 3 || k == 4) {
+                for (int v = 0; v < 16; ++v) S[v] += xs[v >> 2][v & 3];
+                if (vm != 0xffffffffu) {
+                    // accumulator element v holds key 8(v/4) + 4h + v%4: lanes 0..31
+                    // test bit 8(v/4) + v%4 of the tile mask, lanes 32..63 that + 4
 #pragma unroll
-                        for (int v = 8 * (k - 3); v < 8 * (k - 2); ++v) {
-                            S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
-                            psum += S[v];
-                        }
-                    } else if (k == 5) {
-                        l_part += psum;
-                        pf0 = p_fragment(S, 0);
-                        pf1 = p_fragment(S, 1);
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = 8 * (v >> 2) + (v & 3);
+                        const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
+                                               ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
+                        S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
                     }
-                };
-                if (pv) {
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb)
-                        pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
-                    a_cur = v_frag(lds, vb);
                 }
-                piece(0);
-                __builtin_amdgcn_sched_barrier(0);
+                float mx = S[0];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    if (pv) {
-                        const int j = s & 3;
-                        if (s + 1 < 8) a_nxt = v_frag(lds, vb + ((s + 1) >> 2) * 16 * KP + ((s + 1) & 3) * 64);
-#pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * j + hb], a_cur, pf[hb]);
-                        if (s == 3) {
-#pragma unroll
-                            for (int hb = 0; hb < 4; ++hb)
-                                pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
-                        }
-                        if (s + 1 < 8) a_cur = a_nxt;
-                    }
-                    if (s + 1 <= 5) piece(s + 1);
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
+                {
+                    // max with the other half-wave (same head): the swap hands
+                    // lanes 0..31 the upper half's value in the second result
+                    // and lanes 32..63 the lower half's in the first
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                    mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
                 }
+                const float mnew = mx * p.c;
+                m_seen = fmaxf(m_seen, mnew);
+                if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                restart |= __any(mnew > m_ref + p.threshold);
+                float psum = 0.f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
+                    psum += S[v];
+                }
+                l_part += psum;
+                lds_write16(lds, L_XP + wave * 2048 + 16 * ln, p_fragment(S, 0));
+                lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
+                stage_store(lds, g, L_KB + ((t + 1) & 1) * KBB, wave, ln);
+                return vm4;
             };
-            // value MFMAs of the last tile (no softmax left)
+            // value MFMAs of the last tile
             auto values_only = [&](int t, int ln) {
-                const int kb = L_KB + (t & 1) * KBB;
-                const int vb = kb + pv_base(ln) + 64 * 4 * wave;
+                const int vb = L_KB + (t & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
                 bf16x8 pf[4];
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb)
@@ -447,50 +477,34 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (s + 1 < 8) a_cur = a_nxt;
                 }
             };
-            // phase 3: P(t) for every wave's value MFMAs, stage tile t+1
-            auto publish_and_stage = [&](int t, int ln, const u32x4& pf0, const u32x4& pf1) {
-                lds_write16(lds, L_XP + wave * 2048 + 16 * ln, pf0);
-                lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, pf1);
-                if (t + 1 < n_tiles) {
-                    const int slice_next = slice_off + ((t + 1) % NRAW) * RAW_BYTES;
-                    const int kb_next = L_KB + ((t + 1) & 1) * KBB;
-                    stage_rows(lds, slice_next, kb_next, wave, ln);
-                }
-            };
 
             // tile 0: no value work yet
             {
                 const int ln = opaque_lane();
-                uint32_t vm3;
-                f32x16 S = scores(0, ln, vm3);
+                const f32x16 S = phase1(0, ln, false, src_nx);
                 __syncthreads();
-                u32x4 pf0, pf1;
-                softmax_values(S, vm0, 0, ln, false, pf0, pf1);
-                __syncthreads();
-                publish_and_stage(0, ln, pf0, pf1);
+                const uint32_t vm4 = phase2(S, vm0, 0, ln, src_nx);
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;
+                vm3 = vm4;
                 __syncthreads();
             }
             for (int it = 1; it < n_tiles; ++it) {
                 // lane-derived offsets are recomputed every tile (cheap VALU)
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
-                uint32_t vm3;
-                f32x16 S = scores(it, ln, vm3);
+                const f32x16 S = phase1(it, ln, true, src_nx);
                 __syncthreads();
-                u32x4 pf0, pf1;
-                softmax_values(S, vm0, it, ln, true, pf0, pf1);
-                __syncthreads();
-                publish_and_stage(it, ln, pf0, pf1);
+                const uint32_t vm4 = phase2(S, vm0, it, ln, src_nx);
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;
+                vm3 = vm4;
                 __syncthreads();
             }
             values_only(n_tiles - 1, opaque_lane());
-            if (lane == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
+            if (threadIdx.x % 64 == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
             __syncthreads();
             wait_vmcnt<0>();                                    // copies past the piece
             // A score exceeded the reference by more than 2^threshold in some
@@ -503,6 +517,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         }
 
         // ---- epilogue: l and m of every head through LDS
+        const int lane = opaque_lane();
+        const int n = lane & 31, h = lane >> 5;
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[i]));
         const float l_tot = l_part + __shfl_xor(l_part, 32);
@@ -578,11 +594,10 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
         copy_ids(idx, 0, p.topk, it, lane, lds0 + L_IDS + wave * IDS_SLOTS * 128);
         wait_vmcnt<0>();
         const int kr = WROWS * wave + (lane >> 3);
-        const uint8_t* a;
-        const bool ok = token_addr(p, slot[n], it * TILE + n < p.topk, 0, a);
-        token_addr(p, slot[kr], it * TILE + kr < p.topk, kr, a);
+        const bool ok = slot_ok(p, slot[n], it * TILE + n < p.topk);
+        const bool okr = slot_ok(p, slot[kr], it * TILE + kr < p.topk);
         const uint32_t vm = (uint32_t)__ballot(ok);
-        gather_rows(a + 16 * (lane & 7), lane, lds0 + slice_off);
+        gather_rows(row_addr(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, lds0 + slice_off);
         wait_vmcnt<0>();
         stage_rows(lds, slice_off, L_KB, wave, lane);
         __syncthreads();

@@ -154,14 +154,21 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     p->o_accum = a->o_accum;
     p->lse_accum = a->lse_accum;
     p->n_tok = r.num_kv_tokens;
+    p->n_tok32 = (uint32_t)(r.num_kv_tokens < INT32_MAX ? r.num_kv_tokens : INT32_MAX);
     p->b = r.b;
     p->s_q = r.s_q;
     p->h_q = r.h_q;
     p->topk = r.topk;
     p->page_block_size = r.page_block_size;
-    p->page_shift = -1;
-    for (int sh = 0; sh < 31; ++sh)
-        if ((1 << sh) == r.page_block_size) p->page_shift = sh;
+    {
+        // division by the page size as a multiply-high: l = ceil(log2 P),
+        // magic = floor(2^32 (2^l - P) / P) + 1 is exact for every t < 2^31
+        const uint64_t P = (uint64_t)r.page_block_size;
+        int l = 0;
+        while ((1ull << l) < P) ++l;
+        p->page_mshift = l;
+        p->page_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - P)) / P + 1);
+    }
     p->packed_partials = r.kv_format == MLA_KV_FP8_656 && r.h_q == 128;
     p->block = r.block;
     p->c = sm * 1.4426950408889634f;

@@ -33,8 +33,10 @@ struct DecodeParams {
     float* o_accum;
     float* lse_accum;
     int64_t n_tok;
+    uint32_t n_tok32;               // min(n_tok, 2^31 - 1): token ids are int32
     int b, s_q, h_q, topk, page_block_size, block;
-    int page_shift;                 // log2(page_block_size) when a power of two, else -1
+    uint32_t page_magic;            // t / page_block_size == (mulhi(t, page_magic) + t) >> page_mshift
+    int page_mshift;                // for 0 <= t < 2^31 (round-up reciprocal)
     int packed_partials;            // split partials as packed bf16 (128-head FP8 decode)
     float c;                        // sm_scale * log2(e)
     float threshold;                // log2-units gap above the reference max that
