@@ -7,7 +7,11 @@ topk=2048 slots into a paged FP8 cache of 32768 tokens per sequence.  Steps
 rotate over --layers independent layers (own cache, Q and indices each) so
 the gathered rows of one step are not still cached in the 256 MB Infinity
 Cache when that layer comes round again.  Inputs are resident in HBM before
-the timed region starts.
+the timed region starts.  The three kernels of a step are launched one by
+one (--graph replays a captured HIP graph of each layer's step instead, which
+on this stack costs more per step than the launches it saves); the decode
+kernel's duration comes from HIP events around eager launches of the same
+steps.
 
 Prints one JSON line.  With --gpus N > 1 it exits: this build runs on one GPU.
 """
@@ -74,6 +78,9 @@ def main():
     ap.add_argument("--fixed-overhead", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a captured HIP graph of each layer's step instead of launching "
+                         "its three kernels one by one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "kernel for scaling HBM byte counters) and exit")
@@ -131,16 +138,49 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # With --graph, one HIP graph per layer holding that layer's whole step
+    # (scheduler, decode, combine), replayed.  The library calls only launch
+    # kernels on the current stream (no allocation, no memset), which is what
+    # capture needs.
+    graphs = []
+    if args.graph:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(len(argsets)):
+                step(i)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(len(argsets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+
     # ---- timed region: exactly `steps` steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
+    if graphs:
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- decode kernel duration: HIP events on the launch stream around each
+    # decode of `steps` eager steps (the same work, launched one by one)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     flops, bytes_, n_valid = algorithmic(w0)
@@ -158,7 +198,8 @@ def main():
                    "topk": w0.topk, "kv_cache": "fp8 656 B/token, page 64, 32768 tokens/seq",
                    "layers_rotated": args.layers, "split_granularity": args.split_granularity,
                    "fixed_overhead": args.fixed_overhead, "num_parts": plan.shape.num_parts,
-                   "step": "sched + decode + combine"},
+                   "step": "sched + decode + combine",
+                   "launch": "eager" if not graphs else "hip graph per layer"},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None,
                      "kernel": "decode_fp8_h128_kernel", "kernel_ms": decode_ms,

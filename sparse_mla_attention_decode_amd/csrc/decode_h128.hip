@@ -57,6 +57,7 @@ constexpr int KP = 1168;                          // staged row pitch (1152 + 16
 constexpr int KBB = TILE * KP;                    // 37376
 constexpr int IDS_SLOTS = 3;                      // token-id tiles per wave in LDS
 constexpr int ZERO_ROWS = 64;                     // rows of the zero page
+constexpr int KAHEAD = 3;                         // score fragments read ahead of their MFMAs
 
 // LDS map (bytes).  The 16-byte pad at the end of every staged row is never
 // read by the contractions; row 0's pad of staged tile 0 holds the restart
@@ -330,19 +331,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             bool restart = false;
 
             // Phase 1 of tile t: the score MFMAs of tile t (S^T partials for this
-            // wave's 64 heads over its 288 dims) and, with `pv`, the value MFMAs
-            // of tile t-1 (O^T += V^T P^T over this wave's 128 dims), 68 matrix
-            // instructions in one stream.  The ids of tile t + 5 and the copies
-            // of tile t + 3 (into the raw buffer emptied by the staging of tile
-            // t) ride between them.  The partner's partial goes to LDS.
-            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src3) -> f32x16 {
+            // wave's 64 heads over its 288 dims) and, with `pv`, the first
+            // k-step of the value MFMAs of tile t-1 (O^T += V^T P^T over this
+            // wave's 128 dims), 52 matrix instructions in one stream; the ids of
+            // tile t + 5 and the copies of tile t + 3 (into the raw buffer
+            // emptied by the staging of tile t) ride between them.  The operands
+            // of the second value k-step are loaded into registers for phase 2,
+            // and the partner's score partial goes to LDS.
+            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src3, bf16x8 (&v1)[4],
+                              bf16x8 (&pf1)[4]) -> f32x16 {
                 const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
                 const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
                 const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
                 f32x16 S0, S1;
-                bf16x8 ka[3], va, pf[4];
+                bf16x8 ka[KAHEAD], va, pf[4];
 #pragma unroll
-                for (int j = 0; j < 3; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                for (int j = 0; j < KAHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
                 if (pv) {
 #pragma unroll
                     for (int hb = 0; hb < 4; ++hb)
@@ -350,33 +354,24 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     va = v_frag(lds, vb);
                 }
                 copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
-                // 26 slots: value steps at 2, 5, 8, 11, 14, 17, 21, 25, score
-                // steps elsewhere, so the last value MFMAs cover the score result
-                // latency before the partial is stored
+                // 22 slots: value steps at 2, 6, 10, 14, score steps elsewhere
                 int js = 0, jv = 0;
 #pragma unroll
-                for (int slot = 0; slot < 26; ++slot) {
-                    const bool vslot = slot == 2 || slot == 5 || slot == 8 || slot == 11 || slot == 14 ||
-                                       slot == 17 || slot == 21 || slot == 25;
+                for (int slot = 0; slot < 22; ++slot) {
+                    const bool vslot = slot == 2 || slot == 6 || slot == 10 || slot == 14;
                     if (vslot) {
                         if (pv) {
-                            const int jd = jv & 3;
                             bf16x8 vn;
-                            if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * KP + ((jv + 1) & 3) * 64);
+                            if (jv + 1 < 4) vn = v_frag(lds, vb + (jv + 1) * 64);
 #pragma unroll
-                            for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * jd + hb], va, pf[hb]);
-                            if (jv == 3) {
-#pragma unroll
-                                for (int hb = 0; hb < 4; ++hb)
-                                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
-                            }
-                            if (jv + 1 < 8) va = vn;
+                            for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * jv + hb], va, pf[hb]);
+                            if (jv + 1 < 4) va = vn;
                         }
                         ++jv;
                     } else {
-                        const bf16x8 cur = ka[js % 3];
-                        if (js + 3 < 18)
-                            ka[js % 3] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + 3)));
+                        const bf16x8 cur = ka[js % KAHEAD];
+                        if (js + KAHEAD < 18)
+                            ka[js % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + KAHEAD)));
                         if (js == 0) {
                             mfma_qk_first(S0, cur, qa[0]);
                             mfma_qk_first(S1, cur, qb[0]);
@@ -391,6 +386,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (slot == 18) gather_tail(src3, ln, slice3);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                if (pv) {
+                    // operands of the second value k-step (keys 16..31), once the
+                    // score fragments no longer need their registers
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v1[j] = v_frag(lds, vb + 16 * KP + j * 64);
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb)
+                        pf1[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                }
                 mfma_result_fence2(S0, S1);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -399,24 +403,36 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 }
                 return S0;
             };
-            // Phase 2 of tile t: softmax (add the partner's partial, mask empty
-            // slots, base-2 exponent against the reference max), P of both
-            // k-steps to LDS for every wave's value MFMAs, the staging of tile
-            // t + 1 into the K buffer the value MFMAs of tile t - 1 have
-            // released, and the copy source of tile t + 4.  Past the piece the
-            // staged rows are zero rows.
-            auto phase2 = [&](f32x16 S, uint32_t vm, int t, int ln, const uint8_t*& src4) -> uint32_t {
+            // Phase 2 of tile t: with `pv` the second value k-step of tile t-1
+            // (16 MFMAs on operands already in registers) under the softmax of
+            // tile t (add the partner's partial, mask empty slots, base-2
+            // exponent against the reference max); P of both k-steps to LDS for
+            // every wave's value MFMAs, the staging of tile t + 1 into the K
+            // buffer the value MFMAs of tile t - 1 have released, and the copy
+            // source of tile t + 4.  Past the piece the staged rows are zero rows.
+            auto phase2 = [&](f32x16 S, uint32_t vm, int t, int ln, bool pv, const bf16x8 (&v1)[4],
+                              const bf16x8 (&pf1)[4], const uint8_t*& src4) -> uint32_t {
                 // copies of tile t+1 and the ids of tile t+4 have landed (13 newer
                 // ops: copies of tile t+2, ids of tile t+5, copies of tile t+3)
                 wait_vmcnt<13>();
+                {
+                    f32x4 xs[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        xs[c] = *(const LDS_AS f32x4*)(lds + L_XS + wave * 4096 + 1024 * c + 16 * ln);
+                    if (pv) {
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb) mfma_pv(O[hb], v1[0], pf1[hb]);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) S[v] += xs[v >> 2][v & 3];
+                }
                 const StageRegs g = stage_load(lds, slice_off + ((t + 1) % NRAW) * RAW_BYTES, ln);
-                f32x4 xs[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    xs[c] = *(const LDS_AS f32x4*)(lds + L_XS + wave * 4096 + 1024 * c + 16 * ln);
                 const uint32_t vm4 = tile_rows(t + 4, ln, src4);
+                if (pv) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) S[v] += xs[v >> 2][v & 3];
+                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 + hb], v1[1], pf1[hb]);
+                }
                 if (vm != 0xffffffffu) {
                     // accumulator element v holds key 8(v/4) + 4h + v%4: lanes 0..31
                     // test bit 8(v/4) + v%4 of the tile mask, lanes 32..63 that + 4
@@ -442,6 +458,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 m_seen = fmaxf(m_seen, mnew);
                 if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
                 restart |= __any(mnew > m_ref + p.threshold);
+                if (pv) {
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[8 + hb], v1[2], pf1[hb]);
+                }
                 float psum = 0.f;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
@@ -449,6 +469,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     psum += S[v];
                 }
                 l_part += psum;
+                if (pv) {
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[12 + hb], v1[3], pf1[hb]);
+                }
                 lds_write16(lds, L_XP + wave * 2048 + 16 * ln, p_fragment(S, 0));
                 lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
                 stage_store(lds, g, L_KB + ((t + 1) & 1) * KBB, wave, ln);
@@ -479,11 +503,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             };
 
             // tile 0: no value work yet
+            bf16x8 v1[4], pf1[4];
             {
                 const int ln = opaque_lane();
-                const f32x16 S = phase1(0, ln, false, src_nx);
+                const f32x16 S = phase1(0, ln, false, src_nx, v1, pf1);
                 __syncthreads();
-                const uint32_t vm4 = phase2(S, vm0, 0, ln, src_nx);
+                const uint32_t vm4 = phase2(S, vm0, 0, ln, false, v1, pf1, src_nx);
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;
@@ -494,9 +519,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // lane-derived offsets are recomputed every tile (cheap VALU)
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
-                const f32x16 S = phase1(it, ln, true, src_nx);
+                const f32x16 S = phase1(it, ln, true, src_nx, v1, pf1);
                 __syncthreads();
-                const uint32_t vm4 = phase2(S, vm0, it, ln, src_nx);
+                const uint32_t vm4 = phase2(S, vm0, it, ln, true, v1, pf1, src_nx);
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;

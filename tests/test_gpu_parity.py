@@ -203,6 +203,47 @@ def test_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_hip_graph_replay_matches_eager():
+    """The whole step (scheduler, decode, combine) captured in a HIP graph and
+    replayed several times, with other eager work and synchronisations between
+    the replays: every replay must reproduce the eager result bit for bit, and
+    the eager result must match the oracle."""
+    _need_gpu()
+    w = W.make_config(0)
+    q, kv, idx = w.q_device(), w.kv_device(), w.indices_device()
+    plan = _plan(w, split_granularity=32, fixed_overhead=0)
+    out, lse = plan.run(q, kv, idx, w.sm_scale)
+    torch.cuda.synchronize()
+    eager_out, eager_lse = out.clone(), lse.clone()
+    ref_out, ref_lse = oracle(w)
+    assert_parity(eager_out.float().cpu().numpy(), eager_lse.cpu().numpy(), ref_out, ref_lse,
+                  all_queries(w), "graph eager")
+    other = W.paged_decode("graph_other", 77, b=w.b, s_q=1, h_q=128, topk=w.topk, tokens_per_seq=256, P=64)
+    oq, okv, oidx = other.q_device(), other.kv_device(), other.indices_device()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan.run(q, kv, idx, w.sm_scale)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(q, kv, idx, w.sm_scale)
+    for r in range(4):
+        out.zero_()
+        lse.fill_(-1.0)
+        plan.o_accum.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {r}: out differs"
+        assert torch.equal(lse, eager_lse), f"replay {r}: lse differs"
+        # eager work of the program between replays, on the same buffers
+        other_out, _ = plan.run(oq, okv, oidx, other.sm_scale)
+        torch.cuda.synchronize()
+        assert not torch.equal(other_out, eager_out)
+
+
 def test_strided_q_and_out():
     _need_gpu()
     w = W.make_config(0)
