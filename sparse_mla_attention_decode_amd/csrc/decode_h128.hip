@@ -279,22 +279,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             return (uint32_t)__ballot(ok);
         };
 
-        // Q as B operands, loaded once per request: qa = this wave's own heads
+        // Q as B operands, loaded once per request (on the first pass, after the
+        // copies of the first tiles are on their way): qa = this wave's own heads
         // 32w + n, qb = the partner wave's heads; k-step j covers dims
         // 288 dh + 16 j + 8 h .. +7
         bf16x8 qa[18], qb[18];
-        {
-            const int ln = opaque_lane();
-            for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
-            const uint16_t* qbase = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss + 288 * dh + 8 * (ln >> 5);
-            const uint16_t* q_own = qbase + (int64_t)(32 * wave + (ln & 31)) * p.q_sh;
-            const uint16_t* q_oth = qbase + (int64_t)(32 * (wave ^ 1) + (ln & 31)) * p.q_sh;
-#pragma unroll
-            for (int j = 0; j < 18; ++j) {
-                qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
-                qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_oth + 16 * j));
-            }
-        }
         f32x16 O[16];
         float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
         for (int pass = 0;; ++pass) {
@@ -310,9 +299,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             const uint8_t* src_nx;                  // this lane's copy source in tile t+3
             {
                 const int ln = opaque_lane();
-                if (pass > 0)
-                    for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
-                wait_vmcnt<0>();                    // ids of tiles 0..2, and Q on the first pass
+                for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
+                wait_vmcnt<0>();                    // ids of tiles 0..2
                 const uint8_t* src;
                 vm0 = tile_rows(0, ln, src);
                 gather_rows(src, ln, lds0 + slice_off);
@@ -322,9 +310,28 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 copy_ids(idx, k_lo, k_hi, 4, ln, ids_wave + 128);
                 vm2 = tile_rows(2, ln, src);
                 gather_rows(src, ln, lds0 + slice_off + 2 * RAW_BYTES);
-                wait_vmcnt<13>();                   // copies of tile 0, ids of tile 3 (13 newer ops)
+                if (pass == 0) {
+                    const uint16_t* qbase =
+                        p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss + 288 * dh + 8 * (ln >> 5);
+                    const uint16_t* q_own = qbase + (int64_t)(32 * wave + (ln & 31)) * p.q_sh;
+                    const uint16_t* q_oth = qbase + (int64_t)(32 * (wave ^ 1) + (ln & 31)) * p.q_sh;
+#pragma unroll
+                    for (int j = 0; j < 18; ++j) {
+                        qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
+                        qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_oth + 16 * j));
+                    }
+                    // copies of tile 0 and the ids of tile 3 (13 newer copy ops and
+                    // the 36 loads of Q); Q itself is waited for where it is used
+                    wait_vmcnt<49>();
+                } else {
+                    wait_vmcnt<13>();               // copies of tile 0, ids of tile 3 (13 newer ops)
+                }
                 vm3 = tile_rows(3, ln, src_nx);
                 stage_rows(lds, slice_off, L_KB, wave, ln);
+                // Q (the newest loads) before tile 0's score MFMAs: waiting here
+                // keeps the compiler's own waits for Q out of the copy stream
+                // (unconditional, so the compiler sees Q complete on every path)
+                wait_vmcnt<0>();
             }
             __syncthreads();
 
