@@ -30,6 +30,33 @@ METRIC = "sparse-decode query-tokens/s at b=64,h=128,topk=2048; % of MFMA/HBM ro
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 
+# HBM bytes per launch of the decode kernel at this workload, from two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
+# each scaled by what the same counter reads for a plain 1 GiB device copy
+# (bench.py --copy-calibration 1024: FETCH_SIZE reads 524302.8 KiB -> x2.0,
+# WRITE_SIZE 1048576 KiB -> x1.0).  Valid only for the kernel sources they were
+# taken on (sha256 below); for any other source the traffic is reported null.
+DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
+                         "sparse_mla_attention_decode_amd/csrc/device_common.h")
+DECODE_TRAFFIC = {"sources_sha256": "98e6524f405f69780b54e3d6c3759c513789a1ecac8ee1c9b65264418b750d3b",
+                  "fetch_kib": 54188.16, "fetch_scale": 2.0, "write_kib": 33920.0, "write_scale": 1.0}
+
+
+def measured_traffic():
+    """HBM bytes per decode launch if the counters match the current kernel sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    t = DECODE_TRAFFIC
+    if h.hexdigest() != t["sources_sha256"]:
+        return None, None
+    fetch = t["fetch_kib"] * 1024 * t["fetch_scale"]
+    write = t["write_kib"] * 1024 * t["write_scale"]
+    return fetch + write, {"fetch_bytes": fetch, "write_bytes": write,
+                           "counters": "FETCH_SIZE x2.0, WRITE_SIZE x1.0 (copy-calibrated)"}
+
 
 def algorithmic(w):
     """Flops of the two contractions over valid slots and compulsory HBM bytes
@@ -184,6 +211,7 @@ def main():
     decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     flops, bytes_, n_valid = algorithmic(w0)
+    traffic, traffic_detail = measured_traffic()
     achieved_tflops = flops / (decode_ms * 1e-3) / 1e12
     t_roof_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
     q_tokens = w0.b * w0.s_q
@@ -201,7 +229,8 @@ def main():
                    "step": "sched + decode + combine",
                    "launch": "eager" if not graphs else "hip graph per layer"},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "traffic_detail": traffic_detail,
                      "kernel": "decode_fp8_h128_kernel", "kernel_ms": decode_ms,
                      "algorithmic_flop_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
                      "hbm_achieved_GBs": bytes_ / (decode_ms * 1e-3) / 1e9},
