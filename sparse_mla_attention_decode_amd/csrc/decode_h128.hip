@@ -346,7 +346,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // of the second value k-step are loaded into registers for phase 2,
             // and the partner's score partial goes to LDS.
             auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src3, bf16x8 (&v1)[4],
-                              bf16x8 (&pf1)[4]) -> f32x16 {
+                              bf16x8 (&pf1)[4], const uint8_t*& src4, uint32_t& vm4) -> f32x16 {
+                // ids of tile t+4 have landed (6 newer ops: the copies of tile t+2)
+                wait_vmcnt<6>();
+                vm4 = tile_rows(t + 4, ln, src4);
                 const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
                 const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
                 const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
@@ -418,10 +421,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // buffer the value MFMAs of tile t - 1 have released, and the copy
             // source of tile t + 4.  Past the piece the staged rows are zero rows.
             auto phase2 = [&](f32x16 S, uint32_t vm, int t, int ln, bool pv, const bf16x8 (&v1)[4],
-                              const bf16x8 (&pf1)[4], const uint8_t*& src4) -> uint32_t {
-                // copies of tile t+1 and the ids of tile t+4 have landed (13 newer
-                // ops: copies of tile t+2, ids of tile t+5, copies of tile t+3)
-                wait_vmcnt<13>();
+                              const bf16x8 (&pf1)[4]) {
+                // copies of tile t+1 have landed (14 newer ops: ids of tile t+4,
+                // copies of tile t+2, ids of tile t+5, copies of tile t+3)
+                wait_vmcnt<14>();
                 {
                     f32x4 xs[4];
 #pragma unroll
@@ -435,7 +438,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     for (int v = 0; v < 16; ++v) S[v] += xs[v >> 2][v & 3];
                 }
                 const StageRegs g = stage_load(lds, slice_off + ((t + 1) % NRAW) * RAW_BYTES, ln);
-                const uint32_t vm4 = tile_rows(t + 4, ln, src4);
                 if (pv) {
 #pragma unroll
                     for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 + hb], v1[1], pf1[hb]);
@@ -483,7 +485,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 lds_write16(lds, L_XP + wave * 2048 + 16 * ln, p_fragment(S, 0));
                 lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
                 stage_store(lds, g, L_KB + ((t + 1) & 1) * KBB, wave, ln);
-                return vm4;
             };
             // value MFMAs of the last tile
             auto values_only = [&](int t, int ln) {
@@ -513,9 +514,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             bf16x8 v1[4], pf1[4];
             {
                 const int ln = opaque_lane();
-                const f32x16 S = phase1(0, ln, false, src_nx, v1, pf1);
+                const uint8_t* src4;
+                uint32_t vm4;
+                const f32x16 S = phase1(0, ln, false, src_nx, v1, pf1, src4, vm4);
                 __syncthreads();
-                const uint32_t vm4 = phase2(S, vm0, 0, ln, false, v1, pf1, src_nx);
+                phase2(S, vm0, 0, ln, false, v1, pf1);
+                src_nx = src4;
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;
@@ -526,9 +530,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // lane-derived offsets are recomputed every tile (cheap VALU)
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
-                const f32x16 S = phase1(it, ln, true, src_nx, v1, pf1);
+                const uint8_t* src4;
+                uint32_t vm4;
+                const f32x16 S = phase1(it, ln, true, src_nx, v1, pf1, src4, vm4);
                 __syncthreads();
-                const uint32_t vm4 = phase2(S, vm0, it, ln, true, v1, pf1, src_nx);
+                phase2(S, vm0, it, ln, true, v1, pf1);
+                src_nx = src4;
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;

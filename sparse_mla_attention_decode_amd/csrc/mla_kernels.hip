@@ -190,6 +190,58 @@ __global__ void __launch_bounds__(SCHED_THREADS) sched_parallel_kernel(int b, in
     if (tid == 0) prefix[b] = total_pieces;
 }
 
+// Without a per-request overhead the greedy fill gives partition p exactly the
+// blocks [p payload, min((p+1) payload, b B)) of the request-major block
+// sequence, so every record has a closed form; only the split numbering needs
+// a prefix sum (a wave scan plus one pass over the wave totals).
+constexpr int SCHED_FLAT_THREADS = 1024;
+__global__ void __launch_bounds__(SCHED_FLAT_THREADS) sched_flat_kernel(int b, int topk, int block,
+                                                                        int num_parts, int32_t* meta,
+                                                                        int32_t* prefix) {
+    __shared__ int32_t wsum[SCHED_FLAT_THREADS / 64];
+    __shared__ int32_t first_split[SCHED_FLAT_THREADS];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t B = (topk + block - 1) / block, total = (int64_t)b * B;
+    const int64_t payload = (total + num_parts - 1) / num_parts;
+    const int64_t s0 = (int64_t)tid * payload, s1 = min(s0 + payload, total);
+    const bool busy = tid < num_parts && s0 < total;
+    const int pieces = busy ? (int)((s1 - 1) / B - s0 / B + 1) : 0;
+    int incl = pieces;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < wv; ++i) before += wsum[i];
+    const int cursor = before + incl - pieces;
+    first_split[tid] = cursor;
+    if (tid < num_parts) {
+        int32_t* m = meta + 8 * tid;
+        if (!busy) {
+            m[0] = b; m[1] = b; m[2] = 0; m[3] = 0; m[4] = cursor; m[5] = 0; m[6] = 0; m[7] = 0;
+        } else {
+            const int64_t e = s1 - 1;
+            const int begin_block = (int)(s0 % B), end_block = (int)(e % B) + 1;
+            m[0] = (int)(s0 / B); m[1] = (int)(e / B); m[2] = begin_block; m[3] = end_block;
+            m[4] = cursor; m[5] = begin_block > 0; m[6] = end_block < B; m[7] = 0;
+        }
+    }
+    __syncthreads();
+    // request r opens in partition q = floor(r B / payload) as its piece
+    // r - (first request of q)
+    for (int r = tid; r < b; r += SCHED_FLAT_THREADS) {
+        const int64_t q = (int64_t)r * B / payload;
+        prefix[r] = first_split[q] + r - (int)(q * payload / B);
+    }
+    if (tid == SCHED_FLAT_THREADS - 1) {
+        int all = 0;
+        for (int i = 0; i < SCHED_FLAT_THREADS / 64; ++i) all += wsum[i];
+        prefix[b] = all;
+    }
+}
+
 // Sequential fill, one lane (used when the state table does not fit).
 __global__ void __launch_bounds__(64) sched_kernel(int b, int topk, int block, int overhead,
                                                    int num_parts, int32_t* meta, int32_t* prefix) {
@@ -675,7 +727,10 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
 // ----------------------------------------------------------------------------
 hipError_t launch_sched(const ResolvedShape& s, int32_t* meta, int32_t* prefix, hipStream_t st) {
     const int B = (s.topk + s.block - 1) / s.block;
-    if (B <= SCHED_MAX_STATES && s.num_parts < (1 << SCHED_LOG))
+    if (s.overhead == 0 && s.num_parts <= SCHED_FLAT_THREADS)
+        hipLaunchKernelGGL(sched_flat_kernel, dim3(1), dim3(SCHED_FLAT_THREADS), 0, st, s.b, s.topk,
+                           s.block, s.num_parts, meta, prefix);
+    else if (B <= SCHED_MAX_STATES && s.num_parts < (1 << SCHED_LOG))
         hipLaunchKernelGGL(sched_parallel_kernel, dim3(1), dim3(SCHED_THREADS), 0, st, s.b, s.topk,
                            s.block, s.overhead, s.num_parts, meta, prefix);
     else

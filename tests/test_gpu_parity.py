@@ -69,7 +69,10 @@ def all_queries(w):
 
 # ----------------------------------------------------------------------------- scheduler
 @pytest.mark.parametrize("b,topk,parts,gran,ovh", [(2, 128, 66, 64, 5), (64, 2048, 256, 32, 5),
-                                                   (4, 2048, 256, 32, 0), (128, 2048, 512, 64, 5)])
+                                                   (4, 2048, 256, 32, 0), (128, 2048, 512, 64, 5),
+                                                   (64, 2048, 256, 32, 0), (3, 100, 7, 32, 0),
+                                                   (1, 2048, 300, 32, 0), (130, 4999, 1024, 96, 0),
+                                                   (2000, 64, 100, 32, 0)])
 def test_sched_meta_device_matches_oracle(b, topk, parts, gran, ovh):
     _need_gpu()
     shape = M.make_shape(b, 1, 128, topk, 64 * 64, num_parts=parts, split_granularity=gran,
