@@ -264,19 +264,25 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
         const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
 
-        // ids of `tile` (copied earlier into its slot): validity mask of the
-        // tile's 32 keys and the copy source of this lane's row (key
-        // 8w + ln / 8, chunk ln % 8); tiles past the piece copy zero rows
-        auto tile_rows = [&](int tile, int ln, const uint8_t*& src) -> uint32_t {
+        // ids of `tile` (copied earlier into its slot) that this lane needs: key
+        // ln % 32 (validity mask) and key 8w + ln / 8 (its copy row)
+        auto read_ids = [&](int tile, int ln) -> int2 {
             const LDS_AS int32_t* slot =
                 (const LDS_AS int32_t*)(lds + L_IDS + (wave * IDS_SLOTS + tile % IDS_SLOTS) * 128);
+            return int2{slot[ln & 31], slot[WROWS * wave + (ln >> 3)]};
+        };
+        // validity mask of the tile's 32 keys and the copy source of this
+        // lane's row (chunk ln % 8); tiles past the piece copy zero rows
+        auto rows_from = [&](int tile, int ln, int2 id, const uint8_t*& src) -> uint32_t {
             const int kn = ln & 31, kr = WROWS * wave + (ln >> 3);
             const int k0 = k_lo + tile * TILE;
-            const bool ok = slot_ok(p, slot[kn], (tile < n_tiles) & (k0 + kn < k_hi));
-            const int tr = slot[kr];
-            const bool okr = slot_ok(p, tr, (tile < n_tiles) & (k0 + kr < k_hi));
-            src = row_addr(p, tr, okr, (tile * TILE + kr) & (ZERO_ROWS - 1)) + 16 * (ln & 7);
+            const bool ok = slot_ok(p, id.x, (tile < n_tiles) & (k0 + kn < k_hi));
+            const bool okr = slot_ok(p, id.y, (tile < n_tiles) & (k0 + kr < k_hi));
+            src = row_addr(p, id.y, okr, (tile * TILE + kr) & (ZERO_ROWS - 1)) + 16 * (ln & 7);
             return (uint32_t)__ballot(ok);
+        };
+        auto tile_rows = [&](int tile, int ln, const uint8_t*& src) -> uint32_t {
+            return rows_from(tile, ln, read_ids(tile, ln), src);
         };
 
         // Q as B operands, loaded once per request (on the first pass, after the
@@ -297,6 +303,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // of tile 3; stage tile 0
             uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles t .. t+3
             const uint8_t* src_nx;                  // this lane's copy source in tile t+3
+            int2 ids_nx;                            // its ids of tile t+4
             {
                 const int ln = opaque_lane();
                 for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
@@ -332,6 +339,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // keeps the compiler's own waits for Q out of the copy stream
                 // (unconditional, so the compiler sees Q complete on every path)
                 wait_vmcnt<0>();
+                ids_nx = read_ids(4, ln);           // landed with everything else
             }
             __syncthreads();
 
@@ -345,11 +353,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // emptied by the staging of tile t) ride between them.  The operands
             // of the second value k-step are loaded into registers for phase 2,
             // and the partner's score partial goes to LDS.
-            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src3, bf16x8 (&v1)[4],
+            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src3, int2 ids4, bf16x8 (&v1)[4],
                               bf16x8 (&pf1)[4], const uint8_t*& src4, uint32_t& vm4) -> f32x16 {
-                // ids of tile t+4 have landed (6 newer ops: the copies of tile t+2)
-                wait_vmcnt<6>();
-                vm4 = tile_rows(t + 4, ln, src4);
                 const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
                 const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
                 const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
@@ -364,6 +369,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     va = v_frag(lds, vb);
                 }
                 copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
+                __builtin_amdgcn_sched_barrier(0);
                 // 22 slots: value steps at 2, 6, 10, 14, score steps elsewhere
                 int js = 0, jv = 0;
 #pragma unroll
@@ -394,6 +400,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (slot >= 3 && slot <= 15 && slot % 3 == 0)
                         dma16(src3 + 128 * (slot / 3 - 1), __builtin_amdgcn_readfirstlane(slice3 + 1024u * (slot / 3 - 1)));
                     if (slot == 18) gather_tail(src3, ln, slice3);
+                    if (slot == 1) vm4 = rows_from(t + 4, ln, ids4, src4);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (pv) {
@@ -421,7 +428,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // buffer the value MFMAs of tile t - 1 have released, and the copy
             // source of tile t + 4.  Past the piece the staged rows are zero rows.
             auto phase2 = [&](f32x16 S, uint32_t vm, int t, int ln, bool pv, const bf16x8 (&v1)[4],
-                              const bf16x8 (&pf1)[4]) {
+                              const bf16x8 (&pf1)[4], int2& ids5) {
                 // copies of tile t+1 have landed (14 newer ops: ids of tile t+4,
                 // copies of tile t+2, ids of tile t+5, copies of tile t+3)
                 wait_vmcnt<14>();
@@ -485,6 +492,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 lds_write16(lds, L_XP + wave * 2048 + 16 * ln, p_fragment(S, 0));
                 lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
                 stage_store(lds, g, L_KB + ((t + 1) & 1) * KBB, wave, ln);
+                // ids of tile t+5 (issued at the start of phase 1; 6 newer ops:
+                // the copies of tile t+3) for the next phase 1's copy sources
+                wait_vmcnt<6>();
+                ids5 = read_ids(t + 5, ln);
             };
             // value MFMAs of the last tile
             auto values_only = [&](int t, int ln) {
@@ -516,9 +527,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 const uint8_t* src4;
                 uint32_t vm4;
-                const f32x16 S = phase1(0, ln, false, src_nx, v1, pf1, src4, vm4);
+                const f32x16 S = phase1(0, ln, false, src_nx, ids_nx, v1, pf1, src4, vm4);
                 __syncthreads();
-                phase2(S, vm0, 0, ln, false, v1, pf1);
+                phase2(S, vm0, 0, ln, false, v1, pf1, ids_nx);
                 src_nx = src4;
                 vm0 = vm1;
                 vm1 = vm2;
@@ -532,9 +543,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 const uint8_t* src4;
                 uint32_t vm4;
-                const f32x16 S = phase1(it, ln, true, src_nx, v1, pf1, src4, vm4);
+                const f32x16 S = phase1(it, ln, true, src_nx, ids_nx, v1, pf1, src4, vm4);
                 __syncthreads();
-                phase2(S, vm0, it, ln, true, v1, pf1);
+                phase2(S, vm0, it, ln, true, v1, pf1, ids_nx);
                 src_nx = src4;
                 vm0 = vm1;
                 vm1 = vm2;
