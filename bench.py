@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
 """Sparse MLA decode benchmark (one MI355X).
 
-A step is one pass of the whole hot path on one batch: the tile scheduler,
-the decode kernel and the split-KV combine, for b=64 query tokens, 128 heads,
+A step is one pass of the whole hot path on one batch: the tile plan, the
+decode kernel and the split-KV combine, for b=64 query tokens, 128 heads,
 topk=2048 slots into a paged FP8 cache of 32768 tokens per sequence.  Steps
 rotate over --layers independent layers (own cache, Q and indices each) so
 the gathered rows of one step are not still cached in the 256 MB Infinity
-Cache when that layer comes round again.  Inputs are resident in HBM before
-the timed region starts.  The three kernels of a step are launched one by
-one (--graph replays a captured HIP graph of each layer's step instead, which
+Cache when that layer comes round again.  With a per-request scheduler cost
+of zero (the default here) the plan is passed as NULL and every work-group
+evaluates its own partition in closed form, so a step is two launches;
+--plan sched launches the scheduler kernel in every step instead.  Inputs are
+resident in HBM before the timed region starts.  The kernels of a step are
+launched one by one (--graph replays a captured HIP graph of each layer's step instead, which
 on this stack costs more per step than the launches it saves); the decode
 kernel's duration comes from HIP events around eager launches of the same
 steps.
@@ -103,11 +106,15 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--split-granularity", type=int, default=32)
     ap.add_argument("--fixed-overhead", type=int, default=0)
+    ap.add_argument("--plan", choices=("auto", "closed", "sched"), default="auto",
+                    help="closed: NULL plan, the kernels evaluate the greedy plan in closed form "
+                         "(fixed_overhead 0 only); sched: launch the scheduler kernel every step; "
+                         "auto: closed when fixed_overhead is 0")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="replay a captured HIP graph of each layer's step instead of launching "
-                         "its three kernels one by one")
+                         "its kernels one by one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "kernel for scaling HBM byte counters) and exit")
@@ -147,7 +154,8 @@ def main():
     shape = M.make_shape(w0.b, w0.s_q, w0.h_q, w0.topk, w0.num_kv_tokens, w0.kv_format,
                          w0.page_block_size, split_granularity=args.split_granularity,
                          fixed_overhead=args.fixed_overhead)
-    plan = M.DecodePlan(shape, device=dev)
+    closed = args.plan == "closed" or (args.plan == "auto" and args.fixed_overhead == 0)
+    plan = M.DecodePlan(shape, device=dev, closed_form=closed)
     argsets = [plan.args(q, kv, idx, w.sm_scale) for (w, q, kv, idx) in layers]
     stream = torch.cuda.current_stream(dev)
 
@@ -166,7 +174,7 @@ def main():
     torch.cuda.synchronize()
 
     # With --graph, one HIP graph per layer holding that layer's whole step
-    # (scheduler, decode, combine), replayed.  The library calls only launch
+    # (plan, decode, combine), replayed.  The library calls only launch
     # kernels on the current stream (no allocation, no memset), which is what
     # capture needs.
     graphs = []
@@ -226,7 +234,8 @@ def main():
                    "topk": w0.topk, "kv_cache": "fp8 656 B/token, page 64, 32768 tokens/seq",
                    "layers_rotated": args.layers, "split_granularity": args.split_granularity,
                    "fixed_overhead": args.fixed_overhead, "num_parts": plan.shape.num_parts,
-                   "step": "sched + decode + combine",
+                   "step": ("decode (closed-form plan in-kernel) + combine" if closed
+                            else "sched + decode + combine"),
                    "launch": "eager" if not graphs else "hip graph per layer"},
         "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,

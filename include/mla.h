@@ -42,6 +42,7 @@
  *   - Every argument is validated on the host before anything is launched; on
  *     error nothing is launched, the status is returned and mla_last_error()
  *     holds a message (thread-local).  The library never aborts the process.
+ *   - Shape limit: b * ceil(topk / split_granularity) < 2^30.
  *   - Calls that overlap on one stream-ordered pipeline must use distinct
  *     sched/workspace buffers if they run concurrently on different streams.
  */
@@ -118,8 +119,15 @@ typedef struct mla_decode_args {
     const float* attn_sink;             /* must be NULL (not supported by this build)      */
     const int32_t* topk_length;         /* must be NULL (not supported by this build)      */
 
-    const void* sched_meta;             /* from mla_get_sched_meta (same shape)            */
-    const int32_t* num_splits;          /* [b + 1] split prefix from mla_get_sched_meta    */
+    const void* sched_meta;             /* from mla_get_sched_meta (same shape), or NULL   */
+    const int32_t* num_splits;          /* [b + 1] split prefix from mla_get_sched_meta, or
+                                           NULL.  Both NULL (only with fixed_overhead == 0):
+                                           the kernels evaluate the same greedy plan in closed
+                                           form (partition q takes blocks [q p, (q + 1) p) of
+                                           the request-major block sequence, p = ceil(b
+                                           ceil(topk / split_granularity) / num_parts)), so no
+                                           scheduler launch is needed.  One NULL and one set
+                                           is MLA_ERR_INVALID_ARG.                           */
 
     float* o_accum;                     /* workspace, >= mla_workspace_size bytes          */
     float* lse_accum;                   /* workspace, >= mla_workspace_size bytes          */

@@ -169,21 +169,27 @@ class DecodePlan:
     """Device buffers (sched meta, split prefix, workspace, outputs) for one shape,
     allocated with torch.  The plan can be reused for every call of that shape."""
 
-    def __init__(self, shape: mla_shape, device="cuda"):
+    def __init__(self, shape: mla_shape, device="cuda", closed_form: bool = False):
+        """closed_form=True (fixed_overhead 0 only) passes a NULL plan: the
+        kernels evaluate the plan themselves and get_sched_meta does nothing."""
         import torch
         self.shape = mla_resolve_shape(shape)
+        self.closed_form = closed_form
+        if closed_form and self.shape.fixed_overhead != 0:
+            raise MlaError("DecodePlan", MLA_ERR_INVALID_ARG, "closed_form needs fixed_overhead 0")
         meta_b, ns_b = mla_sched_meta_size(self.shape)
         o_b, l_b = mla_workspace_size(self.shape)
         s = self.shape
-        self.sched_meta = torch.empty(meta_b // 4, dtype=torch.int32, device=device)
-        self.num_splits = torch.empty(ns_b // 4, dtype=torch.int32, device=device)
+        self.sched_meta = None if closed_form else torch.empty(meta_b // 4, dtype=torch.int32, device=device)
+        self.num_splits = None if closed_form else torch.empty(ns_b // 4, dtype=torch.int32, device=device)
         self.o_accum = torch.empty(o_b // 4, dtype=torch.float32, device=device)
         self.lse_accum = torch.empty(l_b // 4, dtype=torch.float32, device=device)
         self.out = torch.empty((s.b, s.s_q, s.h_q, 512), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((s.b, s.h_q, s.s_q), dtype=torch.float32, device=device)
 
     def get_sched_meta(self, stream=None):
-        mla_get_sched_meta(self.shape, self.sched_meta.data_ptr(), self.num_splits.data_ptr(), stream)
+        if not self.closed_form:
+            mla_get_sched_meta(self.shape, self.sched_meta.data_ptr(), self.num_splits.data_ptr(), stream)
 
     def args(self, q, kv, indices, sm_scale: float = 0.0, out=None, lse=None) -> mla_decode_args:
         out = self.out if out is None else out
@@ -206,8 +212,8 @@ class DecodePlan:
         a.lse = lse.data_ptr()
         a.attn_sink = None
         a.topk_length = None
-        a.sched_meta = self.sched_meta.data_ptr()
-        a.num_splits = self.num_splits.data_ptr()
+        a.sched_meta = None if self.closed_form else self.sched_meta.data_ptr()
+        a.num_splits = None if self.closed_form else self.num_splits.data_ptr()
         a.o_accum = self.o_accum.data_ptr()
         a.lse_accum = self.lse_accum.data_ptr()
         a.o_accum_bytes = self.o_accum.numel() * 4

@@ -244,11 +244,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int dh = wave & 1;
 
-    const int32_t* meta = p.sched_meta + 8 * part;
-    const int begin_req = meta[0];
+    const PartPlan plan = plan_part(p, part);
+    const int begin_req = plan.begin_req;
     if (begin_req >= p.b) return;
-    const int end_req = meta[1], begin_block = meta[2], end_block = meta[3];
-    const int begin_split = meta[4];
+    const int end_req = plan.end_req, begin_block = plan.begin_block, end_block = plan.end_block;
+    const int begin_split = plan.begin_split;
     const int nblocks = (p.topk + p.block - 1) / p.block;
 
     const uint32_t lds0 = lds_u32(lds);
@@ -580,7 +580,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             const float l = *(const LDS_AS float*)(lds + L_LM + 8 * (32 * hb + n));
             inv[hb] = l > 0.f ? 1.0f / l : 0.f;
         }
-        const int nsplit = p.num_splits[req + 1] - p.num_splits[req];
+        const int first_split = split_prefix(p, req);
+        const int nsplit = split_prefix(p, req + 1) - first_split;
         const int own_head = 32 * wave + n;
         if (nsplit == 1) {
             uint16_t* obase = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss;
@@ -603,7 +604,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         } else {
             // normalised partial O/l as bf16 in the lanes' own layout (packed
             // partials, see combine_packed_kernel) and lse in base 2
-            const int split = req == begin_req ? begin_split : p.num_splits[req];
+            const int split = req == begin_req ? begin_split : first_split;
             const int64_t row0 = ((int64_t)split * p.s_q + sq) * p.h_q;
             u32x4* dst = packed_partial(p, split, sq) + (int64_t)wave * 32 * 64 + lane;
 #pragma unroll
@@ -685,51 +686,52 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
 // step 16): one wave per (query column, output block i = 4 j + hb of decode
 // wave w), 64 waves per column.  M = max_s lse_s (base 2), w_s = 2^(lse_s - M)
 // / sum, out = sum_s w_s O_s, lse = (M + log2 sum) ln 2; out 0 and lse +inf
-// when no split saw a valid key.  Loads of up to four splits are issued
-// together.
+// when no split saw a valid key.  Splits are taken four at a time with their
+// lse and partial loads issued together (one memory round trip per batch);
+// a later batch with a larger max rescales what was accumulated so far.
 __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     const int qi = blockIdx.x, piece = blockIdx.y;          // piece = 16 w + 4 j + hb
     const int req = qi / p.s_q, sq = qi % p.s_q;
-    const int first = p.num_splits[req];
-    const int ns = p.num_splits[req + 1] - first;
+    const int first = split_prefix(p, req);
+    const int ns = split_prefix(p, req + 1) - first;
     if (ns <= 1) return;
     const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
     const int w = piece >> 4, j = (piece >> 2) & 3, hb = piece & 3;
     const int head = 32 * hb + n;
     const float* lse_col = p.lse_accum + (int64_t)first * p.s_q * p.h_q + (int64_t)sq * p.h_q + head;
     const int64_t lse_step = (int64_t)p.s_q * p.h_q;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += 4) {
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = s0 + u < ns ? lse_col[(s0 + u) * lse_step] : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) M = fmaxf(M, v[u]);
-    }
-    float W = 0.f;
+    const int64_t kofs = (int64_t)w * 32 * 64 + (2 * (4 * j + hb)) * 64 + lane;
+    float M = -INFINITY, W = 0.f;
     f32x16 acc = {};
-    if (M != -INFINITY) {
-        const int64_t kofs = (int64_t)w * 32 * 64 + (2 * (4 * j + hb)) * 64 + lane;
-        for (int s0 = 0; s0 < ns; s0 += 4) {
-            float ws[4];
-            u32x4 raw[4][2];
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+        float lv[4];
+        u32x4 raw[4][2];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int s = min(s0 + u, ns - 1);
-                ws[u] = s0 + u < ns ? __builtin_amdgcn_exp2f(lse_col[s * lse_step] - M) : 0.f;
-                const u32x4* src = packed_partial(p, first + s, sq) + kofs;
-                raw[u][0] = src[0];
-                raw[u][1] = src[64];
-            }
+        for (int u = 0; u < 4; ++u) {
+            const int s = min(s0 + u, ns - 1);
+            lv[u] = lse_col[s * lse_step];
+            const u32x4* src = packed_partial(p, first + s, sq) + kofs;
+            raw[u][0] = src[0];
+            raw[u][1] = src[64];
+        }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                W += ws[u];
+        for (int u = 0; u < 4; ++u)
+            if (s0 + u >= ns) lv[u] = -INFINITY;
+        const float Mn = fmaxf(fmaxf(M, fmaxf(lv[0], lv[1])), fmaxf(lv[2], lv[3]));
+        if (Mn == -INFINITY) continue;                     // no valid key so far
+        const float keep = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M is -inf
+        W *= keep;
+        acc *= keep;
+        M = Mn;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t word = raw[u][e >> 3][(e >> 1) & 3];
-                    const float x = __builtin_bit_cast(float, (e & 1) ? (word & 0xffff0000u) : (word << 16));
-                    acc[e] += ws[u] * x;
-                }
+        for (int u = 0; u < 4; ++u) {
+            const float ws = __builtin_amdgcn_exp2f(lv[u] - M);
+            W += ws;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t word = raw[u][e >> 3][(e >> 1) & 3];
+                const float x = __builtin_bit_cast(float, (e & 1) ? (word & 0xffff0000u) : (word << 16));
+                acc[e] += ws * x;
             }
         }
     }

@@ -61,6 +61,8 @@ int resolve(const mla_shape* in, mla::ResolvedShape* out) {
     if (block < 32 || block % 32 != 0)
         return fail(MLA_ERR_INVALID_ARG, "split_granularity must be a positive multiple of 32 (got %d)",
                     s.split_granularity);
+    if ((int64_t)s.b * ((s.topk + block - 1) / block) >= (int64_t)1 << 30)
+        return fail(MLA_ERR_INVALID_ARG, "b * ceil(topk / split_granularity) must be below 2^30");
     int overhead = s.fixed_overhead < 0 ? 5 : s.fixed_overhead;
     if (overhead > (1 << 20)) return fail(MLA_ERR_INVALID_ARG, "fixed_overhead too large (%d)", overhead);
     int parts = s.num_parts;
@@ -103,8 +105,11 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     const mla::ResolvedShape& r = *rs;
     if (!a->q || !a->kv || !a->indices || !a->out || !a->lse)
         return fail(MLA_ERR_INVALID_ARG, "q, kv, indices, out and lse must be non-NULL");
-    if (!a->sched_meta || !a->num_splits)
-        return fail(MLA_ERR_INVALID_ARG, "sched_meta and num_splits must be non-NULL (mla_get_sched_meta)");
+    const bool inline_plan = !a->sched_meta && !a->num_splits;
+    if (!inline_plan && (!a->sched_meta || !a->num_splits))
+        return fail(MLA_ERR_INVALID_ARG, "sched_meta and num_splits must both be set (mla_get_sched_meta) or both NULL");
+    if (inline_plan && r.overhead != 0)
+        return fail(MLA_ERR_INVALID_ARG, "a NULL plan (closed form) needs fixed_overhead 0, got %d", r.overhead);
     if (a->attn_sink) return fail(MLA_ERR_UNSUPPORTED, "attn_sink is not supported by this build");
     if (a->topk_length) return fail(MLA_ERR_UNSUPPORTED, "topk_length is not supported by this build");
     if (!aligned(a->q, 16) || a->q_stride_h % 8 || a->q_stride_s % 8 || a->q_stride_b % 8)
@@ -171,6 +176,23 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     }
     p->packed_partials = r.kv_format == MLA_KV_FP8_656 && r.h_q == 128;
     p->block = r.block;
+    {
+        // closed-form plan constants (used by the kernels only when the plan
+        // pointers are NULL); resolve() keeps b * B below 2^31
+        const int64_t B = (r.topk + r.block - 1) / r.block, T = (int64_t)r.b * B;
+        const int64_t P = (T + r.num_parts - 1) / r.num_parts;
+        int64_t x = B, y = P;
+        while (y) {
+            const int64_t t = x % y;
+            x = y;
+            y = t;
+        }
+        p->plan_nblk = (uint32_t)B;
+        p->plan_total = (uint32_t)T;
+        p->plan_payload = (uint32_t)P;
+        p->plan_gb = (uint32_t)(B / x);
+        p->plan_gp = (uint32_t)(P / x);
+    }
     p->c = sm * 1.4426950408889634f;
     p->threshold = mla::kRefGapLog2;
     return MLA_OK;

@@ -28,7 +28,7 @@ struct DecodeParams {
     uint16_t* out;
     int64_t out_sb, out_ss, out_sh;
     float* lse;
-    const int32_t* sched_meta;
+    const int32_t* sched_meta;      // NULL: closed-form plan (plan_part / split_prefix)
     const int32_t* num_splits;
     float* o_accum;
     float* lse_accum;
@@ -38,10 +38,70 @@ struct DecodeParams {
     uint32_t page_magic;            // t / page_block_size == (mulhi(t, page_magic) + t) >> page_mshift
     int page_mshift;                // for 0 <= t < 2^31 (round-up reciprocal)
     int packed_partials;            // split partials as packed bf16 (128-head FP8 decode)
+    // closed-form plan (per-request cost zero): B blocks per request, total
+    // b * B blocks, partitions of `payload` blocks; gb = B / gcd(B, payload),
+    // gp = payload / gcd(B, payload).  All below 2^31.
+    uint32_t plan_nblk, plan_total, plan_payload, plan_gb, plan_gp;
     float c;                        // sm_scale * log2(e)
     float threshold;                // log2-units gap above the reference max that
                                     // makes a piece recompute with a higher reference
 };
+
+// One partition of the plan: requests begin_req..end_req (inclusive), blocks
+// [begin_block, end_block) of end_req, its first piece has split index
+// begin_split; begin_req >= b marks an idle partition.
+struct PartPlan {
+    int begin_req, end_req, begin_block, end_block, begin_split;
+};
+
+// Partition `part` of the plan, read from the scheduler's output or, with no
+// scheduler output, evaluated in closed form.  With zero per-request cost the
+// greedy fill ("FlashMLA Sparse Decode 完整计算过程详解", step 3) cuts the
+// request-major sequence of T = b B blocks into consecutive runs of
+// payload = ceil(T / num_parts) blocks: partition q holds blocks
+// [q payload, min((q + 1) payload, T)).  Its pieces are the requests that run
+// meets, so the pieces before it number
+//   sum_{q' < q} (floor(e_q' / B) - floor(s_q' / B) + 1)
+//     = q + floor((q payload - 1) / B) - #{0 < q' < q : B divides q' payload}
+// (the sum telescopes; a boundary that is also a request boundary adds no
+// piece), and B divides q' payload exactly when gb divides q'.
+__device__ __forceinline__ PartPlan plan_part(const DecodeParams& p, int part) {
+    PartPlan r;
+    if (p.sched_meta != nullptr) {
+        const int32_t* m = p.sched_meta + 8 * part;
+        r.begin_req = m[0];
+        r.end_req = m[1];
+        r.begin_block = m[2];
+        r.end_block = m[3];
+        r.begin_split = m[4];
+        return r;
+    }
+    const uint32_t B = p.plan_nblk, P = p.plan_payload, T = p.plan_total, q = (uint32_t)part;
+    const uint32_t s0 = q * P;
+    if (s0 >= T) {
+        r.begin_req = r.end_req = p.b;
+        r.begin_block = r.end_block = r.begin_split = 0;
+        return r;
+    }
+    const uint32_t e = min(s0 + P, T) - 1;
+    r.begin_req = (int)(s0 / B);
+    r.end_req = (int)(e / B);
+    r.begin_block = (int)(s0 % B);
+    r.end_block = (int)(e % B) + 1;
+    r.begin_split = q == 0 ? 0 : (int)(q + (s0 - 1) / B - (q - 1) / p.plan_gb);
+    return r;
+}
+
+// Split index of the first piece of request r (the number of pieces at r = b).
+// Closed form as above: request r' covers partitions floor(r' B / payload) ..
+// floor(((r' + 1) B - 1) / payload), so the pieces before request r number
+//   r + floor((r B - 1) / payload) - #{0 < r' < r : payload divides r' B}.
+__device__ __forceinline__ int split_prefix(const DecodeParams& p, int r) {
+    if (p.num_splits != nullptr) return p.num_splits[r];
+    if (r == 0) return 0;
+    const uint32_t u = (uint32_t)r;
+    return (int)(u + (u * p.plan_nblk - 1) / p.plan_payload - (u - 1) / p.plan_gp);
+}
 
 // A tile whose max score exceeds the reference (the first valid tile's max) by
 // more than this many log2 units triggers a recompute.  Below it p <= 2^64, so

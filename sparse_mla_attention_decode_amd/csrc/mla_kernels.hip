@@ -415,11 +415,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
     const int n = lane & 31, h = lane >> 5;
     const int head = 32 * wave + n;
 
-    const int32_t* meta = p.sched_meta + 8 * part;
-    const int begin_req = meta[0];
+    const PartPlan plan = plan_part(p, part);
+    const int begin_req = plan.begin_req;
     if (begin_req >= p.b) return;
-    const int end_req = meta[1], begin_block = meta[2], end_block = meta[3];
-    const int begin_split = meta[4];
+    const int end_req = plan.end_req, begin_block = plan.begin_block, end_block = plan.end_block;
+    const int begin_split = plan.begin_split;
     const int nblocks = (p.topk + p.block - 1) / p.block;
     const int qk_base = n * KROW + 16 * h;          // score operand: key n, dims 16j + 8h
     const int pv_base = pv_read_base(lane);
@@ -588,7 +588,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int mb = 0; mb < 16; ++mb) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[mb]));
         const float l_tot = l_part + __shfl_xor(l_part, 32);
-        const int nsplit = p.num_splits[req + 1] - p.num_splits[req];
+        const int first_split = split_prefix(p, req);
+        const int nsplit = split_prefix(p, req + 1) - first_split;
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
         if (nsplit == 1) {
             uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss +
@@ -607,7 +608,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
                 p.lse[((int64_t)req * p.h_q + head) * p.s_q + sq] =
                     l_tot > 0.f ? (__log2f(l_tot) + m_ref) * 0.69314718055994531f : INFINITY;
         } else {
-            const int split = req == begin_req ? begin_split : p.num_splits[req];
+            const int split = req == begin_req ? begin_split : first_split;
             const int64_t base = ((int64_t)split * p.s_q + sq) * p.h_q + head;
             float* orow = p.o_accum + base * 512;
 #pragma unroll
@@ -689,8 +690,8 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
     const int lane = threadIdx.x & 63;
     const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (head >= p.h_q) return;
-    const int first = p.num_splits[req];
-    const int ns = p.num_splits[req + 1] - first;
+    const int first = split_prefix(p, req);
+    const int ns = split_prefix(p, req + 1) - first;
     if (ns <= 1) return;
     auto lse_at = [&](int j) {
         return p.lse_accum[((int64_t)(first + j) * p.s_q + sq) * p.h_q + head];

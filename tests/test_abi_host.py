@@ -105,7 +105,8 @@ def _args(s, **over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), M.MLA_ERR_INVALID_ARG), (dict(kv=None), M.MLA_ERR_INVALID_ARG),
-    (dict(sched_meta=None), M.MLA_ERR_INVALID_ARG),
+    (dict(sched_meta=None), M.MLA_ERR_INVALID_ARG), (dict(num_splits=None), M.MLA_ERR_INVALID_ARG),
+    (dict(sched_meta=None, num_splits=None), M.MLA_ERR_INVALID_ARG),   # NULL plan needs overhead 0
     (dict(attn_sink=0xA000), M.MLA_ERR_UNSUPPORTED), (dict(topk_length=0xA000), M.MLA_ERR_UNSUPPORTED),
     (dict(q=0x1008), M.MLA_ERR_INVALID_ARG), (dict(q_stride_h=580), M.MLA_ERR_INVALID_ARG),
     (dict(kv_stride_block=64 * 656 - 16), M.MLA_ERR_INVALID_ARG), (dict(kv=0x2004), M.MLA_ERR_INVALID_ARG),
@@ -140,6 +141,54 @@ def test_host_plan_matches_oracle(b, topk, parts, gran, ovh):
     want, prefix = O.sched_plan([topk] * b, gran, ovh, parts)
     assert ns.tolist() == prefix
     assert [tuple(m[:7]) for m in meta.tolist()] == [tuple(w) for w in want]
+
+
+def _closed_form_plan(b, topk, gran, parts):
+    """The plan the kernels evaluate for a NULL plan (per-request cost 0):
+    partition q takes blocks [q p, min((q + 1) p, T)) of the request-major
+    block sequence; the split counts come from the telescoped sums."""
+    from math import gcd
+    B = -(-topk // gran)
+    T = b * B
+    P = -(-T // parts)
+    gb, gp = B // gcd(B, P), P // gcd(B, P)
+    rows = []
+    for q in range(parts):
+        s0 = q * P
+        if s0 >= T:
+            rows.append(None)
+            continue
+        e = min(s0 + P, T) - 1
+        split = 0 if q == 0 else q + (s0 - 1) // B - (q - 1) // gb
+        rows.append((s0 // B, e // B, s0 % B, e % B + 1, split))
+    prefix = [0] + [r + (r * B - 1) // P - (r - 1) // gp for r in range(1, b + 1)]
+    return rows, prefix
+
+
+@pytest.mark.parametrize("b,topk,parts,gran", [
+    (64, 2048, 256, 32), (64, 2048, 256, 64), (2, 128, 66, 64), (4, 2048, 128, 32), (4, 2048, 130, 32),
+    (3, 100, 7, 32), (1, 1, 1, 64), (17, 33, 300, 32), (128, 2048, 256, 32), (5, 96, 3, 32),
+    (7, 320, 9, 32), (6, 192, 4, 32), (1, 4096, 256, 32), (33, 1500, 200, 32), (12, 64, 16, 32),
+])
+def test_closed_form_plan_matches_greedy(b, topk, parts, gran):
+    """With zero per-request cost the greedy fill of the walkthrough's step 3
+    equals the closed form the kernels use when the plan pointers are NULL."""
+    rows, prefix = _closed_form_plan(b, topk, gran, parts)
+    want, want_prefix = O.sched_plan([topk] * b, gran, 0, parts)
+    assert prefix == want_prefix
+    for got, w in zip(rows, want):
+        if got is None:
+            assert w[0] == b
+        else:
+            assert got == tuple(w[:5])
+
+
+def test_closed_form_plan_accepted_with_zero_overhead():
+    s = shape(fixed_overhead=0)
+    # the plan check passes; the kv stride (checked after it) is what fails
+    with pytest.raises(M.MlaError) as e:
+        M.mla_sparse_decode_fwd(_args(s, sched_meta=None, num_splits=None, kv_stride_block=16), stream=0)
+    assert "kv_stride_block" in str(e.value)
 
 
 def test_host_plan_reproduces_walkthrough_example():

@@ -21,18 +21,18 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _plan(w, **kw):
+def _plan(w, closed_form=False, **kw):
     shape = M.make_shape(w.b, w.s_q, w.h_q, w.topk, w.num_kv_tokens, w.kv_format,
                          w.page_block_size, **kw)
-    return M.DecodePlan(shape)
+    return M.DecodePlan(shape, closed_form=closed_form)
 
 
-def run_gpu(w, q=None, kv=None, idx=None, **kw):
+def run_gpu(w, q=None, kv=None, idx=None, closed_form=False, **kw):
     _need_gpu()
     q = w.q_device() if q is None else q
     kv = w.kv_device() if kv is None else kv
     idx = w.indices_device() if idx is None else idx
-    plan = _plan(w, **kw)
+    plan = _plan(w, closed_form=closed_form, **kw)
     out, lse = plan.run(q, kv, idx, w.sm_scale)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy(), plan
@@ -199,6 +199,43 @@ def test_reference_max_recompute_path():
         assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"jump parts={parts}")
 
 
+def _closed_vs_sched(w, tag, **kw):
+    """NULL plan (closed form in the kernels) against the scheduler's plan:
+    the same partition, so the same arithmetic, bit for bit."""
+    a = run_gpu(w, closed_form=True, fixed_overhead=0, **kw)
+    b = run_gpu(w, closed_form=False, fixed_overhead=0, **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), tag
+    return a
+
+
+@pytest.mark.parametrize("parts", [1, 3, 7, 66, 300])
+def test_closed_form_plan_cfg0(parts):
+    w = W.make_config(0)
+    out, lse, _ = _closed_vs_sched(w, f"cfg0 parts={parts}", num_parts=parts, split_granularity=32)
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"closed cfg0 parts={parts}")
+
+
+@pytest.mark.parametrize("kind", ["ragged", "h64", "bf16", "mtp"])
+def test_closed_form_plan_shapes(kind):
+    if kind == "ragged":
+        w = W.paged_decode("cf_ragged", 301, b=5, s_q=2, h_q=128, topk=257, tokens_per_seq=512, P=64)
+        kw = dict(num_parts=9, split_granularity=32)
+    elif kind == "h64":
+        w = W.paged_decode("cf_h64", 302, b=6, s_q=1, h_q=64, topk=300, tokens_per_seq=512, P=64)
+        kw = dict(num_parts=10, split_granularity=64)
+    elif kind == "bf16":
+        w = W.sparse_prefill("cf_bf16", 303, s_q=7, h_q=128, topk=90, s_kv=160, prior=100)
+        kw = dict(num_parts=4, split_granularity=32)
+    else:
+        w = W.paged_decode("cf_mtp", 304, b=4, s_q=2, h_q=128, topk=2048, tokens_per_seq=4096, P=64)
+        kw = dict(num_parts=130, split_granularity=32)
+    out, lse, _ = _closed_vs_sched(w, kind, **kw)
+    qs = all_queries(w)[:6]
+    ref_out, ref_lse = oracle(w, qs)
+    assert_parity(out, lse, ref_out, ref_lse, qs, f"closed {kind}")
+
+
 def test_deterministic():
     w = W.make_config(0)
     a = run_gpu(w)
@@ -278,6 +315,17 @@ def test_cfg1_production_all_queries(cfg1):
     out, lse, plan = run_gpu(w)
     ref_out, ref_lse = oracle(w)
     assert_parity(out, lse, ref_out, ref_lse, all_queries(w), "cfg1")
+
+
+def test_cfg1_closed_form_plan(cfg1):
+    """The benchmarked launch (NULL plan, 32-slot blocks, zero per-request
+    cost, 256 partitions): equal to the scheduler's plan bit for bit, and
+    sampled queries against the oracle."""
+    w = cfg1
+    out, lse, _ = _closed_vs_sched(w, "cfg1", num_parts=256, split_granularity=32)
+    qs = [(0, 0), (31, 0), (63, 0)]
+    ref_out, ref_lse = oracle(w, qs)
+    assert_parity(out, lse, ref_out, ref_lse, qs, "cfg1 closed")
 
 
 def test_cfg1_fine_split(cfg1):
