@@ -40,9 +40,10 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 # WRITE_SIZE 1048576 KiB -> x1.0).  Valid only for the kernel sources they were
 # taken on (sha256 below); for any other source the traffic is reported null.
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
-                         "sparse_mla_attention_decode_amd/csrc/device_common.h")
-DECODE_TRAFFIC = {"sources_sha256": "98e6524f405f69780b54e3d6c3759c513789a1ecac8ee1c9b65264418b750d3b",
-                  "fetch_kib": 54188.16, "fetch_scale": 2.0, "write_kib": 33920.0, "write_scale": 1.0}
+                         "sparse_mla_attention_decode_amd/csrc/device_common.h",
+                         "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
+DECODE_TRAFFIC = {"sources_sha256": "ba9f9b7a2cfdda43db8c00dc31cbe32c34fb47871d2ab23d7267cfcd02bbe319",
+                  "fetch_kib": 54179.8, "fetch_scale": 2.0, "write_kib": 32896.0, "write_scale": 1.0}
 
 
 def measured_traffic():
