@@ -298,25 +298,19 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             l_part = 0.f;
             __syncthreads();                        // LDS free (previous piece / pass done)
 
-            // ---- prologue: ids of tiles 0..2 (copied with Q on the first pass);
-            // copies of tiles 0..2 with the ids of tiles 3 and 4; copy source
-            // of tile 3; stage tile 0
+            // ---- prologue: ids of tiles 0..2, then (first pass) Q, whose loads
+            // are issued while the ids are on their way; copies of tiles 0 and
+            // 1 with the ids of tiles 3 and 4; copy sources of tiles 2 and 3;
+            // stage tile 0.  The copies of tile 2 are issued at the start of
+            // tile 0, so that tile 0 waits for neither them nor the copies of
+            // tile 3.
             uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles t .. t+3
             const uint8_t* src_nx;                  // this lane's copy source in tile t+3
+            const uint8_t* src2;                    // ... and in tile 2 (tile 0 only)
             int2 ids_nx;                            // its ids of tile t+4
             {
                 const int ln = opaque_lane();
                 for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
-                wait_vmcnt<0>();                    // ids of tiles 0..2
-                const uint8_t* src;
-                vm0 = tile_rows(0, ln, src);
-                gather_rows(src, ln, lds0 + slice_off);
-                copy_ids(idx, k_lo, k_hi, 3, ln, ids_wave);
-                vm1 = tile_rows(1, ln, src);
-                gather_rows(src, ln, lds0 + slice_off + RAW_BYTES);
-                copy_ids(idx, k_lo, k_hi, 4, ln, ids_wave + 128);
-                vm2 = tile_rows(2, ln, src);
-                gather_rows(src, ln, lds0 + slice_off + 2 * RAW_BYTES);
                 if (pass == 0) {
                     const uint16_t* qbase =
                         p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss + 288 * dh + 8 * (ln >> 5);
@@ -327,19 +321,27 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
                         qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_oth + 16 * j));
                     }
-                    // copies of tile 0 and the ids of tile 3 (13 newer copy ops and
-                    // the 36 loads of Q); Q itself is waited for where it is used
-                    wait_vmcnt<49>();
+                    // the 36 loads stay above the count below
+                    asm volatile("" ::: "memory");
+                    wait_vmcnt<36>();               // ids of tiles 0..2 (the 36 loads of Q are newer)
                 } else {
-                    wait_vmcnt<13>();               // copies of tile 0, ids of tile 3 (13 newer ops)
+                    wait_vmcnt<0>();                // ids of tiles 0..2
                 }
-                vm3 = tile_rows(3, ln, src_nx);
-                stage_rows(lds, slice_off, L_KB, wave, ln);
-                // Q (the newest loads) before tile 0's score MFMAs: waiting here
-                // keeps the compiler's own waits for Q out of the copy stream
-                // (unconditional, so the compiler sees Q complete on every path)
+                const uint8_t* src;
+                vm0 = tile_rows(0, ln, src);
+                gather_rows(src, ln, lds0 + slice_off);
+                copy_ids(idx, k_lo, k_hi, 3, ln, ids_wave);
+                vm1 = tile_rows(1, ln, src);
+                gather_rows(src, ln, lds0 + slice_off + RAW_BYTES);
+                copy_ids(idx, k_lo, k_hi, 4, ln, ids_wave + 128);
+                vm2 = tile_rows(2, ln, src2);
+                // Q, the copies of tiles 0 and 1 and the ids of tiles 3 and 4
+                // (unconditional and complete, so the compiler sees Q landed on
+                // every path and puts no waits of its own into the tile loop)
                 wait_vmcnt<0>();
-                ids_nx = read_ids(4, ln);           // landed with everything else
+                vm3 = tile_rows(3, ln, src_nx);
+                ids_nx = read_ids(4, ln);
+                stage_rows(lds, slice_off, L_KB, wave, ln);
             }
             __syncthreads();
 
@@ -353,8 +355,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // emptied by the staging of tile t) ride between them.  The operands
             // of the second value k-step are loaded into registers for phase 2,
             // and the partner's score partial goes to LDS.
-            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src3, int2 ids4, bf16x8 (&v1)[4],
-                              bf16x8 (&pf1)[4], const uint8_t*& src4, uint32_t& vm4) -> f32x16 {
+            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src2, const uint8_t* src3, int2 ids4,
+                              bf16x8 (&v1)[4], bf16x8 (&pf1)[4], const uint8_t*& src4, uint32_t& vm4) -> f32x16 {
                 const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
                 const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
                 const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
@@ -368,6 +370,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
                     va = v_frag(lds, vb);
                 }
+                // tile 0: the copies of tile 2 first (they are older than the
+                // ids of tile 5, as in every later tile)
+                if (src2 != nullptr) gather_rows(src2, ln, lds0 + slice_off + 2 * RAW_BYTES);
                 copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
                 __builtin_amdgcn_sched_barrier(0);
                 // 22 slots: value steps at 2, 6, 10, 14, score steps elsewhere
@@ -527,7 +532,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 const uint8_t* src4;
                 uint32_t vm4;
-                const f32x16 S = phase1(0, ln, false, src_nx, ids_nx, v1, pf1, src4, vm4);
+                const f32x16 S = phase1(0, ln, false, src2, src_nx, ids_nx, v1, pf1, src4, vm4);
                 __syncthreads();
                 phase2(S, vm0, 0, ln, false, v1, pf1, ids_nx);
                 src_nx = src4;
@@ -543,7 +548,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 const uint8_t* src4;
                 uint32_t vm4;
-                const f32x16 S = phase1(it, ln, true, src_nx, ids_nx, v1, pf1, src4, vm4);
+                const f32x16 S = phase1(it, ln, true, nullptr, src_nx, ids_nx, v1, pf1, src4, vm4);
                 __syncthreads();
                 phase2(S, vm0, it, ln, true, v1, pf1, ids_nx);
                 src_nx = src4;
