@@ -2,9 +2,9 @@
 // cache ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14).
 //
 // One work-group of 4 waves per scheduler partition; it walks the topk slots
-// of each (request, block range) piece in tiles of 32 keys.  Wave w is
-// (head group w/2, dim half dh = w%2) for the score contraction and owns
-// output dims [128w, 128w+128) of all 128 heads for the value contraction.
+// of each (request, block range) piece in tiles of 32 keys.  Wave w owns
+// heads [32w, 32w+32) for the score contraction and output dims
+// [128w, 128w+128) of all 128 heads for the value contraction.
 //
 //   gather   every wave copies its 8 rows of a tile (keys 8w..8w+7) HBM -> LDS
 //            with direct-to-LDS loads, three tiles ahead; the token ids are
@@ -13,24 +13,22 @@
 //   stage    every wave dequantises the NoPE chunks it copied (code *
 //            power-of-two scale -> bf16, exact) and moves the RoPE chunks
 //            into the staged tile [32 keys][576 bf16];
-//   S^T      = K Q^T over the wave's 288 dims for its 64 heads: each K
-//            fragment read from LDS feeds two MFMAs (36 per wave per tile);
-//            the partial for the partner's 32 heads is swapped through LDS, so
-//            wave w ends with full scores for heads [32w, 32w+32);
+//   S^T      = K Q^T over all 576 dims for the wave's 32 heads (36 MFMAs per
+//            tile, two accumulator chains), so no partial scores cross waves;
 //   softmax  base 2 on the accumulator, masked by slot validity, against a
 //            per-head reference max (see below); P rounded to bf16 and
-//            published in LDS;
+//            published in LDS (two buffers, by tile parity);
 //   O^T     += V^T P^T for the wave's 128 dims and all 128 heads: each V^T
 //            fragment (transposing LDS read) feeds four MFMAs (32 per tile);
 //            O^T [128 dims x 128 heads] lives in the 256 AGPRs.
 //
-// Tile loop, three phases per tile t separated by work-group barriers:
-//   1. S^T(t) MFMAs with the address/copy work for tile t+3 between them;
-//      partner partial -> LDS;
-//   2. softmax(t) interleaved with the value MFMAs of tile t-1 (one
-//      branch-free scheduling region);
-//   3. P(t) -> LDS and staging of tile t+1;
-// so the VALU work of the softmax runs under matrix-core work.
+// Tile loop, two phases per tile t separated by work-group barriers:
+//   A. S^T(t) MFMAs with the copies of tile t+3 and half of the dequant of
+//      tile t+1 between them; then the value MFMAs of tile t-1 with the
+//      softmax of tile t and the other half of the dequant between them;
+//      P(t) -> LDS;
+//   B. the dequantised rows of tile t+1 -> the K buffer tile t-1 released;
+// so the VALU work runs under matrix-core work.
 //
 // The reference max of a piece is the max score of its first tile holding a
 // valid key; later tiles are accumulated against it as long as no score
@@ -61,15 +59,15 @@ constexpr int KAHEAD = 3;                         // score fragments read ahead 
 
 // LDS map (bytes).  The 16-byte pad at the end of every staged row is never
 // read by the contractions; row 0's pad of staged tile 0 holds the restart
-// flags.  The head statistics of the epilogue reuse the score-exchange area.
+// flags.  The head statistics of the epilogue reuse the P area.
+constexpr int XPB = NW * 2048;                          // P of one tile, all 128 heads
 constexpr int L_RAW = 0;                               // [3][4 slices][6][8 rows][8 chunks][16]
 constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;          // [2][32 rows][1168] bf16 K
-constexpr int L_XS = L_KB + 2 * KBB;                    // [4 dest waves][4][64 lanes][16]
-constexpr int L_XP = L_XS + NW * 4096;                  // [4 head blocks][2 k-steps][64][16]
-constexpr int L_IDS = L_XP + NW * 2048;                 // [4 waves][3 slots][32] int32
+constexpr int L_XP = L_KB + 2 * KBB;                    // [2][4 head blocks][2 k-steps][64][16]
+constexpr int L_IDS = L_XP + 2 * XPB;                   // [4 waves][3 slots][32] int32
 constexpr int L_BYTES = L_IDS + NW * IDS_SLOTS * 128;
 constexpr int L_FLAGS = L_KB + 1152;                    // [4] restart flags (row pad)
-constexpr int L_LM = L_XS;                              // [128 heads] {l, m} (epilogue)
+constexpr int L_LM = L_XP;                              // [128 heads] {l, m} (epilogue)
 static_assert(L_BYTES <= 160 * 1024, "LDS budget");
 static_assert(NDMA == 6 && RCH - 8 * (NDMA - 1) == 1, "copy layout");
 
@@ -160,6 +158,45 @@ __device__ __forceinline__ StageRegs stage_load(const LDS_AS uint8_t* lds, int s
     g.rope = lds_read16(lds, slice + raw_off(r, c0 ? 32 + c0 : 40));
     return g;
 }
+// Converted rows of one wave's staging share: chunks c0 + 8 i (i = 0..3) as
+// 2 x 16 bytes of bf16 each, and the RoPE chunk.
+struct StagedRows {
+    u32x4 d[8];
+    u32x4 rope;
+};
+template <int I>
+__device__ __forceinline__ void stage_convert(const StageRegs& g, StagedRows& o) {
+    const u32x4 w = g.w[I];
+    const float sc = g.sc[I];
+    o.d[2 * I] = u32x4{dequant2<false>(w[0], sc), dequant2<true>(w[0], sc),
+                       dequant2<false>(w[1], sc), dequant2<true>(w[1], sc)};
+    o.d[2 * I + 1] = u32x4{dequant2<false>(w[2], sc), dequant2<true>(w[2], sc),
+                           dequant2<false>(w[3], sc), dequant2<true>(w[3], sc)};
+}
+// Quarter K of chunk I (codes w[I][K]: two dwords of bf16) converted at the
+// point of the call: the empty asm statements keep the conversion from being
+// hoisted or sunk across the surrounding matrix instructions.
+template <int I, int K>
+__device__ __forceinline__ void convert_here(const StageRegs& g, StagedRows& o) {
+    uint32_t w = g.w[I][K];
+    float sc = g.sc[I];
+    asm volatile("" : "+v"(w), "+v"(sc));
+    uint32_t lo = dequant2<false>(w, sc), hi = dequant2<true>(w, sc);
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    o.d[2 * I + K / 2][2 * (K & 1)] = lo;
+    o.d[2 * I + K / 2][2 * (K & 1) + 1] = hi;
+}
+__device__ __forceinline__ void stage_write(LDS_AS uint8_t* lds, const StagedRows& o, int kb, int wave, int lane) {
+    const int r = lane >> 3, c0 = lane & 7;
+    const int row = kb + (WROWS * wave + r) * KP;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int off = row + 32 * (c0 + 8 * i);
+        lds_write16(lds, off, o.d[2 * i]);
+        lds_write16(lds, off + 16, o.d[2 * i + 1]);
+    }
+    lds_write16(lds, row + 1024 + 16 * (c0 ? c0 - 1 : 7), o.rope);
+}
 __device__ __forceinline__ void stage_store(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
     const int r = lane >> 3, c0 = lane & 7;
     const int row = kb + (WROWS * wave + r) * KP;
@@ -242,7 +279,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     // wave-uniform values live in scalar registers; lane-derived offsets are
     // recomputed where they are used (opaque_lane) instead of being held
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int dh = wave & 1;
 
     const PartPlan plan = plan_part(p, part);
     const int begin_req = plan.begin_req;
@@ -285,11 +321,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             return rows_from(tile, ln, read_ids(tile, ln), src);
         };
 
-        // Q as B operands, loaded once per request (on the first pass, after the
-        // copies of the first tiles are on their way): qa = this wave's own heads
-        // 32w + n, qb = the partner wave's heads; k-step j covers dims
-        // 288 dh + 16 j + 8 h .. +7
-        bf16x8 qa[18], qb[18];
+        // Q as B operands of the score contraction, loaded once per request:
+        // lane (n, h) holds dims 16 j + 8 h .. +7 of head 32w + n for k-step j
+        bf16x8 qa[36];
         f32x16 O[16];
         float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
         for (int pass = 0;; ++pass) {
@@ -312,15 +346,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
                 if (pass == 0) {
-                    const uint16_t* qbase =
-                        p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss + 288 * dh + 8 * (ln >> 5);
-                    const uint16_t* q_own = qbase + (int64_t)(32 * wave + (ln & 31)) * p.q_sh;
-                    const uint16_t* q_oth = qbase + (int64_t)(32 * (wave ^ 1) + (ln & 31)) * p.q_sh;
+                    const uint16_t* q_own = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss +
+                                            (int64_t)(32 * wave + (ln & 31)) * p.q_sh + 8 * (ln >> 5);
 #pragma unroll
-                    for (int j = 0; j < 18; ++j) {
-                        qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
-                        qb[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_oth + 16 * j));
-                    }
+                    for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
                     // the 36 loads stay above the count below
                     asm volatile("" ::: "memory");
                     wait_vmcnt<36>();               // ids of tiles 0..2 (the 36 loads of Q are newer)
@@ -347,168 +376,149 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 
             bool restart = false;
 
-            // Phase 1 of tile t: the score MFMAs of tile t (S^T partials for this
-            // wave's 64 heads over its 288 dims) and, with `pv`, the first
-            // k-step of the value MFMAs of tile t-1 (O^T += V^T P^T over this
-            // wave's 128 dims), 52 matrix instructions in one stream; the ids of
-            // tile t + 5 and the copies of tile t + 3 (into the raw buffer
-            // emptied by the staging of tile t) ride between them.  The operands
-            // of the second value k-step are loaded into registers for phase 2,
-            // and the partner's score partial goes to LDS.
-            auto phase1 = [&](int t, int ln, bool pv, const uint8_t* src2, const uint8_t* src3, int2 ids4,
-                              bf16x8 (&v1)[4], bf16x8 (&pf1)[4], const uint8_t*& src4, uint32_t& vm4) -> f32x16 {
-                const int qk = L_KB + (t & 1) * KBB + qk_base(ln, dh);
-                const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
+            // Phase A of tile t, one wave-local stream:
+            //  section 1: the 36 score MFMAs of tile t for this wave's 32 heads
+            //  over all 576 dims (two accumulator chains: even and odd k-steps),
+            //  with the ids of tile t+5 and the copies of tile t+3 (tile 0 also
+            //  issues the copies of tile 2 first); the raw rows of tile t+1 are
+            //  read into registers;
+            //  section 2: the 32 value MFMAs of tile t-1 (O^T += V^T P^T over
+            //  this wave's 128 dims, all 128 heads) with the softmax of tile t
+            //  and the dequantisation of tile t+1 between them; P(t) to LDS.
+            auto phaseA = [&](int t, int ln, bool pv, const uint8_t* src2, const uint8_t* src3, int2 ids4,
+                              uint32_t vm, const uint8_t*& src4, uint32_t& vm4, StagedRows& st) {
+                const int qk = L_KB + (t & 1) * KBB + qk_base(ln, 0);
                 const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
-                f32x16 S0, S1;
-                bf16x8 ka[KAHEAD], va, pf[4];
+                // copies of tile t+1 have landed (7 newer ops: ids of tile t+4,
+                // copies of tile t+2; for tile 0 nothing is in flight)
+                wait_vmcnt<7>();
+                f32x16 Sa, Sb;
+                bf16x8 ka[KAHEAD];
 #pragma unroll
                 for (int j = 0; j < KAHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
-                if (pv) {
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb)
-                        pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
-                    va = v_frag(lds, vb);
-                }
+                const StageRegs g = stage_load(lds, slice_off + ((t + 1) % NRAW) * RAW_BYTES, ln);
                 // tile 0: the copies of tile 2 first (they are older than the
                 // ids of tile 5, as in every later tile)
                 if (src2 != nullptr) gather_rows(src2, ln, lds0 + slice_off + 2 * RAW_BYTES);
                 copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
                 __builtin_amdgcn_sched_barrier(0);
-                // 22 slots: value steps at 2, 6, 10, 14, score steps elsewhere
-                int js = 0, jv = 0;
 #pragma unroll
-                for (int slot = 0; slot < 22; ++slot) {
-                    const bool vslot = slot == 2 || slot == 6 || slot == 10 || slot == 14;
-                    if (vslot) {
-                        if (pv) {
-                            bf16x8 vn;
-                            if (jv + 1 < 4) vn = v_frag(lds, vb + (jv + 1) * 64);
-#pragma unroll
-                            for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * jv + hb], va, pf[hb]);
-                            if (jv + 1 < 4) va = vn;
-                        }
-                        ++jv;
-                    } else {
-                        const bf16x8 cur = ka[js % KAHEAD];
-                        if (js + KAHEAD < 18)
-                            ka[js % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + KAHEAD)));
-                        if (js == 0) {
-                            mfma_qk_first(S0, cur, qa[0]);
-                            mfma_qk_first(S1, cur, qb[0]);
-                        } else {
-                            mfma_qk(S0, cur, qa[js]);
-                            mfma_qk(S1, cur, qb[js]);
-                        }
-                        ++js;
-                    }
-                    if (slot >= 3 && slot <= 15 && slot % 3 == 0)
-                        dma16(src3 + 128 * (slot / 3 - 1), __builtin_amdgcn_readfirstlane(slice3 + 1024u * (slot / 3 - 1)));
-                    if (slot == 18) gather_tail(src3, ln, slice3);
-                    if (slot == 1) vm4 = rows_from(t + 4, ln, ids4, src4);
+                for (int js = 0; js < 36; ++js) {
+                    const bf16x8 cur = ka[js % KAHEAD];
+                    if (js + KAHEAD < 36)
+                        ka[js % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + KAHEAD)));
+                    if (js == 0) mfma_qk_first(Sa, cur, qa[0]);
+                    else if (js == 1) mfma_qk_first(Sb, cur, qa[1]);
+                    else if (js & 1) mfma_qk(Sb, cur, qa[js]);
+                    else mfma_qk(Sa, cur, qa[js]);
+                    if (js == 1) vm4 = rows_from(t + 4, ln, ids4, src4);
+                    if (js >= 3 && js <= 23 && js % 5 == 3)
+                        dma16(src3 + 128 * (js / 5), __builtin_amdgcn_readfirstlane(slice3 + 1024u * (js / 5)));
+                    if (js == 28) gather_tail(src3, ln, slice3);
+                    // two chunks of the dequantisation under the matrix work
+                    // (the empty asm statements keep the conversion where it is)
+                    if (js == 6) convert_here<0, 0>(g, st);
+                    if (js == 9) convert_here<0, 1>(g, st);
+                    if (js == 12) convert_here<0, 2>(g, st);
+                    if (js == 15) convert_here<0, 3>(g, st);
+                    if (js == 18) convert_here<1, 0>(g, st);
+                    if (js == 21) convert_here<1, 1>(g, st);
+                    if (js == 24) convert_here<1, 2>(g, st);
+                    if (js == 27) convert_here<1, 3>(g, st);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                mfma_result_fence2(Sa, Sb);
+                f32x16 S = Sa + Sb;
+                const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
+                const int xp_rd = L_XP + ((t + 1) & 1) * XPB;      // P of tile t-1
+                const int xp_wr = L_XP + (t & 1) * XPB;            // P of tile t
+                bf16x8 va, pf[4];
                 if (pv) {
-                    // operands of the second value k-step (keys 16..31), once the
-                    // score fragments no longer need their registers
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v1[j] = v_frag(lds, vb + 16 * KP + j * 64);
 #pragma unroll
                     for (int hb = 0; hb < 4; ++hb)
-                        pf1[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                        pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 16 * ln));
+                    va = v_frag(lds, vb);
                 }
-                mfma_result_fence2(S0, S1);
+                float mx, psum = 0.f;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const f32x4 v = {S1[4 * c], S1[4 * c + 1], S1[4 * c + 2], S1[4 * c + 3]};
-                    *(LDS_AS f32x4*)(lds + L_XS + (wave ^ 1) * 4096 + 1024 * c + 16 * ln) = v;
-                }
-                return S0;
-            };
-            // Phase 2 of tile t: with `pv` the second value k-step of tile t-1
-            // (16 MFMAs on operands already in registers) under the softmax of
-            // tile t (add the partner's partial, mask empty slots, base-2
-            // exponent against the reference max); P of both k-steps to LDS for
-            // every wave's value MFMAs, the staging of tile t + 1 into the K
-            // buffer the value MFMAs of tile t - 1 have released, and the copy
-            // source of tile t + 4.  Past the piece the staged rows are zero rows.
-            auto phase2 = [&](f32x16 S, uint32_t vm, int t, int ln, bool pv, const bf16x8 (&v1)[4],
-                              const bf16x8 (&pf1)[4], int2& ids5) {
-                // copies of tile t+1 have landed (14 newer ops: ids of tile t+4,
-                // copies of tile t+2, ids of tile t+5, copies of tile t+3)
-                wait_vmcnt<14>();
-                {
-                    f32x4 xs[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        xs[c] = *(const LDS_AS f32x4*)(lds + L_XS + wave * 4096 + 1024 * c + 16 * ln);
+                for (int jv = 0; jv < 8; ++jv) {
+                    // value step jv: k-step jv / 4, dim block jv % 4; the next V^T
+                    // fragment is read ahead
                     if (pv) {
+                        bf16x8 vn;
+                        if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * KP + ((jv + 1) & 3) * 64);
 #pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) mfma_pv(O[hb], v1[0], pf1[hb]);
+                        for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
+                        if (jv == 3) {
+#pragma unroll
+                            for (int hb = 0; hb < 4; ++hb)
+                                pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 1024 + 16 * ln));
+                        }
+                        if (jv + 1 < 8) va = vn;
                     }
+                    if (jv == 0) {
+                        if (vm != 0xffffffffu) {
+                            // accumulator element v holds key 8(v/4) + 4h + v%4:
+                            // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) S[v] += xs[v >> 2][v & 3];
-                }
-                const StageRegs g = stage_load(lds, slice_off + ((t + 1) % NRAW) * RAW_BYTES, ln);
-                if (pv) {
+                            for (int v = 0; v < 16; ++v) {
+                                const int key = 8 * (v >> 2) + (v & 3);
+                                const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
+                                                       ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
+                                S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
+                            }
+                        }
+                        mx = S[0];
 #pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 + hb], v1[1], pf1[hb]);
-                }
-                if (vm != 0xffffffffu) {
-                    // accumulator element v holds key 8(v/4) + 4h + v%4: lanes 0..31
-                    // test bit 8(v/4) + v%4 of the tile mask, lanes 32..63 that + 4
+                        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
+                    } else if (jv == 1) {
+                        // max with the other half-wave (same head): the swap hands
+                        // lanes 0..31 the upper half's value in the second result
+                        // and lanes 32..63 the lower half's in the first
+                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                        mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+                        const float mnew = mx * p.c;
+                        m_seen = fmaxf(m_seen, mnew);
+                        if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                        restart |= __any(mnew > m_ref + p.threshold);
+                    } else if (jv >= 2 && jv <= 5) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = 8 * (v >> 2) + (v & 3);
-                        const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
-                                               ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
-                        S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
+                        for (int v = 4 * (jv - 2); v < 4 * (jv - 1); ++v) {
+                            S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
+                            psum += S[v];
+                        }
+                        if (jv == 3) stage_convert<2>(g, st);
+
+                    } else if (jv == 6) {
+                        l_part += psum;
+                        lds_write16(lds, xp_wr + wave * 2048 + 16 * ln, p_fragment(S, 0));
+                        lds_write16(lds, xp_wr + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
+                    } else {
+                        stage_convert<3>(g, st);
+                        st.rope = g.rope;
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                float mx = S[0];
-#pragma unroll
-                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
-                {
-                    // max with the other half-wave (same head): the swap hands
-                    // lanes 0..31 the upper half's value in the second result
-                    // and lanes 32..63 the lower half's in the first
-                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                    mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-                }
-                const float mnew = mx * p.c;
-                m_seen = fmaxf(m_seen, mnew);
-                if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
-                restart |= __any(mnew > m_ref + p.threshold);
-                if (pv) {
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[8 + hb], v1[2], pf1[hb]);
-                }
-                float psum = 0.f;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
-                    psum += S[v];
-                }
-                l_part += psum;
-                if (pv) {
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[12 + hb], v1[3], pf1[hb]);
-                }
-                lds_write16(lds, L_XP + wave * 2048 + 16 * ln, p_fragment(S, 0));
-                lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
-                stage_store(lds, g, L_KB + ((t + 1) & 1) * KBB, wave, ln);
-                // ids of tile t+5 (issued at the start of phase 1; 6 newer ops:
-                // the copies of tile t+3) for the next phase 1's copy sources
+            };
+            // Phase B of tile t: the rows of tile t+1 (converted in phase A) into
+            // the K buffer the value MFMAs of tile t-1 have released; the ids of
+            // tile t+5 for the next copy sources.  Past the piece the staged rows
+            // are zero rows.
+            auto phaseB = [&](int t, int ln, const StagedRows& st, int2& ids5) {
+                stage_write(lds, st, L_KB + ((t + 1) & 1) * KBB, wave, ln);
+                // ids of tile t+5 (issued at the start of phase A; 6 newer ops:
+                // the copies of tile t+3)
                 wait_vmcnt<6>();
                 ids5 = read_ids(t + 5, ln);
             };
             // value MFMAs of the last tile
             auto values_only = [&](int t, int ln) {
                 const int vb = L_KB + (t & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
+                const int xp_rd = L_XP + (t & 1) * XPB;
                 bf16x8 pf[4];
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb)
-                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
+                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 16 * ln));
                 bf16x8 a_cur = v_frag(lds, vb);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
@@ -520,21 +530,21 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (s == 3) {
 #pragma unroll
                         for (int hb = 0; hb < 4; ++hb)
-                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 1024 + 16 * ln));
                     }
                     if (s + 1 < 8) a_cur = a_nxt;
                 }
             };
 
+            StagedRows st;
             // tile 0: no value work yet
-            bf16x8 v1[4], pf1[4];
             {
                 const int ln = opaque_lane();
                 const uint8_t* src4;
                 uint32_t vm4;
-                const f32x16 S = phase1(0, ln, false, src2, src_nx, ids_nx, v1, pf1, src4, vm4);
+                phaseA(0, ln, false, src2, src_nx, ids_nx, vm0, src4, vm4, st);
                 __syncthreads();
-                phase2(S, vm0, 0, ln, false, v1, pf1, ids_nx);
+                phaseB(0, ln, st, ids_nx);
                 src_nx = src4;
                 vm0 = vm1;
                 vm1 = vm2;
@@ -548,9 +558,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 const uint8_t* src4;
                 uint32_t vm4;
-                const f32x16 S = phase1(it, ln, true, nullptr, src_nx, ids_nx, v1, pf1, src4, vm4);
+                phaseA(it, ln, true, nullptr, src_nx, ids_nx, vm0, src4, vm4, st);
                 __syncthreads();
-                phase2(S, vm0, it, ln, true, v1, pf1, ids_nx);
+                phaseB(it, ln, st, ids_nx);
                 src_nx = src4;
                 vm0 = vm1;
                 vm1 = vm2;
