@@ -1,5 +1,8 @@
 // gfx950 sparse MLA decode for 128 query heads over the FP8 656-byte token
-// cache ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14).
+// cache ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14).  64 query
+// heads run the same layout: the upper two head blocks score copies of heads
+// 0..63 and are never stored (the kernel is bound by its per-tile gather,
+// dequant and LDS work, not by the matrix cores, so the idle MFMAs cost little).
 //
 // One work-group of 4 waves per scheduler partition; it walks the topk slots
 // of each (request, block range) piece in tiles of 32 keys.  Wave w owns
@@ -346,8 +349,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
                 if (pass == 0) {
+                    // with 64 query heads, waves 2 and 3 score copies of heads
+                    // 0..63 (their results are never stored)
                     const uint16_t* q_own = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss +
-                                            (int64_t)(32 * wave + (ln & 31)) * p.q_sh + 8 * (ln >> 5);
+                                            (int64_t)((32 * wave + (ln & 31)) & (p.h_q - 1)) * p.q_sh +
+                                            8 * (ln >> 5);
 #pragma unroll
                     for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
                     // the 36 loads stay above the count below
@@ -602,6 +608,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             uint16_t* obase = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss;
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) {
+                if (32 * hb >= p.h_q) break;                   // 64 heads: blocks 0 and 1 only
                 uint16_t* orow = obase + (int64_t)(32 * hb + n) * p.out_sh + 128 * wave + 4 * h;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -613,7 +620,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         *(u32x2*)(orow + 32 * j + 8 * g) = w;
                     }
             }
-            if (h == 0)
+            if (h == 0 && own_head < p.h_q)
                 p.lse[((int64_t)req * p.h_q + own_head) * p.s_q + sq] =
                     l_tot > 0.f ? (__log2f(l_tot) + m_ref) * 0.69314718055994531f : INFINITY;
         } else {
@@ -624,6 +631,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             u32x4* dst = packed_partial(p, split, sq) + (int64_t)wave * 32 * 64 + lane;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+                if (32 * (i & 3) >= p.h_q) continue;           // 64 heads: blocks 0 and 1 only
                 const f32x16& o = O[i];
                 const float sc = inv[i & 3];
 #pragma unroll
@@ -633,7 +641,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                                      pack_bf16(o[8 * half + 4] * sc, o[8 * half + 5] * sc),
                                                      pack_bf16(o[8 * half + 6] * sc, o[8 * half + 7] * sc)};
             }
-            if (h == 0) p.lse_accum[row0 + own_head] = l_tot > 0.f ? __log2f(l_tot) + m_ref : -INFINITY;
+            if (h == 0 && own_head < p.h_q) p.lse_accum[row0 + own_head] = l_tot > 0.f ? __log2f(l_tot) + m_ref : -INFINITY;
         }
         __syncthreads();                                       // head statistics read
     }
@@ -712,6 +720,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     if (ns <= 1) return;
     const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
     const int w = piece >> 4, j = (piece >> 2) & 3, hb = piece & 3;
+    if (32 * hb >= p.h_q) return;                            // 64 heads: blocks 0 and 1 only
     const int head = 32 * hb + n;
     const float* lse_col = p.lse_accum + (int64_t)first * p.s_q * p.h_q + (int64_t)sq * p.h_q + head;
     const int64_t lse_step = (int64_t)p.s_q * p.h_q;

@@ -74,7 +74,9 @@ int resolve(const mla_shape* in, mla::ResolvedShape* out) {
             (void)hipGetLastError();
             return fail(MLA_ERR_NO_DEVICE, "num_parts = 0 needs a device to read its CU count");
         }
-        const int wgs_per_cu = s.h_q == 128 ? 1 : 2;
+        // the FP8 kernel (128-head layout for 64 or 128 heads) needs all of a
+        // CU's LDS; the 64-head BF16 kernel fits two work-groups per CU
+        const int wgs_per_cu = (s.kv_format == MLA_KV_FP8_656 || s.h_q == 128) ? 1 : 2;
         parts = cus * wgs_per_cu / s.s_q;
         if (parts < 1) parts = 1;
     }
@@ -174,7 +176,7 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         p->page_mshift = l;
         p->page_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - P)) / P + 1);
     }
-    p->packed_partials = r.kv_format == MLA_KV_FP8_656 && r.h_q == 128;
+    p->packed_partials = r.kv_format == MLA_KV_FP8_656;
     p->block = r.block;
     {
         // closed-form plan constants (used by the kernels only when the plan

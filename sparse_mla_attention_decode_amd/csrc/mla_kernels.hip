@@ -761,8 +761,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, hipStrea
 
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
     if (kv_format == MLA_KV_FP8_656)
-        return p.h_q == 128 ? launch_decode_fp8_h128(p, num_parts, st)
-                            : launch_decode_t<MLA_KV_FP8_656, 2>(p, num_parts, st);
+        return launch_decode_fp8_h128(p, num_parts, st);
     return p.h_q == 128 ? launch_decode_t<MLA_KV_BF16_576, 4>(p, num_parts, st)
                         : launch_decode_t<MLA_KV_BF16_576, 2>(p, num_parts, st);
 }

@@ -160,6 +160,24 @@ def test_decode_empty_and_duplicate_slots():
         assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"edge parts={parts}")
 
 
+@pytest.mark.parametrize("parts", [0, 1, 5, 37])
+def test_decode_h64_fp8(parts):
+    """64 query heads on the FP8 cache run the 128-head kernel with the upper
+    head blocks scoring copies of heads 0..63 that are never stored: unsplit
+    (one partition) and split paths, empty and out-of-range slots."""
+    w = W.paged_decode("h64", 61, b=5, s_q=2, h_q=64, topk=200, tokens_per_seq=512, P=64)
+    w.indices[0, 0, :] = -1                               # no valid slot
+    w.indices[1, 1, 150:] = -1
+    w.indices[2, 0, 7] = w.num_kv_tokens + 9              # out of range
+    w = W._finish("h64", np.random.default_rng(62), w.kv_format, w.b, w.s_q, w.h_q, w.topk,
+                  w.page_block_size, w.num_kv_tokens, w.indices, q_bits=w.q_bits)
+    out, lse, _ = run_gpu(w, num_parts=parts, split_granularity=32)
+    assert out.shape == (5, 2, 64, 512) and lse.shape == (5, 64, 2)
+    ref_out, ref_lse = oracle(w)
+    assert np.all(out[0, 0] == 0) and np.all(np.isposinf(lse[0, :, 0]))
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"h64 parts={parts}")
+
+
 def test_single_repeated_row_is_exact():
     """All slots name one token: out = V of that row exactly (p = 1 for every
     slot, sums of equal bf16 values are exact), lse = score + ln(topk)."""
