@@ -10,28 +10,29 @@
 // [128w, 128w+128) of all 128 heads for the value contraction.
 //
 //   gather   every wave copies its 8 rows of a tile (keys 8w..8w+7) HBM -> LDS
-//            with direct-to-LDS loads, three tiles ahead; the token ids are
-//            copied into LDS the same way, so memory-counter waits are
+//            with direct-to-LDS loads into a ring of two raw slots; the token
+//            ids are copied into LDS the same way, so memory-counter waits are
 //            explicit and wave-local.  Empty slots copy rows of a zero page.
 //   stage    every wave dequantises the NoPE chunks it copied (code *
 //            power-of-two scale -> bf16, exact) and moves the RoPE chunks
-//            into the staged tile [32 keys][576 bf16];
+//            into a staged tile [32 keys][576 bf16]; three staged buffers;
 //   S^T      = K Q^T over all 576 dims for the wave's 32 heads (36 MFMAs per
 //            tile, two accumulator chains), so no partial scores cross waves;
 //   softmax  base 2 on the accumulator, masked by slot validity, against a
 //            per-head reference max (see below); P rounded to bf16 and
-//            published in LDS (two buffers, by tile parity);
+//            published in LDS;
 //   O^T     += V^T P^T for the wave's 128 dims and all 128 heads: each V^T
 //            fragment (transposing LDS read) feeds four MFMAs (32 per tile);
 //            O^T [128 dims x 128 heads] lives in the 256 AGPRs.
 //
-// Tile loop, two phases per tile t separated by work-group barriers:
-//   A. S^T(t) MFMAs with the copies of tile t+3 and half of the dequant of
-//      tile t+1 between them; then the value MFMAs of tile t-1 with the
-//      softmax of tile t and the other half of the dequant between them;
-//      P(t) -> LDS;
-//   B. the dequantised rows of tile t+1 -> the K buffer tile t-1 released;
-// so the VALU work runs under matrix-core work.
+// Tile loop, two parts per tile i separated by work-group barriers:
+//   1. the score MFMAs of tile i+1 with the softmax of tile i (its scores
+//      were computed one tile earlier), the copies of tile i+3 and the ids
+//      of tile i+5 between them; P(i) -> LDS;
+//   2. the value MFMAs of tile i with the dequant of tile i+2 written
+//      straight into the staged buffer that tile i-1 released;
+// so the VALU work runs under matrix-core work and no phase is left with
+// only LDS stores.
 //
 // The reference max of a piece is the max score of its first tile holding a
 // valid key; later tiles are accumulated against it as long as no score
@@ -53,24 +54,27 @@ constexpr int WROWS = TILE / NW;                  // rows gathered and staged pe
 constexpr int WAVE_RAW = WROWS * ROWB;            // 5248 bytes: one wave's slice
 constexpr int NDMA = (RCH + 7) / 8;               // 6 copies per lane per tile
 constexpr int RAW_BYTES = TILE * ROWB;            // 20992
-constexpr int NRAW = 3;                           // raw tiles in flight / in use
+constexpr int NRAW = 2;                           // raw tiles (one being staged, one landing)
+constexpr int NKB = 3;                            // staged tiles (scores, values, being staged)
 constexpr int KP = 1168;                          // staged row pitch (1152 + 16)
 constexpr int KBB = TILE * KP;                    // 37376
-constexpr int IDS_SLOTS = 3;                      // token-id tiles per wave in LDS
+constexpr int IDS_SLOTS = 2;                      // token-id tiles per wave in LDS
 constexpr int ZERO_ROWS = 64;                     // rows of the zero page
 constexpr int KAHEAD = 3;                         // score fragments read ahead of their MFMAs
 
 // LDS map (bytes).  The 16-byte pad at the end of every staged row is never
-// read by the contractions; row 0's pad of staged tile 0 holds the restart
-// flags.  The head statistics of the epilogue reuse the P area.
+// read by the contractions; row 0's pad of staged buffer 0 holds the restart
+// flags.  The ids of the first four tiles of a pass and the head statistics
+// of the epilogue use the P area.
 constexpr int XPB = NW * 2048;                          // P of one tile, all 128 heads
-constexpr int L_RAW = 0;                               // [3][4 slices][6][8 rows][8 chunks][16]
-constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;          // [2][32 rows][1168] bf16 K
-constexpr int L_XP = L_KB + 2 * KBB;                    // [2][4 head blocks][2 k-steps][64][16]
-constexpr int L_IDS = L_XP + 2 * XPB;                   // [4 waves][3 slots][32] int32
+constexpr int L_RAW = 0;                               // [2][4 slices][6][8 rows][8 chunks][16]
+constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;          // [3][32 rows][1168] bf16 K
+constexpr int L_XP = L_KB + NKB * KBB;                  // [4 head blocks][2 k-steps][64][16]
+constexpr int L_IDS = L_XP + XPB;                       // [4 waves][2 slots][32] int32
 constexpr int L_BYTES = L_IDS + NW * IDS_SLOTS * 128;
 constexpr int L_FLAGS = L_KB + 1152;                    // [4] restart flags (row pad)
 constexpr int L_LM = L_XP;                              // [128 heads] {l, m} (epilogue)
+constexpr int L_IDS0 = L_XP;                            // [4 waves][4 tiles][32] int32 (prologue)
 static_assert(L_BYTES <= 160 * 1024, "LDS budget");
 static_assert(NDMA == 6 && RCH - 8 * (NDMA - 1) == 1, "copy layout");
 
@@ -200,6 +204,21 @@ __device__ __forceinline__ void stage_write(LDS_AS uint8_t* lds, const StagedRow
     }
     lds_write16(lds, row + 1024 + 16 * (c0 ? c0 - 1 : 7), o.rope);
 }
+// Chunk I of this wave's staging share converted and written at once (the
+// target buffer is free): dims 16 (c0 + 8 I) .. +15 of row 8 wave + r.
+template <int I>
+__device__ __forceinline__ void stage_chunk(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
+    const int r = lane >> 3, c0 = lane & 7;
+    StagedRows o;
+    stage_convert<I>(g, o);
+    const int off = kb + (WROWS * wave + r) * KP + 32 * (c0 + 8 * I);
+    lds_write16(lds, off, o.d[2 * I]);
+    lds_write16(lds, off + 16, o.d[2 * I + 1]);
+}
+__device__ __forceinline__ void stage_rope(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
+    const int r = lane >> 3, c0 = lane & 7;
+    lds_write16(lds, kb + (WROWS * wave + r) * KP + 1024 + 16 * (c0 ? c0 - 1 : 7), g.rope);
+}
 __device__ __forceinline__ void stage_store(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
     const int r = lane >> 3, c0 = lane & 7;
     const int row = kb + (WROWS * wave + r) * KP;
@@ -268,8 +287,10 @@ __device__ __forceinline__ u32x4* packed_partial(const DecodeParams& p, int spli
     return (u32x4*)((uint16_t*)p.o_accum + ((int64_t)split * p.s_q + sq) * (128 * 512));
 }
 
+// Lane id from the lane-mask counters (no register has to keep the thread
+// id alive across the kernel).
 __device__ __forceinline__ int opaque_lane() {
-    int l = threadIdx.x & 63;
+    int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     asm volatile("" : "+v"(l));
     return l;
 }
@@ -291,9 +312,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     const int nblocks = (p.topk + p.block - 1) / p.block;
 
     const uint32_t lds0 = lds_u32(lds);
-    const uint32_t ids_wave = lds0 + L_IDS + wave * IDS_SLOTS * 128;
-    const int slice_off = L_RAW + wave * WAVE_RAW;            // this wave's slice in raw tile 0
-    if (threadIdx.x < 4) lds[L_FLAGS + threadIdx.x] = 0;   // ordered by the first barrier
+    const int slice_off = L_RAW + wave * WAVE_RAW;            // this wave's slice in raw slot 0
+    if (wave == 0 && opaque_lane() < 4) lds[L_FLAGS + opaque_lane()] = 0;   // ordered by the first barrier
 
     for (int req = begin_req; req <= end_req; ++req) {
         const int blk_lo = req == begin_req ? begin_block : 0;
@@ -303,11 +323,14 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
         const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
 
-        // ids of `tile` (copied earlier into its slot) that this lane needs: key
-        // ln % 32 (validity mask) and key 8w + ln / 8 (its copy row)
-        auto read_ids = [&](int tile, int ln) -> int2 {
-            const LDS_AS int32_t* slot =
-                (const LDS_AS int32_t*)(lds + L_IDS + (wave * IDS_SLOTS + tile % IDS_SLOTS) * 128);
+        // LDS slots of this wave's token ids: tile t in the ring (t % 2), the
+        // first four tiles of a pass in the prologue area
+        auto ring_slot = [&](int tile) -> int { return L_IDS + (wave * IDS_SLOTS + (tile & 1)) * 128; };
+        auto first_slot = [&](int tile) -> int { return L_IDS0 + wave * 512 + tile * 128; };
+        // ids that this lane needs from a slot: key ln % 32 (validity mask) and
+        // key 8w + ln / 8 (its copy row)
+        auto ids_at = [&](int slot_off, int ln) -> int2 {
+            const LDS_AS int32_t* slot = (const LDS_AS int32_t*)(lds + slot_off);
             return int2{slot[ln & 31], slot[WROWS * wave + (ln >> 3)]};
         };
         // validity mask of the tile's 32 keys and the copy source of this
@@ -320,9 +343,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             src = row_addr(p, id.y, okr, (tile * TILE + kr) & (ZERO_ROWS - 1)) + 16 * (ln & 7);
             return (uint32_t)__ballot(ok);
         };
-        auto tile_rows = [&](int tile, int ln, const uint8_t*& src) -> uint32_t {
-            return rows_from(tile, ln, read_ids(tile, ln), src);
-        };
 
         // Q as B operands of the score contraction, loaded once per request:
         // lane (n, h) holds dims 16 j + 8 h .. +7 of head 32w + n for k-step j
@@ -334,80 +354,25 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             for (int i = 0; i < 16; ++i) O[i] = f32x16{};
             l_part = 0.f;
             __syncthreads();                        // LDS free (previous piece / pass done)
-
-            // ---- prologue: ids of tiles 0..2, then (first pass) Q, whose loads
-            // are issued while the ids are on their way; copies of tiles 0 and
-            // 1 with the ids of tiles 3 and 4; copy sources of tiles 2 and 3;
-            // stage tile 0.  The copies of tile 2 are issued at the start of
-            // tile 0, so that tile 0 waits for neither them nor the copies of
-            // tile 3.
-            uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles t .. t+3
-            const uint8_t* src_nx;                  // this lane's copy source in tile t+3
-            const uint8_t* src2;                    // ... and in tile 2 (tile 0 only)
-            int2 ids_nx;                            // its ids of tile t+4
-            {
-                const int ln = opaque_lane();
-                for (int t = 0; t < 3; ++t) copy_ids(idx, k_lo, k_hi, t, ln, ids_wave + 128 * t);
-                if (pass == 0) {
-                    // with 64 query heads, waves 2 and 3 score copies of heads
-                    // 0..63 (their results are never stored)
-                    const uint16_t* q_own = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss +
-                                            (int64_t)((32 * wave + (ln & 31)) & (p.h_q - 1)) * p.q_sh +
-                                            8 * (ln >> 5);
-#pragma unroll
-                    for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
-                    // the 36 loads stay above the count below
-                    asm volatile("" ::: "memory");
-                    wait_vmcnt<36>();               // ids of tiles 0..2 (the 36 loads of Q are newer)
-                } else {
-                    wait_vmcnt<0>();                // ids of tiles 0..2
-                }
-                const uint8_t* src;
-                vm0 = tile_rows(0, ln, src);
-                gather_rows(src, ln, lds0 + slice_off);
-                copy_ids(idx, k_lo, k_hi, 3, ln, ids_wave);
-                vm1 = tile_rows(1, ln, src);
-                gather_rows(src, ln, lds0 + slice_off + RAW_BYTES);
-                copy_ids(idx, k_lo, k_hi, 4, ln, ids_wave + 128);
-                vm2 = tile_rows(2, ln, src2);
-                // Q, the copies of tiles 0 and 1 and the ids of tiles 3 and 4
-                // (unconditional and complete, so the compiler sees Q landed on
-                // every path and puts no waits of its own into the tile loop)
-                wait_vmcnt<0>();
-                vm3 = tile_rows(3, ln, src_nx);
-                ids_nx = read_ids(4, ln);
-                stage_rows(lds, slice_off, L_KB, wave, ln);
-            }
-            __syncthreads();
-
             bool restart = false;
 
-            // Phase A of tile t, one wave-local stream:
-            //  section 1: the 36 score MFMAs of tile t for this wave's 32 heads
-            //  over all 576 dims (two accumulator chains: even and odd k-steps),
-            //  with the ids of tile t+5 and the copies of tile t+3 (tile 0 also
-            //  issues the copies of tile 2 first); the raw rows of tile t+1 are
-            //  read into registers;
-            //  section 2: the 32 value MFMAs of tile t-1 (O^T += V^T P^T over
-            //  this wave's 128 dims, all 128 heads) with the softmax of tile t
-            //  and the dequantisation of tile t+1 between them; P(t) to LDS.
-            auto phaseA = [&](int t, int ln, bool pv, const uint8_t* src2, const uint8_t* src3, int2 ids4,
-                              uint32_t vm, const uint8_t*& src4, uint32_t& vm4, StagedRows& st) {
-                const int qk = L_KB + (t & 1) * KBB + qk_base(ln, 0);
-                const uint32_t slice3 = lds0 + slice_off + ((t + 3) % NRAW) * RAW_BYTES;
-                // copies of tile t+1 have landed (7 newer ops: ids of tile t+4,
-                // copies of tile t+2; for tile 0 nothing is in flight)
-                wait_vmcnt<7>();
+            // Part 1 of tile i: the 36 score MFMAs of tile i+1 (K buffer
+            // (i+1) % 3) for this wave's 32 heads over all 576 dims (two
+            // accumulator chains) with, between them, the softmax of tile i
+            // (mask empty slots, base-2 exponent against the reference max, P
+            // to LDS), the ids of tile i+5 and the copies of tile i+3.  With
+            // soft == false (the prologue) only the scores of tile 0.
+            auto part1 = [&](int i, int ln, bool soft, const uint8_t* src3, uint32_t vm, f32x16 S,
+                             f32x16& S_next) {
+                const int qk = L_KB + ((i + 1) % NKB) * KBB + qk_base(ln, 0);
+                const uint32_t slot3 = lds0 + slice_off + ((i + 3) & 1) * RAW_BYTES;
                 f32x16 Sa, Sb;
                 bf16x8 ka[KAHEAD];
 #pragma unroll
                 for (int j = 0; j < KAHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
-                const StageRegs g = stage_load(lds, slice_off + ((t + 1) % NRAW) * RAW_BYTES, ln);
-                // tile 0: the copies of tile 2 first (they are older than the
-                // ids of tile 5, as in every later tile)
-                if (src2 != nullptr) gather_rows(src2, ln, lds0 + slice_off + 2 * RAW_BYTES);
-                copy_ids(idx, k_lo, k_hi, t + 5, ln, ids_wave + 128 * ((t + 5) % IDS_SLOTS));
+                if (soft) copy_ids(idx, k_lo, k_hi, i + 5, ln, lds0 + ring_slot(i + 5));
                 __builtin_amdgcn_sched_barrier(0);
+                float mx, psum = 0.f;
 #pragma unroll
                 for (int js = 0; js < 36; ++js) {
                     const bf16x8 cur = ka[js % KAHEAD];
@@ -417,53 +382,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     else if (js == 1) mfma_qk_first(Sb, cur, qa[1]);
                     else if (js & 1) mfma_qk(Sb, cur, qa[js]);
                     else mfma_qk(Sa, cur, qa[js]);
-                    if (js == 1) vm4 = rows_from(t + 4, ln, ids4, src4);
-                    if (js >= 3 && js <= 23 && js % 5 == 3)
-                        dma16(src3 + 128 * (js / 5), __builtin_amdgcn_readfirstlane(slice3 + 1024u * (js / 5)));
-                    if (js == 28) gather_tail(src3, ln, slice3);
-                    // two chunks of the dequantisation under the matrix work
-                    // (the empty asm statements keep the conversion where it is)
-                    if (js == 6) convert_here<0, 0>(g, st);
-                    if (js == 9) convert_here<0, 1>(g, st);
-                    if (js == 12) convert_here<0, 2>(g, st);
-                    if (js == 15) convert_here<0, 3>(g, st);
-                    if (js == 18) convert_here<1, 0>(g, st);
-                    if (js == 21) convert_here<1, 1>(g, st);
-                    if (js == 24) convert_here<1, 2>(g, st);
-                    if (js == 27) convert_here<1, 3>(g, st);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                mfma_result_fence2(Sa, Sb);
-                f32x16 S = Sa + Sb;
-                const int vb = L_KB + ((t + 1) & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
-                const int xp_rd = L_XP + ((t + 1) & 1) * XPB;      // P of tile t-1
-                const int xp_wr = L_XP + (t & 1) * XPB;            // P of tile t
-                bf16x8 va, pf[4];
-                if (pv) {
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb)
-                        pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 16 * ln));
-                    va = v_frag(lds, vb);
-                }
-                float mx, psum = 0.f;
-#pragma unroll
-                for (int jv = 0; jv < 8; ++jv) {
-                    // value step jv: k-step jv / 4, dim block jv % 4; the next V^T
-                    // fragment is read ahead
-                    if (pv) {
-                        bf16x8 vn;
-                        if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * KP + ((jv + 1) & 3) * 64);
-#pragma unroll
-                        for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
-                        if (jv == 3) {
-#pragma unroll
-                            for (int hb = 0; hb < 4; ++hb)
-                                pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 1024 + 16 * ln));
-                        }
-                        if (jv + 1 < 8) va = vn;
-                    }
-                    if (jv == 0) {
-                        if (vm != 0xffffffffu) {
+                    if (soft) {
+                        if (js >= 3 && js <= 23 && js % 5 == 3)
+                            dma16(src3 + 128 * (js / 5), __builtin_amdgcn_readfirstlane(slot3 + 1024u * (js / 5)));
+                        if (js == 28) gather_tail(src3, ln, slot3);
+                        if (js == 1 && vm != 0xffffffffu) {
                             // accumulator element v holds key 8(v/4) + 4h + v%4:
                             // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
 #pragma unroll
@@ -474,108 +397,150 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                 S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
                             }
                         }
-                        mx = S[0];
+                        if (js == 2) {
+                            mx = S[0];
 #pragma unroll
-                        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
-                    } else if (jv == 1) {
-                        // max with the other half-wave (same head): the swap hands
-                        // lanes 0..31 the upper half's value in the second result
-                        // and lanes 32..63 the lower half's in the first
-                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                        mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-                        const float mnew = mx * p.c;
-                        m_seen = fmaxf(m_seen, mnew);
-                        if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
-                        restart |= __any(mnew > m_ref + p.threshold);
-                    } else if (jv >= 2 && jv <= 5) {
-#pragma unroll
-                        for (int v = 4 * (jv - 2); v < 4 * (jv - 1); ++v) {
+                            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
+                        }
+                        if (js == 4) {
+                            // max with the other half-wave (same head): the swap hands
+                            // lanes 0..31 the upper half's value in the second result
+                            // and lanes 32..63 the lower half's in the first
+                            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+                            const float mnew = mx * p.c;
+                            m_seen = fmaxf(m_seen, mnew);
+                            if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                            restart |= __any(mnew > m_ref + p.threshold);
+                        }
+                        if (js >= 6 && js < 22) {
+                            const int v = js - 6;
                             S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
                             psum += S[v];
                         }
-                        if (jv == 3) stage_convert<2>(g, st);
-
-                    } else if (jv == 6) {
-                        l_part += psum;
-                        lds_write16(lds, xp_wr + wave * 2048 + 16 * ln, p_fragment(S, 0));
-                        lds_write16(lds, xp_wr + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
-                    } else {
-                        stage_convert<3>(g, st);
-                        st.rope = g.rope;
+                        if (js == 24) {
+                            l_part += psum;
+                            lds_write16(lds, L_XP + wave * 2048 + 16 * ln, p_fragment(S, 0));
+                        }
+                        if (js == 26) lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                mfma_result_fence2(Sa, Sb);
+                S_next = Sa + Sb;
+            };
+            // Part 2 of tile i: the 32 value MFMAs of tile i (O^T += V^T P^T over
+            // this wave's 128 dims, all 128 heads; V from K buffer i % 3, P from
+            // LDS) with, between them, the dequant of tile i+2 written straight
+            // into K buffer (i+2) % 3 (free since tile i-1 is done) and the copy
+            // source of tile i+4.  Past the piece the staged rows are zero rows.
+            auto part2 = [&](int i, int ln, const uint8_t*& src4, uint32_t& vm4) {
+                const int vb = L_KB + (i % NKB) * KBB + pv_base(ln) + 64 * 4 * wave;
+                const int kb2 = L_KB + ((i + 2) % NKB) * KBB;
+                // the copies of tile i+2 and the ids of tile i+4 have landed (7
+                // newer ops: the ids of tile i+5, the copies of tile i+3)
+                wait_vmcnt<7>();
+                const StageRegs g = stage_load(lds, slice_off + (i & 1) * RAW_BYTES, ln);
+                bf16x8 va, pf[4];
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb)
+                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
+                va = v_frag(lds, vb);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jv = 0; jv < 8; ++jv) {
+                    // value step jv: k-step jv / 4, dim block jv % 4; the next V^T
+                    // fragment is read ahead
+                    bf16x8 vn;
+                    if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * KP + ((jv + 1) & 3) * 64);
+#pragma unroll
+                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
+                    if (jv == 3) {
+#pragma unroll
+                        for (int hb = 0; hb < 4; ++hb)
+                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                    }
+                    if (jv + 1 < 8) va = vn;
+                    if (jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(i + 4), ln), src4);
+                    if (jv == 1) stage_chunk<0>(lds, g, kb2, wave, ln);
+                    if (jv == 3) stage_chunk<1>(lds, g, kb2, wave, ln);
+                    if (jv == 5) stage_chunk<2>(lds, g, kb2, wave, ln);
+                    if (jv == 7) {
+                        stage_chunk<3>(lds, g, kb2, wave, ln);
+                        stage_rope(lds, g, kb2, wave, ln);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
-            // Phase B of tile t: the rows of tile t+1 (converted in phase A) into
-            // the K buffer the value MFMAs of tile t-1 have released; the ids of
-            // tile t+5 for the next copy sources.  Past the piece the staged rows
-            // are zero rows.
-            auto phaseB = [&](int t, int ln, const StagedRows& st, int2& ids5) {
-                stage_write(lds, st, L_KB + ((t + 1) & 1) * KBB, wave, ln);
-                // ids of tile t+5 (issued at the start of phase A; 6 newer ops:
-                // the copies of tile t+3)
-                wait_vmcnt<6>();
-                ids5 = read_ids(t + 5, ln);
-            };
-            // value MFMAs of the last tile
-            auto values_only = [&](int t, int ln) {
-                const int vb = L_KB + (t & 1) * KBB + pv_base(ln) + 64 * 4 * wave;
-                const int xp_rd = L_XP + (t & 1) * XPB;
-                bf16x8 pf[4];
-#pragma unroll
-                for (int hb = 0; hb < 4; ++hb)
-                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 16 * ln));
-                bf16x8 a_cur = v_frag(lds, vb);
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const int j = s & 3;
-                    bf16x8 a_nxt;
-                    if (s + 1 < 8) a_nxt = v_frag(lds, vb + ((s + 1) >> 2) * 16 * KP + ((s + 1) & 3) * 64);
-#pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * j + hb], a_cur, pf[hb]);
-                    if (s == 3) {
-#pragma unroll
-                        for (int hb = 0; hb < 4; ++hb)
-                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp_rd + hb * 2048 + 1024 + 16 * ln));
-                    }
-                    if (s + 1 < 8) a_cur = a_nxt;
-                }
-            };
 
-            StagedRows st;
-            // tile 0: no value work yet
+            // ---- prologue: ids of tiles 0..4, then (first pass) Q, whose loads
+            // are issued while the ids are on their way; copies of tiles 0 and
+            // 1; copy sources of tiles 2 and 3; tiles 0 and 1 staged into K
+            // buffers 0 and 1; the copies of tile 2 into raw slot 0; the
+            // scores of tile 0.
+            uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles i .. i+3
+            const uint8_t* src_nx;                  // this lane's copy source in tile i+3
+            f32x16 S_cur;                           // scores of tile i
             {
                 const int ln = opaque_lane();
-                const uint8_t* src4;
-                uint32_t vm4;
-                phaseA(0, ln, false, src2, src_nx, ids_nx, vm0, src4, vm4, st);
-                __syncthreads();
-                phaseB(0, ln, st, ids_nx);
-                src_nx = src4;
-                vm0 = vm1;
-                vm1 = vm2;
-                vm2 = vm3;
-                vm3 = vm4;
-                __syncthreads();
+                for (int t = 0; t < 4; ++t) copy_ids(idx, k_lo, k_hi, t, ln, lds0 + first_slot(t));
+                copy_ids(idx, k_lo, k_hi, 4, ln, lds0 + ring_slot(4));
+                if (pass == 0) {
+                    // with 64 query heads, waves 2 and 3 score copies of heads
+                    // 0..63 (their results are never stored)
+                    const uint16_t* q_own = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss +
+                                            (int64_t)((32 * wave + (ln & 31)) & (p.h_q - 1)) * p.q_sh +
+                                            8 * (ln >> 5);
+#pragma unroll
+                    for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
+                    // the 36 loads stay above the count below
+                    asm volatile("" ::: "memory");
+                    wait_vmcnt<36>();               // ids of tiles 0..4 (the 36 loads of Q are newer)
+                } else {
+                    wait_vmcnt<0>();                // ids of tiles 0..4
+                }
+                const uint8_t* src;
+                const uint8_t* src2;
+                vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src);
+                gather_rows(src, ln, lds0 + slice_off);
+                vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src);
+                gather_rows(src, ln, lds0 + slice_off + RAW_BYTES);
+                vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2);
+                vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx);
+                // Q and the copies of tiles 0 and 1 (unconditional and complete,
+                // so the compiler sees Q landed on every path and puts no waits
+                // of its own into the tile loop)
+                wait_vmcnt<0>();
+                stage_rows(lds, slice_off, L_KB, wave, ln);
+                stage_rows(lds, slice_off + RAW_BYTES, L_KB + KBB, wave, ln);
+                // raw slot 0 is read (its values went through the conversions)
+                gather_rows(src2, ln, lds0 + slice_off);
             }
-            for (int it = 1; it < n_tiles; ++it) {
+            __syncthreads();
+            {
+                f32x16 none = {};
+                part1(-1, opaque_lane(), false, nullptr, 0u, none, S_cur);
+            }
+
+            for (int i = 0; i < n_tiles; ++i) {
                 // lane-derived offsets are recomputed every tile (cheap VALU)
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
+                f32x16 S_next;
+                part1(i, ln, true, src_nx, vm0, S_cur, S_next);
+                __syncthreads();
                 const uint8_t* src4;
                 uint32_t vm4;
-                phaseA(it, ln, true, nullptr, src_nx, ids_nx, vm0, src4, vm4, st);
+                part2(i, ln, src4, vm4);
                 __syncthreads();
-                phaseB(it, ln, st, ids_nx);
+                S_cur = S_next;
                 src_nx = src4;
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;
                 vm3 = vm4;
-                __syncthreads();
             }
-            values_only(n_tiles - 1, opaque_lane());
-            if (threadIdx.x % 64 == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
+            if (opaque_lane() == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
             __syncthreads();
             wait_vmcnt<0>();                                    // copies past the piece
             // A score exceeded the reference by more than 2^threshold in some
@@ -583,7 +548,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             const uint32_t flags = *(const LDS_AS uint32_t*)(lds + L_FLAGS);
             __syncthreads();
             if (flags == 0u || pass > 0) break;
-            if (threadIdx.x < 4) lds[L_FLAGS + threadIdx.x] = 0;
+            if (wave == 0 && opaque_lane() < 4) lds[L_FLAGS + opaque_lane()] = 0;
             m_ref = m_seen;
         }
 
