@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "mla_internal.h"
 
@@ -82,6 +84,8 @@ static_assert(NDMA == 6 && RCH - 8 * (NDMA - 1) == 1, "copy layout");
 // zero scales, zero RoPE), so staged values of empty slots are zero without
 // masking.  Spread over 64 rows so the reads do not pile onto one L2 channel.
 __device__ __attribute__((aligned(256))) uint8_t g_zero_rows[ZERO_ROWS * ROWB];
+// The id copied for slots past the end of a piece: such slots are empty.
+__device__ int32_t g_no_id[1] = {-1};
 
 // Raw slice layout (5248 bytes): chunk c < 40 of row r at 1024 (c / 8) +
 // 128 r + 16 (c % 8); chunk 40 of row r at 5120 + 16 r.  Copy i < 5 of lane L
@@ -106,27 +110,43 @@ __device__ __forceinline__ int xcd_part(int bid, int nb) {
 __device__ __forceinline__ bool slot_ok(const DecodeParams& p, int t, bool in_range) {
     return in_range & ((uint32_t)t < p.n_tok32);
 }
-// Row address of token t when ok, else row zrow of the zero page.
+// Row address of token t when ok, else row zrow of the zero page.  FLAT:
+// pages back to back and every row offset below 2^32 with t < 2^24, so the
+// offset is one 24-bit multiply instead of a page division.
+template <bool FLAT>
 __device__ __forceinline__ const uint8_t* row_addr(const DecodeParams& p, int t, bool ok, int zrow) {
     const uint32_t tt = ok ? (uint32_t)t : 0u;
-    const uint32_t blk = (__umulhi(tt, p.page_magic) + tt) >> p.page_mshift;
-    const uint32_t off = tt - blk * (uint32_t)p.page_block_size;
-    const uint64_t r = (uint64_t)(uintptr_t)p.kv + (uint64_t)blk * (uint64_t)p.kv_block_stride +
-                       (uint64_t)off * ROWB;
+    uint64_t r;
+    if (FLAT) {
+        r = (uint64_t)(uintptr_t)p.kv + (uint32_t)__umul24(tt, (uint32_t)ROWB);
+    } else {
+        const uint32_t blk = (__umulhi(tt, p.page_magic) + tt) >> p.page_mshift;
+        const uint32_t off = tt - blk * (uint32_t)p.page_block_size;
+        r = (uint64_t)(uintptr_t)p.kv + (uint64_t)blk * (uint64_t)p.kv_block_stride + (uint64_t)off * ROWB;
+    }
     const uint64_t z = (uint64_t)(uintptr_t)g_zero_rows + (uint32_t)zrow * ROWB;
     return (const uint8_t*)(uintptr_t)(ok ? r : z);
 }
 
 // Copies of this wave's 8 rows of a tile into its raw slice; `src` points at
 // chunk lane % 8 of row lane / 8 (key 8w + lane / 8).
-__device__ __forceinline__ void gather_tail(const uint8_t* src, int lane, uint32_t slice) {
+__device__ __forceinline__ const uint8_t* tail_src(const uint8_t* src, int lane) {
     // chunk 40 of row `lane` (lanes 0..7): row starts are held by lanes 8 r
     const uint64_t row = (uint64_t)(uintptr_t)(src - 16 * (lane & 7));
     const int from = 8 * (lane & 7);
     const uint64_t rl = ((uint64_t)(uint32_t)__shfl((uint32_t)(row >> 32), from) << 32) |
                         (uint32_t)__shfl((uint32_t)row, from);
+    return (const uint8_t*)(uintptr_t)rl + 16 * 40;
+}
+__device__ __forceinline__ void gather_tail(const uint8_t* src, int lane, uint32_t slice) {
+    const uint8_t* t = tail_src(src, lane);
     const uint32_t dst = __builtin_amdgcn_readfirstlane(slice + 1024u * (NDMA - 1));
-    if (lane < 8) dma16((const uint8_t*)(uintptr_t)rl + 16 * 40, dst);
+    if (lane < 8) dma16(t, dst);
+}
+// The same with the destination given as a scalar base plus a constant.
+__device__ __forceinline__ void gather_tail_at(const uint8_t* src, int lane, uint32_t base, int off) {
+    const uint8_t* t = tail_src(src, lane);
+    if (lane < 8) dma16_at(t, base, off);
 }
 __device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, uint32_t slice) {
 #pragma unroll
@@ -135,12 +155,14 @@ __device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, uint32
     gather_tail(src, lane, slice);
 }
 
-// Copy the 32 token ids of a tile (clamped to the piece) into an id slot.
+// Copy the 32 token ids of a tile into an id slot; slots past the end of the
+// piece receive -1 (empty), so readers test only the id.
 __device__ __forceinline__ void copy_ids(const int32_t* idx, int k_lo, int k_hi, int tile, int lane,
                                          uint32_t slot_addr) {
-    const int k = min(k_lo + tile * TILE + (lane & 31), k_hi - 1);
+    const int k = k_lo + tile * TILE + (lane & 31);
+    const int32_t* src = k < k_hi ? idx + k : g_no_id;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(slot_addr);
-    if (lane < 32) dma4(idx + k, dst);
+    if (lane < 32) dma4(src, dst);
 }
 
 // Staging of this wave's 8 rows.  Lane L holds chunks (L % 8) + 8 i of row
@@ -162,7 +184,9 @@ __device__ __forceinline__ StageRegs stage_load(const LDS_AS uint8_t* lds, int s
         g.w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
         g.sc[i] = *(const LDS_AS float*)(lds + slice + raw_off(r, 32) + 4 * i);
     }
-    g.rope = lds_read16(lds, slice + raw_off(r, c0 ? 32 + c0 : 40));
+    // RoPE chunk 32 + c0 (c0 > 0) or chunk 40 (c0 == 0), chosen without a branch
+    const int rope_off = c0 ? 4096 + 128 * r + 16 * c0 : 5120 + 16 * r;
+    g.rope = lds_read16(lds, slice + rope_off);
     return g;
 }
 // Converted rows of one wave's staging share: chunks c0 + 8 i (i = 0..3) as
@@ -295,6 +319,16 @@ __device__ __forceinline__ int opaque_lane() {
     return l;
 }
 
+// This lane's 16 bytes in the P area (head block 0, k-step 0), opaque so
+// that head-block and k-step offsets fold into the LDS instructions'
+// immediate offsets (the area lies above 64 KB).
+__device__ __forceinline__ int xp_base(int lane) {
+    int b = L_XP + 16 * lane;
+    asm volatile("" : "+v"(b));
+    return b;
+}
+
+template <bool FLAT>
 __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
@@ -336,11 +370,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         // validity mask of the tile's 32 keys and the copy source of this
         // lane's row (chunk ln % 8); tiles past the piece copy zero rows
         auto rows_from = [&](int tile, int ln, int2 id, const uint8_t*& src) -> uint32_t {
-            const int kn = ln & 31, kr = WROWS * wave + (ln >> 3);
-            const int k0 = k_lo + tile * TILE;
-            const bool ok = slot_ok(p, id.x, (tile < n_tiles) & (k0 + kn < k_hi));
-            const bool okr = slot_ok(p, id.y, (tile < n_tiles) & (k0 + kr < k_hi));
-            src = row_addr(p, id.y, okr, (tile * TILE + kr) & (ZERO_ROWS - 1)) + 16 * (ln & 7);
+            (void)tile;
+            const int kr = WROWS * wave + (ln >> 3);
+            const bool ok = slot_ok(p, id.x, true);
+            const bool okr = slot_ok(p, id.y, true);
+            src = row_addr<FLAT>(p, id.y, okr, kr) + 16 * (ln & 7);
             return (uint32_t)__ballot(ok);
         };
 
@@ -354,23 +388,28 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             for (int i = 0; i < 16; ++i) O[i] = f32x16{};
             l_part = 0.f;
             __syncthreads();                        // LDS free (previous piece / pass done)
-            bool restart = false;
 
-            // Part 1 of tile i: the 36 score MFMAs of tile i+1 (K buffer
-            // (i+1) % 3) for this wave's 32 heads over all 576 dims (two
-            // accumulator chains) with, between them, the softmax of tile i
-            // (mask empty slots, base-2 exponent against the reference max, P
-            // to LDS), the ids of tile i+5 and the copies of tile i+3.  With
-            // soft == false (the prologue) only the scores of tile 0.
-            auto part1 = [&](int i, int ln, bool soft, const uint8_t* src3, uint32_t vm, f32x16 S,
+            // this wave's raw slice in slot 0 (copy destinations are this
+            // plus constants)
+            const uint32_t raw0 = lds0 + slice_off;
+
+            // Part 1 of tile i: the 36 score MFMAs of tile i+1 (K buffer at
+            // kb) for this wave's 32 heads over all 576 dims (two accumulator
+            // chains) with, between them, the softmax of tile i (mask empty
+            // slots, base-2 exponent against the reference max, P to LDS), the
+            // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
+            // 1 - par for tile parity par).  With soft == false (the prologue)
+            // only the scores of tile 0.
+            auto part1 = [&](int i, int par, int kb, int ln, bool soft, const uint8_t* src3, uint32_t vm, f32x16 S,
                              f32x16& S_next) {
-                const int qk = L_KB + ((i + 1) % NKB) * KBB + qk_base(ln, 0);
-                const uint32_t slot3 = lds0 + slice_off + ((i + 3) & 1) * RAW_BYTES;
+                const int qk = kb + qk_base(ln, 0);
+                const int r3 = 1 - par;
+                const uint32_t raw3 = raw0 + r3 * RAW_BYTES;
                 f32x16 Sa, Sb;
                 bf16x8 ka[KAHEAD];
 #pragma unroll
                 for (int j = 0; j < KAHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
-                if (soft) copy_ids(idx, k_lo, k_hi, i + 5, ln, lds0 + ring_slot(i + 5));
+                if (soft) copy_ids(idx, k_lo, k_hi, i + 5, ln, lds0 + ring_slot(r3));
                 __builtin_amdgcn_sched_barrier(0);
                 float mx, psum = 0.f;
 #pragma unroll
@@ -378,14 +417,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     const bf16x8 cur = ka[js % KAHEAD];
                     if (js + KAHEAD < 36)
                         ka[js % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + KAHEAD)));
+                    // two alternating accumulator chains: a score MFMA never
+                    // takes the result of the one issued right before it
                     if (js == 0) mfma_qk_first(Sa, cur, qa[0]);
                     else if (js == 1) mfma_qk_first(Sb, cur, qa[1]);
                     else if (js & 1) mfma_qk(Sb, cur, qa[js]);
                     else mfma_qk(Sa, cur, qa[js]);
                     if (soft) {
                         if (js >= 3 && js <= 23 && js % 5 == 3)
-                            dma16(src3 + 128 * (js / 5), __builtin_amdgcn_readfirstlane(slot3 + 1024u * (js / 5)));
-                        if (js == 28) gather_tail(src3, ln, slot3);
+                            dma16_at(src3 + 128 * (js / 5), raw3, 1024 * (js / 5));
+                        if (js == 28) gather_tail_at(src3, ln, raw3, 1024 * (NDMA - 1));
                         if (js == 1 && vm != 0xffffffffu) {
                             // accumulator element v holds key 8(v/4) + 4h + v%4:
                             // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
@@ -411,7 +452,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                             const float mnew = mx * p.c;
                             m_seen = fmaxf(m_seen, mnew);
                             if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
-                            restart |= __any(mnew > m_ref + p.threshold);
                         }
                         if (js >= 6 && js < 22) {
                             const int v = js - 6;
@@ -420,9 +460,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         }
                         if (js == 24) {
                             l_part += psum;
-                            lds_write16(lds, L_XP + wave * 2048 + 16 * ln, p_fragment(S, 0));
+                            lds_write16(lds, xp_base(ln) + wave * 2048, p_fragment(S, 0));
                         }
-                        if (js == 26) lds_write16(lds, L_XP + wave * 2048 + 1024 + 16 * ln, p_fragment(S, 1));
+                        if (js == 26) lds_write16(lds, xp_base(ln) + wave * 2048 + 1024, p_fragment(S, 1));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -430,21 +470,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 S_next = Sa + Sb;
             };
             // Part 2 of tile i: the 32 value MFMAs of tile i (O^T += V^T P^T over
-            // this wave's 128 dims, all 128 heads; V from K buffer i % 3, P from
-            // LDS) with, between them, the dequant of tile i+2 written straight
-            // into K buffer (i+2) % 3 (free since tile i-1 is done) and the copy
-            // source of tile i+4.  Past the piece the staged rows are zero rows.
-            auto part2 = [&](int i, int ln, const uint8_t*& src4, uint32_t& vm4) {
-                const int vb = L_KB + (i % NKB) * KBB + pv_base(ln) + 64 * 4 * wave;
-                const int kb2 = L_KB + ((i + 2) % NKB) * KBB;
+            // this wave's 128 dims, all 128 heads; V from the K buffer at kbv, P
+            // from LDS) with, between them, the dequant of tile i+2 (raw slot
+            // par) written straight into the K buffer at kb2 (free since tile
+            // i-1 is done) and the copy source of tile i+4 (id slot par).  Past
+            // the piece the staged rows are zero rows.
+            auto part2 = [&](int i, int par, int kbv, int kb2, int ln, const uint8_t*& src4, uint32_t& vm4) {
+                const int vb = kbv + pv_base(ln) + 64 * 4 * wave;
+                const int xp = xp_base(ln);
                 // the copies of tile i+2 and the ids of tile i+4 have landed (7
                 // newer ops: the ids of tile i+5, the copies of tile i+3)
                 wait_vmcnt<7>();
-                const StageRegs g = stage_load(lds, slice_off + (i & 1) * RAW_BYTES, ln);
+                const StageRegs g = stage_load(lds, slice_off + par * RAW_BYTES, ln);
                 bf16x8 va, pf[4];
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb)
-                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 16 * ln));
+                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048));
                 va = v_frag(lds, vb);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -458,10 +499,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (jv == 3) {
 #pragma unroll
                         for (int hb = 0; hb < 4; ++hb)
-                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, L_XP + hb * 2048 + 1024 + 16 * ln));
+                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048 + 1024));
                     }
                     if (jv + 1 < 8) va = vn;
-                    if (jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(i + 4), ln), src4);
+                    if (jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4);
                     if (jv == 1) stage_chunk<0>(lds, g, kb2, wave, ln);
                     if (jv == 3) stage_chunk<1>(lds, g, kb2, wave, ln);
                     if (jv == 5) stage_chunk<2>(lds, g, kb2, wave, ln);
@@ -519,19 +560,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             __syncthreads();
             {
                 f32x16 none = {};
-                part1(-1, opaque_lane(), false, nullptr, 0u, none, S_cur);
+                part1(-1, 1, L_KB, opaque_lane(), false, nullptr, 0u, none, S_cur);
             }
 
-            for (int i = 0; i < n_tiles; ++i) {
+            // K buffers of the values, scores and staging of tile i (buffers
+            // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
+            int kb_v = L_KB, kb_s = L_KB + KBB, kb_g = L_KB + 2 * KBB;
+            auto tile = [&](int i, int par) {
                 // lane-derived offsets are recomputed every tile (cheap VALU)
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
                 f32x16 S_next;
-                part1(i, ln, true, src_nx, vm0, S_cur, S_next);
+                part1(i, par, kb_s, ln, true, src_nx, vm0, S_cur, S_next);
                 __syncthreads();
                 const uint8_t* src4;
                 uint32_t vm4;
-                part2(i, ln, src4, vm4);
+                part2(i, par, kb_v, kb_g, ln, src4, vm4);
                 __syncthreads();
                 S_cur = S_next;
                 src_nx = src4;
@@ -539,7 +583,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 vm1 = vm2;
                 vm2 = vm3;
                 vm3 = vm4;
-            }
+                const int t = kb_v;
+                kb_v = kb_s;
+                kb_s = kb_g;
+                kb_g = t;
+            };
+            for (int i = 0; i < n_tiles; ++i) tile(i, i & 1);
+            // the reference stays fixed once set, so one test of the largest
+            // score max of the pass covers every tile
+            const bool restart = __any(m_seen > m_ref + p.threshold);
             if (opaque_lane() == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
             __syncthreads();
             wait_vmcnt<0>();                                    // copies past the piece
@@ -636,7 +688,7 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
         const bool ok = slot_ok(p, slot[n], it * TILE + n < p.topk);
         const bool okr = slot_ok(p, slot[kr], it * TILE + kr < p.topk);
         const uint32_t vm = (uint32_t)__ballot(ok);
-        gather_rows(row_addr(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, lds0 + slice_off);
+        gather_rows(row_addr<false>(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, lds0 + slice_off);
         wait_vmcnt<0>();
         stage_rows(lds, slice_off, L_KB, wave, lane);
         __syncthreads();
@@ -736,7 +788,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
             M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
 }
 
-bool g_lds_decode = false, g_lds_gather = false;
+bool g_lds_decode = false, g_lds_decode_flat = false, g_lds_gather = false;
 
 template <typename K>
 hipError_t allow_lds_once(K k, bool& done) {
@@ -749,9 +801,15 @@ hipError_t allow_lds_once(K k, bool& done) {
 }  // namespace
 
 hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
-    hipError_t e = allow_lds_once(decode_fp8_h128_kernel, g_lds_decode);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_fp8_h128_kernel, dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st, p);
+    if (p.kv_flat) {
+        hipError_t e = allow_lds_once(decode_fp8_h128_kernel<true>, g_lds_decode_flat);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_fp8_h128_kernel<true>, dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st, p);
+    } else {
+        hipError_t e = allow_lds_once(decode_fp8_h128_kernel<false>, g_lds_decode);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_fp8_h128_kernel<false>, dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st, p);
+    }
     return hipGetLastError();
 }
 

@@ -96,6 +96,11 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  :: "s"(lds_addr), "v"(src) : "memory", "m0");
 }
+// Destination = scalar base + constant, added straight into M0.
+__device__ __forceinline__ void dma16_at(const void* src, uint32_t base, int off) {
+    asm volatile("s_add_u32 m0, %0, %2\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(base), "v"(src), "i"(off) : "memory", "m0", "scc");
+}
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :: "s"(lds_addr), "v"(src) : "memory", "m0");

@@ -177,6 +177,8 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         p->page_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - P)) / P + 1);
     }
     p->packed_partials = r.kv_format == MLA_KV_FP8_656;
+    p->kv_flat = r.kv_format == MLA_KV_FP8_656 && a->kv_stride_block == (int64_t)r.page_block_size * 656 &&
+                 r.num_kv_tokens < (1ll << 24) && r.num_kv_tokens * 656 < (1ll << 32);
     p->block = r.block;
     {
         // closed-form plan constants (used by the kernels only when the plan

@@ -38,6 +38,8 @@ struct DecodeParams {
     uint32_t page_magic;            // t / page_block_size == (mulhi(t, page_magic) + t) >> page_mshift
     int page_mshift;                // for 0 <= t < 2^31 (round-up reciprocal)
     int packed_partials;            // split partials as packed bf16 (128-head FP8 decode)
+    int kv_flat;                    // FP8 pages back to back, n_tok < 2^24 and n_tok * 656 < 2^32:
+                                    // the row of token t is kv + 656 t (32-bit offset)
     // closed-form plan (per-request cost zero): B blocks per request, total
     // b * B blocks, partitions of `payload` blocks; gb = B / gcd(B, payload),
     // gp = payload / gcd(B, payload).  All below 2^31.
