@@ -400,33 +400,36 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
             // 1 - par for tile parity par).  With soft == false (the prologue)
             // only the scores of tile 0.
-            auto part1 = [&](int i, int par, int kb, int ln, bool soft, const uint8_t* src3, uint32_t vm, f32x16 S,
-                             f32x16& S_next) {
+            auto part1 = [&](int i, int par, int kb, int ln, bool soft, bool scores, bool copies, const uint8_t* src3,
+                             uint32_t vm, f32x16 S, f32x16& S_next) {
                 const int qk = kb + qk_base(ln, 0);
                 const int r3 = 1 - par;
                 const uint32_t raw3 = raw0 + r3 * RAW_BYTES;
                 f32x16 Sa, Sb;
                 bf16x8 ka[KAHEAD];
 #pragma unroll
-                for (int j = 0; j < KAHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
-                if (soft) copy_ids(idx, k_lo, k_hi, i + 5, ln, lds0 + ring_slot(r3));
+                for (int j = 0; j < KAHEAD; ++j)
+                    if (scores) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                if (soft && copies) copy_ids(idx, k_lo, k_hi, i + 5, ln, lds0 + ring_slot(r3));
                 __builtin_amdgcn_sched_barrier(0);
                 float mx, psum = 0.f;
 #pragma unroll
                 for (int js = 0; js < 36; ++js) {
-                    const bf16x8 cur = ka[js % KAHEAD];
-                    if (js + KAHEAD < 36)
-                        ka[js % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + KAHEAD)));
-                    // two alternating accumulator chains: a score MFMA never
-                    // takes the result of the one issued right before it
-                    if (js == 0) mfma_qk_first(Sa, cur, qa[0]);
-                    else if (js == 1) mfma_qk_first(Sb, cur, qa[1]);
-                    else if (js & 1) mfma_qk(Sb, cur, qa[js]);
-                    else mfma_qk(Sa, cur, qa[js]);
+                    if (scores) {
+                        const bf16x8 cur = ka[js % KAHEAD];
+                        if (js + KAHEAD < 36)
+                            ka[js % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + KAHEAD)));
+                        // two alternating accumulator chains: a score MFMA never
+                        // takes the result of the one issued right before it
+                        if (js == 0) mfma_qk_first(Sa, cur, qa[0]);
+                        else if (js == 1) mfma_qk_first(Sb, cur, qa[1]);
+                        else if (js & 1) mfma_qk(Sb, cur, qa[js]);
+                        else mfma_qk(Sa, cur, qa[js]);
+                    }
                     if (soft) {
-                        if (js >= 3 && js <= 23 && js % 5 == 3)
+                        if (copies && js >= 3 && js <= 23 && js % 5 == 3)
                             dma16_at(src3 + 128 * (js / 5), raw3, 1024 * (js / 5));
-                        if (js == 28) gather_tail_at(src3, ln, raw3, 1024 * (NDMA - 1));
+                        if (copies && js == 28) gather_tail_at(src3, ln, raw3, 1024 * (NDMA - 1));
                         if (js == 1 && vm != 0xffffffffu) {
                             // accumulator element v holds key 8(v/4) + 4h + v%4:
                             // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
@@ -466,8 +469,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                mfma_result_fence2(Sa, Sb);
-                S_next = Sa + Sb;
+                if (scores) {
+                    mfma_result_fence2(Sa, Sb);
+                    S_next = Sa + Sb;
+                }
             };
             // Part 2 of tile i: the 32 value MFMAs of tile i (O^T += V^T P^T over
             // this wave's 128 dims, all 128 heads; V from the K buffer at kbv, P
@@ -475,13 +480,19 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // par) written straight into the K buffer at kb2 (free since tile
             // i-1 is done) and the copy source of tile i+4 (id slot par).  Past
             // the piece the staged rows are zero rows.
-            auto part2 = [&](int i, int par, int kbv, int kb2, int ln, const uint8_t*& src4, uint32_t& vm4) {
+            auto part2 = [&](int i, int par, int kbv, int kb2, int ln, bool stage, bool copies_out,
+                             const uint8_t*& src4, uint32_t& vm4) {
                 const int vb = kbv + pv_base(ln) + 64 * 4 * wave;
                 const int xp = xp_base(ln);
                 // the copies of tile i+2 and the ids of tile i+4 have landed (7
-                // newer ops: the ids of tile i+5, the copies of tile i+3)
-                wait_vmcnt<7>();
-                const StageRegs g = stage_load(lds, slice_off + par * RAW_BYTES, ln);
+                // newer ops: the ids of tile i+5, the copies of tile i+3; none
+                // near the end of the piece)
+                StageRegs g;
+                if (stage) {
+                    if (copies_out) wait_vmcnt<7>();
+                    else wait_vmcnt<0>();
+                    g = stage_load(lds, slice_off + par * RAW_BYTES, ln);
+                }
                 bf16x8 va, pf[4];
 #pragma unroll
                 for (int hb = 0; hb < 4; ++hb)
@@ -502,11 +513,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                             pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048 + 1024));
                     }
                     if (jv + 1 < 8) va = vn;
-                    if (jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4);
-                    if (jv == 1) stage_chunk<0>(lds, g, kb2, wave, ln);
-                    if (jv == 3) stage_chunk<1>(lds, g, kb2, wave, ln);
-                    if (jv == 5) stage_chunk<2>(lds, g, kb2, wave, ln);
-                    if (jv == 7) {
+                    if (stage && jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4);
+                    if (stage && jv == 1) stage_chunk<0>(lds, g, kb2, wave, ln);
+                    if (stage && jv == 3) stage_chunk<1>(lds, g, kb2, wave, ln);
+                    if (stage && jv == 5) stage_chunk<2>(lds, g, kb2, wave, ln);
+                    if (stage && jv == 7) {
                         stage_chunk<3>(lds, g, kb2, wave, ln);
                         stage_rope(lds, g, kb2, wave, ln);
                     }
@@ -560,22 +571,27 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             __syncthreads();
             {
                 f32x16 none = {};
-                part1(-1, 1, L_KB, opaque_lane(), false, nullptr, 0u, none, S_cur);
+                part1(-1, 1, L_KB, opaque_lane(), false, true, false, nullptr, 0u, none, S_cur);
             }
 
             // K buffers of the values, scores and staging of tile i (buffers
             // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
             int kb_v = L_KB, kb_s = L_KB + KBB, kb_g = L_KB + 2 * KBB;
-            auto tile = [&](int i, int par) {
+            // One tile; near the end of the piece the work for tiles past it is
+            // left out: the copies of tile i+3 (and ids of i+5) from tile n-3 on,
+            // the staging of tile i+2 from n-2 on, the scores of tile i+1 at n-1.
+            auto tile = [&](int i, int par, auto tail_c) {
+                constexpr int left = decltype(tail_c)::value;   // tiles left including i, 0 = more than 3
+                constexpr bool copies = left == 0, stage = left == 0 || left == 3, scores = left != 1;
                 // lane-derived offsets are recomputed every tile (cheap VALU)
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
                 f32x16 S_next;
-                part1(i, par, kb_s, ln, true, src_nx, vm0, S_cur, S_next);
+                part1(i, par, kb_s, ln, true, scores, copies, src_nx, vm0, S_cur, S_next);
                 __syncthreads();
-                const uint8_t* src4;
-                uint32_t vm4;
-                part2(i, par, kb_v, kb_g, ln, src4, vm4);
+                const uint8_t* src4 = src_nx;
+                uint32_t vm4 = 0u;
+                part2(i, par, kb_v, kb_g, ln, stage, copies, src4, vm4);
                 __syncthreads();
                 S_cur = S_next;
                 src_nx = src4;
@@ -588,13 +604,17 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 kb_s = kb_g;
                 kb_g = t;
             };
-            for (int i = 0; i < n_tiles; ++i) tile(i, i & 1);
+            int i = 0;
+            for (; i + 3 < n_tiles; ++i) tile(i, i & 1, std::integral_constant<int, 0>{});
+            if (i + 2 < n_tiles) tile(i, i & 1, std::integral_constant<int, 3>{}), ++i;
+            if (i + 1 < n_tiles) tile(i, i & 1, std::integral_constant<int, 2>{}), ++i;
+            tile(i, i & 1, std::integral_constant<int, 1>{});
             // the reference stays fixed once set, so one test of the largest
             // score max of the pass covers every tile
             const bool restart = __any(m_seen > m_ref + p.threshold);
             if (opaque_lane() == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
             __syncthreads();
-            wait_vmcnt<0>();                                    // copies past the piece
+            wait_vmcnt<0>();                                    // copies still in flight (short pieces)
             // A score exceeded the reference by more than 2^threshold in some
             // wave: recompute the piece against the true max (rare).
             const uint32_t flags = *(const LDS_AS uint32_t*)(lds + L_FLAGS);
