@@ -76,8 +76,12 @@ constexpr int L_IDS = L_XP + XPB;                       // [4 waves][2 slots][32
 constexpr int L_BYTES = L_IDS + NW * IDS_SLOTS * 128;
 constexpr int L_FLAGS = L_KB + 1152;                    // [4] restart flags (row pad)
 constexpr int L_LM = L_XP;                              // [128 heads] {l, m} (epilogue)
+constexpr int QROW = 1168;                              // Q rows in LDS: 72 chunks + pad (prologue)
+constexpr int QCOPIES = (32 * QROW / 16 + 63) / 64;     // 37 whole-line copies per wave
+constexpr int L_Q = 0;                                  // [4 waves][32 heads][QROW] (prologue only)
 constexpr int L_IDS0 = L_XP;                            // [4 waves][4 tiles][32] int32 (prologue)
 static_assert(L_BYTES <= 160 * 1024, "LDS budget");
+static_assert(L_Q + NW * 32 * QROW <= L_IDS0 && QCOPIES == 37 && 32 * QROW == 36 * 1024 + 32 * 16, "Q staging");
 static_assert(NDMA == 6 && RCH - 8 * (NDMA - 1) == 1, "copy layout");
 
 // Rows copied for empty or out-of-range slots: all zero bytes (zero codes,
@@ -525,11 +529,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 }
             };
 
-            // ---- prologue: ids of tiles 0..4, then (first pass) Q, whose loads
-            // are issued while the ids are on their way; copies of tiles 0 and
-            // 1; copy sources of tiles 2 and 3; tiles 0 and 1 staged into K
-            // buffers 0 and 1; the copies of tile 2 into raw slot 0; the
-            // scores of tile 0.
+            // ---- prologue: ids of tiles 0..4; (first pass) Q through LDS; the
+            // copies of tiles 0 and 1; copy sources of tiles 2 and 3; tiles 0
+            // and 1 staged into K buffers 0 and 1; the copies of tile 2 into
+            // raw slot 0; the scores of tile 0.
             uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles i .. i+3
             const uint8_t* src_nx;                  // this lane's copy source in tile i+3
             f32x16 S_cur;                           // scores of tile i
@@ -538,31 +541,47 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 for (int t = 0; t < 4; ++t) copy_ids(idx, k_lo, k_hi, t, ln, lds0 + first_slot(t));
                 copy_ids(idx, k_lo, k_hi, 4, ln, lds0 + ring_slot(4));
                 if (pass == 0) {
-                    // with 64 query heads, waves 2 and 3 score copies of heads
-                    // 0..63 (their results are never stored)
-                    const uint16_t* q_own = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss +
-                                            (int64_t)((32 * wave + (ln & 31)) & (p.h_q - 1)) * p.q_sh +
-                                            8 * (ln >> 5);
+                    // Q of the wave's 32 heads (with 64 query heads waves 2 and
+                    // 3 take heads 0..63 again; those results are never stored)
+                    // copied whole-line into LDS: region row n = head 32w + n,
+                    // QROW bytes (72 chunks of Q and a pad chunk, so the
+                    // operand reads are conflict-free).  Copy m, lane l moves
+                    // region chunk 64 m + l.
+                    const uint16_t* q_req = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss;
+                    const uint32_t qreg = lds0 + L_Q + wave * 32 * QROW;
+                    int n = 0, c = ln;                  // region row and chunk of copy 0
 #pragma unroll
-                    for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_own + 16 * j));
-                    // the 36 loads stay above the count below
-                    asm volatile("" ::: "memory");
-                    wait_vmcnt<36>();               // ids of tiles 0..4 (the 36 loads of Q are newer)
+                    for (int m = 0; m < QCOPIES; ++m) {
+                        const uint16_t* src = q_req + (int64_t)((32 * wave + n) & (p.h_q - 1)) * p.q_sh +
+                                              8 * (c < 72 ? c : 0);
+                        if (m < QCOPIES - 1 || ln < 32) dma16(src, qreg + 1024u * m);
+                        c += 64;
+                        if (c >= 73) { c -= 73; n += 1; }
+                    }
+                    wait_vmcnt<QCOPIES>();              // ids of tiles 0..4 (the copies of Q are newer)
                 } else {
-                    wait_vmcnt<0>();                // ids of tiles 0..4
+                    wait_vmcnt<0>();                    // ids of tiles 0..4
                 }
                 const uint8_t* src;
                 const uint8_t* src2;
                 vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src);
+                vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src2);
+                if (pass == 0) {
+                    // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7 of
+                    // head 32w + n for k-step j
+                    wait_vmcnt<0>();
+                    const int qr = L_Q + wave * 32 * QROW + (ln & 31) * QROW + 16 * (ln >> 5);
+#pragma unroll
+                    for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
+                    // every wave's reads are done before the row copies reuse the area
+                    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                    __syncthreads();
+                }
                 gather_rows(src, ln, lds0 + slice_off);
-                vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src);
-                gather_rows(src, ln, lds0 + slice_off + RAW_BYTES);
+                gather_rows(src2, ln, lds0 + slice_off + RAW_BYTES);
                 vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2);
                 vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx);
-                // Q and the copies of tiles 0 and 1 (unconditional and complete,
-                // so the compiler sees Q landed on every path and puts no waits
-                // of its own into the tile loop)
-                wait_vmcnt<0>();
+                wait_vmcnt<0>();                        // copies of tiles 0 and 1
                 stage_rows(lds, slice_off, L_KB, wave, ln);
                 stage_rows(lds, slice_off + RAW_BYTES, L_KB + KBB, wave, ln);
                 // raw slot 0 is read (its values went through the conversions)
@@ -627,8 +646,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         // ---- epilogue: l and m of every head through LDS
         const int lane = opaque_lane();
         const int n = lane & 31, h = lane >> 5;
+        // the value MFMAs retire in order: one wait after the last (O[15])
+        // covers every accumulator
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[15]));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[i]));
+        for (int i = 0; i < 15; ++i) asm volatile("" : "+a"(O[i]));
         const float l_tot = l_part + __shfl_xor(l_part, 32);
         if (lane < 32) *(LDS_AS f32x2*)(lds + L_LM + 8 * (32 * wave + n)) = f32x2{l_tot, m_ref};
         __syncthreads();
