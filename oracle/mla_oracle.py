@@ -28,6 +28,14 @@ primitives used; no blocking, fusion or online rescaling):
   invalid slots -> -inf, lse = logsumexp(scores), out = exp(scores - lse) V.
   A slot that repeats a token counts once per slot.  When no slot is valid the
   sparse-decode walkthrough (step 14.2) writes lse = +inf; out is then 0.
+* valid length and attention sink -- "FlashMLA 与 DSA" section 4.3: a slot
+  whose position is at or past topk_length[b] is invalid like -1, and an
+  attention sink (one logit per head, natural log) scales the output by
+  1 / (1 + exp(attn_sink - lse)) while lse stays the log-sum-exp of the real
+  slots.  Walkthrough step 13 gives the same as an extra "sink" token whose
+  value row is zero (output scale 1 / (l + 2^(sink log2(e) - m)) in base-2
+  terms).  Lengths are clamped to [0, topk] (the pages do not say what a
+  negative or larger length means; this reading makes them none / all).
 * split-KV combine -- walkthrough step 14.2 (split partials are normalised
   O_j and lse_j = log2(l_j) + m_j in base 2, -inf when empty) and step 16
   (max over splits, weights 2^(lse_j - max), weighted mean of the O_j);
@@ -178,13 +186,25 @@ def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, valid: np.ndarray,
     return w @ V, lse
 
 
+def sink_factor(lse: np.ndarray, attn_sink: np.ndarray) -> np.ndarray:
+    """Output factor of an attention sink: 1 / (1 + exp(sink - lse)) per head;
+    1 where lse is +inf (no valid slot: the output is 0 anyway)."""
+    lse = np.asarray(lse, dtype=np.float64)
+    sink = np.asarray(attn_sink, dtype=np.float64)
+    fin = np.isfinite(lse)
+    return np.where(fin, 1.0 / (1.0 + np.exp(sink - np.where(fin, lse, 0.0))), 1.0)
+
+
 def sparse_mla_decode(q_bits: np.ndarray, kv: np.ndarray, indices: np.ndarray,
                       sm_scale: float, kv_format: int, page_block_size: int,
-                      queries: Optional[Iterable[Tuple[int, int]]] = None):
+                      queries: Optional[Iterable[Tuple[int, int]]] = None,
+                      attn_sink: Optional[np.ndarray] = None,
+                      topk_length: Optional[np.ndarray] = None):
     """Sparse MLA decode by definition.
 
     q_bits: uint16 bf16 [b, s_q, H, 576]; kv: fp8 uint8 [nb, P, 1, 656] or
-    bf16-row bytes uint8 [s_kv, 1152]; indices int32 [b, s_q, topk].
+    bf16-row bytes uint8 [s_kv, 1152]; indices int32 [b, s_q, topk];
+    attn_sink: float [H] (natural log) or None; topk_length: int [b] or None.
     Returns out float64 [b, s_q, H, 512] and lse float64 [b, H, s_q]
     (natural log).  With `queries`, only those (bi, sj) pairs are filled and
     the others are NaN.
@@ -195,10 +215,17 @@ def sparse_mla_decode(q_bits: np.ndarray, kv: np.ndarray, indices: np.ndarray,
     lse = np.full((b, H, s_q), np.nan)
     if queries is None:
         queries = [(bi, sj) for bi in range(b) for sj in range(s_q)]
+    topk = indices.shape[-1]
     for bi, sj in queries:
         rows, valid = gather_dequant(kv, indices[bi, sj], kv_format, page_block_size)
+        if topk_length is not None:
+            n_ok = min(max(int(topk_length[bi]), 0), topk)
+            valid = valid & (np.arange(topk) < n_ok)
+            rows = np.where(valid[:, None], rows, 0.0)
         qh = bf16_value(q_bits[bi, sj])
         o, l = attend(qh, rows, rows[:, :DV], valid, sm_scale)
+        if attn_sink is not None:
+            o = o * sink_factor(l, attn_sink)[:, None]
         out[bi, sj] = o
         lse[bi, :, sj] = l
     return out, lse

@@ -253,6 +253,64 @@ def test_empty_slots_are_ignored():
     assert np.all(o3 == 0) and np.all(np.isposinf(l3))
 
 
+def test_sink_worked_example():
+    """Walkthrough step 13: sink -2.5 with the final l = 80.7 and m = 0.2116
+    (log2 units) of head 0 gives sink log2 = -3.607 and an output scale of
+    0.01238; the oracle's factor 1 / (1 + exp(sink - lse)) applied to O / l
+    must reproduce it."""
+    g = gold("p2_step13_sink_example.json")
+    assert abs(g["attn_sink"] * math.log2(math.e) - g["sink_log2_as_printed"]) < 1e-3
+    lse = (g["M_log2"] + math.log2(g["L"])) * math.log(2.0)
+    scale = O.sink_factor(np.array([lse]), np.array([g["attn_sink"]]))[0] / g["L"]
+    assert abs(scale - g["o_scale_as_printed"]) < g["print_tolerance"]
+
+
+def test_sink_is_an_extra_zero_value_token():
+    """An attention sink equals one more slot whose score is the sink logit
+    and whose value row is zero (softmax by torch over the extended scores);
+    lse stays that of the real slots."""
+    rng = np.random.default_rng(21)
+    kv = _tiny_cache(rng)
+    qb = _q(rng, 16)
+    idx = rng.permutation(256)[:90].astype(np.int32)
+    sink = rng.standard_normal(16) * 3.0
+    out, lse = O.sparse_mla_decode(qb[None, None], kv, idx[None, None], 1 / 24, O.FMT_FP8, 64, attn_sink=sink)
+    base_o, base_l = O.sparse_mla_decode(qb[None, None], kv, idx[None, None], 1 / 24, O.FMT_FP8, 64)
+    K = torch.from_numpy(O.decode_fp8_rows(kv[idx // 64, idx % 64, 0]))
+    q = torch.from_numpy(O.bf16_value(qb))
+    s = torch.cat([(q @ K.T) / 24, torch.from_numpy(sink)[:, None]], dim=1)        # [16, 91]
+    V = torch.cat([K[:, :512], torch.zeros(1, 512, dtype=torch.float64)], dim=0)
+    ref = torch.softmax(s, dim=1) @ V
+    np.testing.assert_allclose(out[0, 0], ref.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_array_equal(lse, base_l)
+    # a sink of -inf changes nothing
+    o2, _ = O.sparse_mla_decode(qb[None, None], kv, idx[None, None], 1 / 24, O.FMT_FP8, 64,
+                                attn_sink=np.full(16, -np.inf))
+    np.testing.assert_array_equal(o2, base_o)
+
+
+def test_topk_length_masks_like_empty_slots():
+    """Slots at or past topk_length[b] count as empty: the same as -1 there;
+    lengths of 0 and >= topk give none and all."""
+    rng = np.random.default_rng(22)
+    kv = _tiny_cache(rng)
+    qb = np.stack([_q(rng, 8), _q(rng, 8)])[:, None]                            # [2, 1, 8, 576]
+    idx = np.stack([rng.permutation(256)[:64], rng.permutation(256)[:64]]).astype(np.int32)[:, None]
+    lens = np.array([37, 0])
+    o, l = O.sparse_mla_decode(qb, kv, idx, 1 / 24, O.FMT_FP8, 64, topk_length=lens)
+    cut = idx.copy()
+    cut[0, 0, 37:] = -1
+    cut[1, 0, :] = -1
+    o2, l2 = O.sparse_mla_decode(qb, kv, cut, 1 / 24, O.FMT_FP8, 64)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+    assert np.all(o[1] == 0) and np.all(np.isposinf(l[1]))
+    o3, l3 = O.sparse_mla_decode(qb, kv, idx, 1 / 24, O.FMT_FP8, 64, topk_length=np.array([64, 1000]))
+    o4, l4 = O.sparse_mla_decode(qb, kv, idx, 1 / 24, O.FMT_FP8, 64)
+    np.testing.assert_array_equal(o3, o4)
+    np.testing.assert_array_equal(l3, l4)
+
+
 def test_bf16_format_dense_case():
     rng = np.random.default_rng(16)
     vals = W.to_bf16_bits(rng.standard_normal((40, 576), dtype=np.float32))
