@@ -116,8 +116,14 @@ typedef struct mla_decode_args {
     int64_t out_stride_b, out_stride_s, out_stride_h;    /* in elements, multiples of 4   */
     float* lse;                         /* fp32 [b, h_q, s_q] contiguous, natural log      */
 
-    const float* attn_sink;             /* must be NULL (not supported by this build)      */
-    const int32_t* topk_length;         /* must be NULL (not supported by this build)      */
+    const float* attn_sink;             /* NULL, or fp32 [h_q] device: one sink logit per
+                                           head (natural log).  out is scaled by
+                                           1 / (1 + exp(attn_sink - lse)); lse is that of
+                                           the real slots ("FlashMLA 与 DSA" section 4.3,
+                                           walkthrough step 13)                            */
+    const int32_t* topk_length;         /* NULL, or int32 [b] device: slots at positions
+                                           >= topk_length[b] are empty (clamped to
+                                           [0, topk]); the plan still covers topk slots   */
 
     const void* sched_meta;             /* from mla_get_sched_meta (same shape), or NULL   */
     const int32_t* num_splits;          /* [b + 1] split prefix from mla_get_sched_meta, or
@@ -167,7 +173,8 @@ int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream);
  * out / lse; unsplit requests are left untouched. */
 int mla_splitkv_combine(const mla_decode_args* args, void* stream);
 
-/* Test hook for the gather + dequant stage: for every (b, s, slot) writes the
+/* Test hook for the gather + dequant stage (attn_sink and topk_length are not
+ * used): for every (b, s, slot) writes the
  * dequantised 576-value row as the decode kernel stages it, bf16
  * [b, s_q, topk, 576] into k_rows; if v_rows is not NULL also the 512 V values
  * read back through the decode kernel's transposed V layout, bf16

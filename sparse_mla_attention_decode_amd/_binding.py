@@ -191,7 +191,10 @@ class DecodePlan:
         if not self.closed_form:
             mla_get_sched_meta(self.shape, self.sched_meta.data_ptr(), self.num_splits.data_ptr(), stream)
 
-    def args(self, q, kv, indices, sm_scale: float = 0.0, out=None, lse=None) -> mla_decode_args:
+    def args(self, q, kv, indices, sm_scale: float = 0.0, out=None, lse=None, attn_sink=None,
+             topk_length=None) -> mla_decode_args:
+        """attn_sink: fp32 [h_q] device tensor or None; topk_length: int32 [b] device
+        tensor or None (both contiguous)."""
         out = self.out if out is None else out
         lse = self.lse if lse is None else lse
         if self.shape.kv_format == MLA_KV_FP8_656:
@@ -210,8 +213,8 @@ class DecodePlan:
         a.out = out.data_ptr()
         a.out_stride_b, a.out_stride_s, a.out_stride_h = out.stride(0), out.stride(1), out.stride(2)
         a.lse = lse.data_ptr()
-        a.attn_sink = None
-        a.topk_length = None
+        a.attn_sink = None if attn_sink is None else attn_sink.data_ptr()
+        a.topk_length = None if topk_length is None else topk_length.data_ptr()
         a.sched_meta = None if self.closed_form else self.sched_meta.data_ptr()
         a.num_splits = None if self.closed_form else self.num_splits.data_ptr()
         a.o_accum = self.o_accum.data_ptr()
@@ -220,11 +223,12 @@ class DecodePlan:
         a.lse_accum_bytes = self.lse_accum.numel() * 4
         return a
 
-    def run(self, q, kv, indices, sm_scale: float = 0.0, stream=None, with_sched: bool = True):
+    def run(self, q, kv, indices, sm_scale: float = 0.0, stream=None, with_sched: bool = True,
+            attn_sink=None, topk_length=None):
         """sched (optional) -> decode -> combine, all on `stream`."""
         if with_sched:
             self.get_sched_meta(stream)
-        a = self.args(q, kv, indices, sm_scale)
+        a = self.args(q, kv, indices, sm_scale, attn_sink=attn_sink, topk_length=topk_length)
         mla_sparse_decode_fwd(a, stream)
         mla_splitkv_combine(a, stream)
         return self.out, self.lse

@@ -360,6 +360,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         const int k_hi = min(blk_hi * p.block, p.topk);
         const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
         const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+        // slots below k_ok hold ids; the ones past the request's valid length
+        // (topk_length) are empty like the ones past the piece
+        const int k_ok = p.topk_length ? min(k_hi, max(p.topk_length[req], 0)) : k_hi;
 
         // LDS slots of this wave's token ids: tile t in the ring (t % 2), the
         // first four tiles of a pass in the prologue area
@@ -414,7 +417,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 #pragma unroll
                 for (int j = 0; j < KAHEAD; ++j)
                     if (scores) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
-                if (soft && copies) copy_ids(idx, k_lo, k_hi, i + 5, ln, lds0 + ring_slot(r3));
+                if (soft && copies) copy_ids(idx, k_lo, k_ok, i + 5, ln, lds0 + ring_slot(r3));
                 __builtin_amdgcn_sched_barrier(0);
                 float mx, psum = 0.f;
 #pragma unroll
@@ -538,8 +541,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             f32x16 S_cur;                           // scores of tile i
             {
                 const int ln = opaque_lane();
-                for (int t = 0; t < 4; ++t) copy_ids(idx, k_lo, k_hi, t, ln, lds0 + first_slot(t));
-                copy_ids(idx, k_lo, k_hi, 4, ln, lds0 + ring_slot(4));
+                for (int t = 0; t < 4; ++t) copy_ids(idx, k_lo, k_ok, t, ln, lds0 + first_slot(t));
+                copy_ids(idx, k_lo, k_ok, 4, ln, lds0 + ring_slot(4));
                 if (pass == 0) {
                     // Q of the wave's 32 heads (with 64 query heads waves 2 and
                     // 3 take heads 0..63 again; those results are never stored)
@@ -655,13 +658,19 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         if (lane < 32) *(LDS_AS f32x2*)(lds + L_LM + 8 * (32 * wave + n)) = f32x2{l_tot, m_ref};
         __syncthreads();
         float inv[4];
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-            const float l = *(const LDS_AS float*)(lds + L_LM + 8 * (32 * hb + n));
-            inv[hb] = l > 0.f ? 1.0f / l : 0.f;
-        }
         const int first_split = split_prefix(p, req);
         const int nsplit = split_prefix(p, req + 1) - first_split;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+            const f32x2 lm = *(const LDS_AS f32x2*)(lds + L_LM + 8 * (32 * hb + n));
+            // the final output of an unsplit request takes the attention sink
+            // as an extra exp-sum term 2^(sink log2(e) - m) (split requests: in
+            // the combine)
+            float den = lm[0];
+            if (nsplit == 1 && p.attn_sink != nullptr && 32 * hb + n < p.h_q)
+                den += __builtin_amdgcn_exp2f(p.attn_sink[32 * hb + n] * 1.4426950408889634f - lm[1]);
+            inv[hb] = lm[0] > 0.f ? 1.0f / den : 0.f;
+        }
         const int own_head = 32 * wave + n;
         if (nsplit == 1) {
             uint16_t* obase = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss;
@@ -818,7 +827,12 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
             }
         }
     }
-    const float inv = W > 0.f ? 1.0f / W : 0.f;
+    // an attention sink adds 2^(sink log2(e) - M) to the exp-sum (base 2, in
+    // units of 2^M); lse stays that of the real slots
+    const float den = p.attn_sink != nullptr && W > 0.f
+                          ? W + __builtin_amdgcn_exp2f(p.attn_sink[head] * 1.4426950408889634f - M)
+                          : W;
+    const float inv = W > 0.f ? 1.0f / den : 0.f;
     uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh +
                      128 * w + 32 * j + 4 * h;
 #pragma unroll

@@ -112,8 +112,8 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         return fail(MLA_ERR_INVALID_ARG, "sched_meta and num_splits must both be set (mla_get_sched_meta) or both NULL");
     if (inline_plan && r.overhead != 0)
         return fail(MLA_ERR_INVALID_ARG, "a NULL plan (closed form) needs fixed_overhead 0, got %d", r.overhead);
-    if (a->attn_sink) return fail(MLA_ERR_UNSUPPORTED, "attn_sink is not supported by this build");
-    if (a->topk_length) return fail(MLA_ERR_UNSUPPORTED, "topk_length is not supported by this build");
+    if ((a->attn_sink && !aligned(a->attn_sink, 4)) || (a->topk_length && !aligned(a->topk_length, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "attn_sink and topk_length must be 4-byte aligned");
     if (!aligned(a->q, 16) || a->q_stride_h % 8 || a->q_stride_s % 8 || a->q_stride_b % 8)
         return fail(MLA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
     if (a->q_stride_h < 576 && r.h_q > 1)
@@ -160,6 +160,8 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     p->num_splits = a->num_splits;
     p->o_accum = a->o_accum;
     p->lse_accum = a->lse_accum;
+    p->attn_sink = a->attn_sink;
+    p->topk_length = a->topk_length;
     p->n_tok = r.num_kv_tokens;
     p->n_tok32 = (uint32_t)(r.num_kv_tokens < INT32_MAX ? r.num_kv_tokens : INT32_MAX);
     p->b = r.b;

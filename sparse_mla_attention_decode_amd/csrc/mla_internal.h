@@ -32,6 +32,8 @@ struct DecodeParams {
     const int32_t* num_splits;
     float* o_accum;
     float* lse_accum;
+    const float* attn_sink;         // [h_q] natural-log sink logits, or NULL
+    const int32_t* topk_length;     // [b] valid slots per request, or NULL
     int64_t n_tok;
     uint32_t n_tok32;               // min(n_tok, 2^31 - 1): token ids are int32
     int b, s_q, h_q, topk, page_block_size, block;

@@ -439,8 +439,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
             const int k = k_lo + tile * TILE + (lane & 31);
             return idx[min(k, k_hi - 1)];
         };
+        // slots past the request's valid length (topk_length) are empty too
+        const int k_ok = p.topk_length ? min(k_hi, max(p.topk_length[req], 0)) : k_hi;
         auto ids_in_range = [&](int tile) -> bool {
-            return tile < n_tiles && k_lo + tile * TILE + (lane & 31) < k_hi;
+            return tile < n_tiles && k_lo + tile * TILE + (lane & 31) < k_ok;
         };
 
         // Q for this wave's heads as B operands: k-step j covers dims
@@ -590,7 +592,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
         const float l_tot = l_part + __shfl_xor(l_part, 32);
         const int first_split = split_prefix(p, req);
         const int nsplit = split_prefix(p, req + 1) - first_split;
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        // the final output of an unsplit request takes the attention sink as an
+        // extra exp-sum term 2^(sink log2(e) - m) (split requests: in the combine)
+        const float den = nsplit == 1 && p.attn_sink != nullptr
+                              ? l_tot + __builtin_amdgcn_exp2f(p.attn_sink[head] * 1.4426950408889634f - m_ref)
+                              : l_tot;
+        const float inv = l_tot > 0.f ? 1.0f / den : 0.f;
         if (nsplit == 1) {
             uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss +
                              (int64_t)head * p.out_sh;
@@ -709,7 +716,12 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
     float tot = 0.f;
     for (int j = lane; j < ns; j += 64) tot += __builtin_amdgcn_exp2f(lse_at(j) - mx);
     tot = wave_sum(tot);
-    const float inv = 1.0f / tot;
+    // an attention sink adds 2^(sink log2(e) - mx) to the exp-sum; lse keeps
+    // the real slots only
+    const float den = p.attn_sink != nullptr
+                          ? tot + __builtin_amdgcn_exp2f(p.attn_sink[head] * 1.4426950408889634f - mx)
+                          : tot;
+    const float inv = 1.0f / den;
     f32x4 a0 = {}, a1 = {};
     for (int j = 0; j < ns; ++j) {
         const float w = __builtin_amdgcn_exp2f(lse_at(j) - mx) * inv;

@@ -107,7 +107,7 @@ def _args(s, **over):
     (dict(q=None), M.MLA_ERR_INVALID_ARG), (dict(kv=None), M.MLA_ERR_INVALID_ARG),
     (dict(sched_meta=None), M.MLA_ERR_INVALID_ARG), (dict(num_splits=None), M.MLA_ERR_INVALID_ARG),
     (dict(sched_meta=None, num_splits=None), M.MLA_ERR_INVALID_ARG),   # NULL plan needs overhead 0
-    (dict(attn_sink=0xA000), M.MLA_ERR_UNSUPPORTED), (dict(topk_length=0xA000), M.MLA_ERR_UNSUPPORTED),
+    (dict(attn_sink=0xA002), M.MLA_ERR_INVALID_ARG), (dict(topk_length=0xA001), M.MLA_ERR_INVALID_ARG),
     (dict(q=0x1008), M.MLA_ERR_INVALID_ARG), (dict(q_stride_h=580), M.MLA_ERR_INVALID_ARG),
     (dict(kv_stride_block=64 * 656 - 16), M.MLA_ERR_INVALID_ARG), (dict(kv=0x2004), M.MLA_ERR_INVALID_ARG),
     (dict(out_stride_h=513), M.MLA_ERR_INVALID_ARG), (dict(o_accum_bytes=16), M.MLA_ERR_WORKSPACE),

@@ -1,0 +1,94 @@
+"""GPU parity of the attention sink and the per-request valid length
+(attn_sink / topk_length) against the CPU oracle: split and unsplit requests,
+the 128- and 64-head FP8 kernel, the generic BF16 kernel, the closed-form
+plan and the benchmark shape."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from sparse_mla_attention_decode_amd import workloads as W
+from test_gpu_parity import _need_gpu, _plan, all_queries, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def run_with(w, sink, lens, closed_form=False, **kw):
+    _need_gpu()
+    plan = _plan(w, closed_form=closed_form, **kw)
+    s_t = None if sink is None else torch.tensor(sink, dtype=torch.float32, device="cuda")
+    l_t = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, lse = plan.run(w.q_device(), w.kv_device(), w.indices_device(), w.sm_scale, attn_sink=s_t, topk_length=l_t)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_with(w, sink, lens, queries=None):
+    return O.sparse_mla_decode(w.q_bits, w.kv_host(), w.indices, w.sm_scale, w.kv_format, w.page_block_size,
+                               queries=queries, attn_sink=sink, topk_length=lens)
+
+
+def _sink(rng, h):
+    s = rng.standard_normal(h) * 2.0 + 1.0
+    s[::7] = 6.0                                          # sinks that take most of the mass
+    s[3] = -np.inf                                        # and one that takes none
+    return s
+
+
+@pytest.mark.parametrize("parts", [0, 1, 7])
+def test_sink_and_length_fp8_h128(parts):
+    rng = np.random.default_rng(91)
+    w = W.paged_decode("sl128", 91, b=6, s_q=2, h_q=128, topk=300, tokens_per_seq=1024, P=64)
+    sink = _sink(rng, 128)
+    lens = np.array([300, 0, 1, 150, 33, 5000])           # full, none, one, mid, within a tile, past topk
+    out, lse = run_with(w, sink, lens, num_parts=parts, split_granularity=32)
+    ref_out, ref_lse = oracle_with(w, sink, lens)
+    assert np.all(out[1] == 0) and np.all(np.isposinf(lse[1]))
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"sink+len h128 parts={parts}")
+
+
+@pytest.mark.parametrize("which", ["sink", "length"])
+def test_sink_or_length_alone_closed_form(which):
+    rng = np.random.default_rng(92)
+    w = W.paged_decode("slcf", 92, b=5, s_q=1, h_q=128, topk=520, tokens_per_seq=1024, P=64)
+    sink = _sink(rng, 128) if which == "sink" else None
+    lens = np.array([520, 77, 260, 1, 519]) if which == "length" else None
+    out, lse = run_with(w, sink, lens, closed_form=True, num_parts=11, split_granularity=32, fixed_overhead=0)
+    ref_out, ref_lse = oracle_with(w, sink, lens)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"{which} closed form")
+
+
+@pytest.mark.parametrize("parts", [0, 1, 5])
+def test_sink_and_length_fp8_h64(parts):
+    rng = np.random.default_rng(93)
+    w = W.paged_decode("sl64", 93, b=4, s_q=2, h_q=64, topk=200, tokens_per_seq=512, P=64)
+    sink = _sink(rng, 64)
+    lens = np.array([200, 64, 0, 131])
+    out, lse = run_with(w, sink, lens, num_parts=parts, split_granularity=32)
+    ref_out, ref_lse = oracle_with(w, sink, lens)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"sink+len h64 parts={parts}")
+
+
+@pytest.mark.parametrize("parts", [1, 4])
+def test_sink_and_length_bf16_prefill(parts):
+    rng = np.random.default_rng(94)
+    w = W.sparse_prefill("slbf", 94, s_q=7, h_q=128, topk=90, s_kv=160, prior=100)
+    sink = _sink(rng, 128)
+    lens = np.array([61])
+    out, lse = run_with(w, sink, lens, num_parts=parts, split_granularity=32)
+    ref_out, ref_lse = oracle_with(w, sink, lens)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"sink+len bf16 parts={parts}")
+
+
+def test_sink_and_length_benchmark_shape():
+    """The benchmarked launch (64 x 128 heads x 2048 slots, NULL plan) with a
+    sink and varied lengths; sampled queries against the oracle."""
+    rng = np.random.default_rng(95)
+    w = W.make_config(1)
+    sink = _sink(rng, 128)
+    lens = rng.integers(0, 2049, size=64)
+    lens[:3] = [2048, 0, 1000]
+    out, lse = run_with(w, sink, lens, closed_form=True, num_parts=256, split_granularity=32, fixed_overhead=0)
+    qs = [(0, 0), (1, 0), (2, 0), (40, 0)]
+    ref_out, ref_lse = oracle_with(w, sink, lens, qs)
+    assert_parity(out, lse, ref_out, ref_lse, qs, "sink+len cfg1")
