@@ -184,7 +184,7 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     p->block = r.block;
     {
         // closed-form plan constants (used by the kernels only when the plan
-        // pointers are NULL); resolve() keeps b * B below 2^31
+        // pointers are NULL); resolve() keeps b * B below 2^30
         const int64_t B = (r.topk + r.block - 1) / r.block, T = (int64_t)r.b * B;
         const int64_t P = (T + r.num_parts - 1) / r.num_parts;
         int64_t x = B, y = P;
@@ -198,6 +198,10 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         p->plan_payload = (uint32_t)P;
         p->plan_gb = (uint32_t)(B / x);
         p->plan_gp = (uint32_t)(P / x);
+        p->div_nblk = mla::make_fastdiv(p->plan_nblk);
+        p->div_payload = mla::make_fastdiv(p->plan_payload);
+        p->div_gb = mla::make_fastdiv(p->plan_gb);
+        p->div_gp = mla::make_fastdiv(p->plan_gp);
     }
     p->c = sm * 1.4426950408889634f;
     p->threshold = mla::kRefGapLog2;

@@ -17,6 +17,20 @@ struct ResolvedShape {
     int overhead;    // scheduler per-request cost in blocks
 };
 
+// Division by a divisor fixed at launch: for 0 <= n < 2^31,
+// n / d == (mulhi(n, m) + n) >> s with s = ceil(log2 d),
+// m = floor(2^32 (2^s - d) / d) + 1 (the round-up reciprocal).
+struct FastDiv {
+    uint32_t m;
+    int s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    int s = 0;
+    while ((1ull << s) < d) ++s;
+    return FastDiv{(uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1), s};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
+
 // Kernel arguments (by value).
 struct DecodeParams {
     const uint16_t* q;
@@ -46,6 +60,7 @@ struct DecodeParams {
     // b * B blocks, partitions of `payload` blocks; gb = B / gcd(B, payload),
     // gp = payload / gcd(B, payload).  All below 2^31.
     uint32_t plan_nblk, plan_total, plan_payload, plan_gb, plan_gp;
+    FastDiv div_nblk, div_payload, div_gb, div_gp;     // the same divisors as reciprocals
     float c;                        // sm_scale * log2(e)
     float threshold;                // log2-units gap above the reference max that
                                     // makes a piece recompute with a higher reference
@@ -88,11 +103,13 @@ __device__ __forceinline__ PartPlan plan_part(const DecodeParams& p, int part) {
         return r;
     }
     const uint32_t e = min(s0 + P, T) - 1;
-    r.begin_req = (int)(s0 / B);
-    r.end_req = (int)(e / B);
-    r.begin_block = (int)(s0 % B);
-    r.end_block = (int)(e % B) + 1;
-    r.begin_split = q == 0 ? 0 : (int)(q + (s0 - 1) / B - (q - 1) / p.plan_gb);
+    // every dividend is below b B < 2^30 (checked on the host)
+    const uint32_t rs = fdiv(s0, p.div_nblk), re = fdiv(e, p.div_nblk);
+    r.begin_req = (int)rs;
+    r.end_req = (int)re;
+    r.begin_block = (int)(s0 - rs * B);
+    r.end_block = (int)(e - re * B) + 1;
+    r.begin_split = q == 0 ? 0 : (int)(q + fdiv(s0 - 1, p.div_nblk) - fdiv(q - 1, p.div_gb));
     return r;
 }
 
@@ -104,7 +121,7 @@ __device__ __forceinline__ int split_prefix(const DecodeParams& p, int r) {
     if (p.num_splits != nullptr) return p.num_splits[r];
     if (r == 0) return 0;
     const uint32_t u = (uint32_t)r;
-    return (int)(u + (u * p.plan_nblk - 1) / p.plan_payload - (u - 1) / p.plan_gp);
+    return (int)(u + fdiv(u * p.plan_nblk - 1, p.div_payload) - fdiv(u - 1, p.div_gp));
 }
 
 // A tile whose max score exceeds the reference (the first valid tile's max) by

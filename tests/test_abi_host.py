@@ -197,3 +197,22 @@ def test_host_plan_reproduces_walkthrough_example():
         (0, 0, 0, 1, 0, 1), (0, 0, 1, 2, 1, 0), (1, 1, 0, 1, 0, 1), (1, 1, 1, 2, 1, 0)]
     assert ns.tolist() == [0, 2, 4]
     assert (meta[4:, 0] >= 2).all()
+
+
+def test_round_up_reciprocal_division_is_exact():
+    """The kernels divide by launch-time divisors (blocks per request, the
+    partition payload and their gcd quotients) as (mulhi(n, m) + n) >> s with
+    s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1; every dividend is below
+    2^30.  Checked here against exact integer division, edge values included."""
+    rng = np.random.default_rng(7)
+    divisors = list(range(1, 3000)) + [int(x) for x in rng.integers(1, 1 << 30, 2000)] + [(1 << 30) - 1, 1 << 30]
+    for d in divisors:
+        s = 0
+        while (1 << s) < d:
+            s += 1
+        m = ((1 << 32) * ((1 << s) - d)) // d + 1
+        assert m < (1 << 32)
+        ns = [0, 1, d - 1, d, d + 1, 2 * d - 1, (1 << 30) - 1] + [int(x) for x in rng.integers(0, 1 << 30, 50)]
+        for n in ns:
+            if n >= 0:
+                assert (((n * m) >> 32) + n) % (1 << 32) >> s == n // d, (n, d)
