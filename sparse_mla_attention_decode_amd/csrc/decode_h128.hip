@@ -408,7 +408,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // 1 - par for tile parity par).  With soft == false (the prologue)
             // only the scores of tile 0.
             auto part1 = [&](int i, int par, int kb, int ln, bool soft, bool scores, bool copies, const uint8_t* src3,
-                             uint32_t vm, f32x16 S, f32x16& S_next) {
+                             uint32_t vm, f32x16 S, f32x16& S_next, const StageRegs* pro_g) {
                 const int qk = kb + qk_base(ln, 0);
                 const int r3 = 1 - par;
                 const uint32_t raw3 = raw0 + r3 * RAW_BYTES;
@@ -432,6 +432,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         else if (js == 1) mfma_qk_first(Sb, cur, qa[1]);
                         else if (js & 1) mfma_qk(Sb, cur, qa[js]);
                         else mfma_qk(Sa, cur, qa[js]);
+                    }
+                    if (pro_g != nullptr) {
+                        // prologue: tile 1 staged into K buffer 1 under the scores of tile 0
+                        if (js == 4) stage_chunk<0>(lds, *pro_g, L_KB + KBB, wave, ln);
+                        if (js == 12) stage_chunk<1>(lds, *pro_g, L_KB + KBB, wave, ln);
+                        if (js == 20) stage_chunk<2>(lds, *pro_g, L_KB + KBB, wave, ln);
+                        if (js == 28) {
+                            stage_chunk<3>(lds, *pro_g, L_KB + KBB, wave, ln);
+                            stage_rope(lds, *pro_g, L_KB + KBB, wave, ln);
+                        }
                     }
                     if (soft) {
                         if (copies && js >= 3 && js <= 23 && js % 5 == 3)
@@ -586,15 +596,19 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx);
                 wait_vmcnt<0>();                        // copies of tiles 0 and 1
                 stage_rows(lds, slice_off, L_KB, wave, ln);
-                stage_rows(lds, slice_off + RAW_BYTES, L_KB + KBB, wave, ln);
                 // raw slot 0 is read (its values went through the conversions)
                 gather_rows(src2, ln, lds0 + slice_off);
             }
-            __syncthreads();
+            __syncthreads();                        // tile 0 staged
             {
+                // the scores of tile 0 with the staging of tile 1 (raw slot 1)
+                // between them
+                const int ln = opaque_lane();
+                const StageRegs g1 = stage_load(lds, slice_off + RAW_BYTES, ln);
                 f32x16 none = {};
-                part1(-1, 1, L_KB, opaque_lane(), false, true, false, nullptr, 0u, none, S_cur);
+                part1(-1, 1, L_KB, ln, false, true, false, nullptr, 0u, none, S_cur, &g1);
             }
+            __syncthreads();                        // tile 1 staged
 
             // K buffers of the values, scores and staging of tile i (buffers
             // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
@@ -609,7 +623,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
                 f32x16 S_next;
-                part1(i, par, kb_s, ln, true, scores, copies, src_nx, vm0, S_cur, S_next);
+                part1(i, par, kb_s, ln, true, scores, copies, src_nx, vm0, S_cur, S_next, nullptr);
                 __syncthreads();
                 const uint8_t* src4 = src_nx;
                 uint32_t vm4 = 0u;
