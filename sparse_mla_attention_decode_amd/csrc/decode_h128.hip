@@ -53,36 +53,39 @@ constexpr int NW = 4;                             // waves per work-group
 constexpr int ROWB = 656;                         // FP8 token row
 constexpr int RCH = ROWB / 16;                    // 41 16-byte chunks per row
 constexpr int WROWS = TILE / NW;                  // rows gathered and staged per wave
-constexpr int WAVE_RAW = WROWS * ROWB;            // 5248 bytes: one wave's slice
-constexpr int NDMA = (RCH + 7) / 8;               // 6 copies per lane per tile
-constexpr int RAW_BYTES = TILE * ROWB;            // 20992
+constexpr int WAVE_RAW = 4 * 1024 + WROWS * 16;   // 4224: NoPE codes and scales of a wave's 8 rows
+constexpr int NDMA = 6;                           // copies per lane per tile: 4 NoPE, RoPE, scales
+constexpr int RAW_BYTES = NW * WAVE_RAW;          // 16896
 constexpr int NRAW = 2;                           // raw tiles (one being staged, one landing)
 constexpr int NKB = 3;                            // staged tiles (scores, values, being staged)
-constexpr int KP = 1168;                          // staged row pitch (1152 + 16)
-constexpr int KBB = TILE * KP;                    // 37376
+constexpr int NP = 1040;                          // staged NoPE row pitch (1024 + 16)
+constexpr int ROPE_OFF = TILE * NP;               // 33280: RoPE rows of a staged tile
+constexpr int KBB = ROPE_OFF + TILE * 128;        // 37376
 constexpr int IDS_SLOTS = 2;                      // token-id tiles per wave in LDS
 constexpr int ZERO_ROWS = 64;                     // rows of the zero page
 constexpr int KAHEAD = 3;                         // score fragments read ahead of their MFMAs
 
-// LDS map (bytes).  The 16-byte pad at the end of every staged row is never
-// read by the contractions; row 0's pad of staged buffer 0 holds the restart
-// flags.  The ids of the first four tiles of a pass and the head statistics
-// of the epilogue use the P area.
+// LDS map (bytes).  A staged tile is 32 NoPE rows of NP bytes (bf16 dims
+// 0..511 and a 16-byte pad that the contractions never read) and 32 RoPE rows
+// of 128 bytes copied straight from the cache, chunk c of key n in slot
+// c ^ ((n / 2) % 8) so that the score reads are conflict-free.  Row 0's pad of
+// staged buffer 0 holds the restart flags; the head statistics of the
+// epilogue use the P area.
 constexpr int XPB = NW * 2048;                          // P of one tile, all 128 heads
-constexpr int L_RAW = 0;                               // [2][4 slices][6][8 rows][8 chunks][16]
-constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;          // [3][32 rows][1168] bf16 K
+constexpr int L_RAW = 0;                               // [2][4 slices][4224]: NoPE codes, scales
+constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;          // [3] x ([32][NP] bf16 NoPE, [32][128] RoPE)
 constexpr int L_XP = L_KB + NKB * KBB;                  // [4 head blocks][2 k-steps][64][16]
 constexpr int L_IDS = L_XP + XPB;                       // [4 waves][2 slots][32] int32
-constexpr int L_BYTES = L_IDS + NW * IDS_SLOTS * 128;
-constexpr int L_FLAGS = L_KB + 1152;                    // [4] restart flags (row pad)
+constexpr int L_IDS0 = L_IDS + NW * IDS_SLOTS * 128;    // [4 waves][4 tiles][32] int32 (prologue)
+constexpr int L_BYTES = L_IDS0 + NW * 4 * 128;
+constexpr int L_FLAGS = L_KB + 1024;                    // [4] restart flags (row pad)
 constexpr int L_LM = L_XP;                              // [128 heads] {l, m} (epilogue)
 constexpr int QROW = 1168;                              // Q rows in LDS: 72 chunks + pad (prologue)
 constexpr int QCOPIES = (32 * QROW / 16 + 63) / 64;     // 37 whole-line copies per wave
 constexpr int L_Q = 0;                                  // [4 waves][32 heads][QROW] (prologue only)
-constexpr int L_IDS0 = L_XP;                            // [4 waves][4 tiles][32] int32 (prologue)
 static_assert(L_BYTES <= 160 * 1024, "LDS budget");
-static_assert(L_Q + NW * 32 * QROW <= L_IDS0 && QCOPIES == 37 && 32 * QROW == 36 * 1024 + 32 * 16, "Q staging");
-static_assert(NDMA == 6 && RCH - 8 * (NDMA - 1) == 1, "copy layout");
+static_assert(L_Q + NW * 32 * QROW <= L_IDS && QCOPIES == 37 && 32 * QROW == 36 * 1024 + 32 * 16, "Q staging");
+static_assert(RCH == 41 && WAVE_RAW == 4224, "copy layout");
 
 // Rows copied for empty or out-of-range slots: all zero bytes (zero codes,
 // zero scales, zero RoPE), so staged values of empty slots are zero without
@@ -91,14 +94,25 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_rows[ZERO_ROWS * ROWB];
 // The id copied for slots past the end of a piece: such slots are empty.
 __device__ int32_t g_no_id[1] = {-1};
 
-// Raw slice layout (5248 bytes): chunk c < 40 of row r at 1024 (c / 8) +
-// 128 r + 16 (c % 8); chunk 40 of row r at 5120 + 16 r.  Copy i < 5 of lane L
-// moves chunk (L % 8) + 8 i of row L / 8, i.e. LDS byte 1024 i + 16 L: every 8
-// lanes read 128 contiguous bytes of one row and each lane needs one row
-// address per tile.  The last copy moves chunk 40 of row L with lanes 0..7.
+// Raw slice layout (4224 bytes): NoPE chunk c < 32 of row r at 1024 (c / 8) +
+// 128 r + 16 (c % 8); the scale chunk (32) of row r at 4096 + 16 r.  Copy
+// i < 4 of lane L moves chunk (L % 8) + 8 i of row L / 8, i.e. LDS byte
+// 1024 i + 16 L: every 8 lanes read 128 contiguous bytes of one row and each
+// lane needs one row address per tile.  The RoPE copy moves the 8 RoPE chunks
+// (33..40) of every row into the staged tile; the scale copy moves chunk 32
+// of row L with lanes 0..7.
 __device__ __forceinline__ int raw_off(int row, int chunk) {
-    return chunk < 40 ? 1024 * (chunk >> 3) + 128 * row + 16 * (chunk & 7) : 5120 + 16 * row;
+    return chunk < 32 ? 1024 * (chunk >> 3) + 128 * row + 16 * (chunk & 7) : 4096 + 16 * row;
 }
+// RoPE copy of lane L (row L / 8 = key 8 w + L / 8 of the tile, slot L % 8):
+// it moves RoPE chunk (L % 8) ^ ((key / 2) % 8) of its row; `src` points at
+// chunk L % 8 of the row.
+__device__ __forceinline__ const uint8_t* rope_src(const uint8_t* src, int lane, int wave) {
+    const int key = WROWS * wave + (lane >> 3), s = lane & 7;
+    return src + 16 * (33 + (s ^ ((key >> 1) & 7)) - s);
+}
+// Byte offset of RoPE chunk c (0..7) of key n in a staged tile.
+__device__ __forceinline__ int rope_off(int n, int c) { return ROPE_OFF + 128 * n + 16 * (c ^ ((n >> 1) & 7)); }
 
 // Partitions of one request are adjacent in the plan and blocks are dealt to
 // the 8 XCDs round robin: map each XCD's blocks to a contiguous partition
@@ -135,16 +149,16 @@ __device__ __forceinline__ const uint8_t* row_addr(const DecodeParams& p, int t,
 // Copies of this wave's 8 rows of a tile into its raw slice; `src` points at
 // chunk lane % 8 of row lane / 8 (key 8w + lane / 8).
 __device__ __forceinline__ const uint8_t* tail_src(const uint8_t* src, int lane) {
-    // chunk 40 of row `lane` (lanes 0..7): row starts are held by lanes 8 r
+    // chunk 32 (scales) of row `lane` (lanes 0..7): row starts are held by lanes 8 r
     const uint64_t row = (uint64_t)(uintptr_t)(src - 16 * (lane & 7));
     const int from = 8 * (lane & 7);
     const uint64_t rl = ((uint64_t)(uint32_t)__shfl((uint32_t)(row >> 32), from) << 32) |
                         (uint32_t)__shfl((uint32_t)row, from);
-    return (const uint8_t*)(uintptr_t)rl + 16 * 40;
+    return (const uint8_t*)(uintptr_t)rl + 16 * 32;
 }
 __device__ __forceinline__ void gather_tail(const uint8_t* src, int lane, uint32_t slice) {
     const uint8_t* t = tail_src(src, lane);
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(slice + 1024u * (NDMA - 1));
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(slice + 4096u);
     if (lane < 8) dma16(t, dst);
 }
 // The same with the destination given as a scalar base plus a constant.
@@ -152,10 +166,13 @@ __device__ __forceinline__ void gather_tail_at(const uint8_t* src, int lane, uin
     const uint8_t* t = tail_src(src, lane);
     if (lane < 8) dma16_at(t, base, off);
 }
-__device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, uint32_t slice) {
+// All six copies of a tile: NoPE and scales into the raw slice, RoPE into
+// the staged tile whose RoPE rows of this wave start at `rope_dst`.
+__device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, int wave, uint32_t slice, uint32_t rope_dst) {
 #pragma unroll
-    for (int i = 0; i < NDMA - 1; ++i)
+    for (int i = 0; i < 4; ++i)
         dma16(src + 128 * i, __builtin_amdgcn_readfirstlane(slice + 1024u * i));
+    dma16(rope_src(src, lane, wave), __builtin_amdgcn_readfirstlane(rope_dst));
     gather_tail(src, lane, slice);
 }
 
@@ -169,99 +186,46 @@ __device__ __forceinline__ void copy_ids(const int32_t* idx, int k_lo, int k_hi,
     if (lane < 32) dma4(src, dst);
 }
 
-// Staging of this wave's 8 rows.  Lane L holds chunks (L % 8) + 8 i of row
-// r = L / 8 (copies i = 0..5).  Copies 0..3 are NoPE codes (dims 16 c ..
-// 16 c + 15, scale group i): dequantised into 32 bytes of the staged row.
-// Chunk 32 is the scale block; chunks 33..40 are RoPE (bf16 already): moved to
-// bytes 1024 + 16 (c - 33) of the staged row.  Split into the LDS reads and
-// the conversion + writes, so a caller can put other work between them.
+// Staging of this wave's 8 rows.  Lane L holds NoPE chunks (L % 8) + 8 i of
+// row r = L / 8 (copies i = 0..3: dims 16 c .. 16 c + 15, scale group i) and
+// the row's four scales: dequantised into 32 bytes of the staged NoPE row.
+// Split into the LDS reads and the conversion + writes, so a caller can put
+// other work between them.  (The RoPE chunks were copied into the staged tile
+// directly.)
 struct StageRegs {
     u32x4 w[4];
     float sc[4];
-    u32x4 rope;
 };
 __device__ __forceinline__ StageRegs stage_load(const LDS_AS uint8_t* lds, int slice, int lane) {
-    const int r = lane >> 3, c0 = lane & 7;
+    const int r = lane >> 3;
     StageRegs g;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         g.w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
         g.sc[i] = *(const LDS_AS float*)(lds + slice + raw_off(r, 32) + 4 * i);
     }
-    // RoPE chunk 32 + c0 (c0 > 0) or chunk 40 (c0 == 0), chosen without a branch
-    const int rope_off = c0 ? 4096 + 128 * r + 16 * c0 : 5120 + 16 * r;
-    g.rope = lds_read16(lds, slice + rope_off);
     return g;
-}
-// Converted rows of one wave's staging share: chunks c0 + 8 i (i = 0..3) as
-// 2 x 16 bytes of bf16 each, and the RoPE chunk.
-struct StagedRows {
-    u32x4 d[8];
-    u32x4 rope;
-};
-template <int I>
-__device__ __forceinline__ void stage_convert(const StageRegs& g, StagedRows& o) {
-    const u32x4 w = g.w[I];
-    const float sc = g.sc[I];
-    o.d[2 * I] = u32x4{dequant2<false>(w[0], sc), dequant2<true>(w[0], sc),
-                       dequant2<false>(w[1], sc), dequant2<true>(w[1], sc)};
-    o.d[2 * I + 1] = u32x4{dequant2<false>(w[2], sc), dequant2<true>(w[2], sc),
-                           dequant2<false>(w[3], sc), dequant2<true>(w[3], sc)};
-}
-// Quarter K of chunk I (codes w[I][K]: two dwords of bf16) converted at the
-// point of the call: the empty asm statements keep the conversion from being
-// hoisted or sunk across the surrounding matrix instructions.
-template <int I, int K>
-__device__ __forceinline__ void convert_here(const StageRegs& g, StagedRows& o) {
-    uint32_t w = g.w[I][K];
-    float sc = g.sc[I];
-    asm volatile("" : "+v"(w), "+v"(sc));
-    uint32_t lo = dequant2<false>(w, sc), hi = dequant2<true>(w, sc);
-    asm volatile("" : "+v"(lo), "+v"(hi));
-    o.d[2 * I + K / 2][2 * (K & 1)] = lo;
-    o.d[2 * I + K / 2][2 * (K & 1) + 1] = hi;
-}
-__device__ __forceinline__ void stage_write(LDS_AS uint8_t* lds, const StagedRows& o, int kb, int wave, int lane) {
-    const int r = lane >> 3, c0 = lane & 7;
-    const int row = kb + (WROWS * wave + r) * KP;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int off = row + 32 * (c0 + 8 * i);
-        lds_write16(lds, off, o.d[2 * i]);
-        lds_write16(lds, off + 16, o.d[2 * i + 1]);
-    }
-    lds_write16(lds, row + 1024 + 16 * (c0 ? c0 - 1 : 7), o.rope);
 }
 // Chunk I of this wave's staging share converted and written at once (the
 // target buffer is free): dims 16 (c0 + 8 I) .. +15 of row 8 wave + r.
 template <int I>
 __device__ __forceinline__ void stage_chunk(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
     const int r = lane >> 3, c0 = lane & 7;
-    StagedRows o;
-    stage_convert<I>(g, o);
-    const int off = kb + (WROWS * wave + r) * KP + 32 * (c0 + 8 * I);
-    lds_write16(lds, off, o.d[2 * I]);
-    lds_write16(lds, off + 16, o.d[2 * I + 1]);
-}
-__device__ __forceinline__ void stage_rope(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
-    const int r = lane >> 3, c0 = lane & 7;
-    lds_write16(lds, kb + (WROWS * wave + r) * KP + 1024 + 16 * (c0 ? c0 - 1 : 7), g.rope);
+    const u32x4 w = g.w[I];
+    const float sc = g.sc[I];
+    const u32x4 lo = {dequant2<false>(w[0], sc), dequant2<true>(w[0], sc),
+                      dequant2<false>(w[1], sc), dequant2<true>(w[1], sc)};
+    const u32x4 hi = {dequant2<false>(w[2], sc), dequant2<true>(w[2], sc),
+                      dequant2<false>(w[3], sc), dequant2<true>(w[3], sc)};
+    const int off = kb + (WROWS * wave + r) * NP + 32 * (c0 + 8 * I);
+    lds_write16(lds, off, lo);
+    lds_write16(lds, off + 16, hi);
 }
 __device__ __forceinline__ void stage_store(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
-    const int r = lane >> 3, c0 = lane & 7;
-    const int row = kb + (WROWS * wave + r) * KP;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 lo = {dequant2<false>(g.w[i][0], g.sc[i]), dequant2<true>(g.w[i][0], g.sc[i]),
-                          dequant2<false>(g.w[i][1], g.sc[i]), dequant2<true>(g.w[i][1], g.sc[i])};
-        const u32x4 hi = {dequant2<false>(g.w[i][2], g.sc[i]), dequant2<true>(g.w[i][2], g.sc[i]),
-                          dequant2<false>(g.w[i][3], g.sc[i]), dequant2<true>(g.w[i][3], g.sc[i])};
-        const int off = row + 32 * (c0 + 8 * i);
-        lds_write16(lds, off, lo);
-        lds_write16(lds, off + 16, hi);
-    }
-    // lane c0 = 0 holds the scale chunk (32) in copy 4 and RoPE chunk 40 in copy 5
-    lds_write16(lds, row + 1024 + 16 * (c0 ? c0 - 1 : 7), g.rope);
+    stage_chunk<0>(lds, g, kb, wave, lane);
+    stage_chunk<1>(lds, g, kb, wave, lane);
+    stage_chunk<2>(lds, g, kb, wave, lane);
+    stage_chunk<3>(lds, g, kb, wave, lane);
 }
 __device__ __forceinline__ void stage_rows(LDS_AS uint8_t* lds, int slice, int kb, int wave, int lane) {
     stage_store(lds, stage_load(lds, slice, lane), kb, wave, lane);
@@ -278,11 +242,11 @@ __device__ __forceinline__ int pv_base(int lane) {
     const int q = (lane & 15) >> 2;
     const int key = 8 * (q & 1) + 4 * (q >> 1) + 2 * (lane >> 5);
     const int dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    return key * KP + 2 * dim;
+    return key * NP + 2 * dim;
 }
 __device__ __forceinline__ bf16x8 v_frag(const LDS_AS uint8_t* lds, int off) {
     const u32x2 r0 = lds_read_tr16(lds, off);
-    const u32x2 r1 = lds_read_tr16(lds, off + KP);
+    const u32x2 r1 = lds_read_tr16(lds, off + NP);
     return __builtin_bit_cast(bf16x8, u32x4{r0[0], r0[1], r1[0], r1[1]});
 }
 
@@ -300,10 +264,12 @@ __device__ __forceinline__ u32x4 p_fragment(const f32x16& p, int t) {
     return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-// Offset of the score A operand for k-step j: dims 288 dh + 16 j + 8 h .. +7
-// of key n in the staged tile.
-__device__ __forceinline__ int qk_base(int lane, int dh) {
-    return (lane & 31) * KP + 576 * dh + 16 * (lane >> 5);
+// Offset of the score A operand for k-step j (dims 16 j + 8 h .. +7 of key n)
+// in a staged tile: NoPE row bytes for j < 32, the RoPE slot of chunk
+// 2 (j - 32) + h otherwise.
+__device__ __forceinline__ int qk_off(int lane, int j) {
+    const int n = lane & 31, h = lane >> 5;
+    return j < 32 ? n * NP + 32 * j + 16 * h : rope_off(n, 2 * (j - 32) + h);
 }
 
 // Packed split partials: for split s and query column sq, 128 KB of bf16 laid
@@ -407,9 +373,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
             // 1 - par for tile parity par).  With soft == false (the prologue)
             // only the scores of tile 0.
-            auto part1 = [&](int i, int par, int kb, int ln, bool soft, bool scores, bool copies, const uint8_t* src3,
-                             uint32_t vm, f32x16 S, f32x16& S_next, const StageRegs* pro_g) {
-                const int qk = kb + qk_base(ln, 0);
+            auto part1 = [&](int i, int par, int kb, int kb3, int ln, bool soft, bool scores, bool copies,
+                             const uint8_t* src3, uint32_t vm, f32x16 S, f32x16& S_next, const StageRegs* pro_g) {
+                const int qk = kb + qk_off(ln, 0);      // NoPE k-steps: qk + 32 j
                 const int r3 = 1 - par;
                 const uint32_t raw3 = raw0 + r3 * RAW_BYTES;
                 f32x16 Sa, Sb;
@@ -417,6 +383,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 #pragma unroll
                 for (int j = 0; j < KAHEAD; ++j)
                     if (scores) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                // RoPE k-steps 32..35 of tile i+1 (lane-dependent slots)
+                auto rope_k = [&](int j) { return kb + qk_off(ln, j); };
                 if (soft && copies) copy_ids(idx, k_lo, k_ok, i + 5, ln, lds0 + ring_slot(r3));
                 __builtin_amdgcn_sched_barrier(0);
                 float mx, psum = 0.f;
@@ -425,7 +393,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (scores) {
                         const bf16x8 cur = ka[js % KAHEAD];
                         if (js + KAHEAD < 36)
-                            ka[js % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * (js + KAHEAD)));
+                            ka[js % KAHEAD] = __builtin_bit_cast(
+                                bf16x8, lds_read16(lds, js + KAHEAD < 32 ? qk + 32 * (js + KAHEAD) : rope_k(js + KAHEAD)));
                         // two alternating accumulator chains: a score MFMA never
                         // takes the result of the one issued right before it
                         if (js == 0) mfma_qk_first(Sa, cur, qa[0]);
@@ -440,13 +409,17 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         if (js == 20) stage_chunk<2>(lds, *pro_g, L_KB + KBB, wave, ln);
                         if (js == 28) {
                             stage_chunk<3>(lds, *pro_g, L_KB + KBB, wave, ln);
-                            stage_rope(lds, *pro_g, L_KB + KBB, wave, ln);
                         }
                     }
                     if (soft) {
-                        if (copies && js >= 3 && js <= 23 && js % 5 == 3)
+                        // copies of tile i+3: NoPE chunks into the raw slot, RoPE
+                        // into the staged tile it will occupy (K buffer kb3, whose
+                        // RoPE rows the scores of its previous tile no longer read)
+                        if (copies && js >= 3 && js <= 18 && js % 5 == 3)
                             dma16_at(src3 + 128 * (js / 5), raw3, 1024 * (js / 5));
-                        if (copies && js == 28) gather_tail_at(src3, ln, raw3, 1024 * (NDMA - 1));
+                        if (copies && js == 23)
+                            dma16_at(rope_src(src3, ln, wave), lds0 + kb3 + ROPE_OFF + 1024u * wave, 0);
+                        if (copies && js == 28) gather_tail_at(src3, ln, raw3, 4096);
                         if (js == 1 && vm != 0xffffffffu) {
                             // accumulator element v holds key 8(v/4) + 4h + v%4:
                             // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
@@ -521,7 +494,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     // value step jv: k-step jv / 4, dim block jv % 4; the next V^T
                     // fragment is read ahead
                     bf16x8 vn;
-                    if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * KP + ((jv + 1) & 3) * 64);
+                    if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * NP + ((jv + 1) & 3) * 64);
 #pragma unroll
                     for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
                     if (jv == 3) {
@@ -536,7 +509,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (stage && jv == 5) stage_chunk<2>(lds, g, kb2, wave, ln);
                     if (stage && jv == 7) {
                         stage_chunk<3>(lds, g, kb2, wave, ln);
-                        stage_rope(lds, g, kb2, wave, ln);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -590,14 +562,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
                     __syncthreads();
                 }
-                gather_rows(src, ln, lds0 + slice_off);
-                gather_rows(src2, ln, lds0 + slice_off + RAW_BYTES);
+                const uint32_t rope0 = lds0 + L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0
+                gather_rows(src, ln, wave, lds0 + slice_off, rope0);
+                gather_rows(src2, ln, wave, lds0 + slice_off + RAW_BYTES, rope0 + KBB);
                 vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2);
                 vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx);
                 wait_vmcnt<0>();                        // copies of tiles 0 and 1
                 stage_rows(lds, slice_off, L_KB, wave, ln);
                 // raw slot 0 is read (its values went through the conversions)
-                gather_rows(src2, ln, lds0 + slice_off);
+                gather_rows(src2, ln, wave, lds0 + slice_off, rope0 + 2 * KBB);
             }
             __syncthreads();                        // tile 0 staged
             {
@@ -606,7 +579,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 const StageRegs g1 = stage_load(lds, slice_off + RAW_BYTES, ln);
                 f32x16 none = {};
-                part1(-1, 1, L_KB, ln, false, true, false, nullptr, 0u, none, S_cur, &g1);
+                part1(-1, 1, L_KB, 0, ln, false, true, false, nullptr, 0u, none, S_cur, &g1);
             }
             __syncthreads();                        // tile 1 staged
 
@@ -623,7 +596,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
                 f32x16 S_next;
-                part1(i, par, kb_s, ln, true, scores, copies, src_nx, vm0, S_cur, S_next, nullptr);
+                part1(i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, vm0, S_cur, S_next, nullptr);
                 __syncthreads();
                 const uint8_t* src4 = src_nx;
                 uint32_t vm4 = 0u;
@@ -753,17 +726,18 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
         const bool ok = slot_ok(p, slot[n], it * TILE + n < p.topk);
         const bool okr = slot_ok(p, slot[kr], it * TILE + kr < p.topk);
         const uint32_t vm = (uint32_t)__ballot(ok);
-        gather_rows(row_addr<false>(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, lds0 + slice_off);
+        gather_rows(row_addr<false>(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, wave, lds0 + slice_off,
+                    lds0 + L_KB + ROPE_OFF + 1024u * wave);
         wait_vmcnt<0>();
         stage_rows(lds, slice_off, L_KB, wave, lane);
         __syncthreads();
         const int key = it * TILE + n;
         if (wave < 2 && key < p.topk) {
-            const int qk = L_KB + qk_base(lane, wave);
             uint16_t* dst = k_rows + ((int64_t)qi * p.topk + key) * 576 + 288 * wave + 8 * h;
             const bool kok = (vm >> n) & 1u;
             for (int j = 0; j < 18; ++j) {
-                u32x4 v = lds_read16(lds, qk + 32 * j);
+                // the score operand read of k-step 18 w + j
+                u32x4 v = lds_read16(lds, L_KB + qk_off(lane, 18 * wave + j));
                 if (!kok) v = u32x4{0, 0, 0, 0};
                 *(u32x4*)(dst + 16 * j) = v;
             }
@@ -772,7 +746,7 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
             const int vb = L_KB + pv_base(lane);
             for (int mb = 8 * (wave - 2); mb < 8 * (wave - 1); ++mb) {
                 for (int tt = 0; tt < 2; ++tt) {
-                    const u32x4 r = __builtin_bit_cast(u32x4, v_frag(lds, vb + tt * 16 * KP + mb * 64));
+                    const u32x4 r = __builtin_bit_cast(u32x4, v_frag(lds, vb + tt * 16 * NP + mb * 64));
                     for (int e = 0; e < 8; ++e) {
                         const int q = e & 3, rr = e >> 2;
                         const int k = it * TILE + 16 * tt + 8 * (q & 1) + 4 * (q >> 1) + 2 * h + rr;
