@@ -44,8 +44,8 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "32dc9080f00cdbddb53b9604badad02ef4632f62edfcbd59f06c43faf3e4b7f5",
-                  "fetch_kib": 54037.6, "fetch_scale": 2.0, "write_kib": 32896.0, "write_scale": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "fc07661c9ee7cf530757cf1572bf78c3c0317e0b8715a06605882e8f05e082e3",
+                  "fetch_kib": 54041.4, "fetch_scale": 2.0, "write_kib": 32896.0, "write_scale": 1.0}
 
 
 def measured_traffic():

@@ -90,10 +90,13 @@ typedef struct mla_shape {
 
 /* One scheduler partition (32 bytes, int32 fields).  end_req is inclusive,
  * end_block is exclusive and counts blocks of end_req; begin_split is the
- * global split index of the first piece; a partition with begin_req >= b is idle. */
+ * global split index of the first piece; a partition with begin_req >= b is idle.
+ * by_length is 1 in a plan made from valid lengths (mla_get_sched_meta_len):
+ * a request that the partition covers whole then spans
+ * ceil(topk_length[r] / split_granularity) blocks; 0 otherwise. */
 typedef struct mla_sched_part {
     int32_t begin_req, end_req, begin_block, end_block;
-    int32_t begin_split, first_splitted, last_splitted, reserved;
+    int32_t begin_split, first_splitted, last_splitted, by_length;
 } mla_sched_part;
 
 typedef struct mla_decode_args {
@@ -123,7 +126,11 @@ typedef struct mla_decode_args {
                                            walkthrough step 13)                            */
     const int32_t* topk_length;         /* NULL, or int32 [b] device: slots at positions
                                            >= topk_length[b] are empty (clamped to
-                                           [0, topk]); the plan still covers topk slots   */
+                                           [0, topk]).  A plan from mla_get_sched_meta or
+                                           the closed form still covers topk slots; one
+                                           from mla_get_sched_meta_len covers only the
+                                           valid ones and must be used with the same
+                                           lengths (its pieces follow them)               */
 
     const void* sched_meta;             /* from mla_get_sched_meta (same shape), or NULL   */
     const int32_t* num_splits;          /* [b + 1] split prefix from mla_get_sched_meta, or
@@ -162,6 +169,24 @@ int mla_get_sched_meta(const mla_shape* shape, void* sched_meta_dev,
 /* The same plan computed on the host into host buffers of the same sizes. */
 int mla_plan_sched_meta_host(const mla_shape* shape, void* sched_meta_host,
                              int32_t* num_splits_host);
+
+/* Tile scheduler with per-request valid lengths ("FlashMLA Sparse Decode
+ * 完整计算过程详解", step 3, where a request's block count follows its valid
+ * top-k length; "FlashMLA 与 DSA" section 4.3 for topk_length): request r costs
+ * ceil(min(max(topk_length_dev[r], 0), topk) / split_granularity) blocks plus
+ * fixed_overhead, so short requests take fewer partitions and tiles.
+ * topk_length_dev is int32 [b] device memory, 4-byte aligned, read by the
+ * scheduler kernel on `stream`; the decode and combine calls must pass the
+ * same array as mla_decode_args.topk_length.  One lane fills the plan
+ * sequentially.  Output buffers and errors as mla_get_sched_meta, plus
+ * MLA_ERR_INVALID_ARG for a NULL or misaligned topk_length_dev. */
+int mla_get_sched_meta_len(const mla_shape* shape, const int32_t* topk_length_dev,
+                           void* sched_meta_dev, int32_t* num_splits_dev, void* stream);
+
+/* The same length-aware plan computed on the host; topk_length_host is int32 [b]
+ * host memory. */
+int mla_plan_sched_meta_len_host(const mla_shape* shape, const int32_t* topk_length_host,
+                                 void* sched_meta_host, int32_t* num_splits_host);
 
 /* Sparse decode ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14):
  * gathers and dequantises the selected rows, runs the two bf16 contractions with

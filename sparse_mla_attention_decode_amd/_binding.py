@@ -25,7 +25,8 @@ MLA_KV_FP8_656 = 0
 MLA_KV_BF16_576 = 1
 
 EXPORTED = ("mla_sched_meta_size", "mla_workspace_size", "mla_resolve_shape",
-            "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_sparse_decode_fwd",
+            "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_get_sched_meta_len",
+            "mla_plan_sched_meta_len_host", "mla_sparse_decode_fwd",
             "mla_splitkv_combine", "mla_debug_gather_dequant", "mla_last_error", "mla_version")
 
 
@@ -79,6 +80,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_resolve_shape": [P(mla_shape)],
         "mla_get_sched_meta": [P(mla_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
         "mla_plan_sched_meta_host": [P(mla_shape), ctypes.c_void_p, ctypes.c_void_p],
+        "mla_get_sched_meta_len": [P(mla_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p],
+        "mla_plan_sched_meta_len_host": [P(mla_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
         "mla_sparse_decode_fwd": [P(mla_decode_args), ctypes.c_void_p],
         "mla_splitkv_combine": [P(mla_decode_args), ctypes.c_void_p],
         "mla_debug_gather_dequant": [P(mla_decode_args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
@@ -143,6 +147,17 @@ def mla_get_sched_meta(shape: mla_shape, meta_ptr: int, num_splits_ptr: int, str
     _check("mla_get_sched_meta", load_library().mla_get_sched_meta(ctypes.byref(shape), meta_ptr, num_splits_ptr, _stream(stream)))
 
 
+def mla_plan_sched_meta_len_host(shape: mla_shape, lengths_ptr: int, meta_ptr: int, num_splits_ptr: int) -> None:
+    _check("mla_plan_sched_meta_len_host",
+           load_library().mla_plan_sched_meta_len_host(ctypes.byref(shape), lengths_ptr, meta_ptr, num_splits_ptr))
+
+
+def mla_get_sched_meta_len(shape: mla_shape, lengths_ptr: int, meta_ptr: int, num_splits_ptr: int,
+                           stream=None) -> None:
+    _check("mla_get_sched_meta_len", load_library().mla_get_sched_meta_len(
+        ctypes.byref(shape), lengths_ptr, meta_ptr, num_splits_ptr, _stream(stream)))
+
+
 def mla_sparse_decode_fwd(args: mla_decode_args, stream=None) -> None:
     _check("mla_sparse_decode_fwd", load_library().mla_sparse_decode_fwd(ctypes.byref(args), _stream(stream)))
 
@@ -169,12 +184,17 @@ class DecodePlan:
     """Device buffers (sched meta, split prefix, workspace, outputs) for one shape,
     allocated with torch.  The plan can be reused for every call of that shape."""
 
-    def __init__(self, shape: mla_shape, device="cuda", closed_form: bool = False):
+    def __init__(self, shape: mla_shape, device="cuda", closed_form: bool = False, by_length: bool = False):
         """closed_form=True (fixed_overhead 0 only) passes a NULL plan: the
-        kernels evaluate the plan themselves and get_sched_meta does nothing."""
+        kernels evaluate the plan themselves and get_sched_meta does nothing.
+        by_length=True makes the plan from the topk_length given to run()
+        (mla_get_sched_meta_len), so requests cost their valid slots only."""
         import torch
         self.shape = mla_resolve_shape(shape)
         self.closed_form = closed_form
+        self.by_length = by_length
+        if closed_form and by_length:
+            raise MlaError("DecodePlan", MLA_ERR_INVALID_ARG, "a closed-form plan cannot follow lengths")
         if closed_form and self.shape.fixed_overhead != 0:
             raise MlaError("DecodePlan", MLA_ERR_INVALID_ARG, "closed_form needs fixed_overhead 0")
         meta_b, ns_b = mla_sched_meta_size(self.shape)
@@ -187,8 +207,15 @@ class DecodePlan:
         self.out = torch.empty((s.b, s.s_q, s.h_q, 512), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((s.b, s.h_q, s.s_q), dtype=torch.float32, device=device)
 
-    def get_sched_meta(self, stream=None):
-        if not self.closed_form:
+    def get_sched_meta(self, stream=None, topk_length=None):
+        if self.closed_form:
+            return
+        if self.by_length:
+            if topk_length is None:
+                raise MlaError("DecodePlan", MLA_ERR_INVALID_ARG, "a by_length plan needs topk_length")
+            mla_get_sched_meta_len(self.shape, topk_length.data_ptr(), self.sched_meta.data_ptr(),
+                                   self.num_splits.data_ptr(), stream)
+        else:
             mla_get_sched_meta(self.shape, self.sched_meta.data_ptr(), self.num_splits.data_ptr(), stream)
 
     def args(self, q, kv, indices, sm_scale: float = 0.0, out=None, lse=None, attn_sink=None,
@@ -227,7 +254,7 @@ class DecodePlan:
             attn_sink=None, topk_length=None):
         """sched (optional) -> decode -> combine, all on `stream`."""
         if with_sched:
-            self.get_sched_meta(stream)
+            self.get_sched_meta(stream, topk_length)
         a = self.args(q, kv, indices, sm_scale, attn_sink=attn_sink, topk_length=topk_length)
         mla_sparse_decode_fwd(a, stream)
         mla_splitkv_combine(a, stream)

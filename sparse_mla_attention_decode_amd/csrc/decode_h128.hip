@@ -313,7 +313,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     if (begin_req >= p.b) return;
     const int end_req = plan.end_req, begin_block = plan.begin_block, end_block = plan.end_block;
     const int begin_split = plan.begin_split;
-    const int nblocks = (p.topk + p.block - 1) / p.block;
 
     const uint32_t lds0 = lds_u32(lds);
     const int slice_off = L_RAW + wave * WAVE_RAW;            // this wave's slice in raw slot 0
@@ -321,7 +320,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 
     for (int req = begin_req; req <= end_req; ++req) {
         const int blk_lo = req == begin_req ? begin_block : 0;
-        const int blk_hi = req == end_req ? end_block : nblocks;
+        const int blk_hi = req == end_req ? end_block : whole_blocks(p, plan, req);
         const int k_lo = blk_lo * p.block;
         const int k_hi = min(blk_hi * p.block, p.topk);
         const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;

@@ -245,19 +245,31 @@ int mla_workspace_size(const mla_shape* shape, size_t* o_accum_bytes, size_t* ls
     return ok();
 }
 
-int mla_plan_sched_meta_host(const mla_shape* shape, void* sched_meta_host, int32_t* num_splits_host) {
+static int plan_host(const mla_shape* shape, const int32_t* lengths, void* sched_meta_host,
+                     int32_t* num_splits_host) {
     mla::ResolvedShape r;
     int st = resolve(shape, &r);
     if (st != MLA_OK) return st;
     if (!sched_meta_host || !num_splits_host)
         return fail(MLA_ERR_INVALID_ARG, "sched_meta_host and num_splits_host must be non-NULL");
-    mla::plan_schedule(r.b, r.topk, r.block, r.overhead, r.num_parts,
+    mla::plan_schedule(r.b, r.topk, r.block, r.overhead, r.num_parts, lengths,
                        static_cast<int32_t*>(sched_meta_host), num_splits_host,
                        [](int32_t* p, int32_t v) { *p = v; });
     return ok();
 }
 
-int mla_get_sched_meta(const mla_shape* shape, void* sched_meta_dev, int32_t* num_splits_dev, void* stream) {
+int mla_plan_sched_meta_host(const mla_shape* shape, void* sched_meta_host, int32_t* num_splits_host) {
+    return plan_host(shape, nullptr, sched_meta_host, num_splits_host);
+}
+
+int mla_plan_sched_meta_len_host(const mla_shape* shape, const int32_t* topk_length_host,
+                                 void* sched_meta_host, int32_t* num_splits_host) {
+    if (!topk_length_host) return fail(MLA_ERR_INVALID_ARG, "topk_length_host must be non-NULL");
+    return plan_host(shape, topk_length_host, sched_meta_host, num_splits_host);
+}
+
+static int plan_dev(const mla_shape* shape, const int32_t* lengths, void* sched_meta_dev,
+                    int32_t* num_splits_dev, void* stream) {
     mla::ResolvedShape r;
     int st = resolve(shape, &r);
     if (st != MLA_OK) return st;
@@ -265,9 +277,20 @@ int mla_get_sched_meta(const mla_shape* shape, void* sched_meta_dev, int32_t* nu
         return fail(MLA_ERR_INVALID_ARG, "sched_meta_dev and num_splits_dev must be non-NULL");
     if (!aligned(sched_meta_dev, 4) || !aligned(num_splits_dev, 4))
         return fail(MLA_ERR_INVALID_ARG, "sched buffers must be 4-byte aligned");
-    return hip_status(mla::launch_sched(r, static_cast<int32_t*>(sched_meta_dev), num_splits_dev,
+    return hip_status(mla::launch_sched(r, lengths, static_cast<int32_t*>(sched_meta_dev), num_splits_dev,
                                         static_cast<hipStream_t>(stream)),
                       "sched kernel launch");
+}
+
+int mla_get_sched_meta(const mla_shape* shape, void* sched_meta_dev, int32_t* num_splits_dev, void* stream) {
+    return plan_dev(shape, nullptr, sched_meta_dev, num_splits_dev, stream);
+}
+
+int mla_get_sched_meta_len(const mla_shape* shape, const int32_t* topk_length_dev, void* sched_meta_dev,
+                           int32_t* num_splits_dev, void* stream) {
+    if (!topk_length_dev || !aligned(topk_length_dev, 4))
+        return fail(MLA_ERR_INVALID_ARG, "topk_length_dev must be non-NULL and 4-byte aligned");
+    return plan_dev(shape, topk_length_dev, sched_meta_dev, num_splits_dev, stream);
 }
 
 int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream) {

@@ -68,10 +68,21 @@ struct DecodeParams {
 
 // One partition of the plan: requests begin_req..end_req (inclusive), blocks
 // [begin_block, end_block) of end_req, its first piece has split index
-// begin_split; begin_req >= b marks an idle partition.
+// begin_split; begin_req >= b marks an idle partition.  by_length: the plan
+// was made from the valid lengths, so a request covered whole spans
+// ceil(length / block) blocks instead of ceil(topk / block).
 struct PartPlan {
-    int begin_req, end_req, begin_block, end_block, begin_split;
+    int begin_req, end_req, begin_block, end_block, begin_split, by_length;
 };
+
+// Blocks of request `req` that a partition covering it whole processes.
+__device__ __forceinline__ int whole_blocks(const DecodeParams& p, const PartPlan& plan, int req) {
+    if (plan.by_length && p.topk_length != nullptr) {
+        const int len = min(max(p.topk_length[req], 0), p.topk);
+        return (len + p.block - 1) / p.block;
+    }
+    return (p.topk + p.block - 1) / p.block;
+}
 
 // Partition `part` of the plan, read from the scheduler's output or, with no
 // scheduler output, evaluated in closed form.  With zero per-request cost the
@@ -93,10 +104,12 @@ __device__ __forceinline__ PartPlan plan_part(const DecodeParams& p, int part) {
         r.begin_block = m[2];
         r.end_block = m[3];
         r.begin_split = m[4];
+        r.by_length = m[7];
         return r;
     }
     const uint32_t B = p.plan_nblk, P = p.plan_payload, T = p.plan_total, q = (uint32_t)part;
     const uint32_t s0 = q * P;
+    r.by_length = 0;
     if (s0 >= T) {
         r.begin_req = r.end_req = p.b;
         r.begin_block = r.end_block = r.begin_split = 0;
@@ -129,7 +142,8 @@ __device__ __forceinline__ int split_prefix(const DecodeParams& p, int r) {
 // l <= topk * 2^64 and every accumulator stays far inside fp32 range.
 constexpr float kRefGapLog2 = 64.0f;
 
-hipError_t launch_sched(const ResolvedShape& s, int32_t* meta, int32_t* prefix, hipStream_t st);
+hipError_t launch_sched(const ResolvedShape& s, const int32_t* lengths, int32_t* meta, int32_t* prefix,
+                        hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st);
 hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st);
 hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows,

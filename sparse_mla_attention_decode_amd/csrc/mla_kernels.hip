@@ -242,11 +242,13 @@ __global__ void __launch_bounds__(SCHED_FLAT_THREADS) sched_flat_kernel(int b, i
     }
 }
 
-// Sequential fill, one lane (used when the state table does not fit).
+// Sequential fill, one lane (used when the state table does not fit, and for
+// plans made from per-request valid lengths).
 __global__ void __launch_bounds__(64) sched_kernel(int b, int topk, int block, int overhead,
-                                                   int num_parts, int32_t* meta, int32_t* prefix) {
+                                                   int num_parts, const int32_t* lengths,
+                                                   int32_t* meta, int32_t* prefix) {
     if (threadIdx.x != 0) return;
-    plan_schedule(b, topk, block, overhead, num_parts, meta, prefix,
+    plan_schedule(b, topk, block, overhead, num_parts, lengths, meta, prefix,
                   [](int32_t* p, int32_t v) { *p = v; });
 }
 
@@ -420,14 +422,13 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
     if (begin_req >= p.b) return;
     const int end_req = plan.end_req, begin_block = plan.begin_block, end_block = plan.end_block;
     const int begin_split = plan.begin_split;
-    const int nblocks = (p.topk + p.block - 1) / p.block;
     const int qk_base = n * KROW + 16 * h;          // score operand: key n, dims 16j + 8h
     const int pv_base = pv_read_base(lane);
     if (threadIdx.x < 4) lds[L::FLAGS + threadIdx.x] = 0;   // ordered by the first barrier
 
     for (int req = begin_req; req <= end_req; ++req) {
         const int blk_lo = req == begin_req ? begin_block : 0;
-        const int blk_hi = req == end_req ? end_block : nblocks;
+        const int blk_hi = req == end_req ? end_block : whole_blocks(p, plan, req);
         const int k_lo = blk_lo * p.block;
         const int k_hi = min(blk_hi * p.block, p.topk);
         const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
@@ -738,9 +739,13 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
 // ----------------------------------------------------------------------------
 // launchers
 // ----------------------------------------------------------------------------
-hipError_t launch_sched(const ResolvedShape& s, int32_t* meta, int32_t* prefix, hipStream_t st) {
+hipError_t launch_sched(const ResolvedShape& s, const int32_t* lengths, int32_t* meta, int32_t* prefix,
+                        hipStream_t st) {
     const int B = (s.topk + s.block - 1) / s.block;
-    if (s.overhead == 0 && s.num_parts <= SCHED_FLAT_THREADS)
+    if (lengths != nullptr)
+        hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(64), 0, st, s.b, s.topk, s.block, s.overhead,
+                           s.num_parts, lengths, meta, prefix);
+    else if (s.overhead == 0 && s.num_parts <= SCHED_FLAT_THREADS)
         hipLaunchKernelGGL(sched_flat_kernel, dim3(1), dim3(SCHED_FLAT_THREADS), 0, st, s.b, s.topk,
                            s.block, s.num_parts, meta, prefix);
     else if (B <= SCHED_MAX_STATES && s.num_parts < (1 << SCHED_LOG))
@@ -748,7 +753,7 @@ hipError_t launch_sched(const ResolvedShape& s, int32_t* meta, int32_t* prefix, 
                            s.block, s.overhead, s.num_parts, meta, prefix);
     else
         hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(64), 0, st, s.b, s.topk, s.block, s.overhead,
-                           s.num_parts, meta, prefix);
+                           s.num_parts, (const int32_t*)nullptr, meta, prefix);
     return hipGetLastError();
 }
 

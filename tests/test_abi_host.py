@@ -143,6 +143,60 @@ def test_host_plan_matches_oracle(b, topk, parts, gran, ovh):
     assert [tuple(m[:7]) for m in meta.tolist()] == [tuple(w) for w in want]
 
 
+def _host_len_plan(s, lengths):
+    r = M.mla_resolve_shape(s)
+    lens = np.ascontiguousarray(lengths, dtype=np.int32)
+    meta = np.full((r.num_parts, 8), -7, np.int32)
+    ns = np.full(r.b + 1, -7, np.int32)
+    M.mla_plan_sched_meta_len_host(s, lens.ctypes.data, meta.ctypes.data, ns.ctypes.data)
+    return r, meta, ns
+
+
+@pytest.mark.parametrize("lengths,topk,parts,gran,ovh", [
+    ([2048, 0, 1000, 1, 5000, -3, 2047, 32], 2048, 64, 32, 5),     # clamped and empty requests
+    ([0, 0, 0], 256, 8, 32, 0),                                    # nothing to do at all
+    ([0, 0, 0], 256, 8, 32, 5),
+    ([100, 600, 33, 512], 512, 7, 64, 2),
+    (list(range(0, 2049, 97)), 2048, 256, 32, 0),
+    ([1] * 40, 2048, 256, 32, 5),                                   # more partitions than work
+])
+def test_host_length_plan_matches_oracle(lengths, topk, parts, gran, ovh):
+    """The length-aware plan is the oracle's greedy plan over the clamped
+    valid lengths (each request costs ceil(len / G) blocks), every record says
+    by_length = 1, and the split prefix matches."""
+    b = len(lengths)
+    s = shape(b=b, topk=topk, num_parts=parts, split_granularity=gran, fixed_overhead=ovh)
+    r, meta, ns = _host_len_plan(s, lengths)
+    valid = [min(max(x, 0), topk) for x in lengths]
+    want, prefix = O.sched_plan(valid, gran, ovh, parts)
+    assert ns.tolist() == prefix
+    assert [tuple(m[:7]) for m in meta.tolist()] == [tuple(w) for w in want]
+    assert np.all(meta[:, 7] == 1)
+    # the unchanged plan keeps by_length = 0
+    _, meta0, _ = _host_plan(s)
+    assert np.all(meta0[:, 7] == 0)
+
+
+def test_length_plan_equals_plain_plan_at_full_length():
+    s = shape(b=64, topk=2048, num_parts=256, split_granularity=32, fixed_overhead=5)
+    _, meta_len, ns_len = _host_len_plan(s, [2048] * 64)
+    _, meta, ns = _host_plan(s)
+    assert ns_len.tolist() == ns.tolist()
+    assert meta_len[:, :7].tolist() == meta[:, :7].tolist()
+
+
+def test_length_plan_rejects_null_lengths():
+    s = shape()
+    meta = np.zeros((66, 8), np.int32)
+    ns = np.zeros(3, np.int32)
+    with pytest.raises(M.MlaError) as e:
+        M.mla_plan_sched_meta_len_host(s, None, meta.ctypes.data, ns.ctypes.data)
+    assert e.value.code == M.MLA_ERR_INVALID_ARG
+    with pytest.raises(M.MlaError) as e:
+        M.mla_get_sched_meta_len(s, 0x1002, 0x2000, 0x3000, stream=0)     # misaligned lengths
+    assert e.value.code == M.MLA_ERR_INVALID_ARG
+
+
 def _closed_form_plan(b, topk, gran, parts):
     """The plan the kernels evaluate for a NULL plan (per-request cost 0):
     partition q takes blocks [q p, min((q + 1) p, T)) of the request-major
