@@ -213,6 +213,45 @@ const char* mla_last_error(void);
 /* Library version string. */
 const char* mla_version(void);
 
+/* Lightning indexer and top-k ("FlashMLA 与 DSA：内核、流水线和正确性边界",
+ * sections 4.1, 4.2, 5.2, 5.3, 5.5): the step upstream of the sparse decode
+ * that picks each request's topk key tokens.  All pointers are device memory
+ * owned by the caller. */
+typedef struct mla_indexer_args {
+    int32_t b;                  /* requests (one query token each), 0 .. 65535          */
+    int32_t n_heads;            /* indexer heads, 32 or 64                               */
+    int32_t max_pages;          /* page-table width; logical tokens < max_pages * 64    */
+    int32_t num_pages;          /* physical pages in kcache                              */
+    int32_t topk;               /* K >= 1 (2048 in DeepSeek-V3.2)                        */
+    const void* q;              /* e4m3 [b, n_heads, 128] contiguous, 16-byte aligned   */
+    const float* weights;       /* fp32 [b, n_heads]: head weights with the q scale and
+                                   1/sqrt(d) folded in (section 4.1)                     */
+    const void* kcache;         /* [num_pages, 8448] bytes: per page 64 x 128 e4m3 key
+                                   codes (token-major) then 64 fp32 scales (5.3)         */
+    const int32_t* page_table;  /* int32 [b, max_pages]: logical page -> physical page;
+                                   an entry outside [0, num_pages) makes its tokens score
+                                   -inf and emit id -1                                   */
+    const int32_t* seq_len;     /* int32 [b]: valid tokens, clamped to [0, max_pages*64] */
+    void* scores;               /* bf16 [b, max_pages * 64]: written by
+                                   mla_indexer_scores for t < seq_len of rows with
+                                   seq_len > topk, read by mla_indexer_topk              */
+    int32_t* indices;           /* int32 [b, topk] output of mla_indexer_topk            */
+} mla_indexer_args;
+
+/* Index scores (section 4.1, Eq. 1): scores[r][t] = bf16( scale_t *
+ * sum_j weights[r][j] * max(0, q[r][j] . codes_t) ), the FP8 products summed in
+ * fp32 on the matrix cores and the positive per-token scale applied after the
+ * head sum (section 5.3).  Rows with seq_len <= topk are skipped (section 5.2).
+ * MLA_ERR_INVALID_ARG / MLA_ERR_UNSUPPORTED for bad sizes or pointers. */
+int mla_indexer_scores(const mla_indexer_args* args, void* stream);
+
+/* Top-k (sections 4.2, 5.5): for each request the topk highest scores among its
+ * first seq_len tokens, written to indices[r] as physical token ids
+ * (page_table[r][t / 64] * 64 + t % 64), in no particular order; ties at the
+ * threshold keep an arbitrary subset.  seq_len <= topk emits tokens
+ * 0 .. seq_len - 1 then -1 (section 5.2).  Reads scores only. */
+int mla_indexer_topk(const mla_indexer_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

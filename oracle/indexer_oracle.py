@@ -63,12 +63,15 @@ def indexer_scores(q_codes: np.ndarray, weights: np.ndarray, kcache: np.ndarray,
     n_max = page_table.shape[1] * PAGE_TOKENS
     out = np.full((b, n_max), -np.inf)
     for r in range(b):
+        n = int(seq_len[r])
+        if n <= 0:
+            continue
         q = e4m3fn_value(q_codes[r])                          # [H, 128]
         w = np.asarray(weights[r], dtype=np.float64)
-        for t in range(int(seq_len[r])):
-            k = page_keys(kcache, int(page_table[r, t // PAGE_TOKENS]))[t % PAGE_TOKENS]
-            dots = q @ k                                      # one dot per head
-            out[r, t] = float(np.sum(w * np.maximum(dots, 0.0)))
+        pages = [page_keys(kcache, int(page_table[r, p])) for p in range((n + PAGE_TOKENS - 1) // PAGE_TOKENS)]
+        k = np.concatenate(pages)[:n]                         # [n, 128] dequantised keys
+        dots = k @ q.T                                        # [n, H]: q_j . k_t
+        out[r, :n] = np.maximum(dots, 0.0) @ w                # sum_j w_j ReLU(.)
     return out
 
 

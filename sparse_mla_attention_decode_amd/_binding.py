@@ -26,7 +26,7 @@ MLA_KV_BF16_576 = 1
 
 EXPORTED = ("mla_sched_meta_size", "mla_workspace_size", "mla_resolve_shape",
             "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_get_sched_meta_len",
-            "mla_plan_sched_meta_len_host", "mla_sparse_decode_fwd",
+            "mla_plan_sched_meta_len_host", "mla_sparse_decode_fwd", "mla_indexer_scores", "mla_indexer_topk",
             "mla_splitkv_combine", "mla_debug_gather_dequant", "mla_last_error", "mla_version")
 
 
@@ -37,6 +37,14 @@ class mla_shape(ctypes.Structure):
                 ("num_kv_tokens", ctypes.c_int64), ("kv_format", ctypes.c_int32),
                 ("num_parts", ctypes.c_int32), ("split_granularity", ctypes.c_int32),
                 ("fixed_overhead", ctypes.c_int32)]
+
+
+class mla_indexer_args(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("weights", ctypes.c_void_p), ("kcache", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("scores", ctypes.c_void_p),
+                ("indices", ctypes.c_void_p)]
 
 
 class mla_decode_args(ctypes.Structure):
@@ -84,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    ctypes.c_void_p],
         "mla_plan_sched_meta_len_host": [P(mla_shape), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
         "mla_sparse_decode_fwd": [P(mla_decode_args), ctypes.c_void_p],
+        "mla_indexer_scores": [P(mla_indexer_args), ctypes.c_void_p],
+        "mla_indexer_topk": [P(mla_indexer_args), ctypes.c_void_p],
         "mla_splitkv_combine": [P(mla_decode_args), ctypes.c_void_p],
         "mla_debug_gather_dequant": [P(mla_decode_args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
     }
@@ -172,6 +182,41 @@ def mla_debug_gather_dequant(args: mla_decode_args, k_rows_ptr: int, v_rows_ptr:
 
 
 # ----------------------------------------------------------------------------- torch plumbing
+def mla_indexer_scores(args: mla_indexer_args, stream=None) -> None:
+    _check("mla_indexer_scores", load_library().mla_indexer_scores(ctypes.byref(args), _stream(stream)))
+
+
+def mla_indexer_topk(args: mla_indexer_args, stream=None) -> None:
+    _check("mla_indexer_topk", load_library().mla_indexer_topk(ctypes.byref(args), _stream(stream)))
+
+
+def indexer_args(q, weights, kcache, page_table, seq_len, topk: int, scores, indices) -> mla_indexer_args:
+    """Marshal contiguous device tensors: q uint8 [b, H, 128], weights fp32 [b, H],
+    kcache uint8 [num_pages, 8448], page_table / seq_len int32, scores bf16
+    [b, max_pages * 64], indices int32 [b, topk]."""
+    a = mla_indexer_args()
+    a.b, a.n_heads = q.shape[0], q.shape[1]
+    a.max_pages, a.num_pages, a.topk = page_table.shape[1], kcache.shape[0], topk
+    a.q, a.weights, a.kcache = q.data_ptr(), weights.data_ptr(), kcache.data_ptr()
+    a.page_table, a.seq_len = page_table.data_ptr(), seq_len.data_ptr()
+    a.scores, a.indices = scores.data_ptr(), indices.data_ptr()
+    return a
+
+
+def indexer_select(q, weights, kcache, page_table, seq_len, topk: int, scores=None, indices=None, stream=None):
+    """scores -> top-k on `stream`; returns (indices int32 [b, topk], scores)."""
+    import torch
+    b, max_pages = page_table.shape
+    if scores is None:
+        scores = torch.empty((b, max_pages * 64), dtype=torch.bfloat16, device=q.device)
+    if indices is None:
+        indices = torch.empty((b, topk), dtype=torch.int32, device=q.device)
+    a = indexer_args(q, weights, kcache, page_table, seq_len, topk, scores, indices)
+    mla_indexer_scores(a, stream)
+    mla_indexer_topk(a, stream)
+    return indices, scores
+
+
 def make_shape(b, s_q, h_q, topk, num_kv_tokens, kv_format=MLA_KV_FP8_656, page_block_size=64,
                num_parts=0, split_granularity=0, fixed_overhead=-1) -> mla_shape:
     return mla_shape(b=b, s_q=s_q, h_q=h_q, h_kv=1, d_qk=576, d_v=512, topk=topk,

@@ -11,6 +11,7 @@
 
 #include "mla.h"
 #include "mla_internal.h"
+#include "indexer_internal.h"
 #include "sched_plan.h"
 
 namespace {
@@ -327,3 +328,48 @@ const char* mla_last_error(void) { return g_err; }
 const char* mla_version(void) { return "libmla 0.1 gfx950"; }
 
 }  // extern "C"
+
+static int indexer_params(const mla_indexer_args* a, mla::IndexerParams* p, bool need_scores_in) {
+    if (!a) return fail(MLA_ERR_INVALID_ARG, "args is NULL");
+    if (a->b < 0 || a->b > 65535) return fail(MLA_ERR_INVALID_ARG, "b must be in [0, 65535] (got %d)", a->b);
+    if (a->n_heads != 32 && a->n_heads != 64)
+        return fail(MLA_ERR_UNSUPPORTED, "n_heads must be 32 or 64 (got %d)", a->n_heads);
+    if (a->topk < 1) return fail(MLA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", a->topk);
+    if (a->max_pages < 1 || (int64_t)a->max_pages * 64 > (1ll << 30))
+        return fail(MLA_ERR_INVALID_ARG, "max_pages must be in [1, 2^24] (got %d)", a->max_pages);
+    if (a->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %d)", a->num_pages);
+    if (!a->page_table || !a->seq_len || !a->scores || !aligned(a->page_table, 4) || !aligned(a->seq_len, 4) ||
+        !aligned(a->scores, 2))
+        return fail(MLA_ERR_INVALID_ARG, "page_table, seq_len (4-byte) and scores (2-byte) must be aligned, non-NULL");
+    if (need_scores_in) {
+        if (!a->q || !a->weights || !a->kcache || !aligned(a->q, 16) || !aligned(a->kcache, 16) ||
+            !aligned(a->weights, 4))
+            return fail(MLA_ERR_INVALID_ARG, "q and kcache must be 16-byte aligned, weights 4-byte, all non-NULL");
+    } else if (!a->indices || !aligned(a->indices, 4)) {
+        return fail(MLA_ERR_INVALID_ARG, "indices must be non-NULL and 4-byte aligned");
+    }
+    p->b = a->b; p->n_heads = a->n_heads; p->max_pages = a->max_pages; p->num_pages = a->num_pages;
+    p->topk = a->topk;
+    p->q = static_cast<const uint8_t*>(a->q);
+    p->weights = a->weights;
+    p->kcache = static_cast<const uint8_t*>(a->kcache);
+    p->page_table = a->page_table;
+    p->seq_len = a->seq_len;
+    p->scores = static_cast<uint16_t*>(a->scores);
+    p->indices = a->indices;
+    return MLA_OK;
+}
+
+int mla_indexer_scores(const mla_indexer_args* args, void* stream) {
+    mla::IndexerParams p;
+    int st = indexer_params(args, &p, true);
+    if (st != MLA_OK) return st;
+    return hip_status(mla::launch_indexer_scores(p, static_cast<hipStream_t>(stream)), "indexer score launch");
+}
+
+int mla_indexer_topk(const mla_indexer_args* args, void* stream) {
+    mla::IndexerParams p;
+    int st = indexer_params(args, &p, false);
+    if (st != MLA_OK) return st;
+    return hip_status(mla::launch_indexer_topk(p, static_cast<hipStream_t>(stream)), "indexer top-k launch");
+}

@@ -262,3 +262,24 @@ def make_config(cfg: int, sort_slots: bool = False, **over) -> Workload:
                             tokens_per_seq=131072, recent_frac=0.5, recent_window=4096,
                             sort_slots=sort_slots, **over)
     raise ValueError(cfg)
+
+
+def indexer_inputs(seed: int, b: int, n_heads: int, seq_lens, max_pages: int, spare_pages: int = 3):
+    """Seeded inputs of the lightning indexer ("FlashMLA 与 DSA" sections 4.1,
+    5.3): e4m3 q codes [b, H, 128] (no NaN codes), fp32 head weights [b, H]
+    (N(0, 1) / sqrt(H), the folded softmax scale), a paged key cache
+    [num_pages, 8448] (64 x 128 e4m3 codes then 64 fp32 scales in
+    [2^-9, 2^-6]) whose physical pages are dealt to requests in a shuffled
+    order, and int32 seq_len.  numpy arrays; no arithmetic of the method."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    num_pages = b * max_pages + spare_pages
+    q = rng.integers(0, 256, (b, n_heads, 128), dtype=np.uint8)
+    q = np.where((q & 0x7F) == 0x7F, q ^ 1, q)
+    w = (rng.standard_normal((b, n_heads)) / np.sqrt(n_heads)).astype(np.float32)
+    codes = rng.integers(0, 256, (num_pages, 64 * 128), dtype=np.uint8)
+    codes = np.where((codes & 0x7F) == 0x7F, codes ^ 1, codes)
+    scales = rng.uniform(2.0 ** -9, 2.0 ** -6, (num_pages, 64)).astype("<f4")
+    kcache = np.concatenate([codes, scales.view(np.uint8)], axis=1)
+    page_table = rng.permutation(num_pages)[: b * max_pages].reshape(b, max_pages).astype(np.int32)
+    return q, w, np.ascontiguousarray(kcache), page_table, lens
