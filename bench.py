@@ -47,6 +47,24 @@ DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
 DECODE_TRAFFIC = {"sources_sha256": "fc07661c9ee7cf530757cf1572bf78c3c0317e0b8715a06605882e8f05e082e3",
                   "fetch_kib": 54041.4, "fetch_scale": 2.0, "write_kib": 32896.0, "write_scale": 1.0}
 
+INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
+                          "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",
+                          "sparse_mla_attention_decode_amd/csrc/device_common.h")
+INDEXER_TRAFFIC = {"sources_sha256": "f1622b8d576bb008ceb9c24bd9b658c628cfa68172039feb4f13368f2d92ca1b",
+                   "fetch_kib": 137577.2, "fetch_scale": 2.0, "write_kib": 4632.1, "write_scale": 1.0}
+
+
+def traffic_of(sources, t):
+    """HBM bytes per launch from stored counters, if they match the sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != t["sources_sha256"]:
+        return None
+    return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
+
 
 def measured_traffic():
     """HBM bytes per decode launch if the counters match the current kernel sources."""
@@ -101,6 +119,79 @@ def cpu_baseline(w, budget_s: float):
                       f"{dt:.1f} s, numpy float64 with {threads} BLAS threads"}
 
 
+def bench_indexer(args, torch, np, M, W, dev):
+    """Lightning indexer + top-k ("FlashMLA 与 DSA" sections 4.1, 5.3, 5.5) for 64
+    requests of one query token at a 32768-token context (512 pages of 64), 64
+    indexer heads, K = 2048: one step = the score kernel + the top-k kernel."""
+    b, heads, pages, K = 64, 64, 512, 2048
+    lens = np.full(b, pages * 64, dtype=np.int32)
+    q, w, kc, pt, lens = W.indexer_inputs(21, b, heads, lens, max_pages=pages)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q_d, w_d, kc_d, pt_d, len_d = d(q), d(w), d(kc), d(pt), d(lens)
+    scores = torch.empty((b, pages * 64), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((b, K), dtype=torch.int32, device=dev)
+    a = M.indexer_args(q_d, w_d, kc_d, pt_d, len_d, K, scores, idx)
+    st = torch.cuda.current_stream()
+    sp = st.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(st)
+        M.mla_indexer_scores(a, sp)
+        if ev is not None:
+            ev[1].record(st)
+        M.mla_indexer_topk(a, sp)
+        if ev is not None:
+            ev[2].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    topk_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    n_tok = int(lens.sum())
+    # algorithmic bytes: every key row (128 codes + 4-byte scale), q, w, the page
+    # table and the bf16 scores written once; top-k reads the scores once and
+    # writes K ids per request
+    score_bytes = n_tok * (132 + 2) + b * heads * (128 + 4) + b * pages * 4
+    topk_bytes = n_tok * 2 + b * K * 4
+    achieved = score_bytes / (score_ms * 1e-3) / 1e9
+    res = {"metric": "indexer query-tokens/s at b=64, 32K context, K=2048 (scores + top-k)",
+           "value": b / dt, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+           "config": {"workload": "indexer_b64_h64_ctx32k_k2048", "b": b, "indexer_heads": heads,
+                      "context": pages * 64, "topk": K, "key_cache": "fp8 128 B + fp32 scale per token, page 64"},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": achieved / PEAK_HBM_GBS,
+                        "traffic": traffic_of(INDEXER_KERNEL_SOURCES, INDEXER_TRAFFIC), "kernel": "indexer_score_kernel",
+                        "kernel_ms": score_ms, "algorithmic_bytes_per_launch": score_bytes},
+           "topk_kernel": {"kernel": "indexer_topk_kernel", "kernel_ms": topk_ms,
+                           "algorithmic_bytes_per_launch": topk_bytes,
+                           "achieved_GBs": topk_bytes / (topk_ms * 1e-3) / 1e9}}
+    if not args.no_cpu_baseline:
+        from oracle import indexer_oracle as X
+        rows, t1 = 0, time.perf_counter()
+        while rows < b and time.perf_counter() - t1 < args.cpu_budget:
+            sc = X.indexer_scores(q[rows:rows + 1], w[rows:rows + 1], kc, pt[rows:rows + 1], lens[rows:rows + 1])
+            X.topk_select(sc[0], int(lens[rows]), K, pt[rows])
+            rows += 1
+        cpu_s = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": rows / cpu_s, "unit": "query-tokens/s",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count())), "kind": "oracle",
+                               "sample": f"{rows} of {b} requests of the same workload, {cpu_s:.1f} s, numpy float64"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +210,9 @@ def main():
                          "auto: closed when fixed_overhead is 0")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("decode", "indexer"), default="decode",
+                    help="decode: the sparse MLA decode step (default); indexer: the lightning "
+                         "indexer scores + top-k that select its tokens")
     ap.add_argument("--graph", action="store_true",
                     help="replay a captured HIP graph of each layer's step instead of launching "
                          "its kernels one by one")
@@ -139,6 +233,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.workload == "indexer":
+        return bench_indexer(args, torch, np, M, W, dev)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)

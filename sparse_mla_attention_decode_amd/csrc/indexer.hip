@@ -11,7 +11,8 @@ namespace {
 constexpr int IX_PAGE = 64;                 // tokens per key-cache page
 constexpr int IX_DIM = 128;                 // e4m3 dims per key
 constexpr int IX_PAGE_BYTES = IX_PAGE * IX_DIM + IX_PAGE * 4;   // codes, then fp32 scales
-constexpr int IX_WAVES = 4;                 // one page per wave
+constexpr int IX_WAVES = 4;
+constexpr int IX_PAGES_PER_WAVE = 4;        // q and the weights stay in registers across them
 constexpr int TOPK_THREADS = 1024;
 
 __device__ __forceinline__ int clamp_len(const IndexerParams& p, int r) {
@@ -23,7 +24,8 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {          // nearest,
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Scores of one request's pages (Eq. 1).  Each wave takes one page as two
+// Scores of one request's pages (Eq. 1).  Each wave takes up to four pages
+// (the work-group's waves read adjacent pages at each step), each as two
 // groups of 32 tokens.  The head-by-token products run on the FP8 matrix
 // cores with q as the A operand (rows = heads) and the keys as B (columns =
 // tokens), so every lane ends with one token's 16 head dot products per head
@@ -38,9 +40,8 @@ __global__ void __launch_bounds__(IX_WAVES * 64) indexer_score_kernel(IndexerPar
     const int len = clamp_len(p, r);
     if (len <= p.topk) return;                                   // passthrough row
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int page_l = blockIdx.x * IX_WAVES + wave;
-    const int t0 = page_l * IX_PAGE;
-    if (t0 >= len) return;
+    const int first_page = blockIdx.x * IX_WAVES * IX_PAGES_PER_WAVE + wave;
+    if (first_page * IX_PAGE >= len) return;
     const int hf = lane >> 5, col = lane & 31;
     const int nt = p.n_heads >> 5;                               // 1 or 2 head tiles
 
@@ -60,10 +61,14 @@ __global__ void __launch_bounds__(IX_WAVES * 64) indexer_score_kernel(IndexerPar
             wv[tile][i] = tile < nt ? wr[ht * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)] : 0.0f;
     }
 
+    uint16_t* out = p.scores + (size_t)r * p.max_pages * IX_PAGE;
+    for (int step = 0; step < IX_PAGES_PER_WAVE; ++step) {
+    const int page_l = first_page + step * IX_WAVES;
+    const int t0 = page_l * IX_PAGE;
+    if (t0 >= len) break;                                        // page_l < max_pages below
     const int pg = p.page_table[(size_t)r * p.max_pages + page_l];
     const bool ok = pg >= 0 && pg < p.num_pages;
     const uint8_t* page = p.kcache + (size_t)(ok ? pg : 0) * IX_PAGE_BYTES;
-    uint16_t* out = p.scores + (size_t)r * p.max_pages * IX_PAGE;
 
     for (int g = 0; g < 2; ++g) {
         const int tok = g * 32 + col;
@@ -86,6 +91,7 @@ __global__ void __launch_bounds__(IX_WAVES * 64) indexer_score_kernel(IndexerPar
         const float scale = ((const float*)(page + IX_PAGE * IX_DIM))[tok];
         const int t = t0 + tok;
         if (hf == 0 && t < len) out[t] = ok ? to_bf16_bits(sum * scale) : (uint16_t)0xFF80u;   // -inf
+    }
     }
 }
 
@@ -175,7 +181,8 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
 
 hipError_t launch_indexer_scores(const IndexerParams& p, hipStream_t st) {
     if (p.b == 0) return hipSuccess;
-    const dim3 grid((p.max_pages + IX_WAVES - 1) / IX_WAVES, p.b);
+    const int per_wg = IX_WAVES * IX_PAGES_PER_WAVE;
+    const dim3 grid((p.max_pages + per_wg - 1) / per_wg, p.b);
     hipLaunchKernelGGL(indexer_score_kernel, grid, dim3(IX_WAVES * 64), 0, st, p);
     return hipGetLastError();
 }
