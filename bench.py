@@ -183,7 +183,7 @@ def bench_indexer(args, torch, np, M, W, dev):
         rows, t1 = 0, time.perf_counter()
         while rows < b and time.perf_counter() - t1 < args.cpu_budget:
             sc = X.indexer_scores(q[rows:rows + 1], w[rows:rows + 1], kc, pt[rows:rows + 1], lens[rows:rows + 1])
-            X.topk_select(sc[0], int(lens[rows]), K, pt[rows])
+            X.topk_select(sc[0], int(lens[rows]), K, pt[rows], kc.shape[0])
             rows += 1
         cpu_s = time.perf_counter() - t1
         res["cpu_baseline"] = {"value": rows / cpu_s, "unit": "query-tokens/s",
