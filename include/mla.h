@@ -29,9 +29,13 @@
  * into blocks of split_granularity slots; a greedy left-to-right plan assigns
  * (request, block range) pieces to num_parts partitions with a fixed per-request
  * cost of fixed_overhead blocks.  A request whose blocks land in more than one
- * partition is "split": each piece writes a normalised fp32 partial O and a
- * base-2 lse (step 14) and mla_splitkv_combine merges them (step 16).  A request
- * that lands in exactly one partition is written to out/lse directly.
+ * partition is "split": each piece writes its normalised partial O/l and a
+ * base-2 lse (step 14) into the workspace and mla_splitkv_combine merges them
+ * (step 16).  A request that lands in exactly one partition is written to
+ * out/lse directly.  Partial O precision: the FP8 cache path stores it as bf16
+ * (narrower than the walkthrough's fp32 o_accum; a partial is bounded by
+ * max |V| and its rounding stays inside the output tolerance), the bf16 cache
+ * path as fp32.  The workspace is sized for fp32 either way.
  *
  * Conventions:
  *   - Every pointer in mla_decode_args is device memory owned by the caller; the
@@ -116,7 +120,7 @@ typedef struct mla_decode_args {
     int64_t idx_stride_b, idx_stride_s; /* in elements                                      */
 
     void* out;                          /* bf16 [b, s_q, h_q, 512], last dim contiguous    */
-    int64_t out_stride_b, out_stride_s, out_stride_h;    /* in elements, multiples of 4   */
+    int64_t out_stride_b, out_stride_s, out_stride_h;    /* in elements, multiples of 8   */
     float* lse;                         /* fp32 [b, h_q, s_q] contiguous, natural log      */
 
     const float* attn_sink;             /* NULL, or fp32 [h_q] device: one sink logit per
@@ -130,7 +134,11 @@ typedef struct mla_decode_args {
                                            the closed form still covers topk slots; one
                                            from mla_get_sched_meta_len covers only the
                                            valid ones and must be used with the same
-                                           lengths (its pieces follow them)               */
+                                           lengths (its pieces follow them).  Such a plan
+                                           passed with topk_length NULL is a contract
+                                           error the host cannot see (the plan is device
+                                           memory): the decode then writes nothing and the
+                                           combine writes NaN to every out and lse element */
 
     const void* sched_meta;             /* from mla_get_sched_meta (same shape), or NULL   */
     const int32_t* num_splits;          /* [b + 1] split prefix from mla_get_sched_meta, or
@@ -160,9 +168,12 @@ int mla_workspace_size(const mla_shape* shape, size_t* o_accum_bytes, size_t* ls
 int mla_resolve_shape(mla_shape* shape);
 
 /* Tile scheduler ("FlashMLA Sparse Decode 完整计算过程详解", step 3): computes
- * the partition plan on the device (one wave) into sched_meta_dev
- * (num_parts mla_sched_part records) and num_splits_dev (b + 1 int32 prefix).
- * It depends on the shape only, so one plan serves every layer of a step. */
+ * the partition plan on the device into sched_meta_dev (num_parts
+ * mla_sched_part records) and num_splits_dev (b + 1 int32 prefix), in one
+ * launch of one work-group (1024 threads evaluating the greedy fill in
+ * parallel; one lane filling it in order when the per-request state does not
+ * fit).  It depends on the shape only, so one plan serves every layer of a
+ * step. */
 int mla_get_sched_meta(const mla_shape* shape, void* sched_meta_dev,
                        int32_t* num_splits_dev, void* stream);
 

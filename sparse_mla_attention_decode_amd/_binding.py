@@ -190,12 +190,36 @@ def mla_indexer_topk(args: mla_indexer_args, stream=None) -> None:
     _check("mla_indexer_topk", load_library().mla_indexer_topk(ctypes.byref(args), _stream(stream)))
 
 
+def _require(ok: bool, fn: str, msg: str) -> None:
+    if not ok:
+        raise MlaError(fn, MLA_ERR_INVALID_ARG, msg)
+
+
 def indexer_args(q, weights, kcache, page_table, seq_len, topk: int, scores, indices) -> mla_indexer_args:
     """Marshal contiguous device tensors: q uint8 [b, H, 128], weights fp32 [b, H],
-    kcache uint8 [num_pages, 8448], page_table / seq_len int32, scores bf16
-    [b, max_pages * 64], indices int32 [b, topk]."""
+    kcache uint8 [num_pages, 8448], page_table int32 [b, max_pages], seq_len
+    int32 [b], scores bf16 [b, max_pages * 64], indices int32 [b, topk].  The
+    shapes and dtypes are checked here: the C ABI takes raw pointers."""
+    import torch
+    fn = "indexer_args"
+    _require(q.dtype == torch.uint8 and q.dim() == 3 and q.shape[2] == 128, fn, "q must be uint8 [b, H, 128]")
+    b, heads = q.shape[0], q.shape[1]
+    _require(weights.dtype == torch.float32 and tuple(weights.shape) == (b, heads), fn,
+             "weights must be float32 [b, H]")
+    _require(kcache.dtype == torch.uint8 and kcache.dim() == 2 and kcache.shape[1] == 8448, fn,
+             "kcache must be uint8 [num_pages, 8448]")
+    _require(page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.shape[0] == b, fn,
+             "page_table must be int32 [b, max_pages]")
+    _require(seq_len.dtype == torch.int32 and tuple(seq_len.shape) == (b,), fn, "seq_len must be int32 [b]")
+    _require(scores.dtype == torch.bfloat16 and tuple(scores.shape) == (b, page_table.shape[1] * 64), fn,
+             "scores must be bfloat16 [b, max_pages * 64]")
+    _require(indices.dtype == torch.int32 and tuple(indices.shape) == (b, topk), fn,
+             "indices must be int32 [b, topk]")
+    for name, t in (("q", q), ("weights", weights), ("kcache", kcache), ("page_table", page_table),
+                    ("seq_len", seq_len), ("scores", scores), ("indices", indices)):
+        _require(t.is_contiguous(), fn, f"{name} must be contiguous")
     a = mla_indexer_args()
-    a.b, a.n_heads = q.shape[0], q.shape[1]
+    a.b, a.n_heads = b, heads
     a.max_pages, a.num_pages, a.topk = page_table.shape[1], kcache.shape[0], topk
     a.q, a.weights, a.kcache = q.data_ptr(), weights.data_ptr(), kcache.data_ptr()
     a.page_table, a.seq_len = page_table.data_ptr(), seq_len.data_ptr()
@@ -267,19 +291,18 @@ class DecodePlan:
              topk_length=None) -> mla_decode_args:
         """attn_sink: fp32 [h_q] device tensor or None; topk_length: int32 [b] device
         tensor or None (both contiguous)."""
+        if self.by_length and topk_length is None:
+            raise MlaError("DecodePlan", MLA_ERR_INVALID_ARG,
+                           "a by_length plan needs the topk_length it was made from")
         out = self.out if out is None else out
         lse = self.lse if lse is None else lse
-        if self.shape.kv_format == MLA_KV_FP8_656:
-            kv_stride = kv.stride(0) * kv.element_size()
-        else:
-            kv_stride = kv.stride(0) * kv.element_size()
         a = mla_decode_args()
         a.shape = self.shape
         a.sm_scale = sm_scale
         a.q = q.data_ptr()
         a.q_stride_b, a.q_stride_s, a.q_stride_h = q.stride(0), q.stride(1), q.stride(2)
         a.kv = kv.data_ptr()
-        a.kv_stride_block = kv_stride
+        a.kv_stride_block = kv.stride(0) * kv.element_size()     # bytes per page / bf16 row
         a.indices = indices.data_ptr()
         a.idx_stride_b, a.idx_stride_s = indices.stride(0), indices.stride(1)
         a.out = out.data_ptr()

@@ -313,6 +313,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     if (begin_req >= p.b) return;
     const int end_req = plan.end_req, begin_block = plan.begin_block, end_block = plan.end_block;
     const int begin_split = plan.begin_split;
+    if (plan.by_length && p.topk_length == nullptr) return;   // contract error: see lengths_missing
 
     const uint32_t lds0 = lds_u32(lds);
     const int slice_off = L_RAW + wave * WAVE_RAW;            // this wave's slice in raw slot 0
@@ -772,7 +773,8 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     const int req = qi / p.s_q, sq = qi % p.s_q;
     const int first = split_prefix(p, req);
     const int ns = split_prefix(p, req + 1) - first;
-    if (ns <= 1) return;
+    const bool poison = lengths_missing(p);                  // contract error: NaN everywhere
+    if (ns <= 1 && !poison) return;
     const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
     const int w = piece >> 4, j = (piece >> 2) & 3, hb = piece & 3;
     if (32 * hb >= p.h_q) return;                            // 64 heads: blocks 0 and 1 only
@@ -782,7 +784,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     const int64_t kofs = (int64_t)w * 32 * 64 + (2 * (4 * j + hb)) * 64 + lane;
     float M = -INFINITY, W = 0.f;
     f32x16 acc = {};
-    for (int s0 = 0; s0 < ns; s0 += 4) {
+    for (int s0 = 0; s0 < (poison ? 0 : ns); s0 += 4) {
         float lv[4];
         u32x4 raw[4][2];
 #pragma unroll
@@ -819,7 +821,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     const float den = p.attn_sink != nullptr && W > 0.f
                           ? W + __builtin_amdgcn_exp2f(p.attn_sink[head] * 1.4426950408889634f - M)
                           : W;
-    const float inv = W > 0.f ? 1.0f / den : 0.f;
+    const float inv = poison ? __builtin_nanf("") : W > 0.f ? 1.0f / den : 0.f;
     uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh +
                      128 * w + 32 * j + 4 * h;
 #pragma unroll
@@ -828,7 +830,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
                                         pack_bf16(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv)};
     if (w == 0 && j == 0 && h == 0)
         p.lse[((int64_t)req * p.h_q + head) * p.s_q + sq] =
-            M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
+            poison ? __builtin_nanf("") : M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
 }
 
 bool g_lds_decode = false, g_lds_decode_flat = false, g_lds_gather = false;

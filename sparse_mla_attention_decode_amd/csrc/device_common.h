@@ -68,9 +68,6 @@ __device__ __forceinline__ void mfma_pv(f32x16& o, const bf16x8& a, const bf16x8
 // The hazard recognizer does not look inside inline asm.  These fences wait
 // out the MFMA result latency before VALU reads an accumulator, and the VALU
 // write -> MFMA operand read latency before freshly computed P is consumed.
-__device__ __forceinline__ void mfma_result_fence(f32x16& s) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s));
-}
 __device__ __forceinline__ void mfma_result_fence2(f32x16& s, f32x16& t) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(s), "+v"(t));
 }

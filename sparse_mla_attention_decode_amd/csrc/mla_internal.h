@@ -76,8 +76,9 @@ struct PartPlan {
 };
 
 // Blocks of request `req` that a partition covering it whole processes.
+// (A by_length plan without lengths never gets here: see lengths_missing.)
 __device__ __forceinline__ int whole_blocks(const DecodeParams& p, const PartPlan& plan, int req) {
-    if (plan.by_length && p.topk_length != nullptr) {
+    if (plan.by_length) {
         const int len = min(max(p.topk_length[req], 0), p.topk);
         return (len + p.block - 1) / p.block;
     }
@@ -124,6 +125,15 @@ __device__ __forceinline__ PartPlan plan_part(const DecodeParams& p, int part) {
     r.end_block = (int)(e - re * B) + 1;
     r.begin_split = q == 0 ? 0 : (int)(q + fdiv(s0 - 1, p.div_nblk) - fdiv(q - 1, p.div_gb));
     return r;
+}
+
+// A plan made from valid lengths (by_length records) passed without the
+// lengths it was made from.  The host cannot see this (the plan is device
+// memory), so it is a contract error found on the device: the decode does
+// nothing and the combine writes NaN to every output (split and unsplit
+// requests alike), instead of silently mixing the two kinds of plan.
+__device__ __forceinline__ bool lengths_missing(const DecodeParams& p) {
+    return p.sched_meta != nullptr && p.topk_length == nullptr && p.sched_meta[7] != 0;
 }
 
 // Split index of the first piece of request r (the number of pieces at r = b).

@@ -1,16 +1,18 @@
-// gfx950 kernels for sparse MLA decode: scheduler, decode, split-KV combine
-// and a gather/dequant test hook.
+// gfx950 kernels for sparse MLA attention: the tile scheduler, the decode and
+// split-KV combine over the flat bf16 cache (sparse prefill), and a
+// gather test hook.  (The FP8 656-byte cache has its own kernels in
+// decode_h128.hip.)
 //
 // Decode work-group = NW waves of 64 lanes; wave w owns query heads
 // [32w, 32w+32).  Each wave keeps Q for its heads in VGPRs (the B operand of
 // the score contraction) and the transposed output accumulator O^T [512 x 32]
 // in AGPRs.  The work-group walks its topk slots in tiles of 32 keys:
 //
-//   1. gather: the tile's token rows (656 B FP8 or 1152 B bf16) are copied
-//      HBM -> LDS by direct-to-LDS loads (16 B per lane, no registers), one
-//      tile ahead of the compute; empty slots are skipped;
-//   2. stage: rows are dequantised to bf16 (code * power-of-two scale, exact)
-//      into K rows [32 keys][576] in LDS; empty slots become zero rows;
+//   1. gather: the tile's 1152-byte bf16 token rows are copied HBM -> LDS by
+//      direct-to-LDS loads (16 B per lane, no registers), one tile ahead of
+//      the compute; empty slots are skipped;
+//   2. stage: rows are copied into padded K rows [32 keys][576] in LDS;
+//      empty slots become zero rows;
 //   3. S^T[key][head] = K Q^T: 36 MFMA 32x32x16 bf16 per wave;
 //   4. softmax in base 2 on the accumulator, masked by slot validity; every
 //      lane holds 16 keys of one head so the row max needs one exchange;
@@ -41,11 +43,10 @@ namespace mla {
 constexpr int KROW = 1168;                 // LDS bytes per staged bf16 K row (1152 + 16 pad)
 constexpr int KB_BYTES = TILE * KROW;      // 37376
 
-// Per-format constants of the raw token row.
+// Per-format constants of the raw token row.  The generic kernels serve the
+// bf16 cache (sparse prefill); the FP8 656-byte cache has its own kernels
+// (decode_h128.hip).
 template <int FMT> struct RowFmt;
-template <> struct RowFmt<MLA_KV_FP8_656> {
-    static constexpr int ROWB = 656, ROPE_OFF = 528;
-};
 template <> struct RowFmt<MLA_KV_BF16_576> {
     static constexpr int ROWB = 1152, ROPE_OFF = 1024;
 };
@@ -58,7 +59,7 @@ template <int FMT, int NW> struct Lds {
     static constexpr int CHUNKS = TILE * CPR;                          // per tile
     static constexpr int NI = ((CHUNKS + 63) / 64 + NW - 1) / NW;      // copies per wave per tile
     static constexpr int RAW_BYTES = NI * NW * 1024;
-    static constexpr int NRAW = (FMT == MLA_KV_FP8_656 && NW == 4) ? 3 : 2;
+    static constexpr int NRAW = 2;
     static constexpr int RAW = 0;
     static constexpr int KB = RAW + NRAW * RAW_BYTES;
     static constexpr int MASK = KB + 2 * KB_BYTES;                      // 4 slots
@@ -259,11 +260,6 @@ __global__ void __launch_bounds__(64) sched_kernel(int b, int topk, int block, i
 template <int FMT>
 __device__ __forceinline__ const uint8_t* row_ptr(const DecodeParams& p, int t) {
     if (t < 0 || (int64_t)t >= p.n_tok) return nullptr;
-    if (FMT == MLA_KV_FP8_656) {
-        const int64_t blk = t / p.page_block_size;
-        const int64_t off = t - blk * p.page_block_size;
-        return p.kv + blk * p.kv_block_stride + off * 656;
-    }
     return p.kv + (int64_t)t * p.kv_block_stride;
 }
 
@@ -313,15 +309,14 @@ __device__ __forceinline__ void gather_tile(const DecodeParams& p, int t, bool i
         dma16(src[i], __builtin_amdgcn_readfirstlane(lds_base + 1024u * NW * i));
 }
 
-// Stage: raw rows -> bf16 K rows (dequantised NoPE, copied RoPE), branch
-// free; empty slots become zero rows.  Split into a read half and a
-// convert+write half so the decode loop can spread it between MFMAs.
+// Stage: raw rows -> K rows (NoPE and RoPE copied into the padded row
+// layout), branch free; empty slots become zero rows.  Split into a read half
+// and a write half so the decode loop can spread it between MFMAs.
 template <int FMT, int NW> struct StageRegs {
     static constexpr int NT = NW * 64;
-    static constexpr int NOPE_UNITS = FMT == MLA_KV_FP8_656 ? 32 * 32 / NT : 32 * 64 / NT;
+    static constexpr int NOPE_UNITS = 32 * 64 / NT;
     static constexpr int ROPE_UNITS = (32 * 8 + NT - 1) / NT;
     u32x4 nope[NOPE_UNITS];
-    float scale[FMT == MLA_KV_FP8_656 ? NOPE_UNITS : 1];
     u32x4 rope[ROPE_UNITS];
 };
 
@@ -333,14 +328,8 @@ __device__ __forceinline__ void stage_read(const LDS_AS uint8_t* lds, int raw_of
 #pragma unroll
     for (int i = i0; i < min(i1, SR::NOPE_UNITS); ++i) {
         const int u = i * SR::NT + threadIdx.x;
-        if (FMT == MLA_KV_FP8_656) {
-            const int row = u >> 5, c = u & 31;
-            R.nope[i] = lds_read16(lds, raw_off + row * ROWB + 16 * c);
-            R.scale[i] = *(const LDS_AS float*)(lds + raw_off + row * ROWB + 512 + 4 * (c >> 3));
-        } else {
-            const int row = u >> 6, c = u & 63;
-            R.nope[i] = lds_read16(lds, raw_off + row * ROWB + 16 * c);
-        }
+        const int row = u >> 6, c = u & 63;
+        R.nope[i] = lds_read16(lds, raw_off + row * ROWB + 16 * c);
     }
     if (i1 <= SR::NOPE_UNITS) return;
 #pragma unroll
@@ -350,7 +339,7 @@ __device__ __forceinline__ void stage_read(const LDS_AS uint8_t* lds, int raw_of
     }
 }
 
-// convert + write NoPE unit i (or the RoPE units when i == NOPE_UNITS)
+// write NoPE unit i (or the RoPE units when i == NOPE_UNITS)
 template <int FMT, int NW>
 __device__ __forceinline__ void stage_write(LDS_AS uint8_t* lds, int kb_off, uint32_t valid,
                                             const StageRegs<FMT, NW>& R, int i) {
@@ -358,21 +347,8 @@ __device__ __forceinline__ void stage_write(LDS_AS uint8_t* lds, int kb_off, uin
     const u32x4 zero = {0, 0, 0, 0};
     if (i < SR::NOPE_UNITS) {
         const int u = i * SR::NT + threadIdx.x;
-        if (FMT == MLA_KV_FP8_656) {
-            const int row = u >> 5, c = u & 31;
-            const bool ok = (valid >> row) & 1u;
-            const u32x4 raw = R.nope[i];
-            const float sc = R.scale[i];
-            u32x4 lo = {dequant2<false>(raw[0], sc), dequant2<true>(raw[0], sc),
-                        dequant2<false>(raw[1], sc), dequant2<true>(raw[1], sc)};
-            u32x4 hi = {dequant2<false>(raw[2], sc), dequant2<true>(raw[2], sc),
-                        dequant2<false>(raw[3], sc), dequant2<true>(raw[3], sc)};
-            lds_write16(lds, kb_off + row * KROW + 32 * c, ok ? lo : zero);
-            lds_write16(lds, kb_off + row * KROW + 32 * c + 16, ok ? hi : zero);
-        } else {
-            const int row = u >> 6, c = u & 63;
-            lds_write16(lds, kb_off + row * KROW + 16 * c, ((valid >> row) & 1u) ? R.nope[i] : zero);
-        }
+        const int row = u >> 6, c = u & 63;
+        lds_write16(lds, kb_off + row * KROW + 16 * c, ((valid >> row) & 1u) ? R.nope[i] : zero);
     } else {
 #pragma unroll
         for (int r = 0; r < SR::ROPE_UNITS; ++r) {
@@ -422,6 +398,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
     if (begin_req >= p.b) return;
     const int end_req = plan.end_req, begin_block = plan.begin_block, end_block = plan.end_block;
     const int begin_split = plan.begin_split;
+    if (plan.by_length && p.topk_length == nullptr) return;   // contract error: see lengths_missing
     const int qk_base = n * KROW + 16 * h;          // score operand: key n, dims 16j + 8h
     const int pv_base = pv_read_base(lane);
     if (threadIdx.x < 4) lds[L::FLAGS + threadIdx.x] = 0;   // ordered by the first barrier
@@ -496,7 +473,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
                 constexpr int NSTAGE = StageRegs<FMT, NW>::NOPE_UNITS + 1;   // units incl. RoPE
                 constexpr int SPAN = 36 / NSTAGE > 1 ? 36 / NSTAGE : 1;        // MFMAs per unit
                 stage_read<FMT, NW>(lds, raw_next, R, 0, 1);
-                f32x16 S;
+                // two alternating accumulator chains: the score MFMAs are inline
+                // asm (register classes pinned), which the compiler's hazard
+                // checks do not see into, so no MFMA may take the result of the
+                // one issued right before it
+                f32x16 Sa, Sb;
                 {
                     constexpr int AHEAD = 2;
                     bf16x8 a[AHEAD];
@@ -508,8 +489,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
                         const bf16x8 cur = a[j % AHEAD];
                         if (j + AHEAD < 36)
                             a[j % AHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, kb_cur + qk_base + 32 * (j + AHEAD)));
-                        if (j == 0) mfma_qk_first(S, cur, qb[j]);
-                        else mfma_qk(S, cur, qb[j]);
+                        if (j == 0) mfma_qk_first(Sa, cur, qb[j]);
+                        else if (j == 1) mfma_qk_first(Sb, cur, qb[j]);
+                        else if (j & 1) mfma_qk(Sb, cur, qb[j]);
+                        else mfma_qk(Sa, cur, qb[j]);
                         // staging unit u is read at MFMA SPAN*u - SPAN/2 and written at SPAN*u + SPAN-1
                         if (j % SPAN == SPAN / 2 && j / SPAN + 1 < NSTAGE)
                             stage_read<FMT, NW>(lds, raw_next, R, j / SPAN + 1, j / SPAN + 2);
@@ -522,7 +505,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
                         stage_write<FMT, NW>(lds, kb_next, vmask_next, R, i);
                     }
                 }
-                mfma_result_fence(S);
+                mfma_result_fence2(Sa, Sb);
+                f32x16 S = Sa + Sb;
 
                 // ---- masked softmax in base 2 against the reference max
                 float mx = -INFINITY;
@@ -700,15 +684,21 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
     if (head >= p.h_q) return;
     const int first = split_prefix(p, req);
     const int ns = split_prefix(p, req + 1) - first;
-    if (ns <= 1) return;
+    const bool poison = lengths_missing(p);                 // contract error: NaN everywhere
+    if (ns <= 1 && !poison) return;
     auto lse_at = [&](int j) {
         return p.lse_accum[((int64_t)(first + j) * p.s_q + sq) * p.h_q + head];
     };
+    uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh;
+    float* lse_out = p.lse + ((int64_t)req * p.h_q + head) * p.s_q + sq;
+    if (poison) {
+        *(u32x4*)(orow + 8 * lane) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+        if (lane == 0) *lse_out = __builtin_nanf("");
+        return;
+    }
     float mx = -INFINITY;
     for (int j = lane; j < ns; j += 64) mx = fmaxf(mx, lse_at(j));
     mx = wave_max(mx);
-    uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh;
-    float* lse_out = p.lse + ((int64_t)req * p.h_q + head) * p.s_q + sq;
     if (mx == -INFINITY) {
         *(u32x4*)(orow + 8 * lane) = u32x4{0, 0, 0, 0};
         if (lane == 0) *lse_out = INFINITY;
@@ -797,9 +787,9 @@ static hipError_t launch_gather_t(const DecodeParams& p, uint16_t* k_rows, uint1
 
 hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows, uint16_t* v_rows,
                          hipStream_t st) {
-    if (kv_format == MLA_KV_FP8_656 && p.h_q == 128) return launch_gather_fp8_h128(p, k_rows, v_rows, st);
-    return kv_format == MLA_KV_FP8_656 ? launch_gather_t<MLA_KV_FP8_656>(p, k_rows, v_rows, st)
-                                       : launch_gather_t<MLA_KV_BF16_576>(p, k_rows, v_rows, st);
+    // the FP8 decode kernel serves 64 and 128 heads; its gather does not depend on h_q
+    if (kv_format == MLA_KV_FP8_656) return launch_gather_fp8_h128(p, k_rows, v_rows, st);
+    return launch_gather_t<MLA_KV_BF16_576>(p, k_rows, v_rows, st);
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t st) {

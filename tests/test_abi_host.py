@@ -270,3 +270,92 @@ def test_round_up_reciprocal_division_is_exact():
         for n in ns:
             if n >= 0:
                 assert (((n * m) >> 32) + n) % (1 << 32) >> s == n // d, (n, d)
+
+
+# ----------------------------------------------------------------------------- indexer C ABI
+def test_indexer_args_layout_matches_header():
+    """mla_indexer_args: five int32 then seven pointers (q at byte 24 after
+    the padding to pointer alignment); read from the header's declaration."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct mla_indexer_args \{(.*?)\} mla_indexer_args;", text, flags=re.S).group(1)
+    fields = re.findall(r"(\w+\*?)\s+(\w+);", re.sub(r"\bconst\s+", "", body))
+    names = [n for _, n in fields]
+    assert names == [f for f, _ in M.mla_indexer_args._fields_]
+    assert M.mla_indexer_args.q.offset == 24 and ctypes.sizeof(M.mla_indexer_args) == 24 + 7 * 8
+
+
+def _ix_args(**over):
+    a = M.mla_indexer_args()
+    a.b, a.n_heads, a.max_pages, a.num_pages, a.topk = 4, 64, 16, 70, 256
+    a.q, a.weights, a.kcache = 0x10000, 0x20000, 0x30000
+    a.page_table, a.seq_len, a.scores, a.indices = 0x40000, 0x50000, 0x60000, 0x70000
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code,both", [
+    (dict(b=-1), M.MLA_ERR_INVALID_ARG, True), (dict(b=65536), M.MLA_ERR_INVALID_ARG, True),
+    (dict(n_heads=48), M.MLA_ERR_UNSUPPORTED, True), (dict(n_heads=128), M.MLA_ERR_UNSUPPORTED, True),
+    (dict(topk=0), M.MLA_ERR_INVALID_ARG, True), (dict(max_pages=0), M.MLA_ERR_INVALID_ARG, True),
+    (dict(max_pages=(1 << 24) + 1), M.MLA_ERR_INVALID_ARG, True), (dict(num_pages=0), M.MLA_ERR_INVALID_ARG, True),
+    (dict(page_table=None), M.MLA_ERR_INVALID_ARG, True), (dict(page_table=0x40002), M.MLA_ERR_INVALID_ARG, True),
+    (dict(seq_len=None), M.MLA_ERR_INVALID_ARG, True), (dict(seq_len=0x50001), M.MLA_ERR_INVALID_ARG, True),
+    (dict(scores=None), M.MLA_ERR_INVALID_ARG, True), (dict(scores=0x60001), M.MLA_ERR_INVALID_ARG, True),
+    (dict(q=None), M.MLA_ERR_INVALID_ARG, False), (dict(q=0x10008), M.MLA_ERR_INVALID_ARG, False),
+    (dict(weights=None), M.MLA_ERR_INVALID_ARG, False), (dict(weights=0x20002), M.MLA_ERR_INVALID_ARG, False),
+    (dict(kcache=None), M.MLA_ERR_INVALID_ARG, False), (dict(kcache=0x30004), M.MLA_ERR_INVALID_ARG, False),
+    (dict(indices=None), M.MLA_ERR_INVALID_ARG, "topk"), (dict(indices=0x70002), M.MLA_ERR_INVALID_ARG, "topk"),
+])
+def test_indexer_args_validated_before_launch(over, code, both):
+    """Every error of mla_indexer_scores / mla_indexer_topk is returned before
+    a launch (the pointers are never dereferenced: no GPU here).  `both`:
+    the check is shared; False: scores only; "topk": top-k only."""
+    a = _ix_args(**over)
+    fns = {True: (M.mla_indexer_scores, M.mla_indexer_topk), False: (M.mla_indexer_scores,),
+           "topk": (M.mla_indexer_topk,)}[both]
+    for fn in fns:
+        with pytest.raises(M.MlaError) as e:
+            fn(a, stream=0)
+        assert e.value.code == code, (fn.__name__, over)
+        assert M.mla_last_error() != ""
+
+
+def test_indexer_args_binding_checks_shapes_and_dtypes():
+    """The binding marshals raw pointers, so it checks what the C ABI cannot:
+    dtypes, shapes and contiguity."""
+    import torch
+    b, H, mp, K = 2, 64, 4, 32
+    ok = dict(q=torch.zeros((b, H, 128), dtype=torch.uint8), weights=torch.zeros((b, H)),
+              kcache=torch.zeros((9, 8448), dtype=torch.uint8), page_table=torch.zeros((b, mp), dtype=torch.int32),
+              seq_len=torch.zeros(b, dtype=torch.int32), topk=K,
+              scores=torch.zeros((b, mp * 64), dtype=torch.bfloat16), indices=torch.zeros((b, K), dtype=torch.int32))
+    a = M.indexer_args(**ok)
+    assert (a.b, a.n_heads, a.max_pages, a.num_pages, a.topk) == (b, H, mp, 9, K)
+    bad = [dict(q=torch.zeros((b, H, 64), dtype=torch.uint8)), dict(q=torch.zeros((b, H, 128))),
+           dict(weights=torch.zeros((b, H), dtype=torch.float64)), dict(weights=torch.zeros((b, H + 1))),
+           dict(kcache=torch.zeros((9, 8192), dtype=torch.uint8)),
+           dict(page_table=torch.zeros((b, mp), dtype=torch.int64)),
+           dict(seq_len=torch.zeros(b, dtype=torch.int64)), dict(seq_len=torch.zeros(b + 1, dtype=torch.int32)),
+           dict(scores=torch.zeros((b, mp * 64), dtype=torch.float16)),
+           dict(indices=torch.zeros((b, K + 1), dtype=torch.int32)),
+           dict(page_table=torch.zeros((mp, b), dtype=torch.int32).t())]
+    for over in bad:
+        with pytest.raises(M.MlaError):
+            M.indexer_args(**{**ok, **over})
+
+
+def test_by_length_plan_needs_its_lengths():
+    """A plan made from valid lengths must be given them at decode time: the
+    binding refuses to marshal it without (the kernels write NaN if a caller
+    of the C ABI does it anyway)."""
+    import torch
+    plan = M.DecodePlan(shape(num_parts=8, fixed_overhead=0), device="cpu", by_length=True)
+    q = torch.zeros((2, 1, 128, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((8, 64, 1, 656), dtype=torch.uint8)
+    idx = torch.zeros((2, 1, 128), dtype=torch.int32)
+    with pytest.raises(M.MlaError) as e:
+        plan.args(q, kv, idx)
+    assert e.value.code == M.MLA_ERR_INVALID_ARG
+    a = plan.args(q, kv, idx, topk_length=torch.full((2,), 100, dtype=torch.int32))
+    assert a.topk_length != 0

@@ -34,33 +34,40 @@ def run(q, w, kc, pt, lens, topk):
 
 def score_bound(q, w, kc, pt, lens):
     """Per token: scale * sum_j |w_j| sum_d |q_jd k_td|, the magnitude that the
-    kernel's sums round against."""
+    kernel's sums round against (0 for tokens of pages outside the cache)."""
     qa = np.abs(e4m3fn_value(q))
     out = np.zeros((q.shape[0], pt.shape[1] * 64))
     for r in range(q.shape[0]):
-        n = int(min(max(lens[r], 0), pt.shape[1] * 64))
+        n = X.clamp_len(lens[r], pt.shape[1])
         if n == 0:
             continue
-        keys = np.concatenate([np.abs(X.page_keys(kc, int(p))) for p in pt[r, : (n + 63) // 64]])[:n]
+        keys = np.concatenate([np.abs(np.nan_to_num(X.page_keys(kc, int(p))))
+                               for p in pt[r, : (n + 63) // 64]])[:n]
         out[r, :n] = (keys @ qa[r].T) @ np.abs(w[r].astype(np.float64))
     return out
 
 
 def check(q, w, kc, pt, lens, topk, rows=None, tag=""):
+    """Kernel scores and top-k of the listed rows against the oracle, which is
+    given the same raw page table and lengths: -inf scores (pages outside the
+    cache) must match exactly, finite ones within the tolerance above."""
     got_idx, got_sc = run(q, w, kc, pt, lens, topk)
     rows = range(q.shape[0]) if rows is None else rows
     sub = list(rows)
     ref = X.indexer_scores(q[sub], w[sub], kc, pt[sub], lens[sub])
     bound = score_bound(q[sub], w[sub], kc, pt[sub], lens[sub])
+    num_pages = kc.shape[0]
     for i, r in enumerate(sub):
-        n = int(min(max(lens[r], 0), pt.shape[1] * 64))
+        n = X.clamp_len(lens[r], pt.shape[1])
         if n > topk:                                       # scored rows only (passthrough skips)
             g, e = got_sc[r, :n], ref[i, :n]
-            err = np.abs(g - e)
-            tol = 2.0 ** -7 * np.abs(e) + 2.0 ** -14 * bound[i, :n]
+            inf = np.isneginf(e)
+            assert np.array_equal(np.isneginf(g), inf), f"{tag} row {r}: -inf pattern differs"
+            err = np.abs(g[~inf] - e[~inf])
+            tol = 2.0 ** -7 * np.abs(e[~inf]) + 2.0 ** -14 * bound[i, :n][~inf]
             bad = np.nonzero(err > tol)[0]
-            assert bad.size == 0, f"{tag} row {r}: {bad.size} scores off, first t={bad[0]} got {g[bad[0]]} want {e[bad[0]]}"
-        msg = X.check_topk(got_idx[r], got_sc[r], n, topk, pt[r])
+            assert bad.size == 0, f"{tag} row {r}: {bad.size} scores off, first got {g[~inf][bad[0]]} want {e[~inf][bad[0]]}"
+        msg = X.check_topk(got_idx[r], got_sc[r], lens[r], topk, pt[r], num_pages)
         assert msg is None, f"{tag} row {r}: {msg}"
     return got_idx, got_sc
 
@@ -86,22 +93,22 @@ def test_indexer_small_k_and_ties():
 
 
 def test_indexer_invalid_pages_and_clamped_lengths():
-    """A page-table entry outside the cache scores -inf (never chosen unless
-    needed) and seq_len beyond the table clamps."""
-    q, w, kc, pt, lens = W.indexer_inputs(13, 2, 64, [900, 10_000], max_pages=16)
+    """A page-table entry outside the cache scores -inf and emits -1, a
+    seq_len beyond the table clamps: the oracle takes the raw table and the
+    raw lengths and decides both.  Rows: an invalid page in a scored row with
+    more finite tokens than K; one with fewer (the -inf tokens fill K with
+    -1); an over-long length; a passthrough row (seq_len <= K) holding an
+    invalid page; a negative length."""
+    q, w, kc, pt, lens = W.indexer_inputs(13, 5, 64, [900, 300, 10_000, 200, -7], max_pages=16)
     pt[0, 3] = -1
-    got_idx, got_sc = run(q, w, kc, pt, lens, 256)
-    assert np.all(np.isneginf(got_sc[0, 192:256]))
-    assert np.all(got_idx[0] >= 0)                            # 836 valid tokens > 256
-    ok = pt.copy()
-    ok[0, 3] = sorted(set(range(kc.shape[0])) - set(pt.ravel().tolist()))[0]   # a page no request maps
-    ref = X.indexer_scores(q, w, kc, ok, np.array([900, 1024]))
-    bound = score_bound(q, w, kc, ok, np.array([900, 1024]))
-    for r, n in ((0, 900), (1, 1024)):
-        keep = np.isfinite(got_sc[r, :n])
-        err = np.abs(got_sc[r, :n] - ref[r, :n])[keep]
-        assert np.all(err <= 2.0 ** -7 * np.abs(ref[r, :n][keep]) + 2.0 ** -14 * bound[r, :n][keep])
-        assert X.check_topk(got_idx[r], got_sc[r], n, 256, pt[r] if r else ok[r]) is None
+    pt[1, 1] = kc.shape[0]                                    # one past the last page
+    pt[1, 3] = -1000
+    pt[3, 2] = -1
+    got_idx, _ = check(q, w, kc, pt, lens, 256, tag="invalid")
+    assert np.all(got_idx[0] >= 0)                            # 836 finite tokens > 256
+    assert np.sum(got_idx[1] == -1) == 256 - (300 - 128)      # 172 finite of 300
+    assert np.all(got_idx[3, 128:192] == -1) and np.all(got_idx[3, 192:200] >= 0)
+    assert np.all(got_idx[4] == -1)
 
 
 def test_indexer_benchmark_shape():
@@ -121,5 +128,5 @@ def test_indexer_benchmark_shape():
         tol = 2.0 ** -7 * np.abs(ref[i, :n]) + 2.0 ** -14 * bound[i, :n]
         assert np.all(np.abs(got_sc[r, :n] - ref[i, :n]) <= tol), r
     for r in range(64):
-        msg = X.check_topk(got_idx[r], got_sc[r], int(lens[r]), 2048, pt[r])
+        msg = X.check_topk(got_idx[r], got_sc[r], int(lens[r]), 2048, pt[r], kc.shape[0])
         assert msg is None, f"row {r}: {msg}"

@@ -338,12 +338,11 @@ def test_cfg1_production_all_queries(cfg1):
 def test_cfg1_closed_form_plan(cfg1):
     """The benchmarked launch (NULL plan, 32-slot blocks, zero per-request
     cost, 256 partitions): equal to the scheduler's plan bit for bit, and
-    sampled queries against the oracle."""
+    every query against the oracle."""
     w = cfg1
     out, lse, _ = _closed_vs_sched(w, "cfg1", num_parts=256, split_granularity=32)
-    qs = [(0, 0), (31, 0), (63, 0)]
-    ref_out, ref_lse = oracle(w, qs)
-    assert_parity(out, lse, ref_out, ref_lse, qs, "cfg1 closed")
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), "cfg1 closed")
 
 
 def test_cfg1_fine_split(cfg1):
@@ -355,19 +354,22 @@ def test_cfg1_fine_split(cfg1):
 
 
 def test_cfg2_half_heads_short_sequences():
+    """64 heads, 128 requests, 13 of them with 1500 valid slots then -1:
+    every query against the oracle."""
     w = W.make_config(2)
     out, lse, plan = run_gpu(w)
-    short = w.meta["short_seqs"]
-    qs = sorted(set([(s, 0) for s in short[:6]] + [(0, 0), (1, 0), (64, 0), (127, 0)]))
-    ref_out, ref_lse = oracle(w, qs)
-    assert_parity(out, lse, ref_out, ref_lse, qs, "cfg2")
-    assert len(short) == 13
+    assert len(w.meta["short_seqs"]) == 13
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), "cfg2")
 
 
 def test_cfg3_sparse_prefill_bf16():
+    """4096 query tokens: 264 of them against the oracle -- every 16th token
+    (one per 16-column stretch of the launch grid) plus both ends."""
     w = W.make_config(3)
     out, lse, plan = run_gpu(w)
-    qs = [(0, t) for t in (0, 1, 2, 1000, 2047, 3000, 4094, 4095)]
+    qs = sorted(set([(0, t) for t in range(0, 4096, 16)] + [(0, t) for t in (1, 2, 2047, 2048, 4094, 4095)]))
+    assert len(qs) >= 256
     ref_out, ref_lse = oracle(w, qs)
     assert_parity(out, lse, ref_out, ref_lse, qs, "cfg3")
 

@@ -181,3 +181,29 @@ def test_length_plan_benchmark_shape(ovh):
     qs = [(0, 0), (1, 0), (2, 0), (3, 0), (40, 0), (63, 0)]
     ref_out, ref_lse = oracle_with(w, None, lens, qs)
     assert_parity(out, lse, ref_out, ref_lse, qs, f"length plan cfg1 ovh={ovh}")
+
+
+@pytest.mark.parametrize("kind,parts", [("fp8", 1), ("fp8", 7), ("bf16", 1), ("bf16", 4)])
+def test_length_plan_without_lengths_is_nan(kind, parts):
+    """A plan made from valid lengths, passed through the C ABI without the
+    lengths: a contract error the host cannot see (the plan is device
+    memory).  Every output -- unsplit ones from the decode, split ones from
+    the combine -- must be NaN, never a silently wrong number."""
+    _need_gpu()
+    if kind == "fp8":
+        w = W.paged_decode("nolen", 95, b=3, s_q=2, h_q=128, topk=256, tokens_per_seq=512, P=64)
+    else:
+        w = W.sparse_prefill("nolen_bf", 96, s_q=5, h_q=128, topk=90, s_kv=160, prior=100)
+    shape = M.make_shape(w.b, w.s_q, w.h_q, w.topk, w.num_kv_tokens, w.kv_format, w.page_block_size,
+                         num_parts=parts, split_granularity=32)
+    plan = M.DecodePlan(shape, by_length=True)
+    lens = torch.full((w.b,), w.topk // 2, dtype=torch.int32, device="cuda")
+    plan.get_sched_meta(topk_length=lens)
+    a = plan.args(w.q_device(), w.kv_device(), w.indices_device(), w.sm_scale, topk_length=lens)
+    a.topk_length = None                                  # the caller's mistake
+    plan.out.zero_()
+    plan.lse.zero_()
+    M.mla_sparse_decode_fwd(a)
+    M.mla_splitkv_combine(a)
+    torch.cuda.synchronize()
+    assert torch.isnan(plan.out.float()).all() and torch.isnan(plan.lse).all()
