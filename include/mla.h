@@ -218,6 +218,21 @@ int mla_splitkv_combine(const mla_decode_args* args, void* stream);
 int mla_debug_gather_dequant(const mla_decode_args* args, void* k_rows, void* v_rows,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * decode step -- the tile plan when fixed_overhead > 0 (else the closed form),
+ * mla_sparse_decode_fwd and mla_splitkv_combine -- in one call that allocates
+ * nothing.  args->sched_meta, num_splits, o_accum and lse_accum must be NULL
+ * (MLA_ERR_INVALID_ARG otherwise); the plan and the split partials live in one
+ * 64 MiB device array of the library, one per GPU, held until the process
+ * ends.  A shape whose split workspace does not fit ((b + num_parts) * s_q
+ * splits of 128 KB plus h_q * 4 B each for the FP8 cache; h_q * 2 KB plus
+ * h_q * 4 B for the bf16 cache) is rejected with MLA_ERR_WORKSPACE before
+ * anything runs.  Every call on a GPU uses that GPU's array: calls that
+ * overlap on one GPU (different streams or threads) race; calls in one
+ * stream are ordered.  Outputs and errors otherwise as the calls above. */
+int mla_sparse_decode_noalloc(const mla_decode_args* args, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* mla_last_error(void);
 

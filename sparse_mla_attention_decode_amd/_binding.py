@@ -27,7 +27,8 @@ MLA_KV_BF16_576 = 1
 EXPORTED = ("mla_sched_meta_size", "mla_workspace_size", "mla_resolve_shape",
             "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_get_sched_meta_len",
             "mla_plan_sched_meta_len_host", "mla_sparse_decode_fwd", "mla_indexer_scores", "mla_indexer_topk",
-            "mla_splitkv_combine", "mla_debug_gather_dequant", "mla_last_error", "mla_version")
+            "mla_splitkv_combine", "mla_debug_gather_dequant", "mla_sparse_decode_noalloc",
+            "mla_last_error", "mla_version")
 
 
 class mla_shape(ctypes.Structure):
@@ -95,6 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_indexer_scores": [P(mla_indexer_args), ctypes.c_void_p],
         "mla_indexer_topk": [P(mla_indexer_args), ctypes.c_void_p],
         "mla_splitkv_combine": [P(mla_decode_args), ctypes.c_void_p],
+        "mla_sparse_decode_noalloc": [P(mla_decode_args), ctypes.c_void_p],
         "mla_debug_gather_dequant": [P(mla_decode_args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
     }
     for name, argtypes in sig.items():
@@ -174,6 +176,10 @@ def mla_sparse_decode_fwd(args: mla_decode_args, stream=None) -> None:
 
 def mla_splitkv_combine(args: mla_decode_args, stream=None) -> None:
     _check("mla_splitkv_combine", load_library().mla_splitkv_combine(ctypes.byref(args), _stream(stream)))
+
+
+def mla_sparse_decode_noalloc(args: mla_decode_args, stream=None) -> None:
+    _check("mla_sparse_decode_noalloc", load_library().mla_sparse_decode_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def mla_debug_gather_dequant(args: mla_decode_args, k_rows_ptr: int, v_rows_ptr: int, stream=None) -> None:

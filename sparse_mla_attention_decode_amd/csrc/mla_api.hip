@@ -101,7 +101,11 @@ void workspace_bytes(const mla::ResolvedShape& r, size_t* o, size_t* l) {
     if (l) *l = rows * sizeof(float);
 }
 
-int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::DecodeParams* p) {
+// Validate `a` and fill the kernel parameters.  With caller_buffers false (the
+// no-allocation entry point) the plan and workspace pointers must be NULL:
+// the library's own array supplies them afterwards.
+int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::DecodeParams* p,
+                      bool caller_buffers = true) {
     if (!a) return fail(MLA_ERR_INVALID_ARG, "args is NULL");
     int st = resolve(&a->shape, rs);
     if (st != MLA_OK) return st;
@@ -109,9 +113,12 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     if (!a->q || !a->kv || !a->indices || !a->out || !a->lse)
         return fail(MLA_ERR_INVALID_ARG, "q, kv, indices, out and lse must be non-NULL");
     const bool inline_plan = !a->sched_meta && !a->num_splits;
+    if (!caller_buffers && (!inline_plan || a->o_accum || a->lse_accum))
+        return fail(MLA_ERR_INVALID_ARG,
+                    "sched_meta, num_splits, o_accum and lse_accum must be NULL: the library's array holds them");
     if (!inline_plan && (!a->sched_meta || !a->num_splits))
         return fail(MLA_ERR_INVALID_ARG, "sched_meta and num_splits must both be set (mla_get_sched_meta) or both NULL");
-    if (inline_plan && r.overhead != 0)
+    if (caller_buffers && inline_plan && r.overhead != 0)
         return fail(MLA_ERR_INVALID_ARG, "a NULL plan (closed form) needs fixed_overhead 0, got %d", r.overhead);
     if ((a->attn_sink && !aligned(a->attn_sink, 4)) || (a->topk_length && !aligned(a->topk_length, 4)))
         return fail(MLA_ERR_INVALID_ARG, "attn_sink and topk_length must be 4-byte aligned");
@@ -133,13 +140,15 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     if (!aligned(a->lse, 4)) return fail(MLA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
     if (!aligned(a->sched_meta, 4) || !aligned(a->num_splits, 4))
         return fail(MLA_ERR_INVALID_ARG, "sched_meta / num_splits must be 4-byte aligned");
-    size_t need_o = 0, need_l = 0;
-    workspace_bytes(r, &need_o, &need_l);
-    if (!a->o_accum || !a->lse_accum || a->o_accum_bytes < need_o || a->lse_accum_bytes < need_l)
-        return fail(MLA_ERR_WORKSPACE, "workspace too small: need o_accum %zu and lse_accum %zu bytes", need_o,
-                    need_l);
-    if (!aligned(a->o_accum, 16) || !aligned(a->lse_accum, 4))
-        return fail(MLA_ERR_INVALID_ARG, "o_accum must be 16-byte aligned, lse_accum 4-byte aligned");
+    if (caller_buffers) {
+        size_t need_o = 0, need_l = 0;
+        workspace_bytes(r, &need_o, &need_l);
+        if (!a->o_accum || !a->lse_accum || a->o_accum_bytes < need_o || a->lse_accum_bytes < need_l)
+            return fail(MLA_ERR_WORKSPACE, "workspace too small: need o_accum %zu and lse_accum %zu bytes", need_o,
+                        need_l);
+        if (!aligned(a->o_accum, 16) || !aligned(a->lse_accum, 4))
+            return fail(MLA_ERR_INVALID_ARG, "o_accum must be 16-byte aligned, lse_accum 4-byte aligned");
+    }
     float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(576.0f);
     if (!std::isfinite(sm)) return fail(MLA_ERR_INVALID_ARG, "sm_scale must be finite");
 
@@ -215,6 +224,15 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 }  // namespace
+
+namespace mla {
+int host_fail(int code, const char* msg) { return fail(code, "%s", msg); }
+int host_ok() { return ok(); }
+int host_hip_status(hipError_t e, const char* what) { return hip_status(e, what); }
+int check_decode_args_noalloc(const mla_decode_args* a, ResolvedShape* rs, DecodeParams* p) {
+    return check_decode_args(a, rs, p, false);
+}
+}  // namespace mla
 
 extern "C" {
 

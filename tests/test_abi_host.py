@@ -359,3 +359,21 @@ def test_by_length_plan_needs_its_lengths():
     assert e.value.code == M.MLA_ERR_INVALID_ARG
     a = plan.args(q, kv, idx, topk_length=torch.full((2,), 100, dtype=torch.int32))
     assert a.topk_length != 0
+
+
+def test_noalloc_rejects_caller_buffers_and_oversized_shapes():
+    """The no-allocation entry point takes no plan or workspace pointers and
+    refuses, before touching a device, a shape whose split workspace exceeds
+    its 64 MiB array."""
+    s = shape(num_parts=66, fixed_overhead=0)
+    for over in (dict(), dict(sched_meta=None), dict(num_splits=None, sched_meta=None),
+                 dict(sched_meta=None, num_splits=None, lse_accum=None)):
+        a = _args(s, **over)
+        with pytest.raises(M.MlaError) as e:
+            M.mla_sparse_decode_noalloc(a, stream=0)
+        assert e.value.code == M.MLA_ERR_INVALID_ARG, over
+    big = shape(b=512, topk=2048, num_parts=256, num_kv_tokens=64 * 1024, fixed_overhead=0)
+    a = _args(big, sched_meta=None, num_splits=None, o_accum=None, lse_accum=None)
+    with pytest.raises(M.MlaError) as e:
+        M.mla_sparse_decode_noalloc(a, stream=0)                  # (512 + 256) * 128 KB > 64 MiB
+    assert e.value.code == M.MLA_ERR_WORKSPACE and M.mla_last_error() != ""
