@@ -36,6 +36,13 @@ primitives used; no blocking, fusion or online rescaling):
   value row is zero (output scale 1 / (l + 2^(sink log2(e) - m)) in base-2
   terms).  Lengths are clamped to [0, topk] (the pages do not say what a
   negative or larger length means; this reading makes them none / all).
+* dense decode -- walkthrough step 1 (no indices: block_table +
+  cache_seqlens, every page of the request walked in block-table order) and
+  "FlashMLA 与 DSA" section 3.3.  Request b sees its first cache_seqlens[b]
+  logical tokens (clamped to the block table's capacity); with causal and
+  s_q > 1 the query tokens are the last s_q positions, token j seeing
+  cache_seqlens[b] - (s_q - 1 - j) of them (the pages do not spell this
+  out; it is the plain reading of multi-token decode).
 * split-KV combine -- walkthrough step 14.2 (split partials are normalised
   O_j and lse_j = log2(l_j) + m_j in base 2, -inf when empty) and step 16
   (max over splits, weights 2^(lse_j - max), weighted mean of the O_j);
@@ -222,6 +229,54 @@ def sparse_mla_decode(q_bits: np.ndarray, kv: np.ndarray, indices: np.ndarray,
             n_ok = min(max(int(topk_length[bi]), 0), topk)
             valid = valid & (np.arange(topk) < n_ok)
             rows = np.where(valid[:, None], rows, 0.0)
+        qh = bf16_value(q_bits[bi, sj])
+        o, l = attend(qh, rows, rows[:, :DV], valid, sm_scale)
+        if attn_sink is not None:
+            o = o * sink_factor(l, attn_sink)[:, None]
+        out[bi, sj] = o
+        lse[bi, :, sj] = l
+    return out, lse
+
+
+def dense_visible(seqlen: int, capacity: int, s_q: int, sj: int, causal: bool) -> int:
+    """Tokens that query token sj of a request sees in dense decode: its
+    cache length clamped to [0, capacity]; with causal, the s_q query tokens
+    are the last s_q positions of the sequence, so token sj sees
+    seqlen - (s_q - 1 - sj) of them (never fewer than none)."""
+    n = max(0, min(int(seqlen), capacity))
+    if causal:
+        n = max(0, n - (s_q - 1 - sj))
+    return n
+
+
+def dense_mla_decode(q_bits: np.ndarray, kv: np.ndarray, block_table: np.ndarray,
+                     cache_seqlens: np.ndarray, sm_scale: float, page_block_size: int,
+                     causal: bool = False, queries: Optional[Iterable[Tuple[int, int]]] = None,
+                     attn_sink: Optional[np.ndarray] = None):
+    """Dense MLA decode by definition ("FlashMLA Sparse Decode 完整计算过程详解",
+    step 1: without indices the call takes block_table + cache_seqlens and
+    walks every page of a request in block-table order; "FlashMLA 与 DSA"
+    section 3.3 for the dense decode itself).
+
+    Request b attends to its logical tokens t < cache_seqlens[b] (see
+    dense_visible for causal), token t living at physical id
+    block_table[b, t // P] * P + t % P of the FP8 cache kv [nb, P, 1, 656].
+    Returns out float64 [b, s_q, H, 512] and natural-log lse [b, H, s_q]
+    (+inf / 0 when a query sees no token).  With `queries`, only those
+    (bi, sj) pairs are filled (NaN elsewhere)."""
+    b, s_q, H, d = q_bits.shape
+    assert d == DQK
+    P = page_block_size
+    capacity = block_table.shape[1] * P
+    out = np.full((b, s_q, H, DV), np.nan)
+    lse = np.full((b, H, s_q), np.nan)
+    if queries is None:
+        queries = [(bi, sj) for bi in range(b) for sj in range(s_q)]
+    for bi, sj in queries:
+        n = dense_visible(cache_seqlens[bi], capacity, s_q, sj, causal)
+        t = np.arange(n, dtype=np.int64)
+        phys = np.asarray(block_table[bi], dtype=np.int64)[t // P] * P + t % P
+        rows, valid = gather_dequant(kv, phys, FMT_FP8, P)
         qh = bf16_value(q_bits[bi, sj])
         o, l = attend(qh, rows, rows[:, :DV], valid, sm_scale)
         if attn_sink is not None:

@@ -218,6 +218,34 @@ def paged_decode(name: str, seed: int, b: int, s_q: int, h_q: int, topk: int,
     return _finish(name, rng, KV_FP8_656, b, s_q, h_q, topk, P, total_pages * P, indices, meta)
 
 
+def dense_decode(name: str, seed: int, b: int, s_q: int, h_q: int, seqlens, pages_per_seq: int,
+                 spare_pages: int = 3) -> Workload:
+    """Paged FP8 cache for dense decode (64-token pages): every request owns
+    pages_per_seq pages dealt from a global shuffled permutation (block table
+    [b, pages_per_seq], meta["block_table"]) and holds cache_seqlens[b]
+    tokens (meta["cache_seqlens"], int32); the rows of those tokens are
+    written, every other byte of the cache (the rest of the pages and
+    `spare_pages` unowned ones) is 0xFF.  `indices` is empty ([b, s_q, 1] of
+    -1): dense decode reads none; `topk` is the tokens a block-table row can
+    name (pages_per_seq * 64)."""
+    P = 64
+    rng = np.random.default_rng(seed)
+    total_pages = b * pages_per_seq + spare_pages
+    block_table = rng.permutation(total_pages)[: b * pages_per_seq].reshape(b, pages_per_seq).astype(np.int32)
+    lens = np.asarray(seqlens, dtype=np.int32)
+    q_bits = to_bf16_bits(rng.standard_normal((b, s_q, h_q, D_QK), dtype=np.float32))
+    written = []
+    for bi in range(b):
+        pos = np.arange(min(max(int(lens[bi]), 0), pages_per_seq * P))
+        written.append(block_table[bi, pos // P].astype(np.int64) * P + pos % P)
+    ref_ids = np.unique(np.concatenate(written)) if written else np.zeros(0, np.int64)
+    ref_rows = _fill_rows(rng, ref_ids, KV_FP8_656)
+    return Workload(name=name, kv_format=KV_FP8_656, b=b, s_q=s_q, h_q=h_q, topk=pages_per_seq * P,
+                    sm_scale=1.0 / np.sqrt(D_QK), q_bits=q_bits, indices=np.full((b, s_q, 1), -1, np.int32),
+                    page_block_size=P, num_kv_tokens=total_pages * P, ref_ids=ref_ids, ref_rows=ref_rows,
+                    meta={"block_table": block_table, "cache_seqlens": lens})
+
+
 def sparse_prefill(name: str, seed: int, s_q: int, h_q: int, topk: int, s_kv: int,
                    prior: int, q_rows: Optional[int] = None) -> Workload:
     """Flat bf16 KV, batch 1, logical indices: query t sees tokens [0, prior + t]."""
