@@ -46,7 +46,8 @@
  *   - Every argument is validated on the host before anything is launched; on
  *     error nothing is launched, the status is returned and mla_last_error()
  *     holds a message (thread-local).  The library never aborts the process.
- *   - Shape limit: b * ceil(topk / split_granularity) < 2^30.
+ *   - Shape limits: b * ceil(topk / split_granularity) < 2^30, s_q <= 65535,
+ *     b * s_q <= 2^24.
  *   - Calls that overlap on one stream-ordered pipeline must use distinct
  *     sched/workspace buffers if they run concurrently on different streams.
  */
@@ -205,8 +206,36 @@ int mla_plan_sched_meta_len_host(const mla_shape* shape, const int32_t* topk_len
  * lse_accum (base 2) for split ones. */
 int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream);
 
+/* Dense decode ("FlashMLA Sparse Decode 完整计算过程详解", step 1: a call
+ * without indices takes block_table + cache_seqlens and walks every page of
+ * a request in block-table order; the caller routes here when the context is
+ * no longer than topk; "FlashMLA 与 DSA" sections 3.3 and 6.1 for the dense
+ * decode and its 64-token pages): request b attends to its first
+ * cache_seqlens[b] logical tokens, token t being physical token
+ *   block_table[b * block_table_stride + t / 64] * 64 + t % 64
+ * of the FP8 656-byte paged cache, with the same scores, softmax, out, lse,
+ * split partials and attention sink as mla_sparse_decode_fwd.
+ *   - args->indices must be NULL; args->topk_length holds cache_seqlens (int32
+ *     [b] device memory, clamped to [0, topk]); args->shape.topk is the
+ *     tokens a block-table row can name (its width * 64); page_block_size 64;
+ *     the page stride below 4 GiB.
+ *   - block_table: int32 device memory, rows block_table_stride (>= topk / 64)
+ *     elements apart, 4-byte aligned.  An entry outside [0, num_kv_tokens / 64)
+ *     makes the tokens of that page empty (like -1 in the sparse indices).
+ *   - causal = 1 (with s_q > 1, multi-token decode): the s_q query tokens are
+ *     the last s_q positions of the sequence, so query token j sees
+ *     cache_seqlens[b] - (s_q - 1 - j) tokens; causal = 0: all of them see
+ *     cache_seqlens[b].
+ *   - Plans: mla_get_sched_meta_len with the cache lengths (a request then
+ *     costs its own pages), mla_get_sched_meta, or the closed form; then
+ *     mla_splitkv_combine with the same args.
+ * MLA_ERR_UNSUPPORTED for the bf16 cache or another page size. */
+int mla_dense_decode_fwd(const mla_decode_args* args, const int32_t* block_table,
+                         int64_t block_table_stride, int causal, void* stream);
+
 /* Split-KV combine (step 16): merges the partials of every split request into
- * out / lse; unsplit requests are left untouched. */
+ * out / lse; unsplit requests are left untouched.  args->indices is not read
+ * (it may be NULL). */
 int mla_splitkv_combine(const mla_decode_args* args, void* stream);
 
 /* Test hook for the gather + dequant stage (attn_sink and topk_length are not

@@ -28,6 +28,7 @@ EXPORTED = ("mla_sched_meta_size", "mla_workspace_size", "mla_resolve_shape",
             "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_get_sched_meta_len",
             "mla_plan_sched_meta_len_host", "mla_sparse_decode_fwd", "mla_indexer_scores", "mla_indexer_topk",
             "mla_splitkv_combine", "mla_debug_gather_dequant", "mla_sparse_decode_noalloc",
+            "mla_dense_decode_fwd",
             "mla_last_error", "mla_version")
 
 
@@ -97,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "mla_indexer_topk": [P(mla_indexer_args), ctypes.c_void_p],
         "mla_splitkv_combine": [P(mla_decode_args), ctypes.c_void_p],
         "mla_sparse_decode_noalloc": [P(mla_decode_args), ctypes.c_void_p],
+        "mla_dense_decode_fwd": [P(mla_decode_args), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                 ctypes.c_void_p],
         "mla_debug_gather_dequant": [P(mla_decode_args), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p],
     }
     for name, argtypes in sig.items():
@@ -176,6 +179,12 @@ def mla_sparse_decode_fwd(args: mla_decode_args, stream=None) -> None:
 
 def mla_splitkv_combine(args: mla_decode_args, stream=None) -> None:
     _check("mla_splitkv_combine", load_library().mla_splitkv_combine(ctypes.byref(args), _stream(stream)))
+
+
+def mla_dense_decode_fwd(args: mla_decode_args, block_table_ptr: int, block_table_stride: int, causal: bool,
+                         stream=None) -> None:
+    _check("mla_dense_decode_fwd", load_library().mla_dense_decode_fwd(
+        ctypes.byref(args), block_table_ptr, block_table_stride, int(causal), _stream(stream)))
 
 
 def mla_sparse_decode_noalloc(args: mla_decode_args, stream=None) -> None:
@@ -309,8 +318,9 @@ class DecodePlan:
         a.q_stride_b, a.q_stride_s, a.q_stride_h = q.stride(0), q.stride(1), q.stride(2)
         a.kv = kv.data_ptr()
         a.kv_stride_block = kv.stride(0) * kv.element_size()     # bytes per page / bf16 row
-        a.indices = indices.data_ptr()
-        a.idx_stride_b, a.idx_stride_s = indices.stride(0), indices.stride(1)
+        if indices is not None:                            # dense decode passes none
+            a.indices = indices.data_ptr()
+            a.idx_stride_b, a.idx_stride_s = indices.stride(0), indices.stride(1)
         a.out = out.data_ptr()
         a.out_stride_b, a.out_stride_s, a.out_stride_h = out.stride(0), out.stride(1), out.stride(2)
         a.lse = lse.data_ptr()
@@ -323,6 +333,23 @@ class DecodePlan:
         a.o_accum_bytes = self.o_accum.numel() * 4
         a.lse_accum_bytes = self.lse_accum.numel() * 4
         return a
+
+    def run_dense(self, q, kv, block_table, cache_seqlens, sm_scale: float = 0.0, causal: bool = False,
+                  stream=None, with_sched: bool = True, attn_sink=None):
+        """Dense decode: sched (optional; a by_length plan follows cache_seqlens)
+        -> mla_dense_decode_fwd -> combine.  block_table int32 [b, topk / 64]
+        (row stride taken from the tensor), cache_seqlens int32 [b]."""
+        import torch
+        _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.stride(1) == 1,
+                 "run_dense", "block_table must be int32 [b, pages] with contiguous rows")
+        _require(cache_seqlens.dtype == torch.int32 and cache_seqlens.is_contiguous(), "run_dense",
+                 "cache_seqlens must be contiguous int32 [b]")
+        if with_sched:
+            self.get_sched_meta(stream, cache_seqlens)
+        a = self.args(q, kv, None, sm_scale, attn_sink=attn_sink, topk_length=cache_seqlens)
+        mla_dense_decode_fwd(a, block_table.data_ptr(), block_table.stride(0), causal, stream)
+        mla_splitkv_combine(a, stream)
+        return self.out, self.lse
 
     def run(self, q, kv, indices, sm_scale: float = 0.0, stream=None, with_sched: bool = True,
             attn_sink=None, topk_length=None):

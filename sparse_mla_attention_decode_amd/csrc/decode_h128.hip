@@ -64,6 +64,7 @@ constexpr int KBB = ROPE_OFF + TILE * 128;        // 37376
 constexpr int IDS_SLOTS = 2;                      // token-id tiles per wave in LDS
 constexpr int ZERO_ROWS = 64;                     // rows of the zero page
 constexpr int KAHEAD = 3;                         // score fragments read ahead of their MFMAs
+constexpr int DENSE_PAGE = 64;                    // tokens per page for dense decode
 
 // LDS map (bytes).  A staged tile is 32 NoPE rows of NP bytes (bf16 dims
 // 0..511 and a 16-byte pad that the contractions never read) and 32 RoPE rows
@@ -146,6 +147,21 @@ __device__ __forceinline__ const uint8_t* row_addr(const DecodeParams& p, int t,
     return (const uint8_t*)(uintptr_t)(ok ? r : z);
 }
 
+// Dense decode: row address of slot `off` (0..63) of page `entry` when ok,
+// else row zrow of the zero page.  FLAT: token entry * 64 + off at 656 bytes
+// per token (pages back to back); otherwise the page's own stride.
+template <bool FLAT>
+__device__ __forceinline__ const uint8_t* dense_row_addr(const DecodeParams& p, int entry, int off, bool ok,
+                                                         int zrow) {
+    if (FLAT) return row_addr<true>(p, entry * DENSE_PAGE + off, ok, zrow);
+    const uint32_t e = ok ? (uint32_t)entry : 0u;
+    // the page stride is below 2^32 for dense decode (checked on the host):
+    // one 32 x 32 -> 64-bit multiply-add
+    const uint64_t r = (uint64_t)(uintptr_t)p.kv + (uint64_t)e * (uint32_t)p.kv_block_stride + (uint32_t)off * ROWB;
+    const uint64_t z = (uint64_t)(uintptr_t)g_zero_rows + (uint32_t)zrow * ROWB;
+    return (const uint8_t*)(uintptr_t)(ok ? r : z);
+}
+
 // Copies of this wave's 8 rows of a tile into its raw slice; `src` points at
 // chunk lane % 8 of row lane / 8 (key 8w + lane / 8).
 __device__ __forceinline__ const uint8_t* tail_src(const uint8_t* src, int lane) {
@@ -185,6 +201,24 @@ __device__ __forceinline__ void copy_ids(const int32_t* idx, int k_lo, int k_hi,
     const uint32_t dst = __builtin_amdgcn_readfirstlane(slot_addr);
     if (lane < 32) dma4(src, dst);
 }
+
+// Dense decode ("FlashMLA Sparse Decode 完整计算过程详解", step 1: the block
+// table walked in order; "FlashMLA 与 DSA" section 6.1: the dense decode
+// pages hold 64 tokens): slot k of a request is its logical token k.  Pieces
+// start on 32-slot boundaries, so the 32 slots of a tile lie in one page;
+// every slot of the id slot receives that page's block-table entry (slots past
+// the piece: -1), copied the same way as sparse ids so the memory-counter
+// accounting is unchanged.  dense_id turns an entry back into a token id when
+// it is read.
+__device__ __forceinline__ void copy_pages(const int32_t* bt_row, int k_lo, int k_hi, int tile, int lane,
+                                           uint32_t slot_addr) {
+    const int k0 = k_lo + tile * TILE;
+    const int k = k0 + (lane & 31);
+    const int32_t* src = k < k_hi ? bt_row + k0 / DENSE_PAGE : g_no_id;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(slot_addr);
+    if (lane < 32) dma4(src, dst);
+}
+
 
 // Staging of this wave's 8 rows.  Lane L holds NoPE chunks (L % 8) + 8 i of
 // row r = L / 8 (copies i = 0..3: dims 16 c .. 16 c + 15, scale group i) and
@@ -298,7 +332,7 @@ __device__ __forceinline__ int xp_base(int lane) {
     return b;
 }
 
-template <bool FLAT>
+template <bool FLAT, bool DENSE>
 __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
@@ -325,10 +359,19 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         const int k_lo = blk_lo * p.block;
         const int k_hi = min(blk_hi * p.block, p.topk);
         const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
-        const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+        // sparse: the request's index row; dense: its block-table row
+        const int32_t* idx = DENSE ? p.block_table + (int64_t)req * p.bt_stride
+                                   : p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
         // slots below k_ok hold ids; the ones past the request's valid length
-        // (topk_length) are empty like the ones past the piece
-        const int k_ok = p.topk_length ? min(k_hi, max(p.topk_length[req], 0)) : k_hi;
+        // (topk_length; dense: the cache length, less the later query tokens
+        // with causal) are empty like the ones past the piece
+        const int k_ok = p.topk_length
+                             ? min(k_hi, max(p.topk_length[req] - (p.causal ? p.s_q - 1 - sq : 0), 0))
+                             : k_hi;
+        auto tile_ids = [&](int tile, int ln, uint32_t slot_addr) {
+            if (DENSE) copy_pages(idx, k_lo, k_ok, tile, ln, slot_addr);
+            else copy_ids(idx, k_lo, k_ok, tile, ln, slot_addr);
+        };
 
         // LDS slots of this wave's token ids: tile t in the ring (t % 2), the
         // first four tiles of a pass in the prologue area
@@ -343,8 +386,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         // validity mask of the tile's 32 keys and the copy source of this
         // lane's row (chunk ln % 8); tiles past the piece copy zero rows
         auto rows_from = [&](int tile, int ln, int2 id, const uint8_t*& src) -> uint32_t {
-            (void)tile;
             const int kr = WROWS * wave + (ln >> 3);
+            if (DENSE) {
+                // the id slot holds the tile's block-table entry (or -1): a
+                // key is valid when the entry names a page of the cache
+                const bool ok = (uint32_t)id.x < p.n_pages;
+                const bool okr = (uint32_t)id.y < p.n_pages;
+                src = dense_row_addr<FLAT>(p, id.y, (k_lo + tile * TILE) % DENSE_PAGE + kr, okr, kr) + 16 * (ln & 7);
+                return (uint32_t)__ballot(ok);
+            }
             const bool ok = slot_ok(p, id.x, true);
             const bool okr = slot_ok(p, id.y, true);
             src = row_addr<FLAT>(p, id.y, okr, kr) + 16 * (ln & 7);
@@ -385,7 +435,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     if (scores) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
                 // RoPE k-steps 32..35 of tile i+1 (lane-dependent slots)
                 auto rope_k = [&](int j) { return kb + qk_off(ln, j); };
-                if (soft && copies) copy_ids(idx, k_lo, k_ok, i + 5, ln, lds0 + ring_slot(r3));
+                if (soft && copies) tile_ids(i + 5, ln, lds0 + ring_slot(r3));
                 __builtin_amdgcn_sched_barrier(0);
                 float mx, psum = 0.f;
 #pragma unroll
@@ -523,8 +573,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             f32x16 S_cur;                           // scores of tile i
             {
                 const int ln = opaque_lane();
-                for (int t = 0; t < 4; ++t) copy_ids(idx, k_lo, k_ok, t, ln, lds0 + first_slot(t));
-                copy_ids(idx, k_lo, k_ok, 4, ln, lds0 + ring_slot(4));
+                for (int t = 0; t < 4; ++t) tile_ids(t, ln, lds0 + first_slot(t));
+                tile_ids(4, ln, lds0 + ring_slot(4));
                 if (pass == 0) {
                     // Q of the wave's 32 heads (with 64 query heads waves 2 and
                     // 3 take heads 0..63 again; those results are never stored)
@@ -768,8 +818,13 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
 // when no split saw a valid key.  Splits are taken four at a time with their
 // lse and partial loads issued together (one memory round trip per batch);
 // a later batch with a larger max rescales what was accumulated so far.
+// The work items (query column, piece) are taken query-major through the same
+// XCD mapping as the decode's partitions, so a request's partials are read
+// back on the XCD whose L2 received them (for b a multiple of 8 and a uniform
+// plan exactly, otherwise approximately).
 __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
-    const int qi = blockIdx.x, piece = blockIdx.y;          // piece = 16 w + 4 j + hb
+    const int item = xcd_part(blockIdx.x, gridDim.x);
+    const int qi = item >> 6, piece = item & 63;             // piece = 16 w + 4 j + hb
     const int req = qi / p.s_q, sq = qi % p.s_q;
     const int first = split_prefix(p, req);
     const int ns = split_prefix(p, req + 1) - first;
@@ -833,7 +888,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
             poison ? __builtin_nanf("") : M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
 }
 
-bool g_lds_decode = false, g_lds_decode_flat = false, g_lds_gather = false;
+bool g_lds_decode[2][2] = {}, g_lds_gather = false;
 
 template <typename K>
 hipError_t allow_lds_once(K k, bool& done) {
@@ -843,23 +898,25 @@ hipError_t allow_lds_once(K k, bool& done) {
     return e;
 }
 
-}  // namespace
-
-hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
-    if (p.kv_flat) {
-        hipError_t e = allow_lds_once(decode_fp8_h128_kernel<true>, g_lds_decode_flat);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(decode_fp8_h128_kernel<true>, dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st, p);
-    } else {
-        hipError_t e = allow_lds_once(decode_fp8_h128_kernel<false>, g_lds_decode);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(decode_fp8_h128_kernel<false>, dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st, p);
-    }
+template <bool FLAT, bool DENSE>
+hipError_t launch_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
+    hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE>, g_lds_decode[FLAT][DENSE]);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE>), dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st,
+                       p);
     return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
+    const bool dense = p.block_table != nullptr;
+    if (p.kv_flat) return dense ? launch_h128<true, true>(p, num_parts, st) : launch_h128<true, false>(p, num_parts, st);
+    return dense ? launch_h128<false, true>(p, num_parts, st) : launch_h128<false, false>(p, num_parts, st);
+}
+
 hipError_t launch_combine_packed(const DecodeParams& p, hipStream_t st) {
-    hipLaunchKernelGGL(combine_packed_kernel, dim3(p.b * p.s_q, 64), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(combine_packed_kernel, dim3(p.b * p.s_q * 64), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 

@@ -39,6 +39,9 @@ int resolve(const mla_shape* in, mla::ResolvedShape* out) {
     const mla_shape& s = *in;
     if (s.b < 1) return fail(MLA_ERR_INVALID_ARG, "b must be >= 1 (got %d)", s.b);
     if (s.s_q < 1) return fail(MLA_ERR_INVALID_ARG, "s_q must be >= 1 (got %d)", s.s_q);
+    if (s.s_q > 65535) return fail(MLA_ERR_INVALID_ARG, "s_q must be <= 65535 (got %d)", s.s_q);
+    if ((int64_t)s.b * s.s_q > (1 << 24))
+        return fail(MLA_ERR_INVALID_ARG, "b * s_q must be <= 2^24 (got %lld)", (long long)s.b * s.s_q);
     if (s.topk < 1) return fail(MLA_ERR_INVALID_ARG, "topk must be >= 1 (got %d)", s.topk);
     if (s.h_q < 1) return fail(MLA_ERR_INVALID_ARG, "h_q must be >= 1 (got %d)", s.h_q);
     if (s.h_q != 64 && s.h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "h_q must be 64 or 128 (got %d)", s.h_q);
@@ -104,13 +107,15 @@ void workspace_bytes(const mla::ResolvedShape& r, size_t* o, size_t* l) {
 // Validate `a` and fill the kernel parameters.  With caller_buffers false (the
 // no-allocation entry point) the plan and workspace pointers must be NULL:
 // the library's own array supplies them afterwards.
+// need_indices: the sparse decode reads them; the combine does not, and dense
+// decode takes a block table instead (it checks that indices is NULL itself).
 int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::DecodeParams* p,
-                      bool caller_buffers = true) {
+                      bool caller_buffers = true, bool need_indices = true) {
     if (!a) return fail(MLA_ERR_INVALID_ARG, "args is NULL");
     int st = resolve(&a->shape, rs);
     if (st != MLA_OK) return st;
     const mla::ResolvedShape& r = *rs;
-    if (!a->q || !a->kv || !a->indices || !a->out || !a->lse)
+    if (!a->q || !a->kv || (need_indices && !a->indices) || !a->out || !a->lse)
         return fail(MLA_ERR_INVALID_ARG, "q, kv, indices, out and lse must be non-NULL");
     const bool inline_plan = !a->sched_meta && !a->num_splits;
     if (!caller_buffers && (!inline_plan || a->o_accum || a->lse_accum))
@@ -172,6 +177,10 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
     p->lse_accum = a->lse_accum;
     p->attn_sink = a->attn_sink;
     p->topk_length = a->topk_length;
+    p->block_table = nullptr;
+    p->bt_stride = 0;
+    p->causal = 0;
+    p->n_pages = (uint32_t)(r.num_kv_tokens / r.page_block_size);
     p->n_tok = r.num_kv_tokens;
     p->n_tok32 = (uint32_t)(r.num_kv_tokens < INT32_MAX ? r.num_kv_tokens : INT32_MAX);
     p->b = r.b;
@@ -321,10 +330,43 @@ int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream) {
                       "decode kernel launch");
 }
 
+int mla_dense_decode_fwd(const mla_decode_args* args, const int32_t* block_table, int64_t block_table_stride,
+                         int causal, void* stream) {
+    mla::ResolvedShape r;
+    mla::DecodeParams p;
+    int st = check_decode_args(args, &r, &p, true, false);
+    if (st != MLA_OK) return st;
+    if (args->indices)
+        return fail(MLA_ERR_INVALID_ARG, "dense decode walks the block table: args->indices must be NULL");
+    if (r.kv_format != MLA_KV_FP8_656)
+        return fail(MLA_ERR_UNSUPPORTED, "dense decode reads the FP8 656-byte paged cache only");
+    if (r.page_block_size != 64)
+        return fail(MLA_ERR_UNSUPPORTED, "dense decode reads 64-token pages (got page_block_size %d)",
+                    r.page_block_size);
+    if (args->kv_stride_block >= ((int64_t)1 << 32))
+        return fail(MLA_ERR_UNSUPPORTED, "dense decode needs a page stride below 4 GiB");
+    if (r.topk % r.page_block_size != 0)
+        return fail(MLA_ERR_INVALID_ARG, "dense decode: topk (%d, tokens a block-table row can hold) must be a "
+                    "multiple of page_block_size (%d)", r.topk, r.page_block_size);
+    if (!args->topk_length)
+        return fail(MLA_ERR_INVALID_ARG, "dense decode needs the cache lengths in args->topk_length");
+    if (!block_table || !aligned(block_table, 4))
+        return fail(MLA_ERR_INVALID_ARG, "block_table must be non-NULL and 4-byte aligned");
+    if (block_table_stride < r.topk / r.page_block_size)
+        return fail(MLA_ERR_INVALID_ARG, "block_table_stride (%lld) < topk / page_block_size (%d)",
+                    (long long)block_table_stride, r.topk / r.page_block_size);
+    if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+    p.block_table = block_table;
+    p.bt_stride = block_table_stride;
+    p.causal = causal;
+    return hip_status(mla::launch_decode(p, r.kv_format, r.num_parts, static_cast<hipStream_t>(stream)),
+                      "dense decode kernel launch");
+}
+
 int mla_splitkv_combine(const mla_decode_args* args, void* stream) {
     mla::ResolvedShape r;
     mla::DecodeParams p;
-    int st = check_decode_args(args, &r, &p);
+    int st = check_decode_args(args, &r, &p, true, false);
     if (st != MLA_OK) return st;
     return hip_status(mla::launch_combine(p, static_cast<hipStream_t>(stream)), "combine kernel launch");
 }

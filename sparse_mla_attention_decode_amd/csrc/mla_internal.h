@@ -47,7 +47,14 @@ struct DecodeParams {
     float* o_accum;
     float* lse_accum;
     const float* attn_sink;         // [h_q] natural-log sink logits, or NULL
-    const int32_t* topk_length;     // [b] valid slots per request, or NULL
+    const int32_t* topk_length;     // [b] valid slots per request (dense decode: the cache
+                                    // lengths), or NULL
+    const int32_t* block_table;     // dense decode: [b, bt_stride] logical page -> physical page;
+                                    // NULL for sparse decode (ids come from `indices`)
+    int64_t bt_stride;              // elements between block-table rows
+    int causal;                     // dense decode with s_q > 1: query token sq sees
+                                    // topk_length - (s_q - 1 - sq) tokens
+    uint32_t n_pages;               // FP8 pages in the cache (n_tok / page_block_size)
     int64_t n_tok;
     uint32_t n_tok32;               // min(n_tok, 2^31 - 1): token ids are int32
     int b, s_q, h_q, topk, page_block_size, block;

@@ -63,6 +63,7 @@ def test_sizes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(b=0), M.MLA_ERR_INVALID_ARG), (dict(s_q=0), M.MLA_ERR_INVALID_ARG),
+    (dict(s_q=65536), M.MLA_ERR_INVALID_ARG), (dict(b=1 << 20, s_q=17), M.MLA_ERR_INVALID_ARG),
     (dict(topk=0), M.MLA_ERR_INVALID_ARG), (dict(h_q=96), M.MLA_ERR_UNSUPPORTED),
     (dict(h_q=-1), M.MLA_ERR_INVALID_ARG), (dict(num_kv_tokens=0), M.MLA_ERR_INVALID_ARG),
     (dict(num_kv_tokens=100), M.MLA_ERR_INVALID_ARG),           # not a multiple of the page size
@@ -377,3 +378,38 @@ def test_noalloc_rejects_caller_buffers_and_oversized_shapes():
     with pytest.raises(M.MlaError) as e:
         M.mla_sparse_decode_noalloc(a, stream=0)                  # (512 + 256) * 128 KB > 64 MiB
     assert e.value.code == M.MLA_ERR_WORKSPACE and M.mla_last_error() != ""
+
+
+@pytest.mark.parametrize("over,extra,code", [
+    (dict(), dict(), M.MLA_ERR_INVALID_ARG),                                   # indices set: dense takes none
+    (dict(indices=None), dict(), M.MLA_ERR_INVALID_ARG),                       # no cache lengths
+    (dict(indices=None, topk_length=0xA000), dict(bt=None), M.MLA_ERR_INVALID_ARG),
+    (dict(indices=None, topk_length=0xA000), dict(bt=0xB002), M.MLA_ERR_INVALID_ARG),
+    (dict(indices=None, topk_length=0xA000), dict(stride=1), M.MLA_ERR_INVALID_ARG),
+    (dict(indices=None, topk_length=0xA000), dict(causal=2), M.MLA_ERR_INVALID_ARG),
+    (dict(indices=None, topk_length=0xA000, kv_stride_block=1 << 32), dict(), M.MLA_ERR_UNSUPPORTED),
+])
+def test_dense_args_validated_before_launch(over, extra, code):
+    """mla_dense_decode_fwd: indices must be NULL, the cache lengths come in
+    topk_length, a block table of at least topk / 64 entries per row, causal
+    0 or 1, a page stride below 4 GiB -- all checked before any launch."""
+    s = shape()                                                               # topk 128 = 2 pages of 64
+    a = _args(s, **over)
+    bt = extra.get("bt", 0xB000)
+    with pytest.raises(M.MlaError) as e:
+        M.mla_dense_decode_fwd(a, bt, extra.get("stride", 2), extra.get("causal", 0), stream=0)
+    assert e.value.code == code, (over, extra, M.mla_last_error())
+
+
+@pytest.mark.parametrize("kw,code", [(dict(page_block_size=32, num_kv_tokens=512), M.MLA_ERR_UNSUPPORTED),
+                                     (dict(topk=100), M.MLA_ERR_INVALID_ARG),
+                                     (dict(kv_format=M.MLA_KV_BF16_576), M.MLA_ERR_UNSUPPORTED)])
+def test_dense_shape_limits(kw, code):
+    """Dense decode reads the FP8 cache in 64-token pages; topk is the
+    block-table capacity in whole pages."""
+    s = shape(**kw)
+    a = _args(s, indices=None, topk_length=0xA000,
+              kv_stride_block=1152 if kw.get("kv_format") == M.MLA_KV_BF16_576 else 64 * 656)
+    with pytest.raises(M.MlaError) as e:
+        M.mla_dense_decode_fwd(a, 0xB000, 64, 0, stream=0)
+    assert e.value.code == code, (kw, M.mla_last_error())

@@ -70,7 +70,7 @@ def test_no_kernel_uses_scratch_or_spills(reports):
 def test_h128_decode_keeps_the_whole_register_file(reports):
     names = {n: r for k in reports.values() for n, r in k.items()}
     dec = [r for n, r in names.items() if "decode_fp8_h128_kernel" in n]
-    assert len(dec) == 2                                   # the flat and the paged address path
+    assert len(dec) == 4                                   # flat / paged address path x sparse / dense
     for r in dec:
         assert r["Occupancy"] == "1" and int(r["AGPRs"]) == 256, r
     for needle in ("combine_packed_kernel", "combine_kernel", "decode_kernel", "indexer_score_kernel",
