@@ -265,6 +265,52 @@ __device__ __forceinline__ void stage_rows(LDS_AS uint8_t* lds, int slice, int k
     stage_store(lds, stage_load(lds, slice, lane), kb, wave, lane);
 }
 
+// The rows of a tile loaded into registers instead of copied into a raw
+// slot (the first two tiles of a pass, while Q still fills the LDS): lane L
+// holds NoPE chunks (L % 8) + 8 i of its row (key 8 w + L / 8), the row's
+// four scales and the RoPE chunk it places in slot L % 8.  Loaded with
+// inline asm so the compiler neither counts nor waits for them: rows_wait
+// waits for every load in flight with the registers tied to the wait.
+struct RowRegs {
+    u32x4 nope[4];
+    u32x4 scales;
+    u32x4 rope;
+};
+__device__ __forceinline__ u32x4 gload16(const uint8_t* src) {
+    u32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(src) : "memory");
+    return v;
+}
+// `src` points at chunk lane % 8 of the lane's row, as for gather_rows
+__device__ __forceinline__ RowRegs load_rows(const uint8_t* src, int lane, int wave) {
+    RowRegs r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.nope[i] = gload16(src + 128 * i);
+    r.scales = gload16(src - 16 * (lane & 7) + 512);
+    r.rope = gload16(rope_src(src, lane, wave));
+    return r;
+}
+// Wait until at most N memory operations newer than the loads of `a` are in
+// flight (so `a` has landed), with its registers tied to the wait.
+template <int N>
+__device__ __forceinline__ void rows_wait(RowRegs& a) {
+    asm volatile("s_waitcnt vmcnt(%6)"
+                 : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.nope[2]), "+v"(a.nope[3]), "+v"(a.scales), "+v"(a.rope)
+                 : "n"(N) : "memory");
+}
+// Staging of a tile from registers into the K buffer at kb: the NoPE chunks
+// dequantised as in stage_chunk, the RoPE chunk written to its slot.
+__device__ __forceinline__ void stage_from_regs(LDS_AS uint8_t* lds, const RowRegs& r, int kb, int wave, int lane) {
+    StageRegs g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        g.w[i] = r.nope[i];
+        g.sc[i] = __uint_as_float(r.scales[i]);
+    }
+    stage_store(lds, g, kb, wave, lane);
+    lds_write16(lds, kb + ROPE_OFF + 1024 * wave + 16 * lane, r.rope);
+}
+
 // Value operand (V^T fragment) of the transposing LDS read, 32 dims x 16 keys
 // of k-step t.  In each 16-lane group, provider lane 4q + b points at the
 // 8-byte row of key 16t + s(q) + 2h + r (s = 0, 8, 4, 12; h = lane / 32;
@@ -564,10 +610,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 }
             };
 
-            // ---- prologue: ids of tiles 0..4; (first pass) Q through LDS; the
-            // copies of tiles 0 and 1; copy sources of tiles 2 and 3; tiles 0
-            // and 1 staged into K buffers 0 and 1; the copies of tile 2 into
-            // raw slot 0; the scores of tile 0.
+            // ---- prologue: ids of tiles 0..4; (first pass) Q through LDS and,
+            // under it, the rows of tile 0 into registers; the copies of tile 1
+            // into raw slot 1; tile 0 staged from the registers into K buffer 0;
+            // copy sources of tiles 2 and 3; the copies of tile 2 into raw slot
+            // 0; the scores of tile 0 with the staging of tile 1.
             uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles i .. i+3
             const uint8_t* src_nx;                  // this lane's copy source in tile i+3
             f32x16 S_cur;                           // scores of tile i
@@ -601,26 +648,40 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const uint8_t* src2;
                 vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src);
                 vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src2);
+                // sparse decode: the rows of tile 0 travel while Q lands (6
+                // loads per lane, newer than the copies of Q).  (Dense decode
+                // copies tile 0 after Q: holding these registers across the Q
+                // reads would make its paged-address instance spill.)
+                RowRegs r0;
+                if (!DENSE) r0 = load_rows(src, ln, wave);
                 if (pass == 0) {
                     // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7 of
                     // head 32w + n for k-step j
-                    wait_vmcnt<0>();
+                    if (DENSE) wait_vmcnt<0>();
+                    else wait_vmcnt<6>();
                     const int qr = L_Q + wave * 32 * QROW + (ln & 31) * QROW + 16 * (ln >> 5);
 #pragma unroll
                     for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
-                    // every wave's reads are done before the row copies reuse the area
+                    // every wave's reads are done before the staging reuses the area
                     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
                     __syncthreads();
                 }
                 const uint32_t rope0 = lds0 + L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0
-                gather_rows(src, ln, wave, lds0 + slice_off, rope0);
+                if (DENSE) gather_rows(src, ln, wave, lds0 + slice_off, rope0);
                 gather_rows(src2, ln, wave, lds0 + slice_off + RAW_BYTES, rope0 + KBB);
                 vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2);
                 vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx);
-                wait_vmcnt<0>();                        // copies of tiles 0 and 1
-                stage_rows(lds, slice_off, L_KB, wave, ln);
-                // raw slot 0 is read (its values went through the conversions)
+                if (DENSE) {
+                    wait_vmcnt<0>();                    // copies of tiles 0 and 1
+                    stage_rows(lds, slice_off, L_KB, wave, ln);
+                } else {
+                    rows_wait<NDMA>(r0);                // tile 0 (the copies of tile 1 are newer)
+                    stage_from_regs(lds, r0, L_KB, wave, ln);
+                }
+                // raw slot 0 is free (tile 0 staged from registers, or its values
+                // went through the conversions)
                 gather_rows(src2, ln, wave, lds0 + slice_off, rope0 + 2 * KBB);
+                wait_vmcnt<NDMA>();                     // the wave's copies of tile 1 (tile 2's are newer)
             }
             __syncthreads();                        // tile 0 staged
             {
