@@ -32,6 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-decode query-tokens/s at b=64,h=128,topk=2048; % of MFMA/HBM roofline"
+METRIC_HALFHEAD = ("sparse-decode query-tokens/s at b=128,h=64,topk=2048 (13 of 128 requests hold 1500 valid "
+                   "slots); % of HBM roofline")
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 
@@ -94,29 +96,39 @@ def algorithmic(w):
     return flops, float(bytes_), n_valid
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, budget_s: float):
-    """The CPU oracle, as it stands, on the first query tokens of layer 0 until
-    the time budget is spent; returns query-tokens/s and what was run."""
-    import numpy as np
+    """The CPU oracle, as it stands, on the query tokens of layer 0 in order
+    (starting over after the last) until the time budget is spent; returns
+    query-tokens/s and what was run."""
     from threadpoolctl import threadpool_info
     from oracle import mla_oracle as O
     kv = w.kv_host()
+    n_q = w.b * w.s_q
     done = 0
     t0 = time.perf_counter()
-    while True:
-        bi, sj = divmod(done, w.s_q)
-        if bi >= w.b:
-            break
+    while time.perf_counter() - t0 < budget_s:
+        bi, sj = divmod(done % n_q, w.s_q)
         O.sparse_mla_decode(w.q_bits, kv, w.indices, w.sm_scale, w.kv_format, w.page_block_size,
                             queries=[(bi, sj)])
         done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     return {"value": done / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {w.b * w.s_q} query tokens of the same workload (layer 0), "
-                      f"{dt:.1f} s, numpy float64 with {threads} BLAS threads"}
+            "cpu_model": cpu_model(),
+            "sample": f"{done} query-token decodes of the same workload (layer 0's {n_q} query tokens in order, "
+                      f"repeated), {dt:.1f} s, numpy float64 with {threads} BLAS threads"}
 
 
 def bench_indexer(args, torch, np, M, W, dev):
@@ -125,16 +137,26 @@ def bench_indexer(args, torch, np, M, W, dev):
     indexer heads, K = 2048: one step = the score kernel + the top-k kernel."""
     b, heads, pages, K = 64, 64, 512, 2048
     lens = np.full(b, pages * 64, dtype=np.int32)
-    q, w, kc, pt, lens = W.indexer_inputs(21, b, heads, lens, max_pages=pages)
+    # steps rotate over independent layers (key cache, q, weights, page table:
+    # 277 MB of keys each) so a step's keys are not still in the 256 MB
+    # Infinity Cache when its layer comes round again
+    n_layers = max(2, min(args.layers, 4))
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    q_d, w_d, kc_d, pt_d, len_d = d(q), d(w), d(kc), d(pt), d(lens)
-    scores = torch.empty((b, pages * 64), dtype=torch.bfloat16, device=dev)
-    idx = torch.empty((b, K), dtype=torch.int32, device=dev)
-    a = M.indexer_args(q_d, w_d, kc_d, pt_d, len_d, K, scores, idx)
+    sets = []
+    for l in range(n_layers):
+        q, w, kc, pt, lens = W.indexer_inputs(21 + 1000 * l, b, heads, lens, max_pages=pages)
+        scores = torch.empty((b, pages * 64), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((b, K), dtype=torch.int32, device=dev)
+        q_d, w_d, kc_d, pt_d, len_d = d(q), d(w), d(kc), d(pt), d(lens)
+        sets.append((M.indexer_args(q_d, w_d, kc_d, pt_d, len_d, K, scores, idx),
+                     (q_d, w_d, kc_d, pt_d, len_d, scores, idx)))
+        if l == 0:
+            q0, w0_, kc0, pt0 = q, w, kc, pt
     st = torch.cuda.current_stream()
     sp = st.cuda_stream
 
-    def step(ev=None):
+    def step(i, ev=None):
+        a = sets[i % n_layers][0]
         if ev is not None:
             ev[0].record(st)
         M.mla_indexer_scores(a, sp)
@@ -144,17 +166,17 @@ def bench_indexer(args, torch, np, M, W, dev):
         if ev is not None:
             ev[2].record(st)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e in evs:
-        step(e)
+    for i, e in enumerate(evs):
+        step(i, e)
     torch.cuda.synchronize()
     score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     topk_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
@@ -170,7 +192,8 @@ def bench_indexer(args, torch, np, M, W, dev):
            "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
            "config": {"workload": "indexer_b64_h64_ctx32k_k2048", "b": b, "indexer_heads": heads,
-                      "context": pages * 64, "topk": K, "key_cache": "fp8 128 B + fp32 scale per token, page 64"},
+                      "context": pages * 64, "topk": K, "key_cache": "fp8 128 B + fp32 scale per token, page 64",
+                      "layers_rotated": n_layers},
            "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": achieved / PEAK_HBM_GBS,
                         "traffic": traffic_of(INDEXER_KERNEL_SOURCES, INDEXER_TRAFFIC), "kernel": "indexer_score_kernel",
@@ -179,16 +202,20 @@ def bench_indexer(args, torch, np, M, W, dev):
                            "algorithmic_bytes_per_launch": topk_bytes,
                            "achieved_GBs": topk_bytes / (topk_ms * 1e-3) / 1e9}}
     if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
         from oracle import indexer_oracle as X
+        q, w, kc, pt = q0, w0_, kc0, pt0
         rows, t1 = 0, time.perf_counter()
         while rows < b and time.perf_counter() - t1 < args.cpu_budget:
             sc = X.indexer_scores(q[rows:rows + 1], w[rows:rows + 1], kc, pt[rows:rows + 1], lens[rows:rows + 1])
             X.topk_select(sc[0], int(lens[rows]), K, pt[rows], kc.shape[0])
             rows += 1
         cpu_s = time.perf_counter() - t1
-        res["cpu_baseline"] = {"value": rows / cpu_s, "unit": "query-tokens/s",
-                               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count())), "kind": "oracle",
-                               "sample": f"{rows} of {b} requests of the same workload, {cpu_s:.1f} s, numpy float64"}
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+        res["cpu_baseline"] = {"value": rows / cpu_s, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+                               "cpu_model": cpu_model(),
+                               "sample": f"{rows} of {b} requests of the same workload (layer 0), {cpu_s:.1f} s, "
+                                         f"numpy float64 with {threads} BLAS threads"}
     print(json.dumps(res), flush=True)
 
 
@@ -210,9 +237,11 @@ def main():
                          "auto: closed when fixed_overhead is 0")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "indexer"), default="decode",
-                    help="decode: the sparse MLA decode step (default); indexer: the lightning "
-                         "indexer scores + top-k that select its tokens")
+    ap.add_argument("--workload", choices=("decode", "halfhead", "indexer"), default="decode",
+                    help="decode: the sparse MLA decode step at b=64, h=128, topk=2048 (default); "
+                         "halfhead: b=128, h=64, topk=2048 over 65536-token contexts with 10%% of the "
+                         "requests holding 1500 valid slots (HBM-bound); indexer: the lightning "
+                         "indexer scores + top-k that select the decode's tokens")
     ap.add_argument("--graph", action="store_true",
                     help="replay a captured HIP graph of each layer's step instead of launching "
                          "its kernels one by one")
@@ -246,12 +275,21 @@ def main():
         return
     M.load_library()
 
-    print(f"[bench] building {args.layers} layers of {W.CONFIG_NAMES[1]}", file=sys.stderr, flush=True)
+    cfg = 1 if args.workload == "decode" else 2
+    # the 64-head workload's cache is 5.4 GB per layer: two layers already
+    # exceed the 256 MB Infinity Cache many times over
+    n_layers = args.layers if cfg == 1 else min(args.layers, 2)
+    print(f"[bench] building {n_layers} layers of {W.CONFIG_NAMES[cfg]}", file=sys.stderr, flush=True)
     layers = []
-    for l in range(args.layers):
-        w = W.make_config(1) if l == 0 else W.paged_decode(
-            f"{W.CONFIG_NAMES[1]}_layer{l}", W.BASE_SEED + 1 + 1000 * l, b=64, s_q=1, h_q=128,
-            topk=2048, tokens_per_seq=32768)
+    for l in range(n_layers):
+        if l == 0:
+            w = W.make_config(cfg)
+        elif cfg == 1:
+            w = W.paged_decode(f"{W.CONFIG_NAMES[1]}_layer{l}", W.BASE_SEED + 1 + 1000 * l, b=64, s_q=1, h_q=128,
+                               topk=2048, tokens_per_seq=32768)
+        else:
+            w = W.paged_decode(f"{W.CONFIG_NAMES[2]}_layer{l}", W.BASE_SEED + 2 + 1000 * l, b=128, s_q=1, h_q=64,
+                               topk=2048, tokens_per_seq=65536, short_frac=0.1, short_len=1500)
         layers.append((w, w.q_device(dev), w.kv_device(dev), w.indices_device(dev)))
     w0 = layers[0][0]
     shape = M.make_shape(w0.b, w0.s_q, w0.h_q, w0.topk, w0.num_kv_tokens, w0.kv_format,
@@ -329,30 +367,38 @@ def main():
     decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     flops, bytes_, n_valid = algorithmic(w0)
-    traffic, traffic_detail = measured_traffic()
+    traffic, traffic_detail = measured_traffic() if cfg == 1 else (None, None)
     achieved_tflops = flops / (decode_ms * 1e-3) / 1e12
+    achieved_gbs = bytes_ / (decode_ms * 1e-3) / 1e9
     t_roof_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
+    mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) >= bytes_ / (PEAK_HBM_GBS * 1e9)
     q_tokens = w0.b * w0.s_q
     value = q_tokens / (ms_per_step * 1e-3)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved_tflops / PEAK_BF16_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / PEAK_HBM_GBS}
+    roof.update({"traffic": traffic, "traffic_detail": traffic_detail,
+                 "kernel": "decode_fp8_h128_kernel", "kernel_ms": decode_ms,
+                 "algorithmic_flop_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
+                 "mfma_achieved_TFLOPs": achieved_tflops, "hbm_achieved_GBs": achieved_gbs})
 
     res = {
-        "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
+        "metric": METRIC if cfg == 1 else METRIC_HALFHEAD, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "prewarm_steps": n_pre, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": W.CONFIG_NAMES[1], "b": w0.b, "s_q": w0.s_q, "h_q": w0.h_q,
-                   "topk": w0.topk, "kv_cache": "fp8 656 B/token, page 64, 32768 tokens/seq",
-                   "layers_rotated": args.layers, "split_granularity": args.split_granularity,
+        "config": {"workload": W.CONFIG_NAMES[cfg], "b": w0.b, "s_q": w0.s_q, "h_q": w0.h_q,
+                   "topk": w0.topk, "valid_slots": n_valid,
+                   "kv_cache": f"fp8 656 B/token, page 64, {w0.num_kv_tokens // w0.b} tokens/seq",
+                   "layers_rotated": n_layers, "split_granularity": args.split_granularity,
                    "fixed_overhead": args.fixed_overhead, "num_parts": plan.shape.num_parts,
                    "step": ("decode (closed-form plan in-kernel) + combine" if closed
                             else "sched + decode + combine"),
                    "launch": "eager" if not graphs else "hip graph per layer"},
-        "roofline": {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "traffic_detail": traffic_detail,
-                     "kernel": "decode_fp8_h128_kernel", "kernel_ms": decode_ms,
-                     "algorithmic_flop_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
-                     "hbm_achieved_GBs": bytes_ / (decode_ms * 1e-3) / 1e9},
+        "roofline": roof,
         "step_roofline_frac": t_roof_ms / ms_per_step,
     }
     if not args.no_cpu_baseline:

@@ -1,8 +1,9 @@
-// gfx950 sparse MLA decode for 128 query heads over the FP8 656-byte token
-// cache ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14).  64 query
-// heads run the same layout: the upper two head blocks score copies of heads
-// 0..63 and are never stored (the kernel is bound by its per-tile gather,
-// dequant and LDS work, not by the matrix cores, so the idle MFMAs cost little).
+// gfx950 sparse MLA decode for 128 or 64 query heads over the FP8 656-byte
+// token cache ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14), and the
+// dense decode that walks a block table instead of indices (step 1).  With 64
+// query heads (the H64 instances) waves 0 and 1 score the heads, waves 2 and
+// 3 only copy and stage their share of the rows, and the value contraction
+// covers two head blocks instead of four.
 //
 // One work-group of 4 waves per scheduler partition; it walks the topk slots
 // of each (request, block range) piece in tiles of 32 keys.  Wave w owns
@@ -378,7 +379,7 @@ __device__ __forceinline__ int xp_base(int lane) {
     return b;
 }
 
-template <bool FLAT, bool DENSE>
+template <bool FLAT, bool DENSE, bool H64>
 __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
@@ -387,6 +388,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     // wave-uniform values live in scalar registers; lane-derived offsets are
     // recomputed where they are used (opaque_lane) instead of being held
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // 64 query heads: waves 0 and 1 score heads 0..63; waves 2 and 3 load no Q
+    // and score nothing (they still copy and stage their share of every tile),
+    // and every wave's value contraction covers head blocks 0 and 1 only
+    const bool sc_wave = !H64 || wave < 2;
+    constexpr int HB = H64 ? 2 : 4;                            // head blocks of 32
 
     const PartPlan plan = plan_part(p, part);
     const int begin_req = plan.begin_req;
@@ -454,7 +460,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
         for (int pass = 0;; ++pass) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) O[i] = f32x16{};
+            for (int i = 0; i < 16; ++i)
+                if ((i & 3) < HB) O[i] = f32x16{};
             l_part = 0.f;
             __syncthreads();                        // LDS free (previous piece / pass done)
 
@@ -478,7 +485,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 bf16x8 ka[KAHEAD];
 #pragma unroll
                 for (int j = 0; j < KAHEAD; ++j)
-                    if (scores) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                    if (scores && sc_wave) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
                 // RoPE k-steps 32..35 of tile i+1 (lane-dependent slots)
                 auto rope_k = [&](int j) { return kb + qk_off(ln, j); };
                 if (soft && copies) tile_ids(i + 5, ln, lds0 + ring_slot(r3));
@@ -486,7 +493,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 float mx, psum = 0.f;
 #pragma unroll
                 for (int js = 0; js < 36; ++js) {
-                    if (scores) {
+                    if (scores && sc_wave) {
                         const bf16x8 cur = ka[js % KAHEAD];
                         if (js + KAHEAD < 36)
                             ka[js % KAHEAD] = __builtin_bit_cast(
@@ -516,6 +523,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         if (copies && js == 23)
                             dma16_at(rope_src(src3, ln, wave), lds0 + kb3 + ROPE_OFF + 1024u * wave, 0);
                         if (copies && js == 28) gather_tail_at(src3, ln, raw3, 4096);
+                    }
+                    if (soft && sc_wave) {
                         if (js == 1 && vm != 0xffffffffu) {
                             // accumulator element v holds key 8(v/4) + 4h + v%4:
                             // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
@@ -555,7 +564,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                if (scores) {
+                if (scores && sc_wave) {
                     mfma_result_fence2(Sa, Sb);
                     S_next = Sa + Sb;
                 }
@@ -581,7 +590,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 }
                 bf16x8 va, pf[4];
 #pragma unroll
-                for (int hb = 0; hb < 4; ++hb)
+                for (int hb = 0; hb < HB; ++hb)
                     pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048));
                 va = v_frag(lds, vb);
                 __builtin_amdgcn_sched_barrier(0);
@@ -592,10 +601,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     bf16x8 vn;
                     if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * NP + ((jv + 1) & 3) * 64);
 #pragma unroll
-                    for (int hb = 0; hb < 4; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
+                    for (int hb = 0; hb < HB; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
                     if (jv == 3) {
 #pragma unroll
-                        for (int hb = 0; hb < 4; ++hb)
+                        for (int hb = 0; hb < HB; ++hb)
                             pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048 + 1024));
                     }
                     if (jv + 1 < 8) va = vn;
@@ -622,7 +631,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const int ln = opaque_lane();
                 for (int t = 0; t < 4; ++t) tile_ids(t, ln, lds0 + first_slot(t));
                 tile_ids(4, ln, lds0 + ring_slot(4));
-                if (pass == 0) {
+                if (pass == 0 && sc_wave) {
                     // Q of the wave's 32 heads (with 64 query heads waves 2 and
                     // 3 take heads 0..63 again; those results are never stored)
                     // copied whole-line into LDS: region row n = head 32w + n,
@@ -655,15 +664,17 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 RowRegs r0;
                 if (!DENSE) r0 = load_rows(src, ln, wave);
                 if (pass == 0) {
-                    // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7 of
-                    // head 32w + n for k-step j
-                    if (DENSE) wait_vmcnt<0>();
-                    else wait_vmcnt<6>();
-                    const int qr = L_Q + wave * 32 * QROW + (ln & 31) * QROW + 16 * (ln >> 5);
+                    if (sc_wave) {
+                        // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7
+                        // of head 32w + n for k-step j
+                        if (DENSE) wait_vmcnt<0>();
+                        else wait_vmcnt<6>();
+                        const int qr = L_Q + wave * 32 * QROW + (ln & 31) * QROW + 16 * (ln >> 5);
 #pragma unroll
-                    for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
+                        for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
+                        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                    }
                     // every wave's reads are done before the staging reuses the area
-                    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
                     __syncthreads();
                 }
                 const uint32_t rope0 = lds0 + L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0
@@ -749,9 +760,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         const int n = lane & 31, h = lane >> 5;
         // the value MFMAs retire in order: one wait after the last (O[15])
         // covers every accumulator
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[15]));
+        constexpr int OLAST = H64 ? 13 : 15;                   // the last accumulator written
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(O[OLAST]));
 #pragma unroll
-        for (int i = 0; i < 15; ++i) asm volatile("" : "+a"(O[i]));
+        for (int i = 0; i < OLAST; ++i)
+            if ((i & 3) < HB) asm volatile("" : "+a"(O[i]));
         const float l_tot = l_part + __shfl_xor(l_part, 32);
         if (lane < 32) *(LDS_AS f32x2*)(lds + L_LM + 8 * (32 * wave + n)) = f32x2{l_tot, m_ref};
         __syncthreads();
@@ -773,8 +786,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         if (nsplit == 1) {
             uint16_t* obase = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss;
 #pragma unroll
-            for (int hb = 0; hb < 4; ++hb) {
-                if (32 * hb >= p.h_q) break;                   // 64 heads: blocks 0 and 1 only
+            for (int hb = 0; hb < HB; ++hb) {                   // 64 heads: blocks 0 and 1 only
                 uint16_t* orow = obase + (int64_t)(32 * hb + n) * p.out_sh + 128 * wave + 4 * h;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -797,7 +809,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             u32x4* dst = packed_partial(p, split, sq) + (int64_t)wave * 32 * 64 + lane;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                if (32 * (i & 3) >= p.h_q) continue;           // 64 heads: blocks 0 and 1 only
+                if ((i & 3) >= HB) continue;                   // 64 heads: blocks 0 and 1 only
                 const f32x16& o = O[i];
                 const float sc = inv[i & 3];
 #pragma unroll
@@ -949,7 +961,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
             poison ? __builtin_nanf("") : M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
 }
 
-bool g_lds_decode[2][2] = {}, g_lds_gather = false;
+bool g_lds_decode[2][2][2] = {}, g_lds_gather = false;
 
 template <typename K>
 hipError_t allow_lds_once(K k, bool& done) {
@@ -959,21 +971,27 @@ hipError_t allow_lds_once(K k, bool& done) {
     return e;
 }
 
-template <bool FLAT, bool DENSE>
+template <bool FLAT, bool DENSE, bool H64>
 hipError_t launch_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
-    hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE>, g_lds_decode[FLAT][DENSE]);
+    hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE, H64>, g_lds_decode[FLAT][DENSE][H64]);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE>), dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES, st,
-                       p);
+    hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE, H64>), dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES,
+                       st, p);
     return hipGetLastError();
+}
+template <bool FLAT, bool DENSE>
+hipError_t launch_h128_heads(const DecodeParams& p, int num_parts, hipStream_t st) {
+    return p.h_q == 64 ? launch_h128<FLAT, DENSE, true>(p, num_parts, st)
+                       : launch_h128<FLAT, DENSE, false>(p, num_parts, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
     const bool dense = p.block_table != nullptr;
-    if (p.kv_flat) return dense ? launch_h128<true, true>(p, num_parts, st) : launch_h128<true, false>(p, num_parts, st);
-    return dense ? launch_h128<false, true>(p, num_parts, st) : launch_h128<false, false>(p, num_parts, st);
+    if (p.kv_flat)
+        return dense ? launch_h128_heads<true, true>(p, num_parts, st) : launch_h128_heads<true, false>(p, num_parts, st);
+    return dense ? launch_h128_heads<false, true>(p, num_parts, st) : launch_h128_heads<false, false>(p, num_parts, st);
 }
 
 hipError_t launch_combine_packed(const DecodeParams& p, hipStream_t st) {

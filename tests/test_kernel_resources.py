@@ -69,10 +69,12 @@ def test_no_kernel_uses_scratch_or_spills(reports):
 
 def test_h128_decode_keeps_the_whole_register_file(reports):
     names = {n: r for k in reports.values() for n, r in k.items()}
-    dec = [r for n, r in names.items() if "decode_fp8_h128_kernel" in n]
-    assert len(dec) == 4                                   # flat / paged address path x sparse / dense
-    for r in dec:
-        assert r["Occupancy"] == "1" and int(r["AGPRs"]) == 256, r
+    dec = {n: r for n, r in names.items() if "decode_fp8_h128_kernel" in n}
+    assert len(dec) == 8                                   # flat / paged address x sparse / dense x 128 / 64 heads
+    for n, r in dec.items():
+        h64 = re.search(r"ILb[01]ELb[01]ELb([01])E", n).group(1) == "1"
+        # O^T for 128 dims x 128 heads fills the 256 AGPRs; with 64 heads half of it
+        assert r["Occupancy"] == "1" and int(r["AGPRs"]) >= (128 if h64 else 256), (n, r)
     for needle in ("combine_packed_kernel", "combine_kernel", "decode_kernel", "indexer_score_kernel",
                    "indexer_topk_kernel", "sched_parallel_kernel"):
         assert any(needle in n for n in names), needle
