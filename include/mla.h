@@ -287,7 +287,7 @@ typedef struct mla_indexer_args {
                                    an entry outside [0, num_pages) makes its tokens score
                                    -inf and emit id -1                                   */
     const int32_t* seq_len;     /* int32 [b]: valid tokens, clamped to [0, max_pages*64] */
-    void* scores;               /* bf16 [b, max_pages * 64]: written by
+    void* scores;               /* bf16 [b, max_pages * 64], 16-byte aligned: written by
                                    mla_indexer_scores for t < seq_len of rows with
                                    seq_len > topk, read by mla_indexer_topk              */
     int32_t* indices;           /* int32 [b, topk] output of mla_indexer_topk            */

@@ -95,8 +95,8 @@ __global__ void __launch_bounds__(IX_WAVES * 64) indexer_score_kernel(IndexerPar
     }
 }
 
-__device__ __forceinline__ uint32_t order_key(uint16_t b) {     // bf16 bits -> unsigned order
-    return (b & 0x8000u) ? (uint32_t)(~b & 0xFFFFu) : (uint32_t)(b | 0x8000u);
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {     // bf16 bits -> unsigned order
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
 }
 
 __device__ __forceinline__ int phys_id(const int32_t* pt, int t, int num_pages) {
@@ -104,38 +104,67 @@ __device__ __forceinline__ int phys_id(const int32_t* pt, int t, int num_pages) 
     return (pg >= 0 && pg < num_pages) ? pg * IX_PAGE + (t & 63) : -1;
 }
 
-// Bin i with S(i) >= target > S(i + 1), S(i) = sum of hist[j >= i]; the
-// count above the bin goes to *above.  S(0) >= target >= 1 and S(256) = 0,
-// so exactly one bin qualifies.
-__device__ void find_bin(uint32_t* hist, uint32_t* scan, uint32_t target, int* bin, uint32_t* above) {
-    const int tid = threadIdx.x;
-    if (tid < 256) scan[tid] = hist[tid];
+constexpr int TK_DIGIT1 = 12;                         // first radix digit: the top 12 bits of the key
+constexpr int TK_BINS = 1 << TK_DIGIT1;              // 4096
+constexpr int TK_CAND = 8192;                         // tokens of the threshold bin kept in LDS
+
+// Block-wide: the largest bin index i of hist[0 .. nbins) whose suffix count
+// S(i) = sum_{j >= i} hist[j] reaches `target` (S(i) >= target > S(i + 1)),
+// and S(i + 1).  nbins = 256 * g; every thread of the block calls it.
+// S(0) >= target >= 1 is required (there is such a bin).
+__device__ void find_threshold_bin(const uint32_t* hist, int nbins, uint32_t target, uint32_t* coarse,
+                                   int* bin_out, uint32_t* above_out) {
+    const int tid = threadIdx.x, g = nbins >> 8;
+    if (tid < 256) {                                  // coarse group sums, then their suffix sums
+        uint32_t sum = 0;
+        for (int j = 0; j < g; ++j) sum += hist[tid * g + j];
+        coarse[tid] = sum;
+    }
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
         uint32_t v = 0;
-        if (tid < 256 && tid + off < 256) v = scan[tid + off];
+        if (tid < 256 && tid + off < 256) v = coarse[tid + off];
         __syncthreads();
-        if (tid < 256) scan[tid] += v;
+        if (tid < 256) coarse[tid] += v;
         __syncthreads();
     }
     if (tid < 256) {
-        const uint32_t si = scan[tid], sn = tid < 255 ? scan[tid + 1] : 0u;
-        if (si >= target && sn < target) { *bin = tid; *above = sn; }
+        const uint32_t si = coarse[tid], sn = tid < 255 ? coarse[tid + 1] : 0u;
+        if (si >= target && sn < target) {            // exactly one group qualifies
+            uint32_t acc = sn;
+            int b = tid * g + g - 1;
+            for (; b > tid * g; --b) {
+                if (acc + hist[b] >= target) break;
+                acc += hist[b];
+            }
+            *bin_out = b;
+            *above_out = acc;
+        }
     }
     __syncthreads();
 }
 
-// Exact top-K of one request's bf16 scores by a two-pass 8-bit radix select
-// (section 5.5): a histogram of the high byte of the order key picks the
-// threshold bin, a histogram of the low byte inside it picks the threshold
-// key T; keys above T are all kept and the first K - #above keys equal to T
-// (in the order the threads reach them) fill the rest.  Ids are remapped
-// through the page table as they are written; rows with seq_len <= K emit
-// tokens 0 .. seq_len - 1 and -1 padding without reading scores (section 5.2).
+// Exact top-K of one request's bf16 scores (sections 4.2, 5.5), one
+// 1024-thread work-group per request, on the 16-bit order key of each score:
+//   1. a 4096-bin histogram of the key's top 12 bits (sign, exponent and three
+//      mantissa bits, so that scores of one magnitude spread over many bins and
+//      the LDS atomics rarely collide), eight scores per 16-byte load;
+//   2. the threshold bin b1: fewer than K keys lie above it, at least K at or
+//      above it;
+//   3. a second pass that emits every key above b1 at once and keeps the
+//      tokens of bin b1 in LDS (or, if there are too many, notes that);
+//   4. among those candidates, the low four bits of the key select the rest:
+//      keys above the threshold key all, equal keys up to K (any of them).
+// Ids are remapped through the page table as they are written; rows with
+// seq_len <= K emit tokens 0 .. seq_len - 1 and -1 padding without reading
+// scores (section 5.2).
 __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParams p) {
-    __shared__ uint32_t hist[256], scan[256];
+    __shared__ uint32_t hist[TK_BINS];
+    __shared__ uint32_t cand[TK_CAND];
+    __shared__ uint32_t coarse[256];
+    __shared__ uint32_t hist2[16];
     __shared__ int bin_s;
-    __shared__ uint32_t above_s, cnt_gt, cnt_eq;
+    __shared__ uint32_t above_s, cnt_out, cnt_cand, cnt_eq;
     const int r = blockIdx.x, tid = threadIdx.x, K = p.topk;
     const int len = clamp_len(p, r);
     const int32_t* pt = p.page_table + (size_t)r * p.max_pages;
@@ -145,34 +174,76 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
         return;
     }
     const uint16_t* s = p.scores + (size_t)r * p.max_pages * IX_PAGE;
+    const u32x4* s16 = (const u32x4*)s;               // rows start on 128-byte boundaries
+    const int n_chunks = (len + 7) >> 3;
 
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < TK_BINS; i += TOPK_THREADS) hist[i] = 0;
+    if (tid == 0) { cnt_out = 0; cnt_cand = 0; cnt_eq = 0; }
+    if (tid < 16) hist2[tid] = 0;
     __syncthreads();
-    for (int t = tid; t < len; t += TOPK_THREADS) atomicAdd(&hist[order_key(s[t]) >> 8], 1u);
-    __syncthreads();
-    find_bin(hist, scan, (uint32_t)K, &bin_s, &above_s);
-    const uint32_t b1 = (uint32_t)bin_s, above1 = above_s;
-
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int t = tid; t < len; t += TOPK_THREADS) {
-        const uint32_t k = order_key(s[t]);
-        if ((k >> 8) == b1) atomicAdd(&hist[k & 255u], 1u);
+    // 1. first-digit histogram
+    for (int c = tid; c < n_chunks; c += TOPK_THREADS) {
+        const u32x4 v = s16[c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 8 * c + e;
+            if (t < len) atomicAdd(&hist[order_key((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) >> 4], 1u);
+        }
     }
     __syncthreads();
-    find_bin(hist, scan, (uint32_t)K - above1, &bin_s, &above_s);
-    const uint32_t T = (b1 << 8) | (uint32_t)bin_s;
-    const uint32_t n_gt = above1 + above_s, take_eq = (uint32_t)K - n_gt;
-
-    if (tid == 0) { cnt_gt = 0; cnt_eq = 0; }
+    // 2. threshold bin
+    find_threshold_bin(hist, TK_BINS, (uint32_t)K, coarse, &bin_s, &above_s);
+    const uint32_t b1 = (uint32_t)bin_s, above1 = above_s;
+    const uint32_t in_bin = hist[b1];
+    const bool stash = in_bin <= (uint32_t)TK_CAND;
+    // 3. keys above b1 are in the top K; the tokens of bin b1 are candidates
+    for (int c = tid; c < n_chunks; c += TOPK_THREADS) {
+        const u32x4 v = s16[c];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 8 * c + e;
+            if (t >= len) continue;
+            const uint32_t k = order_key((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            if ((k >> 4) > b1) {
+                out[atomicAdd(&cnt_out, 1u)] = phys_id(pt, t, p.num_pages);
+            } else if ((k >> 4) == b1) {
+                atomicAdd(&hist2[k & 15u], 1u);
+                if (stash) cand[atomicAdd(&cnt_cand, 1u)] = (uint32_t)t;
+            }
+        }
+    }
     __syncthreads();
-    for (int t = tid; t < len; t += TOPK_THREADS) {
-        const uint32_t k = order_key(s[t]);
-        if (k > T) {
-            out[atomicAdd(&cnt_gt, 1u)] = phys_id(pt, t, p.num_pages);
+    // 4. the threshold key T inside bin b1 and the K - above1 keys taken from it
+    if (tid == 0) {
+        const uint32_t need = (uint32_t)K - above1;
+        uint32_t acc = 0;
+        int lo = 15;
+        for (; lo > 0; --lo) {
+            if (acc + hist2[lo] >= need) break;
+            acc += hist2[lo];
+        }
+        bin_s = lo;                                   // low nibble of T
+        above_s = acc;                                // keys of bin b1 above T
+    }
+    __syncthreads();
+    const uint32_t T = (b1 << 4) | (uint32_t)bin_s, n_gt = above1 + above_s, take_eq = (uint32_t)K - n_gt;
+    auto take = [&](int t, uint32_t k) {
+        if (k > T) {                                  // slots above1 .. n_gt - 1 (cnt_out stands at above1)
+            out[atomicAdd(&cnt_out, 1u)] = phys_id(pt, t, p.num_pages);
         } else if (k == T) {
             const uint32_t e = atomicAdd(&cnt_eq, 1u);
             if (e < take_eq) out[n_gt + e] = phys_id(pt, t, p.num_pages);
+        }
+    };
+    if (stash) {
+        for (uint32_t i = tid; i < in_bin; i += TOPK_THREADS) {
+            const int t = (int)cand[i];
+            take(t, order_key(s[t]));
+        }
+    } else {                                          // the bin did not fit: scan the row again
+        for (int t = tid; t < len; t += TOPK_THREADS) {
+            const uint32_t k = order_key(s[t]);
+            if ((k >> 4) == b1) take(t, k);
         }
     }
 }

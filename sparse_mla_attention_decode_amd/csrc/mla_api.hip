@@ -399,8 +399,8 @@ static int indexer_params(const mla_indexer_args* a, mla::IndexerParams* p, bool
         return fail(MLA_ERR_INVALID_ARG, "max_pages must be in [1, 2^24] (got %d)", a->max_pages);
     if (a->num_pages < 1) return fail(MLA_ERR_INVALID_ARG, "num_pages must be >= 1 (got %d)", a->num_pages);
     if (!a->page_table || !a->seq_len || !a->scores || !aligned(a->page_table, 4) || !aligned(a->seq_len, 4) ||
-        !aligned(a->scores, 2))
-        return fail(MLA_ERR_INVALID_ARG, "page_table, seq_len (4-byte) and scores (2-byte) must be aligned, non-NULL");
+        !aligned(a->scores, 16))
+        return fail(MLA_ERR_INVALID_ARG, "page_table, seq_len (4-byte) and scores (16-byte) must be aligned, non-NULL");
     if (need_scores_in) {
         if (!a->q || !a->weights || !a->kcache || !aligned(a->q, 16) || !aligned(a->kcache, 16) ||
             !aligned(a->weights, 4))

@@ -302,7 +302,7 @@ def _ix_args(**over):
     (dict(max_pages=(1 << 24) + 1), M.MLA_ERR_INVALID_ARG, True), (dict(num_pages=0), M.MLA_ERR_INVALID_ARG, True),
     (dict(page_table=None), M.MLA_ERR_INVALID_ARG, True), (dict(page_table=0x40002), M.MLA_ERR_INVALID_ARG, True),
     (dict(seq_len=None), M.MLA_ERR_INVALID_ARG, True), (dict(seq_len=0x50001), M.MLA_ERR_INVALID_ARG, True),
-    (dict(scores=None), M.MLA_ERR_INVALID_ARG, True), (dict(scores=0x60001), M.MLA_ERR_INVALID_ARG, True),
+    (dict(scores=None), M.MLA_ERR_INVALID_ARG, True), (dict(scores=0x60008), M.MLA_ERR_INVALID_ARG, True),
     (dict(q=None), M.MLA_ERR_INVALID_ARG, False), (dict(q=0x10008), M.MLA_ERR_INVALID_ARG, False),
     (dict(weights=None), M.MLA_ERR_INVALID_ARG, False), (dict(weights=0x20002), M.MLA_ERR_INVALID_ARG, False),
     (dict(kcache=None), M.MLA_ERR_INVALID_ARG, False), (dict(kcache=0x30004), M.MLA_ERR_INVALID_ARG, False),
