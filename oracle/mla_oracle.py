@@ -131,13 +131,6 @@ def token_rows(kv: np.ndarray, kv_format: int) -> np.ndarray:
     return kv
 
 
-def fetch_row(kv: np.ndarray, kv_format: int, idx: int, page_block_size: int) -> np.ndarray:
-    """Bytes of one token row, addressed as page (idx // P), offset (idx % P)."""
-    if kv_format == FMT_FP8:
-        return kv[idx // page_block_size, idx % page_block_size, 0]
-    return kv[idx]
-
-
 def num_tokens_of(kv: np.ndarray, kv_format: int) -> int:
     return kv.shape[0] * kv.shape[1] if kv_format == FMT_FP8 else kv.shape[0]
 
