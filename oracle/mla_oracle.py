@@ -43,6 +43,22 @@ primitives used; no blocking, fusion or online rescaling):
   s_q > 1 the query tokens are the last s_q positions, token j seeing
   cache_seqlens[b] - (s_q - 1 - j) of them (the pages do not spell this
   out; it is the plain reading of multi-token decode).
+* V4 / V4.1 caches (d_qk = 512) -- "FlashMLA 与 DSA：内核、流水线和正确性
+  边界" section 3.1 gives only this: the pages are struct-of-arrays (a page
+  block holds its data rows first, then its scale rows), the scale type is
+  float8_e8m0, the groups shrink to 64 (V4) and 32 (V4.1) elements, and a
+  token takes 584 (V4) or 528 (V4.1) bytes.  The sparse-decode walkthrough,
+  step 2.3, has the model type follow d_qk (576: V3.2, 512: the newer
+  model), so d_qk = 512; "FlashMLA 与 DSA" section 6.1 limits sparse decode
+  to d_qk of 512 or 576 with d_v = 512.  Readings taken (the byte counts admit
+  no other split): V4 data row = 448 e4m3 codes (dims 0..447, one scale per
+  64) then 64 little-endian bf16 values (dims 448..511, not quantised, as the
+  RoPE part of V3.2), scale row = 7 e8m0 bytes and one pad byte; V4.1 data
+  row = 512 e4m3 codes, scale row = 16 e8m0 bytes (one per 32 dims).  A page
+  of P tokens: P data rows back to back, then P scale rows.  An e8m0 byte e
+  is 2^(e - 127), 0xFF is NaN (the OCP E8M0 encoding; the pages say only
+  "pure power of two, no mantissa").  V = K (d_v = d_qk = 512: the first
+  d_v dims of K, as for V3.2).
 * split-KV combine -- walkthrough step 14.2 (split partials are normalised
   O_j and lse_j = log2(l_j) + m_j in base 2, -inf when empty) and step 16
   (max over splits, weights 2^(lse_j - max), weighted mean of the O_j);
@@ -68,6 +84,16 @@ ROW_BF16 = 2 * DQK
 
 FMT_FP8 = 0
 FMT_BF16 = 1
+FMT_V4 = 2          # 584 B per token: 448 e4m3 + 64 bf16 | 7 e8m0 + pad
+FMT_V41 = 3         # 528 B per token: 512 e4m3 | 16 e8m0
+
+DQK_MODEL1 = 512
+# struct-of-arrays formats: data bytes, scale bytes per token, e4m3 dims, dims per scale
+SOA_LAYOUT = {FMT_V4: (576, 8, 448, 64), FMT_V41: (512, 16, 512, 32)}
+
+
+def dqk_of(kv_format: int) -> int:
+    return DQK_MODEL1 if kv_format in SOA_LAYOUT else DQK
 
 
 # ----------------------------------------------------------------------------
@@ -91,6 +117,12 @@ def bf16_value(bits: np.ndarray) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     with np.errstate(invalid="ignore"):
         return b.view(np.float32).astype(np.float64)
+
+
+def e8m0_value(code: np.ndarray) -> np.ndarray:
+    """uint8 e8m0 scale bytes -> float64: 2^(e - 127), NaN for 0xFF."""
+    e = np.asarray(code, dtype=np.int64)
+    return np.where(e == 0xFF, np.nan, np.exp2(e.astype(np.float64) - 127.0))
 
 
 def f32le_value(b4: np.ndarray) -> np.ndarray:
@@ -120,6 +152,41 @@ def decode_bf16_rows(rows: np.ndarray) -> np.ndarray:
     return bf16_value(rows.view("<u2"))
 
 
+def decode_v4_rows(data: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """V4: data uint8 [..., 576], scales uint8 [..., 8] -> K float64 [..., 512]."""
+    data = np.asarray(data, dtype=np.uint8)
+    lead = data.shape[:-1]
+    sc = e8m0_value(np.asarray(scales, dtype=np.uint8)[..., :7])               # [..., 7]
+    q = e4m3fn_value(data[..., :448]).reshape(*lead, 7, 64) * sc[..., None]
+    tail = bf16_value(np.ascontiguousarray(data[..., 448:576]).view("<u2"))    # [..., 64]
+    return np.concatenate([q.reshape(*lead, 448), tail], axis=-1)
+
+
+def decode_v41_rows(data: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """V4.1: data uint8 [..., 512], scales uint8 [..., 16] -> K float64 [..., 512]."""
+    data = np.asarray(data, dtype=np.uint8)
+    lead = data.shape[:-1]
+    sc = e8m0_value(np.asarray(scales, dtype=np.uint8))                        # [..., 16]
+    q = e4m3fn_value(data).reshape(*lead, 16, 32) * sc[..., None]
+    return q.reshape(*lead, 512)
+
+
+def soa_token_bytes(kv: np.ndarray, kv_format: int, ids: np.ndarray,
+                    page_block_size: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Data and scale bytes of tokens `ids` in a struct-of-arrays cache.
+
+    kv: uint8 [num_blocks, page_stride] (page_stride >= P * bytes per token);
+    token t lives in page t // P at offset o = t % P: data row at o * data_b,
+    scale row at P * data_b + o * scale_b."""
+    data_b, scale_b, _, _ = SOA_LAYOUT[kv_format]
+    P = page_block_size
+    ids = np.asarray(ids, dtype=np.int64)
+    blk, off = ids // P, ids % P
+    d_cols = off[..., None] * data_b + np.arange(data_b)
+    s_cols = P * data_b + off[..., None] * scale_b + np.arange(scale_b)
+    return kv[blk[..., None], d_cols], kv[blk[..., None], s_cols]
+
+
 def token_rows(kv: np.ndarray, kv_format: int) -> np.ndarray:
     """View the cache as [num_tokens, row_bytes] bytes (fp8: [nb, P, 1, 656])."""
     if kv_format == FMT_FP8:
@@ -131,7 +198,9 @@ def token_rows(kv: np.ndarray, kv_format: int) -> np.ndarray:
     return kv
 
 
-def num_tokens_of(kv: np.ndarray, kv_format: int) -> int:
+def num_tokens_of(kv: np.ndarray, kv_format: int, page_block_size: int = 1) -> int:
+    if kv_format in SOA_LAYOUT:
+        return kv.shape[0] * page_block_size
     return kv.shape[0] * kv.shape[1] if kv_format == FMT_FP8 else kv.shape[0]
 
 
@@ -142,21 +211,24 @@ def slot_valid(indices: np.ndarray, num_tokens: int) -> np.ndarray:
 
 def gather_dequant(kv: np.ndarray, indices: np.ndarray, kv_format: int,
                    page_block_size: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Rows selected by `indices` [..., topk], decoded to float64 [..., topk, 576].
+    """Rows selected by `indices` [..., topk], decoded to float64
+    [..., topk, d_qk] (576, or 512 for the V4 / V4.1 caches).
 
     Empty slots give zero rows.  Returns (rows, valid_mask)."""
-    P = page_block_size if kv_format == FMT_FP8 else 1
-    n_tok = num_tokens_of(kv, kv_format)
+    P = page_block_size if kv_format != FMT_BF16 else 1
+    n_tok = num_tokens_of(kv, kv_format, P)
     idx = np.asarray(indices, dtype=np.int64)
     valid = slot_valid(idx, n_tok)
-    flat = token_rows(kv, kv_format)
     safe = np.where(valid, idx, 0)
-    if kv_format == FMT_FP8:
+    if kv_format in SOA_LAYOUT:
+        data, scales = soa_token_bytes(kv, kv_format, safe, P)
+        rows = (decode_v4_rows if kv_format == FMT_V4 else decode_v41_rows)(data, scales)
+    elif kv_format == FMT_FP8:
         # page / offset addressing (identical to flat row idx for a dense [nb, P] cache)
         raw = kv[safe // P, safe % P, 0]
         rows = decode_fp8_rows(raw)
     else:
-        rows = decode_bf16_rows(flat[safe])
+        rows = decode_bf16_rows(token_rows(kv, kv_format)[safe])
     rows = np.where(valid[..., None], rows, 0.0)
     return rows, valid
 
@@ -172,7 +244,7 @@ def logsumexp(s: np.ndarray) -> np.ndarray:
 
 def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, valid: np.ndarray,
            sm_scale: float) -> Tuple[np.ndarray, np.ndarray]:
-    """One query token.  qh [H, 576], K [n, 576], V [n, 512], valid [n].
+    """One query token.  qh [H, d_qk], K [n, d_qk], V [n, 512], valid [n].
 
     Returns out [H, 512] and natural-log lse [H] (float64); +inf / 0 when no
     slot is valid."""
@@ -202,15 +274,16 @@ def sparse_mla_decode(q_bits: np.ndarray, kv: np.ndarray, indices: np.ndarray,
                       topk_length: Optional[np.ndarray] = None):
     """Sparse MLA decode by definition.
 
-    q_bits: uint16 bf16 [b, s_q, H, 576]; kv: fp8 uint8 [nb, P, 1, 656] or
-    bf16-row bytes uint8 [s_kv, 1152]; indices int32 [b, s_q, topk];
+    q_bits: uint16 bf16 [b, s_q, H, d_qk]; kv: fp8 uint8 [nb, P, 1, 656],
+    bf16-row bytes uint8 [s_kv, 1152], or a V4 / V4.1 cache uint8
+    [nb, page_stride] (d_qk = 512); indices int32 [b, s_q, topk];
     attn_sink: float [H] (natural log) or None; topk_length: int [b] or None.
     Returns out float64 [b, s_q, H, 512] and lse float64 [b, H, s_q]
     (natural log).  With `queries`, only those (bi, sj) pairs are filled and
     the others are NaN.
     """
     b, s_q, H, d = q_bits.shape
-    assert d == DQK
+    assert d == dqk_of(kv_format)
     out = np.full((b, s_q, H, DV), np.nan)
     lse = np.full((b, H, s_q), np.nan)
     if queries is None:
