@@ -1,7 +1,8 @@
 /*
  * mla.h -- C ABI of libmla, a gfx950 (MI355X) sparse MLA attention decode
  * library for DeepSeek-V3.2-shaped attention: h_q query heads (64 or 128)
- * share one compressed KV head, d_qk = 576 (512 NoPE + 64 RoPE), d_v = 512.
+ * share one compressed KV head, d_qk = 576 (512 NoPE + 64 RoPE), d_v = 512;
+ * and for the V4 / V4.1 caches, d_qk = d_v = 512.
  *
  * Operation (reference semantics: "FlashMLA 与 DSA：内核、流水线和正确性边界",
  * section 4.3; call shapes: "FlashMLA Sparse Decode 完整计算过程详解", steps 1,
@@ -9,7 +10,7 @@
  *   for every query token (b, s) and head h, over the topk slots k with
  *   t = indices[b, s, k]:
  *     slot k is valid iff 0 <= t < num_kv_tokens  (-1 marks an empty slot);
- *     K_t = dequantised token row t (576 values), V_t = K_t[0:512];
+ *     K_t = dequantised token row t (d_qk values), V_t = K_t[0:512];
  *     score_k = sm_scale * <q[b,s,h,:], K_t>        (-inf when invalid)
  *     lse[b,h,s] = ln sum_k exp(score_k)            (+inf when no slot is valid)
  *     out[b,s,h,:] = sum_k exp(score_k - lse) V_t   (0 when no slot is valid)
@@ -22,8 +23,27 @@
  *                   bf16 RoPE values ("FlashMLA Sparse Decode 完整计算过程详解",
  *                   steps 2.2 and 4.3).  Token t lives in page t / P at offset
  *                   t % P (step 7.2); NoPE dequant is code * scale (step 7.4).
+ *                   The scales must be powers of two, as the walkthrough's
+ *                   quantisation makes them (step 4.2): the GPU conversion
+ *                   uses only a scale's exponent (sign and mantissa ignored).
  *   MLA_KV_BF16_576 flat cache [s_kv, 576] bf16 with logical indices (the
  *                   sparse-prefill contract of "FlashMLA 与 DSA", section 4.0).
+ *   MLA_KV_V4_584,  paged struct-of-arrays caches with d_qk = 512 ("FlashMLA
+ *   MLA_KV_V41_528  与 DSA" section 3.1: a page holds its data rows, then its
+ *                   scale rows; e8m0 scales; 584 / 528 bytes per token;
+ *                   walkthrough step 2.3: d_qk 512 selects these models).
+ *                   Page n starts at kv + n * kv_stride_block; with P tokens
+ *                   per page, token t = n P + o has its data row at page +
+ *                   o * D and its scale row at page + P * D + o * S.
+ *                   V4:   D = 576: 448 e4m3fn codes (dims 0..447), then 64
+ *                         little-endian bf16 values (dims 448..511); S = 8:
+ *                         7 e8m0 scales (dims 64 g .. 64 g + 63), 1 pad byte.
+ *                   V4.1: D = 512 e4m3fn codes; S = 16 e8m0 scales (dims
+ *                         32 g .. 32 g + 31).
+ *                   An e8m0 byte e is 2^(e - 127) (0xFF: NaN); dequant is
+ *                   code * scale; V = K.  The split of each token into codes,
+ *                   bf16 values and scales is the one the byte counts allow
+ *                   (the pages give only the counts and the group sizes).
  *
  * Work split (step 3 of the walkthrough): the topk list of every request is cut
  * into blocks of split_granularity slots; a greedy left-to-right plan assigns
@@ -72,6 +92,8 @@ extern "C" {
 /* KV cache formats */
 #define MLA_KV_FP8_656   0
 #define MLA_KV_BF16_576  1
+#define MLA_KV_V4_584    2
+#define MLA_KV_V41_528   3
 
 /* Problem shape.  All fields are plain host values. */
 typedef struct mla_shape {
@@ -79,12 +101,14 @@ typedef struct mla_shape {
     int32_t s_q;               /* query tokens per request, >= 1                       */
     int32_t h_q;               /* query heads: 64 or 128                                */
     int32_t h_kv;              /* KV heads: must be 1                                   */
-    int32_t d_qk;              /* must be 576                                           */
+    int32_t d_qk;              /* 576; 512 for MLA_KV_V4_584 and MLA_KV_V41_528         */
     int32_t d_v;               /* must be 512                                           */
     int32_t topk;              /* slots per query token, >= 1                           */
-    int32_t page_block_size;   /* FP8: tokens per page (>= 1); BF16: ignored (use 1)    */
-    int64_t num_kv_tokens;     /* FP8: num_blocks * page_block_size; BF16: s_kv; >= 1   */
-    int32_t kv_format;         /* MLA_KV_FP8_656 or MLA_KV_BF16_576                     */
+    int32_t page_block_size;   /* paged formats: tokens per page (>= 1); BF16: ignored
+                                  (use 1)                                                */
+    int64_t num_kv_tokens;     /* paged: num_blocks * page_block_size; BF16: s_kv; >= 1 */
+    int32_t kv_format;         /* MLA_KV_FP8_656, MLA_KV_BF16_576, MLA_KV_V4_584 or
+                                  MLA_KV_V41_528                                         */
     int32_t num_parts;         /* scheduler partitions (work-groups per query-token
                                   column); 0 = derive from the current device's CU count */
     int32_t split_granularity; /* topk slots per scheduler block, a multiple of 32;
@@ -108,13 +132,17 @@ typedef struct mla_decode_args {
     mla_shape shape;
     float sm_scale;                     /* softmax scale; <= 0 means 1/sqrt(d_qk)         */
 
-    const void* q;                      /* bf16 [b, s_q, h_q, 576], last dim contiguous    */
+    const void* q;                      /* bf16 [b, s_q, h_q, d_qk], last dim contiguous   */
     int64_t q_stride_b, q_stride_s, q_stride_h;          /* in elements, multiples of 8   */
 
     const void* kv;                     /* FP8: [num_blocks, P, 1, 656] bytes (token stride
-                                           656 B); BF16: [s_kv, kv_stride_block/2] bf16     */
-    int64_t kv_stride_block;            /* FP8: bytes per page (>= P*656); BF16: bytes per
-                                           token row (>= 1152); multiple of 16              */
+                                           656 B); BF16: [s_kv, kv_stride_block/2] bf16;
+                                           V4 / V4.1: [num_blocks, kv_stride_block] bytes,
+                                           pages as described above                        */
+    int64_t kv_stride_block;            /* FP8: bytes per page (>= P*656); V4 / V4.1: bytes
+                                           per page (>= P * 584 / 528, P * that < 2^31);
+                                           BF16: bytes per token row (>= 1152); a multiple
+                                           of 16                                           */
 
     const int32_t* indices;             /* [b, s_q, topk], last dim contiguous; FP8:
                                            physical token ids, BF16: row ids; -1 = empty   */

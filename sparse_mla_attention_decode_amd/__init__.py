@@ -4,7 +4,7 @@ The compute path is the HIP library libmla.so behind the C ABI in
 include/mla.h; this package only loads it and marshals arguments.
 """
 from ._binding import (  # noqa: F401
-    MLA_KV_BF16_576, MLA_KV_FP8_656, MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
+    MLA_KV_BF16_576, MLA_KV_FP8_656, MLA_KV_V4_584, MLA_KV_V41_528, MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED,
     MLA_ERR_WORKSPACE, MLA_ERR_HIP, MLA_ERR_NO_DEVICE, EXPORTED, DecodePlan, MlaError,
     load_library, make_shape, mla_debug_gather_dequant, mla_decode_args, mla_get_sched_meta,
     mla_get_sched_meta_len, mla_plan_sched_meta_len_host, mla_indexer_args, mla_indexer_scores,

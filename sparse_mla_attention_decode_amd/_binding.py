@@ -23,6 +23,8 @@ MLA_ERR_NO_DEVICE = -5
 
 MLA_KV_FP8_656 = 0
 MLA_KV_BF16_576 = 1
+MLA_KV_V4_584 = 2
+MLA_KV_V41_528 = 3
 
 EXPORTED = ("mla_sched_meta_size", "mla_workspace_size", "mla_resolve_shape",
             "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_get_sched_meta_len",
@@ -258,8 +260,10 @@ def indexer_select(q, weights, kcache, page_table, seq_len, topk: int, scores=No
 
 def make_shape(b, s_q, h_q, topk, num_kv_tokens, kv_format=MLA_KV_FP8_656, page_block_size=64,
                num_parts=0, split_granularity=0, fixed_overhead=-1) -> mla_shape:
-    return mla_shape(b=b, s_q=s_q, h_q=h_q, h_kv=1, d_qk=576, d_v=512, topk=topk,
-                     page_block_size=page_block_size if kv_format == MLA_KV_FP8_656 else 1,
+    """d_qk follows the format: 512 for the V4 / V4.1 caches, else 576."""
+    d_qk = 512 if kv_format in (MLA_KV_V4_584, MLA_KV_V41_528) else 576
+    return mla_shape(b=b, s_q=s_q, h_q=h_q, h_kv=1, d_qk=d_qk, d_v=512, topk=topk,
+                     page_block_size=page_block_size if kv_format != MLA_KV_BF16_576 else 1,
                      num_kv_tokens=num_kv_tokens, kv_format=kv_format, num_parts=num_parts,
                      split_granularity=split_granularity, fixed_overhead=fixed_overhead)
 

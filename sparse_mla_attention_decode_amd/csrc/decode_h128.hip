@@ -39,6 +39,16 @@
 // valid key; later tiles are accumulated against it as long as no score
 // exceeds it by more than 2^64.  If one does, the piece is recomputed with the
 // true max, which gives the online-softmax result without rescaling O.
+//
+// The same kernel reads the V4 and V4.1 caches ("FlashMLA 与 DSA：内核、流水线
+// 和正确性边界" section 3.1: struct-of-arrays pages, e8m0 scales; d_qk = 512
+// per the walkthrough's step 2.3).  A page of P tokens holds P data rows, then
+// P scale rows.  V4: 576-byte data rows (448 e4m3 codes, then 64 bf16 values
+// for dims 448..511) and 8-byte scale rows (7 e8m0 bytes, one per 64 dims,
+// and a pad byte); V4.1: 512-byte data rows (512 e4m3 codes) and 16-byte
+// scale rows (one e8m0 byte per 32 dims).  Only the copies and the staging
+// differ: the staged tile holds all 512 dims of K in its NoPE rows, the score
+// contraction takes 32 k-steps instead of 36, and V = K.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,42 +62,57 @@ namespace {
 
 constexpr int NW = 4;                             // waves per work-group
 constexpr int ROWB = 656;                         // FP8 token row
-constexpr int RCH = ROWB / 16;                    // 41 16-byte chunks per row
 constexpr int WROWS = TILE / NW;                  // rows gathered and staged per wave
-constexpr int WAVE_RAW = 4 * 1024 + WROWS * 16;   // 4224: NoPE codes and scales of a wave's 8 rows
-constexpr int NDMA = 6;                           // copies per lane per tile: 4 NoPE, RoPE, scales
-constexpr int RAW_BYTES = NW * WAVE_RAW;          // 16896
 constexpr int NRAW = 2;                           // raw tiles (one being staged, one landing)
 constexpr int NKB = 3;                            // staged tiles (scores, values, being staged)
 constexpr int NP = 1040;                          // staged NoPE row pitch (1024 + 16)
-constexpr int ROPE_OFF = TILE * NP;               // 33280: RoPE rows of a staged tile
-constexpr int KBB = ROPE_OFF + TILE * 128;        // 37376
+constexpr int ROPE_OFF = TILE * NP;               // 33280: RoPE rows of a staged tile (656-byte rows)
 constexpr int IDS_SLOTS = 2;                      // token-id tiles per wave in LDS
 constexpr int ZERO_ROWS = 64;                     // rows of the zero page
 constexpr int KAHEAD = 3;                         // score fragments read ahead of their MFMAs
 constexpr int DENSE_PAGE = 64;                    // tokens per page for dense decode
+constexpr int XPB = NW * 2048;                    // P of one tile, all 128 heads
+constexpr int L_RAW = 0;
 
-// LDS map (bytes).  A staged tile is 32 NoPE rows of NP bytes (bf16 dims
-// 0..511 and a 16-byte pad that the contractions never read) and 32 RoPE rows
-// of 128 bytes copied straight from the cache, chunk c of key n in slot
-// c ^ ((n / 2) % 8) so that the score reads are conflict-free.  Row 0's pad of
-// staged buffer 0 holds the restart flags; the head statistics of the
-// epilogue use the P area.
-constexpr int XPB = NW * 2048;                          // P of one tile, all 128 heads
-constexpr int L_RAW = 0;                               // [2][4 slices][4224]: NoPE codes, scales
-constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;          // [3] x ([32][NP] bf16 NoPE, [32][128] RoPE)
-constexpr int L_XP = L_KB + NKB * KBB;                  // [4 head blocks][2 k-steps][64][16]
-constexpr int L_IDS = L_XP + XPB;                       // [4 waves][2 slots][32] int32
-constexpr int L_IDS0 = L_IDS + NW * IDS_SLOTS * 128;    // [4 waves][4 tiles][32] int32 (prologue)
-constexpr int L_BYTES = L_IDS0 + NW * 4 * 128;
-constexpr int L_FLAGS = L_KB + 1024;                    // [4] restart flags (row pad)
-constexpr int L_LM = L_XP;                              // [128 heads] {l, m} (epilogue)
-constexpr int QROW = 1168;                              // Q rows in LDS: 72 chunks + pad (prologue)
-constexpr int QCOPIES = (32 * QROW / 16 + 63) / 64;     // 37 whole-line copies per wave
-constexpr int L_Q = 0;                                  // [4 waves][32 heads][QROW] (prologue only)
-static_assert(L_BYTES <= 160 * 1024, "LDS budget");
-static_assert(L_Q + NW * 32 * QROW <= L_IDS && QCOPIES == 37 && 32 * QROW == 36 * 1024 + 32 * 16, "Q staging");
-static_assert(RCH == 41 && WAVE_RAW == 4224, "copy layout");
+// Cache formats (the kv_format values).
+constexpr int F32 = MLA_KV_FP8_656;               // 656-byte rows
+constexpr int F4 = MLA_KV_V4_584;                 // pages of 576-byte data rows, then 8-byte scale rows
+constexpr int F41 = MLA_KV_V41_528;               // pages of 512-byte data rows, then 16-byte scale rows
+
+// Per-format sizes and LDS map (bytes).  A staged tile is 32 NoPE rows of NP
+// bytes (bf16 dims 0..511 and a 16-byte pad that the contractions never read)
+// and, for 656-byte rows, 32 RoPE rows of 128 bytes copied straight from the
+// cache, chunk c of key n in slot c ^ ((n / 2) % 8) so that the score reads
+// are conflict-free.  Row 0's pad of staged buffer 0 holds the restart flags;
+// the head statistics of the epilogue use the P area.  Q passes through the
+// bottom of the LDS in the prologue only: 32 rows per wave of QCH chunks and
+// a pad chunk (conflict-free operand reads).
+template <int F>
+struct Lay {
+    static constexpr int DB = F == F32 ? 656 : F == F4 ? 576 : 512;    // data row bytes
+    static constexpr int SB = F == F32 ? 0 : F == F4 ? 8 : 16;         // scale row bytes
+    static constexpr int KSTEPS = F == F32 ? 36 : 32;                  // score k-steps of 16 dims
+    static constexpr int WAVE_RAW = F == F4 ? 5184 : 4224;             // a wave's raw slice
+    static constexpr int NDMA = F == F41 ? 5 : 6;                      // copies per lane per tile
+    static constexpr int NLOAD = F == F41 ? 5 : 6;                     // row loads per lane (prologue)
+    static constexpr int RAW_BYTES = NW * WAVE_RAW;
+    static constexpr int KBB = F == F32 ? ROPE_OFF + TILE * 128 : TILE * NP;
+    static constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;              // [3] staged tiles
+    static constexpr int L_XP = L_KB + NKB * KBB;                      // [4 head blocks][2 k-steps][64][16]
+    static constexpr int L_IDS = L_XP + XPB;                           // [4 waves][2 slots][32] int32
+    static constexpr int L_IDS0 = L_IDS + NW * IDS_SLOTS * 128;        // [4 waves][4 tiles][32] (prologue)
+    static constexpr int L_BYTES = L_IDS0 + NW * 4 * 128;
+    static constexpr int L_FLAGS = L_KB + 1024;                        // [4] restart flags (row pad)
+    static constexpr int L_LM = L_XP;                                  // [128 heads] {l, m} (epilogue)
+    static constexpr int QCH = 2 * KSTEPS;                             // 16-byte chunks of a head's Q
+    static constexpr int QROW = 16 * (QCH + 1);
+    static constexpr int QCOPIES = (32 * QROW / 16 + 63) / 64;         // whole-line copies per wave
+    static constexpr int L_Q = 0;                                      // [4 waves][32 heads][QROW]
+    static_assert(L_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(L_Q + NW * 32 * QROW <= L_IDS && (32 * QROW / 16) % 64 == 32, "Q staging");
+};
+static_assert(Lay<F32>::WAVE_RAW == 4 * 1024 + WROWS * 16 && Lay<F32>::QCOPIES == 37, "copy layout");
+static_assert(Lay<F4>::WAVE_RAW == 5120 + WROWS * 8 && Lay<F41>::QCOPIES == 33, "copy layout");
 
 // Rows copied for empty or out-of-range slots: all zero bytes (zero codes,
 // zero scales, zero RoPE), so staged values of empty slots are zero without
@@ -96,16 +121,18 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_rows[ZERO_ROWS * ROWB];
 // The id copied for slots past the end of a piece: such slots are empty.
 __device__ int32_t g_no_id[1] = {-1};
 
-// Raw slice layout (4224 bytes): NoPE chunk c < 32 of row r at 1024 (c / 8) +
-// 128 r + 16 (c % 8); the scale chunk (32) of row r at 4096 + 16 r.  Copy
-// i < 4 of lane L moves chunk (L % 8) + 8 i of row L / 8, i.e. LDS byte
-// 1024 i + 16 L: every 8 lanes read 128 contiguous bytes of one row and each
-// lane needs one row address per tile.  The RoPE copy moves the 8 RoPE chunks
-// (33..40) of every row into the staged tile; the scale copy moves chunk 32
-// of row L with lanes 0..7.
-__device__ __forceinline__ int raw_off(int row, int chunk) {
-    return chunk < 32 ? 1024 * (chunk >> 3) + 128 * row + 16 * (chunk & 7) : 4096 + 16 * row;
-}
+// Raw slice layout (656-byte rows, 4224 bytes): NoPE chunk c < 32 of row r at
+// 1024 (c / 8) + 128 r + 16 (c % 8); the scale chunk (32) of row r at
+// 4096 + 16 r.  Copy i < 4 of lane L moves chunk (L % 8) + 8 i of row L / 8,
+// i.e. LDS byte 1024 i + 16 L: every 8 lanes read 128 contiguous bytes of one
+// row and each lane needs one row address per tile.  The RoPE copy moves the
+// 8 RoPE chunks (33..40) of every row into the staged tile; the scale copy
+// moves chunk 32 of row L with lanes 0..7.
+//   V4.1 (4224 bytes): the same, with the 16-byte scale row of row L in place
+// of chunk 32.  V4 (5184 bytes): code chunks 0..27 as above (copy 3 by lanes
+// with L % 8 < 4 only), bf16 chunk j (data chunk 28 + j) of row r at
+// 4096 + 128 r + 16 j (one copy by all lanes), and the 8-byte scale row of row
+// r at 5120 + 8 r (4-byte copies by lanes 0..15).
 // RoPE copy of lane L (row L / 8 = key 8 w + L / 8 of the tile, slot L % 8):
 // it moves RoPE chunk (L % 8) ^ ((key / 2) % 8) of its row; `src` points at
 // chunk L % 8 of the row.
@@ -163,6 +190,56 @@ __device__ __forceinline__ const uint8_t* dense_row_addr(const DecodeParams& p, 
     return (const uint8_t*)(uintptr_t)(ok ? r : z);
 }
 
+// V4 / V4.1 rows of token t when ok, else row zrow of the zero page: the
+// data row address, and the scale row as a byte offset from it (page blk at
+// blk * stride, its data rows from the page start, its scale rows from
+// soa_scale_off = P * data row bytes; offsets inside a page are below 2^31,
+// checked on the host).  A 32-bit offset instead of a second address keeps
+// one register per lane across the tile loop.
+template <int F>
+__device__ __forceinline__ const uint8_t* soa_row(const DecodeParams& p, int t, bool ok, int zrow, int& sdel) {
+    const uint32_t tt = ok ? (uint32_t)t : 0u;
+    const uint32_t blk = (__umulhi(tt, p.page_magic) + tt) >> p.page_mshift;
+    const uint32_t off = tt - blk * (uint32_t)p.page_block_size;
+    const uint64_t d = (uint64_t)(uintptr_t)p.kv + (uint64_t)blk * (uint64_t)p.kv_block_stride +
+                       off * (uint32_t)Lay<F>::DB;
+    const uint64_t z = (uint64_t)(uintptr_t)g_zero_rows + (uint32_t)zrow * Lay<F>::DB;
+    // scale row - data row: P D + o S - o D (zero page: z S - z D)
+    sdel = (ok ? (int)p.soa_scale_off : 0) - (int)(ok ? off : (uint32_t)zrow) * (Lay<F>::DB - Lay<F>::SB);
+    return (const uint8_t*)(uintptr_t)(ok ? d : z);
+}
+// Source of this lane's scale copy: V4.1 lanes 0..7 copy the scale row of row
+// L, V4 lanes 0..15 dword L % 2 of the scale row of row L / 2.  `src` and
+// `sdel` are the lanes' own (row L / 8: chunk L % 8 of the data row, scale
+// offset); the row's values come from lane 8 r.
+template <int F>
+__device__ __forceinline__ const uint8_t* scale_src(const uint8_t* src, int sdel, int lane) {
+    const int from = 8 * (F == F41 ? (lane & 7) : ((lane >> 1) & 7));
+    const uint64_t a = (uint64_t)(uintptr_t)(src - 16 * (lane & 7));
+    const uint64_t r = ((uint64_t)(uint32_t)__shfl((uint32_t)(a >> 32), from) << 32) |
+                       (uint32_t)__shfl((uint32_t)a, from);
+    const int del = __shfl(sdel, from);
+    return (const uint8_t*)(uintptr_t)(r + (int64_t)del) + (F == F4 ? 4 * (lane & 1) : 0);
+}
+// The copies of a tile from V4 / V4.1 rows; `src` points at chunk lane % 8 of
+// the lane's data row, `sdel` is its scale offset.
+template <int F>
+__device__ __forceinline__ void gather_soa(const uint8_t* src, int sdel, int lane, uint32_t slice) {
+    const uint32_t sl = __builtin_amdgcn_readfirstlane(slice);
+    const uint8_t* ssrc = scale_src<F>(src, sdel, lane);
+    if constexpr (F == F41) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(src + 128 * i, sl + 1024u * i);
+        if (lane < 8) dma16(ssrc, sl + 4096u);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) dma16(src + 128 * i, sl + 1024u * i);
+        if ((lane & 7) < 4) dma16(src + 384, sl + 3072u);
+        dma16(src + 448, sl + 4096u);
+        if (lane < 16) dma4(ssrc, sl + 5120u);
+    }
+}
+
 // Copies of this wave's 8 rows of a tile into its raw slice; `src` points at
 // chunk lane % 8 of row lane / 8 (key 8w + lane / 8).
 __device__ __forceinline__ const uint8_t* tail_src(const uint8_t* src, int lane) {
@@ -191,6 +268,14 @@ __device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, int wa
         dma16(src + 128 * i, __builtin_amdgcn_readfirstlane(slice + 1024u * i));
     dma16(rope_src(src, lane, wave), __builtin_amdgcn_readfirstlane(rope_dst));
     gather_tail(src, lane, slice);
+}
+// The copies of a tile in any format (rope_dst: 656-byte rows only; sdel:
+// V4 / V4.1 only).
+template <int F>
+__device__ __forceinline__ void gather_tile(const uint8_t* src, int sdel, int lane, int wave, uint32_t slice,
+                                            uint32_t rope_dst) {
+    if constexpr (F == F32) gather_rows(src, lane, wave, slice, rope_dst);
+    else gather_soa<F>(src, sdel, lane, slice);
 }
 
 // Copy the 32 token ids of a tile into an id slot; slots past the end of the
@@ -222,30 +307,74 @@ __device__ __forceinline__ void copy_pages(const int32_t* bt_row, int k_lo, int 
 
 
 // Staging of this wave's 8 rows.  Lane L holds NoPE chunks (L % 8) + 8 i of
-// row r = L / 8 (copies i = 0..3: dims 16 c .. 16 c + 15, scale group i) and
-// the row's four scales: dequantised into 32 bytes of the staged NoPE row.
-// Split into the LDS reads and the conversion + writes, so a caller can put
-// other work between them.  (The RoPE chunks were copied into the staged tile
-// directly.)
+// row r = L / 8 (copies i = 0..3: dims 16 c .. 16 c + 15) and each chunk's
+// scale: dequantised into 32 bytes of the staged NoPE row.  656-byte rows:
+// chunk i has fp32 scale i; V4.1: e8m0 byte c / 2 of the row's scale row;
+// V4: e8m0 byte c / 4, chunk 3 only in lanes with L % 8 < 4, and the lane's
+// bf16 chunk (dims 448 + 8 (L % 8) ..) copied into the row unchanged.  Split
+// into the LDS reads and the conversion + writes, so a caller can put other
+// work between them.  (656-byte rows: the RoPE chunks were copied into the
+// staged tile directly.)
 struct StageRegs {
     u32x4 w[4];
     float sc[4];
+    u32x4 rope;
 };
+// e8m0 byte `byte` of `word` as the conversion's scale operand.  The scaled
+// conversions take only the exponent field of their f32 scale, so the float
+// with exponent bits e is exactly 2^(e - 127) for every byte, 0 included,
+// and NaN for 0xFF: the e8m0 values.
+__device__ __forceinline__ float e8m0_scale(uint32_t word, int byte) {
+    return __uint_as_float(((word >> (8 * byte)) & 0xffu) << 23);
+}
+// Scales of a lane's four chunks from its row's scale bytes (V4.1: 4 words,
+// V4: 2 words).
+template <int F>
+__device__ __forceinline__ void soa_scales(StageRegs& g, const uint32_t* words, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (F == F41) {
+            g.sc[i] = e8m0_scale(words[i], (lane & 7) >> 1);
+        } else {
+            const int grp = ((lane & 7) >> 2) + 2 * i;          // 7 in lanes without a chunk 3: the pad
+            g.sc[i] = e8m0_scale(words[grp >> 2], grp & 3);
+        }
+    }
+}
+// V4: the bf16 chunk of the lane (read late in the tile loop, when the
+// registers of chunks 0..2 are free).
+__device__ __forceinline__ u32x4 stage_load_tail(const LDS_AS uint8_t* lds, int slice, int lane) {
+    return lds_read16(lds, slice + 4096 + 16 * lane);
+}
+// TAIL: V4 reads its bf16 chunk here too (otherwise stage_load_tail does)
+template <int F, bool TAIL = true>
 __device__ __forceinline__ StageRegs stage_load(const LDS_AS uint8_t* lds, int slice, int lane) {
     const int r = lane >> 3;
     StageRegs g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        g.w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
-        g.sc[i] = *(const LDS_AS float*)(lds + slice + raw_off(r, 32) + 4 * i);
+    for (int i = 0; i < 4; ++i) g.w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
+    if constexpr (F == F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g.sc[i] = *(const LDS_AS float*)(lds + slice + 4096 + 16 * r + 4 * i);
+    } else if constexpr (F == F41) {
+        const u32x4 sw = lds_read16(lds, slice + 4096 + 16 * r);
+        const uint32_t words[4] = {sw[0], sw[1], sw[2], sw[3]};
+        soa_scales<F>(g, words, lane);
+    } else {
+        if (TAIL) g.rope = stage_load_tail(lds, slice, lane);
+        const u32x2 sw = *(const LDS_AS u32x2*)(lds + slice + 5120 + 8 * r);
+        const uint32_t words[2] = {sw[0], sw[1]};
+        soa_scales<F>(g, words, lane);
     }
     return g;
 }
 // Chunk I of this wave's staging share converted and written at once (the
 // target buffer is free): dims 16 (c0 + 8 I) .. +15 of row 8 wave + r.
-template <int I>
+template <int I, int F = F32>
 __device__ __forceinline__ void stage_chunk(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
     const int r = lane >> 3, c0 = lane & 7;
+    // V4 has 28 code chunks: in lanes with c0 >= 4 chunk 3 holds bf16 values,
+    // whose conversion lands on dims 448.. and is overwritten by stage_tail
     const u32x4 w = g.w[I];
     const float sc = g.sc[I];
     const u32x4 lo = {dequant2<false>(w[0], sc), dequant2<true>(w[0], sc),
@@ -256,60 +385,106 @@ __device__ __forceinline__ void stage_chunk(LDS_AS uint8_t* lds, const StageRegs
     lds_write16(lds, off, lo);
     lds_write16(lds, off + 16, hi);
 }
-__device__ __forceinline__ void stage_store(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
-    stage_chunk<0>(lds, g, kb, wave, lane);
-    stage_chunk<1>(lds, g, kb, wave, lane);
-    stage_chunk<2>(lds, g, kb, wave, lane);
-    stage_chunk<3>(lds, g, kb, wave, lane);
+// V4: the lane's bf16 chunk into dims 448 + 8 (L % 8) .. of its row.
+template <int F>
+__device__ __forceinline__ void stage_tail(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
+    if constexpr (F == F4) lds_write16(lds, kb + (WROWS * wave + (lane >> 3)) * NP + 896 + 16 * (lane & 7), g.rope);
 }
+template <int F>
+__device__ __forceinline__ void stage_store(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
+    stage_chunk<0, F>(lds, g, kb, wave, lane);
+    stage_chunk<1, F>(lds, g, kb, wave, lane);
+    stage_chunk<2, F>(lds, g, kb, wave, lane);
+    stage_chunk<3, F>(lds, g, kb, wave, lane);
+    stage_tail<F>(lds, g, kb, wave, lane);
+}
+template <int F>
 __device__ __forceinline__ void stage_rows(LDS_AS uint8_t* lds, int slice, int kb, int wave, int lane) {
-    stage_store(lds, stage_load(lds, slice, lane), kb, wave, lane);
+    stage_store<F>(lds, stage_load<F>(lds, slice, lane), kb, wave, lane);
 }
 
 // The rows of a tile loaded into registers instead of copied into a raw
-// slot (the first two tiles of a pass, while Q still fills the LDS): lane L
-// holds NoPE chunks (L % 8) + 8 i of its row (key 8 w + L / 8), the row's
-// four scales and the RoPE chunk it places in slot L % 8.  Loaded with
-// inline asm so the compiler neither counts nor waits for them: rows_wait
-// waits for every load in flight with the registers tied to the wait.
+// slot (the first tile of a pass, while Q still fills the LDS): lane L
+// holds NoPE chunks (L % 8) + 8 i of its row (key 8 w + L / 8) and its
+// scales; 656-byte rows: the row's four scales and the RoPE chunk it places
+// in slot L % 8; V4.1: the 16-byte scale row; V4: the 8-byte scale row and
+// bf16 chunk L % 8 (copy 3 of lanes with L % 8 >= 4 loads bf16 chunks that
+// are not used).  Loaded with inline asm so the compiler neither counts nor
+// waits for them: rows_wait waits for every load in flight with the
+// registers tied to the wait.
 struct RowRegs {
     u32x4 nope[4];
     u32x4 scales;
     u32x4 rope;
+    u32x2 sc8;
 };
 __device__ __forceinline__ u32x4 gload16(const uint8_t* src) {
     u32x4 v;
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(src) : "memory");
     return v;
 }
-// `src` points at chunk lane % 8 of the lane's row, as for gather_rows
-__device__ __forceinline__ RowRegs load_rows(const uint8_t* src, int lane, int wave) {
+__device__ __forceinline__ u32x2 gload8(const uint8_t* src) {
+    u32x2 v;
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(src) : "memory");
+    return v;
+}
+// `src` points at chunk lane % 8 of the lane's row, as for gather_rows;
+// `sdel` (V4 / V4.1) is the row's scale offset
+template <int F>
+__device__ __forceinline__ RowRegs load_rows(const uint8_t* src, int sdel, int lane, int wave) {
+    const uint8_t* sown = src - 16 * (lane & 7) + sdel;
     RowRegs r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.nope[i] = gload16(src + 128 * i);
-    r.scales = gload16(src - 16 * (lane & 7) + 512);
-    r.rope = gload16(rope_src(src, lane, wave));
+    if constexpr (F == F32) {
+        r.scales = gload16(src - 16 * (lane & 7) + 512);
+        r.rope = gload16(rope_src(src, lane, wave));
+    } else if constexpr (F == F41) {
+        r.scales = gload16(sown);
+    } else {
+        r.rope = gload16(src + 448);
+        r.sc8 = gload8(sown);
+    }
     return r;
 }
 // Wait until at most N memory operations newer than the loads of `a` are in
 // flight (so `a` has landed), with its registers tied to the wait.
-template <int N>
+template <int N, int F>
 __device__ __forceinline__ void rows_wait(RowRegs& a) {
-    asm volatile("s_waitcnt vmcnt(%6)"
-                 : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.nope[2]), "+v"(a.nope[3]), "+v"(a.scales), "+v"(a.rope)
-                 : "n"(N) : "memory");
+    if constexpr (F == F32)
+        asm volatile("s_waitcnt vmcnt(%6)"
+                     : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.nope[2]), "+v"(a.nope[3]), "+v"(a.scales), "+v"(a.rope)
+                     : "n"(N) : "memory");
+    else if constexpr (F == F41)
+        asm volatile("s_waitcnt vmcnt(%5)"
+                     : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.nope[2]), "+v"(a.nope[3]), "+v"(a.scales)
+                     : "n"(N) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(%6)"
+                     : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.nope[2]), "+v"(a.nope[3]), "+v"(a.rope), "+v"(a.sc8)
+                     : "n"(N) : "memory");
 }
 // Staging of a tile from registers into the K buffer at kb: the NoPE chunks
-// dequantised as in stage_chunk, the RoPE chunk written to its slot.
+// dequantised as in stage_chunk, the RoPE chunk (656-byte rows) written to
+// its slot, the bf16 chunk (V4) into its row.
+template <int F>
 __device__ __forceinline__ void stage_from_regs(LDS_AS uint8_t* lds, const RowRegs& r, int kb, int wave, int lane) {
     StageRegs g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        g.w[i] = r.nope[i];
-        g.sc[i] = __uint_as_float(r.scales[i]);
+    for (int i = 0; i < 4; ++i) g.w[i] = r.nope[i];
+    if constexpr (F == F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g.sc[i] = __uint_as_float(r.scales[i]);
+    } else if constexpr (F == F41) {
+        const uint32_t words[4] = {r.scales[0], r.scales[1], r.scales[2], r.scales[3]};
+        soa_scales<F>(g, words, lane);
+    } else {
+        g.rope = r.rope;
+        const uint32_t words[2] = {r.sc8[0], r.sc8[1]};
+        soa_scales<F>(g, words, lane);
     }
-    stage_store(lds, g, kb, wave, lane);
-    lds_write16(lds, kb + ROPE_OFF + 1024 * wave + 16 * lane, r.rope);
+    stage_store<F>(lds, g, kb, wave, lane);
+    if constexpr (F == F32) lds_write16(lds, kb + ROPE_OFF + 1024 * wave + 16 * lane, r.rope);
 }
 
 // Value operand (V^T fragment) of the transposing LDS read, 32 dims x 16 keys
@@ -373,14 +548,18 @@ __device__ __forceinline__ int opaque_lane() {
 // This lane's 16 bytes in the P area (head block 0, k-step 0), opaque so
 // that head-block and k-step offsets fold into the LDS instructions'
 // immediate offsets (the area lies above 64 KB).
+template <int F>
 __device__ __forceinline__ int xp_base(int lane) {
-    int b = L_XP + 16 * lane;
+    int b = Lay<F>::L_XP + 16 * lane;
     asm volatile("" : "+v"(b));
     return b;
 }
 
-template <bool FLAT, bool DENSE, bool H64>
+template <bool FLAT, bool DENSE, bool H64, int F>
 __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParams p) {
+    static_assert(F == F32 || (!FLAT && !DENSE), "V4 / V4.1: paged sparse decode only");
+    using L = Lay<F>;
+    constexpr int KSTEPS = L::KSTEPS, NDMA = L::NDMA;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
 
@@ -402,8 +581,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     if (plan.by_length && p.topk_length == nullptr) return;   // contract error: see lengths_missing
 
     const uint32_t lds0 = lds_u32(lds);
-    const int slice_off = L_RAW + wave * WAVE_RAW;            // this wave's slice in raw slot 0
-    if (wave == 0 && opaque_lane() < 4) lds[L_FLAGS + opaque_lane()] = 0;   // ordered by the first barrier
+    const int slice_off = L_RAW + wave * L::WAVE_RAW;         // this wave's slice in raw slot 0
+    if (wave == 0 && opaque_lane() < 4) lds[L::L_FLAGS + opaque_lane()] = 0;   // ordered by the first barrier
 
     for (int req = begin_req; req <= end_req; ++req) {
         const int blk_lo = req == begin_req ? begin_block : 0;
@@ -427,8 +606,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 
         // LDS slots of this wave's token ids: tile t in the ring (t % 2), the
         // first four tiles of a pass in the prologue area
-        auto ring_slot = [&](int tile) -> int { return L_IDS + (wave * IDS_SLOTS + (tile & 1)) * 128; };
-        auto first_slot = [&](int tile) -> int { return L_IDS0 + wave * 512 + tile * 128; };
+        auto ring_slot = [&](int tile) -> int { return L::L_IDS + (wave * IDS_SLOTS + (tile & 1)) * 128; };
+        auto first_slot = [&](int tile) -> int { return L::L_IDS0 + wave * 512 + tile * 128; };
         // ids that this lane needs from a slot: key ln % 32 (validity mask) and
         // key 8w + ln / 8 (its copy row)
         auto ids_at = [&](int slot_off, int ln) -> int2 {
@@ -436,8 +615,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             return int2{slot[ln & 31], slot[WROWS * wave + (ln >> 3)]};
         };
         // validity mask of the tile's 32 keys and the copy source of this
-        // lane's row (chunk ln % 8); tiles past the piece copy zero rows
-        auto rows_from = [&](int tile, int ln, int2 id, const uint8_t*& src) -> uint32_t {
+        // lane's row (chunk ln % 8; V4 / V4.1: and the row's scale offset in
+        // sdel); tiles past the piece copy zero rows
+        auto rows_from = [&](int tile, int ln, int2 id, const uint8_t*& src, int& sdel) -> uint32_t {
             const int kr = WROWS * wave + (ln >> 3);
             if (DENSE) {
                 // the id slot holds the tile's block-table entry (or -1): a
@@ -449,13 +629,14 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             }
             const bool ok = slot_ok(p, id.x, true);
             const bool okr = slot_ok(p, id.y, true);
-            src = row_addr<FLAT>(p, id.y, okr, kr) + 16 * (ln & 7);
+            if constexpr (F == F32) src = row_addr<FLAT>(p, id.y, okr, kr) + 16 * (ln & 7);
+            else src = soa_row<F>(p, id.y, okr, kr, sdel) + 16 * (ln & 7);
             return (uint32_t)__ballot(ok);
         };
 
         // Q as B operands of the score contraction, loaded once per request:
         // lane (n, h) holds dims 16 j + 8 h .. +7 of head 32w + n for k-step j
-        bf16x8 qa[36];
+        bf16x8 qa[KSTEPS];
         f32x16 O[16];
         float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
         for (int pass = 0;; ++pass) {
@@ -477,10 +658,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // 1 - par for tile parity par).  With soft == false (the prologue)
             // only the scores of tile 0.
             auto part1 = [&](int i, int par, int kb, int kb3, int ln, bool soft, bool scores, bool copies,
-                             const uint8_t* src3, uint32_t vm, f32x16 S, f32x16& S_next, const StageRegs* pro_g) {
+                             const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S, f32x16& S_next,
+                             const StageRegs* pro_g) {
                 const int qk = kb + qk_off(ln, 0);      // NoPE k-steps: qk + 32 j
                 const int r3 = 1 - par;
-                const uint32_t raw3 = raw0 + r3 * RAW_BYTES;
+                const uint32_t raw3 = raw0 + r3 * L::RAW_BYTES;
                 f32x16 Sa, Sb;
                 bf16x8 ka[KAHEAD];
 #pragma unroll
@@ -492,10 +674,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 __builtin_amdgcn_sched_barrier(0);
                 float mx, psum = 0.f;
 #pragma unroll
-                for (int js = 0; js < 36; ++js) {
+                for (int js = 0; js < KSTEPS; ++js) {
                     if (scores && sc_wave) {
                         const bf16x8 cur = ka[js % KAHEAD];
-                        if (js + KAHEAD < 36)
+                        if (js + KAHEAD < KSTEPS)
                             ka[js % KAHEAD] = __builtin_bit_cast(
                                 bf16x8, lds_read16(lds, js + KAHEAD < 32 ? qk + 32 * (js + KAHEAD) : rope_k(js + KAHEAD)));
                         // two alternating accumulator chains: a score MFMA never
@@ -507,22 +689,40 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     }
                     if (pro_g != nullptr) {
                         // prologue: tile 1 staged into K buffer 1 under the scores of tile 0
-                        if (js == 4) stage_chunk<0>(lds, *pro_g, L_KB + KBB, wave, ln);
-                        if (js == 12) stage_chunk<1>(lds, *pro_g, L_KB + KBB, wave, ln);
-                        if (js == 20) stage_chunk<2>(lds, *pro_g, L_KB + KBB, wave, ln);
+                        if (js == 4) stage_chunk<0, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                        if (js == 12) stage_chunk<1, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                        if (js == 20) stage_chunk<2, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
                         if (js == 28) {
-                            stage_chunk<3>(lds, *pro_g, L_KB + KBB, wave, ln);
+                            stage_chunk<3, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                            stage_tail<F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
                         }
                     }
                     if (soft) {
                         // copies of tile i+3: NoPE chunks into the raw slot, RoPE
                         // into the staged tile it will occupy (K buffer kb3, whose
-                        // RoPE rows the scores of its previous tile no longer read)
-                        if (copies && js >= 3 && js <= 18 && js % 5 == 3)
-                            dma16_at(src3 + 128 * (js / 5), raw3, 1024 * (js / 5));
-                        if (copies && js == 23)
-                            dma16_at(rope_src(src3, ln, wave), lds0 + kb3 + ROPE_OFF + 1024u * wave, 0);
-                        if (copies && js == 28) gather_tail_at(src3, ln, raw3, 4096);
+                        // RoPE rows the scores of its previous tile no longer read);
+                        // V4 / V4.1: code chunks, bf16 chunks and scale rows into
+                        // the raw slot
+                        if (copies && js >= 3 && js <= 18 && js % 5 == 3) {
+                            if (F != F4 || js < 18) dma16_at(src3 + 128 * (js / 5), raw3, 1024 * (js / 5));
+                            else if ((ln & 7) < 4) dma16_at(src3 + 384, raw3, 3072);
+                        }
+                        if (copies && js == 23) {
+                            if constexpr (F == F32)
+                                dma16_at(rope_src(src3, ln, wave), lds0 + kb3 + ROPE_OFF + 1024u * wave, 0);
+                            if constexpr (F == F4) dma16_at(src3 + 448, raw3, 4096);
+                        }
+                        if (copies && js == 28) {
+                            if constexpr (F == F32) gather_tail_at(src3, ln, raw3, 4096);
+                            if constexpr (F == F41) {
+                                const uint8_t* ssrc3 = scale_src<F>(src3, sdel3, ln);
+                                if (ln < 8) dma16_at(ssrc3, raw3, 4096);
+                            }
+                            if constexpr (F == F4) {
+                                const uint8_t* ssrc3 = scale_src<F>(src3, sdel3, ln);
+                                if (ln < 16) dma4_at(ssrc3, raw3, 5120);
+                            }
+                        }
                     }
                     if (soft && sc_wave) {
                         if (js == 1 && vm != 0xffffffffu) {
@@ -558,9 +758,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         }
                         if (js == 24) {
                             l_part += psum;
-                            lds_write16(lds, xp_base(ln) + wave * 2048, p_fragment(S, 0));
+                            lds_write16(lds, xp_base<F>(ln) + wave * 2048, p_fragment(S, 0));
                         }
-                        if (js == 26) lds_write16(lds, xp_base(ln) + wave * 2048 + 1024, p_fragment(S, 1));
+                        if (js == 26) lds_write16(lds, xp_base<F>(ln) + wave * 2048 + 1024, p_fragment(S, 1));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -576,17 +776,17 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // i-1 is done) and the copy source of tile i+4 (id slot par).  Past
             // the piece the staged rows are zero rows.
             auto part2 = [&](int i, int par, int kbv, int kb2, int ln, bool stage, bool copies_out,
-                             const uint8_t*& src4, uint32_t& vm4) {
+                             const uint8_t*& src4, int& sdel4, uint32_t& vm4) {
                 const int vb = kbv + pv_base(ln) + 64 * 4 * wave;
-                const int xp = xp_base(ln);
-                // the copies of tile i+2 and the ids of tile i+4 have landed (7
-                // newer ops: the ids of tile i+5, the copies of tile i+3; none
-                // near the end of the piece)
+                const int xp = xp_base<F>(ln);
+                // the copies of tile i+2 and the ids of tile i+4 have landed
+                // (1 + NDMA newer ops: the ids of tile i+5, the copies of tile
+                // i+3; none near the end of the piece)
                 StageRegs g;
                 if (stage) {
-                    if (copies_out) wait_vmcnt<7>();
+                    if (copies_out) wait_vmcnt<1 + NDMA>();
                     else wait_vmcnt<0>();
-                    g = stage_load(lds, slice_off + par * RAW_BYTES, ln);
+                    g = stage_load<F, false>(lds, slice_off + par * L::RAW_BYTES, ln);
                 }
                 bf16x8 va, pf[4];
 #pragma unroll
@@ -608,12 +808,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                             pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048 + 1024));
                     }
                     if (jv + 1 < 8) va = vn;
-                    if (stage && jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4);
-                    if (stage && jv == 1) stage_chunk<0>(lds, g, kb2, wave, ln);
-                    if (stage && jv == 3) stage_chunk<1>(lds, g, kb2, wave, ln);
-                    if (stage && jv == 5) stage_chunk<2>(lds, g, kb2, wave, ln);
+                    if (stage && jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4, sdel4);
+                    if (stage && jv == 1) stage_chunk<0, F>(lds, g, kb2, wave, ln);
+                    if (stage && jv == 3) stage_chunk<1, F>(lds, g, kb2, wave, ln);
+                    if (stage && jv == 5) {
+                        stage_chunk<2, F>(lds, g, kb2, wave, ln);
+                        if constexpr (F == F4) g.rope = stage_load_tail(lds, slice_off + par * L::RAW_BYTES, ln);
+                    }
                     if (stage && jv == 7) {
-                        stage_chunk<3>(lds, g, kb2, wave, ln);
+                        stage_chunk<3, F>(lds, g, kb2, wave, ln);
+                        stage_tail<F>(lds, g, kb2, wave, ln);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -626,6 +830,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // 0; the scores of tile 0 with the staging of tile 1.
             uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles i .. i+3
             const uint8_t* src_nx;                  // this lane's copy source in tile i+3
+            int sdel_nx = 0;                        // and its scale offset (V4 / V4.1)
             f32x16 S_cur;                           // scores of tile i
             {
                 const int ln = opaque_lane();
@@ -635,63 +840,65 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     // Q of the wave's 32 heads (with 64 query heads waves 2 and
                     // 3 take heads 0..63 again; those results are never stored)
                     // copied whole-line into LDS: region row n = head 32w + n,
-                    // QROW bytes (72 chunks of Q and a pad chunk, so the
-                    // operand reads are conflict-free).  Copy m, lane l moves
-                    // region chunk 64 m + l.
+                    // QROW bytes (the QCH chunks of a head's Q and a pad chunk,
+                    // so the operand reads are conflict-free).  Copy m, lane l
+                    // moves region chunk 64 m + l.
                     const uint16_t* q_req = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss;
-                    const uint32_t qreg = lds0 + L_Q + wave * 32 * QROW;
+                    const uint32_t qreg = lds0 + L::L_Q + wave * 32 * L::QROW;
                     int n = 0, c = ln;                  // region row and chunk of copy 0
 #pragma unroll
-                    for (int m = 0; m < QCOPIES; ++m) {
+                    for (int m = 0; m < L::QCOPIES; ++m) {
                         const uint16_t* src = q_req + (int64_t)((32 * wave + n) & (p.h_q - 1)) * p.q_sh +
-                                              8 * (c < 72 ? c : 0);
-                        if (m < QCOPIES - 1 || ln < 32) dma16(src, qreg + 1024u * m);
+                                              8 * (c < L::QCH ? c : 0);
+                        if (m < L::QCOPIES - 1 || ln < 32) dma16(src, qreg + 1024u * m);
                         c += 64;
-                        if (c >= 73) { c -= 73; n += 1; }
+                        if (c >= L::QCH + 1) { c -= L::QCH + 1; n += 1; }
                     }
-                    wait_vmcnt<QCOPIES>();              // ids of tiles 0..4 (the copies of Q are newer)
+                    wait_vmcnt<L::QCOPIES>();           // ids of tiles 0..4 (the copies of Q are newer)
                 } else {
                     wait_vmcnt<0>();                    // ids of tiles 0..4
                 }
                 const uint8_t* src;
                 const uint8_t* src2;
-                vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src);
-                vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src2);
-                // sparse decode: the rows of tile 0 travel while Q lands (6
+                int sdel = 0, sdel2 = 0;
+                vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src, sdel);
+                vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src2, sdel2);
+                // sparse decode: the rows of tile 0 travel while Q lands (NLOAD
                 // loads per lane, newer than the copies of Q).  (Dense decode
                 // copies tile 0 after Q: holding these registers across the Q
                 // reads would make its paged-address instance spill.)
                 RowRegs r0;
-                if (!DENSE) r0 = load_rows(src, ln, wave);
+                if (!DENSE) r0 = load_rows<F>(src, sdel, ln, wave);
                 if (pass == 0) {
                     if (sc_wave) {
                         // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7
                         // of head 32w + n for k-step j
                         if (DENSE) wait_vmcnt<0>();
-                        else wait_vmcnt<6>();
-                        const int qr = L_Q + wave * 32 * QROW + (ln & 31) * QROW + 16 * (ln >> 5);
+                        else wait_vmcnt<L::NLOAD>();
+                        const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5);
 #pragma unroll
-                        for (int j = 0; j < 36; ++j) qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
+                        for (int j = 0; j < KSTEPS; ++j)
+                            qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
                         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
                     }
                     // every wave's reads are done before the staging reuses the area
                     __syncthreads();
                 }
-                const uint32_t rope0 = lds0 + L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0
+                const uint32_t rope0 = lds0 + L::L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0 (656-byte rows)
                 if (DENSE) gather_rows(src, ln, wave, lds0 + slice_off, rope0);
-                gather_rows(src2, ln, wave, lds0 + slice_off + RAW_BYTES, rope0 + KBB);
-                vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2);
-                vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx);
+                gather_tile<F>(src2, sdel2, ln, wave, lds0 + slice_off + L::RAW_BYTES, rope0 + L::KBB);
+                vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2, sdel2);
+                vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx, sdel_nx);
                 if (DENSE) {
                     wait_vmcnt<0>();                    // copies of tiles 0 and 1
-                    stage_rows(lds, slice_off, L_KB, wave, ln);
+                    stage_rows<F>(lds, slice_off, L::L_KB, wave, ln);
                 } else {
-                    rows_wait<NDMA>(r0);                // tile 0 (the copies of tile 1 are newer)
-                    stage_from_regs(lds, r0, L_KB, wave, ln);
+                    rows_wait<NDMA, F>(r0);             // tile 0 (the copies of tile 1 are newer)
+                    stage_from_regs<F>(lds, r0, L::L_KB, wave, ln);
                 }
                 // raw slot 0 is free (tile 0 staged from registers, or its values
                 // went through the conversions)
-                gather_rows(src2, ln, wave, lds0 + slice_off, rope0 + 2 * KBB);
+                gather_tile<F>(src2, sdel2, ln, wave, lds0 + slice_off, rope0 + 2 * L::KBB);
                 wait_vmcnt<NDMA>();                     // the wave's copies of tile 1 (tile 2's are newer)
             }
             __syncthreads();                        // tile 0 staged
@@ -699,15 +906,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // the scores of tile 0 with the staging of tile 1 (raw slot 1)
                 // between them
                 const int ln = opaque_lane();
-                const StageRegs g1 = stage_load(lds, slice_off + RAW_BYTES, ln);
+                const StageRegs g1 = stage_load<F>(lds, slice_off + L::RAW_BYTES, ln);
                 f32x16 none = {};
-                part1(-1, 1, L_KB, 0, ln, false, true, false, nullptr, 0u, none, S_cur, &g1);
+                part1(-1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
             }
             __syncthreads();                        // tile 1 staged
 
             // K buffers of the values, scores and staging of tile i (buffers
             // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
-            int kb_v = L_KB, kb_s = L_KB + KBB, kb_g = L_KB + 2 * KBB;
+            int kb_v = L::L_KB, kb_s = L::L_KB + L::KBB, kb_g = L::L_KB + 2 * L::KBB;
             // One tile; near the end of the piece the work for tiles past it is
             // left out: the copies of tile i+3 (and ids of i+5) from tile n-3 on,
             // the staging of tile i+2 from n-2 on, the scores of tile i+1 at n-1.
@@ -718,14 +925,16 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // rather than held in registers across the loop
                 const int ln = opaque_lane();
                 f32x16 S_next;
-                part1(i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, vm0, S_cur, S_next, nullptr);
+                part1(i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0, S_cur, S_next, nullptr);
                 __syncthreads();
                 const uint8_t* src4 = src_nx;
+                int sdel4 = sdel_nx;
                 uint32_t vm4 = 0u;
-                part2(i, par, kb_v, kb_g, ln, stage, copies, src4, vm4);
+                part2(i, par, kb_v, kb_g, ln, stage, copies, src4, sdel4, vm4);
                 __syncthreads();
                 S_cur = S_next;
                 src_nx = src4;
+                sdel_nx = sdel4;
                 vm0 = vm1;
                 vm1 = vm2;
                 vm2 = vm3;
@@ -743,15 +952,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             // the reference stays fixed once set, so one test of the largest
             // score max of the pass covers every tile
             const bool restart = __any(m_seen > m_ref + p.threshold);
-            if (opaque_lane() == 0) lds[L_FLAGS + wave] = restart ? 1 : 0;
+            if (opaque_lane() == 0) lds[L::L_FLAGS + wave] = restart ? 1 : 0;
             __syncthreads();
             wait_vmcnt<0>();                                    // copies still in flight (short pieces)
             // A score exceeded the reference by more than 2^threshold in some
             // wave: recompute the piece against the true max (rare).
-            const uint32_t flags = *(const LDS_AS uint32_t*)(lds + L_FLAGS);
+            const uint32_t flags = *(const LDS_AS uint32_t*)(lds + L::L_FLAGS);
             __syncthreads();
             if (flags == 0u || pass > 0) break;
-            if (wave == 0 && opaque_lane() < 4) lds[L_FLAGS + opaque_lane()] = 0;
+            if (wave == 0 && opaque_lane() < 4) lds[L::L_FLAGS + opaque_lane()] = 0;
             m_ref = m_seen;
         }
 
@@ -765,22 +974,25 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 #pragma unroll
         for (int i = 0; i < OLAST; ++i)
             if ((i & 3) < HB) asm volatile("" : "+a"(O[i]));
-        const float l_tot = l_part + __shfl_xor(l_part, 32);
-        if (lane < 32) *(LDS_AS f32x2*)(lds + L_LM + 8 * (32 * wave + n)) = f32x2{l_tot, m_ref};
+        // exp-sum over both half-waves (same head): the swap leaves a lane's
+        // own value in one result and the other half's in the other
+        const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+        const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+        if (lane < 32) *(LDS_AS f32x2*)(lds + L::L_LM + 8 * (32 * wave + n)) = f32x2{l_tot, m_ref};
         __syncthreads();
         float inv[4];
         const int first_split = split_prefix(p, req);
         const int nsplit = split_prefix(p, req + 1) - first_split;
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-            const f32x2 lm = *(const LDS_AS f32x2*)(lds + L_LM + 8 * (32 * hb + n));
+            const f32x2 lm = *(const LDS_AS f32x2*)(lds + L::L_LM + 8 * (32 * hb + n));
             // the final output of an unsplit request takes the attention sink
             // as an extra exp-sum term 2^(sink log2(e) - m) (split requests: in
             // the combine)
             float den = lm[0];
             if (nsplit == 1 && p.attn_sink != nullptr && 32 * hb + n < p.h_q)
                 den += __builtin_amdgcn_exp2f(p.attn_sink[32 * hb + n] * 1.4426950408889634f - lm[1]);
-            inv[hb] = lm[0] > 0.f ? 1.0f / den : 0.f;
+            inv[hb] = lm[0] == 0.f ? 0.f : 1.0f / den;        // a NaN sum (NaN in the cache) stays NaN
         }
         const int own_head = 32 * wave + n;
         if (nsplit == 1) {
@@ -800,7 +1012,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             }
             if (h == 0 && own_head < p.h_q)
                 p.lse[((int64_t)req * p.h_q + own_head) * p.s_q + sq] =
-                    l_tot > 0.f ? (__log2f(l_tot) + m_ref) * 0.69314718055994531f : INFINITY;
+                    l_tot == 0.f ? INFINITY : (__log2f(l_tot) + m_ref) * 0.69314718055994531f;
         } else {
             // normalised partial O/l as bf16 in the lanes' own layout (packed
             // partials, see combine_packed_kernel) and lse in base 2
@@ -819,7 +1031,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                                      pack_bf16(o[8 * half + 4] * sc, o[8 * half + 5] * sc),
                                                      pack_bf16(o[8 * half + 6] * sc, o[8 * half + 7] * sc)};
             }
-            if (h == 0 && own_head < p.h_q) p.lse_accum[row0 + own_head] = l_tot > 0.f ? __log2f(l_tot) + m_ref : -INFINITY;
+            if (h == 0 && own_head < p.h_q)
+                p.lse_accum[row0 + own_head] = l_tot == 0.f ? -INFINITY : __log2f(l_tot) + m_ref;
         }
         __syncthreads();                                       // head statistics read
     }
@@ -838,21 +1051,22 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
     const int n = lane & 31, h = lane >> 5;
     const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
     const int n_tiles = (p.topk + TILE - 1) / TILE;
+    using L = Lay<F32>;
     const uint32_t lds0 = lds_u32(lds);
-    const int slice_off = L_RAW + wave * WAVE_RAW;
-    const LDS_AS int32_t* slot = (const LDS_AS int32_t*)(lds + L_IDS + wave * IDS_SLOTS * 128);
+    const int slice_off = L_RAW + wave * L::WAVE_RAW;
+    const LDS_AS int32_t* slot = (const LDS_AS int32_t*)(lds + L::L_IDS + wave * IDS_SLOTS * 128);
     for (int it = 0; it < n_tiles; ++it) {
         __syncthreads();
-        copy_ids(idx, 0, p.topk, it, lane, lds0 + L_IDS + wave * IDS_SLOTS * 128);
+        copy_ids(idx, 0, p.topk, it, lane, lds0 + L::L_IDS + wave * IDS_SLOTS * 128);
         wait_vmcnt<0>();
         const int kr = WROWS * wave + (lane >> 3);
         const bool ok = slot_ok(p, slot[n], it * TILE + n < p.topk);
         const bool okr = slot_ok(p, slot[kr], it * TILE + kr < p.topk);
         const uint32_t vm = (uint32_t)__ballot(ok);
         gather_rows(row_addr<false>(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, wave, lds0 + slice_off,
-                    lds0 + L_KB + ROPE_OFF + 1024u * wave);
+                    lds0 + L::L_KB + ROPE_OFF + 1024u * wave);
         wait_vmcnt<0>();
-        stage_rows(lds, slice_off, L_KB, wave, lane);
+        stage_rows<F32>(lds, slice_off, L::L_KB, wave, lane);
         __syncthreads();
         const int key = it * TILE + n;
         if (wave < 2 && key < p.topk) {
@@ -860,13 +1074,13 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
             const bool kok = (vm >> n) & 1u;
             for (int j = 0; j < 18; ++j) {
                 // the score operand read of k-step 18 w + j
-                u32x4 v = lds_read16(lds, L_KB + qk_off(lane, 18 * wave + j));
+                u32x4 v = lds_read16(lds, L::L_KB + qk_off(lane, 18 * wave + j));
                 if (!kok) v = u32x4{0, 0, 0, 0};
                 *(u32x4*)(dst + 16 * j) = v;
             }
         }
         if (v_rows != nullptr && wave >= 2) {
-            const int vb = L_KB + pv_base(lane);
+            const int vb = L::L_KB + pv_base(lane);
             for (int mb = 8 * (wave - 2); mb < 8 * (wave - 1); ++mb) {
                 for (int tt = 0; tt < 2; ++tt) {
                     const u32x4 r = __builtin_bit_cast(u32x4, v_frag(lds, vb + tt * 16 * NP + mb * 64));
@@ -911,6 +1125,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     const int64_t lse_step = (int64_t)p.s_q * p.h_q;
     const int64_t kofs = (int64_t)w * 32 * 64 + (2 * (4 * j + hb)) * 64 + lane;
     float M = -INFINITY, W = 0.f;
+    bool nan_lse = false;                                    // a split saw NaN (NaN in the cache)
     f32x16 acc = {};
     for (int s0 = 0; s0 < (poison ? 0 : ns); s0 += 4) {
         float lv[4];
@@ -924,8 +1139,10 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
             raw[u][1] = src[64];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
             if (s0 + u >= ns) lv[u] = -INFINITY;
+            nan_lse |= lv[u] != lv[u];
+        }
         const float Mn = fmaxf(fmaxf(M, fmaxf(lv[0], lv[1])), fmaxf(lv[2], lv[3]));
         if (Mn == -INFINITY) continue;                     // no valid key so far
         const float keep = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M is -inf
@@ -949,7 +1166,8 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     const float den = p.attn_sink != nullptr && W > 0.f
                           ? W + __builtin_amdgcn_exp2f(p.attn_sink[head] * 1.4426950408889634f - M)
                           : W;
-    const float inv = poison ? __builtin_nanf("") : W > 0.f ? 1.0f / den : 0.f;
+    const bool nan_out = poison || nan_lse;
+    const float inv = nan_out ? __builtin_nanf("") : W > 0.f ? 1.0f / den : 0.f;
     uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh +
                      128 * w + 32 * j + 4 * h;
 #pragma unroll
@@ -958,36 +1176,41 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
                                         pack_bf16(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv)};
     if (w == 0 && j == 0 && h == 0)
         p.lse[((int64_t)req * p.h_q + head) * p.s_q + sq] =
-            poison ? __builtin_nanf("") : M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
+            nan_out ? __builtin_nanf("") : M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
 }
 
-bool g_lds_decode[2][2][2] = {}, g_lds_gather = false;
+// per instance: dynamic LDS size allowed (FLAT, DENSE, H64, format 0 / V4 / V4.1)
+bool g_lds_decode[2][2][2][3] = {}, g_lds_gather = false;
 
 template <typename K>
-hipError_t allow_lds_once(K k, bool& done) {
+hipError_t allow_lds_once(K k, bool& done, int bytes) {
     if (done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, L_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e == hipSuccess) done = true;
     return e;
 }
 
-template <bool FLAT, bool DENSE, bool H64>
+template <bool FLAT, bool DENSE, bool H64, int F>
 hipError_t launch_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
-    hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE, H64>, g_lds_decode[FLAT][DENSE][H64]);
+    constexpr int fi = F == F32 ? 0 : F == F4 ? 1 : 2;
+    hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE, H64, F>, g_lds_decode[FLAT][DENSE][H64][fi],
+                                  Lay<F>::L_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE, H64>), dim3(num_parts, p.s_q), dim3(NW * 64), L_BYTES,
-                       st, p);
+    hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE, H64, F>), dim3(num_parts, p.s_q), dim3(NW * 64),
+                       Lay<F>::L_BYTES, st, p);
     return hipGetLastError();
 }
-template <bool FLAT, bool DENSE>
+template <bool FLAT, bool DENSE, int F = F32>
 hipError_t launch_h128_heads(const DecodeParams& p, int num_parts, hipStream_t st) {
-    return p.h_q == 64 ? launch_h128<FLAT, DENSE, true>(p, num_parts, st)
-                       : launch_h128<FLAT, DENSE, false>(p, num_parts, st);
+    return p.h_q == 64 ? launch_h128<FLAT, DENSE, true, F>(p, num_parts, st)
+                       : launch_h128<FLAT, DENSE, false, F>(p, num_parts, st);
 }
 
 }  // namespace
 
-hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
+hipError_t launch_decode_fp8_h128(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
+    if (kv_format == MLA_KV_V4_584) return launch_h128_heads<false, false, F4>(p, num_parts, st);
+    if (kv_format == MLA_KV_V41_528) return launch_h128_heads<false, false, F41>(p, num_parts, st);
     const bool dense = p.block_table != nullptr;
     if (p.kv_flat)
         return dense ? launch_h128_heads<true, true>(p, num_parts, st) : launch_h128_heads<true, false>(p, num_parts, st);
@@ -1000,9 +1223,10 @@ hipError_t launch_combine_packed(const DecodeParams& p, hipStream_t st) {
 }
 
 hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows, hipStream_t st) {
-    hipError_t e = allow_lds_once(gather_fp8_h128_kernel, g_lds_gather);
+    hipError_t e = allow_lds_once(gather_fp8_h128_kernel, g_lds_gather, Lay<F32>::L_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gather_fp8_h128_kernel, dim3(p.b * p.s_q), dim3(NW * 64), L_BYTES, st, p, k_rows, v_rows);
+    hipLaunchKernelGGL(gather_fp8_h128_kernel, dim3(p.b * p.s_q), dim3(NW * 64), Lay<F32>::L_BYTES, st, p, k_rows,
+                       v_rows);
     return hipGetLastError();
 }
 

@@ -102,6 +102,10 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :: "s"(lds_addr), "v"(src) : "memory", "m0");
 }
+__device__ __forceinline__ void dma4_at(const void* src, uint32_t base, int off) {
+    asm volatile("s_add_u32 m0, %0, %2\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(base), "v"(src), "i"(off) : "memory", "m0", "scc");
+}
 
 // s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
 template <int N>

@@ -46,15 +46,18 @@ int resolve(const mla_shape* in, mla::ResolvedShape* out) {
     if (s.h_q < 1) return fail(MLA_ERR_INVALID_ARG, "h_q must be >= 1 (got %d)", s.h_q);
     if (s.h_q != 64 && s.h_q != 128) return fail(MLA_ERR_UNSUPPORTED, "h_q must be 64 or 128 (got %d)", s.h_q);
     if (s.h_kv != 1) return fail(MLA_ERR_UNSUPPORTED, "h_kv must be 1 (got %d)", s.h_kv);
-    if (s.d_qk != 576) return fail(MLA_ERR_UNSUPPORTED, "d_qk must be 576 (got %d)", s.d_qk);
-    if (s.d_v != 512) return fail(MLA_ERR_UNSUPPORTED, "d_v must be 512 (got %d)", s.d_v);
-    if (s.kv_format != MLA_KV_FP8_656 && s.kv_format != MLA_KV_BF16_576)
+    if (s.kv_format != MLA_KV_FP8_656 && s.kv_format != MLA_KV_BF16_576 && s.kv_format != MLA_KV_V4_584 &&
+        s.kv_format != MLA_KV_V41_528)
         return fail(MLA_ERR_INVALID_ARG, "unknown kv_format %d", s.kv_format);
+    const bool model1 = s.kv_format == MLA_KV_V4_584 || s.kv_format == MLA_KV_V41_528;
+    if (s.d_qk != (model1 ? 512 : 576))
+        return fail(MLA_ERR_UNSUPPORTED, "d_qk must be %d for this kv_format (got %d)", model1 ? 512 : 576, s.d_qk);
+    if (s.d_v != 512) return fail(MLA_ERR_UNSUPPORTED, "d_v must be 512 (got %d)", s.d_v);
     if (s.num_kv_tokens < 1 || s.num_kv_tokens > INT32_MAX)
         return fail(MLA_ERR_INVALID_ARG, "num_kv_tokens must be in [1, 2^31) (got %lld)",
                     (long long)s.num_kv_tokens);
     int P = 1;
-    if (s.kv_format == MLA_KV_FP8_656) {
+    if (s.kv_format != MLA_KV_BF16_576) {                    // paged formats
         P = s.page_block_size;
         if (P < 1) return fail(MLA_ERR_INVALID_ARG, "page_block_size must be >= 1 (got %d)", P);
         if (s.num_kv_tokens % P != 0)
@@ -78,9 +81,10 @@ int resolve(const mla_shape* in, mla::ResolvedShape* out) {
             (void)hipGetLastError();
             return fail(MLA_ERR_NO_DEVICE, "num_parts = 0 needs a device to read its CU count");
         }
-        // the FP8 kernel (128-head layout for 64 or 128 heads) needs all of a
-        // CU's LDS; the 64-head BF16 kernel fits two work-groups per CU
-        const int wgs_per_cu = (s.kv_format == MLA_KV_FP8_656 || s.h_q == 128) ? 1 : 2;
+        // the FP8 kernel (128-head layout for 64 or 128 heads, every FP8
+        // format) needs all of a CU's LDS; the 64-head BF16 kernel fits two
+        // work-groups per CU
+        const int wgs_per_cu = (s.kv_format != MLA_KV_BF16_576 || s.h_q == 128) ? 1 : 2;
         parts = cus * wgs_per_cu / s.s_q;
         if (parts < 1) parts = 1;
     }
@@ -129,13 +133,22 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         return fail(MLA_ERR_INVALID_ARG, "attn_sink and topk_length must be 4-byte aligned");
     if (!aligned(a->q, 16) || a->q_stride_h % 8 || a->q_stride_s % 8 || a->q_stride_b % 8)
         return fail(MLA_ERR_INVALID_ARG, "q must be 16-byte aligned with strides that are multiples of 8 elements");
-    if (a->q_stride_h < 576 && r.h_q > 1)
-        return fail(MLA_ERR_INVALID_ARG, "q_stride_h (%lld) < 576", (long long)a->q_stride_h);
+    const int d_qk = a->shape.d_qk;                          // 576, or 512 for V4 / V4.1 (resolve)
+    if (a->q_stride_h < d_qk && r.h_q > 1)
+        return fail(MLA_ERR_INVALID_ARG, "q_stride_h (%lld) < d_qk (%d)", (long long)a->q_stride_h, d_qk);
     if (!aligned(a->kv, 16) || a->kv_stride_block % 16)
         return fail(MLA_ERR_INVALID_ARG, "kv must be 16-byte aligned and kv_stride_block a multiple of 16");
     if (r.kv_format == MLA_KV_FP8_656 && a->kv_stride_block < (int64_t)r.page_block_size * 656)
         return fail(MLA_ERR_INVALID_ARG, "kv_stride_block (%lld) < page_block_size * 656",
                     (long long)a->kv_stride_block);
+    if (r.kv_format == MLA_KV_V4_584 || r.kv_format == MLA_KV_V41_528) {
+        const int64_t tok_b = r.kv_format == MLA_KV_V4_584 ? 584 : 528;
+        if ((int64_t)r.page_block_size * tok_b >= (1ll << 31))
+            return fail(MLA_ERR_INVALID_ARG, "page_block_size * %lld bytes must be below 2^31", (long long)tok_b);
+        if (a->kv_stride_block < (int64_t)r.page_block_size * tok_b)
+            return fail(MLA_ERR_INVALID_ARG, "kv_stride_block (%lld) < page_block_size * %lld",
+                        (long long)a->kv_stride_block, (long long)tok_b);
+    }
     if (r.kv_format == MLA_KV_BF16_576 && a->kv_stride_block < 1152)
         return fail(MLA_ERR_INVALID_ARG, "kv_stride_block (%lld) < 1152 bytes per bf16 row",
                     (long long)a->kv_stride_block);
@@ -154,7 +167,7 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         if (!aligned(a->o_accum, 16) || !aligned(a->lse_accum, 4))
             return fail(MLA_ERR_INVALID_ARG, "o_accum must be 16-byte aligned, lse_accum 4-byte aligned");
     }
-    float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(576.0f);
+    float sm = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt((float)d_qk);
     if (!std::isfinite(sm)) return fail(MLA_ERR_INVALID_ARG, "sm_scale must be finite");
 
     p->q = static_cast<const uint16_t*>(a->q);
@@ -197,7 +210,10 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         p->page_mshift = l;
         p->page_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - P)) / P + 1);
     }
-    p->packed_partials = r.kv_format == MLA_KV_FP8_656;
+    p->packed_partials = r.kv_format != MLA_KV_BF16_576;     // the 128-head FP8 kernel
+    p->soa_scale_off = r.kv_format == MLA_KV_V4_584    ? (uint32_t)(r.page_block_size * 576)
+                       : r.kv_format == MLA_KV_V41_528 ? (uint32_t)(r.page_block_size * 512)
+                                                       : 0u;
     p->kv_flat = r.kv_format == MLA_KV_FP8_656 && a->kv_stride_block == (int64_t)r.page_block_size * 656 &&
                  r.num_kv_tokens < (1ll << 24) && r.num_kv_tokens * 656 < (1ll << 32);
     p->block = r.block;
@@ -378,6 +394,8 @@ int mla_debug_gather_dequant(const mla_decode_args* args, void* k_rows, void* v_
     if (st != MLA_OK) return st;
     if (!k_rows || !aligned(k_rows, 16) || (v_rows && !aligned(v_rows, 2)))
         return fail(MLA_ERR_INVALID_ARG, "k_rows must be non-NULL and 16-byte aligned");
+    if (r.kv_format != MLA_KV_FP8_656 && r.kv_format != MLA_KV_BF16_576)
+        return fail(MLA_ERR_UNSUPPORTED, "the gather check covers the 656-byte and bf16 caches only");
     return hip_status(mla::launch_gather(p, r.kv_format, static_cast<uint16_t*>(k_rows),
                                          static_cast<uint16_t*>(v_rows), static_cast<hipStream_t>(stream)),
                       "gather kernel launch");

@@ -61,6 +61,7 @@ struct DecodeParams {
     uint32_t page_magic;            // t / page_block_size == (mulhi(t, page_magic) + t) >> page_mshift
     int page_mshift;                // for 0 <= t < 2^31 (round-up reciprocal)
     int packed_partials;            // split partials as packed bf16 (128-head FP8 decode)
+    uint32_t soa_scale_off;         // V4 / V4.1: byte offset of a page's scale rows (P * data row)
     int kv_flat;                    // FP8 pages back to back, n_tok < 2^24 and n_tok * 656 < 2^32:
                                     // the row of token t is kv + 656 t (32-bit offset)
     // closed-form plan (per-request cost zero): B blocks per request, total
@@ -162,7 +163,7 @@ constexpr float kRefGapLog2 = 64.0f;
 hipError_t launch_sched(const ResolvedShape& s, const int32_t* lengths, int32_t* meta, int32_t* prefix,
                         hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st);
-hipError_t launch_decode_fp8_h128(const DecodeParams& p, int num_parts, hipStream_t st);
+hipError_t launch_decode_fp8_h128(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st);
 hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows,
                                   hipStream_t st);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t st);

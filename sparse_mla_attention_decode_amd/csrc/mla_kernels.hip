@@ -582,7 +582,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
         const float den = nsplit == 1 && p.attn_sink != nullptr
                               ? l_tot + __builtin_amdgcn_exp2f(p.attn_sink[head] * 1.4426950408889634f - m_ref)
                               : l_tot;
-        const float inv = l_tot > 0.f ? 1.0f / den : 0.f;
+        const float inv = l_tot == 0.f ? 0.f : 1.0f / den;     // a NaN sum (NaN in the cache) stays NaN
         if (nsplit == 1) {
             uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss +
                              (int64_t)head * p.out_sh;
@@ -598,7 +598,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
             }
             if (h == 0)
                 p.lse[((int64_t)req * p.h_q + head) * p.s_q + sq] =
-                    l_tot > 0.f ? (__log2f(l_tot) + m_ref) * 0.69314718055994531f : INFINITY;
+                    l_tot == 0.f ? INFINITY : (__log2f(l_tot) + m_ref) * 0.69314718055994531f;
         } else {
             const int split = req == begin_req ? begin_split : first_split;
             const int64_t base = ((int64_t)split * p.s_q + sq) * p.h_q + head;
@@ -612,7 +612,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_kernel(DecodeParams p) {
                                                 O[mb][4 * g + 2] * inv, O[mb][4 * g + 3] * inv};
                 }
             }
-            if (h == 0) p.lse_accum[base] = l_tot > 0.f ? __log2f(l_tot) + m_ref : -INFINITY;
+            if (h == 0) p.lse_accum[base] = l_tot == 0.f ? -INFINITY : __log2f(l_tot) + m_ref;
         }
     }
 }
@@ -684,11 +684,15 @@ __global__ void __launch_bounds__(256) combine_kernel(DecodeParams p) {
     if (head >= p.h_q) return;
     const int first = split_prefix(p, req);
     const int ns = split_prefix(p, req + 1) - first;
-    const bool poison = lengths_missing(p);                 // contract error: NaN everywhere
+    bool poison = lengths_missing(p);                       // contract error: NaN everywhere
     if (ns <= 1 && !poison) return;
     auto lse_at = [&](int j) {
         return p.lse_accum[((int64_t)(first + j) * p.s_q + sq) * p.h_q + head];
     };
+    // a split whose lse is NaN (NaN in the cache) makes the output NaN
+    bool nan_lse = false;
+    for (int j = lane; j < (poison ? 0 : ns); j += 64) nan_lse |= lse_at(j) != lse_at(j);
+    poison = poison || __any(nan_lse);
     uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh;
     float* lse_out = p.lse + ((int64_t)req * p.h_q + head) * p.s_q + sq;
     if (poison) {
@@ -767,8 +771,8 @@ static hipError_t launch_decode_t(const DecodeParams& p, int num_parts, hipStrea
 }
 
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
-    if (kv_format == MLA_KV_FP8_656)
-        return launch_decode_fp8_h128(p, num_parts, st);
+    if (kv_format != MLA_KV_BF16_576)                  // the 656-byte, V4 and V4.1 FP8 caches
+        return launch_decode_fp8_h128(p, kv_format, num_parts, st);
     return p.h_q == 128 ? launch_decode_t<MLA_KV_BF16_576, 4>(p, num_parts, st)
                         : launch_decode_t<MLA_KV_BF16_576, 2>(p, num_parts, st);
 }
@@ -789,6 +793,7 @@ hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows,
                          hipStream_t st) {
     // the FP8 decode kernel serves 64 and 128 heads; its gather does not depend on h_q
     if (kv_format == MLA_KV_FP8_656) return launch_gather_fp8_h128(p, k_rows, v_rows, st);
+    if (kv_format != MLA_KV_BF16_576) return hipErrorNotSupported;    // checked on the host first
     return launch_gather_t<MLA_KV_BF16_576>(p, k_rows, v_rows, st);
 }
 

@@ -1,8 +1,8 @@
 """Seeded synthetic workloads for DeepSeek-V3.2-shaped sparse MLA decode.
 
 This module only *builds inputs*: random Q, a paged FP8 KV cache in the
-656-byte V3.2 token format (or a flat bf16 cache), and int32 top-k index
-lists.  It holds none of the decode arithmetic (no gather, no dequant, no
+656-byte V3.2 token format (or a flat bf16 cache, or a V4 / V4.1
+struct-of-arrays cache), and int32 top-k index lists.  It holds none of the decode arithmetic (no gather, no dequant, no
 softmax) so that the CPU oracle and the HIP path can both consume its bytes
 without sharing any of the computation they are checked on.
 
@@ -17,6 +17,12 @@ Sources for the shapes and formats (page titles as published):
   * "FlashMLA 与 DSA：内核、流水线和正确性边界", section 4.0 (sparse prefill
     takes logical indices into a flat kv[s_kv, d_qk] with no batch dim) and
     section 5.5 (logical positions are emitted through the page table).
+
+  * "FlashMLA 与 DSA" section 3.1 (V4 / V4.1: pages hold their data rows,
+    then their scale rows; e8m0 scales per 64 / 32 elements; 584 / 528 bytes
+    per token) and the walkthrough's step 2.3 (d_qk 512 for those models).
+    The V4 token is 448 e4m3 codes + 64 bf16 values | 7 scales + a zero pad
+    byte; the V4.1 token 512 e4m3 codes | 16 scales.
 
 The FP8 encoder below follows step 4.2 of the sparse-decode walkthrough:
 amax per 128-group (clamped to 1e-4 so an all-zero group still gets a finite
@@ -43,6 +49,15 @@ E4M3_MAX = 448.0
 
 KV_FP8_656 = 0
 KV_BF16_576 = 1
+KV_V4_584 = 2
+KV_V41_528 = 3
+D_QK_SOA = 512
+# struct-of-arrays formats: (data bytes, scale bytes, e4m3 dims, dims per scale)
+SOA = {KV_V4_584: (576, 8, 448, 64), KV_V41_528: (512, 16, 512, 32)}
+
+
+def d_qk_of(kv_format: int) -> int:
+    return D_QK_SOA if kv_format in SOA else D_QK
 
 BASE_SEED = 20261202
 
@@ -86,6 +101,28 @@ def encode_fp8_rows(nope: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
     return rows
 
 
+def encode_soa_tokens(x: np.ndarray, kv_format: int) -> np.ndarray:
+    """Quantise tokens x float32 [n, 512] for a V4 / V4.1 cache (step 4.2's
+    recipe with e8m0 scales: amax per group clamped to 1e-4, scale =
+    2**ceil(log2(amax / 448)), code = e4m3fn(x / scale); V4 dims 448.. as
+    bf16).  Returns uint8 [n, data bytes + scale bytes]: the data row, then
+    the scale row."""
+    db, sb, nq, grp = SOA[kv_format]
+    n = x.shape[0]
+    g = x[:, :nq].astype(np.float32).reshape(n, nq // grp, grp)
+    amax = np.maximum(np.abs(g).max(axis=-1).astype(np.float64), 1e-4)
+    m, e = np.frexp(amax / E4M3_MAX)
+    exp = np.where(m == 0.5, e - 1, e)                                     # [n, groups]
+    scaled = (g / np.ldexp(np.ones_like(amax), exp)[:, :, None]).astype(np.float32)
+    assert np.all(np.abs(scaled) <= E4M3_MAX)
+    out = np.zeros((n, db + sb), dtype=np.uint8)
+    out[:, :nq] = torch.from_numpy(scaled.reshape(n, nq)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if nq < D_QK_SOA:
+        out[:, nq:db] = to_bf16_bits(x[:, nq:]).astype("<u2").view(np.uint8).reshape(n, 2 * (D_QK_SOA - nq))
+    out[:, db:db + nq // grp] = (exp + 127).astype(np.uint8)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # workload container
 # ----------------------------------------------------------------------------
@@ -98,7 +135,7 @@ class Workload:
     h_q: int
     topk: int
     sm_scale: float
-    q_bits: np.ndarray           # uint16 [b, s_q, h_q, 576]
+    q_bits: np.ndarray           # uint16 [b, s_q, h_q, d_qk] (576; 512 for V4 / V4.1)
     indices: np.ndarray          # int32 [b, s_q, topk]
     page_block_size: int         # fp8: tokens per page; bf16: 1
     num_kv_tokens: int           # fp8: num_blocks * page_block_size; bf16: s_kv
@@ -106,18 +143,46 @@ class Workload:
     ref_rows: np.ndarray         # uint8 [n_ref, row_bytes] their bytes
     fill_byte: int = 0xFF        # bytes of unreferenced rows (0xFF = NaN codes/scales)
     meta: Optional[dict] = None
+    page_pad: int = 0            # V4 / V4.1: bytes after each page's scale rows
 
     @property
     def row_bytes(self) -> int:
+        """Bytes of one token (V4 / V4.1: data row + scale row)."""
+        if self.kv_format in SOA:
+            return sum(SOA[self.kv_format][:2])
         return FP8_ROW_BYTES if self.kv_format == KV_FP8_656 else BF16_ROW_BYTES
 
     @property
     def num_blocks(self) -> int:
         return self.num_kv_tokens // self.page_block_size
 
+    @property
+    def page_stride(self) -> int:
+        """V4 / V4.1: bytes from one page to the next (the pages' bytes and
+        page_pad, rounded up to 16: page starts are 16-byte aligned)."""
+        return (self.page_block_size * self.row_bytes + self.page_pad + 15) // 16 * 16
+
+    def _soa_views(self, kv):
+        """(data [nb, P, D], scales [nb, P, S]) views of a V4 / V4.1 cache [nb, stride]."""
+        db, sb = SOA[self.kv_format][:2]
+        P = self.page_block_size
+        return (kv[:, :P * db].unflatten(1, (P, db)) if isinstance(kv, torch.Tensor)
+                else kv[:, :P * db].reshape(-1, P, db),
+                kv[:, P * db:P * (db + sb)].unflatten(1, (P, sb)) if isinstance(kv, torch.Tensor)
+                else kv[:, P * db:P * (db + sb)].reshape(-1, P, sb))
+
     def kv_host(self) -> np.ndarray:
         """Full cache as host bytes: fp8 -> uint8 [num_blocks, P, 1, 656];
-        bf16 -> uint8 [s_kv, 1152] (row-major bf16 [s_kv, 576])."""
+        bf16 -> uint8 [s_kv, 1152] (row-major bf16 [s_kv, 576]); V4 / V4.1 ->
+        uint8 [num_blocks, page_stride] (P data rows, P scale rows, pad)."""
+        if self.kv_format in SOA:
+            db = SOA[self.kv_format][0]
+            kv = np.full((self.num_blocks, self.page_stride), self.fill_byte, dtype=np.uint8)
+            data, scales = self._soa_views(kv)
+            blk, off = self.ref_ids // self.page_block_size, self.ref_ids % self.page_block_size
+            data[blk, off] = self.ref_rows[:, :db]
+            scales[blk, off] = self.ref_rows[:, db:]
+            return kv
         flat = np.full((self.num_kv_tokens, self.row_bytes), self.fill_byte, dtype=np.uint8)
         flat[self.ref_ids] = self.ref_rows
         if self.kv_format == KV_FP8_656:
@@ -126,6 +191,17 @@ class Workload:
 
     def kv_device(self, device="cuda") -> torch.Tensor:
         """Same bytes as kv_host(), built on the device (fill + scatter of referenced rows)."""
+        if self.kv_format in SOA:
+            db = SOA[self.kv_format][0]
+            kv = torch.full((self.num_blocks, self.page_stride), self.fill_byte, dtype=torch.uint8, device=device)
+            if len(self.ref_ids):
+                data, scales = self._soa_views(kv)
+                ids = torch.from_numpy(self.ref_ids).to(device)
+                blk, off = ids // self.page_block_size, ids % self.page_block_size
+                rows = torch.from_numpy(self.ref_rows).to(device)
+                data[blk, off] = rows[:, :db]
+                scales[blk, off] = rows[:, db:]
+            return kv
         flat = torch.full((self.num_kv_tokens, self.row_bytes), self.fill_byte,
                           dtype=torch.uint8, device=device)
         if len(self.ref_ids):
@@ -144,6 +220,8 @@ class Workload:
 
 def _fill_rows(rng, ids: np.ndarray, kv_format: int) -> np.ndarray:
     n = len(ids)
+    if kv_format in SOA:
+        return encode_soa_tokens(rng.standard_normal((n, D_QK_SOA), dtype=np.float32), kv_format)
     if kv_format == KV_FP8_656:
         nope = rng.standard_normal((n, D_NOPE), dtype=np.float32)
         rope = to_bf16_bits(rng.standard_normal((n, D_ROPE), dtype=np.float32))
@@ -153,16 +231,17 @@ def _fill_rows(rng, ids: np.ndarray, kv_format: int) -> np.ndarray:
 
 
 def _finish(name, rng, kv_format, b, s_q, h_q, topk, P, num_tokens, indices, meta=None,
-            q_bits=None):
+            q_bits=None, page_pad=0):
+    dqk = d_qk_of(kv_format)
     if q_bits is None:
-        q_bits = to_bf16_bits(rng.standard_normal((b, s_q, h_q, D_QK), dtype=np.float32))
+        q_bits = to_bf16_bits(rng.standard_normal((b, s_q, h_q, dqk), dtype=np.float32))
     valid = indices[(indices >= 0) & (indices < num_tokens)]
     ref_ids = np.unique(valid.astype(np.int64))
     ref_rows = _fill_rows(rng, ref_ids, kv_format)
     return Workload(name=name, kv_format=kv_format, b=b, s_q=s_q, h_q=h_q, topk=topk,
-                    sm_scale=1.0 / np.sqrt(D_QK), q_bits=q_bits, indices=indices,
+                    sm_scale=1.0 / np.sqrt(dqk), q_bits=q_bits, indices=indices,
                     page_block_size=P, num_kv_tokens=num_tokens, ref_ids=ref_ids,
-                    ref_rows=ref_rows, meta=meta)
+                    ref_rows=ref_rows, meta=meta, page_pad=page_pad)
 
 
 def _distinct(rng, n_pool: int, k: int) -> np.ndarray:
@@ -181,8 +260,10 @@ def paged_decode(name: str, seed: int, b: int, s_q: int, h_q: int, topk: int,
                  tokens_per_seq: int, P: int = 64, shuffle_pages: bool = True,
                  short_frac: float = 0.0, short_len: int = 0,
                  recent_frac: float = 0.0, recent_window: int = 0,
-                 sort_slots: bool = False) -> Workload:
-    """Paged FP8 decode workload.
+                 sort_slots: bool = False, kv_format: int = KV_FP8_656, page_pad: int = 0) -> Workload:
+    """Paged FP8 decode workload (the 656-byte cache, or with kv_format the
+    V4 / V4.1 cache, whose pages may carry page_pad bytes after the scale
+    rows).
 
     Each sequence owns tokens_per_seq/P pages; the page table is a global
     shuffled permutation (or contiguous when shuffle_pages=False).  Each query
@@ -215,7 +296,8 @@ def paged_decode(name: str, seed: int, b: int, s_q: int, h_q: int, topk: int,
             phys = block_table[bi, pos // P] * P + pos % P
             indices[bi, sj, :n_valid] = phys
     meta = {"block_table_shape": list(block_table.shape), "short_seqs": short_seqs.tolist()}
-    return _finish(name, rng, KV_FP8_656, b, s_q, h_q, topk, P, total_pages * P, indices, meta)
+    return _finish(name, rng, kv_format, b, s_q, h_q, topk, P, total_pages * P, indices, meta,
+                   page_pad=page_pad)
 
 
 def dense_decode(name: str, seed: int, b: int, s_q: int, h_q: int, seqlens, pages_per_seq: int,

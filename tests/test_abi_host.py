@@ -413,3 +413,38 @@ def test_dense_shape_limits(kw, code):
     with pytest.raises(M.MlaError) as e:
         M.mla_dense_decode_fwd(a, 0xB000, 64, 0, stream=0)
     assert e.value.code == code, (kw, M.mla_last_error())
+
+
+# ----------------------------------------------------------------------------- V4 / V4.1 caches
+@pytest.mark.parametrize("fmt,tok_b", [(M.MLA_KV_V4_584, 584), (M.MLA_KV_V41_528, 528)])
+def test_struct_of_arrays_shapes(fmt, tok_b):
+    """The V4 / V4.1 formats take d_qk = 512 (576 is rejected), pages of P
+    tokens at kv_stride_block >= P * bytes per token with P * that below 2^31,
+    q rows of 512 elements; the gather check and dense decode do not read them."""
+    s = shape(kv_format=fmt)
+    assert s.d_qk == 512 and s.page_block_size == 64
+    assert M.mla_workspace_size(s) == M.mla_workspace_size(shape())     # same split partials
+    bad = shape(kv_format=fmt)
+    bad.d_qk = 576
+    with pytest.raises(M.MlaError) as e:
+        M.mla_workspace_size(bad)
+    assert e.value.code == M.MLA_ERR_UNSUPPORTED
+    ok = dict(kv_stride_block=64 * tok_b + (-64 * tok_b) % 16, q_stride_b=128 * 512, q_stride_s=128 * 512,
+              q_stride_h=512)
+    for over, code in [(dict(kv_stride_block=64 * tok_b - 16), M.MLA_ERR_INVALID_ARG),
+                       (dict(q_stride_h=504), M.MLA_ERR_INVALID_ARG)]:
+        a = _args(s, **{**ok, **over})
+        with pytest.raises(M.MlaError) as e:
+            M.mla_sparse_decode_fwd(a, stream=0)
+        assert e.value.code == code, (over, M.mla_last_error())
+    big = shape(kv_format=fmt, page_block_size=1 << 22, num_kv_tokens=1 << 22)
+    a = _args(big, **{**ok, "kv_stride_block": (1 << 22) * tok_b})
+    with pytest.raises(M.MlaError) as e:
+        M.mla_sparse_decode_fwd(a, stream=0)
+    assert e.value.code == M.MLA_ERR_INVALID_ARG and "2^31" in M.mla_last_error()
+    with pytest.raises(M.MlaError) as e:
+        M.mla_debug_gather_dequant(_args(s, **ok), 0xC000, 0xD000, stream=0)
+    assert e.value.code == M.MLA_ERR_UNSUPPORTED
+    with pytest.raises(M.MlaError) as e:
+        M.mla_dense_decode_fwd(_args(s, **ok, indices=None, topk_length=0xA000), 0xB000, 2, 0, stream=0)
+    assert e.value.code == M.MLA_ERR_UNSUPPORTED
