@@ -32,6 +32,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-decode query-tokens/s at b=64,h=128,topk=2048; % of MFMA/HBM roofline"
+METRIC_SOA = ("sparse-decode query-tokens/s at b=64,h=128,topk=2048 on the {} cache (d_qk 512); "
+              "% of MFMA/HBM roofline")
 METRIC_HALFHEAD = ("sparse-decode query-tokens/s at b=128,h=64,topk=2048 (13 of 128 requests hold 1500 valid "
                    "slots); % of HBM roofline")
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
@@ -90,8 +92,9 @@ def algorithmic(w):
     import numpy as np
     valid = (w.indices >= 0) & (w.indices < w.num_kv_tokens)
     n_valid = int(valid.sum())
-    flops = 2.0 * w.h_q * n_valid * (576 + 512)
-    bytes_ = (n_valid * w.row_bytes + w.b * w.s_q * w.h_q * 576 * 2 + w.b * w.s_q * w.h_q * 512 * 2
+    d_qk = w.q_bits.shape[-1]                       # 576; 512 for the V4 / V4.1 caches
+    flops = 2.0 * w.h_q * n_valid * (d_qk + 512)
+    bytes_ = (n_valid * w.row_bytes + w.b * w.s_q * w.h_q * d_qk * 2 + w.b * w.s_q * w.h_q * 512 * 2
               + w.indices.size * 4 + w.b * w.s_q * w.h_q * 4)
     return flops, float(bytes_), n_valid
 
@@ -237,11 +240,12 @@ def main():
                          "auto: closed when fixed_overhead is 0")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "halfhead", "indexer"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "halfhead", "indexer", "v4", "v41"), default="decode",
                     help="decode: the sparse MLA decode step at b=64, h=128, topk=2048 (default); "
                          "halfhead: b=128, h=64, topk=2048 over 65536-token contexts with 10%% of the "
                          "requests holding 1500 valid slots (HBM-bound); indexer: the lightning "
-                         "indexer scores + top-k that select the decode's tokens")
+                         "indexer scores + top-k that select the decode's tokens; v4 / v41: the "
+                         "decode step's shape on the V4 (584 B/token) / V4.1 (528 B/token) cache")
     ap.add_argument("--graph", action="store_true",
                     help="replay a captured HIP graph of each layer's step instead of launching "
                          "its kernels one by one")
@@ -275,18 +279,21 @@ def main():
         return
     M.load_library()
 
-    cfg = 1 if args.workload == "decode" else 2
+    cfg = 2 if args.workload == "halfhead" else 1
+    kv_format = {"v4": W.KV_V4_584, "v41": W.KV_V41_528}.get(args.workload, W.KV_FP8_656)
+    soa = kv_format != W.KV_FP8_656
+    wl_name = W.CONFIG_NAMES[cfg] + (f"_{args.workload}kv" if soa else "")
     # the 64-head workload's cache is 5.4 GB per layer: two layers already
     # exceed the 256 MB Infinity Cache many times over
     n_layers = args.layers if cfg == 1 else min(args.layers, 2)
-    print(f"[bench] building {n_layers} layers of {W.CONFIG_NAMES[cfg]}", file=sys.stderr, flush=True)
+    print(f"[bench] building {n_layers} layers of {wl_name}", file=sys.stderr, flush=True)
     layers = []
     for l in range(n_layers):
-        if l == 0:
+        if l == 0 and not soa:
             w = W.make_config(cfg)
         elif cfg == 1:
-            w = W.paged_decode(f"{W.CONFIG_NAMES[1]}_layer{l}", W.BASE_SEED + 1 + 1000 * l, b=64, s_q=1, h_q=128,
-                               topk=2048, tokens_per_seq=32768)
+            w = W.paged_decode(f"{wl_name}_layer{l}", W.BASE_SEED + 1 + 1000 * l, b=64, s_q=1, h_q=128,
+                               topk=2048, tokens_per_seq=32768, kv_format=kv_format)
         else:
             w = W.paged_decode(f"{W.CONFIG_NAMES[2]}_layer{l}", W.BASE_SEED + 2 + 1000 * l, b=128, s_q=1, h_q=64,
                                topk=2048, tokens_per_seq=65536, short_frac=0.1, short_len=1500)
@@ -367,7 +374,7 @@ def main():
     decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     flops, bytes_, n_valid = algorithmic(w0)
-    traffic, traffic_detail = measured_traffic() if cfg == 1 else (None, None)
+    traffic, traffic_detail = measured_traffic() if cfg == 1 and not soa else (None, None)
     achieved_tflops = flops / (decode_ms * 1e-3) / 1e12
     achieved_gbs = bytes_ / (decode_ms * 1e-3) / 1e9
     t_roof_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
@@ -386,13 +393,14 @@ def main():
                  "mfma_achieved_TFLOPs": achieved_tflops, "hbm_achieved_GBs": achieved_gbs})
 
     res = {
-        "metric": METRIC if cfg == 1 else METRIC_HALFHEAD, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
+        "metric": (METRIC_SOA.format({"v4": "V4", "v41": "V4.1"}[args.workload]) if soa
+                   else METRIC if cfg == 1 else METRIC_HALFHEAD), "value": value, "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "prewarm_steps": n_pre, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": W.CONFIG_NAMES[cfg], "b": w0.b, "s_q": w0.s_q, "h_q": w0.h_q,
+        "config": {"workload": wl_name, "b": w0.b, "s_q": w0.s_q, "h_q": w0.h_q,
                    "topk": w0.topk, "valid_slots": n_valid,
-                   "kv_cache": f"fp8 656 B/token, page 64, {w0.num_kv_tokens // w0.b} tokens/seq",
+                   "kv_cache": f"fp8 {w0.row_bytes} B/token, page 64, {w0.num_kv_tokens // w0.b} tokens/seq",
                    "layers_rotated": n_layers, "split_granularity": args.split_granularity,
                    "fixed_overhead": args.fixed_overhead, "num_parts": plan.shape.num_parts,
                    "step": ("decode (closed-form plan in-kernel) + combine" if closed
