@@ -54,5 +54,31 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (raises if absent)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the AddressSanitizer runtime was not found")
+    return path
+
+
+def build_sanitized(out: str) -> str:
+    """The same library with its host code under AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code is built as usual: every
+    sanitizer flag applies to the host pass only).  For host-side tests run
+    with the runtime preloaded (sanitizer_runtime)."""
+    host = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer"):
+        host += ["-Xarch_host", f]
+    flags = [f for f in compile_flags() if f != "-O3"]
+    cmd = [hipcc(), "-O1", "-g", *flags, *host, "-shared-libsan", "-shared", "-o", out, *sources()]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("sanitized libmla build failed:\n" + res.stderr[-4000:])
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
