@@ -130,3 +130,20 @@ def test_indexer_benchmark_shape():
     for r in range(64):
         msg = X.check_topk(got_idx[r], got_sc[r], int(lens[r]), 2048, pt[r], kc.shape[0])
         assert msg is None, f"row {r}: {msg}"
+
+
+def test_indexer_topk_selection_paths():
+    """Both selections of the top-k kernel against the oracle: rows whose top K
+    lie within 4094 order-key steps of the largest score (one histogram of
+    distances), rows where they do not (one page's scales raised by 2^40, so
+    its 64 tokens sit far above the rest: the two-level radix selection), and
+    rows longer than the 65536 scores kept on chip (keys re-read from the
+    scores), with the exact 65536 boundary."""
+    lens = [70_000, 65_536, 5_000, 5_000, 65_537]
+    q, w, kc, pt, lens = W.indexer_inputs(15, 5, 64, lens, max_pages=1100)
+    for r in (2, 3, 4):
+        page = pt[r, 7]
+        sc = kc[page, 8192:].copy().view("<f4") * np.float32(2.0 ** 40)
+        kc[page, 8192:] = sc.view(np.uint8)
+    check(q, w, kc, pt, lens, 256, tag="paths K=256")
+    check(q, w, kc, pt, lens, 48, rows=[2, 3], tag="paths K=48")
