@@ -92,6 +92,19 @@ def test_indexer_small_k_and_ties():
     assert np.all(sc[1, :700] == sc[1, 0])
 
 
+def test_indexer_topk_crowded_threshold_bin():
+    """6000 equal scores and K = 256: the threshold bin holds more tokens
+    than the on-chip stash (4160), so the kernel re-reads the row for them."""
+    q, w, kc, pt, lens = W.indexer_inputs(16, 2, 64, [6000, 6000], max_pages=100)
+    tok = kc[pt[0, 0], :128].copy()
+    scale = kc[pt[0, 0], 8192:8196].copy()
+    for p in pt[0, :94]:
+        kc[p, :8192] = np.tile(tok, 64)
+        kc[p, 8192:] = np.tile(scale, 64)
+    idx, sc = check(q, w, kc, pt, lens, 256, tag="crowded bin")
+    assert np.all(sc[0, :6000] == sc[0, 0])
+
+
 def test_indexer_invalid_pages_and_clamped_lengths():
     """A page-table entry outside the cache scores -inf and emits -1, a
     seq_len beyond the table clamps: the oracle takes the raw table and the
