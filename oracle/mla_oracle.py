@@ -59,6 +59,18 @@ primitives used; no blocking, fusion or online rescaling):
   is 2^(e - 127), 0xFF is NaN (the OCP E8M0 encoding; the pages say only
   "pure power of two, no mantissa").  V = K (d_v = d_qk = 512: the first
   d_v dims of K, as for V3.2).
+* FP4 extra cache -- "FlashMLA 与 DSA" section 3.1 lists a 288-byte FP4
+  token with e8m0 scales per 16 elements, section 6.1 allows FP4 only as an
+  extra cache beside a V4.1 main cache, section 3.2 has split-KV decided on
+  topk + extra_topk and section 3.5 has the decode walk the main and the
+  extra blocks in one loop per format: a query token attends over its topk
+  main slots and its extra_topk extra slots in one softmax.  Readings taken: the token is 512
+  OCP E2M1 values (256 bytes, element 2i in the low nibble of byte i) and 32
+  e8m0 scales (one per 16 dims), pages struct-of-arrays as for V4.1
+  (section 3.1 says FP4 scales are e8m0 here, while the kernel table of
+  section 2 pairs FP4 with e4m3; e8m0 is taken); extra slots are valid under
+  the same rules as main slots (an id in [0, extra tokens), before an extra
+  valid length when one is given); V = K.
 * split-KV combine -- walkthrough step 14.2 (split partials are normalised
   O_j and lse_j = log2(l_j) + m_j in base 2, -inf when empty) and step 16
   (max over splits, weights 2^(lse_j - max), weighted mean of the O_j);
@@ -90,6 +102,8 @@ FMT_V41 = 3         # 528 B per token: 512 e4m3 | 16 e8m0
 DQK_MODEL1 = 512
 # struct-of-arrays formats: data bytes, scale bytes per token, e4m3 dims, dims per scale
 SOA_LAYOUT = {FMT_V4: (576, 8, 448, 64), FMT_V41: (512, 16, 512, 32)}
+FMT_FP4 = 4         # 288 B per token: 512 e2m1 (two per byte) | 32 e8m0 (extra cache only)
+FP4_LAYOUT = (256, 32, 512, 16)
 
 
 def dqk_of(kv_format: int) -> int:
@@ -123,6 +137,17 @@ def e8m0_value(code: np.ndarray) -> np.ndarray:
     """uint8 e8m0 scale bytes -> float64: 2^(e - 127), NaN for 0xFF."""
     e = np.asarray(code, dtype=np.int64)
     return np.where(e == 0xFF, np.nan, np.exp2(e.astype(np.float64) - 127.0))
+
+
+def e2m1_value(nib: np.ndarray) -> np.ndarray:
+    """4-bit e2m1 codes (0..15) -> float64: sign bit 3, exponent bits 2..1
+    (bias 1, field 0 subnormal), mantissa bit 0."""
+    c = np.asarray(nib, dtype=np.int64)
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    val = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0))
+    return sign * val
 
 
 def f32le_value(b4: np.ndarray) -> np.ndarray:
@@ -171,6 +196,16 @@ def decode_v41_rows(data: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return q.reshape(*lead, 512)
 
 
+def decode_fp4_rows(data: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """FP4: data uint8 [..., 256] (element 2i in the low nibble of byte i),
+    scales uint8 [..., 32] -> K float64 [..., 512]."""
+    data = np.asarray(data, dtype=np.uint8)
+    lead = data.shape[:-1]
+    nib = np.stack([data & 0xF, data >> 4], axis=-1).reshape(*lead, 512)
+    sc = e8m0_value(np.asarray(scales, dtype=np.uint8))                        # [..., 32]
+    return (e2m1_value(nib).reshape(*lead, 32, 16) * sc[..., None]).reshape(*lead, 512)
+
+
 def soa_token_bytes(kv: np.ndarray, kv_format: int, ids: np.ndarray,
                     page_block_size: int) -> Tuple[np.ndarray, np.ndarray]:
     """Data and scale bytes of tokens `ids` in a struct-of-arrays cache.
@@ -178,7 +213,7 @@ def soa_token_bytes(kv: np.ndarray, kv_format: int, ids: np.ndarray,
     kv: uint8 [num_blocks, page_stride] (page_stride >= P * bytes per token);
     token t lives in page t // P at offset o = t % P: data row at o * data_b,
     scale row at P * data_b + o * scale_b."""
-    data_b, scale_b, _, _ = SOA_LAYOUT[kv_format]
+    data_b, scale_b, _, _ = FP4_LAYOUT if kv_format == FMT_FP4 else SOA_LAYOUT[kv_format]
     P = page_block_size
     ids = np.asarray(ids, dtype=np.int64)
     blk, off = ids // P, ids % P
@@ -199,7 +234,7 @@ def token_rows(kv: np.ndarray, kv_format: int) -> np.ndarray:
 
 
 def num_tokens_of(kv: np.ndarray, kv_format: int, page_block_size: int = 1) -> int:
-    if kv_format in SOA_LAYOUT:
+    if kv_format in SOA_LAYOUT or kv_format == FMT_FP4:
         return kv.shape[0] * page_block_size
     return kv.shape[0] * kv.shape[1] if kv_format == FMT_FP8 else kv.shape[0]
 
@@ -220,9 +255,10 @@ def gather_dequant(kv: np.ndarray, indices: np.ndarray, kv_format: int,
     idx = np.asarray(indices, dtype=np.int64)
     valid = slot_valid(idx, n_tok)
     safe = np.where(valid, idx, 0)
-    if kv_format in SOA_LAYOUT:
+    if kv_format in SOA_LAYOUT or kv_format == FMT_FP4:
         data, scales = soa_token_bytes(kv, kv_format, safe, P)
-        rows = (decode_v4_rows if kv_format == FMT_V4 else decode_v41_rows)(data, scales)
+        dec = {FMT_V4: decode_v4_rows, FMT_V41: decode_v41_rows, FMT_FP4: decode_fp4_rows}[kv_format]
+        rows = dec(data, scales)
     elif kv_format == FMT_FP8:
         # page / offset addressing (identical to flat row idx for a dense [nb, P] cache)
         raw = kv[safe // P, safe % P, 0]
@@ -271,13 +307,17 @@ def sparse_mla_decode(q_bits: np.ndarray, kv: np.ndarray, indices: np.ndarray,
                       sm_scale: float, kv_format: int, page_block_size: int,
                       queries: Optional[Iterable[Tuple[int, int]]] = None,
                       attn_sink: Optional[np.ndarray] = None,
-                      topk_length: Optional[np.ndarray] = None):
+                      topk_length: Optional[np.ndarray] = None,
+                      extra: Optional[dict] = None):
     """Sparse MLA decode by definition.
 
     q_bits: uint16 bf16 [b, s_q, H, d_qk]; kv: fp8 uint8 [nb, P, 1, 656],
     bf16-row bytes uint8 [s_kv, 1152], or a V4 / V4.1 cache uint8
     [nb, page_stride] (d_qk = 512); indices int32 [b, s_q, topk];
     attn_sink: float [H] (natural log) or None; topk_length: int [b] or None.
+    extra (V4.1 main cache only): {"kv": FP4 cache uint8 [nb, page_stride],
+    "indices": int32 [b, s_q, extra_topk], "page_block_size": P, and
+    optionally "topk_length": int [b]} -- its slots join the main ones.
     Returns out float64 [b, s_q, H, 512] and lse float64 [b, H, s_q]
     (natural log).  With `queries`, only those (bi, sj) pairs are filled and
     the others are NaN.
@@ -289,12 +329,23 @@ def sparse_mla_decode(q_bits: np.ndarray, kv: np.ndarray, indices: np.ndarray,
     if queries is None:
         queries = [(bi, sj) for bi in range(b) for sj in range(s_q)]
     topk = indices.shape[-1]
+    if extra is not None:
+        assert kv_format == FMT_V41
     for bi, sj in queries:
         rows, valid = gather_dequant(kv, indices[bi, sj], kv_format, page_block_size)
         if topk_length is not None:
             n_ok = min(max(int(topk_length[bi]), 0), topk)
             valid = valid & (np.arange(topk) < n_ok)
             rows = np.where(valid[:, None], rows, 0.0)
+        if extra is not None:
+            xi = extra["indices"][bi, sj]
+            xrows, xvalid = gather_dequant(extra["kv"], xi, FMT_FP4, extra["page_block_size"])
+            if extra.get("topk_length") is not None:
+                n_ok = min(max(int(extra["topk_length"][bi]), 0), len(xi))
+                xvalid = xvalid & (np.arange(len(xi)) < n_ok)
+                xrows = np.where(xvalid[:, None], xrows, 0.0)
+            rows = np.concatenate([rows, xrows])
+            valid = np.concatenate([valid, xvalid])
         qh = bf16_value(q_bits[bi, sj])
         o, l = attend(qh, rows, rows[:, :DV], valid, sm_scale)
         if attn_sink is not None:

@@ -225,3 +225,108 @@ def test_attention_matches_torch_on_decoded_rows():
     ref = torch.softmax(s, dim=-1) @ Ks
     assert np.allclose(out[0, 0], ref.numpy(), rtol=1e-12, atol=1e-14)
     assert np.allclose(lse[0, :, 0], torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- FP4 extra cache
+# The OCP FP4 (E2M1) value set: codes 0..7 are the magnitudes below, codes
+# 8..15 their negatives.
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_codes_are_the_format_values():
+    got = O.e2m1_value(np.arange(16))
+    assert got[:8].tolist() == E2M1_MAGNITUDES
+    assert (-got[8:]).tolist() == E2M1_MAGNITUDES and np.all(np.signbit(got[8:]))
+    # every value is exact in e4m3 (so an FP4 token can be restated as V4.1)
+    e4 = torch.tensor(got.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(e4, got)
+
+
+def _fp4_code(x):
+    """Nearest e2m1 code of x (ties to the even code), by search over the value set."""
+    vals = np.array(E2M1_MAGNITUDES)
+    mag = np.abs(x)
+    d = np.abs(mag[..., None] - vals)
+    best = np.argmin(d + 1e-9 * (np.arange(8) % 2), axis=-1)          # ties: the even code
+    return (best | np.where(x < 0, 8, 0)).astype(np.uint8)
+
+
+def _fp4_tokens(x):
+    """x float32 [n, 512] -> (data [n, 256], scales [n, 32]): scale 2^ceil(log2(amax / 6))."""
+    n = x.shape[0]
+    g = x.reshape(n, 32, 16).astype(np.float64)
+    amax = np.maximum(np.abs(g).max(axis=-1), 1e-4)
+    m, e = np.frexp(amax / 6.0)
+    ex = np.where(m == 0.5, e - 1, e)
+    codes = _fp4_code(g / np.exp2(ex)[..., None]).reshape(n, 512)
+    data = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return data, (ex + 127).astype(np.uint8)
+
+
+def test_fp4_nibble_order_and_scale_groups():
+    data = np.zeros((1, 256), np.uint8)
+    data[0, 0] = 0x72            # element 0 = code 2 (1.0), element 1 = code 7 (6.0)
+    data[0, 9] = 0xB0            # element 18 = 0, element 19 = code 11 (-1.5)
+    sc = np.full((1, 32), 127, np.uint8)
+    sc[0, 1] = 130               # dims 16..31 scaled by 8
+    K = O.decode_fp4_rows(data, sc)[0]
+    want = np.zeros(512)
+    want[0], want[1], want[19] = 1.0, 6.0, -1.5 * 8
+    assert np.array_equal(K, want)
+
+
+def test_fp4_row_decode_matches_the_encoder():
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((64, 512)) * rng.uniform(1e-2, 1e2, size=(64, 1))).astype(np.float32)
+    data, sc = _fp4_tokens(x)
+    K = O.decode_fp4_rows(data, sc)
+    scale = np.repeat(np.exp2(sc.astype(np.float64) - 127), 16, axis=1)
+    nib = np.stack([data & 0xF, data >> 4], axis=-1).reshape(64, 512)
+    mag = np.array(E2M1_MAGNITUDES)[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    assert np.array_equal(K, mag * scale)
+    # within half a step of the e2m1 grid (largest gap 2, at 4..6) of the value
+    assert np.all(np.abs(K - x) <= scale * 1.0 + 1e-12)
+
+
+def _v41_from_fp4(data, sc):
+    """The same numbers as a V4.1 token (codes to e4m3, one scale per 32),
+    possible when both 16-groups of each 32-group share their scale."""
+    assert np.array_equal(sc[:, 0::2], sc[:, 1::2])
+    vals = O.decode_fp4_rows(data, np.full_like(sc, 127))            # e2m1 values (scale 1)
+    codes = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, sc[:, 0::2].copy()
+
+
+@pytest.mark.parametrize("with_lengths", [False, True])
+def test_extra_slots_equal_the_same_tokens_in_the_main_cache(with_lengths):
+    # FP4 tokens whose two 16-groups per 32 share a scale are V4.1 tokens in
+    # disguise: attention over main slots + extra slots must equal attention
+    # over the concatenated slots of one V4.1 cache holding all the tokens
+    rng = np.random.default_rng(43)
+    P, h = 16, 8
+    nm, nx = 6 * P, 4 * P                                   # main and extra tokens
+    xm = (rng.standard_normal((nm, 512)) * 0.5).astype(np.float32)
+    dm, sm = _token_bytes_v41(xm)
+    xx = (rng.standard_normal((nx, 512)) * 0.5).astype(np.float32)
+    dx, sx = _fp4_tokens(xx)
+    sx[:, 1::2] = sx[:, 0::2]                              # shared scale per 32 (values shrink or stay)
+    main = _build_cache(dm, sm, P, nm // P, P * 528, rng, np.arange(nm))
+    extra = _build_cache(dx, sx, P, nx // P, P * 288 + 32, rng, np.arange(nx))
+    dxc, sxc = _v41_from_fp4(dx, sx)
+    both = _build_cache(np.concatenate([dm, dxc]), np.concatenate([sm, sxc]), P, (nm + nx) // P, P * 528, rng,
+                        np.arange(nm + nx))
+    b, s_q, tk, xk = 3, 2, 40, 24
+    q = _bf16_bits(rng.standard_normal((b, s_q, h, 512)).astype(np.float32))
+    idx = rng.integers(-1, nm, size=(b, s_q, tk)).astype(np.int32)
+    xidx = rng.integers(-1, nx + 3, size=(b, s_q, xk)).astype(np.int32)   # some out of range
+    mlen = np.array([40, 13, 0]) if with_lengths else None
+    xlen = np.array([5, 24, 30]) if with_lengths else None
+    out, lse = O.sparse_mla_decode(q, main, idx, 0.04, O.FMT_V41, P, topk_length=mlen,
+                                   extra={"kv": extra, "indices": xidx, "page_block_size": P, "topk_length": xlen})
+    cat = np.concatenate([idx, np.where((xidx >= 0) & (xidx < nx), xidx + nm, -1)], axis=-1).astype(np.int32)
+    if with_lengths:
+        for bi in range(b):
+            cat[bi, :, max(0, min(mlen[bi], tk)):tk] = -1
+            cat[bi, :, tk + max(0, min(xlen[bi], xk)):] = -1
+    ref_o, ref_l = O.sparse_mla_decode(q, both, cat, 0.04, O.FMT_V41, P)
+    assert np.array_equal(out, ref_o) and np.array_equal(lse, ref_l)
