@@ -234,6 +234,44 @@ int mla_plan_sched_meta_len_host(const mla_shape* shape, const int32_t* topk_len
  * lse_accum (base 2) for split ones. */
 int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream);
 
+/* FP4 extra cache beside a V4.1 main cache ("FlashMLA 与 DSA" section 3.1:
+ * 288 bytes per token, e8m0 scales per 16 elements; section 6.1: FP4 only as
+ * an extra cache, with V4.1; section 3.2: split-KV decided on topk +
+ * extra_topk; section 3.5: main and extra blocks walked in one loop each).
+ * A query token attends over its main slots and its extra slots in one
+ * softmax.  Page n of P tokens starts at kv + n * kv_stride_block; token
+ * t = n P + o has its data row (512 E2M1 values, element 2 i in the low
+ * nibble of byte i: 256 bytes) at page + 256 o and its scale row (32 e8m0
+ * bytes, one per 16 dims) at page + 256 P + 32 o.  The split of the 288
+ * bytes, the nibble order and the e8m0 scale type (the pages name both e8m0
+ * and e4m3 for FP4 scales) are readings; V = K.  All pointers are device
+ * memory owned by the caller. */
+typedef struct mla_extra_kv {
+    const void* kv;                 /* [num_blocks, kv_stride_block] bytes, 16-byte aligned       */
+    int64_t kv_stride_block;        /* bytes per page: >= P * 288, a multiple of 16, P * 288 < 2^31 */
+    int32_t page_block_size;        /* P >= 1                                                      */
+    int64_t num_kv_tokens;          /* num_blocks * P, in [1, 2^31)                               */
+    const int32_t* indices;         /* [b, s_q, extra_topk] physical token ids of this cache, -1 =
+                                       empty (ids outside [0, num_kv_tokens) are empty too);
+                                       last dim contiguous, 4-byte aligned                        */
+    int64_t idx_stride_b, idx_stride_s;   /* in elements                                          */
+    int32_t extra_topk;             /* extra slots per query token, in [1, shape.topk)           */
+    const int32_t* topk_length;     /* NULL, or int32 [b]: extra slots at positions >= it are
+                                       empty (clamped to [0, extra_topk])                         */
+} mla_extra_kv;
+
+/* Sparse decode over a V4.1 main cache and an FP4 extra cache.  args is as
+ * for mla_sparse_decode_fwd with kv_format MLA_KV_V41_528, except that
+ * args->shape.topk counts every slot of a query token: its first
+ * shape.topk - extra->extra_topk slots are the main slots (args->indices
+ * rows of that many ids, args->topk_length their valid lengths), the rest
+ * the extra slots.  The plan (mla_get_sched_meta, or NULL for the closed
+ * form) and mla_splitkv_combine take that same args->shape; plans made from
+ * valid lengths are not supported here (the decode and the combine then
+ * write NaN).  MLA_ERR_UNSUPPORTED for another main format; MLA_ERR_INVALID_ARG
+ * for a NULL extra or a bad extra field. */
+int mla_sparse_decode_extra_fwd(const mla_decode_args* args, const mla_extra_kv* extra, void* stream);
+
 /* Dense decode ("FlashMLA Sparse Decode 完整计算过程详解", step 1: a call
  * without indices takes block_table + cache_seqlens and walks every page of
  * a request in block-table order; the caller routes here when the context is

@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     mla_get_sched_meta_len, mla_plan_sched_meta_len_host, mla_indexer_args, mla_indexer_scores,
     mla_indexer_topk, indexer_args, indexer_select,
     mla_last_error, mla_plan_sched_meta_host, mla_resolve_shape, mla_sched_meta_size, mla_shape,
-    mla_dense_decode_fwd, mla_sparse_decode_fwd, mla_sparse_decode_noalloc, mla_splitkv_combine, mla_version, mla_workspace_size,
+    mla_dense_decode_fwd, mla_sparse_decode_fwd, mla_sparse_decode_extra_fwd, mla_extra_kv, extra_kv_args, mla_sparse_decode_noalloc, mla_splitkv_combine, mla_version, mla_workspace_size,
 )

@@ -30,7 +30,7 @@ EXPORTED = ("mla_sched_meta_size", "mla_workspace_size", "mla_resolve_shape",
             "mla_get_sched_meta", "mla_plan_sched_meta_host", "mla_get_sched_meta_len",
             "mla_plan_sched_meta_len_host", "mla_sparse_decode_fwd", "mla_indexer_scores", "mla_indexer_topk",
             "mla_splitkv_combine", "mla_debug_gather_dequant", "mla_sparse_decode_noalloc",
-            "mla_dense_decode_fwd",
+            "mla_dense_decode_fwd", "mla_sparse_decode_extra_fwd",
             "mla_last_error", "mla_version")
 
 
@@ -49,6 +49,13 @@ class mla_indexer_args(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("weights", ctypes.c_void_p), ("kcache", ctypes.c_void_p),
                 ("page_table", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("scores", ctypes.c_void_p),
                 ("indices", ctypes.c_void_p)]
+
+
+class mla_extra_kv(ctypes.Structure):
+    _fields_ = [("kv", ctypes.c_void_p), ("kv_stride_block", ctypes.c_int64),
+                ("page_block_size", ctypes.c_int32), ("num_kv_tokens", ctypes.c_int64),
+                ("indices", ctypes.c_void_p), ("idx_stride_b", ctypes.c_int64), ("idx_stride_s", ctypes.c_int64),
+                ("extra_topk", ctypes.c_int32), ("topk_length", ctypes.c_void_p)]
 
 
 class mla_decode_args(ctypes.Structure):
@@ -183,6 +190,34 @@ def mla_splitkv_combine(args: mla_decode_args, stream=None) -> None:
     _check("mla_splitkv_combine", load_library().mla_splitkv_combine(ctypes.byref(args), _stream(stream)))
 
 
+def mla_sparse_decode_extra_fwd(args: mla_decode_args, extra: mla_extra_kv, stream=None) -> None:
+    _check("mla_sparse_decode_extra_fwd", load_library().mla_sparse_decode_extra_fwd(
+        ctypes.byref(args), ctypes.byref(extra), _stream(stream)))
+
+
+def extra_kv_args(kv, page_block_size: int, indices, topk_length=None) -> mla_extra_kv:
+    """Marshal an FP4 extra cache: kv uint8 [num_blocks, page stride] (contiguous
+    rows), indices int32 [b, s_q, extra_topk] (last dim contiguous), topk_length
+    int32 [b] or None (device tensors).  The returned struct keeps the tensors
+    alive for as long as it lives."""
+    import torch
+    fn = "extra_kv_args"
+    _require(kv.dtype == torch.uint8 and kv.dim() == 2 and kv.stride(1) == 1, fn,
+             "kv must be uint8 [num_blocks, page stride] with contiguous rows")
+    _require(indices.dtype == torch.int32 and indices.dim() == 3 and indices.stride(2) == 1, fn,
+             "indices must be int32 [b, s_q, extra_topk] with a contiguous last dim")
+    _require(topk_length is None or (topk_length.dtype == torch.int32 and topk_length.is_contiguous()), fn,
+             "topk_length must be contiguous int32 [b]")
+    x = mla_extra_kv()
+    x.kv, x.kv_stride_block = kv.data_ptr(), kv.stride(0)
+    x.page_block_size, x.num_kv_tokens = page_block_size, kv.shape[0] * page_block_size
+    x.indices, x.idx_stride_b, x.idx_stride_s = indices.data_ptr(), indices.stride(0), indices.stride(1)
+    x.extra_topk = indices.shape[2]
+    x.topk_length = None if topk_length is None else topk_length.data_ptr()
+    x.tensors = (kv, indices, topk_length)        # the struct holds raw pointers: keep their memory alive
+    return x
+
+
 def mla_dense_decode_fwd(args: mla_decode_args, block_table_ptr: int, block_table_stride: int, causal: bool,
                          stream=None) -> None:
     _check("mla_dense_decode_fwd", load_library().mla_dense_decode_fwd(
@@ -241,6 +276,7 @@ def indexer_args(q, weights, kcache, page_table, seq_len, topk: int, scores, ind
     a.q, a.weights, a.kcache = q.data_ptr(), weights.data_ptr(), kcache.data_ptr()
     a.page_table, a.seq_len = page_table.data_ptr(), seq_len.data_ptr()
     a.scores, a.indices = scores.data_ptr(), indices.data_ptr()
+    a.tensors = (q, weights, kcache, page_table, seq_len, scores, indices)   # keep the memory alive
     return a
 
 
@@ -336,6 +372,7 @@ class DecodePlan:
         a.lse_accum = self.lse_accum.data_ptr()
         a.o_accum_bytes = self.o_accum.numel() * 4
         a.lse_accum_bytes = self.lse_accum.numel() * 4
+        a.tensors = (q, kv, indices, out, lse, attn_sink, topk_length)   # keep the memory alive
         return a
 
     def run_dense(self, q, kv, block_table, cache_seqlens, sm_scale: float = 0.0, causal: bool = False,
@@ -352,6 +389,17 @@ class DecodePlan:
             self.get_sched_meta(stream, cache_seqlens)
         a = self.args(q, kv, None, sm_scale, attn_sink=attn_sink, topk_length=cache_seqlens)
         mla_dense_decode_fwd(a, block_table.data_ptr(), block_table.stride(0), causal, stream)
+        mla_splitkv_combine(a, stream)
+        return self.out, self.lse
+
+    def run_extra(self, q, kv, indices, extra, sm_scale: float = 0.0, stream=None, with_sched: bool = True,
+                  attn_sink=None, topk_length=None):
+        """V4.1 main cache + FP4 extra cache (extra: mla_extra_kv, see
+        extra_kv_args): the plan's shape.topk counts main and extra slots."""
+        if with_sched:
+            self.get_sched_meta(stream, topk_length)
+        a = self.args(q, kv, indices, sm_scale, attn_sink=attn_sink, topk_length=topk_length)
+        mla_sparse_decode_extra_fwd(a, extra, stream)
         mla_splitkv_combine(a, stream)
         return self.out, self.lse
 

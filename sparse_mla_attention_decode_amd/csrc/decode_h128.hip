@@ -78,6 +78,8 @@ constexpr int L_RAW = 0;
 constexpr int F32 = MLA_KV_FP8_656;               // 656-byte rows
 constexpr int F4 = MLA_KV_V4_584;                 // pages of 576-byte data rows, then 8-byte scale rows
 constexpr int F41 = MLA_KV_V41_528;               // pages of 512-byte data rows, then 16-byte scale rows
+constexpr int FX = 4;                             // FP4 extra cache: pages of 256-byte data rows, then 32-byte
+                                                  // scale rows (read beside a V4.1 main cache)
 
 // Per-format sizes and LDS map (bytes).  A staged tile is 32 NoPE rows of NP
 // bytes (bf16 dims 0..511 and a 16-byte pad that the contractions never read)
@@ -89,12 +91,12 @@ constexpr int F41 = MLA_KV_V41_528;               // pages of 512-byte data rows
 // a pad chunk (conflict-free operand reads).
 template <int F>
 struct Lay {
-    static constexpr int DB = F == F32 ? 656 : F == F4 ? 576 : 512;    // data row bytes
-    static constexpr int SB = F == F32 ? 0 : F == F4 ? 8 : 16;         // scale row bytes
+    static constexpr int DB = F == F32 ? 656 : F == F4 ? 576 : F == F41 ? 512 : 256;   // data row bytes
+    static constexpr int SB = F == F32 ? 0 : F == F4 ? 8 : F == F41 ? 16 : 32;        // scale row bytes
     static constexpr int KSTEPS = F == F32 ? 36 : 32;                  // score k-steps of 16 dims
     static constexpr int WAVE_RAW = F == F4 ? 5184 : 4224;             // a wave's raw slice
-    static constexpr int NDMA = F == F41 ? 5 : 6;                      // copies per lane per tile
-    static constexpr int NLOAD = F == F41 ? 5 : 6;                     // row loads per lane (prologue)
+    static constexpr int NDMA = F == F41 ? 5 : F == FX ? 3 : 6;        // copies per lane per tile
+    static constexpr int NLOAD = F == F41 ? 5 : F == FX ? 4 : 6;       // row loads per lane (prologue)
     static constexpr int RAW_BYTES = NW * WAVE_RAW;
     static constexpr int KBB = F == F32 ? ROPE_OFF + TILE * 128 : TILE * NP;
     static constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;              // [3] staged tiles
@@ -113,6 +115,7 @@ struct Lay {
 };
 static_assert(Lay<F32>::WAVE_RAW == 4 * 1024 + WROWS * 16 && Lay<F32>::QCOPIES == 37, "copy layout");
 static_assert(Lay<F4>::WAVE_RAW == 5120 + WROWS * 8 && Lay<F41>::QCOPIES == 33, "copy layout");
+static_assert(Lay<FX>::L_BYTES == Lay<F41>::L_BYTES && Lay<FX>::L_KB == Lay<F41>::L_KB, "one LDS map for V4.1 + FP4");
 
 // Rows copied for empty or out-of-range slots: all zero bytes (zero codes,
 // zero scales, zero RoPE), so staged values of empty slots are zero without
@@ -132,7 +135,9 @@ __device__ int32_t g_no_id[1] = {-1};
 // of chunk 32.  V4 (5184 bytes): code chunks 0..27 as above (copy 3 by lanes
 // with L % 8 < 4 only), bf16 chunk j (data chunk 28 + j) of row r at
 // 4096 + 128 r + 16 j (one copy by all lanes), and the 8-byte scale row of row
-// r at 5120 + 8 r (4-byte copies by lanes 0..15).
+// r at 5120 + 8 r (4-byte copies by lanes 0..15).  FP4 (the V4.1 slice
+// size): code chunks 0..15 as above (copies 0 and 1), the 32-byte scale row
+// of row r at 2048 + 32 r (16-byte copies by lanes 0..15).
 // RoPE copy of lane L (row L / 8 = key 8 w + L / 8 of the tile, slot L % 8):
 // it moves RoPE chunk (L % 8) ^ ((key / 2) % 8) of its row; `src` points at
 // chunk L % 8 of the row.
@@ -198,20 +203,23 @@ __device__ __forceinline__ const uint8_t* dense_row_addr(const DecodeParams& p, 
 // one register per lane across the tile loop.
 template <int F>
 __device__ __forceinline__ const uint8_t* soa_row(const DecodeParams& p, int t, bool ok, int zrow, int& sdel) {
+    constexpr bool X = F == FX;                   // the extra cache's own pages
     const uint32_t tt = ok ? (uint32_t)t : 0u;
-    const uint32_t blk = (__umulhi(tt, p.page_magic) + tt) >> p.page_mshift;
-    const uint32_t off = tt - blk * (uint32_t)p.page_block_size;
-    const uint64_t d = (uint64_t)(uintptr_t)p.kv + (uint64_t)blk * (uint64_t)p.kv_block_stride +
-                       off * (uint32_t)Lay<F>::DB;
+    const uint32_t blk = (__umulhi(tt, X ? p.x_page_magic : p.page_magic) + tt) >> (X ? p.x_page_mshift : p.page_mshift);
+    const uint32_t off = tt - blk * (uint32_t)(X ? p.x_page_block_size : p.page_block_size);
+    const uint64_t d = (uint64_t)(uintptr_t)(X ? p.x_kv : p.kv) +
+                       (uint64_t)blk * (uint64_t)(X ? p.x_block_stride : p.kv_block_stride) + off * (uint32_t)Lay<F>::DB;
     const uint64_t z = (uint64_t)(uintptr_t)g_zero_rows + (uint32_t)zrow * Lay<F>::DB;
     // scale row - data row: P D + o S - o D (zero page: z S - z D)
-    sdel = (ok ? (int)p.soa_scale_off : 0) - (int)(ok ? off : (uint32_t)zrow) * (Lay<F>::DB - Lay<F>::SB);
+    sdel = (ok ? (int)(X ? p.x_scale_off : p.soa_scale_off) : 0) -
+           (int)(ok ? off : (uint32_t)zrow) * (Lay<F>::DB - Lay<F>::SB);
     return (const uint8_t*)(uintptr_t)(ok ? d : z);
 }
 // Source of this lane's scale copy: V4.1 lanes 0..7 copy the scale row of row
-// L, V4 lanes 0..15 dword L % 2 of the scale row of row L / 2.  `src` and
-// `sdel` are the lanes' own (row L / 8: chunk L % 8 of the data row, scale
-// offset); the row's values come from lane 8 r.
+// L, V4 lanes 0..15 dword L % 2 of the scale row of row L / 2, FP4 lanes
+// 0..15 half L % 2 of the scale row of row L / 2.  `src` and `sdel` are the
+// lanes' own (row L / 8: chunk L % 8 of the data row, scale offset); the
+// row's values come from lane 8 r.
 template <int F>
 __device__ __forceinline__ const uint8_t* scale_src(const uint8_t* src, int sdel, int lane) {
     const int from = 8 * (F == F41 ? (lane & 7) : ((lane >> 1) & 7));
@@ -219,7 +227,7 @@ __device__ __forceinline__ const uint8_t* scale_src(const uint8_t* src, int sdel
     const uint64_t r = ((uint64_t)(uint32_t)__shfl((uint32_t)(a >> 32), from) << 32) |
                        (uint32_t)__shfl((uint32_t)a, from);
     const int del = __shfl(sdel, from);
-    return (const uint8_t*)(uintptr_t)(r + (int64_t)del) + (F == F4 ? 4 * (lane & 1) : 0);
+    return (const uint8_t*)(uintptr_t)(r + (int64_t)del) + (F == F4 ? 4 * (lane & 1) : F == FX ? 16 * (lane & 1) : 0);
 }
 // The copies of a tile from V4 / V4.1 rows; `src` points at chunk lane % 8 of
 // the lane's data row, `sdel` is its scale offset.
@@ -231,6 +239,10 @@ __device__ __forceinline__ void gather_soa(const uint8_t* src, int sdel, int lan
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(src + 128 * i, sl + 1024u * i);
         if (lane < 8) dma16(ssrc, sl + 4096u);
+    } else if constexpr (F == FX) {
+        dma16(src, sl);
+        dma16(src + 128, sl + 1024u);
+        if (lane < 16) dma16(ssrc, sl + 2048u);
     } else {
 #pragma unroll
         for (int i = 0; i < 3; ++i) dma16(src + 128 * i, sl + 1024u * i);
@@ -327,14 +339,28 @@ struct StageRegs {
 __device__ __forceinline__ float e8m0_scale(uint32_t word, int byte) {
     return __uint_as_float(((word >> (8 * byte)) & 0xffu) << 23);
 }
+// Byte `sel` of w (two e2m1 values, the first in the low nibble) times the
+// scale -> two bf16 (the same exponent-only scale operand as above).
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float scale, int sel) {
+    switch (sel) {
+        case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+        case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+        case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+        default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    }
+}
 // Scales of a lane's four chunks from its row's scale bytes (V4.1: 4 words,
-// V4: 2 words).
+// V4: 2 words).  FP4: a lane holds two 32-dim chunks c = L % 8 and c + 8,
+// each with two scales (bytes 2 c, 2 c + 1 and 2 c + 16, 2 c + 17 of the
+// row), from the two words that hold them.
 template <int F>
 __device__ __forceinline__ void soa_scales(StageRegs& g, const uint32_t* words, int lane) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (F == F41) {
             g.sc[i] = e8m0_scale(words[i], (lane & 7) >> 1);
+        } else if constexpr (F == FX) {
+            g.sc[i] = e8m0_scale(words[i >> 1], 2 * (lane & 1) + (i & 1));
         } else {
             const int grp = ((lane & 7) >> 2) + 2 * i;          // 7 in lanes without a chunk 3: the pad
             g.sc[i] = e8m0_scale(words[grp >> 2], grp & 3);
@@ -352,13 +378,17 @@ __device__ __forceinline__ StageRegs stage_load(const LDS_AS uint8_t* lds, int s
     const int r = lane >> 3;
     StageRegs g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) g.w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
+    for (int i = 0; i < (F == FX ? 2 : 4); ++i) g.w[i] = lds_read16(lds, slice + 1024 * i + 16 * lane);
     if constexpr (F == F32) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) g.sc[i] = *(const LDS_AS float*)(lds + slice + 4096 + 16 * r + 4 * i);
     } else if constexpr (F == F41) {
         const u32x4 sw = lds_read16(lds, slice + 4096 + 16 * r);
         const uint32_t words[4] = {sw[0], sw[1], sw[2], sw[3]};
+        soa_scales<F>(g, words, lane);
+    } else if constexpr (F == FX) {
+        const int wo = slice + 2048 + 32 * r + 4 * ((lane & 7) >> 1);
+        const uint32_t words[2] = {*(const LDS_AS uint32_t*)(lds + wo), *(const LDS_AS uint32_t*)(lds + wo + 16)};
         soa_scales<F>(g, words, lane);
     } else {
         if (TAIL) g.rope = stage_load_tail(lds, slice, lane);
@@ -373,6 +403,19 @@ __device__ __forceinline__ StageRegs stage_load(const LDS_AS uint8_t* lds, int s
 template <int I, int F = F32>
 __device__ __forceinline__ void stage_chunk(LDS_AS uint8_t* lds, const StageRegs& g, int kb, int wave, int lane) {
     const int r = lane >> 3, c0 = lane & 7;
+    if constexpr (F == FX) {
+        // FP4: half H = I % 2 of chunk c0 + 8 (I / 2): 16 e2m1 values in two
+        // words -> dims 32 (c0 + 8 (I / 2)) + 16 H .. + 15
+        const u32x4 w = g.w[I >> 1];
+        const float sc = g.sc[I];
+        const uint32_t a = w[2 * (I & 1)], b = w[2 * (I & 1) + 1];
+        const u32x4 lo = {fp4_pair(a, sc, 0), fp4_pair(a, sc, 1), fp4_pair(a, sc, 2), fp4_pair(a, sc, 3)};
+        const u32x4 hi = {fp4_pair(b, sc, 0), fp4_pair(b, sc, 1), fp4_pair(b, sc, 2), fp4_pair(b, sc, 3)};
+        const int off = kb + (WROWS * wave + r) * NP + 64 * (c0 + 8 * (I >> 1)) + 32 * (I & 1);
+        lds_write16(lds, off, lo);
+        lds_write16(lds, off + 16, hi);
+        return;
+    }
     // V4 has 28 code chunks: in lanes with c0 >= 4 chunk 3 holds bf16 values,
     // whose conversion lands on dims 448.. and is overwritten by stage_tail
     const u32x4 w = g.w[I];
@@ -417,6 +460,7 @@ struct RowRegs {
     u32x4 scales;
     u32x4 rope;
     u32x2 sc8;
+    uint32_t s0, s1;                               // FP4: the two scale words of the lane
 };
 __device__ __forceinline__ u32x4 gload16(const uint8_t* src) {
     u32x4 v;
@@ -428,6 +472,11 @@ __device__ __forceinline__ u32x2 gload8(const uint8_t* src) {
     asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(src) : "memory");
     return v;
 }
+__device__ __forceinline__ uint32_t gload4(const uint8_t* src) {
+    uint32_t v;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(src) : "memory");
+    return v;
+}
 // `src` points at chunk lane % 8 of the lane's row, as for gather_rows;
 // `sdel` (V4 / V4.1) is the row's scale offset
 template <int F>
@@ -435,12 +484,15 @@ __device__ __forceinline__ RowRegs load_rows(const uint8_t* src, int sdel, int l
     const uint8_t* sown = src - 16 * (lane & 7) + sdel;
     RowRegs r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.nope[i] = gload16(src + 128 * i);
+    for (int i = 0; i < (F == FX ? 2 : 4); ++i) r.nope[i] = gload16(src + 128 * i);
     if constexpr (F == F32) {
         r.scales = gload16(src - 16 * (lane & 7) + 512);
         r.rope = gload16(rope_src(src, lane, wave));
     } else if constexpr (F == F41) {
         r.scales = gload16(sown);
+    } else if constexpr (F == FX) {
+        r.s0 = gload4(sown + 4 * ((lane & 7) >> 1));
+        r.s1 = gload4(sown + 16 + 4 * ((lane & 7) >> 1));
     } else {
         r.rope = gload16(src + 448);
         r.sc8 = gload8(sown);
@@ -459,6 +511,10 @@ __device__ __forceinline__ void rows_wait(RowRegs& a) {
         asm volatile("s_waitcnt vmcnt(%5)"
                      : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.nope[2]), "+v"(a.nope[3]), "+v"(a.scales)
                      : "n"(N) : "memory");
+    else if constexpr (F == FX)
+        asm volatile("s_waitcnt vmcnt(%4)"
+                     : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.s0), "+v"(a.s1)
+                     : "n"(N) : "memory");
     else
         asm volatile("s_waitcnt vmcnt(%6)"
                      : "+v"(a.nope[0]), "+v"(a.nope[1]), "+v"(a.nope[2]), "+v"(a.nope[3]), "+v"(a.rope), "+v"(a.sc8)
@@ -471,12 +527,15 @@ template <int F>
 __device__ __forceinline__ void stage_from_regs(LDS_AS uint8_t* lds, const RowRegs& r, int kb, int wave, int lane) {
     StageRegs g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) g.w[i] = r.nope[i];
+    for (int i = 0; i < (F == FX ? 2 : 4); ++i) g.w[i] = r.nope[i];
     if constexpr (F == F32) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) g.sc[i] = __uint_as_float(r.scales[i]);
     } else if constexpr (F == F41) {
         const uint32_t words[4] = {r.scales[0], r.scales[1], r.scales[2], r.scales[3]};
+        soa_scales<F>(g, words, lane);
+    } else if constexpr (F == FX) {
+        const uint32_t words[2] = {r.s0, r.s1};
         soa_scales<F>(g, words, lane);
     } else {
         g.rope = r.rope;
@@ -555,11 +614,12 @@ __device__ __forceinline__ int xp_base(int lane) {
     return b;
 }
 
-template <bool FLAT, bool DENSE, bool H64, int F>
+template <bool FLAT, bool DENSE, bool H64, int F, bool EXTRA = false>
 __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParams p) {
     static_assert(F == F32 || (!FLAT && !DENSE), "V4 / V4.1: paged sparse decode only");
+    static_assert(!EXTRA || F == F41, "an FP4 extra cache goes with a V4.1 main cache");
     using L = Lay<F>;
-    constexpr int KSTEPS = L::KSTEPS, NDMA = L::NDMA;
+    constexpr int KSTEPS = L::KSTEPS;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
 
@@ -589,366 +649,400 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         const int blk_hi = req == end_req ? end_block : whole_blocks(p, plan, req);
         const int k_lo = blk_lo * p.block;
         const int k_hi = min(blk_hi * p.block, p.topk);
-        const int n_tiles = (k_hi - k_lo + TILE - 1) / TILE;
         // sparse: the request's index row; dense: its block-table row
-        const int32_t* idx = DENSE ? p.block_table + (int64_t)req * p.bt_stride
-                                   : p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
-        // slots below k_ok hold ids; the ones past the request's valid length
-        // (topk_length; dense: the cache length, less the later query tokens
-        // with causal) are empty like the ones past the piece
-        const int k_ok = p.topk_length
-                             ? min(k_hi, max(p.topk_length[req] - (p.causal ? p.s_q - 1 - sq : 0), 0))
-                             : k_hi;
-        auto tile_ids = [&](int tile, int ln, uint32_t slot_addr) {
-            if (DENSE) copy_pages(idx, k_lo, k_ok, tile, ln, slot_addr);
-            else copy_ids(idx, k_lo, k_ok, tile, ln, slot_addr);
-        };
-
-        // LDS slots of this wave's token ids: tile t in the ring (t % 2), the
-        // first four tiles of a pass in the prologue area
-        auto ring_slot = [&](int tile) -> int { return L::L_IDS + (wave * IDS_SLOTS + (tile & 1)) * 128; };
-        auto first_slot = [&](int tile) -> int { return L::L_IDS0 + wave * 512 + tile * 128; };
-        // ids that this lane needs from a slot: key ln % 32 (validity mask) and
-        // key 8w + ln / 8 (its copy row)
-        auto ids_at = [&](int slot_off, int ln) -> int2 {
-            const LDS_AS int32_t* slot = (const LDS_AS int32_t*)(lds + slot_off);
-            return int2{slot[ln & 31], slot[WROWS * wave + (ln >> 3)]};
-        };
-        // validity mask of the tile's 32 keys and the copy source of this
-        // lane's row (chunk ln % 8; V4 / V4.1: and the row's scale offset in
-        // sdel); tiles past the piece copy zero rows
-        auto rows_from = [&](int tile, int ln, int2 id, const uint8_t*& src, int& sdel) -> uint32_t {
-            const int kr = WROWS * wave + (ln >> 3);
-            if (DENSE) {
-                // the id slot holds the tile's block-table entry (or -1): a
-                // key is valid when the entry names a page of the cache
-                const bool ok = (uint32_t)id.x < p.n_pages;
-                const bool okr = (uint32_t)id.y < p.n_pages;
-                src = dense_row_addr<FLAT>(p, id.y, (k_lo + tile * TILE) % DENSE_PAGE + kr, okr, kr) + 16 * (ln & 7);
-                return (uint32_t)__ballot(ok);
-            }
-            const bool ok = slot_ok(p, id.x, true);
-            const bool okr = slot_ok(p, id.y, true);
-            if constexpr (F == F32) src = row_addr<FLAT>(p, id.y, okr, kr) + 16 * (ln & 7);
-            else src = soa_row<F>(p, id.y, okr, kr, sdel) + 16 * (ln & 7);
-            return (uint32_t)__ballot(ok);
-        };
+        const int32_t* idx_main = DENSE ? p.block_table + (int64_t)req * p.bt_stride
+                                        : p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
+        // main slots below min(piece end, len_main) hold ids; the ones past the
+        // request's valid length (topk_length; dense: the cache length, less
+        // the later query tokens with causal) are empty like the ones past the
+        // piece.  With an extra cache, slots from main_topk on are its slots.
+        const int main_top = EXTRA ? p.main_topk : p.topk;
+        const int len_main = p.topk_length ? max(p.topk_length[req] - (p.causal ? p.s_q - 1 - sq : 0), 0) : k_hi;
 
         // Q as B operands of the score contraction, loaded once per request:
         // lane (n, h) holds dims 16 j + 8 h .. +7 of head 32w + n for k-step j
         bf16x8 qa[KSTEPS];
         f32x16 O[16];
         float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
+        // One segment of the piece: slots [s_lo, s_hi) of one cache (the main
+        // cache, or the extra cache with its slots counted from 0), slots from
+        // s_ok on empty, in one format FS (the formats are never mixed inside a
+        // tile loop, so each loop keeps the registers of one format only).  O,
+        // l and the reference max carry over from segment to segment.
+        auto segment = [&](auto fs_tag, const int s_lo, const int s_hi, const int32_t* idx, const int s_ok,
+                           const int pass, const bool load_q) {
+            constexpr int FS = decltype(fs_tag)::value;
+            constexpr int NDMA = Lay<FS>::NDMA;
+            const int n_tiles = (s_hi - s_lo + TILE - 1) / TILE;
+            auto tile_ids = [&](int tile, int ln, uint32_t slot_addr) {
+                if (DENSE) copy_pages(idx, s_lo, s_ok, tile, ln, slot_addr);
+                else copy_ids(idx, s_lo, s_ok, tile, ln, slot_addr);
+            };
+
+            // LDS slots of this wave's token ids: tile t in the ring (t % 2), the
+            // first four tiles of a pass in the prologue area
+            auto ring_slot = [&](int tile) -> int { return L::L_IDS + (wave * IDS_SLOTS + (tile & 1)) * 128; };
+            auto first_slot = [&](int tile) -> int { return L::L_IDS0 + wave * 512 + tile * 128; };
+            // ids that this lane needs from a slot: key ln % 32 (validity mask) and
+            // key 8w + ln / 8 (its copy row)
+            auto ids_at = [&](int slot_off, int ln) -> int2 {
+                const LDS_AS int32_t* slot = (const LDS_AS int32_t*)(lds + slot_off);
+                return int2{slot[ln & 31], slot[WROWS * wave + (ln >> 3)]};
+            };
+            // validity mask of the tile's 32 keys and the copy source of this
+            // lane's row (chunk ln % 8; V4 / V4.1: and the row's scale offset in
+            // sdel); tiles past the piece copy zero rows
+            auto rows_from = [&](int tile, int ln, int2 id, const uint8_t*& src, int& sdel) -> uint32_t {
+                const int kr = WROWS * wave + (ln >> 3);
+                if (DENSE) {
+                    // the id slot holds the tile's block-table entry (or -1): a
+                    // key is valid when the entry names a page of the cache
+                    const bool ok = (uint32_t)id.x < p.n_pages;
+                    const bool okr = (uint32_t)id.y < p.n_pages;
+                    src = dense_row_addr<FLAT>(p, id.y, (s_lo + tile * TILE) % DENSE_PAGE + kr, okr, kr) + 16 * (ln & 7);
+                    return (uint32_t)__ballot(ok);
+                }
+                const uint32_t n_tok = FS == FX ? p.x_n_tok32 : p.n_tok32;   // ids name tokens of the segment's cache
+                const bool ok = (uint32_t)id.x < n_tok;
+                const bool okr = (uint32_t)id.y < n_tok;
+                if constexpr (FS == F32) src = row_addr<FLAT>(p, id.y, okr, kr) + 16 * (ln & 7);
+                else src = soa_row<FS>(p, id.y, okr, kr, sdel) + 16 * (ln & 7);
+                return (uint32_t)__ballot(ok);
+            };
+
+
+                // this wave's raw slice in slot 0 (copy destinations are this
+                // plus constants)
+                const uint32_t raw0 = lds0 + slice_off;
+
+                // Part 1 of tile i: the 36 score MFMAs of tile i+1 (K buffer at
+                // kb) for this wave's 32 heads over all 576 dims (two accumulator
+                // chains) with, between them, the softmax of tile i (mask empty
+                // slots, base-2 exponent against the reference max, P to LDS), the
+                // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
+                // 1 - par for tile parity par).  With soft == false (the prologue)
+                // only the scores of tile 0.
+                auto part1 = [&](int i, int par, int kb, int kb3, int ln, bool soft, bool scores, bool copies,
+                                 const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S, f32x16& S_next,
+                                 const StageRegs* pro_g) {
+                    const int qk = kb + qk_off(ln, 0);      // NoPE k-steps: qk + 32 j
+                    const int r3 = 1 - par;
+                    const uint32_t raw3 = raw0 + r3 * L::RAW_BYTES;
+                    f32x16 Sa, Sb;
+                    bf16x8 ka[KAHEAD];
+    #pragma unroll
+                    for (int j = 0; j < KAHEAD; ++j)
+                        if (scores && sc_wave) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                    // RoPE k-steps 32..35 of tile i+1 (lane-dependent slots)
+                    auto rope_k = [&](int j) { return kb + qk_off(ln, j); };
+                    if (soft && copies) tile_ids(i + 5, ln, lds0 + ring_slot(r3));
+                    __builtin_amdgcn_sched_barrier(0);
+                    float mx, psum = 0.f;
+    #pragma unroll
+                    for (int js = 0; js < KSTEPS; ++js) {
+                        if (scores && sc_wave) {
+                            const bf16x8 cur = ka[js % KAHEAD];
+                            if (js + KAHEAD < KSTEPS)
+                                ka[js % KAHEAD] = __builtin_bit_cast(
+                                    bf16x8, lds_read16(lds, js + KAHEAD < 32 ? qk + 32 * (js + KAHEAD) : rope_k(js + KAHEAD)));
+                            // two alternating accumulator chains: a score MFMA never
+                            // takes the result of the one issued right before it
+                            // (64 heads leave AGPRs free for the compiler: guarded MFMAs)
+                            if (js == 0) mfma_qk_first<H64>(Sa, cur, qa[0]);
+                            else if (js == 1) mfma_qk_first<H64>(Sb, cur, qa[1]);
+                            else if (js & 1) mfma_qk<H64>(Sb, cur, qa[js]);
+                            else mfma_qk<H64>(Sa, cur, qa[js]);
+                        }
+                        if (pro_g != nullptr) {
+                            // prologue: tile 1 staged into K buffer 1 under the scores of tile 0
+                            if (js == 4) stage_chunk<0, FS>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                            if (js == 12) stage_chunk<1, FS>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                            if (js == 20) stage_chunk<2, FS>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                            if (js == 28) {
+                                stage_chunk<3, FS>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                                stage_tail<FS>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
+                            }
+                        }
+                        if (soft) {
+                            // copies of tile i+3: NoPE chunks into the raw slot, RoPE
+                            // into the staged tile it will occupy (K buffer kb3, whose
+                            // RoPE rows the scores of its previous tile no longer read);
+                            // V4 / V4.1: code chunks, bf16 chunks and scale rows into
+                            // the raw slot
+                            if (copies && js >= 3 && js <= 18 && js % 5 == 3) {
+                                if (FS == FX ? js <= 8 : FS != F4 || js < 18)
+                                    dma16_at(src3 + 128 * (js / 5), raw3, 1024 * (js / 5));
+                                else if (FS == F4 && (ln & 7) < 4) dma16_at(src3 + 384, raw3, 3072);
+                            }
+                            if (copies && js == 23) {
+                                if constexpr (FS == F32)
+                                    dma16_at(rope_src(src3, ln, wave), lds0 + kb3 + ROPE_OFF + 1024u * wave, 0);
+                                if constexpr (FS == F4) dma16_at(src3 + 448, raw3, 4096);
+                            }
+                            if (copies && js == 28) {
+                                if constexpr (FS == F32) gather_tail_at(src3, ln, raw3, 4096);
+                                if constexpr (FS == F41) {
+                                    const uint8_t* ssrc3 = scale_src<FS>(src3, sdel3, ln);
+                                    if (ln < 8) dma16_at(ssrc3, raw3, 4096);
+                                }
+                                if constexpr (FS == F4) {
+                                    const uint8_t* ssrc3 = scale_src<FS>(src3, sdel3, ln);
+                                    if (ln < 16) dma4_at(ssrc3, raw3, 5120);
+                                }
+                                if constexpr (FS == FX) {
+                                    const uint8_t* ssrc3 = scale_src<FS>(src3, sdel3, ln);
+                                    if (ln < 16) dma16_at(ssrc3, raw3, 2048);
+                                }
+                            }
+                        }
+                        if (soft && sc_wave) {
+                            if (js == 1 && vm != 0xffffffffu) {
+                                // accumulator element v holds key 8(v/4) + 4h + v%4:
+                                // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
+    #pragma unroll
+                                for (int v = 0; v < 16; ++v) {
+                                    const int key = 8 * (v >> 2) + (v & 3);
+                                    const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
+                                                           ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
+                                    S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
+                                }
+                            }
+                            if (js == 2) {
+                                mx = S[0];
+    #pragma unroll
+                                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
+                            }
+                            if (js == 4) {
+                                // max with the other half-wave (same head): the swap hands
+                                // lanes 0..31 the upper half's value in the second result
+                                // and lanes 32..63 the lower half's in the first
+                                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                                mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+                                const float mnew = mx * p.c;
+                                m_seen = fmaxf(m_seen, mnew);
+                                if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                            }
+                            if (js >= 6 && js < 22) {
+                                const int v = js - 6;
+                                S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
+                                psum += S[v];
+                            }
+                            if (js == 24) {
+                                l_part += psum;
+                                lds_write16(lds, xp_base<FS>(ln) + wave * 2048, p_fragment(S, 0));
+                            }
+                            if (js == 26) lds_write16(lds, xp_base<FS>(ln) + wave * 2048 + 1024, p_fragment(S, 1));
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    if (scores && sc_wave) {
+                        mfma_result_fence2(Sa, Sb);
+                        S_next = Sa + Sb;
+                    }
+                };
+                // Part 2 of tile i: the 32 value MFMAs of tile i (O^T += V^T P^T over
+                // this wave's 128 dims, all 128 heads; V from the K buffer at kbv, P
+                // from LDS) with, between them, the dequant of tile i+2 (raw slot
+                // par) written straight into the K buffer at kb2 (free since tile
+                // i-1 is done) and the copy source of tile i+4 (id slot par).  Past
+                // the piece the staged rows are zero rows.
+                auto part2 = [&](int i, int par, int kbv, int kb2, int ln, bool stage, bool copies_out,
+                                 const uint8_t*& src4, int& sdel4, uint32_t& vm4) {
+                    const int vb = kbv + pv_base(ln) + 64 * 4 * wave;
+                    const int xp = xp_base<FS>(ln);
+                    // the copies of tile i+2 and the ids of tile i+4 have landed
+                    // (1 + NDMA newer ops: the ids of tile i+5, the copies of tile
+                    // i+3; none near the end of the piece)
+                    StageRegs g;
+                    if (stage) {
+                        if (copies_out) wait_vmcnt<1 + NDMA>();
+                        else wait_vmcnt<0>();
+                        g = stage_load<FS, false>(lds, slice_off + par * L::RAW_BYTES, ln);
+                    }
+                    bf16x8 va, pf[4];
+    #pragma unroll
+                    for (int hb = 0; hb < HB; ++hb)
+                        pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048));
+                    va = v_frag(lds, vb);
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int jv = 0; jv < 8; ++jv) {
+                        // value step jv: k-step jv / 4, dim block jv % 4; the next V^T
+                        // fragment is read ahead
+                        bf16x8 vn;
+                        if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * NP + ((jv + 1) & 3) * 64);
+    #pragma unroll
+                        for (int hb = 0; hb < HB; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
+                        if (jv == 3) {
+    #pragma unroll
+                            for (int hb = 0; hb < HB; ++hb)
+                                pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048 + 1024));
+                        }
+                        if (jv + 1 < 8) va = vn;
+                        if (stage && jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4, sdel4);
+                        if (stage && jv == 1) stage_chunk<0, FS>(lds, g, kb2, wave, ln);
+                        if (stage && jv == 3) stage_chunk<1, FS>(lds, g, kb2, wave, ln);
+                        if (stage && jv == 5) {
+                            stage_chunk<2, FS>(lds, g, kb2, wave, ln);
+                            if constexpr (FS == F4) g.rope = stage_load_tail(lds, slice_off + par * L::RAW_BYTES, ln);
+                        }
+                        if (stage && jv == 7) {
+                            stage_chunk<3, FS>(lds, g, kb2, wave, ln);
+                            stage_tail<FS>(lds, g, kb2, wave, ln);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                };
+
+                // ---- prologue: ids of tiles 0..4; (first pass) Q through LDS and,
+                // under it, the rows of tile 0 into registers; the copies of tile 1
+                // into raw slot 1; tile 0 staged from the registers into K buffer 0;
+                // copy sources of tiles 2 and 3; the copies of tile 2 into raw slot
+                // 0; the scores of tile 0 with the staging of tile 1.
+                uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles i .. i+3
+                const uint8_t* src_nx;                  // this lane's copy source in tile i+3
+                int sdel_nx = 0;                        // and its scale offset (V4 / V4.1)
+                f32x16 S_cur;                           // scores of tile i
+                {
+                    const int ln = opaque_lane();
+                    for (int t = 0; t < 4; ++t) tile_ids(t, ln, lds0 + first_slot(t));
+                    tile_ids(4, ln, lds0 + ring_slot(4));
+                    if (pass == 0 && load_q && sc_wave) {
+                        // Q of the wave's 32 heads (with 64 query heads waves 2 and
+                        // 3 take heads 0..63 again; those results are never stored)
+                        // copied whole-line into LDS: region row n = head 32w + n,
+                        // QROW bytes (the QCH chunks of a head's Q and a pad chunk,
+                        // so the operand reads are conflict-free).  Copy m, lane l
+                        // moves region chunk 64 m + l.
+                        const uint16_t* q_req = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss;
+                        const uint32_t qreg = lds0 + L::L_Q + wave * 32 * L::QROW;
+                        int n = 0, c = ln;                  // region row and chunk of copy 0
+    #pragma unroll
+                        for (int m = 0; m < L::QCOPIES; ++m) {
+                            const uint16_t* src = q_req + (int64_t)((32 * wave + n) & (p.h_q - 1)) * p.q_sh +
+                                                  8 * (c < L::QCH ? c : 0);
+                            if (m < L::QCOPIES - 1 || ln < 32) dma16(src, qreg + 1024u * m);
+                            c += 64;
+                            if (c >= L::QCH + 1) { c -= L::QCH + 1; n += 1; }
+                        }
+                        wait_vmcnt<L::QCOPIES>();           // ids of tiles 0..4 (the copies of Q are newer)
+                    } else {
+                        wait_vmcnt<0>();                    // ids of tiles 0..4
+                    }
+                    const uint8_t* src;
+                    const uint8_t* src2;
+                    int sdel = 0, sdel2 = 0;
+                    vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src, sdel);
+                    vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src2, sdel2);
+                    // sparse decode: the rows of tile 0 travel while Q lands (NLOAD
+                    // loads per lane, newer than the copies of Q).  (Dense decode
+                    // copies tile 0 after Q: holding these registers across the Q
+                    // reads would make its paged-address instance spill.)
+                    RowRegs r0;
+                    if (!DENSE) r0 = load_rows<FS>(src, sdel, ln, wave);
+                    if (pass == 0 && load_q) {
+                        if (sc_wave) {
+                            // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7
+                            // of head 32w + n for k-step j
+                            if (DENSE) wait_vmcnt<0>();
+                            else wait_vmcnt<Lay<FS>::NLOAD>();
+                            const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5);
+    #pragma unroll
+                            for (int j = 0; j < KSTEPS; ++j)
+                                qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
+                            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                        }
+                        // every wave's reads are done before the staging reuses the area
+                        __syncthreads();
+                    }
+                    const uint32_t rope0 = lds0 + L::L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0 (656-byte rows)
+                    if (DENSE) gather_rows(src, ln, wave, lds0 + slice_off, rope0);
+                    gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off + L::RAW_BYTES, rope0 + L::KBB);
+                    vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2, sdel2);
+                    vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx, sdel_nx);
+                    if (DENSE) {
+                        wait_vmcnt<0>();                    // copies of tiles 0 and 1
+                        stage_rows<FS>(lds, slice_off, L::L_KB, wave, ln);
+                    } else {
+                        rows_wait<NDMA, FS>(r0);             // tile 0 (the copies of tile 1 are newer)
+                        stage_from_regs<FS>(lds, r0, L::L_KB, wave, ln);
+                    }
+                    // raw slot 0 is free (tile 0 staged from registers, or its values
+                    // went through the conversions)
+                    gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off, rope0 + 2 * L::KBB);
+                    wait_vmcnt<NDMA>();                     // the wave's copies of tile 1 (tile 2's are newer)
+                }
+                __syncthreads();                        // tile 0 staged
+                {
+                    // the scores of tile 0 with the staging of tile 1 (raw slot 1)
+                    // between them
+                    const int ln = opaque_lane();
+                    const StageRegs g1 = stage_load<FS>(lds, slice_off + L::RAW_BYTES, ln);
+                    f32x16 none = {};
+                    part1(-1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
+                }
+                __syncthreads();                        // tile 1 staged
+
+                // K buffers of the values, scores and staging of tile i (buffers
+                // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
+                int kb_v = L::L_KB, kb_s = L::L_KB + L::KBB, kb_g = L::L_KB + 2 * L::KBB;
+                // One tile; near the end of the piece the work for tiles past it is
+                // left out: the copies of tile i+3 (and ids of i+5) from tile n-3 on,
+                // the staging of tile i+2 from n-2 on, the scores of tile i+1 at n-1.
+                auto tile = [&](int i, int par, auto tail_c) {
+                    constexpr int left = decltype(tail_c)::value;   // tiles left including i, 0 = more than 3
+                    constexpr bool copies = left == 0, stage = left == 0 || left == 3, scores = left != 1;
+                    // lane-derived offsets are recomputed every tile (cheap VALU)
+                    // rather than held in registers across the loop
+                    const int ln = opaque_lane();
+                    f32x16 S_next;
+                    part1(i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0, S_cur, S_next, nullptr);
+                    __syncthreads();
+                    const uint8_t* src4 = src_nx;
+                    int sdel4 = sdel_nx;
+                    uint32_t vm4 = 0u;
+                    part2(i, par, kb_v, kb_g, ln, stage, copies, src4, sdel4, vm4);
+                    __syncthreads();
+                    S_cur = S_next;
+                    src_nx = src4;
+                    sdel_nx = sdel4;
+                    vm0 = vm1;
+                    vm1 = vm2;
+                    vm2 = vm3;
+                    vm3 = vm4;
+                    const int t = kb_v;
+                    kb_v = kb_s;
+                    kb_s = kb_g;
+                    kb_g = t;
+                };
+                int i = 0;
+                for (; i + 3 < n_tiles; ++i) tile(i, i & 1, std::integral_constant<int, 0>{});
+                if (i + 2 < n_tiles) tile(i, i & 1, std::integral_constant<int, 3>{}), ++i;
+                if (i + 1 < n_tiles) tile(i, i & 1, std::integral_constant<int, 2>{}), ++i;
+                tile(i, i & 1, std::integral_constant<int, 1>{});
+        };
+
         for (int pass = 0;; ++pass) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if ((i & 3) < HB) O[i] = f32x16{};
             l_part = 0.f;
             __syncthreads();                        // LDS free (previous piece / pass done)
-
-            // this wave's raw slice in slot 0 (copy destinations are this
-            // plus constants)
-            const uint32_t raw0 = lds0 + slice_off;
-
-            // Part 1 of tile i: the 36 score MFMAs of tile i+1 (K buffer at
-            // kb) for this wave's 32 heads over all 576 dims (two accumulator
-            // chains) with, between them, the softmax of tile i (mask empty
-            // slots, base-2 exponent against the reference max, P to LDS), the
-            // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
-            // 1 - par for tile parity par).  With soft == false (the prologue)
-            // only the scores of tile 0.
-            auto part1 = [&](int i, int par, int kb, int kb3, int ln, bool soft, bool scores, bool copies,
-                             const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S, f32x16& S_next,
-                             const StageRegs* pro_g) {
-                const int qk = kb + qk_off(ln, 0);      // NoPE k-steps: qk + 32 j
-                const int r3 = 1 - par;
-                const uint32_t raw3 = raw0 + r3 * L::RAW_BYTES;
-                f32x16 Sa, Sb;
-                bf16x8 ka[KAHEAD];
-#pragma unroll
-                for (int j = 0; j < KAHEAD; ++j)
-                    if (scores && sc_wave) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
-                // RoPE k-steps 32..35 of tile i+1 (lane-dependent slots)
-                auto rope_k = [&](int j) { return kb + qk_off(ln, j); };
-                if (soft && copies) tile_ids(i + 5, ln, lds0 + ring_slot(r3));
-                __builtin_amdgcn_sched_barrier(0);
-                float mx, psum = 0.f;
-#pragma unroll
-                for (int js = 0; js < KSTEPS; ++js) {
-                    if (scores && sc_wave) {
-                        const bf16x8 cur = ka[js % KAHEAD];
-                        if (js + KAHEAD < KSTEPS)
-                            ka[js % KAHEAD] = __builtin_bit_cast(
-                                bf16x8, lds_read16(lds, js + KAHEAD < 32 ? qk + 32 * (js + KAHEAD) : rope_k(js + KAHEAD)));
-                        // two alternating accumulator chains: a score MFMA never
-                        // takes the result of the one issued right before it
-                        if (js == 0) mfma_qk_first(Sa, cur, qa[0]);
-                        else if (js == 1) mfma_qk_first(Sb, cur, qa[1]);
-                        else if (js & 1) mfma_qk(Sb, cur, qa[js]);
-                        else mfma_qk(Sa, cur, qa[js]);
+            const int m_hi = min(k_hi, main_top);
+            if (k_lo < m_hi)
+                segment(std::integral_constant<int, F>{}, k_lo, m_hi, idx_main, min(m_hi, len_main), pass, true);
+            if constexpr (EXTRA) {
+                if (k_hi > main_top) {
+                    if (k_lo < m_hi) {
+                        wait_vmcnt<0>();            // copies past the main slots
+                        __syncthreads();            // LDS free for the extra segment
                     }
-                    if (pro_g != nullptr) {
-                        // prologue: tile 1 staged into K buffer 1 under the scores of tile 0
-                        if (js == 4) stage_chunk<0, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
-                        if (js == 12) stage_chunk<1, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
-                        if (js == 20) stage_chunk<2, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
-                        if (js == 28) {
-                            stage_chunk<3, F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
-                            stage_tail<F>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
-                        }
-                    }
-                    if (soft) {
-                        // copies of tile i+3: NoPE chunks into the raw slot, RoPE
-                        // into the staged tile it will occupy (K buffer kb3, whose
-                        // RoPE rows the scores of its previous tile no longer read);
-                        // V4 / V4.1: code chunks, bf16 chunks and scale rows into
-                        // the raw slot
-                        if (copies && js >= 3 && js <= 18 && js % 5 == 3) {
-                            if (F != F4 || js < 18) dma16_at(src3 + 128 * (js / 5), raw3, 1024 * (js / 5));
-                            else if ((ln & 7) < 4) dma16_at(src3 + 384, raw3, 3072);
-                        }
-                        if (copies && js == 23) {
-                            if constexpr (F == F32)
-                                dma16_at(rope_src(src3, ln, wave), lds0 + kb3 + ROPE_OFF + 1024u * wave, 0);
-                            if constexpr (F == F4) dma16_at(src3 + 448, raw3, 4096);
-                        }
-                        if (copies && js == 28) {
-                            if constexpr (F == F32) gather_tail_at(src3, ln, raw3, 4096);
-                            if constexpr (F == F41) {
-                                const uint8_t* ssrc3 = scale_src<F>(src3, sdel3, ln);
-                                if (ln < 8) dma16_at(ssrc3, raw3, 4096);
-                            }
-                            if constexpr (F == F4) {
-                                const uint8_t* ssrc3 = scale_src<F>(src3, sdel3, ln);
-                                if (ln < 16) dma4_at(ssrc3, raw3, 5120);
-                            }
-                        }
-                    }
-                    if (soft && sc_wave) {
-                        if (js == 1 && vm != 0xffffffffu) {
-                            // accumulator element v holds key 8(v/4) + 4h + v%4:
-                            // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
-#pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                const int key = 8 * (v >> 2) + (v & 3);
-                                const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
-                                                       ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
-                                S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
-                            }
-                        }
-                        if (js == 2) {
-                            mx = S[0];
-#pragma unroll
-                            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, S[v]);
-                        }
-                        if (js == 4) {
-                            // max with the other half-wave (same head): the swap hands
-                            // lanes 0..31 the upper half's value in the second result
-                            // and lanes 32..63 the lower half's in the first
-                            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-                            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
-                            const float mnew = mx * p.c;
-                            m_seen = fmaxf(m_seen, mnew);
-                            if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
-                        }
-                        if (js >= 6 && js < 22) {
-                            const int v = js - 6;
-                            S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
-                            psum += S[v];
-                        }
-                        if (js == 24) {
-                            l_part += psum;
-                            lds_write16(lds, xp_base<F>(ln) + wave * 2048, p_fragment(S, 0));
-                        }
-                        if (js == 26) lds_write16(lds, xp_base<F>(ln) + wave * 2048 + 1024, p_fragment(S, 1));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                    const int x_lo = max(k_lo, main_top) - main_top, x_hi = k_hi - main_top;
+                    const int32_t* idx_x = p.x_indices + (int64_t)req * p.x_idx_sb + (int64_t)sq * p.x_idx_ss;
+                    const int x_ok = p.x_topk_length ? min(x_hi, max(p.x_topk_length[req], 0)) : x_hi;
+                    segment(std::integral_constant<int, FX>{}, x_lo, x_hi, idx_x, x_ok, pass, k_lo >= m_hi);
                 }
-                if (scores && sc_wave) {
-                    mfma_result_fence2(Sa, Sb);
-                    S_next = Sa + Sb;
-                }
-            };
-            // Part 2 of tile i: the 32 value MFMAs of tile i (O^T += V^T P^T over
-            // this wave's 128 dims, all 128 heads; V from the K buffer at kbv, P
-            // from LDS) with, between them, the dequant of tile i+2 (raw slot
-            // par) written straight into the K buffer at kb2 (free since tile
-            // i-1 is done) and the copy source of tile i+4 (id slot par).  Past
-            // the piece the staged rows are zero rows.
-            auto part2 = [&](int i, int par, int kbv, int kb2, int ln, bool stage, bool copies_out,
-                             const uint8_t*& src4, int& sdel4, uint32_t& vm4) {
-                const int vb = kbv + pv_base(ln) + 64 * 4 * wave;
-                const int xp = xp_base<F>(ln);
-                // the copies of tile i+2 and the ids of tile i+4 have landed
-                // (1 + NDMA newer ops: the ids of tile i+5, the copies of tile
-                // i+3; none near the end of the piece)
-                StageRegs g;
-                if (stage) {
-                    if (copies_out) wait_vmcnt<1 + NDMA>();
-                    else wait_vmcnt<0>();
-                    g = stage_load<F, false>(lds, slice_off + par * L::RAW_BYTES, ln);
-                }
-                bf16x8 va, pf[4];
-#pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-                    pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048));
-                va = v_frag(lds, vb);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int jv = 0; jv < 8; ++jv) {
-                    // value step jv: k-step jv / 4, dim block jv % 4; the next V^T
-                    // fragment is read ahead
-                    bf16x8 vn;
-                    if (jv + 1 < 8) vn = v_frag(lds, vb + ((jv + 1) >> 2) * 16 * NP + ((jv + 1) & 3) * 64);
-#pragma unroll
-                    for (int hb = 0; hb < HB; ++hb) mfma_pv(O[4 * (jv & 3) + hb], va, pf[hb]);
-                    if (jv == 3) {
-#pragma unroll
-                        for (int hb = 0; hb < HB; ++hb)
-                            pf[hb] = __builtin_bit_cast(bf16x8, lds_read16(lds, xp + hb * 2048 + 1024));
-                    }
-                    if (jv + 1 < 8) va = vn;
-                    if (stage && jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4, sdel4);
-                    if (stage && jv == 1) stage_chunk<0, F>(lds, g, kb2, wave, ln);
-                    if (stage && jv == 3) stage_chunk<1, F>(lds, g, kb2, wave, ln);
-                    if (stage && jv == 5) {
-                        stage_chunk<2, F>(lds, g, kb2, wave, ln);
-                        if constexpr (F == F4) g.rope = stage_load_tail(lds, slice_off + par * L::RAW_BYTES, ln);
-                    }
-                    if (stage && jv == 7) {
-                        stage_chunk<3, F>(lds, g, kb2, wave, ln);
-                        stage_tail<F>(lds, g, kb2, wave, ln);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            };
-
-            // ---- prologue: ids of tiles 0..4; (first pass) Q through LDS and,
-            // under it, the rows of tile 0 into registers; the copies of tile 1
-            // into raw slot 1; tile 0 staged from the registers into K buffer 0;
-            // copy sources of tiles 2 and 3; the copies of tile 2 into raw slot
-            // 0; the scores of tile 0 with the staging of tile 1.
-            uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles i .. i+3
-            const uint8_t* src_nx;                  // this lane's copy source in tile i+3
-            int sdel_nx = 0;                        // and its scale offset (V4 / V4.1)
-            f32x16 S_cur;                           // scores of tile i
-            {
-                const int ln = opaque_lane();
-                for (int t = 0; t < 4; ++t) tile_ids(t, ln, lds0 + first_slot(t));
-                tile_ids(4, ln, lds0 + ring_slot(4));
-                if (pass == 0 && sc_wave) {
-                    // Q of the wave's 32 heads (with 64 query heads waves 2 and
-                    // 3 take heads 0..63 again; those results are never stored)
-                    // copied whole-line into LDS: region row n = head 32w + n,
-                    // QROW bytes (the QCH chunks of a head's Q and a pad chunk,
-                    // so the operand reads are conflict-free).  Copy m, lane l
-                    // moves region chunk 64 m + l.
-                    const uint16_t* q_req = p.q + (int64_t)req * p.q_sb + (int64_t)sq * p.q_ss;
-                    const uint32_t qreg = lds0 + L::L_Q + wave * 32 * L::QROW;
-                    int n = 0, c = ln;                  // region row and chunk of copy 0
-#pragma unroll
-                    for (int m = 0; m < L::QCOPIES; ++m) {
-                        const uint16_t* src = q_req + (int64_t)((32 * wave + n) & (p.h_q - 1)) * p.q_sh +
-                                              8 * (c < L::QCH ? c : 0);
-                        if (m < L::QCOPIES - 1 || ln < 32) dma16(src, qreg + 1024u * m);
-                        c += 64;
-                        if (c >= L::QCH + 1) { c -= L::QCH + 1; n += 1; }
-                    }
-                    wait_vmcnt<L::QCOPIES>();           // ids of tiles 0..4 (the copies of Q are newer)
-                } else {
-                    wait_vmcnt<0>();                    // ids of tiles 0..4
-                }
-                const uint8_t* src;
-                const uint8_t* src2;
-                int sdel = 0, sdel2 = 0;
-                vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src, sdel);
-                vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src2, sdel2);
-                // sparse decode: the rows of tile 0 travel while Q lands (NLOAD
-                // loads per lane, newer than the copies of Q).  (Dense decode
-                // copies tile 0 after Q: holding these registers across the Q
-                // reads would make its paged-address instance spill.)
-                RowRegs r0;
-                if (!DENSE) r0 = load_rows<F>(src, sdel, ln, wave);
-                if (pass == 0) {
-                    if (sc_wave) {
-                        // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7
-                        // of head 32w + n for k-step j
-                        if (DENSE) wait_vmcnt<0>();
-                        else wait_vmcnt<L::NLOAD>();
-                        const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5);
-#pragma unroll
-                        for (int j = 0; j < KSTEPS; ++j)
-                            qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
-                        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-                    }
-                    // every wave's reads are done before the staging reuses the area
-                    __syncthreads();
-                }
-                const uint32_t rope0 = lds0 + L::L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0 (656-byte rows)
-                if (DENSE) gather_rows(src, ln, wave, lds0 + slice_off, rope0);
-                gather_tile<F>(src2, sdel2, ln, wave, lds0 + slice_off + L::RAW_BYTES, rope0 + L::KBB);
-                vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2, sdel2);
-                vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx, sdel_nx);
-                if (DENSE) {
-                    wait_vmcnt<0>();                    // copies of tiles 0 and 1
-                    stage_rows<F>(lds, slice_off, L::L_KB, wave, ln);
-                } else {
-                    rows_wait<NDMA, F>(r0);             // tile 0 (the copies of tile 1 are newer)
-                    stage_from_regs<F>(lds, r0, L::L_KB, wave, ln);
-                }
-                // raw slot 0 is free (tile 0 staged from registers, or its values
-                // went through the conversions)
-                gather_tile<F>(src2, sdel2, ln, wave, lds0 + slice_off, rope0 + 2 * L::KBB);
-                wait_vmcnt<NDMA>();                     // the wave's copies of tile 1 (tile 2's are newer)
             }
-            __syncthreads();                        // tile 0 staged
-            {
-                // the scores of tile 0 with the staging of tile 1 (raw slot 1)
-                // between them
-                const int ln = opaque_lane();
-                const StageRegs g1 = stage_load<F>(lds, slice_off + L::RAW_BYTES, ln);
-                f32x16 none = {};
-                part1(-1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
-            }
-            __syncthreads();                        // tile 1 staged
-
-            // K buffers of the values, scores and staging of tile i (buffers
-            // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
-            int kb_v = L::L_KB, kb_s = L::L_KB + L::KBB, kb_g = L::L_KB + 2 * L::KBB;
-            // One tile; near the end of the piece the work for tiles past it is
-            // left out: the copies of tile i+3 (and ids of i+5) from tile n-3 on,
-            // the staging of tile i+2 from n-2 on, the scores of tile i+1 at n-1.
-            auto tile = [&](int i, int par, auto tail_c) {
-                constexpr int left = decltype(tail_c)::value;   // tiles left including i, 0 = more than 3
-                constexpr bool copies = left == 0, stage = left == 0 || left == 3, scores = left != 1;
-                // lane-derived offsets are recomputed every tile (cheap VALU)
-                // rather than held in registers across the loop
-                const int ln = opaque_lane();
-                f32x16 S_next;
-                part1(i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0, S_cur, S_next, nullptr);
-                __syncthreads();
-                const uint8_t* src4 = src_nx;
-                int sdel4 = sdel_nx;
-                uint32_t vm4 = 0u;
-                part2(i, par, kb_v, kb_g, ln, stage, copies, src4, sdel4, vm4);
-                __syncthreads();
-                S_cur = S_next;
-                src_nx = src4;
-                sdel_nx = sdel4;
-                vm0 = vm1;
-                vm1 = vm2;
-                vm2 = vm3;
-                vm3 = vm4;
-                const int t = kb_v;
-                kb_v = kb_s;
-                kb_s = kb_g;
-                kb_g = t;
-            };
-            int i = 0;
-            for (; i + 3 < n_tiles; ++i) tile(i, i & 1, std::integral_constant<int, 0>{});
-            if (i + 2 < n_tiles) tile(i, i & 1, std::integral_constant<int, 3>{}), ++i;
-            if (i + 1 < n_tiles) tile(i, i & 1, std::integral_constant<int, 2>{}), ++i;
-            tile(i, i & 1, std::integral_constant<int, 1>{});
             // the reference stays fixed once set, so one test of the largest
             // score max of the pass covers every tile
             const bool restart = __any(m_seen > m_ref + p.threshold);
@@ -1179,8 +1273,8 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
             nan_out ? __builtin_nanf("") : M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
 }
 
-// per instance: dynamic LDS size allowed (FLAT, DENSE, H64, format 0 / V4 / V4.1)
-bool g_lds_decode[2][2][2][3] = {}, g_lds_gather = false;
+// per instance: dynamic LDS size allowed (FLAT, DENSE, H64, format 656 / V4 / V4.1 / V4.1 + FP4)
+bool g_lds_decode[2][2][2][4] = {}, g_lds_gather = false;
 
 template <typename K>
 hipError_t allow_lds_once(K k, bool& done, int bytes) {
@@ -1190,27 +1284,29 @@ hipError_t allow_lds_once(K k, bool& done, int bytes) {
     return e;
 }
 
-template <bool FLAT, bool DENSE, bool H64, int F>
+template <bool FLAT, bool DENSE, bool H64, int F, bool EXTRA = false>
 hipError_t launch_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
-    constexpr int fi = F == F32 ? 0 : F == F4 ? 1 : 2;
-    hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE, H64, F>, g_lds_decode[FLAT][DENSE][H64][fi],
-                                  Lay<F>::L_BYTES);
+    constexpr int fi = F == F32 ? 0 : F == F4 ? 1 : EXTRA ? 3 : 2;
+    hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE, H64, F, EXTRA>,
+                                  g_lds_decode[FLAT][DENSE][H64][fi], Lay<F>::L_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE, H64, F>), dim3(num_parts, p.s_q), dim3(NW * 64),
+    hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE, H64, F, EXTRA>), dim3(num_parts, p.s_q), dim3(NW * 64),
                        Lay<F>::L_BYTES, st, p);
     return hipGetLastError();
 }
-template <bool FLAT, bool DENSE, int F = F32>
+template <bool FLAT, bool DENSE, int F = F32, bool EXTRA = false>
 hipError_t launch_h128_heads(const DecodeParams& p, int num_parts, hipStream_t st) {
-    return p.h_q == 64 ? launch_h128<FLAT, DENSE, true, F>(p, num_parts, st)
-                       : launch_h128<FLAT, DENSE, false, F>(p, num_parts, st);
+    return p.h_q == 64 ? launch_h128<FLAT, DENSE, true, F, EXTRA>(p, num_parts, st)
+                       : launch_h128<FLAT, DENSE, false, F, EXTRA>(p, num_parts, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode_fp8_h128(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
     if (kv_format == MLA_KV_V4_584) return launch_h128_heads<false, false, F4>(p, num_parts, st);
-    if (kv_format == MLA_KV_V41_528) return launch_h128_heads<false, false, F41>(p, num_parts, st);
+    if (kv_format == MLA_KV_V41_528)
+        return p.x_kv != nullptr ? launch_h128_heads<false, false, F41, true>(p, num_parts, st)
+                                 : launch_h128_heads<false, false, F41>(p, num_parts, st);
     const bool dense = p.block_table != nullptr;
     if (p.kv_flat)
         return dense ? launch_h128_heads<true, true>(p, num_parts, st) : launch_h128_heads<true, false>(p, num_parts, st);

@@ -56,11 +56,20 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // 256 VGPRs + 256 AGPRs: the output accumulator takes all AGPRs; Q, the score
 // accumulators and everything else live in VGPRs.  Without the constraints the
 // compiler puts every accumulator in AGPRs and spills.
+// GUARD: two wait states before the MFMA.  When spare AGPRs exist (a kernel
+// whose accumulators leave some free) the compiler may park an operand there
+// and reload it into its VGPR right before the asm; that VALU write followed
+// by the MFMA's read needs two wait states, and the compiler's hazard
+// recognizer does not insert them for inline asm.
+template <bool GUARD = false>
 __device__ __forceinline__ void mfma_qk_first(f32x16& s, const bf16x8& a, const bf16x8& q) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(q));
+    if (GUARD) asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(q));
+    else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(q));
 }
+template <bool GUARD = false>
 __device__ __forceinline__ void mfma_qk(f32x16& s, const bf16x8& a, const bf16x8& q) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(q));
+    if (GUARD) asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(q));
+    else asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(q));
 }
 __device__ __forceinline__ void mfma_pv(f32x16& o, const bf16x8& a, const bf16x8& pm) {
     o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pm, o, 0, 0, 0);

@@ -211,6 +211,18 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         p->page_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - P)) / P + 1);
     }
     p->packed_partials = r.kv_format != MLA_KV_BF16_576;     // the 128-head FP8 kernel
+    p->x_kv = nullptr;                                        // no extra cache (mla_sparse_decode_extra_fwd)
+    p->x_indices = nullptr;
+    p->x_topk_length = nullptr;
+    p->x_block_stride = 0;
+    p->x_idx_sb = p->x_idx_ss = 0;
+    p->main_topk = r.topk;
+    p->x_topk = 0;
+    p->x_page_block_size = 1;
+    p->x_page_mshift = 0;
+    p->x_page_magic = 0;
+    p->x_scale_off = 0;
+    p->x_n_tok32 = 0;
     p->soa_scale_off = r.kv_format == MLA_KV_V4_584    ? (uint32_t)(r.page_block_size * 576)
                        : r.kv_format == MLA_KV_V41_528 ? (uint32_t)(r.page_block_size * 512)
                                                        : 0u;
@@ -342,6 +354,48 @@ int mla_sparse_decode_fwd(const mla_decode_args* args, void* stream) {
     mla::DecodeParams p;
     int st = check_decode_args(args, &r, &p);
     if (st != MLA_OK) return st;
+    return hip_status(mla::launch_decode(p, r.kv_format, r.num_parts, static_cast<hipStream_t>(stream)),
+                      "decode kernel launch");
+}
+
+int mla_sparse_decode_extra_fwd(const mla_decode_args* args, const mla_extra_kv* x, void* stream) {
+    mla::ResolvedShape r;
+    mla::DecodeParams p;
+    int st = check_decode_args(args, &r, &p);
+    if (st != MLA_OK) return st;
+    if (r.kv_format != MLA_KV_V41_528)
+        return fail(MLA_ERR_UNSUPPORTED, "an FP4 extra cache goes with the V4.1 main cache (kv_format %d)", r.kv_format);
+    if (!x) return fail(MLA_ERR_INVALID_ARG, "extra is NULL");
+    if (x->extra_topk < 1 || x->extra_topk >= r.topk)
+        return fail(MLA_ERR_INVALID_ARG, "extra_topk must be in [1, shape.topk) (got %d of %d)", x->extra_topk, r.topk);
+    const int64_t P = x->page_block_size;
+    if (P < 1 || P * 288 >= (1ll << 31))
+        return fail(MLA_ERR_INVALID_ARG, "extra page_block_size must be >= 1 with P * 288 < 2^31 (got %lld)",
+                    (long long)P);
+    if (x->num_kv_tokens < 1 || x->num_kv_tokens >= INT32_MAX || x->num_kv_tokens % P != 0)
+        return fail(MLA_ERR_INVALID_ARG, "extra num_kv_tokens must be a multiple of its page size in [1, 2^31)");
+    if (!x->kv || !aligned(x->kv, 16) || x->kv_stride_block % 16 || x->kv_stride_block < P * 288)
+        return fail(MLA_ERR_INVALID_ARG,
+                    "extra kv must be 16-byte aligned with kv_stride_block >= page_block_size * 288, a multiple of 16");
+    if (!x->indices || !aligned(x->indices, 4) || (x->topk_length && !aligned(x->topk_length, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "extra indices (and topk_length) must be non-NULL, 4-byte aligned");
+    p.main_topk = r.topk - x->extra_topk;
+    p.x_topk = x->extra_topk;
+    p.x_kv = static_cast<const uint8_t*>(x->kv);
+    p.x_block_stride = x->kv_stride_block;
+    p.x_indices = x->indices;
+    p.x_idx_sb = x->idx_stride_b;
+    p.x_idx_ss = x->idx_stride_s;
+    p.x_topk_length = x->topk_length;
+    p.x_page_block_size = (int)P;
+    {
+        int l = 0;                                            // division by P as a multiply-high (as above)
+        while ((1ll << l) < P) ++l;
+        p.x_page_mshift = l;
+        p.x_page_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - (uint64_t)P)) / (uint64_t)P + 1);
+    }
+    p.x_scale_off = (uint32_t)(P * 256);
+    p.x_n_tok32 = (uint32_t)x->num_kv_tokens;
     return hip_status(mla::launch_decode(p, r.kv_format, r.num_parts, static_cast<hipStream_t>(stream)),
                       "decode kernel launch");
 }

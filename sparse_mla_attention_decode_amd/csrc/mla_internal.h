@@ -62,6 +62,16 @@ struct DecodeParams {
     int page_mshift;                // for 0 <= t < 2^31 (round-up reciprocal)
     int packed_partials;            // split partials as packed bf16 (128-head FP8 decode)
     uint32_t soa_scale_off;         // V4 / V4.1: byte offset of a page's scale rows (P * data row)
+    // FP4 extra cache beside a V4.1 main cache (x_kv NULL: none).  Its slots
+    // follow the main ones: slot k >= main_topk is extra slot k - main_topk,
+    // and topk counts both.
+    const uint8_t* x_kv;
+    int64_t x_block_stride;
+    const int32_t* x_indices;
+    int64_t x_idx_sb, x_idx_ss;
+    const int32_t* x_topk_length;   // NULL or [b]
+    int main_topk, x_topk, x_page_block_size, x_page_mshift;
+    uint32_t x_page_magic, x_scale_off, x_n_tok32;
     int kv_flat;                    // FP8 pages back to back, n_tok < 2^24 and n_tok * 656 < 2^32:
                                     // the row of token t is kv + 656 t (32-bit offset)
     // closed-form plan (per-request cost zero): B blocks per request, total
@@ -141,7 +151,8 @@ __device__ __forceinline__ PartPlan plan_part(const DecodeParams& p, int part) {
 // nothing and the combine writes NaN to every output (split and unsplit
 // requests alike), instead of silently mixing the two kinds of plan.
 __device__ __forceinline__ bool lengths_missing(const DecodeParams& p) {
-    return p.sched_meta != nullptr && p.topk_length == nullptr && p.sched_meta[7] != 0;
+    // (also a length plan with an extra cache: such a plan covers main slots only)
+    return p.sched_meta != nullptr && p.sched_meta[7] != 0 && (p.topk_length == nullptr || p.x_kv != nullptr);
 }
 
 // Split index of the first piece of request r (the number of pieces at r = b).

@@ -59,6 +59,10 @@ SOA = {KV_V4_584: (576, 8, 448, 64), KV_V41_528: (512, 16, 512, 32)}
 def d_qk_of(kv_format: int) -> int:
     return D_QK_SOA if kv_format in SOA else D_QK
 
+
+FP4_DATA, FP4_SCALE = 256, 32    # FP4 extra cache token: 512 e2m1 (two per byte) | 32 e8m0
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
 BASE_SEED = 20261202
 
 
@@ -121,6 +125,61 @@ def encode_soa_tokens(x: np.ndarray, kv_format: int) -> np.ndarray:
         out[:, nq:db] = to_bf16_bits(x[:, nq:]).astype("<u2").view(np.uint8).reshape(n, 2 * (D_QK_SOA - nq))
     out[:, db:db + nq // grp] = (exp + 127).astype(np.uint8)
     return out
+
+
+def encode_fp4_tokens(x: np.ndarray) -> np.ndarray:
+    """Quantise tokens x float32 [n, 512] for the FP4 extra cache: per 16
+    dims, amax clamped to 1e-4, scale = 2**ceil(log2(amax / 6)), code = the
+    nearest e2m1 value of x / scale (ties to the even code), element 2i in
+    the low nibble of byte i.  Returns uint8 [n, 288]: data row, scale row."""
+    n = x.shape[0]
+    g = x.astype(np.float64).reshape(n, 32, 16)
+    amax = np.maximum(np.abs(g).max(axis=-1), 1e-4)
+    m, e = np.frexp(amax / 6.0)
+    exp = np.where(m == 0.5, e - 1, e)                                     # [n, 32]
+    y = g / np.ldexp(np.ones_like(amax), exp)[:, :, None]
+    d = np.abs(np.abs(y)[..., None] - E2M1_GRID) + 1e-9 * (np.arange(8) % 2)
+    code = (np.argmin(d, axis=-1) | np.where(y < 0, 8, 0)).astype(np.uint8).reshape(n, 512)
+    out = np.empty((n, FP4_DATA + FP4_SCALE), dtype=np.uint8)
+    out[:, :FP4_DATA] = code[:, 0::2] | (code[:, 1::2] << 4)
+    out[:, FP4_DATA:] = (exp + 127).astype(np.uint8)
+    return out
+
+
+@dataclasses.dataclass
+class ExtraCache:
+    """An FP4 extra cache and its slots (beside a V4.1 main cache)."""
+    page_block_size: int
+    num_blocks: int
+    indices: np.ndarray          # int32 [b, s_q, extra_topk]
+    ref_ids: np.ndarray          # int64 sorted unique referenced tokens
+    ref_rows: np.ndarray         # uint8 [n_ref, 288]
+    page_pad: int = 0
+    fill_byte: int = 0xFF
+
+    @property
+    def num_kv_tokens(self) -> int:
+        return self.num_blocks * self.page_block_size
+
+    @property
+    def page_stride(self) -> int:
+        return (self.page_block_size * (FP4_DATA + FP4_SCALE) + self.page_pad + 15) // 16 * 16
+
+    def kv_host(self) -> np.ndarray:
+        P = self.page_block_size
+        kv = np.full((self.num_blocks, self.page_stride), self.fill_byte, dtype=np.uint8)
+        data = kv[:, :P * FP4_DATA].reshape(-1, P, FP4_DATA)
+        scales = kv[:, P * FP4_DATA:P * (FP4_DATA + FP4_SCALE)].reshape(-1, P, FP4_SCALE)
+        blk, off = self.ref_ids // P, self.ref_ids % P
+        data[blk, off] = self.ref_rows[:, :FP4_DATA]
+        scales[blk, off] = self.ref_rows[:, FP4_DATA:]
+        return kv
+
+    def kv_device(self, device="cuda") -> torch.Tensor:
+        return torch.from_numpy(self.kv_host()).to(device)
+
+    def indices_device(self, device="cuda") -> torch.Tensor:
+        return torch.from_numpy(self.indices).to(device)
 
 
 # ----------------------------------------------------------------------------
@@ -298,6 +357,30 @@ def paged_decode(name: str, seed: int, b: int, s_q: int, h_q: int, topk: int,
     meta = {"block_table_shape": list(block_table.shape), "short_seqs": short_seqs.tolist()}
     return _finish(name, rng, kv_format, b, s_q, h_q, topk, P, total_pages * P, indices, meta,
                    page_pad=page_pad)
+
+
+def extra_decode(name: str, seed: int, b: int, s_q: int, h_q: int, topk: int, extra_topk: int,
+                 tokens_per_seq: int, extra_tokens_per_seq: int, P: int = 64, extra_P: int = 64,
+                 extra_pad: int = 0) -> Workload:
+    """A V4.1 paged decode workload (topk main slots per query token) with an
+    FP4 extra cache in meta["extra"] (ExtraCache): every request owns
+    extra_tokens_per_seq / extra_P pages of it, dealt from a shuffled
+    permutation, and each query token picks extra_topk distinct positions of
+    them."""
+    w = paged_decode(name, seed, b, s_q, h_q, topk, tokens_per_seq, P=P, kv_format=KV_V41_528)
+    rng = np.random.default_rng(seed + 7919)
+    pages = extra_tokens_per_seq // extra_P
+    table = rng.permutation(b * pages).reshape(b, pages)
+    idx = np.full((b, s_q, extra_topk), -1, dtype=np.int32)
+    for bi in range(b):
+        for sj in range(s_q):
+            pos = _distinct(rng, extra_tokens_per_seq, extra_topk)
+            idx[bi, sj] = table[bi, pos // extra_P] * extra_P + pos % extra_P
+    ref = np.unique(idx[idx >= 0].astype(np.int64))
+    rows = encode_fp4_tokens(rng.standard_normal((len(ref), D_QK_SOA), dtype=np.float32))
+    w.meta = dict(w.meta or {}, extra=ExtraCache(page_block_size=extra_P, num_blocks=b * pages, indices=idx,
+                                                 ref_ids=ref, ref_rows=rows, page_pad=extra_pad))
+    return w
 
 
 def dense_decode(name: str, seed: int, b: int, s_q: int, h_q: int, seqlens, pages_per_seq: int,

@@ -448,3 +448,32 @@ def test_struct_of_arrays_shapes(fmt, tok_b):
     with pytest.raises(M.MlaError) as e:
         M.mla_dense_decode_fwd(_args(s, **ok, indices=None, topk_length=0xA000), 0xB000, 2, 0, stream=0)
     assert e.value.code == M.MLA_ERR_UNSUPPORTED
+
+
+def test_extra_cache_args_validated():
+    """mla_sparse_decode_extra_fwd: V4.1 main cache only, extra_topk in
+    [1, shape.topk), the extra page geometry, pointers -- all before a launch."""
+    s = shape(kv_format=M.MLA_KV_V41_528, topk=160)
+    ok = dict(kv_stride_block=64 * 528, q_stride_b=128 * 512, q_stride_s=128 * 512, q_stride_h=512)
+
+    def x(**over):
+        e = M.mla_extra_kv()
+        e.kv, e.kv_stride_block, e.page_block_size, e.num_kv_tokens = 0xE000, 64 * 288, 64, 512
+        e.indices, e.idx_stride_b, e.idx_stride_s, e.extra_topk = 0xF000, 60, 60, 60
+        for k, v in over.items():
+            setattr(e, k, v)
+        return e
+    cases = [(x(extra_topk=0), M.MLA_ERR_INVALID_ARG), (x(extra_topk=160), M.MLA_ERR_INVALID_ARG),
+             (x(page_block_size=0), M.MLA_ERR_INVALID_ARG), (x(num_kv_tokens=100), M.MLA_ERR_INVALID_ARG),
+             (x(kv=None), M.MLA_ERR_INVALID_ARG), (x(kv=0xE008), M.MLA_ERR_INVALID_ARG),
+             (x(kv_stride_block=64 * 288 - 16), M.MLA_ERR_INVALID_ARG), (x(indices=None), M.MLA_ERR_INVALID_ARG),
+             (x(topk_length=0xA002), M.MLA_ERR_INVALID_ARG),
+             (x(page_block_size=1 << 23, num_kv_tokens=1 << 23, kv_stride_block=(1 << 23) * 288),
+              M.MLA_ERR_INVALID_ARG)]
+    for e, code in cases:
+        with pytest.raises(M.MlaError) as err:
+            M.mla_sparse_decode_extra_fwd(_args(s, **ok), e, stream=0)
+        assert err.value.code == code, M.mla_last_error()
+    with pytest.raises(M.MlaError) as err:                           # main cache not V4.1
+        M.mla_sparse_decode_extra_fwd(_args(shape(topk=160)), x(), stream=0)
+    assert err.value.code == M.MLA_ERR_UNSUPPORTED

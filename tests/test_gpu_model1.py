@@ -159,3 +159,86 @@ def test_decode_bench_shape_sampled(fmt):
     queries = [(0, 0), (17, 0), (42, 0), (63, 0)]
     ref_out, ref_lse = _oracle(w, queries=queries)
     _check(out, lse, ref_out, ref_lse, queries, f"{fmt} b64 topk2048")
+
+
+# ----------------------------------------------------------------------------- FP4 extra cache
+def _run_extra(w, main_len=None, extra_len=None, attn_sink=None, **kw):
+    _need_gpu()
+    x = w.meta["extra"]
+    xk = x.indices.shape[2]
+    shape = M.make_shape(w.b, w.s_q, w.h_q, w.topk + xk, w.num_kv_tokens, w.kv_format, w.page_block_size, **kw)
+    plan = M.DecodePlan(shape)
+    d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    xl = d(None if extra_len is None else np.asarray(extra_len, np.int32))
+    extra = M.extra_kv_args(x.kv_device(), x.page_block_size, x.indices_device(), xl)
+    out, lse = plan.run_extra(w.q_device(), w.kv_device(), w.indices_device(), extra, w.sm_scale,
+                              attn_sink=d(attn_sink),
+                              topk_length=d(None if main_len is None else np.asarray(main_len, np.int32)))
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _oracle_extra(w, queries=None, main_len=None, extra_len=None, attn_sink=None):
+    x = w.meta["extra"]
+    return O.sparse_mla_decode(w.q_bits, w.kv_host(), w.indices, w.sm_scale, w.kv_format, w.page_block_size,
+                               queries=queries, attn_sink=attn_sink, topk_length=main_len,
+                               extra={"kv": x.kv_host(), "indices": x.indices, "page_block_size": x.page_block_size,
+                                      "topk_length": extra_len})
+
+
+@pytest.mark.parametrize("h_q", [128, 64])
+@pytest.mark.parametrize("parts,gran", [(0, 32), (1, 32), (7, 32), (5, 64)])
+def test_extra_cache_small(h_q, parts, gran):
+    # 100 main + 60 extra slots: the main / extra boundary inside a tile, and
+    # pieces that straddle it (split and unsplit requests)
+    w = W.extra_decode("x-small", 1000 + h_q + parts, b=3, s_q=2, h_q=h_q, topk=100, extra_topk=60,
+                       tokens_per_seq=512, extra_tokens_per_seq=256, extra_P=16, extra_pad=40)
+    out, lse = _run_extra(w, num_parts=parts, split_granularity=gran)
+    ref_out, ref_lse = _oracle_extra(w)
+    _check(out, lse, ref_out, ref_lse, _all(w), f"extra h={h_q} parts={parts} G={gran}")
+
+
+def test_extra_cache_lengths_sink_and_empty_parts():
+    w = W.extra_decode("x-len", 1100, b=4, s_q=2, h_q=128, topk=96, extra_topk=64, tokens_per_seq=512,
+                       extra_tokens_per_seq=512, extra_P=64)
+    x = w.meta["extra"]
+    x.indices[3, 1, :] = -1                                # request 3, token 1: no extra slot
+    x.indices[2, 0, 5] = x.num_kv_tokens + 2              # out of range: empty
+    main_len = [0, 96, 40, 7]                              # request 0: extra slots only
+    extra_len = [64, 0, 20, 64]                            # request 1: main slots only
+    sink = np.random.default_rng(1101).standard_normal(128).astype(np.float32)
+    for parts in (1, 9):
+        out, lse = _run_extra(w, main_len=main_len, extra_len=extra_len, attn_sink=sink, num_parts=parts,
+                              split_granularity=32)
+        ref_out, ref_lse = _oracle_extra(w, main_len=np.array(main_len), extra_len=np.array(extra_len),
+                                         attn_sink=sink)
+        _check(out, lse, ref_out, ref_lse, _all(w), f"extra lengths + sink parts={parts}")
+
+
+def test_extra_cache_single_token_is_exact():
+    """No main slot and every extra slot the same token: out = that FP4 token's
+    512 values exactly (e2m1 times a power of two is exact in bf16)."""
+    w = W.extra_decode("x-rep", 1200, b=2, s_q=1, h_q=128, topk=64, extra_topk=96, tokens_per_seq=256,
+                       extra_tokens_per_seq=256)
+    w.indices[:] = -1
+    x = w.meta["extra"]
+    x.indices[:] = x.indices[:, :, :1]
+    out, lse = _run_extra(w, num_parts=1)
+    kvx = x.kv_host()
+    for bi in range(w.b):
+        rows, _ = O.gather_dequant(kvx, x.indices[bi, 0, :1], O.FMT_FP4, x.page_block_size)
+        assert np.array_equal(out[bi, 0], np.broadcast_to(rows[0], (128, 512)).astype(np.float32))
+        s = O.bf16_value(w.q_bits[bi, 0]) @ rows[0] * w.sm_scale
+        assert np.all(np.abs(lse[bi, :, 0] - (s + math.log(96))) <= LSE_TOL)
+    print("[model1 extra single token] exact", flush=True)
+
+
+def test_extra_cache_bench_shape_sampled():
+    """2048 main + 512 extra slots per query token, 64 requests, 128 heads,
+    the default launch (one work-group per CU): sampled query tokens."""
+    w = W.extra_decode("x-b64", 1300, b=64, s_q=1, h_q=128, topk=2048, extra_topk=512, tokens_per_seq=32768,
+                       extra_tokens_per_seq=8192)
+    out, lse = _run_extra(w)
+    queries = [(0, 0), (21, 0), (63, 0)]
+    ref_out, ref_lse = _oracle_extra(w, queries=queries)
+    _check(out, lse, ref_out, ref_lse, queries, "extra b64 2048+512")
