@@ -721,10 +721,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // slots, base-2 exponent against the reference max, P to LDS), the
                 // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
                 // 1 - par for tile parity par).  With soft == false (the prologue)
-                // only the scores of tile 0.
-                auto part1 = [&](int i, int par, int kb, int kb3, int ln, bool soft, bool scores, bool copies,
-                                 const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S, f32x16& S_next,
-                                 const StageRegs* pro_g) {
+                // only the scores of tile 0.  sc_c: whether this wave scores
+                // (compile time, so a wave that does not takes no branch per step).
+                auto part1 = [&](auto sc_c, int i, int par, int kb, int kb3, int ln, bool soft, bool scores,
+                                 bool copies, const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S,
+                                 f32x16& S_next, const StageRegs* pro_g) {
+                    constexpr bool SC = decltype(sc_c)::value;
                     const int qk = kb + qk_off(ln, 0);      // NoPE k-steps: qk + 32 j
                     const int r3 = 1 - par;
                     const uint32_t raw3 = raw0 + r3 * L::RAW_BYTES;
@@ -732,7 +734,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     bf16x8 ka[KAHEAD];
     #pragma unroll
                     for (int j = 0; j < KAHEAD; ++j)
-                        if (scores && sc_wave) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
+                        if (scores && SC) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
                     // RoPE k-steps 32..35 of tile i+1 (lane-dependent slots)
                     auto rope_k = [&](int j) { return kb + qk_off(ln, j); };
                     if (soft && copies) tile_ids(i + 5, ln, lds0 + ring_slot(r3));
@@ -740,7 +742,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     float mx, psum = 0.f;
     #pragma unroll
                     for (int js = 0; js < KSTEPS; ++js) {
-                        if (scores && sc_wave) {
+                        if (scores && SC) {
                             const bf16x8 cur = ka[js % KAHEAD];
                             if (js + KAHEAD < KSTEPS)
                                 ka[js % KAHEAD] = __builtin_bit_cast(
@@ -795,7 +797,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                 }
                             }
                         }
-                        if (soft && sc_wave) {
+                        if (soft && SC) {
                             if (js == 1 && vm != 0xffffffffu) {
                                 // accumulator element v holds key 8(v/4) + 4h + v%4:
                                 // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
@@ -835,7 +837,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                    if (scores && sc_wave) {
+                    if (scores && SC) {
                         mfma_result_fence2(Sa, Sb);
                         S_next = Sa + Sb;
                     }
@@ -979,7 +981,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     const int ln = opaque_lane();
                     const StageRegs g1 = stage_load<FS>(lds, slice_off + L::RAW_BYTES, ln);
                     f32x16 none = {};
-                    part1(-1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
+                    if (sc_wave) part1(std::true_type{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
+                    else if constexpr (H64)
+                        part1(std::false_type{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
                 }
                 __syncthreads();                        // tile 1 staged
 
@@ -996,7 +1000,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     // rather than held in registers across the loop
                     const int ln = opaque_lane();
                     f32x16 S_next;
-                    part1(i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0, S_cur, S_next, nullptr);
+                    if (sc_wave)
+                        part1(std::true_type{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0, S_cur,
+                              S_next, nullptr);
+                    else if constexpr (H64)
+                        part1(std::false_type{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0,
+                              S_cur, S_next, nullptr);
                     __syncthreads();
                     const uint8_t* src4 = src_nx;
                     int sdel4 = sdel_nx;
