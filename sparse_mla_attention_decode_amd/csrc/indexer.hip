@@ -19,6 +19,13 @@ __device__ __forceinline__ int clamp_len(const IndexerParams& p, int r) {
     return min(max(p.seq_len[r], 0), p.max_pages * IX_PAGE);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32 contiguous bytes of an operand row as the 8-dword operand of a k-64 MFMA
+__device__ __forceinline__ i32x8 join8(u32x4 a, u32x4 b) {
+    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) {          // nearest, ties to even
     const uint32_t u = __float_as_uint(x);
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
@@ -35,7 +42,7 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {          // nearest,
 // lane reads 64 contiguous bytes of its head row and of its token row.  The
 // per-token scale multiplies the head sum (it is positive, so it commutes
 // with the ReLU: section 5.3).
-__global__ void __launch_bounds__(IX_WAVES * 64) indexer_score_kernel(IndexerParams p) {
+__global__ void __launch_bounds__(IX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3))) indexer_score_kernel(IndexerParams p) {
     const int r = blockIdx.y;
     const int len = clamp_len(p, r);
     if (len <= p.topk) return;                                   // passthrough row
@@ -45,53 +52,78 @@ __global__ void __launch_bounds__(IX_WAVES * 64) indexer_score_kernel(IndexerPar
     const int hf = lane >> 5, col = lane & 31;
     const int nt = p.n_heads >> 5;                               // 1 or 2 head tiles
 
-    long qa[2][8];
+    i32x8 qa[2][2];
     float wv[2][16];
     const uint8_t* qr = p.q + (size_t)r * p.n_heads * IX_DIM;
     const float* wr = p.weights + (size_t)r * p.n_heads;
     for (int tile = 0; tile < 2; ++tile) {
         const int ht = tile < nt ? tile : 0;
         const u32x4* src = (const u32x4*)(qr + (ht * 32 + col) * IX_DIM + 64 * hf);
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 v = src[c];
-            qa[tile][2 * c] = (long)(((uint64_t)v[1] << 32) | v[0]);
-            qa[tile][2 * c + 1] = (long)(((uint64_t)v[3] << 32) | v[2]);
-        }
+        for (int s = 0; s < 2; ++s) qa[tile][s] = join8(src[2 * s], src[2 * s + 1]);
         for (int i = 0; i < 16; ++i)
             wv[tile][i] = tile < nt ? wr[ht * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)] : 0.0f;
     }
 
-    uint16_t* out = p.scores + (size_t)r * p.max_pages * IX_PAGE;
+    // the wave's page-table entries up front (one round trip), then the keys
+    // of page s + 1 in flight while page s is scored
+    const int32_t* pt = p.page_table + (size_t)r * p.max_pages;
+    int pgs[IX_PAGES_PER_WAVE];
+    int n_steps = 0;
+#pragma unroll
     for (int step = 0; step < IX_PAGES_PER_WAVE; ++step) {
-    const int page_l = first_page + step * IX_WAVES;
-    const int t0 = page_l * IX_PAGE;
-    if (t0 >= len) break;                                        // page_l < max_pages below
-    const int pg = p.page_table[(size_t)r * p.max_pages + page_l];
-    const bool ok = pg >= 0 && pg < p.num_pages;
-    const uint8_t* page = p.kcache + (size_t)(ok ? pg : 0) * IX_PAGE_BYTES;
-
-    for (int g = 0; g < 2; ++g) {
-        const int tok = g * 32 + col;
-        const u32x4* ks = (const u32x4*)(page + tok * IX_DIM + 64 * hf);
-        long kb[8];
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 v = ks[c];
-            kb[2 * c] = (long)(((uint64_t)v[1] << 32) | v[0]);
-            kb[2 * c + 1] = (long)(((uint64_t)v[3] << 32) | v[2]);
-        }
-        float sum = 0.0f;
-        for (int tile = 0; tile < 2; ++tile) {
-            if (tile >= nt) break;
-            f32x16 acc = {};
-            for (int s = 0; s < 8; ++s)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(qa[tile][s], kb[s], acc, 0, 0, 0);
-            for (int i = 0; i < 16; ++i) sum += wv[tile][i] * fmaxf(acc[i], 0.0f);
-        }
-        sum += __shfl_xor(sum, 32);
-        const float scale = ((const float*)(page + IX_PAGE * IX_DIM))[tok];
-        const int t = t0 + tok;
-        if (hf == 0 && t < len) out[t] = ok ? to_bf16_bits(sum * scale) : (uint16_t)0xFF80u;   // -inf
+        const int page_l = first_page + step * IX_WAVES;
+        const bool in = page_l * IX_PAGE < len;                  // then page_l < max_pages
+        pgs[step] = in ? pt[page_l] : -1;
+        n_steps += in ? 1 : 0;
     }
+    struct PageRegs {
+        i32x8 kb[2][2];
+        float scale[2];
+    };
+    auto load_page = [&](int step, PageRegs& d) {
+        const int pg = pgs[step];
+        const bool ok = pg >= 0 && pg < p.num_pages;
+        const uint8_t* page = p.kcache + (size_t)(ok ? pg : 0) * IX_PAGE_BYTES;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int tok = g * 32 + col;
+            const u32x4* ks = (const u32x4*)(page + tok * IX_DIM + 64 * hf);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) d.kb[g][s] = join8(ks[2 * s], ks[2 * s + 1]);
+            d.scale[g] = ((const float*)(page + IX_PAGE * IX_DIM))[tok];
+        }
+    };
+
+    uint16_t* out = p.scores + (size_t)r * p.max_pages * IX_PAGE;
+    PageRegs buf[2];
+    load_page(0, buf[0]);
+#pragma unroll
+    for (int step = 0; step < IX_PAGES_PER_WAVE; ++step) {
+        if (step >= n_steps) break;
+        if (step + 1 < n_steps) load_page(step + 1, buf[(step + 1) & 1]);
+        const PageRegs& cur = buf[step & 1];
+        const int t0 = (first_page + step * IX_WAVES) * IX_PAGE;
+        const bool ok = pgs[step] >= 0 && pgs[step] < p.num_pages;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int tile = 0; tile < 2; ++tile) {
+                if (tile >= nt) break;
+                // two k-64 steps on e4m3 operands (format code 0 for both), block
+                // scales 2^0 (e8m0 code 127): plain fp8 products summed in fp32
+                f32x16 acc = {};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[tile][s], cur.kb[g][s], acc, 0, 0, 0, 127,
+                                                                          0, 127);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sum += wv[tile][i] * fmaxf(acc[i], 0.0f);
+            }
+            sum += __shfl_xor(sum, 32);
+            const int t = t0 + g * 32 + col;
+            if (hf == 0 && t < len) out[t] = ok ? to_bf16_bits(sum * cur.scale[g]) : (uint16_t)0xFF80u;   // -inf
+        }
     }
 }
 
