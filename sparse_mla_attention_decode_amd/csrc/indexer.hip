@@ -12,7 +12,7 @@ constexpr int IX_PAGE = 64;                 // tokens per key-cache page
 constexpr int IX_DIM = 128;                 // e4m3 dims per key
 constexpr int IX_PAGE_BYTES = IX_PAGE * IX_DIM + IX_PAGE * 4;   // codes, then fp32 scales
 constexpr int IX_WAVES = 4;
-constexpr int IX_PAGES_PER_WAVE = 4;        // q and the weights stay in registers across them
+constexpr int IX_PAGES_PER_WAVE = 11;       // 12 x 64 work-groups for 512-page rows: one round at 3 per CU
 constexpr int TOPK_THREADS = 1024;
 
 __device__ __forceinline__ int clamp_len(const IndexerParams& p, int r) {
@@ -64,24 +64,18 @@ __global__ void __launch_bounds__(IX_WAVES * 64) __attribute__((amdgpu_waves_per
             wv[tile][i] = tile < nt ? wr[ht * 32 + 8 * (i >> 2) + 4 * hf + (i & 3)] : 0.0f;
     }
 
-    // the wave's page-table entries up front (one round trip), then the keys
-    // of page s + 1 in flight while page s is scored
+    // the wave's page-table entries up front (one round trip; lane s holds the
+    // entry of its step s), then the keys of page s + 1 in flight while page s
+    // is scored (two register sets, pages taken in pairs)
     const int32_t* pt = p.page_table + (size_t)r * p.max_pages;
-    int pgs[IX_PAGES_PER_WAVE];
-    int n_steps = 0;
-#pragma unroll
-    for (int step = 0; step < IX_PAGES_PER_WAVE; ++step) {
-        const int page_l = first_page + step * IX_WAVES;
-        const bool in = page_l * IX_PAGE < len;                  // then page_l < max_pages
-        pgs[step] = in ? pt[page_l] : -1;
-        n_steps += in ? 1 : 0;
-    }
+    const int n_steps = min(IX_PAGES_PER_WAVE, (len - first_page * IX_PAGE + IX_WAVES * IX_PAGE - 1) / (IX_WAVES * IX_PAGE));
+    const int pg_lane = lane < n_steps ? pt[first_page + lane * IX_WAVES] : -1;   // below max_pages
     struct PageRegs {
         i32x8 kb[2][2];
         float scale[2];
     };
     auto load_page = [&](int step, PageRegs& d) {
-        const int pg = pgs[step];
+        const int pg = __builtin_amdgcn_readlane(pg_lane, step);
         const bool ok = pg >= 0 && pg < p.num_pages;
         const uint8_t* page = p.kcache + (size_t)(ok ? pg : 0) * IX_PAGE_BYTES;
 #pragma unroll
@@ -93,17 +87,11 @@ __global__ void __launch_bounds__(IX_WAVES * 64) __attribute__((amdgpu_waves_per
             d.scale[g] = ((const float*)(page + IX_PAGE * IX_DIM))[tok];
         }
     };
-
     uint16_t* out = p.scores + (size_t)r * p.max_pages * IX_PAGE;
-    PageRegs buf[2];
-    load_page(0, buf[0]);
-#pragma unroll
-    for (int step = 0; step < IX_PAGES_PER_WAVE; ++step) {
-        if (step >= n_steps) break;
-        if (step + 1 < n_steps) load_page(step + 1, buf[(step + 1) & 1]);
-        const PageRegs& cur = buf[step & 1];
+    auto score_page = [&](int step, const PageRegs& cur) {
         const int t0 = (first_page + step * IX_WAVES) * IX_PAGE;
-        const bool ok = pgs[step] >= 0 && pgs[step] < p.num_pages;
+        const int pg = __builtin_amdgcn_readlane(pg_lane, step);
+        const bool ok = pg >= 0 && pg < p.num_pages;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             float sum = 0.0f;
@@ -124,6 +112,15 @@ __global__ void __launch_bounds__(IX_WAVES * 64) __attribute__((amdgpu_waves_per
             const int t = t0 + g * 32 + col;
             if (hf == 0 && t < len) out[t] = ok ? to_bf16_bits(sum * cur.scale[g]) : (uint16_t)0xFF80u;   // -inf
         }
+    };
+    PageRegs a, b;
+    load_page(0, a);
+    for (int step = 0; step < n_steps; step += 2) {
+        if (step + 1 < n_steps) load_page(step + 1, b);
+        score_page(step, a);
+        if (step + 1 >= n_steps) break;
+        if (step + 2 < n_steps) load_page(step + 2, a);
+        score_page(step + 1, b);
     }
 }
 
