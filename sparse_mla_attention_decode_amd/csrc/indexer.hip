@@ -31,15 +31,16 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {          // nearest,
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Scores of one request's pages (Eq. 1).  Each wave takes up to four pages
-// (the work-group's waves read adjacent pages at each step), each as two
-// groups of 32 tokens.  The head-by-token products run on the FP8 matrix
-// cores with q as the A operand (rows = heads) and the keys as B (columns =
-// tokens), so every lane ends with one token's 16 head dot products per head
-// tile: ReLU, the head weights and the sum over heads stay in the lane, and
-// one exchange joins the two lane halves.  The contraction's k slots of lane
-// half hf at step s are dims 64 hf + 8 s .. + 7 for both operands, so each
-// lane reads 64 contiguous bytes of its head row and of its token row.  The
+// Scores of one request's pages (Eq. 1).  Each wave takes up to
+// IX_PAGES_PER_WAVE pages (the work-group's waves read adjacent pages at each
+// step), each as two groups of 32 tokens, with the keys of its next page in
+// flight while a page is scored.  The head-by-token products run on the FP8
+// matrix cores with q as the A operand (rows = heads) and the keys as B
+// (columns = tokens), so every lane ends with one token's 16 head dot products
+// per head tile: ReLU, the head weights and the sum over heads stay in the
+// lane, and one exchange joins the two lane halves.  The contraction's k slots
+// of lane half hf at step s are dims 64 hf + 32 s .. + 31 for both operands, so
+// each lane reads 64 contiguous bytes of its head row and of its token row.  The
 // per-token scale multiplies the head sum (it is positive, so it commutes
 // with the ReLU: section 5.3).
 __global__ void __launch_bounds__(IX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(3))) indexer_score_kernel(IndexerParams p) {
