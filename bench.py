@@ -42,20 +42,23 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 # HBM bytes per launch of the decode kernel at this workload, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
 # each scaled by what the same counter reads for a plain 1 GiB device copy
-# (bench.py --copy-calibration 1024: FETCH_SIZE reads 524302.8 KiB -> x2.0,
+# (bench.py --copy-calibration 1024: FETCH_SIZE reads 524301.3 KiB -> x2.0,
 # WRITE_SIZE 1048576 KiB -> x1.0).  Valid only for the kernel sources they were
 # taken on (sha256 below); for any other source the traffic is reported null.
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "fc07661c9ee7cf530757cf1572bf78c3c0317e0b8715a06605882e8f05e082e3",
-                  "fetch_kib": 54041.4, "fetch_scale": 2.0, "write_kib": 32896.0, "write_scale": 1.0}
+DECODE_TRAFFIC = {"sources_sha256": "e04466943fce259062b7253919a8c94b0c0946bcb2dbb00db46aa0680aa99719",
+                  "fetch_scale": 2.0, "write_scale": 1.0,
+                  # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per decode dispatch
+                  "kib": {"decode": (54056.0, 32896.0), "halfhead": (100946.5, 16448.0),
+                          "v4": (51785.4, 32896.0), "v41": (44531.1, 32896.0)}}
 
 INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
                           "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",
                           "sparse_mla_attention_decode_amd/csrc/device_common.h")
-INDEXER_TRAFFIC = {"sources_sha256": "f1622b8d576bb008ceb9c24bd9b658c628cfa68172039feb4f13368f2d92ca1b",
-                   "fetch_kib": 137577.2, "fetch_scale": 2.0, "write_kib": 4632.1, "write_scale": 1.0}
+INDEXER_TRAFFIC = {"sources_sha256": "533c1ac63acadf58b014e7e8f584eb49914a42f4a4932c9b29c0e7183a53ef28",
+                   "fetch_kib": 137459.3, "fetch_scale": 2.0, "write_kib": 4223.8, "write_scale": 1.0}
 
 
 def traffic_of(sources, t):
@@ -70,18 +73,20 @@ def traffic_of(sources, t):
     return t["fetch_kib"] * 1024 * t["fetch_scale"] + t["write_kib"] * 1024 * t["write_scale"]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch if the counters match the current kernel sources."""
+def measured_traffic(workload):
+    """HBM bytes per decode launch of this workload if the counters match the
+    current kernel sources."""
     import hashlib
     h = hashlib.sha256()
     for f in DECODE_KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     t = DECODE_TRAFFIC
-    if h.hexdigest() != t["sources_sha256"]:
+    if h.hexdigest() != t["sources_sha256"] or workload not in t["kib"]:
         return None, None
-    fetch = t["fetch_kib"] * 1024 * t["fetch_scale"]
-    write = t["write_kib"] * 1024 * t["write_scale"]
+    fetch_kib, write_kib = t["kib"][workload]
+    fetch = fetch_kib * 1024 * t["fetch_scale"]
+    write = write_kib * 1024 * t["write_scale"]
     return fetch + write, {"fetch_bytes": fetch, "write_bytes": write,
                            "counters": "FETCH_SIZE x2.0, WRITE_SIZE x1.0 (copy-calibrated)"}
 
@@ -374,7 +379,7 @@ def main():
     decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     flops, bytes_, n_valid = algorithmic(w0)
-    traffic, traffic_detail = measured_traffic() if cfg == 1 and not soa else (None, None)
+    traffic, traffic_detail = measured_traffic(args.workload)
     achieved_tflops = flops / (decode_ms * 1e-3) / 1e12
     achieved_gbs = bytes_ / (decode_ms * 1e-3) / 1e9
     t_roof_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), bytes_ / (PEAK_HBM_GBS * 1e9)) * 1e3
