@@ -299,7 +299,7 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
                 const int c = c0 + lane + u * TOPK_THREADS;
-                if (c < n_chunks) k[u] = in_lds ? *(const u32x4*)(keys + 8 * c) : s16[c];
+                k[u] = c < n_chunks ? (in_lds ? *(const u32x4*)(keys + 8 * c) : s16[c]) : u32x4{0u, 0u, 0u, 0u};
             }
             if (!in_lds) {
 #pragma unroll
@@ -326,15 +326,24 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
         }
     }
     __syncthreads();
-    // 2. first digit
+    // 2. first digit (only the row's last chunk can hold tokens past it: the
+    // test is per chunk, so a full chunk costs an extract and an atomic per key)
     for_rounds([&](int cb, u32x4* k) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             const int c = cb + u * TOPK_THREADS;
             if (c >= n_chunks) break;
+            if (8 * c + 8 <= len) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                atomicAdd(&hist[8 * c + e < len ? key_of(k[u], e) >> 4 : TK_BINS + lane], 1u);
+                for (int w = 0; w < 4; ++w) {
+                    atomicAdd(&hist[(k[u][w] >> 4) & 0xFFFu], 1u);
+                    atomicAdd(&hist[k[u][w] >> 20], 1u);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    atomicAdd(&hist[8 * c + e < len ? key_of(k[u], e) >> 4 : TK_BINS + lane], 1u);
+            }
         }
     });
     __syncthreads();
@@ -348,20 +357,31 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
     // the key of token t (from LDS, or from the scores for long rows)
     auto key_at = [&](int t) -> uint32_t { return in_lds ? keys[t] : order_key(s[t]); };
     // 4. the tokens above b1 out; those in b1 to the stash
+    // digit above b1 <=> key >= (b1 + 1) * 16; digit >= b1 <=> key >= b1 * 16
+    const uint32_t thr_gt = (b1 + 1u) << 4, thr_ge = b1 << 4;
     for_rounds([&](int cb, u32x4* k) {
-        uint32_t mup = 0, mb1 = 0;                    // bit 8 u + e: key e of round chunk u
+        uint32_t mup = 0, mge = 0;                    // bit 8 u + e: key e of round chunk u
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
+        for (int u = BATCH - 1; u >= 0; --u) {        // bits shifted in from the top
             const int c = cb + u * TOPK_THREADS;
-            if (c >= n_chunks) break;
+            if (8 * c + 8 <= len) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t key = key_of(k[u], e);
-                const bool ok = 8 * c + e < len;
-                mup |= (uint32_t)(ok && (key >> 4) > b1) << (8 * u + e);
-                mb1 |= (uint32_t)(ok && (key >> 4) == b1) << (8 * u + e);
+                for (int e = 7; e >= 0; --e) {
+                    const uint32_t key = key_of(k[u], e);
+                    mup = (mup << 1) | (uint32_t)(key >= thr_gt);
+                    mge = (mge << 1) | (uint32_t)(key >= thr_ge);
+                }
+            } else {                                  // the row's last chunk, or past the row
+#pragma unroll
+                for (int e = 7; e >= 0; --e) {
+                    const uint32_t key = key_of(k[u], e);
+                    const bool ok = 8 * c + e < len;
+                    mup = (mup << 1) | (uint32_t)(ok && key >= thr_gt);
+                    mge = (mge << 1) | (uint32_t)(ok && key >= thr_ge);
+                }
             }
         }
+        uint32_t mb1 = mge & ~mup;
         uint32_t o = wave_slots((uint32_t)__popc(mup), &cnt_gt);
         while (mup) {
             const int i = __ffs(mup) - 1;
