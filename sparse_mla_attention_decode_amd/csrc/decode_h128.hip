@@ -103,7 +103,8 @@ struct Lay {
     static constexpr int L_XP = L_KB + NKB * KBB;                      // [4 head blocks][2 k-steps][64][16]
     static constexpr int L_IDS = L_XP + XPB;                           // [4 waves][2 slots][32] int32
     static constexpr int L_IDS0 = L_IDS + NW * IDS_SLOTS * 128;        // [4 waves][4 tiles][32] (prologue)
-    static constexpr int L_BYTES = L_IDS0 + NW * 4 * 128;
+    static constexpr int L_MREF = L_IDS0 + NW * 4 * 128;               // [64 heads] shared reference max (64 heads)
+    static constexpr int L_BYTES = L_MREF + 256;
     static constexpr int L_FLAGS = L_KB + 1024;                        // [4] restart flags (row pad)
     static constexpr int L_LM = L_XP;                                  // [128 heads] {l, m} (epilogue)
     static constexpr int QCH = 2 * KSTEPS;                             // 16-byte chunks of a head's Q
@@ -627,10 +628,14 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     // wave-uniform values live in scalar registers; lane-derived offsets are
     // recomputed where they are used (opaque_lane) instead of being held
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // 64 query heads: waves 0 and 1 score heads 0..63; waves 2 and 3 load no Q
-    // and score nothing (they still copy and stage their share of every tile),
-    // and every wave's value contraction covers head blocks 0 and 1 only
-    const bool sc_wave = !H64 || wave < 2;
+    // 64 query heads: the two wave pairs (0, 1) and (2, 3) both hold Q of heads
+    // 0..63 (wave w: heads 32 (w % 2) ..) and take turns by tile: pair (i + 1)
+    // % 2 scores tile i + 1 while the other pair runs the softmax of tile i,
+    // which it scored the tile before.  A head's two waves share its reference
+    // max through LDS and add their exp-sums in the epilogue.  Every wave's
+    // value contraction covers head blocks 0 and 1 only.
+    const bool sc_wave = true;
+    const int pair = wave >> 1;
     constexpr int HB = H64 ? 2 : 4;                            // head blocks of 32
 
     const PartPlan plan = plan_part(p, part);
@@ -721,12 +726,14 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // slots, base-2 exponent against the reference max, P to LDS), the
                 // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
                 // 1 - par for tile parity par).  With soft == false (the prologue)
-                // only the scores of tile 0.  sc_c: whether this wave scores
-                // (compile time, so a wave that does not takes no branch per step).
-                auto part1 = [&](auto sc_c, int i, int par, int kb, int kb3, int ln, bool soft, bool scores,
+                // only the scores of tile 0.  role_c: bit 0 = this wave scores,
+                // bit 1 = it runs the softmax (compile time, so a wave takes no
+                // branch per step for the work it does not do; 128 heads: both).
+                auto part1 = [&](auto role_c, int i, int par, int kb, int kb3, int ln, bool soft, bool scores,
                                  bool copies, const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S,
                                  f32x16& S_next, const StageRegs* pro_g) {
-                    constexpr bool SC = decltype(sc_c)::value;
+                    constexpr bool SC = (decltype(role_c)::value & 1) != 0;
+                    constexpr bool SM = (decltype(role_c)::value & 2) != 0;
                     const int qk = kb + qk_off(ln, 0);      // NoPE k-steps: qk + 32 j
                     const int r3 = 1 - par;
                     const uint32_t raw3 = raw0 + r3 * L::RAW_BYTES;
@@ -797,7 +804,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                 }
                             }
                         }
-                        if (soft && SC) {
+                        if (soft && SM) {
+                            if (H64 && js == 1 && m_ref == INIT_MAX)   // set by the other pair?
+                                m_ref = *(const LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (wave & 1) + (ln & 31)));
                             if (js == 1 && vm != 0xffffffffu) {
                                 // accumulator element v holds key 8(v/4) + 4h + v%4:
                                 // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
@@ -822,7 +831,11 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                 mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
                                 const float mnew = mx * p.c;
                                 m_seen = fmaxf(m_seen, mnew);
-                                if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                                if (m_ref == INIT_MAX && mnew > -INFINITY) {   // O, l still zero
+                                    m_ref = mnew;
+                                    if (H64 && ln < 32)
+                                        *(LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (wave & 1) + ln)) = mnew;
+                                }
                             }
                             if (js >= 6 && js < 22) {
                                 const int v = js - 6;
@@ -831,9 +844,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                             }
                             if (js == 24) {
                                 l_part += psum;
-                                lds_write16(lds, xp_base<FS>(ln) + wave * 2048, p_fragment(S, 0));
+                                lds_write16(lds, xp_base<FS>(ln) + (wave & (HB - 1)) * 2048, p_fragment(S, 0));
                             }
-                            if (js == 26) lds_write16(lds, xp_base<FS>(ln) + wave * 2048 + 1024, p_fragment(S, 1));
+                            if (js == 26) lds_write16(lds, xp_base<FS>(ln) + (wave & (HB - 1)) * 2048 + 1024, p_fragment(S, 1));
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -981,9 +994,13 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     const int ln = opaque_lane();
                     const StageRegs g1 = stage_load<FS>(lds, slice_off + L::RAW_BYTES, ln);
                     f32x16 none = {};
-                    if (sc_wave) part1(std::true_type{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
+                    // pair 0 scores tile 0 (64 heads)
+                    if (!H64 || pair == 0)
+                        part1(std::integral_constant<int, 3>{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u,
+                              none, S_cur, &g1);
                     else if constexpr (H64)
-                        part1(std::false_type{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u, none, S_cur, &g1);
+                        part1(std::integral_constant<int, 0>{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u,
+                              none, S_cur, &g1);
                 }
                 __syncthreads();                        // tile 1 staged
 
@@ -1000,12 +1017,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     // rather than held in registers across the loop
                     const int ln = opaque_lane();
                     f32x16 S_next;
-                    if (sc_wave)
-                        part1(std::true_type{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0, S_cur,
-                              S_next, nullptr);
-                    else if constexpr (H64)
-                        part1(std::false_type{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx, sdel_nx, vm0,
-                              S_cur, S_next, nullptr);
+                    if constexpr (!H64)
+                        part1(std::integral_constant<int, 3>{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx,
+                              sdel_nx, vm0, S_cur, S_next, nullptr);
+                    else if (((i + 1) & 1) == pair)     // scores tile i + 1
+                        part1(std::integral_constant<int, 1>{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx,
+                              sdel_nx, vm0, S_cur, S_next, nullptr);
+                    else                                // softmax of tile i (scored the tile before)
+                        part1(std::integral_constant<int, 2>{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx,
+                              sdel_nx, vm0, S_cur, S_next, nullptr);
                     __syncthreads();
                     const uint8_t* src4 = src_nx;
                     int sdel4 = sdel_nx;
@@ -1036,6 +1056,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             for (int i = 0; i < 16; ++i)
                 if ((i & 3) < HB) O[i] = f32x16{};
             l_part = 0.f;
+            // 64 heads: the shared reference max starts as this pass's (unset
+            // on the first pass; the true max on a recompute)
+            if (H64 && wave < 2 && opaque_lane() < 32)
+                *(LDS_AS float*)(lds + L::L_MREF + 4 * (32 * wave + opaque_lane())) = m_ref;
             __syncthreads();                        // LDS free (previous piece / pass done)
             const int m_hi = min(k_hi, main_top);
             if (k_lo < m_hi)
@@ -1052,6 +1076,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     segment(std::integral_constant<int, FX>{}, x_lo, x_hi, idx_x, x_ok, pass, k_lo >= m_hi);
                 }
             }
+            // 64 heads: the shared reference is the one both waves of a head
+            // used (a wave whose own tiles had no valid key may not hold it)
+            if constexpr (H64)
+                m_ref = *(const LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (wave & 1) + (opaque_lane() & 31)));
             // the reference stays fixed once set, so one test of the largest
             // score max of the pass covers every tile
             const bool restart = __any(m_seen > m_ref + p.threshold);
@@ -1065,6 +1093,14 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             if (flags == 0u || pass > 0) break;
             if (wave == 0 && opaque_lane() < 4) lds[L::L_FLAGS + opaque_lane()] = 0;
             m_ref = m_seen;
+            if constexpr (H64) {
+                // the true max of a head over the tiles of both of its waves
+                if (opaque_lane() < 32) *(LDS_AS float*)(lds + L::L_LM + 4 * (32 * wave + opaque_lane())) = m_seen;
+                __syncthreads();
+                m_ref = fmaxf(m_ref, *(const LDS_AS float*)(lds + L::L_LM + 4 * (32 * (wave ^ 2) + (opaque_lane() & 31))));
+                m_seen = m_ref;
+                __syncthreads();
+            }
         }
 
         // ---- epilogue: l and m of every head through LDS
@@ -1080,15 +1116,18 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         // exp-sum over both half-waves (same head): the swap leaves a lane's
         // own value in one result and the other half's in the other
         const auto lsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-        const float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
+        float l_tot = __uint_as_float(lsw[0]) + __uint_as_float(lsw[1]);
         if (lane < 32) *(LDS_AS f32x2*)(lds + L::L_LM + 8 * (32 * wave + n)) = f32x2{l_tot, m_ref};
         __syncthreads();
+        // 64 heads: a head's exp-sum is split over waves w and w + 2
+        if constexpr (H64) l_tot += (*(const LDS_AS f32x2*)(lds + L::L_LM + 8 * (32 * (wave ^ 2) + n)))[0];
         float inv[4];
         const int first_split = split_prefix(p, req);
         const int nsplit = split_prefix(p, req + 1) - first_split;
 #pragma unroll
         for (int hb = 0; hb < 4; ++hb) {
-            const f32x2 lm = *(const LDS_AS f32x2*)(lds + L::L_LM + 8 * (32 * hb + n));
+            f32x2 lm = *(const LDS_AS f32x2*)(lds + L::L_LM + 8 * (32 * hb + n));
+            if (H64 && hb < 2) lm[0] += (*(const LDS_AS f32x2*)(lds + L::L_LM + 8 * (32 * (hb + 2) + n)))[0];
             // the final output of an unsplit request takes the attention sink
             // as an extra exp-sum term 2^(sink log2(e) - m) (split requests: in
             // the combine)

@@ -196,14 +196,16 @@ def test_single_repeated_row_is_exact():
             assert np.all(np.abs(lse[bi, :, 0] - (s + math.log(w.topk))) <= LSE_TOL)
 
 
-def test_reference_max_recompute_path():
+@pytest.mark.parametrize("h_q,slot", [(128, 100), (64, 100), (64, 70)])
+def test_reference_max_recompute_path(h_q, slot):
     """A late tile whose scores exceed the first tile's max by far more than
     2^64 (log2 units) forces the piece to be recomputed; the result must still
-    match the definition."""
-    rng = np.random.default_rng(41)
-    w = W.paged_decode("jump", 41, b=2, s_q=1, h_q=128, topk=128, tokens_per_seq=256, P=64)
+    match the definition.  With 64 heads the two wave pairs take turns by tile
+    (slot 100: the 4th tile, slot 70: the 3rd), so the large score is seen by
+    one wave of the head and the recompute must use it in both."""
+    w = W.paged_decode("jump", 41, b=2, s_q=1, h_q=h_q, topk=128, tokens_per_seq=256, P=64)
     q = O.bf16_value(w.q_bits[0, 0, 0])
-    big_tok = int(w.indices[0, 0, 100])                  # slot in the 4th tile
+    big_tok = int(w.indices[0, 0, slot])
     nope = (q[:512] * 6.0).astype(np.float32)[None]
     rope = W.to_bf16_bits((q[512:] * 6.0).astype(np.float32))[None]
     row = W.encode_fp8_rows(nope, rope)[0]
@@ -215,6 +217,20 @@ def test_reference_max_recompute_path():
         ref_out, ref_lse = oracle(w)
         assert ref_lse[0, 0, 0] * math.log2(math.e) > 100      # really beyond the threshold
         assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"jump parts={parts}")
+
+
+@pytest.mark.parametrize("h_q", [128, 64])
+@pytest.mark.parametrize("empty_tiles,topk", [(1, 64), (2, 96), (3, 128)])
+def test_leading_empty_tiles(h_q, empty_tiles, topk):
+    """The first tiles of a piece hold only empty slots, so the reference max
+    is set by a later tile (with 64 heads: possibly by the other wave pair than
+    the one that ran the first softmax); every plan must still match."""
+    w = W.paged_decode("lead_empty", 43, b=2, s_q=1, h_q=h_q, topk=topk, tokens_per_seq=256, P=64)
+    w.indices[:, :, : 32 * empty_tiles] = -1
+    ref_out, ref_lse = oracle(w)
+    for parts in (0, 1, 3):
+        out, lse, _ = run_gpu(w, num_parts=parts)
+        assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"lead_empty h={h_q} e={empty_tiles} parts={parts}")
 
 
 def _closed_vs_sched(w, tag, **kw):
