@@ -48,17 +48,17 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "e04466943fce259062b7253919a8c94b0c0946bcb2dbb00db46aa0680aa99719",
+DECODE_TRAFFIC = {"sources_sha256": "3dd48266187f3e8a1e72e6b1a222fc87024ecc34787381c38f0c34fe78f1b99d",
                   "fetch_scale": 2.0, "write_scale": 1.0,
                   # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per decode dispatch
-                  "kib": {"decode": (54056.0, 32896.0), "halfhead": (100946.5, 16448.0),
-                          "v4": (51785.4, 32896.0), "v41": (44531.1, 32896.0)}}
+                  "kib": {"decode": (54051.5, 32896.0), "halfhead": (100953.2, 16448.0),
+                          "v4": (51788.3, 32896.0), "v41": (44525.4, 32896.0)}}
 
 INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
                           "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",
                           "sparse_mla_attention_decode_amd/csrc/device_common.h")
-INDEXER_TRAFFIC = {"sources_sha256": "533c1ac63acadf58b014e7e8f584eb49914a42f4a4932c9b29c0e7183a53ef28",
-                   "fetch_kib": 137459.3, "fetch_scale": 2.0, "write_kib": 4223.8, "write_scale": 1.0}
+INDEXER_TRAFFIC = {"sources_sha256": "2d84fdfdf40a31353ba5711c2552f91cc7a02a9291f961879694dda6673b9e3d",
+                   "fetch_kib": 137459.3, "fetch_scale": 2.0, "write_kib": 4224.0, "write_scale": 1.0}
 
 
 def traffic_of(sources, t):

@@ -379,6 +379,16 @@ def test_cfg2_half_heads_short_sequences():
     assert_parity(out, lse, ref_out, ref_lse, all_queries(w), "cfg2")
 
 
+def test_cfg2_bench_launch():
+    """The 64-head workload in the launch bench.py times (NULL plan: the
+    closed form in the kernels, 32-slot blocks, no per-request cost, one
+    partition per CU): every query against the oracle."""
+    w = W.make_config(2)
+    out, lse, plan = run_gpu(w, closed_form=True, split_granularity=32, fixed_overhead=0)
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), "cfg2 bench launch")
+
+
 def test_cfg3_sparse_prefill_bf16():
     """4096 query tokens: 264 of them against the oracle -- every 16th token
     (one per 16-column stretch of the launch grid) plus both ends."""
