@@ -36,6 +36,8 @@ METRIC_SOA = ("sparse-decode query-tokens/s at b=64,h=128,topk=2048 on the {} ca
               "% of MFMA/HBM roofline")
 METRIC_HALFHEAD = ("sparse-decode query-tokens/s at b=128,h=64,topk=2048 (13 of 128 requests hold 1500 valid "
                    "slots); % of HBM roofline")
+METRIC_PREFILL = ("sparse-prefill query-tokens/s at s_q=4096,h=128,topk=2048 over a bf16 cache of 8192 tokens; "
+                  "% of MFMA roofline")
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 
@@ -91,15 +93,19 @@ def measured_traffic(workload):
                            "counters": "FETCH_SIZE x2.0, WRITE_SIZE x1.0 (copy-calibrated)"}
 
 
-def algorithmic(w):
+def algorithmic(w, unique_rows: bool = False):
     """Flops of the two contractions over valid slots and compulsory HBM bytes
-    (gathered rows + Q + out + indices + lse) of one decode of workload w."""
+    (gathered rows + Q + out + indices + lse) of one decode of workload w.
+    unique_rows: count each cache row once however many query tokens select
+    it (the sparse prefill: 4096 query tokens share an 8192-row cache, so
+    repeated rows come from the caches, not from HBM)."""
     import numpy as np
     valid = (w.indices >= 0) & (w.indices < w.num_kv_tokens)
     n_valid = int(valid.sum())
     d_qk = w.q_bits.shape[-1]                       # 576; 512 for the V4 / V4.1 caches
     flops = 2.0 * w.h_q * n_valid * (d_qk + 512)
-    bytes_ = (n_valid * w.row_bytes + w.b * w.s_q * w.h_q * d_qk * 2 + w.b * w.s_q * w.h_q * 512 * 2
+    rows = len(np.unique(w.indices[valid])) if unique_rows else n_valid
+    bytes_ = (rows * w.row_bytes + w.b * w.s_q * w.h_q * d_qk * 2 + w.b * w.s_q * w.h_q * 512 * 2
               + w.indices.size * 4 + w.b * w.s_q * w.h_q * 4)
     return flops, float(bytes_), n_valid
 
@@ -245,12 +251,15 @@ def main():
                          "auto: closed when fixed_overhead is 0")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "halfhead", "indexer", "v4", "v41"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "halfhead", "indexer", "v4", "v41", "prefill"),
+                    default="decode",
                     help="decode: the sparse MLA decode step at b=64, h=128, topk=2048 (default); "
                          "halfhead: b=128, h=64, topk=2048 over 65536-token contexts with 10%% of the "
                          "requests holding 1500 valid slots (HBM-bound); indexer: the lightning "
                          "indexer scores + top-k that select the decode's tokens; v4 / v41: the "
-                         "decode step's shape on the V4 (584 B/token) / V4.1 (528 B/token) cache")
+                         "decode step's shape on the V4 (584 B/token) / V4.1 (528 B/token) cache; prefill: "
+                         "the sparse prefill, 4096 query tokens of one sequence selecting 2048 of an "
+                         "8192-token bf16 cache each (MFMA-bound)")
     ap.add_argument("--graph", action="store_true",
                     help="replay a captured HIP graph of each layer's step instead of launching "
                          "its kernels one by one")
@@ -284,18 +293,20 @@ def main():
         return
     M.load_library()
 
-    cfg = 2 if args.workload == "halfhead" else 1
+    cfg = {"halfhead": 2, "prefill": 3}.get(args.workload, 1)
     kv_format = {"v4": W.KV_V4_584, "v41": W.KV_V41_528}.get(args.workload, W.KV_FP8_656)
     soa = kv_format != W.KV_FP8_656
     wl_name = W.CONFIG_NAMES[cfg] + (f"_{args.workload}kv" if soa else "")
     # the 64-head workload's cache is 5.4 GB per layer: two layers already
     # exceed the 256 MB Infinity Cache many times over
-    n_layers = args.layers if cfg == 1 else min(args.layers, 2)
+    # (the prefill: 1.2 GB of Q and out per step, far past that cache, and a
+    # 9 MB cache that every step reads anyway)
+    n_layers = args.layers if cfg == 1 else 1 if cfg == 3 else min(args.layers, 2)
     print(f"[bench] building {n_layers} layers of {wl_name}", file=sys.stderr, flush=True)
     layers = []
     for l in range(n_layers):
         if l == 0 and not soa:
-            w = W.make_config(cfg)
+            w = W.make_config(cfg)             # (the prefill: one layer)
         elif cfg == 1:
             w = W.paged_decode(f"{wl_name}_layer{l}", W.BASE_SEED + 1 + 1000 * l, b=64, s_q=1, h_q=128,
                                topk=2048, tokens_per_seq=32768, kv_format=kv_format)
@@ -378,7 +389,7 @@ def main():
     torch.cuda.synchronize()
     decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
-    flops, bytes_, n_valid = algorithmic(w0)
+    flops, bytes_, n_valid = algorithmic(w0, unique_rows=cfg == 3)
     traffic, traffic_detail = measured_traffic(args.workload)
     achieved_tflops = flops / (decode_ms * 1e-3) / 1e12
     achieved_gbs = bytes_ / (decode_ms * 1e-3) / 1e9
@@ -393,19 +404,21 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / PEAK_HBM_GBS}
     roof.update({"traffic": traffic, "traffic_detail": traffic_detail,
-                 "kernel": "decode_fp8_h128_kernel", "kernel_ms": decode_ms,
+                 "kernel": "decode_kernel" if cfg == 3 else "decode_fp8_h128_kernel", "kernel_ms": decode_ms,
                  "algorithmic_flop_per_launch": flops, "algorithmic_bytes_per_launch": bytes_,
                  "mfma_achieved_TFLOPs": achieved_tflops, "hbm_achieved_GBs": achieved_gbs})
 
     res = {
         "metric": (METRIC_SOA.format({"v4": "V4", "v41": "V4.1"}[args.workload]) if soa
-                   else METRIC if cfg == 1 else METRIC_HALFHEAD), "value": value, "unit": "query-tokens/s", "n_gpus": 1,
+                   else {1: METRIC, 2: METRIC_HALFHEAD, 3: METRIC_PREFILL}[cfg]), "value": value,
+        "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "prewarm_steps": n_pre, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl_name, "b": w0.b, "s_q": w0.s_q, "h_q": w0.h_q,
                    "topk": w0.topk, "valid_slots": n_valid,
-                   "kv_cache": f"fp8 {w0.row_bytes} B/token, page 64, {w0.num_kv_tokens // w0.b} tokens/seq",
+                   "kv_cache": (f"bf16 {w0.row_bytes} B/token, flat, {w0.num_kv_tokens} tokens" if cfg == 3 else
+                                f"fp8 {w0.row_bytes} B/token, page 64, {w0.num_kv_tokens // w0.b} tokens/seq"),
                    "layers_rotated": n_layers, "split_granularity": args.split_granularity,
                    "fixed_overhead": args.fixed_overhead, "num_parts": plan.shape.num_parts,
                    "step": ("decode (closed-form plan in-kernel) + combine" if closed

@@ -52,10 +52,10 @@
  * partition is "split": each piece writes its normalised partial O/l and a
  * base-2 lse (step 14) into the workspace and mla_splitkv_combine merges them
  * (step 16).  A request that lands in exactly one partition is written to
- * out/lse directly.  Partial O precision: the FP8 cache path stores it as bf16
- * (narrower than the walkthrough's fp32 o_accum; a partial is bounded by
- * max |V| and its rounding stays inside the output tolerance), the bf16 cache
- * path as fp32.  The workspace is sized for fp32 either way.
+ * out/lse directly.  Partial O precision: stored as bf16, packed in the
+ * decode's register layout (narrower than the walkthrough's fp32 o_accum; a
+ * partial is bounded by max |V| and its rounding stays inside the output
+ * tolerance).  The workspace is sized for fp32 partials.
  *
  * Conventions:
  *   - Every pointer in mla_decode_args is device memory owned by the caller; the
@@ -321,8 +321,7 @@ int mla_debug_gather_dequant(const mla_decode_args* args, void* k_rows, void* v_
  * (MLA_ERR_INVALID_ARG otherwise); the plan and the split partials live in one
  * 64 MiB device array of the library, one per GPU, held until the process
  * ends.  A shape whose split workspace does not fit ((b + num_parts) * s_q
- * splits of 128 KB plus h_q * 4 B each for the FP8 cache; h_q * 2 KB plus
- * h_q * 4 B for the bf16 cache) is rejected with MLA_ERR_WORKSPACE before
+ * splits of 128 KB plus h_q * 4 B each) is rejected with MLA_ERR_WORKSPACE before
  * anything runs.  Every call on a GPU uses that GPU's array: calls that
  * overlap on one GPU (different streams or threads) race; calls in one
  * stream are ordered.  Outputs and errors otherwise as the calls above. */

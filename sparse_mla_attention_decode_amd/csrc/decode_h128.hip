@@ -64,7 +64,6 @@ constexpr int NW = 4;                             // waves per work-group
 constexpr int ROWB = 656;                         // FP8 token row
 constexpr int WROWS = TILE / NW;                  // rows gathered and staged per wave
 constexpr int NRAW = 2;                           // raw tiles (one being staged, one landing)
-constexpr int NKB = 3;                            // staged tiles (scores, values, being staged)
 constexpr int NP = 1040;                          // staged NoPE row pitch (1024 + 16)
 constexpr int ROPE_OFF = TILE * NP;               // 33280: RoPE rows of a staged tile (656-byte rows)
 constexpr int IDS_SLOTS = 2;                      // token-id tiles per wave in LDS
@@ -80,6 +79,8 @@ constexpr int F4 = MLA_KV_V4_584;                 // pages of 576-byte data rows
 constexpr int F41 = MLA_KV_V41_528;               // pages of 512-byte data rows, then 16-byte scale rows
 constexpr int FX = 4;                             // FP4 extra cache: pages of 256-byte data rows, then 32-byte
                                                   // scale rows (read beside a V4.1 main cache)
+constexpr int FB = MLA_KV_BF16_576;               // bf16 rows of 1152 bytes (576 values), one per token, at the
+                                                  // cache's row stride: copied straight into the staged tile
 
 // Per-format sizes and LDS map (bytes).  A staged tile is 32 NoPE rows of NP
 // bytes (bf16 dims 0..511 and a 16-byte pad that the contractions never read)
@@ -91,15 +92,19 @@ constexpr int FX = 4;                             // FP4 extra cache: pages of 2
 // a pad chunk (conflict-free operand reads).
 template <int F>
 struct Lay {
-    static constexpr int DB = F == F32 ? 656 : F == F4 ? 576 : F == F41 ? 512 : 256;   // data row bytes
-    static constexpr int SB = F == F32 ? 0 : F == F4 ? 8 : F == F41 ? 16 : 32;        // scale row bytes
-    static constexpr int KSTEPS = F == F32 ? 36 : 32;                  // score k-steps of 16 dims
-    static constexpr int WAVE_RAW = F == F4 ? 5184 : 4224;             // a wave's raw slice
-    static constexpr int NDMA = F == F41 ? 5 : F == FX ? 3 : 6;        // copies per lane per tile
+    static constexpr int DB = F == F32 ? 656 : F == F4 ? 576 : F == F41 ? 512 : F == FB ? 1152 : 256;   // data row
+    static constexpr int SB = F == F32 || F == FB ? 0 : F == F4 ? 8 : F == F41 ? 16 : 32;            // scale row
+    static constexpr int KSTEPS = F == F32 || F == FB ? 36 : 32;       // score k-steps of 16 dims
+    // bf16 rows need no conversion: the copies land in the staged tile itself
+    // (one 1 KB copy per NoPE row, one for the RoPE chunks), so there are no
+    // raw slots and a fourth staged buffer takes the tile copied 3 ahead
+    static constexpr int WAVE_RAW = F == FB ? 0 : F == F4 ? 5184 : 4224;   // a wave's raw slice
+    static constexpr int NDMA = F == F41 ? 5 : F == FX ? 3 : F == FB ? WROWS + 1 : 6;   // copies per lane per tile
     static constexpr int NLOAD = F == F41 ? 5 : F == FX ? 4 : 6;       // row loads per lane (prologue)
+    static constexpr int NKB = F == FB ? 4 : 3;                         // staged tiles
     static constexpr int RAW_BYTES = NW * WAVE_RAW;
-    static constexpr int KBB = F == F32 ? ROPE_OFF + TILE * 128 : TILE * NP;
-    static constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;              // [3] staged tiles
+    static constexpr int KBB = F == F32 || F == FB ? ROPE_OFF + TILE * 128 : TILE * NP;
+    static constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;              // [NKB] staged tiles
     static constexpr int L_XP = L_KB + NKB * KBB;                      // [4 head blocks][2 k-steps][64][16]
     static constexpr int L_IDS = L_XP + XPB;                           // [4 waves][2 slots][32] int32
     static constexpr int L_IDS0 = L_IDS + NW * IDS_SLOTS * 128;        // [4 waves][4 tiles][32] (prologue)
@@ -121,7 +126,7 @@ static_assert(Lay<FX>::L_BYTES == Lay<F41>::L_BYTES && Lay<FX>::L_KB == Lay<F41>
 // Rows copied for empty or out-of-range slots: all zero bytes (zero codes,
 // zero scales, zero RoPE), so staged values of empty slots are zero without
 // masking.  Spread over 64 rows so the reads do not pile onto one L2 channel.
-__device__ __attribute__((aligned(256))) uint8_t g_zero_rows[ZERO_ROWS * ROWB];
+__device__ __attribute__((aligned(256))) uint8_t g_zero_rows[ZERO_ROWS * 1152];
 // The id copied for slots past the end of a piece: such slots are empty.
 __device__ int32_t g_no_id[1] = {-1};
 
@@ -193,6 +198,14 @@ __device__ __forceinline__ const uint8_t* dense_row_addr(const DecodeParams& p, 
     // one 32 x 32 -> 64-bit multiply-add
     const uint64_t r = (uint64_t)(uintptr_t)p.kv + (uint64_t)e * (uint32_t)p.kv_block_stride + (uint32_t)off * ROWB;
     const uint64_t z = (uint64_t)(uintptr_t)g_zero_rows + (uint32_t)zrow * ROWB;
+    return (const uint8_t*)(uintptr_t)(ok ? r : z);
+}
+
+// bf16 cache: the row of token t when ok, else row zrow of the zero rows
+// (1152-byte rows there).
+__device__ __forceinline__ const uint8_t* bf16_row(const DecodeParams& p, int t, bool ok, int zrow) {
+    const uint64_t r = (uint64_t)(uintptr_t)p.kv + (uint64_t)(uint32_t)(ok ? t : 0) * (uint64_t)p.kv_block_stride;
+    const uint64_t z = (uint64_t)(uintptr_t)g_zero_rows + (uint32_t)zrow * 1152u;
     return (const uint8_t*)(uintptr_t)(ok ? r : z);
 }
 
@@ -282,6 +295,36 @@ __device__ __forceinline__ void gather_rows(const uint8_t* src, int lane, int wa
     dma16(rope_src(src, lane, wave), __builtin_amdgcn_readfirstlane(rope_dst));
     gather_tail(src, lane, slice);
 }
+// bf16 rows: copy r (0..7) of a wave moves NoPE row 8w + r whole (1 KB: lane
+// L reads its bytes 16 L ..) into that row of the staged tile at kb; the row's
+// address comes from lane 8 r, which holds it (`row` is the lane's own row,
+// key 8w + L / 8).  The RoPE copy moves chunk (L % 8) ^ ((key / 2) % 8) of the
+// lane's row, as for 656-byte rows.
+template <int R>
+__device__ __forceinline__ void bf16_row_copy(const uint8_t* row, int lane, int wave, uint32_t kb_addr) {
+    const uint64_t a = (uint64_t)(uintptr_t)row;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)a, 8 * R);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(a >> 32), 8 * R);
+    dma16_row(((uint64_t)hi << 32) | lo, 16u * (uint32_t)lane,
+              __builtin_amdgcn_readfirstlane(kb_addr + (uint32_t)((WROWS * wave + R) * NP)));
+}
+__device__ __forceinline__ void bf16_rope_copy(const uint8_t* row, int lane, int wave, uint32_t kb_addr) {
+    const int key = WROWS * wave + (lane >> 3), s = lane & 7;
+    dma16(row + 1024 + 16 * (s ^ ((key >> 1) & 7)),
+          __builtin_amdgcn_readfirstlane(kb_addr + ROPE_OFF + 1024u * wave));
+}
+__device__ __forceinline__ void bf16_tile_copy(const uint8_t* row, int lane, int wave, uint32_t kb_addr) {
+    bf16_row_copy<0>(row, lane, wave, kb_addr);
+    bf16_row_copy<1>(row, lane, wave, kb_addr);
+    bf16_row_copy<2>(row, lane, wave, kb_addr);
+    bf16_row_copy<3>(row, lane, wave, kb_addr);
+    bf16_row_copy<4>(row, lane, wave, kb_addr);
+    bf16_row_copy<5>(row, lane, wave, kb_addr);
+    bf16_row_copy<6>(row, lane, wave, kb_addr);
+    bf16_row_copy<7>(row, lane, wave, kb_addr);
+    bf16_rope_copy(row, lane, wave, kb_addr);
+}
+
 // The copies of a tile in any format (rope_dst: 656-byte rows only; sdel:
 // V4 / V4.1 only).
 template <int F>
@@ -711,6 +754,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 const bool ok = (uint32_t)id.x < n_tok;
                 const bool okr = (uint32_t)id.y < n_tok;
                 if constexpr (FS == F32) src = row_addr<FLAT>(p, id.y, okr, kr) + 16 * (ln & 7);
+                else if constexpr (FS == FB) src = bf16_row(p, id.y, okr, kr);     // the row itself
                 else src = soa_row<FS>(p, id.y, okr, kr, sdel) + 16 * (ln & 7);
                 return (uint32_t)__ballot(ok);
             };
@@ -772,7 +816,22 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                 stage_tail<FS>(lds, *pro_g, L::L_KB + L::KBB, wave, ln);
                             }
                         }
-                        if (soft) {
+                        if constexpr (FS == FB) {
+                            // bf16 rows: the copies of tile i+3 straight into its staged
+                            // tile (K buffer kb3), rows 0..7 at js 3, 6, .., 24, RoPE at 27
+                            if (soft && copies && js >= 3 && js <= 24 && js % 3 == 0) {
+                                const uint32_t kbc = lds0 + kb3;
+                                if (js == 3) bf16_row_copy<0>(src3, ln, wave, kbc);
+                                if (js == 6) bf16_row_copy<1>(src3, ln, wave, kbc);
+                                if (js == 9) bf16_row_copy<2>(src3, ln, wave, kbc);
+                                if (js == 12) bf16_row_copy<3>(src3, ln, wave, kbc);
+                                if (js == 15) bf16_row_copy<4>(src3, ln, wave, kbc);
+                                if (js == 18) bf16_row_copy<5>(src3, ln, wave, kbc);
+                                if (js == 21) bf16_row_copy<6>(src3, ln, wave, kbc);
+                                if (js == 24) bf16_row_copy<7>(src3, ln, wave, kbc);
+                            }
+                            if (soft && copies && js == 27) bf16_rope_copy(src3, ln, wave, lds0 + kb3);
+                        } else if (soft) {
                             // copies of tile i+3: NoPE chunks into the raw slot, RoPE
                             // into the staged tile it will occupy (K buffer kb3, whose
                             // RoPE rows the scores of its previous tile no longer read);
@@ -868,11 +927,14 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     // the copies of tile i+2 and the ids of tile i+4 have landed
                     // (1 + NDMA newer ops: the ids of tile i+5, the copies of tile
                     // i+3; none near the end of the piece)
+                    // bf16 rows: nothing to stage, but tile i+2 must have landed
+                    // before its scores (the next part 1)
+                    constexpr bool ST = FS != FB;
                     StageRegs g;
                     if (stage) {
                         if (copies_out) wait_vmcnt<1 + NDMA>();
                         else wait_vmcnt<0>();
-                        g = stage_load<FS, false>(lds, slice_off + par * L::RAW_BYTES, ln);
+                        if constexpr (ST) g = stage_load<FS, false>(lds, slice_off + par * L::RAW_BYTES, ln);
                     }
                     bf16x8 va, pf[4];
     #pragma unroll
@@ -895,13 +957,13 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         }
                         if (jv + 1 < 8) va = vn;
                         if (stage && jv == 0) vm4 = rows_from(i + 4, ln, ids_at(ring_slot(par), ln), src4, sdel4);
-                        if (stage && jv == 1) stage_chunk<0, FS>(lds, g, kb2, wave, ln);
-                        if (stage && jv == 3) stage_chunk<1, FS>(lds, g, kb2, wave, ln);
-                        if (stage && jv == 5) {
+                        if (ST && stage && jv == 1) stage_chunk<0, FS>(lds, g, kb2, wave, ln);
+                        if (ST && stage && jv == 3) stage_chunk<1, FS>(lds, g, kb2, wave, ln);
+                        if (ST && stage && jv == 5) {
                             stage_chunk<2, FS>(lds, g, kb2, wave, ln);
                             if constexpr (FS == F4) g.rope = stage_load_tail(lds, slice_off + par * L::RAW_BYTES, ln);
                         }
-                        if (stage && jv == 7) {
+                        if (ST && stage && jv == 7) {
                             stage_chunk<3, FS>(lds, g, kb2, wave, ln);
                             stage_tail<FS>(lds, g, kb2, wave, ln);
                         }
@@ -944,6 +1006,31 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     } else {
                         wait_vmcnt<0>();                    // ids of tiles 0..4
                     }
+                    if constexpr (FS == FB) {
+                        // bf16 rows: tiles 0..2 copied straight into K buffers 0..2
+                        // once Q has left the LDS
+                        const uint8_t* s0;
+                        const uint8_t* s1;
+                        const uint8_t* s2;
+                        int sd = 0;
+                        vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), s0, sd);
+                        vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), s1, sd);
+                        vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), s2, sd);
+                        vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx, sdel_nx);
+                        if (pass == 0 && load_q) {
+                            wait_vmcnt<0>();
+                            const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5);
+    #pragma unroll
+                            for (int j = 0; j < KSTEPS; ++j)
+                                qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
+                            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                        }
+                        __syncthreads();                    // every wave's Q reads are done
+                        bf16_tile_copy(s0, ln, wave, lds0 + L::L_KB);
+                        bf16_tile_copy(s1, ln, wave, lds0 + L::L_KB + L::KBB);
+                        bf16_tile_copy(s2, ln, wave, lds0 + L::L_KB + 2 * L::KBB);
+                        wait_vmcnt<2 * NDMA>();             // the wave's copies of tile 0 (tiles 1 and 2 newer)
+                    } else {
                     const uint8_t* src;
                     const uint8_t* src2;
                     int sdel = 0, sdel2 = 0;
@@ -986,27 +1073,32 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     // went through the conversions)
                     gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off, rope0 + 2 * L::KBB);
                     wait_vmcnt<NDMA>();                     // the wave's copies of tile 1 (tile 2's are newer)
+                    }
                 }
                 __syncthreads();                        // tile 0 staged
                 {
                     // the scores of tile 0 with the staging of tile 1 (raw slot 1)
                     // between them
                     const int ln = opaque_lane();
-                    const StageRegs g1 = stage_load<FS>(lds, slice_off + L::RAW_BYTES, ln);
+                    StageRegs g1;
+                    if constexpr (FS != FB) g1 = stage_load<FS>(lds, slice_off + L::RAW_BYTES, ln);
+                    const StageRegs* pg = FS != FB ? &g1 : nullptr;
                     f32x16 none = {};
                     // pair 0 scores tile 0 (64 heads)
                     if (!H64 || pair == 0)
                         part1(std::integral_constant<int, 3>{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u,
-                              none, S_cur, &g1);
+                              none, S_cur, pg);
                     else if constexpr (H64)
                         part1(std::integral_constant<int, 0>{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u,
-                              none, S_cur, &g1);
+                              none, S_cur, pg);
+                    if constexpr (FS == FB) wait_vmcnt<NDMA>();   // tile 1 landed (tile 2's copies newer)
                 }
                 __syncthreads();                        // tile 1 staged
 
                 // K buffers of the values, scores and staging of tile i (buffers
                 // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
                 int kb_v = L::L_KB, kb_s = L::L_KB + L::KBB, kb_g = L::L_KB + 2 * L::KBB;
+                int kb_c = L::L_KB + 3 * L::KBB;        // bf16 rows: the buffer tile i+3 is copied into
                 // One tile; near the end of the piece the work for tiles past it is
                 // left out: the copies of tile i+3 (and ids of i+5) from tile n-3 on,
                 // the staging of tile i+2 from n-2 on, the scores of tile i+1 at n-1.
@@ -1017,14 +1109,17 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     // rather than held in registers across the loop
                     const int ln = opaque_lane();
                     f32x16 S_next;
+                    // the buffer of tile i+3's RoPE (656-byte rows: tile i's, whose
+                    // NoPE rows the values still read) or of all of it (bf16 rows)
+                    const int kb3 = FS == FB ? kb_c : kb_v;
                     if constexpr (!H64)
-                        part1(std::integral_constant<int, 3>{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx,
+                        part1(std::integral_constant<int, 3>{}, i, par, kb_s, kb3, ln, true, scores, copies, src_nx,
                               sdel_nx, vm0, S_cur, S_next, nullptr);
                     else if (((i + 1) & 1) == pair)     // scores tile i + 1
-                        part1(std::integral_constant<int, 1>{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx,
+                        part1(std::integral_constant<int, 1>{}, i, par, kb_s, kb3, ln, true, scores, copies, src_nx,
                               sdel_nx, vm0, S_cur, S_next, nullptr);
                     else                                // softmax of tile i (scored the tile before)
-                        part1(std::integral_constant<int, 2>{}, i, par, kb_s, kb_v, ln, true, scores, copies, src_nx,
+                        part1(std::integral_constant<int, 2>{}, i, par, kb_s, kb3, ln, true, scores, copies, src_nx,
                               sdel_nx, vm0, S_cur, S_next, nullptr);
                     __syncthreads();
                     const uint8_t* src4 = src_nx;
@@ -1042,7 +1137,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     const int t = kb_v;
                     kb_v = kb_s;
                     kb_s = kb_g;
-                    kb_g = t;
+                    if constexpr (FS == FB) {
+                        kb_g = kb_c;
+                        kb_c = t;
+                    } else {
+                        kb_g = t;
+                    }
                 };
                 int i = 0;
                 for (; i + 3 < n_tiles; ++i) tile(i, i & 1, std::integral_constant<int, 0>{});
@@ -1181,10 +1281,13 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 }
 
 // Test hook: gathers and stages every tile exactly as the decode kernel does
-// and reads the operands back through its two read paths (score A operands
-// for K, transposing reads for V).  Rows of empty slots are the zero page.
-__global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParams p, uint16_t* k_rows,
-                                                                     uint16_t* v_rows) {
+// (656-byte rows: copies into the raw slot, dequant into the staged tile;
+// bf16 rows: copies straight into the staged tile) and reads the operands
+// back through its two read paths (score A operands for K, transposing reads
+// for V).  Rows of empty slots are the zero page.
+template <int F>
+__global__ void __launch_bounds__(NW * 64, 1) gather_h128_kernel(DecodeParams p, uint16_t* k_rows,
+                                                                 uint16_t* v_rows) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
     const int qi = blockIdx.x;                    // query token = req * s_q + sq
@@ -1193,7 +1296,7 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
     const int n = lane & 31, h = lane >> 5;
     const int32_t* idx = p.indices + (int64_t)req * p.idx_sb + (int64_t)sq * p.idx_ss;
     const int n_tiles = (p.topk + TILE - 1) / TILE;
-    using L = Lay<F32>;
+    using L = Lay<F>;
     const uint32_t lds0 = lds_u32(lds);
     const int slice_off = L_RAW + wave * L::WAVE_RAW;
     const LDS_AS int32_t* slot = (const LDS_AS int32_t*)(lds + L::L_IDS + wave * IDS_SLOTS * 128);
@@ -1205,10 +1308,15 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_fp8_h128_kernel(DecodeParam
         const bool ok = slot_ok(p, slot[n], it * TILE + n < p.topk);
         const bool okr = slot_ok(p, slot[kr], it * TILE + kr < p.topk);
         const uint32_t vm = (uint32_t)__ballot(ok);
-        gather_rows(row_addr<false>(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, wave, lds0 + slice_off,
-                    lds0 + L::L_KB + ROPE_OFF + 1024u * wave);
-        wait_vmcnt<0>();
-        stage_rows<F32>(lds, slice_off, L::L_KB, wave, lane);
+        if constexpr (F == FB) {
+            bf16_tile_copy(bf16_row(p, slot[kr], okr, kr), lane, wave, lds0 + L::L_KB);
+            wait_vmcnt<0>();
+        } else {
+            gather_rows(row_addr<false>(p, slot[kr], okr, kr) + 16 * (lane & 7), lane, wave, lds0 + slice_off,
+                        lds0 + L::L_KB + ROPE_OFF + 1024u * wave);
+            wait_vmcnt<0>();
+            stage_rows<F32>(lds, slice_off, L::L_KB, wave, lane);
+        }
         __syncthreads();
         const int key = it * TILE + n;
         if (wave < 2 && key < p.topk) {
@@ -1322,7 +1430,7 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
 }
 
 // per instance: dynamic LDS size allowed (FLAT, DENSE, H64, format 656 / V4 / V4.1 / V4.1 + FP4)
-bool g_lds_decode[2][2][2][4] = {}, g_lds_gather = false;
+bool g_lds_decode[2][2][2][5] = {}, g_lds_gather[2] = {};
 
 template <typename K>
 hipError_t allow_lds_once(K k, bool& done, int bytes) {
@@ -1334,12 +1442,20 @@ hipError_t allow_lds_once(K k, bool& done, int bytes) {
 
 template <bool FLAT, bool DENSE, bool H64, int F, bool EXTRA = false>
 hipError_t launch_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
-    constexpr int fi = F == F32 ? 0 : F == F4 ? 1 : EXTRA ? 3 : 2;
+    constexpr int fi = F == F32 ? 0 : F == F4 ? 1 : F == FB ? 4 : EXTRA ? 3 : 2;
     hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE, H64, F, EXTRA>,
                                   g_lds_decode[FLAT][DENSE][H64][fi], Lay<F>::L_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE, H64, F, EXTRA>), dim3(num_parts, p.s_q), dim3(NW * 64),
                        Lay<F>::L_BYTES, st, p);
+    return hipGetLastError();
+}
+template <int F>
+hipError_t launch_gather_t(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows, hipStream_t st) {
+    hipError_t e = allow_lds_once(gather_h128_kernel<F>, g_lds_gather[F == FB], Lay<F>::L_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gather_h128_kernel<F>, dim3(p.b * p.s_q), dim3(NW * 64), Lay<F>::L_BYTES, st, p, k_rows,
+                       v_rows);
     return hipGetLastError();
 }
 template <bool FLAT, bool DENSE, int F = F32, bool EXTRA = false>
@@ -1350,7 +1466,8 @@ hipError_t launch_h128_heads(const DecodeParams& p, int num_parts, hipStream_t s
 
 }  // namespace
 
-hipError_t launch_decode_fp8_h128(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
+hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st) {
+    if (kv_format == MLA_KV_BF16_576) return launch_h128_heads<false, false, FB>(p, num_parts, st);
     if (kv_format == MLA_KV_V4_584) return launch_h128_heads<false, false, F4>(p, num_parts, st);
     if (kv_format == MLA_KV_V41_528)
         return p.x_kv != nullptr ? launch_h128_heads<false, false, F41, true>(p, num_parts, st)
@@ -1361,17 +1478,15 @@ hipError_t launch_decode_fp8_h128(const DecodeParams& p, int kv_format, int num_
     return dense ? launch_h128_heads<false, true>(p, num_parts, st) : launch_h128_heads<false, false>(p, num_parts, st);
 }
 
-hipError_t launch_combine_packed(const DecodeParams& p, hipStream_t st) {
+hipError_t launch_combine(const DecodeParams& p, hipStream_t st) {
     hipLaunchKernelGGL(combine_packed_kernel, dim3(p.b * p.s_q * 64), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 
-hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows, hipStream_t st) {
-    hipError_t e = allow_lds_once(gather_fp8_h128_kernel, g_lds_gather, Lay<F32>::L_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gather_fp8_h128_kernel, dim3(p.b * p.s_q), dim3(NW * 64), Lay<F32>::L_BYTES, st, p, k_rows,
-                       v_rows);
-    return hipGetLastError();
+hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows, uint16_t* v_rows,
+                         hipStream_t st) {
+    return kv_format == MLA_KV_BF16_576 ? launch_gather_t<FB>(p, k_rows, v_rows, st)
+                                        : launch_gather_t<F32>(p, k_rows, v_rows, st);
 }
 
 }  // namespace mla

@@ -107,6 +107,12 @@ __device__ __forceinline__ void dma16_at(const void* src, uint32_t base, int off
     asm volatile("s_add_u32 m0, %0, %2\n\tglobal_load_lds_dwordx4 %1, off"
                  :: "s"(base), "v"(src), "i"(off) : "memory", "m0", "scc");
 }
+// Scalar row base + per-lane 32-bit offset (every lane reads 16 bytes of one
+// row), destination given as a scalar LDS address.
+__device__ __forceinline__ void dma16_row(uint64_t row, uint32_t lane_off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(lane_off), "s"(row) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :: "s"(lds_addr), "v"(src) : "memory", "m0");

@@ -81,11 +81,9 @@ int resolve(const mla_shape* in, mla::ResolvedShape* out) {
             (void)hipGetLastError();
             return fail(MLA_ERR_NO_DEVICE, "num_parts = 0 needs a device to read its CU count");
         }
-        // the FP8 kernel (128-head layout for 64 or 128 heads, every FP8
-        // format) needs all of a CU's LDS; the 64-head BF16 kernel fits two
-        // work-groups per CU
-        const int wgs_per_cu = (s.kv_format != MLA_KV_BF16_576 || s.h_q == 128) ? 1 : 2;
-        parts = cus * wgs_per_cu / s.s_q;
+        // the decode kernel (128-head layout for 64 or 128 heads, every cache
+        // format) needs all of a CU's LDS: one work-group per CU
+        parts = cus / s.s_q;
         if (parts < 1) parts = 1;
     }
     if (parts > 65535) return fail(MLA_ERR_INVALID_ARG, "num_parts must be <= 65535 (got %d)", parts);
@@ -210,7 +208,6 @@ int check_decode_args(const mla_decode_args* a, mla::ResolvedShape* rs, mla::Dec
         p->page_mshift = l;
         p->page_magic = (uint32_t)(((1ull << 32) * ((1ull << l) - P)) / P + 1);
     }
-    p->packed_partials = r.kv_format != MLA_KV_BF16_576;     // the 128-head FP8 kernel
     p->x_kv = nullptr;                                        // no extra cache (mla_sparse_decode_extra_fwd)
     p->x_indices = nullptr;
     p->x_topk_length = nullptr;

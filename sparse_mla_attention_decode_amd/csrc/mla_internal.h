@@ -60,7 +60,6 @@ struct DecodeParams {
     int b, s_q, h_q, topk, page_block_size, block;
     uint32_t page_magic;            // t / page_block_size == (mulhi(t, page_magic) + t) >> page_mshift
     int page_mshift;                // for 0 <= t < 2^31 (round-up reciprocal)
-    int packed_partials;            // split partials as packed bf16 (128-head FP8 decode)
     uint32_t soa_scale_off;         // V4 / V4.1: byte offset of a page's scale rows (P * data row)
     // FP4 extra cache beside a V4.1 main cache (x_kv NULL: none).  Its slots
     // follow the main ones: slot k >= main_topk is extra slot k - main_topk,
@@ -173,12 +172,11 @@ constexpr float kRefGapLog2 = 64.0f;
 
 hipError_t launch_sched(const ResolvedShape& s, const int32_t* lengths, int32_t* meta, int32_t* prefix,
                         hipStream_t st);
+// decode_h128.hip: every cache format (656-byte, V4, V4.1 with the FP4 extra
+// cache, bf16 rows), sparse and dense; the split-KV combine over its packed
+// partials; the gather test hook (656-byte and bf16 rows)
 hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st);
-hipError_t launch_decode_fp8_h128(const DecodeParams& p, int kv_format, int num_parts, hipStream_t st);
-hipError_t launch_gather_fp8_h128(const DecodeParams& p, uint16_t* k_rows, uint16_t* v_rows,
-                                  hipStream_t st);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t st);
-hipError_t launch_combine_packed(const DecodeParams& p, hipStream_t st);
 hipError_t launch_gather(const DecodeParams& p, int kv_format, uint16_t* k_rows, uint16_t* v_rows,
                          hipStream_t st);
 

@@ -68,12 +68,12 @@ extern "C" int mla_sparse_decode_noalloc(const mla_decode_args* args, void* stre
     // Array layout: [plan records][split prefix] (only with a per-request
     // cost; with none the kernels evaluate the plan in closed form), then the
     // split partials (packed bf16, 128 KB per split and query column, for the
-    // FP8 caches; fp32 rows for the bf16 cache) and their base-2 lse.
+    // cache formats alike) and their base-2 lse.
     const bool sched = r.overhead != 0;
     const size_t meta_b = sched ? align256((size_t)r.num_parts * sizeof(mla_sched_part)) : 0;
     const size_t prefix_b = sched ? align256((size_t)(r.b + 1) * sizeof(int32_t)) : 0;
     const size_t splits = (size_t)(r.b + r.num_parts) * r.s_q;     // pieces are at most b + num_parts
-    const size_t o_b = align256(splits * (r.kv_format != MLA_KV_BF16_576 ? 128 * 512 * 2 : (size_t)r.h_q * 512 * 4));
+    const size_t o_b = align256(splits * 128 * 512 * 2);
     const size_t l_b = align256(splits * r.h_q * sizeof(float));
     const size_t need = meta_b + prefix_b + o_b + l_b;
     if (need > kScratchBytes) {

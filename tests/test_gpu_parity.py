@@ -389,6 +389,22 @@ def test_cfg2_bench_launch():
     assert_parity(out, lse, ref_out, ref_lse, all_queries(w), "cfg2 bench launch")
 
 
+@pytest.mark.parametrize("parts", [1, 5])
+def test_bf16_prefill_h64_padded_rows(parts):
+    """The bf16 cache with 64 heads (the 64-head instance of the bf16 format),
+    rows 1280 bytes apart (a padded row stride), unsplit and split plans:
+    every query against the oracle."""
+    _need_gpu()
+    w = W.sparse_prefill("bf16_h64", 311, s_q=6, h_q=64, topk=100, s_kv=200, prior=120)
+    flat = w.kv_device()
+    padded = torch.zeros((flat.shape[0], 1280), dtype=torch.uint8, device="cuda")
+    padded[:, :1152] = flat
+    out, lse, plan = run_gpu(w, kv=padded[:, :1152], num_parts=parts, split_granularity=32)
+    assert plan.args(w.q_device(), padded[:, :1152], w.indices_device()).kv_stride_block == 1280
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"bf16 h64 padded parts={parts}")
+
+
 def test_cfg3_sparse_prefill_bf16():
     """4096 query tokens: 264 of them against the oracle -- every 16th token
     (one per 16-column stretch of the launch grid) plus both ends."""

@@ -1,6 +1,6 @@
 """GPU parity of the attention sink and the per-request valid length
 (attn_sink / topk_length) against the CPU oracle: split and unsplit requests,
-the 128- and 64-head FP8 kernel, the generic BF16 kernel, the closed-form
+the 128- and 64-head kernel over the FP8 and bf16 caches, the closed-form
 plan and the benchmark shape."""
 import numpy as np
 import pytest
