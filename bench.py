@@ -50,11 +50,12 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "3dd48266187f3e8a1e72e6b1a222fc87024ecc34787381c38f0c34fe78f1b99d",
+DECODE_TRAFFIC = {"sources_sha256": "034ac98765bc006bb3351aa518acb93bd2a93141d143be0500d1392bfcf7455e",
                   "fetch_scale": 2.0, "write_scale": 1.0,
                   # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per decode dispatch
-                  "kib": {"decode": (54051.5, 32896.0), "halfhead": (100953.2, 16448.0),
-                          "v4": (51788.3, 32896.0), "v41": (44525.4, 32896.0)}}
+                  "kib": {"decode": (54051.8, 32896.0), "halfhead": (100954.9, 16448.0),
+                          "v4": (51791.0, 32896.0), "v41": (44525.3, 32896.0),
+                          "prefill": (2330462.3, 541004.3)}}
 
 INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
                           "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",

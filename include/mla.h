@@ -301,7 +301,9 @@ int mla_dense_decode_fwd(const mla_decode_args* args, const int32_t* block_table
 
 /* Split-KV combine (step 16): merges the partials of every split request into
  * out / lse; unsplit requests are left untouched.  args->indices is not read
- * (it may be NULL). */
+ * (it may be NULL).  With the closed-form plan (plan pointers NULL) and
+ * partitions that hold whole requests only, nothing is split and nothing is
+ * launched. */
 int mla_splitkv_combine(const mla_decode_args* args, void* stream);
 
 /* Test hook for the gather + dequant stage (attn_sink and topk_length are not

@@ -435,6 +435,9 @@ int mla_splitkv_combine(const mla_decode_args* args, void* stream) {
     mla::DecodeParams p;
     int st = check_decode_args(args, &r, &p, true, false);
     if (st != MLA_OK) return st;
+    // closed-form plan with partitions of whole requests (payload a multiple
+    // of the request's block count): no request is split, nothing to merge
+    if (!p.sched_meta && p.plan_payload % p.plan_nblk == 0) return ok();
     return hip_status(mla::launch_combine(p, static_cast<hipStream_t>(stream)), "combine kernel launch");
 }
 
