@@ -1350,8 +1350,8 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_h128_kernel(DecodeParams p,
 
 // Split-KV combine over packed partials ("FlashMLA Sparse Decode 完整计算过程详解",
 // step 16): one wave per (query column, output block i = 4 j + hb of decode
-// wave w), 64 waves per column.  M = max_s lse_s (base 2), w_s = 2^(lse_s - M)
-// / sum, out = sum_s w_s O_s, lse = (M + log2 sum) ln 2; out 0 and lse +inf
+// wave w), 64 waves per column (32 with 64 heads).  M = max_s lse_s (base 2),
+// w_s = 2^(lse_s - M) / sum, out = sum_s w_s O_s, lse = (M + log2 sum) ln 2; out 0 and lse +inf
 // when no split saw a valid key.  Splits are taken four at a time with their
 // lse and partial loads issued together (one memory round trip per batch);
 // a later batch with a larger max rescales what was accumulated so far.
@@ -1361,7 +1361,11 @@ __global__ void __launch_bounds__(NW * 64, 1) gather_h128_kernel(DecodeParams p,
 // plan exactly, otherwise approximately).
 __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     const int item = xcd_part(blockIdx.x, gridDim.x);
-    const int qi = item >> 6, piece = item & 63;             // piece = 16 w + 4 j + hb
+    // 128 heads: 64 pieces per column (piece = 16 w + 4 j + hb); 64 heads: the
+    // 32 of head blocks 0 and 1 only (8 w + 2 j + hb)
+    const bool h64 = p.h_q == 64;
+    const int qi = h64 ? item >> 5 : item >> 6;
+    const int piece = h64 ? (((item >> 1) & 15) << 2) | (item & 1) : item & 63;
     const int req = qi / p.s_q, sq = qi % p.s_q;
     const int first = split_prefix(p, req);
     const int ns = split_prefix(p, req + 1) - first;
@@ -1369,7 +1373,6 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
     if (ns <= 1 && !poison) return;
     const int lane = threadIdx.x, n = lane & 31, h = lane >> 5;
     const int w = piece >> 4, j = (piece >> 2) & 3, hb = piece & 3;
-    if (32 * hb >= p.h_q) return;                            // 64 heads: blocks 0 and 1 only
     const int head = 32 * hb + n;
     const float* lse_col = p.lse_accum + (int64_t)first * p.s_q * p.h_q + (int64_t)sq * p.h_q + head;
     const int64_t lse_step = (int64_t)p.s_q * p.h_q;
@@ -1479,7 +1482,7 @@ hipError_t launch_decode(const DecodeParams& p, int kv_format, int num_parts, hi
 }
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t st) {
-    hipLaunchKernelGGL(combine_packed_kernel, dim3(p.b * p.s_q * 64), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(combine_packed_kernel, dim3(p.b * p.s_q * (p.h_q == 64 ? 32 : 64)), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 
