@@ -1,9 +1,9 @@
 // gfx950 sparse MLA decode for 128 or 64 query heads over the FP8 656-byte
 // token cache ("FlashMLA Sparse Decode 完整计算过程详解", steps 7-14), and the
 // dense decode that walks a block table instead of indices (step 1).  With 64
-// query heads (the H64 instances) waves 0 and 1 score the heads, waves 2 and
-// 3 only copy and stage their share of the rows, and the value contraction
-// covers two head blocks instead of four.
+// query heads (the H64 instances) waves w and w + 2 split the score
+// contraction of head block w % 2 by dims and the softmax by keys, and the
+// value contraction covers two head blocks instead of four.
 //
 // One work-group of 4 waves per scheduler partition; it walks the topk slots
 // of each (request, block range) piece in tiles of 32 keys.  Wave w owns
@@ -90,7 +90,10 @@ constexpr int FB = MLA_KV_BF16_576;               // bf16 rows of 1152 bytes (57
 // the head statistics of the epilogue use the P area.  Q passes through the
 // bottom of the LDS in the prologue only: 32 rows per wave of QCH chunks and
 // a pad chunk (conflict-free operand reads).
-template <int F>
+// 64 query heads: P takes two head blocks, and the partial scores the two
+// waves of a head block exchange take [2 head blocks][2 key halves][2][64
+// lanes][16 B] (the ids of tiles 0..3 use its start in the prologue).
+template <int F, bool H64 = false>
 struct Lay {
     static constexpr int DB = F == F32 ? 656 : F == F4 ? 576 : F == F41 ? 512 : F == FB ? 1152 : 256;   // data row
     static constexpr int SB = F == F32 || F == FB ? 0 : F == F4 ? 8 : F == F41 ? 16 : 32;            // scale row
@@ -105,11 +108,13 @@ struct Lay {
     static constexpr int RAW_BYTES = NW * WAVE_RAW;
     static constexpr int KBB = F == F32 || F == FB ? ROPE_OFF + TILE * 128 : TILE * NP;
     static constexpr int L_KB = L_RAW + NRAW * RAW_BYTES;              // [NKB] staged tiles
-    static constexpr int L_XP = L_KB + NKB * KBB;                      // [4 head blocks][2 k-steps][64][16]
-    static constexpr int L_IDS = L_XP + XPB;                           // [4 waves][2 slots][32] int32
-    static constexpr int L_IDS0 = L_IDS + NW * IDS_SLOTS * 128;        // [4 waves][4 tiles][32] (prologue)
-    static constexpr int L_MREF = L_IDS0 + NW * 4 * 128;               // [64 heads] shared reference max (64 heads)
-    static constexpr int L_BYTES = L_MREF + 256;
+    static constexpr int L_XP = L_KB + NKB * KBB;                      // [head blocks][2 k-steps][64][16]
+    static constexpr int L_XS = L_XP + (H64 ? 2 : 4) * 2048;           // 64 heads: partial-score exchange
+    static constexpr int L_IDS = L_XS + (H64 ? 8192 : 0);              // [4 waves][2 slots][32] int32
+    static constexpr int L_IDS0 = H64 ? L_XS : L_IDS + NW * IDS_SLOTS * 128;   // [4 waves][4 tiles][32] (prologue)
+    static constexpr int L_MREF = H64 ? L_IDS + NW * IDS_SLOTS * 128 : L_IDS0 + NW * 4 * 128;   // 64 heads:
+                                                                       // [2 head blocks][2 key halves][32] maxima
+    static constexpr int L_BYTES = L_MREF + (H64 ? 512 : 256);
     static constexpr int L_FLAGS = L_KB + 1024;                        // [4] restart flags (row pad)
     static constexpr int L_LM = L_XP;                                  // [128 heads] {l, m} (epilogue)
     static constexpr int QCH = 2 * KSTEPS;                             // 16-byte chunks of a head's Q
@@ -122,6 +127,9 @@ struct Lay {
 static_assert(Lay<F32>::WAVE_RAW == 4 * 1024 + WROWS * 16 && Lay<F32>::QCOPIES == 37, "copy layout");
 static_assert(Lay<F4>::WAVE_RAW == 5120 + WROWS * 8 && Lay<F41>::QCOPIES == 33, "copy layout");
 static_assert(Lay<FX>::L_BYTES == Lay<F41>::L_BYTES && Lay<FX>::L_KB == Lay<F41>::L_KB, "one LDS map for V4.1 + FP4");
+static_assert(Lay<FX, true>::L_BYTES == Lay<F41, true>::L_BYTES, "one LDS map for V4.1 + FP4");
+static_assert(Lay<F32, true>::L_BYTES <= 160 * 1024 && Lay<FB, true>::L_BYTES <= 160 * 1024 &&
+              Lay<F4, true>::L_BYTES <= 160 * 1024, "LDS budget, 64 heads");
 
 // Rows copied for empty or out-of-range slots: all zero bytes (zero codes,
 // zero scales, zero RoPE), so staged values of empty slots are zero without
@@ -651,9 +659,9 @@ __device__ __forceinline__ int opaque_lane() {
 // This lane's 16 bytes in the P area (head block 0, k-step 0), opaque so
 // that head-block and k-step offsets fold into the LDS instructions'
 // immediate offsets (the area lies above 64 KB).
-template <int F>
+template <int F, bool H64>
 __device__ __forceinline__ int xp_base(int lane) {
-    int b = Lay<F>::L_XP + 16 * lane;
+    int b = Lay<F, H64>::L_XP + 16 * lane;
     asm volatile("" : "+v"(b));
     return b;
 }
@@ -662,8 +670,11 @@ template <bool FLAT, bool DENSE, bool H64, int F, bool EXTRA = false>
 __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParams p) {
     static_assert(F == F32 || (!FLAT && !DENSE), "V4 / V4.1: paged sparse decode only");
     static_assert(!EXTRA || F == F41, "an FP4 extra cache goes with a V4.1 main cache");
-    using L = Lay<F>;
+    using L = Lay<F, H64>;
     constexpr int KSTEPS = L::KSTEPS;
+    // 64 heads: wave w scores head block w % 2 over half w / 2 of the k-steps
+    // and runs the softmax of that block over half w / 2 of a tile's keys
+    constexpr int QA = H64 ? KSTEPS / 2 : KSTEPS;                // Q k-steps a wave holds
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_raw[];
     LDS_AS uint8_t* lds = (LDS_AS uint8_t*)lds_raw;
 
@@ -671,14 +682,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
     // wave-uniform values live in scalar registers; lane-derived offsets are
     // recomputed where they are used (opaque_lane) instead of being held
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // 64 query heads: the two wave pairs (0, 1) and (2, 3) both hold Q of heads
-    // 0..63 (wave w: heads 32 (w % 2) ..) and take turns by tile: pair (i + 1)
-    // % 2 scores tile i + 1 while the other pair runs the softmax of tile i,
-    // which it scored the tile before.  A head's two waves share its reference
-    // max through LDS and add their exp-sums in the epilogue.  Every wave's
+    // 64 query heads: waves w and w + 2 share head block w % 2 (heads 32 (w %
+    // 2) ..).  Wave w holds Q of dims half w / 2 (k-steps 18 (w / 2) ..) and
+    // scores every tile over those dims; the partners swap the partial scores
+    // of each other's key half through LDS, so wave w then holds the whole
+    // scores of keys 16 (w / 2) .. +15 and runs their softmax.  The tile
+    // maximum comes from both halves, so the two waves of a head keep the same
+    // reference max; their exp-sums are added in the epilogue.  Every wave's
     // value contraction covers head blocks 0 and 1 only.
-    const bool sc_wave = true;
-    const int pair = wave >> 1;
+    const int dh = wave >> 1;                                  // 64 heads: the wave's half
     constexpr int HB = H64 ? 2 : 4;                            // head blocks of 32
 
     const PartPlan plan = plan_part(p, part);
@@ -709,7 +721,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
 
         // Q as B operands of the score contraction, loaded once per request:
         // lane (n, h) holds dims 16 j + 8 h .. +7 of head 32w + n for k-step j
-        bf16x8 qa[KSTEPS];
+        bf16x8 qa[QA];
         f32x16 O[16];
         float m_ref = INIT_MAX, m_seen = -INFINITY, l_part = 0.f;
         // One segment of the piece: slots [s_lo, s_hi) of one cache (the main
@@ -720,7 +732,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         auto segment = [&](auto fs_tag, const int s_lo, const int s_hi, const int32_t* idx, const int s_ok,
                            const int pass, const bool load_q) {
             constexpr int FS = decltype(fs_tag)::value;
-            constexpr int NDMA = Lay<FS>::NDMA;
+            constexpr int NDMA = Lay<FS, H64>::NDMA;
             const int n_tiles = (s_hi - s_lo + TILE - 1) / TILE;
             auto tile_ids = [&](int tile, int ln, uint32_t slot_addr) {
                 if (DENSE) copy_pages(idx, s_lo, s_ok, tile, ln, slot_addr);
@@ -770,41 +782,46 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // slots, base-2 exponent against the reference max, P to LDS), the
                 // ids of tile i+5 and the copies of tile i+3 (raw slot and id slot
                 // 1 - par for tile parity par).  With soft == false (the prologue)
-                // only the scores of tile 0.  role_c: bit 0 = this wave scores,
-                // bit 1 = it runs the softmax (compile time, so a wave takes no
-                // branch per step for the work it does not do; 128 heads: both).
-                auto part1 = [&](auto role_c, int i, int par, int kb, int kb3, int ln, bool soft, bool scores,
-                                 bool copies, const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S,
+                // only the scores of tile 0.  d_c (64 heads, compile time): the
+                // wave's half -- k-steps D QA .. of the scores (one MFMA every
+                // other step), keys 16 D .. of the softmax, whose tile maximum
+                // also takes the other half's (hm: this half's, from part 2); at
+                // the end the other key half of the partial scores goes to LDS
+                // for the partner wave.  128 heads: d_c is unused.
+                auto part1 = [&](auto d_c, int i, int par, int kb, int kb3, int ln, bool soft, bool scores,
+                                 bool copies, const uint8_t* src3, int sdel3, uint32_t vm, f32x16 S, float hm,
                                  f32x16& S_next, const StageRegs* pro_g) {
-                    constexpr bool SC = (decltype(role_c)::value & 1) != 0;
-                    constexpr bool SM = (decltype(role_c)::value & 2) != 0;
+                    constexpr int D = decltype(d_c)::value & 1;
                     const int qk = kb + qk_off(ln, 0);      // NoPE k-steps: qk + 32 j
                     const int r3 = 1 - par;
                     const uint32_t raw3 = raw0 + r3 * L::RAW_BYTES;
                     f32x16 Sa, Sb;
                     bf16x8 ka[KAHEAD];
+                    // K operand of k-step j: NoPE rows, or RoPE k-steps 32..35
+                    // (lane-dependent slots)
+                    auto kofs = [&](int j) { return j < 32 ? qk + 32 * j : kb + qk_off(ln, j); };
+                    constexpr int K0 = H64 ? D * QA : 0;    // first k-step of this wave
     #pragma unroll
                     for (int j = 0; j < KAHEAD; ++j)
-                        if (scores && SC) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qk + 32 * j));
-                    // RoPE k-steps 32..35 of tile i+1 (lane-dependent slots)
-                    auto rope_k = [&](int j) { return kb + qk_off(ln, j); };
+                        if (scores) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, kofs(K0 + j)));
                     if (soft && copies) tile_ids(i + 5, ln, lds0 + ring_slot(r3));
                     __builtin_amdgcn_sched_barrier(0);
-                    float mx, psum = 0.f;
+                    float mx, psum = 0.f, other = 0.f;
     #pragma unroll
                     for (int js = 0; js < KSTEPS; ++js) {
-                        if (scores && SC) {
-                            const bf16x8 cur = ka[js % KAHEAD];
-                            if (js + KAHEAD < KSTEPS)
-                                ka[js % KAHEAD] = __builtin_bit_cast(
-                                    bf16x8, lds_read16(lds, js + KAHEAD < 32 ? qk + 32 * (js + KAHEAD) : rope_k(js + KAHEAD)));
+                        // 128 heads: k-step js; 64 heads: k-step K0 + js / 2 on even js
+                        if (scores && (!H64 || (js & 1) == 0)) {
+                            const int t = H64 ? js >> 1 : js;
+                            const bf16x8 cur = ka[t % KAHEAD];
+                            if (t + KAHEAD < QA)
+                                ka[t % KAHEAD] = __builtin_bit_cast(bf16x8, lds_read16(lds, kofs(K0 + t + KAHEAD)));
                             // two alternating accumulator chains: a score MFMA never
                             // takes the result of the one issued right before it
                             // (64 heads leave AGPRs free for the compiler: guarded MFMAs)
-                            if (js == 0) mfma_qk_first<H64>(Sa, cur, qa[0]);
-                            else if (js == 1) mfma_qk_first<H64>(Sb, cur, qa[1]);
-                            else if (js & 1) mfma_qk<H64>(Sb, cur, qa[js]);
-                            else mfma_qk<H64>(Sa, cur, qa[js]);
+                            if (t == 0) mfma_qk_first<H64>(Sa, cur, qa[0]);
+                            else if (t == 1) mfma_qk_first<H64>(Sb, cur, qa[1]);
+                            else if (t & 1) mfma_qk<H64>(Sb, cur, qa[t]);
+                            else mfma_qk<H64>(Sa, cur, qa[t]);
                         }
                         if (pro_g != nullptr) {
                             // prologue: tile 1 staged into K buffer 1 under the scores of tile 0
@@ -863,9 +880,27 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                 }
                             }
                         }
-                        if (soft && SM) {
-                            if (H64 && js == 1 && m_ref == INIT_MAX)   // set by the other pair?
-                                m_ref = *(const LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (wave & 1) + (ln & 31)));
+                        if (soft && H64) {
+                            // 64 heads: keys 16 D .. 16 D + 15 of head block wave % 2
+                            // (values 8 D .. 8 D + 7, masked in part 2)
+                            if (js == 0)
+                                other = *(const LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (2 * (wave & 1) + 1 - D) + (ln & 31)));
+                            if (js == 2) {
+                                const float mnew = fmaxf(hm, other) * p.c;
+                                m_seen = fmaxf(m_seen, mnew);
+                                if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
+                            }
+                            if (js >= 4 && js < 12) {
+                                const int v = 8 * D + js - 4;
+                                S[v] = __builtin_amdgcn_exp2f(S[v] * p.c - m_ref);
+                                psum += S[v];
+                            }
+                            if (js == 14) {
+                                l_part += psum;
+                                lds_write16(lds, xp_base<FS, H64>(ln) + (wave & 1) * 2048 + D * 1024, p_fragment(S, D));
+                            }
+                        }
+                        if (soft && !H64) {
                             if (js == 1 && vm != 0xffffffffu) {
                                 // accumulator element v holds key 8(v/4) + 4h + v%4:
                                 // lanes 0..31 test bit 8(v/4) + v%4, lanes 32..63 that + 4
@@ -890,11 +925,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                                 mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
                                 const float mnew = mx * p.c;
                                 m_seen = fmaxf(m_seen, mnew);
-                                if (m_ref == INIT_MAX && mnew > -INFINITY) {   // O, l still zero
-                                    m_ref = mnew;
-                                    if (H64 && ln < 32)
-                                        *(LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (wave & 1) + ln)) = mnew;
-                                }
+                                if (m_ref == INIT_MAX && mnew > -INFINITY) m_ref = mnew;   // O, l still zero
                             }
                             if (js >= 6 && js < 22) {
                                 const int v = js - 6;
@@ -903,16 +934,61 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                             }
                             if (js == 24) {
                                 l_part += psum;
-                                lds_write16(lds, xp_base<FS>(ln) + (wave & (HB - 1)) * 2048, p_fragment(S, 0));
+                                lds_write16(lds, xp_base<FS, H64>(ln) + wave * 2048, p_fragment(S, 0));
                             }
-                            if (js == 26) lds_write16(lds, xp_base<FS>(ln) + (wave & (HB - 1)) * 2048 + 1024, p_fragment(S, 1));
+                            if (js == 26) lds_write16(lds, xp_base<FS, H64>(ln) + wave * 2048 + 1024, p_fragment(S, 1));
                         }
                         __builtin_amdgcn_sched_barrier(0);
                     }
-                    if (scores && SC) {
+                    if (scores) {
                         mfma_result_fence2(Sa, Sb);
                         S_next = Sa + Sb;
+                        if constexpr (H64) {
+                            // the other key half of this partial to the partner wave:
+                            // [head block][key half][2][64 lanes][16 B]
+                            const int xo = L::L_XS + (2 * (wave & 1) + 1 - D) * 2048 + 16 * ln;
+                            constexpr int V0 = 8 * (1 - D);
+                            lds_write16(lds, xo, u32x4{__float_as_uint(S_next[V0]), __float_as_uint(S_next[V0 + 1]),
+                                                      __float_as_uint(S_next[V0 + 2]), __float_as_uint(S_next[V0 + 3])});
+                            lds_write16(lds, xo + 1024, u32x4{__float_as_uint(S_next[V0 + 4]), __float_as_uint(S_next[V0 + 5]),
+                                                             __float_as_uint(S_next[V0 + 6]), __float_as_uint(S_next[V0 + 7])});
+                        }
                     }
+                };
+                // 64 heads, after part 2: this wave's key half of the scores in
+                // S (its partial plus the partner's, from LDS), masked by the
+                // tile's validity vm, and its maximum (both half-waves) in hm and
+                // in LDS for the partner's next part 1.
+                auto xs_read = [&](auto d_c, int ln, u32x4& a, u32x4& b) {
+                    constexpr int D = decltype(d_c)::value & 1;
+                    const int xi = L::L_XS + (2 * (wave & 1) + D) * 2048 + 16 * ln;
+                    a = lds_read16(lds, xi);
+                    b = lds_read16(lds, xi + 1024);
+                };
+                auto assemble = [&](auto d_c, f32x16& S, const u32x4& a, const u32x4& b, uint32_t vm, float& hm, int ln) {
+                    constexpr int D = decltype(d_c)::value & 1;
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        S[8 * D + e] += __uint_as_float(a[e]);
+                        S[8 * D + 4 + e] += __uint_as_float(b[e]);
+                    }
+                    if (vm != 0xffffffffu) {
+                        // element v holds key 8(v/4) + 4h + v%4 (as in the 128-head mask)
+    #pragma unroll
+                        for (int v = 8 * D; v < 8 * D + 8; ++v) {
+                            const int key = 8 * (v >> 2) + (v & 3);
+                            const uint64_t lanes = (uint64_t)(0u - ((vm >> key) & 1u)) |
+                                                   ((uint64_t)(0u - ((vm >> (key + 4)) & 1u)) << 32);
+                            S[v] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? S[v] : -INFINITY;
+                        }
+                    }
+                    float mx = S[8 * D];
+    #pragma unroll
+                    for (int v = 8 * D + 1; v < 8 * D + 8; ++v) mx = fmaxf(mx, S[v]);
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                    mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+                    hm = mx;
+                    if (ln < 32) *(LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (2 * (wave & 1) + D) + ln)) = mx;
                 };
                 // Part 2 of tile i: the 32 value MFMAs of tile i (O^T += V^T P^T over
                 // this wave's 128 dims, all 128 heads; V from the K buffer at kbv, P
@@ -921,9 +997,9 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // i-1 is done) and the copy source of tile i+4 (id slot par).  Past
                 // the piece the staged rows are zero rows.
                 auto part2 = [&](int i, int par, int kbv, int kb2, int ln, bool stage, bool copies_out,
-                                 const uint8_t*& src4, int& sdel4, uint32_t& vm4) {
+                                 const uint8_t*& src4, int& sdel4, uint32_t& vm4, auto&& step_hook) {
                     const int vb = kbv + pv_base(ln) + 64 * 4 * wave;
-                    const int xp = xp_base<FS>(ln);
+                    const int xp = xp_base<FS, H64>(ln);
                     // the copies of tile i+2 and the ids of tile i+4 have landed
                     // (1 + NDMA newer ops: the ids of tile i+5, the copies of tile
                     // i+3; none near the end of the piece)
@@ -967,24 +1043,28 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                             stage_chunk<3, FS>(lds, g, kb2, wave, ln);
                             stage_tail<FS>(lds, g, kb2, wave, ln);
                         }
+                        step_hook(jv);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 };
 
                 // ---- prologue: ids of tiles 0..4; (first pass) Q through LDS and,
-                // under it, the rows of tile 0 into registers; the copies of tile 1
-                // into raw slot 1; tile 0 staged from the registers into K buffer 0;
-                // copy sources of tiles 2 and 3; the copies of tile 2 into raw slot
-                // 0; the scores of tile 0 with the staging of tile 1.
+                // under it, the rows of tiles 0 and 1 into registers; copy sources
+                // of tiles 2 and 3; the copies of tile 2 into raw slot 0; tiles 0
+                // and 1 staged from the registers into K buffers 0 and 1; the
+                // scores of tile 0.  (Dense decode: tiles 0 and 1 copied into the
+                // raw slots after Q, tile 1 staged under the scores of tile 0;
+                // bf16 rows: tiles 0..2 copied into K buffers 0..2 after Q.)
                 uint32_t vm0, vm1, vm2, vm3;            // validity masks of tiles i .. i+3
                 const uint8_t* src_nx;                  // this lane's copy source in tile i+3
                 int sdel_nx = 0;                        // and its scale offset (V4 / V4.1)
                 f32x16 S_cur;                           // scores of tile i
+                float hm_cur = -INFINITY;               // 64 heads: max of this wave's key half
                 {
                     const int ln = opaque_lane();
                     for (int t = 0; t < 4; ++t) tile_ids(t, ln, lds0 + first_slot(t));
                     tile_ids(4, ln, lds0 + ring_slot(4));
-                    if (pass == 0 && load_q && sc_wave) {
+                    if (pass == 0 && load_q) {
                         // Q of the wave's 32 heads (with 64 query heads waves 2 and
                         // 3 take heads 0..63 again; those results are never stored)
                         // copied whole-line into LDS: region row n = head 32w + n,
@@ -1019,9 +1099,10 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx, sdel_nx);
                         if (pass == 0 && load_q) {
                             wait_vmcnt<0>();
-                            const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5);
+                            const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5) +
+                                           32 * (H64 ? dh * QA : 0);
     #pragma unroll
-                            for (int j = 0; j < KSTEPS; ++j)
+                            for (int j = 0; j < QA; ++j)
                                 qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
                             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
                         }
@@ -1036,21 +1117,26 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     int sdel = 0, sdel2 = 0;
                     vm0 = rows_from(0, ln, ids_at(first_slot(0), ln), src, sdel);
                     vm1 = rows_from(1, ln, ids_at(first_slot(1), ln), src2, sdel2);
-                    // sparse decode: the rows of tile 0 travel while Q lands (NLOAD
-                    // loads per lane, newer than the copies of Q).  (Dense decode
-                    // copies tile 0 after Q: holding these registers across the Q
-                    // reads would make its paged-address instance spill.)
-                    RowRegs r0;
-                    if (!DENSE) r0 = load_rows<FS>(src, sdel, ln, wave);
+                    // sparse decode: the rows of tiles 0 and 1 travel while Q lands
+                    // (NLOAD loads per lane each, newer than the copies of Q), so
+                    // no copy waits for the Q reads to free the LDS.  (Dense decode
+                    // copies its tiles after Q: holding these registers across the
+                    // Q reads would make its paged-address instance spill.)
+                    RowRegs r0, r1;
+                    if (!DENSE) {
+                        r0 = load_rows<FS>(src, sdel, ln, wave);
+                        r1 = load_rows<FS>(src2, sdel2, ln, wave);
+                    }
                     if (pass == 0 && load_q) {
-                        if (sc_wave) {
+                        {
                             // Q into registers: lane (n, h) holds dims 16 j + 8 h .. +7
                             // of head 32w + n for k-step j
                             if (DENSE) wait_vmcnt<0>();
-                            else wait_vmcnt<Lay<FS>::NLOAD>();
-                            const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5);
+                            else wait_vmcnt<2 * Lay<FS, H64>::NLOAD>();
+                            const int qr = L::L_Q + wave * 32 * L::QROW + (ln & 31) * L::QROW + 16 * (ln >> 5) +
+                                           32 * (H64 ? dh * QA : 0);
     #pragma unroll
-                            for (int j = 0; j < KSTEPS; ++j)
+                            for (int j = 0; j < QA; ++j)
                                 qa[j] = __builtin_bit_cast(bf16x8, lds_read16(lds, qr + 32 * j));
                             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
                         }
@@ -1058,42 +1144,59 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         __syncthreads();
                     }
                     const uint32_t rope0 = lds0 + L::L_KB + ROPE_OFF + 1024u * wave;   // K buffer 0 (656-byte rows)
-                    if (DENSE) gather_rows(src, ln, wave, lds0 + slice_off, rope0);
-                    gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off + L::RAW_BYTES, rope0 + L::KBB);
+                    if (DENSE) {
+                        gather_rows(src, ln, wave, lds0 + slice_off, rope0);
+                        gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off + L::RAW_BYTES, rope0 + L::KBB);
+                    }
                     vm2 = rows_from(2, ln, ids_at(first_slot(2), ln), src2, sdel2);
                     vm3 = rows_from(3, ln, ids_at(first_slot(3), ln), src_nx, sdel_nx);
                     if (DENSE) {
                         wait_vmcnt<0>();                    // copies of tiles 0 and 1
                         stage_rows<FS>(lds, slice_off, L::L_KB, wave, ln);
+                        // raw slot 0 is free (its values went through the conversions)
+                        gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off, rope0 + 2 * L::KBB);
+                        wait_vmcnt<NDMA>();                 // the wave's copies of tile 1 (tile 2's are newer)
                     } else {
-                        rows_wait<NDMA, FS>(r0);             // tile 0 (the copies of tile 1 are newer)
+                        // tile 2 into raw slot 0, then tiles 0 and 1 staged from registers
+                        gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off, rope0 + 2 * L::KBB);
+                        rows_wait<Lay<FS, H64>::NLOAD + NDMA, FS>(r0);   // tile 0 (tile 1, tile 2 newer)
                         stage_from_regs<FS>(lds, r0, L::L_KB, wave, ln);
+                        rows_wait<NDMA, FS>(r1);            // tile 1 (the copies of tile 2 are newer)
+                        stage_from_regs<FS>(lds, r1, L::L_KB + L::KBB, wave, ln);
                     }
-                    // raw slot 0 is free (tile 0 staged from registers, or its values
-                    // went through the conversions)
-                    gather_tile<FS>(src2, sdel2, ln, wave, lds0 + slice_off, rope0 + 2 * L::KBB);
-                    wait_vmcnt<NDMA>();                     // the wave's copies of tile 1 (tile 2's are newer)
                     }
                 }
-                __syncthreads();                        // tile 0 staged
+                __syncthreads();                        // tiles 0 and 1 staged (dense: tile 0)
                 {
-                    // the scores of tile 0 with the staging of tile 1 (raw slot 1)
-                    // between them
+                    // the scores of tile 0
                     const int ln = opaque_lane();
+                    // (dense decode: tile 1 staged under them from raw slot 1)
                     StageRegs g1;
-                    if constexpr (FS != FB) g1 = stage_load<FS>(lds, slice_off + L::RAW_BYTES, ln);
-                    const StageRegs* pg = FS != FB ? &g1 : nullptr;
+                    if constexpr (DENSE && FS != FB) g1 = stage_load<FS>(lds, slice_off + L::RAW_BYTES, ln);
+                    const StageRegs* pg = DENSE && FS != FB ? &g1 : nullptr;
                     f32x16 none = {};
-                    // pair 0 scores tile 0 (64 heads)
-                    if (!H64 || pair == 0)
-                        part1(std::integral_constant<int, 3>{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u,
-                              none, S_cur, pg);
-                    else if constexpr (H64)
+                    if (!H64 || dh == 0)
                         part1(std::integral_constant<int, 0>{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u,
-                              none, S_cur, pg);
+                              none, 0.f, S_cur, pg);
+                    else if constexpr (H64)
+                        part1(std::integral_constant<int, 1>{}, -1, 1, L::L_KB, 0, ln, false, true, false, nullptr, 0, 0u,
+                              none, 0.f, S_cur, pg);
                     if constexpr (FS == FB) wait_vmcnt<NDMA>();   // tile 1 landed (tile 2's copies newer)
                 }
                 __syncthreads();                        // tile 1 staged
+                if constexpr (H64) {
+                    // the partner's half of the scores of tile 0; both halves' maxima
+                    // in LDS before the softmax of tile 0 reads them
+                    auto pro = [&](auto d_c) {
+                        const int ln = opaque_lane();
+                        u32x4 a, b;
+                        xs_read(d_c, ln, a, b);
+                        assemble(d_c, S_cur, a, b, vm0, hm_cur, ln);
+                    };
+                    if (dh == 0) pro(std::integral_constant<int, 0>{});
+                    else pro(std::integral_constant<int, 1>{});
+                    __syncthreads();
+                }
 
                 // K buffers of the values, scores and staging of tile i (buffers
                 // i % 3, (i + 1) % 3, (i + 2) % 3), rotated every tile
@@ -1102,32 +1205,37 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // One tile; near the end of the piece the work for tiles past it is
                 // left out: the copies of tile i+3 (and ids of i+5) from tile n-3 on,
                 // the staging of tile i+2 from n-2 on, the scores of tile i+1 at n-1.
-                auto tile = [&](int i, int par, auto tail_c) {
+                auto tile = [&](int i, int par, auto tail_c, auto d_c) {
                     constexpr int left = decltype(tail_c)::value;   // tiles left including i, 0 = more than 3
                     constexpr bool copies = left == 0, stage = left == 0 || left == 3, scores = left != 1;
                     // lane-derived offsets are recomputed every tile (cheap VALU)
                     // rather than held in registers across the loop
                     const int ln = opaque_lane();
                     f32x16 S_next;
+                    float hm_next = -INFINITY;
                     // the buffer of tile i+3's RoPE (656-byte rows: tile i's, whose
                     // NoPE rows the values still read) or of all of it (bf16 rows)
                     const int kb3 = FS == FB ? kb_c : kb_v;
-                    if constexpr (!H64)
-                        part1(std::integral_constant<int, 3>{}, i, par, kb_s, kb3, ln, true, scores, copies, src_nx,
-                              sdel_nx, vm0, S_cur, S_next, nullptr);
-                    else if (((i + 1) & 1) == pair)     // scores tile i + 1
-                        part1(std::integral_constant<int, 1>{}, i, par, kb_s, kb3, ln, true, scores, copies, src_nx,
-                              sdel_nx, vm0, S_cur, S_next, nullptr);
-                    else                                // softmax of tile i (scored the tile before)
-                        part1(std::integral_constant<int, 2>{}, i, par, kb_s, kb3, ln, true, scores, copies, src_nx,
-                              sdel_nx, vm0, S_cur, S_next, nullptr);
+                    part1(d_c, i, par, kb_s, kb3, ln, true, scores, copies, src_nx, sdel_nx, vm0, S_cur, hm_cur,
+                          S_next, nullptr);
                     __syncthreads();
                     const uint8_t* src4 = src_nx;
                     int sdel4 = sdel_nx;
                     uint32_t vm4 = 0u;
-                    part2(i, par, kb_v, kb_g, ln, stage, copies, src4, sdel4, vm4);
+                    // 64 heads, tile i + 1: the partner's half of the scores (written
+                    // before the barrier above) read under the first value steps and
+                    // added in the middle ones; the maxima reach the partner by the
+                    // barrier below
+                    u32x4 xa, xb;
+                    part2(i, par, kb_v, kb_g, ln, stage, copies, src4, sdel4, vm4, [&](int jv) {
+                        if constexpr (H64) {
+                            if (scores && jv == 0) xs_read(d_c, ln, xa, xb);
+                            if (scores && jv == 3) assemble(d_c, S_next, xa, xb, vm1, hm_next, ln);
+                        }
+                    });
                     __syncthreads();
                     S_cur = S_next;
+                    hm_cur = hm_next;
                     src_nx = src4;
                     sdel_nx = sdel4;
                     vm0 = vm1;
@@ -1144,11 +1252,17 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         kb_g = t;
                     }
                 };
-                int i = 0;
-                for (; i + 3 < n_tiles; ++i) tile(i, i & 1, std::integral_constant<int, 0>{});
-                if (i + 2 < n_tiles) tile(i, i & 1, std::integral_constant<int, 3>{}), ++i;
-                if (i + 1 < n_tiles) tile(i, i & 1, std::integral_constant<int, 2>{}), ++i;
-                tile(i, i & 1, std::integral_constant<int, 1>{});
+                // 64 heads: one loop per key half (its part 1 and 2 are compiled
+                // for it)
+                auto loop = [&](auto d_c) {
+                    int i = 0;
+                    for (; i + 3 < n_tiles; ++i) tile(i, i & 1, std::integral_constant<int, 0>{}, d_c);
+                    if (i + 2 < n_tiles) tile(i, i & 1, std::integral_constant<int, 3>{}, d_c), ++i;
+                    if (i + 1 < n_tiles) tile(i, i & 1, std::integral_constant<int, 2>{}, d_c), ++i;
+                    tile(i, i & 1, std::integral_constant<int, 1>{}, d_c);
+                };
+                if (!H64 || dh == 0) loop(std::integral_constant<int, 0>{});
+                else if constexpr (H64) loop(std::integral_constant<int, 1>{});
         };
 
         for (int pass = 0;; ++pass) {
@@ -1156,10 +1270,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             for (int i = 0; i < 16; ++i)
                 if ((i & 3) < HB) O[i] = f32x16{};
             l_part = 0.f;
-            // 64 heads: the shared reference max starts as this pass's (unset
-            // on the first pass; the true max on a recompute)
-            if (H64 && wave < 2 && opaque_lane() < 32)
-                *(LDS_AS float*)(lds + L::L_MREF + 4 * (32 * wave + opaque_lane())) = m_ref;
             __syncthreads();                        // LDS free (previous piece / pass done)
             const int m_hi = min(k_hi, main_top);
             if (k_lo < m_hi)
@@ -1176,10 +1286,6 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                     segment(std::integral_constant<int, FX>{}, x_lo, x_hi, idx_x, x_ok, pass, k_lo >= m_hi);
                 }
             }
-            // 64 heads: the shared reference is the one both waves of a head
-            // used (a wave whose own tiles had no valid key may not hold it)
-            if constexpr (H64)
-                m_ref = *(const LDS_AS float*)(lds + L::L_MREF + 4 * (32 * (wave & 1) + (opaque_lane() & 31)));
             // the reference stays fixed once set, so one test of the largest
             // score max of the pass covers every tile
             const bool restart = __any(m_seen > m_ref + p.threshold);
@@ -1192,15 +1298,7 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
             __syncthreads();
             if (flags == 0u || pass > 0) break;
             if (wave == 0 && opaque_lane() < 4) lds[L::L_FLAGS + opaque_lane()] = 0;
-            m_ref = m_seen;
-            if constexpr (H64) {
-                // the true max of a head over the tiles of both of its waves
-                if (opaque_lane() < 32) *(LDS_AS float*)(lds + L::L_LM + 4 * (32 * wave + opaque_lane())) = m_seen;
-                __syncthreads();
-                m_ref = fmaxf(m_ref, *(const LDS_AS float*)(lds + L::L_LM + 4 * (32 * (wave ^ 2) + (opaque_lane() & 31))));
-                m_seen = m_ref;
-                __syncthreads();
-            }
+            m_ref = m_seen;     // 64 heads: both waves of a head saw the same maxima
         }
 
         // ---- epilogue: l and m of every head through LDS
@@ -1446,11 +1544,12 @@ hipError_t allow_lds_once(K k, bool& done, int bytes) {
 template <bool FLAT, bool DENSE, bool H64, int F, bool EXTRA = false>
 hipError_t launch_h128(const DecodeParams& p, int num_parts, hipStream_t st) {
     constexpr int fi = F == F32 ? 0 : F == F4 ? 1 : F == FB ? 4 : EXTRA ? 3 : 2;
+    constexpr int bytes = Lay<F, H64>::L_BYTES;
     hipError_t e = allow_lds_once(decode_fp8_h128_kernel<FLAT, DENSE, H64, F, EXTRA>,
-                                  g_lds_decode[FLAT][DENSE][H64][fi], Lay<F>::L_BYTES);
+                                  g_lds_decode[FLAT][DENSE][H64][fi], bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_fp8_h128_kernel<FLAT, DENSE, H64, F, EXTRA>), dim3(num_parts, p.s_q), dim3(NW * 64),
-                       Lay<F>::L_BYTES, st, p);
+                       bytes, st, p);
     return hipGetLastError();
 }
 template <int F>
