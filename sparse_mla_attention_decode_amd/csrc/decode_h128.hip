@@ -70,7 +70,6 @@ constexpr int IDS_SLOTS = 2;                      // token-id tiles per wave in 
 constexpr int ZERO_ROWS = 64;                     // rows of the zero page
 constexpr int KAHEAD = 3;                         // score fragments read ahead of their MFMAs
 constexpr int DENSE_PAGE = 64;                    // tokens per page for dense decode
-constexpr int XPB = NW * 2048;                    // P of one tile, all 128 heads
 constexpr int L_RAW = 0;
 
 // Cache formats (the kv_format values).

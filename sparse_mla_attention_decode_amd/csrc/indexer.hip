@@ -262,7 +262,11 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
     const uint16_t* s = p.scores + (size_t)r * p.max_pages * IX_PAGE;
     const u32x4* s16 = (const u32x4*)s;               // rows start on 128-byte boundaries
     const int n_chunks = (len + 7) >> 3;              // 8 scores per 16-byte chunk (inside the row)
-    const bool in_lds = len <= TK_LDS_KEYS;
+    // the body is compiled for rows kept in LDS and for longer ones: in the
+    // first no loop holds a global load, whose wait would also wait for the
+    // id stores issued before it
+    auto body = [&](auto lds_c) {
+    constexpr bool in_lds = decltype(lds_c)::value;
     constexpr int BATCH = 4;                          // chunks per thread per round (32 keys)
     const int n_pages = (len + IX_PAGE - 1) / IX_PAGE;
     if (in_lds)
@@ -471,6 +475,9 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
             take_b1(mgt, meq, [&](int i) { return 8 * (cb + (i >> 3) * TOPK_THREADS) + (i & 7); });
         });
     }
+    };
+    if (len <= TK_LDS_KEYS) body(std::integral_constant<bool, true>{});
+    else body(std::integral_constant<bool, false>{});
 }
 
 }  // namespace

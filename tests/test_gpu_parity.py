@@ -196,14 +196,14 @@ def test_single_repeated_row_is_exact():
             assert np.all(np.abs(lse[bi, :, 0] - (s + math.log(w.topk))) <= LSE_TOL)
 
 
-@pytest.mark.parametrize("h_q,slot", [(128, 100), (64, 100), (64, 70)])
+@pytest.mark.parametrize("h_q,slot", [(128, 100), (64, 100), (64, 70), (64, 120)])
 def test_reference_max_recompute_path(h_q, slot):
     """A late tile whose scores exceed the first tile's max by far more than
     2^64 (log2 units) forces the piece to be recomputed; the result must still
     match the definition.  With 64 heads the two waves of a head block run
-    the softmax of different key halves (slot 100: the 4th tile, slot 70: the
-    3rd), so the large score lies in one wave's half and the recompute must
-    use it in both."""
+    the softmax of different key halves (slot 100: key 4 of the 4th tile,
+    slot 70: key 6 of the 3rd, slot 120: key 24 of the 4th), so the large
+    score lies in one wave's half and the recompute must use it in both."""
     w = W.paged_decode("jump", 41, b=2, s_q=1, h_q=h_q, topk=128, tokens_per_seq=256, P=64)
     q = O.bf16_value(w.q_bits[0, 0, 0])
     big_tok = int(w.indices[0, 0, slot])
