@@ -50,18 +50,18 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "034ac98765bc006bb3351aa518acb93bd2a93141d143be0500d1392bfcf7455e",
+DECODE_TRAFFIC = {"sources_sha256": "c90726d895c50c5c62eae7d1f54538b3722c80ec5fe404edb5f5b33fbcfa04e0",
                   "fetch_scale": 2.0, "write_scale": 1.0,
                   # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per decode dispatch
-                  "kib": {"decode": (54051.8, 32896.0), "halfhead": (100954.9, 16448.0),
-                          "v4": (51791.0, 32896.0), "v41": (44525.3, 32896.0),
-                          "prefill": (2330462.3, 541004.3)}}
+                  "kib": {"decode": (54051.3, 32896.0), "halfhead": (100991.4, 16448.0),
+                          "v4": (51774.1, 32896.0), "v41": (44517.5, 32896.0),
+                          "prefill": (2329602.9, 540858.0)}}
 
 INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
                           "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",
                           "sparse_mla_attention_decode_amd/csrc/device_common.h")
-INDEXER_TRAFFIC = {"sources_sha256": "2d84fdfdf40a31353ba5711c2552f91cc7a02a9291f961879694dda6673b9e3d",
-                   "fetch_kib": 137459.3, "fetch_scale": 2.0, "write_kib": 4224.0, "write_scale": 1.0}
+INDEXER_TRAFFIC = {"sources_sha256": "444c2128acb86be6dcdeae5131b166b2c72fc67a7735e40f785ae3c85732929c",
+                   "fetch_kib": 137458.0, "fetch_scale": 2.0, "write_kib": 4223.7, "write_scale": 1.0}
 
 
 def traffic_of(sources, t):
