@@ -228,7 +228,7 @@ __device__ __forceinline__ uint32_t wave_slots(uint32_t n, uint32_t* counter) {
 //      (longer rows re-read the scores in every pass);
 //   2. a histogram of the key's top 12 bits (sign, exponent and three
 //      mantissa bits: scores of one magnitude spread over eight bins per
-//      octave);
+//      octave), counted in the pass that copies the keys into LDS;
 //   3. the threshold bin b1: fewer than K keys above it, at least K at or
 //      above it (one wave, shuffle scans);
 //   4. one pass that writes every token whose key lies above b1 and keeps
@@ -315,7 +315,25 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
     };
     auto key_of = [](const u32x4& k, int e) -> uint32_t { return (k[e >> 1] >> (16 * (e & 1))) & 0xFFFFu; };
 
-    // 1. keys into LDS
+    // first digit of one chunk's keys (only the row's last chunk can hold
+    // tokens past it: the test is per chunk, so a full chunk costs an extract
+    // and an atomic per key)
+    auto hist_chunk = [&](const u32x4& k, int c) {
+        if (8 * c + 8 <= len) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                atomicAdd(&hist[(k[w] >> 4) & 0xFFFu], 1u);
+                atomicAdd(&hist[k[w] >> 20], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                atomicAdd(&hist[8 * c + e < len ? key_of(k, e) >> 4 : TK_BINS + lane], 1u);
+        }
+    };
+    __syncthreads();                                  // histogram cleared
+    // 1 + 2. keys into LDS with their first digit counted on the way (rows
+    // kept in LDS), or the first digit from the scores (longer rows)
     if (in_lds) {
         for (int c0 = tid; c0 < n_chunks; c0 += BATCH * TOPK_THREADS) {
             u32x4 v[BATCH];
@@ -325,31 +343,23 @@ __global__ void __launch_bounds__(TOPK_THREADS) indexer_topk_kernel(IndexerParam
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
                 const int c = c0 + u * TOPK_THREADS;
-                if (c < n_chunks) *(u32x4*)(keys + 8 * c) = to_keys(v[u], c);
-            }
-        }
-    }
-    __syncthreads();
-    // 2. first digit (only the row's last chunk can hold tokens past it: the
-    // test is per chunk, so a full chunk costs an extract and an atomic per key)
-    for_rounds([&](int cb, u32x4* k) {
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int c = cb + u * TOPK_THREADS;
-            if (c >= n_chunks) break;
-            if (8 * c + 8 <= len) {
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    atomicAdd(&hist[(k[u][w] >> 4) & 0xFFFu], 1u);
-                    atomicAdd(&hist[k[u][w] >> 20], 1u);
+                if (c < n_chunks) {
+                    const u32x4 k = to_keys(v[u], c);
+                    *(u32x4*)(keys + 8 * c) = k;
+                    hist_chunk(k, c);
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    atomicAdd(&hist[8 * c + e < len ? key_of(k[u], e) >> 4 : TK_BINS + lane], 1u);
             }
         }
-    });
+    } else {
+        for_rounds([&](int cb, u32x4* k) {
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int c = cb + u * TOPK_THREADS;
+                if (c >= n_chunks) break;
+                hist_chunk(k[u], c);
+            }
+        });
+    }
     __syncthreads();
     // 3. threshold bin (exists: len > K)
     find_threshold_bin(hist, (uint32_t)K, gsum, &bin_s, &above_s);
