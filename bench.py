@@ -60,8 +60,8 @@ DECODE_TRAFFIC = {"sources_sha256": "c90726d895c50c5c62eae7d1f54538b3722c80ec5fe
 INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
                           "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",
                           "sparse_mla_attention_decode_amd/csrc/device_common.h")
-INDEXER_TRAFFIC = {"sources_sha256": "444c2128acb86be6dcdeae5131b166b2c72fc67a7735e40f785ae3c85732929c",
-                   "fetch_kib": 137458.0, "fetch_scale": 2.0, "write_kib": 4223.7, "write_scale": 1.0}
+INDEXER_TRAFFIC = {"sources_sha256": "43a82353eb4f8e99b5d4f8faf4e90e5f4c4b50b042e65242dcd76bdb3f4d4c26",
+                   "fetch_kib": 137458.8, "fetch_scale": 2.0, "write_kib": 4223.3, "write_scale": 1.0}
 
 
 def traffic_of(sources, t):
