@@ -1335,10 +1335,18 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
         }
         const int own_head = 32 * wave + n;
         if (nsplit == 1) {
-            uint16_t* obase = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss;
+            // O/l as bf16 through LDS, so that every store writes whole
+            // 256-byte row segments: the wave's 128 dims of head r at
+            // 32768 w + 256 r, its 16-byte chunk c at position c ^ (r % 16)
+            // (conflict-free column writes), read back four heads per
+            // instruction.  The LDS below 128 KB is free here: the tiles are
+            // done and the head statistics live above it.
+            static_assert(L::L_LM >= NW * 32768, "epilogue transpose area");
+            uint16_t* obase = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + 128 * wave;
+            const int treg = wave * 32768;
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {                   // 64 heads: blocks 0 and 1 only
-                uint16_t* orow = obase + (int64_t)(32 * hb + n) * p.out_sh + 128 * wave + 4 * h;
+                const int r = 32 * hb + n;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -1346,8 +1354,15 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         const f32x16& o = O[4 * j + hb];
                         const u32x2 w = {pack_bf16(o[4 * g] * inv[hb], o[4 * g + 1] * inv[hb]),
                                          pack_bf16(o[4 * g + 2] * inv[hb], o[4 * g + 3] * inv[hb])};
-                        *(u32x2*)(orow + 32 * j + 8 * g) = w;
+                        *(LDS_AS u32x2*)(lds + treg + 256 * r + 16 * ((4 * j + g) ^ (r & 15)) + 8 * h) = w;
                     }
+            }
+            const int k = lane & 15;
+#pragma unroll
+            for (int i = 0; i < 8 * HB; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                const u32x4 v = lds_read16(lds, treg + 256 * r + 16 * (k ^ (r & 15)));
+                *(u32x4*)(obase + (int64_t)r * p.out_sh + 8 * k) = v;
             }
             if (h == 0 && own_head < p.h_q)
                 p.lse[((int64_t)req * p.h_q + own_head) * p.s_q + sq] =
