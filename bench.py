@@ -50,12 +50,12 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "c90726d895c50c5c62eae7d1f54538b3722c80ec5fe404edb5f5b33fbcfa04e0",
+DECODE_TRAFFIC = {"sources_sha256": "05898edee3cb2bc5ac0a14343a8567cd9b28d0ede6508f7e99c4e057bc7ab9a5",
                   "fetch_scale": 2.0, "write_scale": 1.0,
                   # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per decode dispatch
-                  "kib": {"decode": (54051.3, 32896.0), "halfhead": (100991.4, 16448.0),
-                          "v4": (51774.1, 32896.0), "v41": (44517.5, 32896.0),
-                          "prefill": (2329602.9, 540858.0)}}
+                  "kib": {"decode": (54056.2, 32896.0), "halfhead": (100993.4, 16448.0),
+                          "v4": (51779.8, 32896.0), "v41": (44524.5, 32896.0),
+                          "prefill": (2331524.1, 541232.2)}}
 
 INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
                           "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",
