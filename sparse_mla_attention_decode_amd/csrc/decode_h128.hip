@@ -954,10 +954,12 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                         }
                     }
                 };
-                // 64 heads, after part 2: this wave's key half of the scores in
-                // S (its partial plus the partner's, from LDS), masked by the
+                // 64 heads, under the value steps of part 2 (xs_read, then
+                // assemble): this wave's key half of the next tile's scores in S
+                // (its partial plus the partner's, from LDS), masked by that
                 // tile's validity vm, and its maximum (both half-waves) in hm and
-                // in LDS for the partner's next part 1.
+                // in LDS for the partner's next part 1; the prologue does the
+                // same for tile 0.
                 auto xs_read = [&](auto d_c, int ln, u32x4& a, u32x4& b) {
                     constexpr int D = decltype(d_c)::value & 1;
                     const int xi = L::L_XS + (2 * (wave & 1) + D) * 2048 + 16 * ln;
@@ -994,7 +996,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_fp8_h128_kernel(DecodeParam
                 // from LDS) with, between them, the dequant of tile i+2 (raw slot
                 // par) written straight into the K buffer at kb2 (free since tile
                 // i-1 is done) and the copy source of tile i+4 (id slot par).  Past
-                // the piece the staged rows are zero rows.
+                // the piece the staged rows are zero rows.  step_hook(jv) runs at
+                // the end of value step jv (64 heads: the score exchange).
                 auto part2 = [&](int i, int par, int kbv, int kb2, int ln, bool stage, bool copies_out,
                                  const uint8_t*& src4, int& sdel4, uint32_t& vm4, auto&& step_hook) {
                     const int vb = kbv + pv_base(ln) + 64 * 4 * wave;
