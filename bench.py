@@ -50,7 +50,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "05898edee3cb2bc5ac0a14343a8567cd9b28d0ede6508f7e99c4e057bc7ab9a5",
+DECODE_TRAFFIC = {"sources_sha256": "17f3352790d66d9ceaba96936a99de183d820249de8b3b345929b0c489744fda",
                   "fetch_scale": 2.0, "write_scale": 1.0,
                   # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per decode dispatch
                   "kib": {"decode": (54056.2, 32896.0), "halfhead": (100993.4, 16448.0),
