@@ -406,6 +406,29 @@ def test_bf16_prefill_h64_padded_rows(parts):
     assert_parity(out, lse, ref_out, ref_lse, all_queries(w), f"bf16 h64 padded parts={parts}")
 
 
+@pytest.mark.parametrize("h_q,parts", [(128, 1), (128, 5), (64, 1), (64, 5)])
+def test_strided_out_rows(h_q, parts):
+    """The output as a view whose head rows are 640 elements apart: the
+    unsplit epilogue (one partition per query column, whole 256-byte row
+    segments per store) and the combine (split plan) write every query's rows
+    right and leave the 128 padding elements of each row alone."""
+    _need_gpu()
+    w = W.paged_decode("strided_out", 321, b=3, s_q=2, h_q=h_q, topk=200, tokens_per_seq=512, P=64)
+    plan = _plan(w, num_parts=parts, split_granularity=32)
+    buf = torch.full((w.b, w.s_q, h_q, 640), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[..., :512]
+    plan.get_sched_meta()
+    a = plan.args(w.q_device(), w.kv_device(), w.indices_device(), w.sm_scale, out=out)
+    assert a.out_stride_h == 640
+    M.mla_sparse_decode_fwd(a)
+    M.mla_splitkv_combine(a)
+    torch.cuda.synchronize()
+    assert bool(torch.all(buf[..., 512:] == 7.0)), "padding written"
+    ref_out, ref_lse = oracle(w)
+    assert_parity(out.float().cpu().numpy(), plan.lse.cpu().numpy(), ref_out, ref_lse, all_queries(w),
+                  f"strided out h={h_q} parts={parts}")
+
+
 def test_cfg3_sparse_prefill_bf16():
     """4096 query tokens: 264 of them against the oracle -- every 16th token
     (one per 16-column stretch of the launch grid) plus both ends."""
