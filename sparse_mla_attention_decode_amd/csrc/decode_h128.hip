@@ -1536,12 +1536,29 @@ __global__ void __launch_bounds__(64) combine_packed_kernel(DecodeParams p) {
                           : W;
     const bool nan_out = poison || nan_lse;
     const float inv = nan_out ? __builtin_nanf("") : W > 0.f ? 1.0f / den : 0.f;
-    uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh +
-                     128 * w + 32 * j + 4 * h;
+    // lane (n, h) holds dims 8 g + 4 h .. + 3 (g < 4) of the piece's 32; one
+    // swap between the half-waves gives lane (n, h) dims 16 h .. 16 h + 15,
+    // written as two 16-byte stores
+    uint32_t wd[8];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-        *(u32x2*)(orow + 8 * g) = u32x2{pack_bf16(acc[4 * g] * inv, acc[4 * g + 1] * inv),
-                                        pack_bf16(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv)};
+    for (int g = 0; g < 4; ++g) {
+        wd[2 * g] = pack_bf16(acc[4 * g] * inv, acc[4 * g + 1] * inv);
+        wd[2 * g + 1] = pack_bf16(acc[4 * g + 2] * inv, acc[4 * g + 3] * inv);
+    }
+    uint32_t mine[4], theirs[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t send = h ? wd[k] : wd[4 + k];      // the other half's dims
+        const auto sw = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+        theirs[k] = h ? sw[0] : sw[1];
+        mine[k] = h ? wd[4 + k] : wd[k];
+    }
+    uint16_t* orow = p.out + (int64_t)req * p.out_sb + (int64_t)sq * p.out_ss + (int64_t)head * p.out_sh +
+                     128 * w + 32 * j + 16 * h;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        *(u32x4*)(orow + 8 * q) = h ? u32x4{theirs[2 * q], theirs[2 * q + 1], mine[2 * q], mine[2 * q + 1]}
+                                    : u32x4{mine[2 * q], mine[2 * q + 1], theirs[2 * q], theirs[2 * q + 1]};
     if (w == 0 && j == 0 && h == 0)
         p.lse[((int64_t)req * p.h_q + head) * p.s_q + sq] =
             nan_out ? __builtin_nanf("") : M == -INFINITY ? INFINITY : (M + __log2f(W)) * 0.69314718055994531f;
