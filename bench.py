@@ -50,12 +50,12 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 DECODE_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/decode_h128.hip",
                          "sparse_mla_attention_decode_amd/csrc/device_common.h",
                          "sparse_mla_attention_decode_amd/csrc/mla_internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "17f3352790d66d9ceaba96936a99de183d820249de8b3b345929b0c489744fda",
+DECODE_TRAFFIC = {"sources_sha256": "ec72c735b050720b7c380e04e5f809359d37947662c2598559cb0e678b54d4fd",
                   "fetch_scale": 2.0, "write_scale": 1.0,
                   # workload: (FETCH_SIZE KiB, WRITE_SIZE KiB) per decode dispatch
-                  "kib": {"decode": (54056.2, 32896.0), "halfhead": (100993.4, 16448.0),
-                          "v4": (51779.8, 32896.0), "v41": (44524.5, 32896.0),
-                          "prefill": (2331524.1, 541232.2)}}
+                  "kib": {"decode": (54055.7, 32896.0), "halfhead": (100990.4, 16448.0),
+                          "v4": (51776.3, 32896.0), "v41": (44524.8, 32896.0),
+                          "prefill": (2331126.8, 541269.6)}}
 
 INDEXER_KERNEL_SOURCES = ("sparse_mla_attention_decode_amd/csrc/indexer.hip",
                           "sparse_mla_attention_decode_amd/csrc/indexer_internal.h",
